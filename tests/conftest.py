@@ -1,0 +1,24 @@
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+
+def pytest_configure(config):
+    config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
+    config.addinivalue_line("markers", "slow: full-size case (minutes of oracle time)")
+
+
+@pytest.fixture(scope="session")
+def gpu_lib():
+    """The built HIP library on cuda:0; fails loudly if it is missing."""
+    import torch
+    if not torch.cuda.is_available():
+        pytest.fail("GPU test collected on a machine without a GPU")
+    import gated_deltanet_chunked_04_amd as gdn
+    gdn.load_library()
+    return gdn
