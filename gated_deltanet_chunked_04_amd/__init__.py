@@ -1,0 +1,242 @@
+"""Gated DeltaNet chunked prefill on AMD MI355X (gfx950): Python binding of libgdn.
+
+The functions below carry the C ABI's names (include/gdn.h) and only marshal
+torch tensors into it: device pointers, sizes and the current HIP stream.
+Every step of the computation runs in the HIP library; if libgdn.so is
+missing they raise instead of computing anything elsewhere.
+
+  gdn_plan(...)               host-side plan (AutoCP decision, sub-sequence length, workspace)
+  gdn_chunk_fwd(...)          O and the final state
+  gdn_chunk_bwd(...)          gradients of <dO, O> + <dS_T, S_T>
+  gdn_intra_chunk(...)        the intra-chunk kernel alone (gate cumsum, w, u)
+  gdn_cp_modes(...)           per sequence-head CP decision (0 none, 1 warmup, 2 exact)
+  chunk_gated_delta_rule(...) autograd wrapper over gdn_chunk_fwd / gdn_chunk_bwd
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional
+
+import numpy as np
+import torch
+
+from ._abi import (CP_MODES, EXPORTS, GDN_DTYPE_BF16, GDN_DTYPE_FP32, GdnDesc, GdnError,  # noqa: F401
+                   GdnPlanInfo, check, load_library, status_string)
+
+__all__ = ["gdn_plan", "gdn_chunk_fwd", "gdn_chunk_bwd", "gdn_intra_chunk", "gdn_cp_modes",
+           "chunk_gated_delta_rule", "load_library", "make_desc", "GdnError"]
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+class Desc:
+    """A gdn_desc plus the host objects its pointers refer to."""
+
+    def __init__(self, B, T, H, K, V, dtype, *, scale=1.0, cu_seqlens=None, cu_seqlens_host=None,
+                 cp_mode="auto", warmup_chunks=0, seg_chunks=0, warmup_eps=0.0, num_cus=0):
+        d = GdnDesc()
+        d.B, d.T, d.H, d.K, d.V = int(B), int(T), int(H), int(K), int(V)
+        d.chunk = 64
+        if dtype == torch.bfloat16:
+            d.dtype = GDN_DTYPE_BF16
+        elif dtype == torch.float32:
+            d.dtype = GDN_DTYPE_FP32
+        else:
+            raise TypeError(f"unsupported input dtype {dtype} (bf16 or fp32)")
+        d.scale = float(scale)
+        self._host_cu = None
+        self._dev_cu = None
+        if cu_seqlens is not None:
+            if cu_seqlens_host is None:
+                cu_seqlens_host = cu_seqlens.detach().cpu()
+            hc = np.ascontiguousarray(np.asarray(
+                cu_seqlens_host.numpy() if hasattr(cu_seqlens_host, "numpy") else cu_seqlens_host,
+                dtype=np.int32))
+            self._host_cu = hc
+            if cu_seqlens.dtype != torch.int32 or not cu_seqlens.is_cuda:
+                raise TypeError("cu_seqlens must be an int32 device tensor")
+            self._dev_cu = cu_seqlens.contiguous()
+            d.num_seqs = len(hc) - 1
+            d.cu_seqlens = self._dev_cu.data_ptr()
+            d.cu_seqlens_host = hc.ctypes.data
+        d.cp_mode = CP_MODES[cp_mode] if isinstance(cp_mode, str) else int(cp_mode)
+        d.warmup_chunks = int(warmup_chunks)
+        d.seg_chunks = int(seg_chunks)
+        d.warmup_eps = float(warmup_eps)
+        d.num_cus = int(num_cus)
+        self.c = d
+
+    @property
+    def ref(self):
+        return ctypes.byref(self.c)
+
+
+def make_desc(q, v, **kw) -> Desc:
+    B, T, H, K = q.shape
+    return Desc(B, T, H, K, v.shape[-1], q.dtype, **kw)
+
+
+def gdn_plan(desc: Desc) -> dict:
+    info = GdnPlanInfo()
+    check(load_library().gdn_plan(desc.ref, ctypes.byref(info)), "gdn_plan")
+    return {f: getattr(info, f) for f, _ in GdnPlanInfo._fields_}
+
+
+def _workspace(nbytes: int, device, workspace=None):
+    if workspace is not None:
+        if workspace.numel() * workspace.element_size() < nbytes:
+            raise ValueError("workspace too small")
+        return workspace
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+def _check_inputs(q, k, v, g, beta, initial_state, N):
+    B, T, H, K = q.shape
+    V = v.shape[-1]
+    dev = q.device
+    if not q.is_cuda:
+        raise ValueError("inputs must be device tensors")
+    for name, t, shape in (("k", k, (B, T, H, K)), ("v", v, (B, T, H, V))):
+        if tuple(t.shape) != shape or t.dtype != q.dtype or t.device != dev or not t.is_contiguous():
+            raise ValueError(f"{name}: expected contiguous {shape} {q.dtype} on {dev}")
+    for name, t in (("g", g), ("beta", beta)):
+        if tuple(t.shape) != (B, T, H) or t.dtype != torch.float32 or t.device != dev or not t.is_contiguous():
+            raise ValueError(f"{name}: expected contiguous fp32 {(B, T, H)} on {dev}")
+    if not q.is_contiguous():
+        raise ValueError("q must be contiguous")
+    if initial_state is not None:
+        if (tuple(initial_state.shape) != (N, H, V, K) or initial_state.dtype != torch.float32
+                or not initial_state.is_contiguous() or initial_state.device != dev):
+            raise ValueError(f"initial_state: expected contiguous fp32 {(N, H, V, K)} on {dev}")
+
+
+def _num_seqs(q, cu_seqlens):
+    return q.shape[0] if cu_seqlens is None else int(cu_seqlens.numel()) - 1
+
+
+def gdn_chunk_fwd(q, k, v, g, beta, initial_state=None, *, scale=1.0, cu_seqlens=None,
+                  cu_seqlens_host=None, output_final_state=True, cp_mode="auto", warmup_chunks=0,
+                  seg_chunks=0, warmup_eps=0.0, workspace=None, o=None, final_state=None):
+    """Forward. Returns (o, final_state or None). Runs on the current stream."""
+    N = _num_seqs(q, cu_seqlens)
+    _check_inputs(q, k, v, g, beta, initial_state, N)
+    desc = make_desc(q, v, scale=scale, cu_seqlens=cu_seqlens, cu_seqlens_host=cu_seqlens_host,
+                     cp_mode=cp_mode, warmup_chunks=warmup_chunks, seg_chunks=seg_chunks,
+                     warmup_eps=warmup_eps)
+    lib = load_library()
+    nbytes = ctypes.c_size_t()
+    check(lib.gdn_chunk_fwd_workspace_size(desc.ref, ctypes.byref(nbytes)), "gdn_chunk_fwd_workspace_size")
+    ws = _workspace(nbytes.value, q.device, workspace)
+    B, T, H, K = q.shape
+    V = v.shape[-1]
+    if o is None:
+        o = torch.empty((B, T, H, V), dtype=q.dtype, device=q.device)
+    if output_final_state and final_state is None:
+        final_state = torch.empty((N, H, V, K), dtype=torch.float32, device=q.device)
+    if not output_final_state:
+        final_state = None
+    check(lib.gdn_chunk_fwd(desc.ref, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state),
+                            _ptr(o), _ptr(final_state), _ptr(ws), ctypes.c_size_t(ws.numel()), _stream()),
+          "gdn_chunk_fwd")
+    return o, final_state
+
+
+def gdn_chunk_bwd(q, k, v, g, beta, d_o, initial_state=None, d_final_state=None, *, scale=1.0,
+                  cu_seqlens=None, cu_seqlens_host=None, cp_mode="auto", warmup_chunks=0, seg_chunks=0,
+                  warmup_eps=0.0, workspace=None, need_d_initial_state=True):
+    """Backward. Returns dict(dq, dk, dv, dg, dbeta, d_initial_state)."""
+    N = _num_seqs(q, cu_seqlens)
+    _check_inputs(q, k, v, g, beta, initial_state, N)
+    B, T, H, K = q.shape
+    V = v.shape[-1]
+    if tuple(d_o.shape) != (B, T, H, V) or d_o.dtype != q.dtype or not d_o.is_contiguous():
+        raise ValueError("d_o must match o")
+    if d_final_state is not None and (tuple(d_final_state.shape) != (N, H, V, K)
+                                      or d_final_state.dtype != torch.float32
+                                      or not d_final_state.is_contiguous()):
+        raise ValueError("d_final_state must be contiguous fp32 [N,H,V,K]")
+    desc = make_desc(q, v, scale=scale, cu_seqlens=cu_seqlens, cu_seqlens_host=cu_seqlens_host,
+                     cp_mode=cp_mode, warmup_chunks=warmup_chunks, seg_chunks=seg_chunks,
+                     warmup_eps=warmup_eps)
+    lib = load_library()
+    nbytes = ctypes.c_size_t()
+    check(lib.gdn_chunk_bwd_workspace_size(desc.ref, ctypes.byref(nbytes)), "gdn_chunk_bwd_workspace_size")
+    ws = _workspace(nbytes.value, q.device, workspace)
+    out = dict(dq=torch.empty_like(q), dk=torch.empty_like(k), dv=torch.empty_like(v),
+               dg=torch.empty_like(g), dbeta=torch.empty_like(beta),
+               d_initial_state=(torch.empty((N, H, V, K), dtype=torch.float32, device=q.device)
+                                if need_d_initial_state else None))
+    check(lib.gdn_chunk_bwd(desc.ref, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state),
+                            _ptr(d_o), _ptr(d_final_state), _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]),
+                            _ptr(out["dg"]), _ptr(out["dbeta"]), _ptr(out["d_initial_state"]),
+                            _ptr(ws), ctypes.c_size_t(ws.numel()), _stream()),
+          "gdn_chunk_bwd")
+    return out
+
+
+def gdn_intra_chunk(k, v, g, beta, *, cu_seqlens=None, cu_seqlens_host=None):
+    """The intra-chunk kernel alone: returns (gam [B,T,H] fp32, w [B,T,H,K], u [B,T,H,V])."""
+    B, T, H, K = k.shape
+    desc = make_desc(k, v, cu_seqlens=cu_seqlens, cu_seqlens_host=cu_seqlens_host)
+    lib = load_library()
+    nbytes = ctypes.c_size_t()
+    check(lib.gdn_chunk_fwd_workspace_size(desc.ref, ctypes.byref(nbytes)), "gdn_chunk_fwd_workspace_size")
+    ws = _workspace(nbytes.value, k.device)
+    gam = torch.empty((B, T, H), dtype=torch.float32, device=k.device)
+    w = torch.empty_like(k)
+    u = torch.empty_like(v)
+    check(lib.gdn_intra_chunk(desc.ref, _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(gam), _ptr(w), _ptr(u),
+                              _ptr(ws), ctypes.c_size_t(ws.numel()), _stream()), "gdn_intra_chunk")
+    return gam, w, u
+
+
+def gdn_cp_modes(k, v, g, beta, *, cu_seqlens=None, cu_seqlens_host=None, cp_mode="auto",
+                 warmup_chunks=0, seg_chunks=0, warmup_eps=0.0):
+    """Per sequence-head CP decision [N, H] int32: 0 no split, 1 warmup, 2 exact."""
+    N = _num_seqs(k, cu_seqlens)
+    desc = make_desc(k, v, cu_seqlens=cu_seqlens, cu_seqlens_host=cu_seqlens_host, cp_mode=cp_mode,
+                     warmup_chunks=warmup_chunks, seg_chunks=seg_chunks, warmup_eps=warmup_eps)
+    lib = load_library()
+    nbytes = ctypes.c_size_t()
+    check(lib.gdn_chunk_fwd_workspace_size(desc.ref, ctypes.byref(nbytes)), "gdn_chunk_fwd_workspace_size")
+    ws = _workspace(nbytes.value, k.device)
+    modes = torch.empty((N, k.shape[2]), dtype=torch.int32, device=k.device)
+    check(lib.gdn_cp_modes(desc.ref, _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(modes), _ptr(ws),
+                           ctypes.c_size_t(ws.numel()), _stream()), "gdn_cp_modes")
+    return modes
+
+
+class _GDNFunction(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, q, k, v, g, beta, initial_state, scale, cu_seqlens, cp_mode):
+        o, sT = gdn_chunk_fwd(q, k, v, g, beta, initial_state, scale=scale, cu_seqlens=cu_seqlens,
+                              cp_mode=cp_mode)
+        ctx.save_for_backward(q, k, v, g, beta, initial_state, cu_seqlens)
+        ctx.scale = scale
+        ctx.cp_mode = cp_mode
+        return o, sT
+
+    @staticmethod
+    def backward(ctx, d_o, d_sT):
+        q, k, v, g, beta, s0, cu = ctx.saved_tensors
+        gr = gdn_chunk_bwd(q, k, v, g, beta, d_o.contiguous(), s0,
+                           None if d_sT is None else d_sT.contiguous(), scale=ctx.scale,
+                           cu_seqlens=cu, cp_mode=ctx.cp_mode, need_d_initial_state=s0 is not None)
+        return (gr["dq"], gr["dk"], gr["dv"], gr["dg"], gr["dbeta"], gr["d_initial_state"], None, None, None)
+
+
+def chunk_gated_delta_rule(q, k, v, g, beta, scale: float = 1.0, initial_state=None,
+                           output_final_state: bool = True, cu_seqlens=None, cp_mode: str = "auto"):
+    """High-level call: (o, final_state) with autograd through gdn_chunk_bwd.
+
+    q, k: [B,T,H,K]; v: [B,T,H,V] (bf16 or fp32); g (natural-log decay) and beta: [B,T,H] fp32;
+    initial_state: [N,H,V,K] fp32 or None; cu_seqlens: int32 [N+1] device tensor (B must be 1).
+    """
+    o, sT = _GDNFunction.apply(q, k, v, g, beta, initial_state, scale, cu_seqlens, cp_mode)
+    return (o, sT) if output_final_state else (o, None)

@@ -1,0 +1,95 @@
+"""ctypes mirror of include/gdn.h and the loader of libgdn.so.
+
+Argument marshalling only: every step of the computation runs in the HIP
+library. If the library has not been built this module raises; nothing falls
+back to another implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libgdn.so")
+
+GDN_OK, GDN_ERR_INVALID_ARG, GDN_ERR_UNSUPPORTED, GDN_ERR_WORKSPACE, GDN_ERR_HIP = range(5)
+GDN_DTYPE_BF16, GDN_DTYPE_FP32 = 0, 1
+CP_MODES = {"auto": 0, "off": 1, "on": 2, "exact": 3, "warmup": 4}
+
+# Declared entry points of include/gdn.h (checked by the ABI test).
+EXPORTS = ("gdn_abi_version", "gdn_status_string", "gdn_plan", "gdn_chunk_fwd_workspace_size",
+           "gdn_chunk_fwd", "gdn_chunk_bwd_workspace_size", "gdn_chunk_bwd", "gdn_intra_chunk",
+           "gdn_cp_modes")
+
+
+class GdnDesc(ctypes.Structure):
+    _fields_ = [
+        ("B", ctypes.c_int64), ("T", ctypes.c_int64), ("H", ctypes.c_int64),
+        ("K", ctypes.c_int64), ("V", ctypes.c_int64),
+        ("chunk", ctypes.c_int32), ("dtype", ctypes.c_int32), ("scale", ctypes.c_float),
+        ("num_seqs", ctypes.c_int32),
+        ("cu_seqlens", ctypes.c_void_p), ("cu_seqlens_host", ctypes.c_void_p),
+        ("cp_mode", ctypes.c_int32), ("warmup_chunks", ctypes.c_int32),
+        ("seg_chunks", ctypes.c_int32), ("warmup_eps", ctypes.c_float),
+        ("num_cus", ctypes.c_int32), ("reserved", ctypes.c_int32 * 7),
+    ]
+
+
+class GdnPlanInfo(ctypes.Structure):
+    _fields_ = [
+        ("num_seqs", ctypes.c_int32), ("cp_on", ctypes.c_int32), ("seg_chunks", ctypes.c_int32),
+        ("warmup_chunks", ctypes.c_int32), ("warmup_eps", ctypes.c_float), ("v_tiles", ctypes.c_int32),
+        ("max_len", ctypes.c_int64), ("total_chunks", ctypes.c_int64),
+        ("total_segments", ctypes.c_int64),
+        ("fwd_workspace_bytes", ctypes.c_size_t), ("bwd_workspace_bytes", ctypes.c_size_t),
+    ]
+
+
+_LIB = None
+
+
+class GdnError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {status_string(status)} (status {status})")
+        self.status = status
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libgdn.so (built by gated_deltanet_chunked_04_amd.build). Raises if it is missing."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    if not os.path.exists(path):
+        raise RuntimeError(f"libgdn.so not found at {path}: build it first "
+                           "(python gated_deltanet_chunked_04_amd/build.py)")
+    lib = ctypes.CDLL(path)
+    vp, sz, i32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
+    dp = ctypes.POINTER(GdnDesc)
+    lib.gdn_abi_version.restype = i32
+    lib.gdn_abi_version.argtypes = []
+    lib.gdn_status_string.restype = ctypes.c_char_p
+    lib.gdn_status_string.argtypes = [i32]
+    lib.gdn_plan.restype = i32
+    lib.gdn_plan.argtypes = [dp, ctypes.POINTER(GdnPlanInfo)]
+    for f in ("gdn_chunk_fwd_workspace_size", "gdn_chunk_bwd_workspace_size"):
+        getattr(lib, f).restype = i32
+        getattr(lib, f).argtypes = [dp, ctypes.POINTER(sz)]
+    lib.gdn_chunk_fwd.restype = i32
+    lib.gdn_chunk_fwd.argtypes = [dp] + [vp] * 8 + [vp, sz, vp]
+    lib.gdn_chunk_bwd.restype = i32
+    lib.gdn_chunk_bwd.argtypes = [dp] + [vp] * 14 + [vp, sz, vp]
+    lib.gdn_intra_chunk.restype = i32
+    lib.gdn_intra_chunk.argtypes = [dp] + [vp] * 7 + [vp, sz, vp]
+    lib.gdn_cp_modes.restype = i32
+    lib.gdn_cp_modes.argtypes = [dp] + [vp] * 5 + [vp, sz, vp]
+    _LIB = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load_library().gdn_status_string(int(status)).decode()
+
+
+def check(status: int, where: str):
+    if status != GDN_OK:
+        raise GdnError(status, where)

@@ -1,0 +1,399 @@
+// gdn_api.hip -- the C ABI of libgdn: argument checks, the AutoCP planner, workspace
+// layout and the launch sequence. Host code only; kernels live in the other files.
+//
+// AutoCP rule (FlashQLA pages, ollai.cn article, "core advantages", AutoCP item): split
+// sequences inside the card only when batch x heads <= 40, or batch x heads <= 56 and the
+// sequence is at least 8192 tokens long. "batch" is read as the number of sequences and
+// "seq_len" as the longest one. The pages tuned these thresholds on a 132-SM GPU; they are
+// kept as the default and the sub-sequence length is chosen from this device's CU count.
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <algorithm>
+
+#include "../../include/gdn.h"
+#include "gdn_kernels.h"
+
+namespace gdn {
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr int kDefaultWarmup = 8;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+struct Plan {
+    int32_t N = 0;
+    int32_t varlen = 0;
+    int64_t Ttot = 0;
+    int64_t max_len = 0;
+    int64_t total_chunks = 0;
+    int32_t nt = 0;        // uniform: chunks per sequence
+    int32_t cp_on = 0;
+    int32_t seg_len = 1;
+    int32_t nseg = 1;      // uniform: segments per sequence
+    int64_t total_segs = 0;
+    int32_t W = kDefaultWarmup;
+    float eps = 1e-4f;
+    int32_t forced = 0;
+    int32_t esize = 2;
+    // forward workspace
+    size_t o_gam = 0, o_w = 0, o_u = 0, o_cstat = 0, o_bos = 0, o_len = 0, o_choff = 0, o_segoff = 0,
+           o_ctab = 0, o_stab = 0, o_modes = 0, o_seginit = 0, o_prep = 0, fwd_bytes = 0;
+    size_t bwd_bytes = 0;
+};
+
+int query_cus() {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 256;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+        return 256;
+    return cus;
+}
+
+gdn_status make_plan(const gdn_desc* d, Plan& p) {
+    if (!d) return GDN_ERR_INVALID_ARG;
+    for (int i = 0; i < 7; ++i)
+        if (d->reserved[i] != 0) return GDN_ERR_INVALID_ARG;
+    if (d->B < 1 || d->T < 0 || d->H < 1 || d->K < 1 || d->V < 1) return GDN_ERR_INVALID_ARG;
+    if (!(d->chunk == 0 || d->chunk == 64)) return GDN_ERR_UNSUPPORTED;
+    if (!(d->K == 64 || d->K == 128) || !(d->V == 64 || d->V == 128)) return GDN_ERR_UNSUPPORTED;
+    if (d->dtype != GDN_DTYPE_BF16 && d->dtype != GDN_DTYPE_FP32) return GDN_ERR_INVALID_ARG;
+    if (!isfinite(d->scale)) return GDN_ERR_INVALID_ARG;
+    if (d->cp_mode < GDN_CP_AUTO || d->cp_mode > GDN_CP_WARMUP) return GDN_ERR_INVALID_ARG;
+    if (d->warmup_chunks < 0 || d->warmup_chunks > 16) return GDN_ERR_INVALID_ARG;
+    if (d->seg_chunks < 0 || d->num_cus < 0) return GDN_ERR_INVALID_ARG;
+    if (!(d->warmup_eps >= 0.f && d->warmup_eps < 1.f)) return GDN_ERR_INVALID_ARG;
+    if (d->H > 65535) return GDN_ERR_UNSUPPORTED;
+    p.esize = d->dtype == GDN_DTYPE_BF16 ? 2 : 4;
+    p.W = d->warmup_chunks ? d->warmup_chunks : kDefaultWarmup;
+    p.eps = d->warmup_eps > 0.f ? d->warmup_eps : (d->dtype == GDN_DTYPE_BF16 ? 1e-4f : 1e-6f);
+    p.Ttot = d->B * d->T;
+    int64_t max_nt = 0;
+    if (d->cu_seqlens || d->cu_seqlens_host) {
+        if (!d->cu_seqlens || !d->cu_seqlens_host || d->B != 1 || d->num_seqs < 1) return GDN_ERR_INVALID_ARG;
+        const int32_t* cu = d->cu_seqlens_host;
+        if (cu[0] != 0 || cu[d->num_seqs] != d->T) return GDN_ERR_INVALID_ARG;
+        p.varlen = 1;
+        p.N = d->num_seqs;
+        for (int32_t n = 0; n < p.N; ++n) {
+            const int64_t len = (int64_t)cu[n + 1] - cu[n];
+            if (len < 0) return GDN_ERR_INVALID_ARG;
+            p.max_len = std::max(p.max_len, len);
+            p.total_chunks += (len + 63) / 64;
+        }
+        max_nt = (p.max_len + 63) / 64;
+    } else {
+        if (d->B > INT32_MAX) return GDN_ERR_INVALID_ARG;
+        p.N = (int32_t)d->B;
+        p.max_len = d->T;
+        p.nt = (int32_t)((d->T + 63) / 64);
+        p.total_chunks = (int64_t)p.N * p.nt;
+        max_nt = p.nt;
+    }
+    if (p.total_chunks > INT32_MAX || max_nt > INT32_MAX / 2) return GDN_ERR_UNSUPPORTED;
+
+    // AutoCP
+    const int64_t NH = (int64_t)p.N * d->H;
+    bool cp = false;
+    switch (d->cp_mode) {
+        case GDN_CP_AUTO: cp = (NH <= 40) || (NH <= 56 && p.max_len >= 8192); break;
+        case GDN_CP_OFF: cp = false; break;
+        default: cp = true; break;
+    }
+    p.forced = d->cp_mode == GDN_CP_WARMUP ? 1 : (d->cp_mode == GDN_CP_EXACT ? 2 : 0);
+    const int vtiles = (int)(d->V / 64);
+    int64_t seg_len = std::max<int64_t>(max_nt, 1);
+    if (cp) {
+        if (d->seg_chunks > 0) {
+            seg_len = d->seg_chunks;
+        } else {
+            const int cus = d->num_cus > 0 ? d->num_cus : query_cus();
+            const int64_t target = 2 * (int64_t)cus;            // workgroups to aim for
+            const int64_t units = NH * vtiles;                   // workgroups per segment layer
+            const int64_t want = std::max<int64_t>(1, target / std::max<int64_t>(units, 1));
+            seg_len = std::max<int64_t>(16, (max_nt + want - 1) / want);
+        }
+        if (seg_len >= max_nt) {
+            cp = false;
+            seg_len = std::max<int64_t>(max_nt, 1);
+        }
+    }
+    p.cp_on = cp ? 1 : 0;
+    p.seg_len = (int32_t)seg_len;
+    if (p.varlen) {
+        p.total_segs = 0;
+        const int32_t* cu = d->cu_seqlens_host;
+        for (int32_t n = 0; n < p.N; ++n) {
+            const int64_t nch = ((int64_t)cu[n + 1] - cu[n] + 63) / 64;
+            p.total_segs += nch <= seg_len ? 1 : (nch + seg_len - 1) / seg_len;
+        }
+    } else {
+        p.nseg = p.nt <= seg_len ? 1 : (int32_t)((p.nt + seg_len - 1) / seg_len);
+        p.total_segs = (int64_t)p.N * p.nseg;
+    }
+    if (p.total_segs > INT32_MAX) return GDN_ERR_UNSUPPORTED;
+
+    // forward workspace
+    const size_t H = (size_t)d->H, K = (size_t)d->K, V = (size_t)d->V, T = (size_t)p.Ttot;
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t o = off;
+        off = align_up(off + bytes);
+        return o;
+    };
+    p.o_gam = take(T * H * 4);
+    p.o_w = take(T * H * K * p.esize);
+    p.o_u = take(T * H * V * p.esize);
+    p.o_cstat = take((size_t)p.total_chunks * H * 8);
+    p.o_modes = take((size_t)p.N * H * 4);
+    if (p.varlen) {
+        p.o_bos = take((size_t)p.N * 8);
+        p.o_len = take((size_t)p.N * 4);
+        p.o_choff = take((size_t)(p.N + 1) * 4);
+        p.o_segoff = take((size_t)(p.N + 1) * 4);
+        p.o_ctab = take((size_t)p.total_chunks * 8);
+        p.o_stab = take((size_t)p.total_segs * 16);
+    }
+    if (p.cp_on) {
+        p.o_seginit = take((size_t)p.total_segs * H * V * K * 4);
+        p.o_prep = take((size_t)p.total_segs * H * (V + K) * K * 4);
+    }
+    p.fwd_bytes = std::max<size_t>(off, kAlign);
+    p.bwd_bytes = 0;
+    return GDN_OK;
+}
+
+Geo make_geo(const gdn_desc* d, const Plan& p, unsigned char* ws) {
+    Geo g;
+    memset(&g, 0, sizeof(g));
+    g.N = p.N;
+    g.H = (int32_t)d->H;
+    g.K = (int32_t)d->K;
+    g.V = (int32_t)d->V;
+    g.T = p.varlen ? p.Ttot : d->T;
+    g.varlen = p.varlen;
+    g.nt = p.nt;
+    g.seg_len = p.seg_len;
+    g.nseg = p.nseg;
+    g.total_chunks = p.total_chunks;
+    g.total_segs = p.total_segs;
+    if (p.varlen) {
+        g.seq_bos = reinterpret_cast<const int64_t*>(ws + p.o_bos);
+        g.seq_len = reinterpret_cast<const int32_t*>(ws + p.o_len);
+        g.seq_choff = reinterpret_cast<const int32_t*>(ws + p.o_choff);
+        g.seq_segoff = reinterpret_cast<const int32_t*>(ws + p.o_segoff);
+        g.chunk_tab = reinterpret_cast<const int2*>(ws + p.o_ctab);
+        g.seg_tab = reinterpret_cast<const int4*>(ws + p.o_stab);
+    }
+    return g;
+}
+
+
+#define GDN_TRY_HIP(x)                           \
+    do {                                         \
+        hipError_t e_ = (x);                     \
+        if (e_ != hipSuccess) return GDN_ERR_HIP; \
+    } while (0)
+
+gdn_status check_ws(const Plan& p, size_t need, void* ws, size_t bytes) {
+    if (!ws || bytes < need) return GDN_ERR_WORKSPACE;
+    if (reinterpret_cast<uintptr_t>(ws) % kAlign) return GDN_ERR_WORKSPACE;
+    (void)p;
+    return GDN_OK;
+}
+
+// Tables (varlen) + intra-chunk kernel into the given output buffers.
+gdn_status run_intra(const gdn_desc* d, const Plan& p, unsigned char* ws, const void* k, const void* v,
+                     const float* g, const float* beta, float* gam, void* w, void* u, hipStream_t st) {
+    if (p.varlen) {
+        TableArgs t;
+        t.cu = d->cu_seqlens;
+        t.N = p.N;
+        t.Ttot = p.Ttot;
+        t.seg_len = p.seg_len;
+        t.total_chunks = p.total_chunks;
+        t.total_segs = p.total_segs;
+        t.seq_bos = reinterpret_cast<int64_t*>(ws + p.o_bos);
+        t.seq_len = reinterpret_cast<int32_t*>(ws + p.o_len);
+        t.seq_choff = reinterpret_cast<int32_t*>(ws + p.o_choff);
+        t.seq_segoff = reinterpret_cast<int32_t*>(ws + p.o_segoff);
+        t.chunk_tab = reinterpret_cast<int2*>(ws + p.o_ctab);
+        t.seg_tab = reinterpret_cast<int4*>(ws + p.o_stab);
+        GDN_TRY_HIP(launch_tables(t, st));
+    }
+    IntraArgs ia;
+    ia.geo = make_geo(d, p, ws);
+    ia.k = k;
+    ia.v = v;
+    ia.g = g;
+    ia.beta = beta;
+    ia.gam = gam;
+    ia.w = w;
+    ia.u = u;
+    ia.cstat = reinterpret_cast<float2*>(ws + p.o_cstat);
+    GDN_TRY_HIP(launch_intra(ia, d->dtype, st));
+    return GDN_OK;
+}
+
+gdn_status run_decide(const gdn_desc* d, const Plan& p, unsigned char* ws, int32_t* modes, hipStream_t st) {
+    DecideArgs da;
+    da.geo = make_geo(d, p, ws);
+    da.cstat = reinterpret_cast<const float2*>(ws + p.o_cstat);
+    da.modes = modes;
+    da.warmup = p.W;
+    da.log_eps = logf(p.eps);
+    da.forced = p.forced;
+    GDN_TRY_HIP(launch_decide(da, st));
+    return GDN_OK;
+}
+
+}  // namespace
+}  // namespace gdn
+
+using namespace gdn;
+
+extern "C" {
+
+int gdn_abi_version(void) { return GDN_ABI_VERSION; }
+
+const char* gdn_status_string(gdn_status s) {
+    switch (s) {
+        case GDN_OK: return "ok";
+        case GDN_ERR_INVALID_ARG: return "invalid argument";
+        case GDN_ERR_UNSUPPORTED: return "unsupported configuration";
+        case GDN_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+        case GDN_ERR_HIP: return "HIP runtime or kernel launch error";
+    }
+    return "unknown status";
+}
+
+gdn_status gdn_plan(const gdn_desc* desc, gdn_plan_info* out) {
+    if (!out) return GDN_ERR_INVALID_ARG;
+    Plan p;
+    const gdn_status s = make_plan(desc, p);
+    if (s != GDN_OK) return s;
+    memset(out, 0, sizeof(*out));
+    out->num_seqs = p.N;
+    out->cp_on = p.cp_on;
+    out->seg_chunks = p.seg_len;
+    out->warmup_chunks = p.W;
+    out->warmup_eps = p.eps;
+    out->v_tiles = (int32_t)(desc->V / 64);
+    out->max_len = p.max_len;
+    out->total_chunks = p.total_chunks;
+    out->total_segments = p.total_segs;
+    out->fwd_workspace_bytes = p.fwd_bytes;
+    out->bwd_workspace_bytes = p.bwd_bytes;
+    return GDN_OK;
+}
+
+gdn_status gdn_chunk_fwd_workspace_size(const gdn_desc* desc, size_t* bytes) {
+    if (!bytes) return GDN_ERR_INVALID_ARG;
+    Plan p;
+    const gdn_status s = make_plan(desc, p);
+    if (s != GDN_OK) return s;
+    *bytes = p.fwd_bytes;
+    return GDN_OK;
+}
+
+gdn_status gdn_chunk_fwd(const gdn_desc* desc, const void* q, const void* k, const void* v, const float* g,
+                         const float* beta, const float* initial_state, void* o, float* final_state,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+    Plan p;
+    gdn_status s = make_plan(desc, p);
+    if (s != GDN_OK) return s;
+    if (p.Ttot > 0 && (!q || !k || !v || !g || !beta || !o)) return GDN_ERR_INVALID_ARG;
+    if ((s = check_ws(p, p.fwd_bytes, workspace, workspace_bytes)) != GDN_OK) return s;
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    unsigned char* ws = static_cast<unsigned char*>(workspace);
+    float* gam = reinterpret_cast<float*>(ws + p.o_gam);
+    void* w = ws + p.o_w;
+    void* u = ws + p.o_u;
+    if ((s = run_intra(desc, p, ws, k, v, g, beta, gam, w, u, st)) != GDN_OK) return s;
+
+    RecurArgs ra;
+    memset(&ra, 0, sizeof(ra));
+    ra.geo = make_geo(desc, p, ws);
+    ra.q = q;
+    ra.k = k;
+    ra.gam = gam;
+    ra.w = w;
+    ra.u = u;
+    ra.s0 = initial_state;
+    ra.o = o;
+    ra.sT = final_state;
+    ra.scale = desc->scale;
+    ra.warmup = p.W;
+    ra.use_cp = p.cp_on;
+    int32_t* modes = reinterpret_cast<int32_t*>(ws + p.o_modes);
+    ra.modes = modes;
+    if (p.cp_on) {
+        float* seginit = reinterpret_cast<float*>(ws + p.o_seginit);
+        float* prep = reinterpret_cast<float*>(ws + p.o_prep);
+        if ((s = run_decide(desc, p, ws, modes, st)) != GDN_OK) return s;
+        ra.seginit_out = seginit;
+        ra.prep = prep;
+        GDN_TRY_HIP(launch_recur(ra, desc->dtype, kRecurPrepass, p.total_segs,
+                                 (int)((desc->V + desc->K) / 64), st));
+        ScanArgs sa;
+        sa.geo = ra.geo;
+        sa.s0 = initial_state;
+        sa.prep = prep;
+        sa.seginit = seginit;
+        sa.modes = modes;
+        GDN_TRY_HIP(launch_scan(sa, desc->dtype, st));
+        ra.seginit = seginit;
+    }
+    GDN_TRY_HIP(launch_recur(ra, desc->dtype, kRecurOut, p.total_segs, (int)(desc->V / 64), st));
+    return GDN_OK;
+}
+
+gdn_status gdn_chunk_bwd_workspace_size(const gdn_desc* desc, size_t* bytes) {
+    if (!bytes) return GDN_ERR_INVALID_ARG;
+    Plan p;
+    const gdn_status s = make_plan(desc, p);
+    if (s != GDN_OK) return s;
+    *bytes = p.bwd_bytes;
+    return GDN_ERR_UNSUPPORTED;
+}
+
+gdn_status gdn_chunk_bwd(const gdn_desc* desc, const void* q, const void* k, const void* v, const float* g,
+                         const float* beta, const float* initial_state, const void* d_o,
+                         const float* d_final_state, void* dq, void* dk, void* dv, float* dg, float* dbeta,
+                         float* d_initial_state, void* workspace, size_t workspace_bytes, void* stream) {
+    (void)desc; (void)q; (void)k; (void)v; (void)g; (void)beta; (void)initial_state; (void)d_o;
+    (void)d_final_state; (void)dq; (void)dk; (void)dv; (void)dg; (void)dbeta; (void)d_initial_state;
+    (void)workspace; (void)workspace_bytes; (void)stream;
+    return GDN_ERR_UNSUPPORTED;
+}
+
+gdn_status gdn_intra_chunk(const gdn_desc* desc, const void* k, const void* v, const float* g,
+                           const float* beta, float* gam_out, void* w_out, void* u_out, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+    Plan p;
+    gdn_status s = make_plan(desc, p);
+    if (s != GDN_OK) return s;
+    if (p.Ttot > 0 && (!k || !v || !g || !beta || !gam_out || !w_out || !u_out)) return GDN_ERR_INVALID_ARG;
+    if ((s = check_ws(p, p.fwd_bytes, workspace, workspace_bytes)) != GDN_OK) return s;
+    unsigned char* ws = static_cast<unsigned char*>(workspace);
+    return run_intra(desc, p, ws, k, v, g, beta, gam_out, w_out, u_out, reinterpret_cast<hipStream_t>(stream));
+}
+
+gdn_status gdn_cp_modes(const gdn_desc* desc, const void* k, const void* v, const float* g, const float* beta,
+                        int32_t* modes_out, void* workspace, size_t workspace_bytes, void* stream) {
+    Plan p;
+    gdn_status s = make_plan(desc, p);
+    if (s != GDN_OK) return s;
+    if (!modes_out || (p.Ttot > 0 && (!k || !v || !g || !beta))) return GDN_ERR_INVALID_ARG;
+    if ((s = check_ws(p, p.fwd_bytes, workspace, workspace_bytes)) != GDN_OK) return s;
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    unsigned char* ws = static_cast<unsigned char*>(workspace);
+    if ((s = run_intra(desc, p, ws, k, v, g, beta, reinterpret_cast<float*>(ws + p.o_gam), ws + p.o_w,
+                       ws + p.o_u, st)) != GDN_OK)
+        return s;
+    return run_decide(desc, p, ws, modes_out, st);
+}
+
+}  // extern "C"

@@ -1,0 +1,234 @@
+// gdn_common.h -- device helpers shared by the libgdn HIP kernels (gfx950 only).
+//
+// Matrix-core convention used everywhere (16x16 output tiles, 64-lane waves):
+//   lane l, ln = l & 15, gq = l >> 4.
+//   Accumulator (f32x4) of a 16x16 tile C: lane l holds C[gq*4 + i][ln], i = 0..3.
+//   A k32 "fragment" is what one lane feeds for a 32-wide slice of the
+//   contraction: 8 values, slots e = 0..7, where slot e of lane group gq is
+//   the logical index  kappa(gq, e) = (e >> 2) * 16 + gq * 4 + (e & 3).
+//   An A fragment of row m = ln holds A[m][k0 + kappa]; a B fragment of
+//   column n = ln holds B[k0 + kappa][n]. Because A and B use the same slot
+//   map, the product sums over every k of the slice exactly once, whatever
+//   order the hardware walks the slots in.
+//   Two consequences make the recurrence cheap:
+//     * two accumulator tiles of X (rows k0..k0+15 and k0+16..k0+31) are, lane
+//       for lane, a B fragment of X;
+//     * two accumulator tiles of X^T are an A fragment of X.
+//   bf16 fragments go through one v_mfma_f32_16x16x32_bf16; fp32 fragments
+//   through eight v_mfma_f32_16x16x4_f32 (lane group gq feeds k = gq of each).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdn {
+
+typedef uint16_t bf16_t;  // raw bfloat16 bits
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+
+constexpr int kChunk = 64;   // tokens per chunk (one wave64 lane per token in scans)
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float bf2f(bf16_t x) { return __uint_as_float((uint32_t)x << 16); }
+
+// fp32 -> bf16, round to nearest even (inputs are finite).
+__device__ __forceinline__ uint32_t f2bf_bits(float f) {
+    uint32_t u = __float_as_uint(f);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+__device__ __forceinline__ bf16_t f2bf(float f) { return (bf16_t)f2bf_bits(f); }
+__device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
+    return f2bf_bits(lo) | (f2bf_bits(hi) << 16);
+}
+
+__device__ __forceinline__ float fast_exp(float x) { return __expf(x); }
+
+// ---------------------------------------------------------------------------
+// Element traits: storage type T in memory (bf16_t or float).
+template <typename T> struct Elem;
+template <> struct Elem<bf16_t> {
+    static constexpr int kVec = 8;  // elements per 16-byte vector
+    __device__ static float to_f(bf16_t x) { return bf2f(x); }
+    __device__ static bf16_t from_f(float f) { return f2bf(f); }
+};
+template <> struct Elem<float> {
+    static constexpr int kVec = 4;
+    __device__ static float to_f(float x) { return x; }
+    __device__ static float from_f(float f) { return f; }
+};
+
+// ---------------------------------------------------------------------------
+// k32 fragments.
+template <typename T> struct Frag;
+template <> struct Frag<bf16_t> {
+    u32x4 v;  // slots (0,1) (2,3) (4,5) (6,7), low half = even slot
+};
+template <> struct Frag<float> {
+    f32x4 lo, hi;  // slots 0..3, 4..7
+};
+
+// Fragment of row `row` of a row-major matrix (leading dimension ld elements)
+// over columns k0 .. k0+31: slot kappa -> column k0 + kappa.
+__device__ __forceinline__ void frag_row(Frag<bf16_t>& f, const bf16_t* base, int ld, int row, int k0) {
+    const int gq = threadIdx.x >> 4 & 3;
+    const bf16_t* p = base + (size_t)row * ld + k0 + gq * 4;
+    const u32x2 a = *reinterpret_cast<const u32x2*>(p);
+    const u32x2 b = *reinterpret_cast<const u32x2*>(p + 16);
+    f.v = u32x4{a.x, a.y, b.x, b.y};
+}
+__device__ __forceinline__ void frag_row(Frag<float>& f, const float* base, int ld, int row, int k0) {
+    const int gq = threadIdx.x >> 4 & 3;
+    const float* p = base + (size_t)row * ld + k0 + gq * 4;
+    f.lo = *reinterpret_cast<const f32x4*>(p);
+    f.hi = *reinterpret_cast<const f32x4*>(p + 16);
+}
+
+// Fragment of column `col` of a row-major matrix over rows k0 .. k0+31
+// (slot kappa -> row k0 + kappa): strided scalar reads.
+template <typename T>
+__device__ __forceinline__ void frag_col(Frag<T>& f, const T* base, int ld, int col, int k0);
+template <>
+__device__ __forceinline__ void frag_col(Frag<bf16_t>& f, const bf16_t* base, int ld, int col, int k0) {
+    const int gq = threadIdx.x >> 4 & 3;
+    const bf16_t* p = base + (size_t)(k0 + gq * 4) * ld + col;
+    uint32_t s[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s[e] = p[(size_t)((e >> 2) * 16 + (e & 3)) * ld];
+    f.v = u32x4{s[0] | s[1] << 16, s[2] | s[3] << 16, s[4] | s[5] << 16, s[6] | s[7] << 16};
+}
+template <>
+__device__ __forceinline__ void frag_col(Frag<float>& f, const float* base, int ld, int col, int k0) {
+    const int gq = threadIdx.x >> 4 & 3;
+    const float* p = base + (size_t)(k0 + gq * 4) * ld + col;
+    f.lo = f32x4{p[0], p[(size_t)ld], p[(size_t)2 * ld], p[(size_t)3 * ld]};
+    f.hi = f32x4{p[(size_t)16 * ld], p[(size_t)17 * ld], p[(size_t)18 * ld], p[(size_t)19 * ld]};
+}
+
+// Fragment from two fp32 accumulator tiles (rows k0..k0+15 and k0+16..k0+31 of X),
+// each element multiplied by s; as a B fragment of X, or an A fragment of X^T.
+__device__ __forceinline__ void frag_acc(Frag<bf16_t>& f, const f32x4& t0, const f32x4& t1, float s = 1.f) {
+    f.v = u32x4{pack_bf2(t0.x * s, t0.y * s), pack_bf2(t0.z * s, t0.w * s),
+                pack_bf2(t1.x * s, t1.y * s), pack_bf2(t1.z * s, t1.w * s)};
+}
+__device__ __forceinline__ void frag_acc(Frag<float>& f, const f32x4& t0, const f32x4& t1, float s = 1.f) {
+    f.lo = t0 * s;
+    f.hi = t1 * s;
+}
+// Same, with a per-slot scale (row-dependent factors r0 for tile 0, r1 for tile 1).
+__device__ __forceinline__ void frag_acc_rows(Frag<bf16_t>& f, const f32x4& t0, const f32x4& t1,
+                                              const f32x4& r0, const f32x4& r1) {
+    f.v = u32x4{pack_bf2(t0.x * r0.x, t0.y * r0.y), pack_bf2(t0.z * r0.z, t0.w * r0.w),
+                pack_bf2(t1.x * r1.x, t1.y * r1.y), pack_bf2(t1.z * r1.z, t1.w * r1.w)};
+}
+__device__ __forceinline__ void frag_acc_rows(Frag<float>& f, const f32x4& t0, const f32x4& t1,
+                                              const f32x4& r0, const f32x4& r1) {
+    f.lo = t0 * r0;
+    f.hi = t1 * r1;
+}
+
+// C += A * B over one k32 slice.
+__device__ __forceinline__ void mma(f32x4& c, const Frag<bf16_t>& a, const Frag<bf16_t>& b) {
+    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a.v),
+                                                __builtin_bit_cast(bf16x8_t, b.v), c, 0, 0, 0);
+}
+__device__ __forceinline__ void mma(f32x4& c, const Frag<float>& a, const Frag<float>& b) {
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.lo.x, b.lo.x, c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.lo.y, b.lo.y, c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.lo.z, b.lo.z, c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.lo.w, b.lo.w, c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.hi.x, b.hi.x, c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.hi.y, b.hi.y, c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.hi.z, b.hi.z, c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.hi.w, b.hi.w, c, 0, 0, 0);
+}
+
+// fp32 16x16x16 product helpers for the triangular inverse (k16 slices).
+// A value of lane (ln, gq) at step s is A[ln][4*gq + s]; B value is B[4*gq + s][ln].
+__device__ __forceinline__ void mma_f32_k16(f32x4& c, const f32x4& a, const f32x4& b) {
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.x, b.x, c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.y, b.y, c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.z, b.z, c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.w, b.w, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+// Four consecutive elements from an accumulator (one vector store: 8 B bf16, 16 B fp32).
+__device__ __forceinline__ void store4(bf16_t* p, const f32x4& x) {
+    *reinterpret_cast<u32x2*>(p) = u32x2{pack_bf2(x.x, x.y), pack_bf2(x.z, x.w)};
+}
+__device__ __forceinline__ void store4(float* p, const f32x4& x) { *reinterpret_cast<f32x4*>(p) = x; }
+
+// ---------------------------------------------------------------------------
+// Sequence / chunk bookkeeping shared by the kernels.
+struct SeqInfo {
+    int64_t bos;   // first token (flattened over batch)
+    int32_t len;   // tokens
+    int32_t nchunks;
+};
+
+// ---------------------------------------------------------------------------
+// LDS staging (256-thread workgroups).
+// Copy `rows` (<= 64) rows of a [.., H, D] tensor for head h into LDS, row-major and/or
+// transposed; rows beyond `rows` are zero.
+template <typename T, int D, bool kRowMajor, bool kTrans = true>
+__device__ __forceinline__ void stage_rows(const T* __restrict__ src, int64_t t0, int64_t H, int h,
+                                           int rows, T* rm, int ldr, T* tr, int ldt) {
+    constexpr int VEC = Elem<T>::kVec;
+    constexpr int NV = D / VEC;          // vectors per row
+    constexpr int UNITS = 32 * NV;       // (row pair, vector)
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int it = 0; it < UNITS / 256; ++it) {
+        const int u = tid + it * 256;
+        const int cv = u % NV;
+        const int rp = u / NV;
+        const int r0 = 2 * rp, r1 = 2 * rp + 1;
+        u32x4 a = u32x4{0u, 0u, 0u, 0u}, b = u32x4{0u, 0u, 0u, 0u};
+        if (r0 < rows) a = *reinterpret_cast<const u32x4*>(src + ((t0 + r0) * H + h) * D + cv * VEC);
+        if (r1 < rows) b = *reinterpret_cast<const u32x4*>(src + ((t0 + r1) * H + h) * D + cv * VEC);
+        if (kRowMajor) {
+            *reinterpret_cast<u32x4*>(rm + r0 * ldr + cv * VEC) = a;
+            *reinterpret_cast<u32x4*>(rm + r1 * ldr + cv * VEC) = b;
+        }
+        if constexpr (!kTrans) {
+        } else if constexpr (sizeof(T) == 2) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const uint32_t lo = (a[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu;
+                const uint32_t hi = (b[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu;
+                *reinterpret_cast<uint32_t*>(tr + (cv * VEC + e) * ldt + r0) = lo | (hi << 16);
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                *reinterpret_cast<u32x2*>(tr + (cv * VEC + e) * ldt + r0) = u32x2{a[e], b[e]};
+        }
+    }
+}
+
+// Store a [64][D] row-major LDS tile (rows < rows) to a [.., H, D] tensor.
+template <typename T, int D>
+__device__ __forceinline__ void store_rows(T* __restrict__ dst, int64_t t0, int64_t H, int h, int rows,
+                                           const T* sm, int ld) {
+    constexpr int VEC = Elem<T>::kVec;
+    constexpr int NV = D / VEC;
+    constexpr int UNITS = 64 * NV;
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int it = 0; it < UNITS / 256; ++it) {
+        const int u = tid + it * 256;
+        const int cv = u % NV;
+        const int r = u / NV;
+        if (r < rows)
+            *reinterpret_cast<u32x4*>(dst + ((t0 + r) * H + h) * D + cv * VEC) =
+                *reinterpret_cast<const u32x4*>(sm + r * ld + cv * VEC);
+    }
+}
+
+}  // namespace gdn

@@ -1,0 +1,299 @@
+// gdn_intra.hip -- first fused forward kernel: gate cumsum + intra-chunk WY factors.
+//
+// The FlashQLA pages split the GDN chunked prefill into two fused kernels with a
+// context-parallel preprocessing step between them (ollai.cn article, "technical
+// principles", last item; "core advantages", first item) and round-trip the
+// "intermediate variables" through HBM. This kernel is the first of the two. For one
+// chunk of c <= 64 tokens of one head it computes
+//   gam_r = sum_{j<=r} g_j                         (gate preprocessing: chunk-local cumsum)
+//   A     = strict_lower(diag(beta) (exp(gam_r - gam_j) k_r . k_j))
+//   T     = (I + A)^{-1}                          (unit lower triangular, always invertible)
+//   w     = T diag(beta exp(gam)) K,    u = T diag(beta) V
+// and per-chunk statistics for the CP decision: the chunk's gate total and the largest
+// beta_r |k_r|^2. The algebra follows from the gated delta rule
+// S_t = exp(g_t) S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T: inside a chunk the
+// per-token corrections delta_r = beta_r (v_r - S'_r k_r) solve (I + A) Delta = U - W S^T.
+//
+// One workgroup (4 waves) per (chunk, head). K is staged twice in LDS: row-major for
+// the Gram matrix and transposed for T*K; V only transposed. The inverse is blocked:
+// 16x16 diagonal blocks by forward substitution, then off-diagonal blocks level by
+// level with fp32 matrix-core products. T stays fp32; the products T*K and T*V run on
+// the matrix cores in the input precision with fp32 accumulation.
+#include "gdn_common.h"
+#include "gdn_kernels.h"
+
+namespace gdn {
+
+namespace {
+
+constexpr int kThreads = 256;
+
+template <typename T> struct IntraPad;
+template <> struct IntraPad<bf16_t> { static constexpr int row = 8, tr = 8; };
+template <> struct IntraPad<float> { static constexpr int row = 4, tr = 4; };
+
+constexpr int kLdA = 68;  // fp32 [64][68] for A and T
+
+template <typename T, int K, int V>
+struct IntraSmem {
+    static constexpr int LDR = K + IntraPad<T>::row;   // row-major K
+    static constexpr int LDT = 64 + IntraPad<T>::tr;   // transposed K / V
+    static constexpr int kKrmBytes = 64 * LDR * (int)sizeof(T);
+    static constexpr int kTBytes = 64 * kLdA * 4;
+    static constexpr int kUnionBytes = kKrmBytes > kTBytes ? kKrmBytes : kTBytes;
+    static constexpr int kKtBytes = K * LDT * (int)sizeof(T);
+    static constexpr int kVtBytes = V * LDT * (int)sizeof(T);
+    static constexpr int kABytes = 64 * kLdA * 4;
+    static constexpr int off_union = 0;
+    static constexpr int off_kt = off_union + kUnionBytes;
+    static constexpr int off_vt = off_kt + kKtBytes;
+    static constexpr int off_a = off_vt + kVtBytes;
+    static constexpr int off_gam = off_a + kABytes;
+    static constexpr int off_beta = off_gam + 256;
+    static constexpr int off_kk = off_beta + 256;
+    static constexpr int total = off_kk + 256;
+    // Output staging reuses the transposed regions: W as [64][K+pad], U as [64][V+pad].
+    static constexpr int LDO_K = K + IntraPad<T>::row;
+    static constexpr int LDO_V = V + IntraPad<T>::row;
+    static_assert(64 * LDO_K * (int)sizeof(T) <= kKtBytes, "W staging does not fit");
+    static_assert(64 * LDO_V * (int)sizeof(T) <= kVtBytes, "U staging does not fit");
+};
+
+// Gram tiles (row tile >= column tile) of a 64x64 lower triangle.
+__constant__ int8_t kTri[10][2] = {{0, 0}, {1, 0}, {1, 1}, {2, 0}, {2, 1}, {2, 2},
+                                   {3, 0}, {3, 1}, {3, 2}, {3, 3}};
+
+// Y = sum_{m=j}^{i-1} A_{i,m} T_{m,j}; T_{i,j} = -T_{i,i} Y   (16x16 blocks, fp32 matrix cores)
+__device__ __forceinline__ void tri_offdiag_block(float* sA, float* sT, int i, int j) {
+    const int lane = threadIdx.x & 63;
+    const int ln = lane & 15, gq = lane >> 4;
+    f32x4 y = zero4();
+    for (int m = j; m < i; ++m) {
+        const f32x4 a = *reinterpret_cast<const f32x4*>(sA + (16 * i + ln) * kLdA + 16 * m + 4 * gq);
+        f32x4 b;
+        b.x = sT[(16 * m + 4 * gq + 0) * kLdA + 16 * j + ln];
+        b.y = sT[(16 * m + 4 * gq + 1) * kLdA + 16 * j + ln];
+        b.z = sT[(16 * m + 4 * gq + 2) * kLdA + 16 * j + ln];
+        b.w = sT[(16 * m + 4 * gq + 3) * kLdA + 16 * j + ln];
+        mma_f32_k16(y, a, b);
+    }
+    // y[s] = Y[4*gq + s][ln] is a B operand as is.
+    const f32x4 a = *reinterpret_cast<const f32x4*>(sT + (16 * i + ln) * kLdA + 16 * i + 4 * gq);
+    f32x4 r = zero4();
+    mma_f32_k16(r, a, y);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) sT[(16 * i + 4 * gq + s) * kLdA + 16 * j + ln] = -r[s];
+}
+
+template <typename T, int K, int V>
+__global__ __launch_bounds__(kThreads) void k_intra(IntraArgs args) {
+    using S = IntraSmem<T, K, V>;
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    T* sKrm = reinterpret_cast<T*>(smem + S::off_union);
+    float* sT = reinterpret_cast<float*>(smem + S::off_union);
+    T* sKt = reinterpret_cast<T*>(smem + S::off_kt);
+    T* sVt = reinterpret_cast<T*>(smem + S::off_vt);
+    float* sA = reinterpret_cast<float*>(smem + S::off_a);
+    float* sGam = reinterpret_cast<float*>(smem + S::off_gam);
+    float* sBeta = reinterpret_cast<float*>(smem + S::off_beta);
+    float* sKK = reinterpret_cast<float*>(smem + S::off_kk);
+
+    const Geo& geo = args.geo;
+    const int64_t gc = blockIdx.x;
+    const int h = blockIdx.y;
+    ChunkLoc L;
+    if (!locate_chunk(geo, gc, L)) return;
+    const int64_t H = geo.H;
+    const int c = L.c;
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6;
+    const int lane = tid & 63;
+    const int ln = lane & 15, gq = lane >> 4;
+
+    // ---- stage 1: operands into LDS, gate cumsum --------------------------------
+    stage_rows<T, K, true>(reinterpret_cast<const T*>(args.k), L.t0, H, h, c, sKrm, S::LDR, sKt, S::LDT);
+    stage_rows<T, V, false>(reinterpret_cast<const T*>(args.v), L.t0, H, h, c, nullptr, 0, sVt, S::LDT);
+    if (wave == 0) {
+        const bool in = lane < c;
+        float x = in ? args.g[(L.t0 + lane) * H + h] : 0.f;
+        const float b = in ? args.beta[(L.t0 + lane) * H + h] : 0.f;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const float y = __shfl_up(x, off, 64);
+            if (lane >= off) x += y;
+        }
+        sGam[lane] = x;   // rows past the chunk end carry the chunk total
+        sBeta[lane] = b;
+        if (in) args.gam[(L.t0 + lane) * H + h] = x;
+    }
+    __syncthreads();
+
+    // ---- stage 2: A = strict_lower(diag(beta) (D .* K K^T)) -----------------------
+    for (int idx = wave; idx < 10; idx += 4) {
+        const int ti = kTri[idx][0], tj = kTri[idx][1];
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int kb = 0; kb < K / 32; ++kb) {
+            Frag<T> a, b;
+            frag_row(a, sKrm, S::LDR, ti * 16 + ln, kb * 32);
+            frag_row(b, sKrm, S::LDR, tj * 16 + ln, kb * 32);
+            mma(acc, a, b);
+        }
+        const int j = tj * 16 + ln;
+        const float gj = sGam[j];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = ti * 16 + gq * 4 + i;
+            const float val = (j < r) ? sBeta[r] * fast_exp(sGam[r] - gj) * acc[i] : 0.f;
+            sA[r * kLdA + j] = val;
+            if (r == j) sKK[r] = sBeta[r] * acc[i];
+        }
+    }
+    __syncthreads();
+
+    // ---- stage 3: T = (I + A)^{-1} --------------------------------------------------
+    // 3a: diagonal blocks by forward substitution (wave b, lanes 0..15 = columns of block b)
+    if (gq == 0) {
+        const int b = wave;
+        const int col = ln;
+        float x[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            float s = (r == col) ? 1.f : 0.f;
+            const float* arow = sA + (16 * b + r) * kLdA + 16 * b;
+#pragma unroll
+            for (int j = 0; j < r; ++j) s -= arow[j] * x[j];
+            x[r] = s;
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sT[(16 * b + r) * kLdA + 16 * b + col] = x[r];
+    }
+    // zero the strictly upper blocks (read by the k32 slices of stage 4)
+    for (int e = tid; e < 6 * 256; e += kThreads) {
+        const int blk = e >> 8, off = e & 255;
+        const int bi = blk < 3 ? 0 : (blk < 5 ? 1 : 2);
+        const int bj = blk < 3 ? blk + 1 : (blk < 5 ? blk - 1 : 3);
+        sT[(16 * bi + (off >> 4)) * kLdA + 16 * bj + (off & 15)] = 0.f;
+    }
+    __syncthreads();
+    if (wave < 3) tri_offdiag_block(sA, sT, wave + 1, wave);
+    __syncthreads();
+    if (wave < 2) tri_offdiag_block(sA, sT, wave + 2, wave);
+    __syncthreads();
+    if (wave == 0) tri_offdiag_block(sA, sT, 3, 0);
+    if (wave == 1) {
+        // chunk statistics for the CP decision
+        float m = lane < c ? sKK[lane] : 0.f;
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+        if (lane == 0) args.cstat[gc * H + h] = make_float2(sGam[63], m);
+    }
+    __syncthreads();
+
+    // ---- stage 4: W = T diag(beta e^gam) K, U = T diag(beta) V ------------------------
+    const int rt = wave;
+    constexpr int NKB = 2;  // k32 slices over the 64 chunk rows
+    Frag<T> aw[NKB], au[NKB];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+        Frag<float> tf;
+        frag_row(tf, sT, kLdA, rt * 16 + ln, kb * 32);
+        float fw[8], fu[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int j = kb * 32 + (e >> 2) * 16 + gq * 4 + (e & 3);
+            const float tv = e < 4 ? tf.lo[e] : tf.hi[e - 4];
+            const float bj = sBeta[j];
+            fu[e] = tv * bj;
+            fw[e] = fu[e] * fast_exp(sGam[j]);
+        }
+        if constexpr (sizeof(T) == 2) {
+            aw[kb].v = u32x4{pack_bf2(fw[0], fw[1]), pack_bf2(fw[2], fw[3]), pack_bf2(fw[4], fw[5]),
+                             pack_bf2(fw[6], fw[7])};
+            au[kb].v = u32x4{pack_bf2(fu[0], fu[1]), pack_bf2(fu[2], fu[3]), pack_bf2(fu[4], fu[5]),
+                             pack_bf2(fu[6], fu[7])};
+        } else {
+            reinterpret_cast<Frag<float>&>(aw[kb]).lo = f32x4{fw[0], fw[1], fw[2], fw[3]};
+            reinterpret_cast<Frag<float>&>(aw[kb]).hi = f32x4{fw[4], fw[5], fw[6], fw[7]};
+            reinterpret_cast<Frag<float>&>(au[kb]).lo = f32x4{fu[0], fu[1], fu[2], fu[3]};
+            reinterpret_cast<Frag<float>&>(au[kb]).hi = f32x4{fu[4], fu[5], fu[6], fu[7]};
+        }
+    }
+    const int nkb = (rt >> 1) + 1;  // T[r][j] = 0 for j > r
+    // Transposed tiles: with A = rows of K^T (V^T) and B = the scaled rows of T, accw[ct]
+    // holds W^T[ct*16 + gq*4 + i][rt*16 + ln], i.e. four consecutive columns of row
+    // rt*16 + ln, which each lane stages with one vector store.
+    f32x4 accw[K / 16], accu[V / 16];
+#pragma unroll
+    for (int ct = 0; ct < K / 16; ++ct) {
+        accw[ct] = zero4();
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+            if (kb < nkb) {
+                Frag<T> b;
+                frag_row(b, sKt, S::LDT, ct * 16 + ln, kb * 32);
+                mma(accw[ct], b, aw[kb]);
+            }
+        }
+    }
+#pragma unroll
+    for (int ct = 0; ct < V / 16; ++ct) {
+        accu[ct] = zero4();
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+            if (kb < nkb) {
+                Frag<T> b;
+                frag_row(b, sVt, S::LDT, ct * 16 + ln, kb * 32);
+                mma(accu[ct], b, au[kb]);
+            }
+        }
+    }
+    __syncthreads();
+    T* sWo = sKt;
+    T* sUo = sVt;
+    const int orow = rt * 16 + ln;
+#pragma unroll
+    for (int ct = 0; ct < K / 16; ++ct) store4(sWo + orow * S::LDO_K + ct * 16 + gq * 4, accw[ct]);
+#pragma unroll
+    for (int ct = 0; ct < V / 16; ++ct) store4(sUo + orow * S::LDO_V + ct * 16 + gq * 4, accu[ct]);
+    __syncthreads();
+    store_rows<T, K>(reinterpret_cast<T*>(args.w), L.t0, H, h, c, sWo, S::LDO_K);
+    store_rows<T, V>(reinterpret_cast<T*>(args.u), L.t0, H, h, c, sUo, S::LDO_V);
+}
+
+template <typename T, int K, int V>
+hipError_t launch_intra_t(const IntraArgs& a, hipStream_t st) {
+    using S = IntraSmem<T, K, V>;
+    static_assert(S::total <= 160 * 1024, "LDS budget");
+    auto kern = k_intra<T, K, V>;
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, S::total);
+    if (e != hipSuccess) return e;
+    dim3 grid((unsigned)a.geo.total_chunks, (unsigned)a.geo.H);
+    hipLaunchKernelGGL(kern, grid, dim3(kThreads), S::total, st, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_intra(const IntraArgs& a, int dtype, hipStream_t st) {
+    if (a.geo.total_chunks == 0) return hipSuccess;
+    const int K = a.geo.K, V = a.geo.V;
+#define GDN_INTRA_CASE(TT, KK, VV) \
+    if (K == KK && V == VV) return launch_intra_t<TT, KK, VV>(a, st);
+    if (dtype == 0) {
+        GDN_INTRA_CASE(bf16_t, 64, 64)
+        GDN_INTRA_CASE(bf16_t, 64, 128)
+        GDN_INTRA_CASE(bf16_t, 128, 64)
+        GDN_INTRA_CASE(bf16_t, 128, 128)
+    } else {
+        GDN_INTRA_CASE(float, 64, 64)
+        GDN_INTRA_CASE(float, 64, 128)
+        GDN_INTRA_CASE(float, 128, 64)
+        GDN_INTRA_CASE(float, 128, 128)
+    }
+#undef GDN_INTRA_CASE
+    return hipErrorInvalidValue;
+}
+
+}  // namespace gdn

@@ -1,0 +1,186 @@
+// gdn_kernels.h -- argument blocks and launchers of the libgdn kernels.
+// Host and device code both include this file; nothing here is part of the C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdn {
+
+// Where sequences, chunks and sub-sequences ("segments") live.
+// Uniform batches (varlen == 0) compute everything from T; packed batches
+// read the tables built on the device from cu_seqlens.
+struct Geo {
+    int32_t N, H, K, V;
+    int64_t T;            // tokens per batch row (uniform) / packed total (varlen)
+    int32_t varlen;
+    int32_t nt;           // chunks per sequence (uniform)
+    int32_t seg_len;      // chunks per segment
+    int32_t nseg;         // segments per sequence (uniform)
+    int64_t total_chunks;
+    int64_t total_segs;
+    const int64_t* seq_bos;     // [N]   (varlen)
+    const int32_t* seq_len;     // [N]
+    const int32_t* seq_choff;   // [N+1] first global chunk of each sequence
+    const int32_t* seq_segoff;  // [N+1] first global segment of each sequence
+    const int2* chunk_tab;      // [total_chunks] (n, chunk index in sequence); n < 0: unused
+    const int4* seg_tab;        // [total_segs]   (n, s, c0, c1); n < 0: unused
+};
+
+struct ChunkLoc {
+    int32_t n;        // sequence
+    int32_t j;        // chunk index in the sequence
+    int64_t t0;       // first token (flattened)
+    int32_t c;        // tokens in this chunk (1..64)
+};
+
+__device__ __forceinline__ bool locate_chunk(const Geo& g, int64_t gc, ChunkLoc& L) {
+    if (g.varlen) {
+        const int2 e = g.chunk_tab[gc];
+        if (e.x < 0) return false;
+        L.n = e.x;
+        L.j = e.y;
+        const int32_t len = g.seq_len[e.x];
+        L.t0 = g.seq_bos[e.x] + (int64_t)e.y * 64;
+        L.c = min(64, len - e.y * 64);
+    } else {
+        L.n = (int32_t)(gc / g.nt);
+        L.j = (int32_t)(gc % g.nt);
+        L.t0 = (int64_t)L.n * g.T + (int64_t)L.j * 64;
+        L.c = (int32_t)min((int64_t)64, g.T - (int64_t)L.j * 64);
+    }
+    return L.c > 0;
+}
+
+struct SegLoc {
+    int32_t n, s, c0, c1;  // sequence, segment index, chunk range [c0, c1) in the sequence
+    int32_t nseg;          // segments of this sequence
+    int32_t nchunks;       // chunks of this sequence
+    int64_t bos;
+    int32_t len;
+    int64_t choff;         // global index of the sequence's first chunk
+};
+
+__device__ __forceinline__ bool locate_seg(const Geo& g, int64_t gs, SegLoc& S) {
+    if (g.varlen) {
+        const int4 e = g.seg_tab[gs];
+        if (e.x < 0) return false;
+        S.n = e.x;
+        S.s = e.y;
+        S.c0 = e.z;
+        S.c1 = e.w;
+        S.nseg = g.seq_segoff[e.x + 1] - g.seq_segoff[e.x];
+        S.bos = g.seq_bos[e.x];
+        S.len = g.seq_len[e.x];
+        S.nchunks = (S.len + 63) / 64;
+        S.choff = g.seq_choff[e.x];
+    } else {
+        S.n = (int32_t)(gs / g.nseg);
+        S.s = (int32_t)(gs % g.nseg);
+        S.c0 = S.s * g.seg_len;
+        S.c1 = min(S.c0 + g.seg_len, g.nt);
+        S.nseg = g.nseg;
+        S.bos = (int64_t)S.n * g.T;
+        S.len = (int32_t)g.T;
+        S.nchunks = g.nt;
+        S.choff = (int64_t)S.n * g.nt;
+    }
+    return true;
+}
+
+// Per sequence: segments count and the global index of segment 0.
+__device__ __forceinline__ void seq_segs(const Geo& g, int32_t n, int32_t& nseg, int64_t& segoff,
+                                         int32_t& nchunks, int64_t& choff) {
+    if (g.varlen) {
+        segoff = g.seq_segoff[n];
+        nseg = g.seq_segoff[n + 1] - g.seq_segoff[n];
+        nchunks = (g.seq_len[n] + 63) / 64;
+        choff = g.seq_choff[n];
+    } else {
+        segoff = (int64_t)n * g.nseg;
+        nseg = g.nseg;
+        nchunks = g.nt;
+        choff = (int64_t)n * g.nt;
+    }
+}
+
+// ---------------------------------------------------------------------------
+struct IntraArgs {
+    Geo geo;
+    const void* k;
+    const void* v;
+    const float* g;
+    const float* beta;
+    float* gam;      // [Ttot, H]
+    void* w;         // [Ttot, H, K]
+    void* u;         // [Ttot, H, V]
+    float2* cstat;   // [total_chunks, H]: (chunk gate total, max beta*|k|^2)
+};
+
+enum RecurMode : int {
+    kRecurOut = 0,      // outputs O (and the final state) for each segment
+    kRecurPrepass = 1,  // CP preprocessing: warmup windows and exact (R, M) segment maps
+    kRecurStates = 2    // chunk-entry states for the backward (h), no output
+};
+
+struct RecurArgs {
+    Geo geo;
+    const void* q;
+    const void* k;
+    const float* gam;
+    const void* w;
+    const void* u;
+    const float* s0;          // [N,H,V,K] or null
+    void* o;                  // [Ttot,H,V]
+    float* sT;                // [N,H,V,K] or null
+    const float* seginit;     // [total_segs,H,V,K] initial state of every segment (s >= 1)
+    float* seginit_out;       // prepass: warmup states written here
+    float* prep;              // prepass: [total_segs,H,V+K,K] exact maps (R rows, then M^T)
+    const int32_t* modes;     // [N,H] 0 none, 1 warmup, 2 exact
+    void* hstates;            // kRecurStates: [total_chunks,H,V,K] entry state of every chunk
+    float scale;
+    int32_t warmup;           // W chunks
+    int32_t use_cp;           // segments >= 1 read seginit
+};
+
+struct DecideArgs {
+    Geo geo;
+    const float2* cstat;
+    int32_t* modes;
+    int32_t warmup;
+    float log_eps;
+    int32_t forced;  // 0 gate test, 1 warmup, 2 exact
+};
+
+struct ScanArgs {
+    Geo geo;
+    const float* s0;
+    const float* prep;
+    float* seginit;
+    const int32_t* modes;
+};
+
+struct TableArgs {
+    const int32_t* cu;
+    int32_t N;
+    int64_t Ttot;
+    int32_t seg_len;
+    int64_t total_chunks;
+    int64_t total_segs;
+    int64_t* seq_bos;
+    int32_t* seq_len;
+    int32_t* seq_choff;
+    int32_t* seq_segoff;
+    int2* chunk_tab;
+    int4* seg_tab;
+};
+
+// Launchers (return hipGetLastError of the launch).
+hipError_t launch_tables(const TableArgs& a, hipStream_t st);
+hipError_t launch_intra(const IntraArgs& a, int dtype, hipStream_t st);
+hipError_t launch_decide(const DecideArgs& a, hipStream_t st);
+hipError_t launch_recur(const RecurArgs& a, int dtype, int mode, int64_t nsegs_grid, int vtiles,
+                        hipStream_t st);
+hipError_t launch_scan(const ScanArgs& a, int dtype, hipStream_t st);
+
+}  // namespace gdn

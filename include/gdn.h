@@ -1,0 +1,187 @@
+/*
+ * gdn.h -- C ABI of libgdn: Gated DeltaNet (GDN) chunked prefill, forward and
+ * backward, on one AMD Instinct MI355X (gfx950).
+ *
+ * The operation. The FlashQLA pages describe a linear-attention kernel library
+ * for the Gated Delta Network's chunked prefill (ollai.cn article, sections
+ * "what it is" and "main features"): it takes q, k, v, a gate g and a write
+ * strength beta, returns O and the final state, and accepts an optional
+ * initial state and packed variable-length sequences via cu_seqlens
+ * ("how to use"). It offers low-level forward / backward entry points
+ * ("main features", two-level API). The pages print no formula; this library
+ * computes the standard gated delta rule, per sequence and head,
+ *
+ *     S_t = exp(g_t) S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T
+ *     o_t = scale * S_t q_t
+ *
+ * S is V x K (row i over the value dimension, column j over the key
+ * dimension). The state enters as initial_state (zeros when NULL) and leaves
+ * as final_state. g is a natural-log decay (exp(g_t) multiplies the state).
+ * q and k are used as given (no normalisation inside).
+ *
+ * Layouts (all row-major, contiguous, device memory unless stated):
+ *   q, k, dq, dk        [B, T, H, K]   element type desc->dtype
+ *   v, o, d_o, dv       [B, T, H, V]   element type desc->dtype
+ *   g, beta, dg, dbeta  [B, T, H]      fp32
+ *   initial_state, final_state, d_final_state, d_initial_state
+ *                       [N, H, V, K]   fp32, N = number of sequences
+ *   With varlen (cu_seqlens != NULL) B must be 1, T is the packed token count
+ *   and sequence n owns tokens [cu_seqlens[n], cu_seqlens[n+1]).
+ *
+ * How it runs (the split the pages describe in "technical principles" and
+ * "core advantages"): a gate-cumsum + intra-chunk kernel writes the WY factors
+ * w and u, an optional intra-card context-parallel (CP) preprocessing step
+ * gives every sub-sequence its initial state, and an inter-chunk recurrence
+ * kernel produces O and the final state. CP turns on by itself for small
+ * batch x heads ("AutoCP": B*H <= 40, or B*H <= 56 with seq_len >= 8192) and
+ * picks per sequence-head either the exact correction or a sliding-window
+ * warmup of a few chunks where the gate decay makes the warmup exact within
+ * tolerance ("gate-driven" warmup, "core advantages").
+ *
+ * Ownership and errors: the caller allocates every buffer, including the
+ * workspace, whose size the *_workspace_size calls return. The library
+ * allocates no memory, keeps no pointer after a call returns, never
+ * synchronises the host with the device and never aborts. All work is
+ * enqueued on `stream` (a hipStream_t; NULL = the default stream). Outputs
+ * are overwritten, never accumulated, and must not alias inputs. Argument
+ * checks run on the host before any launch; a failed launch reports
+ * GDN_ERR_HIP. Results are deterministic (no atomics).
+ */
+#ifndef GDN_H_
+#define GDN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GDN_ABI_VERSION 1
+
+typedef enum gdn_status {
+    GDN_OK = 0,
+    GDN_ERR_INVALID_ARG = 1, /* null pointer, bad size, inconsistent cu_seqlens */
+    GDN_ERR_UNSUPPORTED = 2, /* K or V not in {64,128}, chunk != 64, fp32 with K=V=128 beyond LDS */
+    GDN_ERR_WORKSPACE = 3,   /* workspace NULL or smaller than required */
+    GDN_ERR_HIP = 4          /* a HIP call or kernel launch failed */
+} gdn_status;
+
+typedef enum gdn_dtype {
+    GDN_DTYPE_BF16 = 0, /* q,k,v,o and their gradients in bf16; fp32 accumulation and state */
+    GDN_DTYPE_FP32 = 1  /* everything fp32 */
+} gdn_dtype;
+
+typedef enum gdn_cp_mode {
+    GDN_CP_AUTO = 0,   /* shape rule decides; per sequence-head gate test picks warmup or exact */
+    GDN_CP_OFF = 1,    /* one serial pass per sequence-head */
+    GDN_CP_ON = 2,     /* CP regardless of the shape rule; per sequence-head gate test */
+    GDN_CP_EXACT = 3,  /* CP, exact correction for every sequence-head */
+    GDN_CP_WARMUP = 4  /* CP, warmup for every sequence-head (caller asserts fast decay) */
+} gdn_cp_mode;
+
+/* Problem descriptor. Zero-initialise, then fill. */
+typedef struct gdn_desc {
+    int64_t B, T, H, K, V;          /* batch, tokens per row (packed total if varlen), heads, key dim, value dim */
+    int32_t chunk;                  /* chunk length; must be 64 (0 = 64) */
+    int32_t dtype;                  /* gdn_dtype */
+    float scale;                    /* query scale applied to o (the rule above has none: pass 1.0) */
+    int32_t num_seqs;               /* varlen: N (>= 1); ignored otherwise */
+    const int32_t* cu_seqlens;      /* device [N+1] token offsets, or NULL (then N = B) */
+    const int32_t* cu_seqlens_host; /* host copy of cu_seqlens; required with it (planning needs no sync) */
+    int32_t cp_mode;                /* gdn_cp_mode */
+    int32_t warmup_chunks;          /* warmup window in chunks, 1..16 (0 = 8) */
+    int32_t seg_chunks;             /* CP sub-sequence length in chunks (0 = chosen from the CU count) */
+    float warmup_eps;               /* warmup acceptance: exp(window gate sum) <= eps (0 = 1e-4 bf16, 1e-6 fp32) */
+    int32_t num_cus;                /* compute units to plan for (0 = query the current device) */
+    int32_t reserved[7];            /* must be zero */
+} gdn_desc;
+
+/* Host-side plan of a call (filled by gdn_plan; no device work). */
+typedef struct gdn_plan_info {
+    int32_t num_seqs;               /* N */
+    int32_t cp_on;                  /* 1 if the call splits sequences into sub-sequences */
+    int32_t seg_chunks;             /* chunks per sub-sequence (the last one may be shorter) */
+    int32_t warmup_chunks;          /* warmup window W in chunks */
+    float warmup_eps;               /* warmup acceptance threshold */
+    int32_t v_tiles;                /* value-row tiles per sequence-head in the recurrence kernel */
+    int64_t max_len;                /* longest sequence, tokens */
+    int64_t total_chunks;           /* sum over sequences of ceil(len / 64) */
+    int64_t total_segments;         /* sum over sequences of sub-sequence counts */
+    size_t fwd_workspace_bytes;
+    size_t bwd_workspace_bytes;
+} gdn_plan_info;
+
+/* ABI version (GDN_ABI_VERSION of the built library). */
+int gdn_abi_version(void);
+
+/* Static English text for a status code; never NULL. */
+const char* gdn_status_string(gdn_status status);
+
+/* Validate `desc` and fill `out` with the plan the calls below would use:
+ * whether CP is on (the pages' AutoCP rule, "core advantages"), sub-sequence
+ * length, warmup window and workspace sizes. Host only: reads
+ * cu_seqlens_host, never cu_seqlens; queries the device CU count only when
+ * desc->num_cus == 0. */
+gdn_status gdn_plan(const gdn_desc* desc, gdn_plan_info* out);
+
+/* Workspace bytes that gdn_chunk_fwd needs for `desc`. */
+gdn_status gdn_chunk_fwd_workspace_size(const gdn_desc* desc, size_t* bytes);
+
+/* Forward (the pages' low-level fwd entry, "main features"): O and the final
+ * state of the gated delta rule above.
+ *   q, k, v, g, beta : inputs (layouts above)
+ *   initial_state    : [N,H,V,K] fp32 or NULL (zeros)
+ *   o                : output [B,T,H,V]
+ *   final_state      : output [N,H,V,K] fp32, or NULL (not written)
+ *   workspace        : device scratch of at least gdn_chunk_fwd_workspace_size bytes, 256-byte aligned
+ *   stream           : hipStream_t (NULL = default stream)
+ * Returns GDN_OK once all work is enqueued. */
+gdn_status gdn_chunk_fwd(const gdn_desc* desc, const void* q, const void* k, const void* v,
+                         const float* g, const float* beta, const float* initial_state,
+                         void* o, float* final_state,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes that gdn_chunk_bwd needs for `desc`. */
+gdn_status gdn_chunk_bwd_workspace_size(const gdn_desc* desc, size_t* bytes);
+
+/* Backward (the pages' low-level bwd entry): gradients of
+ * L = <d_o, O> + <d_final_state, final_state> with respect to every input.
+ *   q, k, v, g, beta, initial_state : the forward's inputs (initial_state may be NULL)
+ *   d_o             : [B,T,H,V] upstream gradient of O
+ *   d_final_state   : [N,H,V,K] fp32 upstream gradient of the final state, or NULL (zeros)
+ *   dq, dk, dv      : outputs, same layouts and dtype as q, k, v
+ *   dg, dbeta       : outputs [B,T,H] fp32 (dg is with respect to the raw per-token g)
+ *   d_initial_state : output [N,H,V,K] fp32, or NULL (not written)
+ * The forward is recomputed inside; nothing from gdn_chunk_fwd is reused. */
+gdn_status gdn_chunk_bwd(const gdn_desc* desc, const void* q, const void* k, const void* v,
+                         const float* g, const float* beta, const float* initial_state,
+                         const void* d_o, const float* d_final_state,
+                         void* dq, void* dk, void* dv, float* dg, float* dbeta,
+                         float* d_initial_state,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/* Intra-chunk step alone (the first fused kernel): chunk-local cumulative gate
+ * sum and the WY factors, for kernel-level checks. With gam the chunk-local
+ * cumsum of g, A = strict_lower(diag(beta) (exp(gam_r - gam_j) k_r.k_j)) and
+ * T = (I + A)^-1 per chunk:
+ *   gam_out [B,T,H] fp32; w_out = T diag(beta exp(gam)) K  [B,T,H,K];
+ *   u_out   = T diag(beta) V  [B,T,H,V]  (dtype desc->dtype).
+ * Uses the forward workspace. */
+gdn_status gdn_intra_chunk(const gdn_desc* desc, const void* k, const void* v,
+                           const float* g, const float* beta,
+                           float* gam_out, void* w_out, void* u_out,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/* CP decision per sequence-head, as the forward would take it:
+ * modes_out [N, H] int32 (device): 0 = no split needed, 1 = warmup, 2 = exact.
+ * Uses the forward workspace; runs the intra-chunk kernel to get the gates. */
+gdn_status gdn_cp_modes(const gdn_desc* desc, const void* k, const void* v,
+                        const float* g, const float* beta, int32_t* modes_out,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H_ */

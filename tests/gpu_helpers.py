@@ -1,0 +1,71 @@
+"""Shared helpers of the GPU parity tests: seeded inputs on the device and the
+oracle on the same bytes (upcast exactly to fp64 on the CPU)."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from oracle import ref_fwd, rel_l2  # noqa: F401
+
+BF16_TOL = 1e-2   # relative L2, bf16 inputs with fp32 accumulation
+FP32_TOL = 1e-4   # relative L2, fp32 mode
+
+
+def check(x, ref, tol, what=""):
+    """Relative L2 of a device tensor against an fp64 reference; short message on failure."""
+    err = rel_l2(x.detach().cpu() if hasattr(x, "detach") else x, ref)
+    assert err < tol, f"{what} rel_l2={err:.3e} > {tol:.1e}"
+    return err
+
+
+def tol_for(dtype):
+    return BF16_TOL if dtype == torch.bfloat16 else FP32_TOL
+
+
+def to_dev(inp: dict) -> dict:
+    out = {}
+    for k, v in inp.items():
+        out[k] = v.cuda() if isinstance(v, torch.Tensor) else v
+    return out
+
+
+def small_inputs(B=2, T=1000, H=2, K=128, V=128, dtype=torch.bfloat16, seed=0, init_std=0.1,
+                 lengths=None, decay=1.0):
+    """Inputs with the workloads' distributions at a size the oracle finishes quickly."""
+    gen = torch.Generator().manual_seed(seed)
+    if lengths is not None:
+        B, T = 1, int(sum(lengths))
+        cu = torch.tensor(np.concatenate([[0], np.cumsum(lengths)]), dtype=torch.int32)
+        N = len(lengths)
+    else:
+        cu = None
+        N = B
+    q = torch.randn((B, T, H, K), generator=gen)
+    q = (q / q.norm(dim=-1, keepdim=True)).to(dtype)
+    k = torch.randn((B, T, H, K), generator=gen)
+    k = (k / k.norm(dim=-1, keepdim=True)).to(dtype)
+    v = torch.randn((B, T, H, V), generator=gen).to(dtype)
+    beta = torch.sigmoid(torch.randn((B, T, H), generator=gen))
+    g = (-torch.nn.functional.softplus(torch.randn((B, T, H), generator=gen)) * 0.1 * decay).contiguous()
+    s0 = None if init_std is None else torch.randn((N, H, V, K), generator=gen) * init_std
+    return dict(q=q, k=k, v=v, g=g, beta=beta, initial_state=s0, cu_seqlens=cu)
+
+
+def oracle(inp, scale=1.0, heads=None, rows=None):
+    """Oracle forward on (optionally) a subset of heads and value rows."""
+    q, k, v, g, beta, s0 = (inp[x] for x in ("q", "k", "v", "g", "beta", "initial_state"))
+    if heads is not None:
+        q, k, v, g, beta = q[:, :, heads], k[:, :, heads], v[:, :, heads], g[:, :, heads], beta[:, :, heads]
+        s0 = None if s0 is None else s0[:, heads]
+    if rows is not None:
+        v = v[..., rows]
+        s0 = None if s0 is None else s0[:, :, rows]
+    return ref_fwd(q, k, v, g, beta, scale, s0, cu_seqlens=inp.get("cu_seqlens"))
+
+
+def gpu_fwd(dinp, **kw):
+    import gated_deltanet_chunked_04_amd as gdn
+    o, sT = gdn.gdn_chunk_fwd(dinp["q"], dinp["k"], dinp["v"], dinp["g"], dinp["beta"],
+                              dinp["initial_state"], cu_seqlens=dinp.get("cu_seqlens"), **kw)
+    torch.cuda.synchronize()
+    return o, sT

@@ -1,0 +1,156 @@
+"""The C ABI on the host (no GPU): the library loads, exports every entry point the
+header declares, plans as the AutoCP rule says and rejects bad arguments before
+touching the device.
+
+AutoCP rule (FlashQLA pages, ollai.cn article, "core advantages"): CP turns on
+when batch x heads <= 40, or batch x heads <= 56 with seq_len >= 8192.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import gated_deltanet_chunked_04_amd as gdn
+from gated_deltanet_chunked_04_amd import _abi
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _abi.load_library()
+
+
+def header_functions():
+    src = open(os.path.join(ROOT, "include", "gdn.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdn_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol(lib):
+    declared = header_functions()
+    assert set(declared) == set(_abi.EXPORTS)
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert lib.gdn_abi_version() == 1
+
+
+def test_status_strings(lib):
+    for s in range(5):
+        assert len(_abi.status_string(s)) > 0
+    assert _abi.status_string(99) == "unknown status"
+
+
+def desc(B=1, T=32768, H=16, K=128, V=128, dtype=torch.bfloat16, **kw):
+    kw.setdefault("num_cus", 256)
+    return gdn.Desc(B, T, H, K, V, dtype, **kw)
+
+
+def plan(**kw):
+    return gdn.gdn_plan(desc(**kw))
+
+
+@pytest.mark.parametrize("B,H,T,on", [
+    (1, 40, 100000, True), (1, 41, 100000, True), (1, 41, 8191, False), (1, 41, 8192, True),
+    (1, 56, 8192, True), (1, 57, 8192, False), (8, 5, 20000, True), (8, 6, 20000, True),
+    (8, 7, 20000, True), (8, 8, 20000, False), (2, 20, 4096, True), (1, 40, 4096, True),
+])
+def test_autocp_rule(B, H, T, on):
+    p = plan(B=B, H=H, T=T)
+    # CP only splits when a sequence is longer than one sub-sequence
+    rule = (B * H <= 40) or (B * H <= 56 and T >= 8192)
+    assert rule == on
+    if not rule:
+        assert p["cp_on"] == 0
+        assert p["total_segments"] == B
+    else:
+        nt = (T + 63) // 64
+        assert p["cp_on"] == int(nt > p["seg_chunks"])
+        if p["cp_on"]:
+            assert p["seg_chunks"] >= 16
+            assert p["total_segments"] == B * -(-nt // p["seg_chunks"])
+
+
+def test_workload_plans():
+    # batch-1 agentic prefill: 16 heads x 512 chunks -> CP on, 16 sub-sequences of 32 chunks
+    p = plan(B=1, H=16, T=32768)
+    assert p["cp_on"] == 1 and p["seg_chunks"] == 32 and p["total_segments"] == 16
+    # one TP8 shard of a 256K prompt
+    p = plan(B=1, H=8, T=262144)
+    assert p["cp_on"] == 1 and p["seg_chunks"] == 128 and p["total_segments"] == 32
+    # tiny case: CP by rule but a single sub-sequence
+    p = plan(B=1, H=2, T=256, K=64, V=64, dtype=torch.float32)
+    assert p["cp_on"] == 0 and p["total_chunks"] == 4
+    # forced modes always split long sequences, off never does
+    assert plan(B=4, H=32, T=32768, cp_mode="exact")["cp_on"] == 1
+    assert plan(B=1, H=1, T=32768, cp_mode="off")["cp_on"] == 0
+    assert plan(seg_chunks=100)["seg_chunks"] == 100
+    assert plan()["warmup_chunks"] == 8
+    assert plan(warmup_chunks=6)["warmup_chunks"] == 6
+
+
+def test_varlen_plan():
+    lens = [1000, 0, 64, 20000, 65]
+    cu = torch.tensor([0] + list(torch.tensor(lens).cumsum(0)), dtype=torch.int32)
+    d = gdn.Desc(1, int(cu[-1]), 4, 128, 128, torch.bfloat16, num_cus=256)
+    # varlen needs the device pointer too; build the struct by hand for a host-only plan
+    hc = cu.numpy().astype("int32")
+    d.c.num_seqs = len(lens)
+    d.c.cu_seqlens = 0x1000  # never dereferenced by the planner
+    d.c.cu_seqlens_host = hc.ctypes.data
+    p = gdn.gdn_plan(d)
+    assert p["num_seqs"] == 5
+    assert p["total_chunks"] == sum((n + 63) // 64 for n in lens)
+    assert p["max_len"] == 20000
+    assert p["cp_on"] == 1  # N*H = 20 <= 40
+    segs = sum(max(1, -(-((n + 63) // 64) // p["seg_chunks"])) for n in lens)
+    assert p["total_segments"] == segs
+
+
+def test_argument_errors(lib):
+    d = desc()
+    out = _abi.GdnPlanInfo()
+    bad = [("K", 96), ("V", 32), ("H", 0), ("B", 0), ("T", -1), ("chunk", 32), ("dtype", 7),
+           ("cp_mode", 9), ("warmup_chunks", 17), ("warmup_eps", 1.5)]
+    codes = {"K": 2, "V": 2, "chunk": 2}
+    for field, val in bad:
+        d2 = desc()
+        setattr(d2.c, field, val)
+        assert lib.gdn_plan(d2.ref, ctypes.byref(out)) == codes.get(field, 1), field
+    d2 = desc()
+    d2.c.reserved[3] = 1
+    assert lib.gdn_plan(d2.ref, ctypes.byref(out)) == 1
+    # varlen with B != 1, or without the host copy
+    d2 = desc(B=2)
+    d2.c.cu_seqlens = 0x1000
+    assert lib.gdn_plan(d2.ref, ctypes.byref(out)) == 1
+    d2 = desc()
+    d2.c.cu_seqlens = 0x1000
+    d2.c.num_seqs = 1
+    assert lib.gdn_plan(d2.ref, ctypes.byref(out)) == 1
+    # inconsistent host offsets
+    import numpy as np
+    hc = np.array([0, 10, 5, 32768], dtype=np.int32)
+    d2 = desc()
+    d2.c.cu_seqlens = 0x1000
+    d2.c.cu_seqlens_host = hc.ctypes.data
+    d2.c.num_seqs = 3
+    assert lib.gdn_plan(d2.ref, ctypes.byref(out)) == 1
+    assert lib.gdn_plan(None, ctypes.byref(out)) == 1
+
+
+def test_call_errors_before_launch(lib):
+    d = desc(T=256, H=2)
+    nb = ctypes.c_size_t()
+    assert lib.gdn_chunk_fwd_workspace_size(d.ref, ctypes.byref(nb)) == 0 and nb.value > 0
+    p = ctypes.c_void_p(0x1000)
+    # null inputs
+    assert lib.gdn_chunk_fwd(d.ref, None, p, p, p, p, None, p, None, p, nb, None) == 1
+    # missing / short / misaligned workspace
+    assert lib.gdn_chunk_fwd(d.ref, p, p, p, p, p, None, p, None, None, nb, None) == 3
+    assert lib.gdn_chunk_fwd(d.ref, p, p, p, p, p, None, p, None, p, ctypes.c_size_t(nb.value - 1), None) == 3
+    assert lib.gdn_chunk_fwd(d.ref, p, p, p, p, p, None, p, None, ctypes.c_void_p(0x1010), nb, None) == 3
+    assert lib.gdn_intra_chunk(d.ref, p, p, p, p, None, p, p, p, nb, None) == 1
+    assert lib.gdn_cp_modes(d.ref, p, p, p, p, None, p, nb, None) == 1
