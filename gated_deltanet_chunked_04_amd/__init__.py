@@ -21,10 +21,11 @@ import numpy as np
 import torch
 
 from ._abi import (CP_MODES, EXPORTS, GDN_DTYPE_BF16, GDN_DTYPE_FP32, GdnDesc, GdnError,  # noqa: F401
-                   GdnPlanInfo, check, load_library, status_string)
+                   GdnKernelTime, GdnPlanInfo, check, load_library, status_string)
 
 __all__ = ["gdn_plan", "gdn_chunk_fwd", "gdn_chunk_bwd", "gdn_intra_chunk", "gdn_cp_modes",
-           "chunk_gated_delta_rule", "load_library", "make_desc", "GdnError"]
+           "gdn_profile_enable", "gdn_profile_read", "chunk_gated_delta_rule", "load_library",
+           "make_desc", "GdnError"]
 
 
 def _ptr(t: Optional[torch.Tensor]):
@@ -210,6 +211,20 @@ def gdn_cp_modes(k, v, g, beta, *, cu_seqlens=None, cu_seqlens_host=None, cp_mod
     check(lib.gdn_cp_modes(desc.ref, _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(modes), _ptr(ws),
                            ctypes.c_size_t(ws.numel()), _stream()), "gdn_cp_modes")
     return modes
+
+
+def gdn_profile_enable(enable: bool = True) -> None:
+    """Bracket every kernel launch with HIP events (see gdn_profile_read)."""
+    check(load_library().gdn_profile_enable(int(bool(enable))), "gdn_profile_enable")
+
+
+def gdn_profile_read() -> dict:
+    """Wait for the recorded events; return {kernel: (launches, total_ms)} and clear the totals."""
+    buf = (GdnKernelTime * 32)()
+    n = load_library().gdn_profile_read(buf, 32)
+    if n < 0:
+        raise GdnError(4, "gdn_profile_read")
+    return {buf[i].name.decode(): (int(buf[i].launches), float(buf[i].total_ms)) for i in range(n)}
 
 
 class _GDNFunction(torch.autograd.Function):

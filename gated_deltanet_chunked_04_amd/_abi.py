@@ -19,7 +19,7 @@ CP_MODES = {"auto": 0, "off": 1, "on": 2, "exact": 3, "warmup": 4}
 # Declared entry points of include/gdn.h (checked by the ABI test).
 EXPORTS = ("gdn_abi_version", "gdn_status_string", "gdn_plan", "gdn_chunk_fwd_workspace_size",
            "gdn_chunk_fwd", "gdn_chunk_bwd_workspace_size", "gdn_chunk_bwd", "gdn_intra_chunk",
-           "gdn_cp_modes")
+           "gdn_cp_modes", "gdn_profile_enable", "gdn_profile_read")
 
 
 class GdnDesc(ctypes.Structure):
@@ -43,6 +43,10 @@ class GdnPlanInfo(ctypes.Structure):
         ("total_segments", ctypes.c_int64),
         ("fwd_workspace_bytes", ctypes.c_size_t), ("bwd_workspace_bytes", ctypes.c_size_t),
     ]
+
+
+class GdnKernelTime(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char * 32), ("launches", ctypes.c_int64), ("total_ms", ctypes.c_double)]
 
 
 _LIB = None
@@ -82,6 +86,10 @@ def load_library(path: str = LIB_PATH):
     lib.gdn_intra_chunk.argtypes = [dp] + [vp] * 7 + [vp, sz, vp]
     lib.gdn_cp_modes.restype = i32
     lib.gdn_cp_modes.argtypes = [dp] + [vp] * 5 + [vp, sz, vp]
+    lib.gdn_profile_enable.restype = i32
+    lib.gdn_profile_enable.argtypes = [i32]
+    lib.gdn_profile_read.restype = i32
+    lib.gdn_profile_read.argtypes = [ctypes.POINTER(GdnKernelTime), i32]
     _LIB = lib
     return lib
 

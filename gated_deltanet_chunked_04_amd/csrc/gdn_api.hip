@@ -11,6 +11,8 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
+#include <vector>
 
 #include "../../include/gdn.h"
 #include "gdn_kernels.h"
@@ -197,6 +199,69 @@ Geo make_geo(const gdn_desc* d, const Plan& p, unsigned char* ws) {
         if (e_ != hipSuccess) return GDN_ERR_HIP; \
     } while (0)
 
+// ---------------------------------------------------------------------------
+// Kernel timing (gdn_profile_enable / gdn_profile_read).
+enum KernelId { kKTables = 0, kKIntra, kKDecide, kKPrepass, kKScan, kKRecurOut, kKRecurStates,
+                kKBwdPrepass, kKBwdScan, kKBwdReverse, kKBwdGrads, kKCount };
+const char* const kKernelNames[kKCount] = {"tables", "intra", "cp_decide", "cp_prepass", "cp_scan",
+                                           "recur_out", "recur_states", "bwd_cp_prepass", "bwd_cp_scan",
+                                           "bwd_reverse", "bwd_grads"};
+struct Pending {
+    int kid;
+    hipEvent_t start, stop;
+};
+struct Profiler {
+    std::mutex mu;
+    bool on = false;
+    std::vector<hipEvent_t> pool;
+    std::vector<Pending> pending;
+    int64_t launches[kKCount] = {};
+    double total_ms[kKCount] = {};
+    hipEvent_t get() {
+        if (!pool.empty()) {
+            hipEvent_t e = pool.back();
+            pool.pop_back();
+            return e;
+        }
+        hipEvent_t e = nullptr;
+        if (hipEventCreate(&e) != hipSuccess) return nullptr;
+        return e;
+    }
+};
+Profiler& profiler() {
+    static Profiler p;
+    return p;
+}
+
+// Brackets one launch with events when profiling is on.
+struct ProfScope {
+    int kid;
+    hipStream_t st;
+    hipEvent_t a = nullptr, b = nullptr;
+    ProfScope(int k, hipStream_t s) : kid(k), st(s) {
+        Profiler& p = profiler();
+        std::lock_guard<std::mutex> g(p.mu);
+        if (!p.on) return;
+        a = p.get();
+        b = p.get();
+        if (a && b) hipEventRecord(a, st);
+    }
+    ~ProfScope() {
+        if (!a || !b) return;
+        hipEventRecord(b, st);
+        Profiler& p = profiler();
+        std::lock_guard<std::mutex> g(p.mu);
+        p.pending.push_back(Pending{kid, a, b});
+    }
+};
+
+#define GDN_LAUNCH(kid, st, call)         \
+    do {                                  \
+        ProfScope ps_(kid, st);           \
+        hipError_t e_ = (call);           \
+        if (e_ != hipSuccess) return GDN_ERR_HIP; \
+    } while (0)
+
 gdn_status check_ws(const Plan& p, size_t need, void* ws, size_t bytes) {
     if (!ws || bytes < need) return GDN_ERR_WORKSPACE;
     if (reinterpret_cast<uintptr_t>(ws) % kAlign) return GDN_ERR_WORKSPACE;
@@ -221,7 +286,7 @@ gdn_status run_intra(const gdn_desc* d, const Plan& p, unsigned char* ws, const 
         t.seq_segoff = reinterpret_cast<int32_t*>(ws + p.o_segoff);
         t.chunk_tab = reinterpret_cast<int2*>(ws + p.o_ctab);
         t.seg_tab = reinterpret_cast<int4*>(ws + p.o_stab);
-        GDN_TRY_HIP(launch_tables(t, st));
+        GDN_LAUNCH(kKTables, st, launch_tables(t, st));
     }
     IntraArgs ia;
     ia.geo = make_geo(d, p, ws);
@@ -233,7 +298,7 @@ gdn_status run_intra(const gdn_desc* d, const Plan& p, unsigned char* ws, const 
     ia.w = w;
     ia.u = u;
     ia.cstat = reinterpret_cast<float2*>(ws + p.o_cstat);
-    GDN_TRY_HIP(launch_intra(ia, d->dtype, st));
+    GDN_LAUNCH(kKIntra, st, launch_intra(ia, d->dtype, st));
     return GDN_OK;
 }
 
@@ -245,7 +310,7 @@ gdn_status run_decide(const gdn_desc* d, const Plan& p, unsigned char* ws, int32
     da.warmup = p.W;
     da.log_eps = logf(p.eps);
     da.forced = p.forced;
-    GDN_TRY_HIP(launch_decide(da, st));
+    GDN_LAUNCH(kKDecide, st, launch_decide(da, st));
     return GDN_OK;
 }
 
@@ -335,18 +400,18 @@ gdn_status gdn_chunk_fwd(const gdn_desc* desc, const void* q, const void* k, con
         if ((s = run_decide(desc, p, ws, modes, st)) != GDN_OK) return s;
         ra.seginit_out = seginit;
         ra.prep = prep;
-        GDN_TRY_HIP(launch_recur(ra, desc->dtype, kRecurPrepass, p.total_segs,
-                                 (int)((desc->V + desc->K) / 64), st));
+        GDN_LAUNCH(kKPrepass, st, launch_recur(ra, desc->dtype, kRecurPrepass, p.total_segs,
+                                               (int)((desc->V + desc->K) / 64), st));
         ScanArgs sa;
         sa.geo = ra.geo;
         sa.s0 = initial_state;
         sa.prep = prep;
         sa.seginit = seginit;
         sa.modes = modes;
-        GDN_TRY_HIP(launch_scan(sa, desc->dtype, st));
+        GDN_LAUNCH(kKScan, st, launch_scan(sa, desc->dtype, st));
         ra.seginit = seginit;
     }
-    GDN_TRY_HIP(launch_recur(ra, desc->dtype, kRecurOut, p.total_segs, (int)(desc->V / 64), st));
+    GDN_LAUNCH(kKRecurOut, st, launch_recur(ra, desc->dtype, kRecurOut, p.total_segs, (int)(desc->V / 64), st));
     return GDN_OK;
 }
 
@@ -394,6 +459,44 @@ gdn_status gdn_cp_modes(const gdn_desc* desc, const void* k, const void* v, cons
                        ws + p.o_u, st)) != GDN_OK)
         return s;
     return run_decide(desc, p, ws, modes_out, st);
+}
+
+gdn_status gdn_profile_enable(int enable) {
+    Profiler& p = profiler();
+    std::lock_guard<std::mutex> g(p.mu);
+    p.on = enable != 0;
+    return GDN_OK;
+}
+
+int gdn_profile_read(gdn_kernel_time* out, int max_entries) {
+    Profiler& p = profiler();
+    std::lock_guard<std::mutex> g(p.mu);
+    int rc = 0;
+    for (const Pending& e : p.pending) {
+        float ms = 0.f;
+        if (hipEventSynchronize(e.stop) != hipSuccess || hipEventElapsedTime(&ms, e.start, e.stop) != hipSuccess)
+            rc = -1;
+        p.launches[e.kid] += 1;
+        p.total_ms[e.kid] += ms;
+        p.pool.push_back(e.start);
+        p.pool.push_back(e.stop);
+    }
+    p.pending.clear();
+    if (rc < 0) return -1;
+    int n = 0;
+    for (int k = 0; k < kKCount; ++k) {
+        if (p.launches[k] == 0) continue;
+        if (out && n < max_entries) {
+            memset(&out[n], 0, sizeof(out[n]));
+            strncpy(out[n].name, kKernelNames[k], sizeof(out[n].name) - 1);
+            out[n].launches = p.launches[k];
+            out[n].total_ms = p.total_ms[k];
+            ++n;
+        }
+        p.launches[k] = 0;
+        p.total_ms[k] = 0.0;
+    }
+    return n;
 }
 
 }  // extern "C"

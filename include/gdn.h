@@ -62,7 +62,7 @@ extern "C" {
 typedef enum gdn_status {
     GDN_OK = 0,
     GDN_ERR_INVALID_ARG = 1, /* null pointer, bad size, inconsistent cu_seqlens */
-    GDN_ERR_UNSUPPORTED = 2, /* K or V not in {64,128}, chunk != 64, fp32 with K=V=128 beyond LDS */
+    GDN_ERR_UNSUPPORTED = 2, /* K or V not in {64,128}, chunk != 64, sizes beyond 32-bit grids */
     GDN_ERR_WORKSPACE = 3,   /* workspace NULL or smaller than required */
     GDN_ERR_HIP = 4          /* a HIP call or kernel launch failed */
 } gdn_status;
@@ -179,6 +179,21 @@ gdn_status gdn_intra_chunk(const gdn_desc* desc, const void* k, const void* v,
 gdn_status gdn_cp_modes(const gdn_desc* desc, const void* k, const void* v,
                         const float* g, const float* beta, int32_t* modes_out,
                         void* workspace, size_t workspace_bytes, void* stream);
+
+/* Per-kernel timing, for measurement tools (off by default). While enabled, each kernel
+ * launch of the calls above is bracketed by two HIP events recorded on the call's stream
+ * (this adds a few microseconds per launch). gdn_profile_read waits for the recorded
+ * events, writes up to max_entries per-kernel totals (kernel name, launches, total
+ * milliseconds) and clears them; it returns the number of entries written, or -1 on a
+ * HIP error. The state is process-wide and guarded by a mutex. */
+typedef struct gdn_kernel_time {
+    char name[32];
+    int64_t launches;
+    double total_ms;
+} gdn_kernel_time;
+
+gdn_status gdn_profile_enable(int enable);
+int gdn_profile_read(gdn_kernel_time* out, int max_entries);
 
 #ifdef __cplusplus
 }
