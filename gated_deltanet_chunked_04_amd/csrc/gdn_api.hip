@@ -105,14 +105,16 @@ gdn_status make_plan(const gdn_desc* d, Plan& p) {
         default: cp = true; break;
     }
     p.forced = d->cp_mode == GDN_CP_WARMUP ? 1 : (d->cp_mode == GDN_CP_EXACT ? 2 : 0);
-    const int vtiles = (int)(d->V / 64);
+    const int vtiles = (int)(d->V / recur_rows((int)d->V, (int)d->K));
     int64_t seg_len = std::max<int64_t>(max_nt, 1);
     if (cp) {
         if (d->seg_chunks > 0) {
             seg_len = d->seg_chunks;
         } else {
+            // One recurrence workgroup per CU at V = K = 128 (8 waves, ~95 KB of LDS), two otherwise.
             const int cus = d->num_cus > 0 ? d->num_cus : query_cus();
-            const int64_t target = 2 * (int64_t)cus;            // workgroups to aim for
+            const int per_cu = recur_rows((int)d->V, (int)d->K) == 128 ? 1 : 2;
+            const int64_t target = (int64_t)per_cu * cus;       // workgroups to aim for
             const int64_t units = NH * vtiles;                   // workgroups per segment layer
             const int64_t want = std::max<int64_t>(1, target / std::max<int64_t>(units, 1));
             seg_len = std::max<int64_t>(16, (max_nt + want - 1) / want);
@@ -345,7 +347,7 @@ gdn_status gdn_plan(const gdn_desc* desc, gdn_plan_info* out) {
     out->seg_chunks = p.seg_len;
     out->warmup_chunks = p.W;
     out->warmup_eps = p.eps;
-    out->v_tiles = (int32_t)(desc->V / 64);
+    out->v_tiles = (int32_t)(desc->V / recur_rows((int)desc->V, (int)desc->K));
     out->max_len = p.max_len;
     out->total_chunks = p.total_chunks;
     out->total_segments = p.total_segs;
@@ -400,8 +402,9 @@ gdn_status gdn_chunk_fwd(const gdn_desc* desc, const void* q, const void* k, con
         if ((s = run_decide(desc, p, ws, modes, st)) != GDN_OK) return s;
         ra.seginit_out = seginit;
         ra.prep = prep;
+        const int rt = recur_rows((int)desc->V, (int)desc->K);
         GDN_LAUNCH(kKPrepass, st, launch_recur(ra, desc->dtype, kRecurPrepass, p.total_segs,
-                                               (int)((desc->V + desc->K) / 64), st));
+                                               (int)((desc->V + desc->K + rt - 1) / rt), st));
         ScanArgs sa;
         sa.geo = ra.geo;
         sa.s0 = initial_state;
@@ -411,7 +414,8 @@ gdn_status gdn_chunk_fwd(const gdn_desc* desc, const void* q, const void* k, con
         GDN_LAUNCH(kKScan, st, launch_scan(sa, desc->dtype, st));
         ra.seginit = seginit;
     }
-    GDN_LAUNCH(kKRecurOut, st, launch_recur(ra, desc->dtype, kRecurOut, p.total_segs, (int)(desc->V / 64), st));
+    GDN_LAUNCH(kKRecurOut, st, launch_recur(ra, desc->dtype, kRecurOut, p.total_segs,
+                                            (int)(desc->V / recur_rows((int)desc->V, (int)desc->K)), st));
     return GDN_OK;
 }
 

@@ -158,6 +158,15 @@ __device__ __forceinline__ void mma_f32_k16(f32x4& c, const f32x4& a, const f32x
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
+// Workgroup barrier that orders LDS accesses only. __syncthreads() also drains every
+// outstanding global load and store of the wave (s_waitcnt vmcnt(0)), which would stall
+// on prefetches and output stores that nothing in the workgroup waits for.
+__device__ __forceinline__ void lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Four consecutive elements from an accumulator (one vector store: 8 B bf16, 16 B fp32).
 __device__ __forceinline__ void store4(bf16_t* p, const f32x4& x) {
     *reinterpret_cast<u32x2*>(p) = u32x2{pack_bf2(x.x, x.y), pack_bf2(x.z, x.w)};

@@ -126,7 +126,7 @@ __global__ __launch_bounds__(kThreads) void k_intra(IntraArgs args) {
         sBeta[lane] = b;
         if (in) args.gam[(L.t0 + lane) * H + h] = x;
     }
-    __syncthreads();
+    lds_sync();
 
     // ---- stage 2: A = strict_lower(diag(beta) (D .* K K^T)) -----------------------
     for (int idx = wave; idx < 10; idx += 4) {
@@ -149,7 +149,7 @@ __global__ __launch_bounds__(kThreads) void k_intra(IntraArgs args) {
             if (r == j) sKK[r] = sBeta[r] * acc[i];
         }
     }
-    __syncthreads();
+    lds_sync();
 
     // ---- stage 3: T = (I + A)^{-1} --------------------------------------------------
     // 3a: diagonal blocks by forward substitution (wave b, lanes 0..15 = columns of block b)
@@ -175,11 +175,11 @@ __global__ __launch_bounds__(kThreads) void k_intra(IntraArgs args) {
         const int bj = blk < 3 ? blk + 1 : (blk < 5 ? blk - 1 : 3);
         sT[(16 * bi + (off >> 4)) * kLdA + 16 * bj + (off & 15)] = 0.f;
     }
-    __syncthreads();
+    lds_sync();
     if (wave < 3) tri_offdiag_block(sA, sT, wave + 1, wave);
-    __syncthreads();
+    lds_sync();
     if (wave < 2) tri_offdiag_block(sA, sT, wave + 2, wave);
-    __syncthreads();
+    lds_sync();
     if (wave == 0) tri_offdiag_block(sA, sT, 3, 0);
     if (wave == 1) {
         // chunk statistics for the CP decision
@@ -188,7 +188,7 @@ __global__ __launch_bounds__(kThreads) void k_intra(IntraArgs args) {
         for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
         if (lane == 0) args.cstat[gc * H + h] = make_float2(sGam[63], m);
     }
-    __syncthreads();
+    lds_sync();
 
     // ---- stage 4: W = T diag(beta e^gam) K, U = T diag(beta) V ------------------------
     const int rt = wave;
@@ -248,7 +248,7 @@ __global__ __launch_bounds__(kThreads) void k_intra(IntraArgs args) {
             }
         }
     }
-    __syncthreads();
+    lds_sync();
     T* sWo = sKt;
     T* sUo = sVt;
     const int orow = rt * 16 + ln;
@@ -256,7 +256,7 @@ __global__ __launch_bounds__(kThreads) void k_intra(IntraArgs args) {
     for (int ct = 0; ct < K / 16; ++ct) store4(sWo + orow * S::LDO_K + ct * 16 + gq * 4, accw[ct]);
 #pragma unroll
     for (int ct = 0; ct < V / 16; ++ct) store4(sUo + orow * S::LDO_V + ct * 16 + gq * 4, accu[ct]);
-    __syncthreads();
+    lds_sync();
     store_rows<T, K>(reinterpret_cast<T*>(args.w), L.t0, H, h, c, sWo, S::LDO_K);
     store_rows<T, V>(reinterpret_cast<T*>(args.u), L.t0, H, h, c, sUo, S::LDO_V);
 }

@@ -175,6 +175,10 @@ struct TableArgs {
     int4* seg_tab;
 };
 
+// State rows per workgroup of the recurrence kernels: all 128 value rows when
+// V = K = 128 (8 waves), else 64 (4 waves). V and K are multiples of it.
+__host__ __device__ constexpr int recur_rows(int V, int K) { return (V == 128 && K == 128) ? 128 : 64; }
+
 // Launchers (return hipGetLastError of the launch).
 hipError_t launch_tables(const TableArgs& a, hipStream_t st);
 hipError_t launch_intra(const IntraArgs& a, int dtype, hipStream_t st);

@@ -31,27 +31,38 @@ namespace gdn {
 
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 256;  // decision / table kernels
 
 template <typename T> struct RPad;
 template <> struct RPad<bf16_t> { static constexpr int row = 8, tr = 8; };
 template <> struct RPad<float> { static constexpr int row = 4, tr = 4; };
 
-template <typename T, int K>
-struct RecurSmem {
+// RT state rows per workgroup (one wave per 16 rows), chunk operands staged in LDS.
+template <typename T, int K, int RT>
+struct RCfg {
+    static constexpr int NW = RT / 16;
+    static constexpr int NT = NW * 64;
     static constexpr bool kTrans = sizeof(T) == 2;  // transposed K copy (bf16 only)
+    static constexpr int VEC = Elem<T>::kVec;
     static constexpr int LD = K + RPad<T>::row;
     static constexpr int LDT = 64 + RPad<T>::tr;
-    static constexpr int LDU = 64 + RPad<T>::row;
+    static constexpr int LDU = RT + RPad<T>::row;
+    static constexpr int LDP = 64 + RPad<T>::row;
     static constexpr int kMat = 64 * LD * (int)sizeof(T);
     static constexpr int off_q = 0;
     static constexpr int off_k = off_q + kMat;
     static constexpr int off_w = off_k + kMat;
     static constexpr int off_u = off_w + kMat;
     static constexpr int off_pm = off_u + 64 * LDU * (int)sizeof(T);
-    static constexpr int off_kt = off_pm + 64 * LDU * (int)sizeof(T);
+    static constexpr int off_kt = off_pm + 64 * LDP * (int)sizeof(T);
     static constexpr int off_gam = off_kt + (kTrans ? K * LDT * (int)sizeof(T) : 0);
     static constexpr int total = off_gam + 256;
+    // register prefetch: 16-byte vectors per thread
+    static constexpr int NVK = K / VEC;                        // vectors per row of q/k/w
+    static constexpr int NVU = RT / VEC;                       // vectors per row of the u tile
+    static constexpr int IQ = (64 * NVK + NT - 1) / NT;        // q, w rows
+    static constexpr int IK = (32 * NVK + NT - 1) / NT;        // k row pairs
+    static constexpr int IU = (64 * NVU + NT - 1) / NT;        // u rows
 };
 
 // (row tile, column tile) of the 64x64 P matrix: the 10 lower tiles plus the two upper
@@ -59,26 +70,61 @@ struct RecurSmem {
 __constant__ int8_t kTriR[12][2] = {{0, 0}, {1, 0}, {1, 1}, {2, 0}, {2, 1}, {2, 2},
                                     {3, 0}, {3, 1}, {3, 2}, {3, 3}, {0, 1}, {2, 3}};
 
-// Stage columns [col0, col0+64) of rows of a [.., H, D] tensor (zero past `rows`).
-template <typename T>
-__device__ __forceinline__ void stage_cols64(const T* __restrict__ src, int64_t t0, int64_t H, int h,
-                                             int D, int col0, int rows, T* dst, int ld) {
-    constexpr int VEC = Elem<T>::kVec;
-    constexpr int NV = 64 / VEC;
-    constexpr int UNITS = 64 * NV;
+// One chunk's operands in registers (loaded one chunk ahead of use).
+template <typename T, int K, int RT, bool kQ>
+struct ChunkRegs {
+    using C = RCfg<T, K, RT>;
+    u32x4 q[kQ ? C::IQ : 1];
+    u32x4 w[C::IQ];
+    u32x4 ka[C::IK], kb[C::IK];
+    u32x4 u[C::IU];
+    float gam;
+};
+
+template <typename T, int K, int RT, bool kQ>
+__device__ __forceinline__ void chunk_fetch(ChunkRegs<T, K, RT, kQ>& R, const RecurArgs& a, int64_t t0, int c, int h,
+                                            int ucol0) {
+    using C = RCfg<T, K, RT>;
     const int tid = threadIdx.x;
+    const int64_t H = a.geo.H;
+    const T* q = reinterpret_cast<const T*>(a.q);
+    const T* k = reinterpret_cast<const T*>(a.k);
+    const T* w = reinterpret_cast<const T*>(a.w);
+    const T* u = reinterpret_cast<const T*>(a.u);
+    const u32x4 z = u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int it = 0; it < UNITS / kThreads; ++it) {
-        const int u = tid + it * kThreads;
-        const int cv = u % NV, r = u / NV;
-        u32x4 x = u32x4{0u, 0u, 0u, 0u};
-        if (r < rows) x = *reinterpret_cast<const u32x4*>(src + ((t0 + r) * H + h) * D + col0 + cv * VEC);
-        *reinterpret_cast<u32x4*>(dst + r * ld + cv * VEC) = x;
+    for (int it = 0; it < C::IQ; ++it) {
+        const int e = tid + it * C::NT;
+        const int r = e / C::NVK, cv = e % C::NVK;
+        const bool ok = e < 64 * C::NVK && r < c;
+        const size_t off = ((t0 + r) * H + h) * K + cv * C::VEC;
+        if (kQ) R.q[it] = ok ? *reinterpret_cast<const u32x4*>(q + off) : z;
+        R.w[it] = ok ? *reinterpret_cast<const u32x4*>(w + off) : z;
+    }
+#pragma unroll
+    for (int it = 0; it < C::IK; ++it) {
+        const int e = tid + it * C::NT;
+        const int rp = e / C::NVK, cv = e % C::NVK;
+        const bool in = e < 32 * C::NVK;
+        const int r0 = 2 * rp, r1 = 2 * rp + 1;
+        R.ka[it] = (in && r0 < c) ? *reinterpret_cast<const u32x4*>(k + ((t0 + r0) * H + h) * K + cv * C::VEC) : z;
+        R.kb[it] = (in && r1 < c) ? *reinterpret_cast<const u32x4*>(k + ((t0 + r1) * H + h) * K + cv * C::VEC) : z;
+    }
+#pragma unroll
+    for (int it = 0; it < C::IU; ++it) {
+        const int e = tid + it * C::NT;
+        const int r = e / C::NVU, cv = e % C::NVU;
+        const bool ok = ucol0 >= 0 && e < 64 * C::NVU && r < c;
+        R.u[it] = ok ? *reinterpret_cast<const u32x4*>(u + ((t0 + r) * H + h) * a.geo.V + ucol0 + cv * C::VEC) : z;
+    }
+    if (tid < 64) {
+        const int r = tid < c ? tid : c - 1;  // rows past the chunk end carry the chunk total
+        R.gam = a.gam[(t0 + r) * H + h];
     }
 }
 
-template <typename T, int K>
-struct ChunkCtx {
+template <typename T, int K, int RT>
+struct ChunkLds {
     T* sQ;
     T* sK;
     T* sW;
@@ -88,112 +134,129 @@ struct ChunkCtx {
     float* sGam;
 };
 
-// Load one chunk's operands. kOut needs Q; u columns for value rows [ucol0, ucol0+64)
-// (ucol0 < 0: no U rows, zeros).
-template <typename T, int K, bool kOut>
-__device__ __forceinline__ void load_chunk(const RecurArgs& a, const ChunkCtx<T, K>& cx, int64_t t0, int c,
-                                           int h, int ucol0) {
-    using S = RecurSmem<T, K>;
-    const int64_t H = a.geo.H;
-    if (kOut) stage_rows<T, K, true, false>(reinterpret_cast<const T*>(a.q), t0, H, h, c, cx.sQ, S::LD, nullptr, 0);
-    if constexpr (S::kTrans)
-        stage_rows<T, K, true, true>(reinterpret_cast<const T*>(a.k), t0, H, h, c, cx.sK, S::LD, cx.sKt, S::LDT);
-    else
-        stage_rows<T, K, true, false>(reinterpret_cast<const T*>(a.k), t0, H, h, c, cx.sK, S::LD, nullptr, 0);
-    stage_rows<T, K, true, false>(reinterpret_cast<const T*>(a.w), t0, H, h, c, cx.sW, S::LD, nullptr, 0);
-    if (ucol0 >= 0) {
-        stage_cols64<T>(reinterpret_cast<const T*>(a.u), t0, H, h, a.geo.V, ucol0, c, cx.sU, S::LDU);
-    } else {
-        for (int e = threadIdx.x; e < 64 * S::LDU; e += kThreads) cx.sU[e] = T(0);
-    }
+template <typename T, int K, int RT, bool kQ>
+__device__ __forceinline__ void chunk_stage(const ChunkRegs<T, K, RT, kQ>& R, const ChunkLds<T, K, RT>& L) {
+    using C = RCfg<T, K, RT>;
     const int tid = threadIdx.x;
-    if (tid < 64) {
-        // chunk-local gate cumsum; rows past the end carry the chunk total
-        const int r = tid < c ? tid : c - 1;
-        cx.sGam[tid] = a.gam[(t0 + r) * H + h];
+#pragma unroll
+    for (int it = 0; it < C::IQ; ++it) {
+        const int e = tid + it * C::NT;
+        if (e < 64 * C::NVK) {
+            const int r = e / C::NVK, cv = e % C::NVK;
+            if (kQ) *reinterpret_cast<u32x4*>(L.sQ + r * C::LD + cv * C::VEC) = R.q[it];
+            *reinterpret_cast<u32x4*>(L.sW + r * C::LD + cv * C::VEC) = R.w[it];
+        }
     }
+#pragma unroll
+    for (int it = 0; it < C::IK; ++it) {
+        const int e = tid + it * C::NT;
+        if (e < 32 * C::NVK) {
+            const int rp = e / C::NVK, cv = e % C::NVK;
+            const int r0 = 2 * rp;
+            const u32x4 A = R.ka[it], B = R.kb[it];
+            *reinterpret_cast<u32x4*>(L.sK + r0 * C::LD + cv * C::VEC) = A;
+            *reinterpret_cast<u32x4*>(L.sK + (r0 + 1) * C::LD + cv * C::VEC) = B;
+            if constexpr (C::kTrans) {
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const uint32_t lo = (A[j >> 1] >> ((j & 1) * 16)) & 0xFFFFu;
+                    const uint32_t hi = (B[j >> 1] >> ((j & 1) * 16)) & 0xFFFFu;
+                    *reinterpret_cast<uint32_t*>(L.sKt + (cv * 8 + j) * C::LDT + r0) = lo | (hi << 16);
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int it = 0; it < C::IU; ++it) {
+        const int e = tid + it * C::NT;
+        if (e < 64 * C::NVU) {
+            const int r = e / C::NVU, cv = e % C::NVU;
+            *reinterpret_cast<u32x4*>(L.sU + r * C::LDU + cv * C::VEC) = R.u[it];
+        }
+    }
+    if (tid < 64) L.sGam[tid] = R.gam;
 }
 
-// One chunk of the recurrence for this wave's 16 value rows.
-//   accS[kt] : S^T tiles (rows k = kt*16.., columns = the wave's value rows)
-//   kOut     : also produce O rows into o (value columns vcol0 + wave*16 + ln)
-template <typename T, int K, bool kOut>
-__device__ __forceinline__ void chunk_step(const RecurArgs& a, const ChunkCtx<T, K>& cx, f32x4 (&accS)[K / 16],
-                                           int64_t t0, int c, int h, int vcol0) {
-    using S = RecurSmem<T, K>;
+// One chunk of the recurrence for this wave's 16 state rows (columns of S^T).
+//   accS[kt]: S^T tiles (k rows kt*16.., the wave's 16 state rows)
+//   kOut    : also produce O for value columns vcol0 + wave*16 ..
+// Part 1 writes this wave's share of the P tiles; the caller's barrier separates it
+// from part 2.
+template <typename T, int K, int RT, bool kOut>
+__device__ __forceinline__ void chunk_part1(const ChunkLds<T, K, RT>& L, const f32x4 (&accS)[K / 16],
+                                            Frag<T> (&sf)[K / 32], f32x4 (&accD)[4], f32x4 (&accO)[4]) {
+    using C = RCfg<T, K, RT>;
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63, ln = lane & 15, gq = lane >> 4;
-
-    Frag<T> sf[K / 32], nsf[K / 32];
+    Frag<T> nsf[K / 32];
 #pragma unroll
     for (int kb = 0; kb < K / 32; ++kb) {
         frag_acc(sf[kb], accS[2 * kb], accS[2 * kb + 1]);
         frag_acc(nsf[kb], accS[2 * kb], accS[2 * kb + 1], -1.f);
     }
-
     if (kOut) {
-        // P^T tiles (j-tile, r-tile) of (L .* Q K^T), shared by all waves through LDS.
-        for (int idx = wave; idx < 12; idx += 4) {
+        for (int idx = wave; idx < 12; idx += C::NW) {
             const int rt = kTriR[idx][0], jt = kTriR[idx][1];
             f32x4 acc = zero4();
 #pragma unroll
             for (int kb = 0; kb < (jt <= rt ? K / 32 : 0); ++kb) {
                 Frag<T> fa, fb;
-                frag_row(fa, cx.sK, S::LD, jt * 16 + ln, kb * 32);
-                frag_row(fb, cx.sQ, S::LD, rt * 16 + ln, kb * 32);
+                frag_row(fa, L.sK, C::LD, jt * 16 + ln, kb * 32);
+                frag_row(fb, L.sQ, C::LD, rt * 16 + ln, kb * 32);
                 mma(acc, fa, fb);
             }
             // acc[i] = (Q K^T)[r = rt*16+ln][j = jt*16+gq*4+i]
             const int r = rt * 16 + ln;
-            const float gr = cx.sGam[r];
-            float v[4];
+            const float gr = L.sGam[r];
+            f32x4 v;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int j = jt * 16 + gq * 4 + i;
-                v[i] = (j <= r) ? acc[i] * fast_exp(gr - cx.sGam[j]) : 0.f;
+                v[i] = (j <= r) ? acc[i] * fast_exp(gr - L.sGam[j]) : 0.f;
             }
-            T* dst = cx.sPm + r * S::LDU + jt * 16 + gq * 4;
-            if constexpr (sizeof(T) == 2) {
-                *reinterpret_cast<u32x2*>(dst) = u32x2{pack_bf2(v[0], v[1]), pack_bf2(v[2], v[3])};
-            } else {
-                *reinterpret_cast<f32x4*>(dst) = f32x4{v[0], v[1], v[2], v[3]};
-            }
+            store4(L.sPm + r * C::LDP + jt * 16 + gq * 4, v);
         }
     }
-
-    // Delta = U - W S^T   (rows j of the chunk, columns = the wave's value rows)
-    f32x4 accD[4];
+    // Delta = U - W S^T  (rows j of the chunk, columns = the wave's state rows)
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            accD[rt][i] = Elem<T>::to_f(cx.sU[(rt * 16 + gq * 4 + i) * S::LDU + wave * 16 + ln]);
+            accD[rt][i] = Elem<T>::to_f(L.sU[(rt * 16 + gq * 4 + i) * C::LDU + wave * 16 + ln]);
 #pragma unroll
         for (int kb = 0; kb < K / 32; ++kb) {
             Frag<T> fa;
-            frag_row(fa, cx.sW, S::LD, rt * 16 + ln, kb * 32);
+            frag_row(fa, L.sW, C::LD, rt * 16 + ln, kb * 32);
             mma(accD[rt], fa, nsf[kb]);
         }
     }
-
     // O^T tiles: accO[rt][i] = O^T[v = wave*16 + gq*4 + i][r = rt*16 + ln]. The S^T
     // accumulators are an A fragment of S and the Delta accumulators an A fragment of
-    // Delta^T, so O^T = S Q^T diag(e^gam) + Delta^T P^T needs no data movement, and each lane
-    // ends up with four consecutive value columns of one token row (one vector store).
+    // Delta^T, so O^T = S Q^T diag(e^gam) + Delta^T P^T needs no data movement, and each
+    // lane ends up with four consecutive value columns of one token row.
     if (kOut) {
-        f32x4 accO[4];
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) {
             accO[rt] = zero4();
 #pragma unroll
             for (int kb = 0; kb < K / 32; ++kb) {
                 Frag<T> fb;
-                frag_row(fb, cx.sQ, S::LD, rt * 16 + ln, kb * 32);
+                frag_row(fb, L.sQ, C::LD, rt * 16 + ln, kb * 32);
                 mma(accO[rt], sf[kb], fb);
             }
-            accO[rt] *= fast_exp(cx.sGam[rt * 16 + ln]);
+            accO[rt] *= fast_exp(L.sGam[rt * 16 + ln]);
         }
-        __syncthreads();  // P tiles complete
+    }
+}
+
+template <typename T, int K, int RT, bool kOut>
+__device__ __forceinline__ void chunk_part2(const RecurArgs& a, const ChunkLds<T, K, RT>& L, f32x4 (&accS)[K / 16],
+                                            f32x4 (&accD)[4], f32x4 (&accO)[4], int64_t t0, int c, int h,
+                                            int vcol0) {
+    using C = RCfg<T, K, RT>;
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63, ln = lane & 15, gq = lane >> 4;
+    if (kOut) {
         Frag<T> df[2];
         frag_acc(df[0], accD[0], accD[1]);
         frag_acc(df[1], accD[2], accD[3]);
@@ -202,7 +265,7 @@ __device__ __forceinline__ void chunk_step(const RecurArgs& a, const ChunkCtx<T,
 #pragma unroll
             for (int kb = 0; kb <= (rt >> 1); ++kb) {
                 Frag<T> fb;
-                frag_row(fb, cx.sPm, S::LDU, rt * 16 + ln, kb * 32);
+                frag_row(fb, L.sPm, C::LDP, rt * 16 + ln, kb * 32);
                 mma(accO[rt], df[kb], fb);
             }
         }
@@ -215,9 +278,8 @@ __device__ __forceinline__ void chunk_step(const RecurArgs& a, const ChunkCtx<T,
             if (r < c) store4(o + ((t0 + r) * H + h) * V + vcol0 + wave * 16 + gq * 4, accO[rt] * a.scale);
         }
     }
-
     // S^T <- e^Gam S^T + K^T diag(e^{Gam-gam}) Delta
-    const float G = cx.sGam[63];
+    const float G = L.sGam[63];
     const float eG = fast_exp(G);
     Frag<T> dtf[2];
 #pragma unroll
@@ -225,8 +287,8 @@ __device__ __forceinline__ void chunk_step(const RecurArgs& a, const ChunkCtx<T,
         f32x4 r0, r1;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            r0[i] = fast_exp(G - cx.sGam[kb * 32 + gq * 4 + i]);
-            r1[i] = fast_exp(G - cx.sGam[kb * 32 + 16 + gq * 4 + i]);
+            r0[i] = fast_exp(G - L.sGam[kb * 32 + gq * 4 + i]);
+            r1[i] = fast_exp(G - L.sGam[kb * 32 + 16 + gq * 4 + i]);
         }
         frag_acc_rows(dtf[kb], accD[2 * kb], accD[2 * kb + 1], r0, r1);
     }
@@ -236,16 +298,16 @@ __device__ __forceinline__ void chunk_step(const RecurArgs& a, const ChunkCtx<T,
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
             Frag<T> fa;
-            if constexpr (S::kTrans)
-                frag_row(fa, cx.sKt, S::LDT, kt * 16 + ln, kb * 32);
+            if constexpr (C::kTrans)
+                frag_row(fa, L.sKt, C::LDT, kt * 16 + ln, kb * 32);
             else
-                frag_col(fa, cx.sK, S::LD, kt * 16 + ln, kb * 32);
+                frag_col(fa, L.sK, C::LD, kt * 16 + ln, kb * 32);
             mma(accS[kt], fa, dtf[kb]);
         }
     }
 }
 
-// accS <- rows [row0, row0+16) of a [rows][K] fp32 state (S^T tiles)
+// accS <- row `lrow` of a [rows][K] fp32 state (as S^T tiles)
 template <int K>
 __device__ __forceinline__ void load_state(f32x4 (&accS)[K / 16], const float* src, int lrow) {
     const int gq = (threadIdx.x & 63) >> 4;
@@ -261,18 +323,19 @@ __device__ __forceinline__ void store_state(const f32x4 (&accS)[K / 16], float* 
         *reinterpret_cast<f32x4*>(dst + (size_t)lrow * K + kt * 16 + gq * 4) = accS[kt];
 }
 
-template <typename T, int K, int MODE>
-__global__ __launch_bounds__(kThreads) void k_recur(RecurArgs a) {
-    using S = RecurSmem<T, K>;
+template <typename T, int K, int RT, int MODE>
+__global__ __launch_bounds__(RT * 4) void k_recur(RecurArgs a) {
+    using C = RCfg<T, K, RT>;
+    constexpr bool kOut = MODE == kRecurOut;
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-    ChunkCtx<T, K> cx;
-    cx.sQ = reinterpret_cast<T*>(smem + S::off_q);
-    cx.sK = reinterpret_cast<T*>(smem + S::off_k);
-    cx.sW = reinterpret_cast<T*>(smem + S::off_w);
-    cx.sU = reinterpret_cast<T*>(smem + S::off_u);
-    cx.sPm = reinterpret_cast<T*>(smem + S::off_pm);
-    cx.sKt = reinterpret_cast<T*>(smem + S::off_kt);
-    cx.sGam = reinterpret_cast<float*>(smem + S::off_gam);
+    ChunkLds<T, K, RT> L;
+    L.sQ = reinterpret_cast<T*>(smem + C::off_q);
+    L.sK = reinterpret_cast<T*>(smem + C::off_k);
+    L.sW = reinterpret_cast<T*>(smem + C::off_w);
+    L.sU = reinterpret_cast<T*>(smem + C::off_u);
+    L.sPm = reinterpret_cast<T*>(smem + C::off_pm);
+    L.sKt = reinterpret_cast<T*>(smem + C::off_kt);
+    L.sGam = reinterpret_cast<float*>(smem + C::off_gam);
 
     const Geo& geo = a.geo;
     const int64_t gs = blockIdx.x;
@@ -284,15 +347,16 @@ __global__ __launch_bounds__(kThreads) void k_recur(RecurArgs a) {
     if (!locate_seg(geo, gs, sg)) return;
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63, ln = lane & 15, gq = lane >> 4;
-    const int row = vt * 64 + wave * 16 + ln;  // this lane's state row (value row, or V + M row)
+    const int row = vt * RT + wave * 16 + ln;  // this lane's state row (value row, or V + M row)
     const size_t VK = (size_t)V * K;
 
     f32x4 accS[K / 16];
     int cbeg = sg.c0, cend = sg.c1;
+    int mode = 0;
     if (MODE == kRecurPrepass) {
-        const int mode = a.modes[sg.n * H + h];
+        mode = a.modes[sg.n * H + h];
         if (mode == 1) {
-            if (sg.s == 0 || vt * 64 >= V) return;
+            if (sg.s == 0 || vt * RT >= V) return;
             cend = sg.c0;
             cbeg = max(0, sg.c0 - a.warmup);
             if (cbeg == 0 && a.s0)
@@ -301,7 +365,7 @@ __global__ __launch_bounds__(kThreads) void k_recur(RecurArgs a) {
 #pragma unroll
                 for (int kt = 0; kt < K / 16; ++kt) accS[kt] = zero4();
         } else if (mode == 2) {
-            if (sg.s == sg.nseg - 1) return;
+            if (sg.s == sg.nseg - 1 || vt * RT >= V + K) return;
 #pragma unroll
             for (int kt = 0; kt < K / 16; ++kt) {
                 f32x4 z = zero4();
@@ -325,7 +389,9 @@ __global__ __launch_bounds__(kThreads) void k_recur(RecurArgs a) {
         }
     }
 
-    const int ucol0 = (vt * 64 < V) ? vt * 64 : -1;
+    const int ucol0 = (vt * RT < V) ? vt * RT : -1;
+    ChunkRegs<T, K, RT, kOut> R;
+    if (cbeg < cend) chunk_fetch<T, K, RT, kOut>(R, a, sg.bos + (int64_t)cbeg * 64, min(64, sg.len - cbeg * 64), h, ucol0);
     for (int ci = cbeg; ci < cend; ++ci) {
         const int64_t t0 = sg.bos + (int64_t)ci * 64;
         const int c = min(64, sg.len - ci * 64);
@@ -333,30 +399,28 @@ __global__ __launch_bounds__(kThreads) void k_recur(RecurArgs a) {
             // entry state of this chunk, in the input precision
             T* hs = reinterpret_cast<T*>(a.hstates) + ((size_t)(sg.choff + ci) * H + h) * VK + (size_t)row * K;
 #pragma unroll
-            for (int kt = 0; kt < K / 16; ++kt) {
-                if constexpr (sizeof(T) == 2) {
-                    *reinterpret_cast<u32x2*>(hs + kt * 16 + gq * 4) =
-                        u32x2{pack_bf2(accS[kt][0], accS[kt][1]), pack_bf2(accS[kt][2], accS[kt][3])};
-                } else {
-                    *reinterpret_cast<f32x4*>(hs + kt * 16 + gq * 4) = accS[kt];
-                }
-            }
+            for (int kt = 0; kt < K / 16; ++kt) store4(hs + kt * 16 + gq * 4, accS[kt]);
         }
-        __syncthreads();
-        load_chunk<T, K, MODE == kRecurOut>(a, cx, t0, c, h, ucol0);
-        __syncthreads();
-        chunk_step<T, K, MODE == kRecurOut>(a, cx, accS, t0, c, h, vt * 64);
+        lds_sync();  // previous chunk's LDS reads are done
+        chunk_stage<T, K, RT, kOut>(R, L);
+        lds_sync();
+        if (ci + 1 < cend)
+            chunk_fetch<T, K, RT, kOut>(R, a, t0 + 64, min(64, sg.len - (ci + 1) * 64), h, ucol0);
+        Frag<T> sf[K / 32];
+        f32x4 accD[4], accO[4];
+        chunk_part1<T, K, RT, kOut>(L, accS, sf, accD, accO);
+        if (kOut) lds_sync();  // P tiles complete
+        chunk_part2<T, K, RT, kOut>(a, L, accS, accD, accO, t0, c, h, vt * RT);
     }
 
     if (MODE == kRecurPrepass) {
-        const int mode = a.modes[sg.n * H + h];
         if (mode == 1) {
             store_state<K>(accS, a.seginit_out + ((size_t)gs * H + h) * VK, row);
         } else {
             float* P = a.prep + ((size_t)gs * H + h) * (size_t)(V + K) * K;
             if (row < V) {
                 store_state<K>(accS, P, row);
-            } else {
+            } else if (row < V + K) {
                 // M^T[k][i] at P + V*K + k*K + i, i = row - V
                 const int i = row - V;
 #pragma unroll
@@ -370,16 +434,16 @@ __global__ __launch_bounds__(kThreads) void k_recur(RecurArgs a) {
     }
 }
 
-template <typename T, int K, int MODE>
+template <typename T, int K, int RT, int MODE>
 hipError_t launch_recur_t(const RecurArgs& a, int64_t nsegs_grid, int vtiles, hipStream_t st) {
-    using S = RecurSmem<T, K>;
-    static_assert(S::total <= 160 * 1024, "LDS budget");
-    auto kern = k_recur<T, K, MODE>;
+    using C = RCfg<T, K, RT>;
+    static_assert(C::total <= 160 * 1024, "LDS budget");
+    auto kern = k_recur<T, K, RT, MODE>;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, S::total);
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, C::total);
     if (e != hipSuccess) return e;
     dim3 grid((unsigned)nsegs_grid, (unsigned)a.geo.H, (unsigned)vtiles);
-    hipLaunchKernelGGL(kern, grid, dim3(kThreads), S::total, st, a);
+    hipLaunchKernelGGL(kern, grid, dim3(C::NT), C::total, st, a);
     return hipGetLastError();
 }
 
@@ -424,53 +488,77 @@ __global__ __launch_bounds__(kThreads) void k_decide(DecideArgs a) {
 
 // ---------------------------------------------------------------------------
 // Exact CP: S_{s+1} = S_s M_s + R~_s across segments, for sequence-heads in mode 2.
-// Grid (N, H, V/64); the state rows live in S^T accumulators as in k_recur.
-template <typename T>
-__device__ __forceinline__ void frag_row_f32(Frag<T>& f, const float* base, int ld, int row, int k0);
-template <>
-__device__ __forceinline__ void frag_row_f32(Frag<bf16_t>& f, const float* base, int ld, int row, int k0) {
-    const int gq = (threadIdx.x & 63) >> 4;
-    const float* p = base + (size_t)row * ld + k0 + gq * 4;
-    const f32x4 x = *reinterpret_cast<const f32x4*>(p);
-    const f32x4 y = *reinterpret_cast<const f32x4*>(p + 16);
-    f.v = u32x4{pack_bf2(x.x, x.y), pack_bf2(x.z, x.w), pack_bf2(y.x, y.y), pack_bf2(y.z, y.w)};
-}
-template <>
-__device__ __forceinline__ void frag_row_f32(Frag<float>& f, const float* base, int ld, int row, int k0) {
-    frag_row(f, base, ld, row, k0);
-}
+// Grid (N, H, V/RT); the state rows live in S^T accumulators as in k_recur. Segment s's
+// M^T is staged in LDS (in the matrix-core operand precision) while segment s+1's map
+// is already in flight into registers.
+template <typename T, int K, int RT>
+struct ScanCfg {
+    static constexpr int NT = RT * 4;
+    static constexpr int LDM = K + RPad<T>::row;
+    static constexpr int IM = (K * K / 4 + NT - 1) / NT;  // fp32x4 vectors of M^T per thread
+    static constexpr int total = K * LDM * (int)sizeof(T);
+};
 
-template <typename T, int K>
-__global__ __launch_bounds__(kThreads) void k_scan(ScanArgs a) {
+template <typename T, int K, int RT>
+__global__ __launch_bounds__(RT * 4) void k_scan(ScanArgs a) {
+    using SC = ScanCfg<T, K, RT>;
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    T* sM = reinterpret_cast<T*>(smem);
     const int n = blockIdx.x, h = blockIdx.y, vt = blockIdx.z;
     const int H = a.geo.H, V = a.geo.V;
     if (a.modes[(int64_t)n * H + h] != 2) return;
     int32_t nseg, nchunks;
     int64_t segoff, choff;
     seq_segs(a.geo, n, nseg, segoff, nchunks, choff);
+    if (nseg < 2) return;
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63, ln = lane & 15;
-    const int row = vt * 64 + wave * 16 + ln;
+    const int row = vt * RT + wave * 16 + ln;
     const size_t VK = (size_t)V * K;
+    const size_t PS = (size_t)(V + K) * K;  // floats per (segment, head) map
     f32x4 accS[K / 16];
     if (a.s0)
         load_state<K>(accS, a.s0 + ((size_t)n * H + h) * VK, row);
     else
 #pragma unroll
         for (int kt = 0; kt < K / 16; ++kt) accS[kt] = zero4();
+
+    f32x4 mreg[SC::IM];
+    f32x4 rreg[K / 16];
+    auto fetch = [&](int s) {
+        const float* P = a.prep + ((size_t)(segoff + s) * H + h) * PS;
+#pragma unroll
+        for (int it = 0; it < SC::IM; ++it) {
+            const int e = tid + it * SC::NT;
+            mreg[it] = e < K * K / 4 ? *reinterpret_cast<const f32x4*>(P + VK + (size_t)e * 4) : zero4();
+        }
+        load_state<K>(rreg, P, row);
+    };
+    fetch(0);
     for (int s = 0; s + 1 < nseg; ++s) {
-        const float* P = a.prep + ((size_t)(segoff + s) * H + h) * (size_t)(V + K) * K;
+        lds_sync();
+#pragma unroll
+        for (int it = 0; it < SC::IM; ++it) {
+            const int e = tid + it * SC::NT;
+            if (e < K * K / 4) {
+                const int r = (e * 4) / K, cc = (e * 4) % K;
+                store4(sM + r * SC::LDM + cc, mreg[it]);
+            }
+        }
+        lds_sync();
+        f32x4 nx[K / 16];
+#pragma unroll
+        for (int kt = 0; kt < K / 16; ++kt) nx[kt] = rreg[kt];
+        if (s + 2 < nseg) fetch(s + 1);
         Frag<T> sf[K / 32];
 #pragma unroll
         for (int kb = 0; kb < K / 32; ++kb) frag_acc(sf[kb], accS[2 * kb], accS[2 * kb + 1]);
-        f32x4 nx[K / 16];
-        load_state<K>(nx, P, row);  // R~ rows
 #pragma unroll
         for (int kt = 0; kt < K / 16; ++kt) {
 #pragma unroll
             for (int kb = 0; kb < K / 32; ++kb) {
                 Frag<T> fa;
-                frag_row_f32(fa, P + VK, K, kt * 16 + ln, kb * 32);  // M^T rows
+                frag_row(fa, sM, SC::LDM, kt * 16 + ln, kb * 32);  // rows of M^T
                 mma(nx[kt], fa, sf[kb]);
             }
         }
@@ -478,6 +566,18 @@ __global__ __launch_bounds__(kThreads) void k_scan(ScanArgs a) {
         for (int kt = 0; kt < K / 16; ++kt) accS[kt] = nx[kt];
         store_state<K>(accS, a.seginit + ((size_t)(segoff + s + 1) * H + h) * VK, row);
     }
+}
+
+template <typename T, int K, int RT>
+hipError_t launch_scan_t(const ScanArgs& a, hipStream_t st) {
+    using SC = ScanCfg<T, K, RT>;
+    auto kern = k_scan<T, K, RT>;
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, SC::total);
+    if (e != hipSuccess) return e;
+    dim3 grid((unsigned)a.geo.N, (unsigned)a.geo.H, (unsigned)(a.geo.V / RT));
+    hipLaunchKernelGGL(kern, grid, dim3(SC::NT), SC::total, st, a);
+    return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
@@ -559,18 +659,21 @@ hipError_t launch_recur(const RecurArgs& a, int dtype, int mode, int64_t nsegs_g
                         hipStream_t st) {
     if (nsegs_grid == 0) return hipSuccess;
     const int K = a.geo.K;
-#define GDN_RECUR_CASE(TT, KK)                                                                       \
-    if (K == KK) {                                                                                   \
-        if (mode == kRecurOut) return launch_recur_t<TT, KK, kRecurOut>(a, nsegs_grid, vtiles, st);   \
-        if (mode == kRecurPrepass) return launch_recur_t<TT, KK, kRecurPrepass>(a, nsegs_grid, vtiles, st); \
-        if (mode == kRecurStates) return launch_recur_t<TT, KK, kRecurStates>(a, nsegs_grid, vtiles, st); \
+    const int RT = recur_rows(a.geo.V, K);
+#define GDN_RECUR_CASE(TT, KK, RR)                                                                         \
+    if (K == KK && RT == RR) {                                                                             \
+        if (mode == kRecurOut) return launch_recur_t<TT, KK, RR, kRecurOut>(a, nsegs_grid, vtiles, st);     \
+        if (mode == kRecurPrepass) return launch_recur_t<TT, KK, RR, kRecurPrepass>(a, nsegs_grid, vtiles, st); \
+        if (mode == kRecurStates) return launch_recur_t<TT, KK, RR, kRecurStates>(a, nsegs_grid, vtiles, st); \
     }
     if (dtype == 0) {
-        GDN_RECUR_CASE(bf16_t, 64)
-        GDN_RECUR_CASE(bf16_t, 128)
+        GDN_RECUR_CASE(bf16_t, 64, 64)
+        GDN_RECUR_CASE(bf16_t, 128, 64)
+        GDN_RECUR_CASE(bf16_t, 128, 128)
     } else {
-        GDN_RECUR_CASE(float, 64)
-        GDN_RECUR_CASE(float, 128)
+        GDN_RECUR_CASE(float, 64, 64)
+        GDN_RECUR_CASE(float, 128, 64)
+        GDN_RECUR_CASE(float, 128, 128)
     }
 #undef GDN_RECUR_CASE
     return hipErrorInvalidValue;
@@ -584,17 +687,19 @@ hipError_t launch_decide(const DecideArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_scan(const ScanArgs& a, int dtype, hipStream_t st) {
-    dim3 grid((unsigned)a.geo.N, (unsigned)a.geo.H, (unsigned)(a.geo.V / 64));
     if (a.geo.N == 0) return hipSuccess;
     const int K = a.geo.K;
+    const int RT = recur_rows(a.geo.V, K);
     if (dtype == 0) {
-        if (K == 64) hipLaunchKernelGGL((k_scan<bf16_t, 64>), grid, dim3(kThreads), 0, st, a);
-        else hipLaunchKernelGGL((k_scan<bf16_t, 128>), grid, dim3(kThreads), 0, st, a);
+        if (K == 64 && RT == 64) return launch_scan_t<bf16_t, 64, 64>(a, st);
+        if (K == 128 && RT == 64) return launch_scan_t<bf16_t, 128, 64>(a, st);
+        if (K == 128 && RT == 128) return launch_scan_t<bf16_t, 128, 128>(a, st);
     } else {
-        if (K == 64) hipLaunchKernelGGL((k_scan<float, 64>), grid, dim3(kThreads), 0, st, a);
-        else hipLaunchKernelGGL((k_scan<float, 128>), grid, dim3(kThreads), 0, st, a);
+        if (K == 64 && RT == 64) return launch_scan_t<float, 64, 64>(a, st);
+        if (K == 128 && RT == 64) return launch_scan_t<float, 128, 64>(a, st);
+        if (K == 128 && RT == 128) return launch_scan_t<float, 128, 128>(a, st);
     }
-    return hipGetLastError();
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_tables(const TableArgs& a, hipStream_t st) {
