@@ -43,7 +43,10 @@ struct Plan {
     // forward workspace
     size_t o_gam = 0, o_w = 0, o_u = 0, o_cstat = 0, o_bos = 0, o_len = 0, o_choff = 0, o_segoff = 0,
            o_ctab = 0, o_stab = 0, o_modes = 0, o_seginit = 0, o_prep = 0, fwd_bytes = 0;
-    size_t bwd_bytes = 0;
+    // backward workspace: the forward's layout, then these
+    size_t o_modes_r = 0, o_seginit_r = 0, o_prep_r = 0, o_h = 0, o_gst = 0, o_dw = 0, o_du = 0, o_dkp = 0,
+           o_dgp = 0, bwd_bytes = 0;
+    int32_t bwd_ok = 1;  // fp32 backward supports K = V = 64 only (LDS)
 };
 
 int query_cus() {
@@ -165,7 +168,20 @@ gdn_status make_plan(const gdn_desc* d, Plan& p) {
         p.o_prep = take((size_t)p.total_segs * H * (V + K) * K * 4);
     }
     p.fwd_bytes = std::max<size_t>(off, kAlign);
-    p.bwd_bytes = 0;
+    // backward workspace continues after the forward's
+    if (p.cp_on) {
+        p.o_modes_r = take((size_t)p.N * H * 4);
+        p.o_seginit_r = take((size_t)p.total_segs * H * V * K * 4);
+        p.o_prep_r = take((size_t)p.total_segs * H * (V + K) * K * 4);
+    }
+    p.o_h = take((size_t)p.total_chunks * H * V * K * p.esize);
+    p.o_gst = take((size_t)p.total_chunks * H * V * K * p.esize);
+    p.o_dw = take(T * H * K * 4);
+    p.o_du = take(T * H * V * 4);
+    p.o_dkp = take(T * H * K * 4);
+    p.o_dgp = take(T * H * 4);
+    p.bwd_bytes = std::max<size_t>(off, kAlign);
+    p.bwd_ok = (d->dtype == GDN_DTYPE_BF16) || (d->K == 64 && d->V == 64);
     return GDN_OK;
 }
 
@@ -204,10 +220,10 @@ Geo make_geo(const gdn_desc* d, const Plan& p, unsigned char* ws) {
 // ---------------------------------------------------------------------------
 // Kernel timing (gdn_profile_enable / gdn_profile_read).
 enum KernelId { kKTables = 0, kKIntra, kKDecide, kKPrepass, kKScan, kKRecurOut, kKRecurStates,
-                kKBwdPrepass, kKBwdScan, kKBwdReverse, kKBwdGrads, kKCount };
+                kKBwdPrepass, kKBwdScan, kKBwdReverse, kKBwdGrads, kKBwdWy, kKCount };
 const char* const kKernelNames[kKCount] = {"tables", "intra", "cp_decide", "cp_prepass", "cp_scan",
                                            "recur_out", "recur_states", "bwd_cp_prepass", "bwd_cp_scan",
-                                           "bwd_reverse", "bwd_grads"};
+                                           "bwd_reverse", "bwd_state", "bwd_wy"};
 struct Pending {
     int kid;
     hipEvent_t start, stop;
@@ -275,7 +291,7 @@ gdn_status check_ws(const Plan& p, size_t need, void* ws, size_t bytes) {
 gdn_status run_intra(const gdn_desc* d, const Plan& p, unsigned char* ws, const void* k, const void* v,
                      const float* g, const float* beta, float* gam, void* w, void* u, hipStream_t st) {
     if (p.varlen) {
-        TableArgs t;
+        TableArgs t{};
         t.cu = d->cu_seqlens;
         t.N = p.N;
         t.Ttot = p.Ttot;
@@ -290,7 +306,7 @@ gdn_status run_intra(const gdn_desc* d, const Plan& p, unsigned char* ws, const 
         t.seg_tab = reinterpret_cast<int4*>(ws + p.o_stab);
         GDN_LAUNCH(kKTables, st, launch_tables(t, st));
     }
-    IntraArgs ia;
+    IntraArgs ia{};
     ia.geo = make_geo(d, p, ws);
     ia.k = k;
     ia.v = v;
@@ -304,8 +320,10 @@ gdn_status run_intra(const gdn_desc* d, const Plan& p, unsigned char* ws, const 
     return GDN_OK;
 }
 
-gdn_status run_decide(const gdn_desc* d, const Plan& p, unsigned char* ws, int32_t* modes, hipStream_t st) {
-    DecideArgs da;
+gdn_status run_decide(const gdn_desc* d, const Plan& p, unsigned char* ws, int32_t* modes, hipStream_t st,
+                      int reverse = 0) {
+    DecideArgs da{};
+    da.reverse = reverse;
     da.geo = make_geo(d, p, ws);
     da.cstat = reinterpret_cast<const float2*>(ws + p.o_cstat);
     da.modes = modes;
@@ -380,7 +398,7 @@ gdn_status gdn_chunk_fwd(const gdn_desc* desc, const void* q, const void* k, con
     void* u = ws + p.o_u;
     if ((s = run_intra(desc, p, ws, k, v, g, beta, gam, w, u, st)) != GDN_OK) return s;
 
-    RecurArgs ra;
+    RecurArgs ra{};
     memset(&ra, 0, sizeof(ra));
     ra.geo = make_geo(desc, p, ws);
     ra.q = q;
@@ -405,7 +423,7 @@ gdn_status gdn_chunk_fwd(const gdn_desc* desc, const void* q, const void* k, con
         const int rt = recur_rows((int)desc->V, (int)desc->K);
         GDN_LAUNCH(kKPrepass, st, launch_recur(ra, desc->dtype, kRecurPrepass, p.total_segs,
                                                (int)((desc->V + desc->K + rt - 1) / rt), st));
-        ScanArgs sa;
+        ScanArgs sa{};
         sa.geo = ra.geo;
         sa.s0 = initial_state;
         sa.prep = prep;
@@ -424,18 +442,129 @@ gdn_status gdn_chunk_bwd_workspace_size(const gdn_desc* desc, size_t* bytes) {
     Plan p;
     const gdn_status s = make_plan(desc, p);
     if (s != GDN_OK) return s;
+    if (!p.bwd_ok) return GDN_ERR_UNSUPPORTED;
     *bytes = p.bwd_bytes;
-    return GDN_ERR_UNSUPPORTED;
+    return GDN_OK;
 }
 
 gdn_status gdn_chunk_bwd(const gdn_desc* desc, const void* q, const void* k, const void* v, const float* g,
                          const float* beta, const float* initial_state, const void* d_o,
                          const float* d_final_state, void* dq, void* dk, void* dv, float* dg, float* dbeta,
                          float* d_initial_state, void* workspace, size_t workspace_bytes, void* stream) {
-    (void)desc; (void)q; (void)k; (void)v; (void)g; (void)beta; (void)initial_state; (void)d_o;
-    (void)d_final_state; (void)dq; (void)dk; (void)dv; (void)dg; (void)dbeta; (void)d_initial_state;
-    (void)workspace; (void)workspace_bytes; (void)stream;
-    return GDN_ERR_UNSUPPORTED;
+    Plan p;
+    gdn_status s = make_plan(desc, p);
+    if (s != GDN_OK) return s;
+    if (!p.bwd_ok) return GDN_ERR_UNSUPPORTED;
+    if (p.Ttot > 0 && (!q || !k || !v || !g || !beta || !d_o || !dq || !dk || !dv || !dg || !dbeta))
+        return GDN_ERR_INVALID_ARG;
+    if ((s = check_ws(p, p.bwd_bytes, workspace, workspace_bytes)) != GDN_OK) return s;
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    unsigned char* ws = static_cast<unsigned char*>(workspace);
+    float* gam = reinterpret_cast<float*>(ws + p.o_gam);
+    void* w = ws + p.o_w;
+    void* u = ws + p.o_u;
+    // 1. recompute the gate cumsum and the WY factors
+    if ((s = run_intra(desc, p, ws, k, v, g, beta, gam, w, u, st)) != GDN_OK) return s;
+    const int rt = recur_rows((int)desc->V, (int)desc->K);
+    const int vtiles = (int)(desc->V / rt);
+    const int vktiles = (int)((desc->V + desc->K + rt - 1) / rt);
+    // 2. chunk-entry states, with the forward's CP
+    RecurArgs ra{};
+    memset(&ra, 0, sizeof(ra));
+    ra.geo = make_geo(desc, p, ws);
+    ra.k = k;
+    ra.gam = gam;
+    ra.w = w;
+    ra.u = u;
+    ra.s0 = initial_state;
+    ra.scale = desc->scale;
+    ra.warmup = p.W;
+    ra.use_cp = p.cp_on;
+    int32_t* modes = reinterpret_cast<int32_t*>(ws + p.o_modes);
+    ra.modes = modes;
+    ra.hstates = ws + p.o_h;
+    if (p.cp_on) {
+        float* seginit = reinterpret_cast<float*>(ws + p.o_seginit);
+        float* prep = reinterpret_cast<float*>(ws + p.o_prep);
+        if ((s = run_decide(desc, p, ws, modes, st)) != GDN_OK) return s;
+        ra.seginit_out = seginit;
+        ra.prep = prep;
+        GDN_LAUNCH(kKPrepass, st, launch_recur(ra, desc->dtype, kRecurPrepass, p.total_segs, vktiles, st));
+        ScanArgs sa{};
+        memset(&sa, 0, sizeof(sa));
+        sa.geo = ra.geo;
+        sa.s0 = initial_state;
+        sa.prep = prep;
+        sa.seginit = seginit;
+        sa.modes = modes;
+        GDN_LAUNCH(kKScan, st, launch_scan(sa, desc->dtype, st));
+        ra.seginit = seginit;
+    }
+    GDN_LAUNCH(kKRecurStates, st, launch_recur(ra, desc->dtype, kRecurStates, p.total_segs, vtiles, st));
+    // 3. reverse adjoint pass, with CP mirrored (windows and scan from the sequence end)
+    RevArgs va;
+    memset(&va, 0, sizeof(va));
+    va.geo = ra.geo;
+    va.q = q;
+    va.k = k;
+    va.gam = gam;
+    va.w = w;
+    va.d_o = d_o;
+    va.dsT = d_final_state;
+    va.ds0 = d_initial_state;
+    va.gstates = ws + p.o_gst;
+    va.scale = desc->scale;
+    va.warmup = p.W;
+    va.use_cp = p.cp_on;
+    if (p.cp_on) {
+        int32_t* modes_r = reinterpret_cast<int32_t*>(ws + p.o_modes_r);
+        float* seginit_r = reinterpret_cast<float*>(ws + p.o_seginit_r);
+        float* prep_r = reinterpret_cast<float*>(ws + p.o_prep_r);
+        if ((s = run_decide(desc, p, ws, modes_r, st, 1)) != GDN_OK) return s;
+        va.modes = modes_r;
+        va.seginit_out = seginit_r;
+        va.prep = prep_r;
+        GDN_LAUNCH(kKBwdPrepass, st, launch_reverse(va, desc->dtype, kRecurPrepass, p.total_segs, vktiles, st));
+        ScanArgs sa{};
+        memset(&sa, 0, sizeof(sa));
+        sa.geo = ra.geo;
+        sa.s0 = d_final_state;
+        sa.prep = prep_r;
+        sa.seginit = seginit_r;
+        sa.modes = modes_r;
+        sa.reverse = 1;
+        GDN_LAUNCH(kKBwdScan, st, launch_scan(sa, desc->dtype, st));
+        va.seginit = seginit_r;
+    }
+    GDN_LAUNCH(kKBwdReverse, st, launch_reverse(va, desc->dtype, kRecurOut, p.total_segs, vtiles, st));
+    // 4. per-chunk gradients
+    BwdChunkArgs ba;
+    memset(&ba, 0, sizeof(ba));
+    ba.geo = ra.geo;
+    ba.q = q;
+    ba.k = k;
+    ba.v = v;
+    ba.g = g;
+    ba.beta = beta;
+    ba.gam = gam;
+    ba.w = w;
+    ba.u = u;
+    ba.d_o = d_o;
+    ba.hstates = ws + p.o_h;
+    ba.gstates = ws + p.o_gst;
+    ba.dw = reinterpret_cast<float*>(ws + p.o_dw);
+    ba.du = reinterpret_cast<float*>(ws + p.o_du);
+    ba.dk_part = reinterpret_cast<float*>(ws + p.o_dkp);
+    ba.dgam_part = reinterpret_cast<float*>(ws + p.o_dgp);
+    ba.dq = dq;
+    ba.dk = dk;
+    ba.dv = dv;
+    ba.dg = dg;
+    ba.dbeta = dbeta;
+    ba.scale = desc->scale;
+    GDN_LAUNCH(kKBwdGrads, st, launch_bwd_state(ba, desc->dtype, st));
+    GDN_LAUNCH(kKBwdWy, st, launch_bwd_wy(ba, desc->dtype, st));
+    return GDN_OK;
 }
 
 gdn_status gdn_intra_chunk(const gdn_desc* desc, const void* k, const void* v, const float* g,

@@ -1,0 +1,1207 @@
+// gdn_bwd.hip -- backward of the GDN chunked prefill (the pages ask for fwd and bwd entry
+// points; ollai.cn article, "main features", and say the backward "was the hardest part").
+//
+// Reverse mode of the chunk map, derived from the gated delta rule. For a chunk entering
+// with state S, with G = dL/dS' the adjoint of the state leaving it and dO the output
+// gradient (P = L .* Q K^T with the chunk's decay mask, Kt = diag(e^{Gam-gam}) K):
+//   dDelta = P^T dO + Kt G^T
+//   G_in   = e^Gam G + dO^T diag(e^gam) Q - dDelta^T W      (adjoint entering the chunk)
+// G_in is affine in G with the transposed chunk map, so the same CP scheme as the forward
+// splits the serial chain: warmup windows after each sub-sequence, or exact maps composed
+// from the end. The per-chunk gradients then run in parallel over all chunks:
+//   state side (k_bwd_state): Delta = U - W S^T, dQt = dO S, dP = dO U^T - dQt W^T,
+//     dKt = Delta G, dW = -dDelta S  ->  dq, the P and Kt terms of dk and d(gam), dW, dU
+//   WY side (k_bwd_wy): recompute T = (I + A)^{-1}; dT = dW Bk^T + dU Bv^T,
+//     dA = strict_lower(-T^T dT T^T), dBk = T^T dW, dBv = T^T dU  ->  dk, dv, dbeta, and
+//     dg as the in-chunk reverse cumulative sum of d(gam).
+#include "gdn_common.h"
+#include "gdn_kernels.h"
+
+namespace gdn {
+
+namespace {
+
+template <typename T> struct BPad;
+template <> struct BPad<bf16_t> { static constexpr int row = 8, tr = 8; };
+template <> struct BPad<float> { static constexpr int row = 4, tr = 4; };
+
+// ---------------------------------------------------------------------------
+// Reverse adjoint recurrence. RT adjoint rows (value rows, or V + M-hat rows in the
+// exact prepass) per workgroup, one wave per 16 rows; the adjoint lives in registers as
+// fp32 accumulator tiles of G^T, which are a B fragment of G^T.
+template <typename T, int K, int RT>
+struct VCfg {
+    static constexpr int NW = RT / 16;
+    static constexpr int NT = NW * 64;
+    static constexpr bool kTrans = sizeof(T) == 2;  // transposed LDS copies (bf16); fp32 gathers columns
+    static constexpr int VEC = Elem<T>::kVec;
+    static constexpr int LD = K + BPad<T>::row;     // row-major q, k, w  [64][K]
+    static constexpr int LDD = RT + BPad<T>::row;   // row-major dO tile  [64][RT]
+    static constexpr int LDT = 64 + BPad<T>::tr;    // transposed copies  [K or RT][64]
+    static constexpr int LDP = 64 + BPad<T>::row;   // P^T                [64][64]
+    static constexpr int kMat = 64 * LD * (int)sizeof(T);
+    static constexpr int off_q = 0;                                        // Q  (row-major)
+    static constexpr int off_k = off_q + kMat;                             // K  (row-major)
+    static constexpr int off_w = off_k + kMat;                             // W^T (bf16) / W (fp32)
+    static constexpr int kWBytes = kTrans ? K * LDT * (int)sizeof(T) : kMat;
+    static constexpr int off_qt = off_w + kWBytes;                         // (e^gam Q)^T (bf16 only)
+    static constexpr int kQtBytes = kTrans ? K * LDT * (int)sizeof(T) : 0;
+    static constexpr int off_do = off_qt + kQtBytes;                       // dO^T (bf16) / dO (fp32)
+    static constexpr int kDoBytes = kTrans ? RT * LDT * (int)sizeof(T) : 64 * LDD * (int)sizeof(T);
+    static constexpr int off_pm = off_do + kDoBytes;                       // P^T
+    static constexpr int off_gam = off_pm + 64 * LDP * (int)sizeof(T);
+    static constexpr int total = off_gam + 256;
+    static constexpr int NVK = K / VEC;
+    static constexpr int NVD = RT / VEC;
+    static constexpr int IQ = (32 * NVK + NT - 1) / NT;   // q row pairs
+    static constexpr int IK = (64 * NVK + NT - 1) / NT;   // k rows
+    static constexpr int IW = (32 * NVK + NT - 1) / NT;   // w row pairs
+    static constexpr int ID = (32 * NVD + NT - 1) / NT;   // dO row pairs
+};
+
+// (row tile, column tile) of the 64x64 product Q K^T whose transpose P^T is staged: the
+// 10 tiles with r >= j plus the two zero tiles read inside the k32 slices of P^T dO.
+__constant__ int8_t kTriB[12][2] = {{0, 0}, {1, 0}, {1, 1}, {2, 0}, {2, 1}, {2, 2},
+                                    {3, 0}, {3, 1}, {3, 2}, {3, 3}, {0, 1}, {2, 3}};
+
+template <typename T, int K, int RT>
+struct RevRegs {
+    using C = VCfg<T, K, RT>;
+    u32x4 qa[C::IQ], qb[C::IQ];
+    u32x4 k[C::IK];
+    u32x4 wa[C::IW], wb[C::IW];
+    u32x4 da[C::ID], db[C::ID];
+    float gq0[C::IQ], gq1[C::IQ];  // gate cumsum of the q row pair (scales the transposed copy)
+    float gam;
+};
+
+template <typename T, int K, int RT>
+__device__ __forceinline__ void rev_fetch(RevRegs<T, K, RT>& R, const RevArgs& a, int64_t t0, int c, int h,
+                                          int dcol0) {
+    using C = VCfg<T, K, RT>;
+    const int tid = threadIdx.x;
+    const int64_t H = a.geo.H;
+    const T* q = reinterpret_cast<const T*>(a.q);
+    const T* k = reinterpret_cast<const T*>(a.k);
+    const T* w = reinterpret_cast<const T*>(a.w);
+    const T* d_o = reinterpret_cast<const T*>(a.d_o);
+    const u32x4 z = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int it = 0; it < C::IQ; ++it) {
+        const int e = tid + it * C::NT;
+        const int rp = e / C::NVK, cv = e % C::NVK;
+        const bool in = e < 32 * C::NVK;
+        const int r0 = 2 * rp, r1 = 2 * rp + 1;
+        R.qa[it] = (in && r0 < c) ? *reinterpret_cast<const u32x4*>(q + ((t0 + r0) * H + h) * K + cv * C::VEC) : z;
+        R.qb[it] = (in && r1 < c) ? *reinterpret_cast<const u32x4*>(q + ((t0 + r1) * H + h) * K + cv * C::VEC) : z;
+        R.gq0[it] = (in && r0 < c) ? a.gam[(t0 + r0) * H + h] : 0.f;
+        R.gq1[it] = (in && r1 < c) ? a.gam[(t0 + r1) * H + h] : 0.f;
+        R.wa[it] = (in && r0 < c) ? *reinterpret_cast<const u32x4*>(w + ((t0 + r0) * H + h) * K + cv * C::VEC) : z;
+        R.wb[it] = (in && r1 < c) ? *reinterpret_cast<const u32x4*>(w + ((t0 + r1) * H + h) * K + cv * C::VEC) : z;
+    }
+#pragma unroll
+    for (int it = 0; it < C::IK; ++it) {
+        const int e = tid + it * C::NT;
+        const int r = e / C::NVK, cv = e % C::NVK;
+        R.k[it] = (e < 64 * C::NVK && r < c) ? *reinterpret_cast<const u32x4*>(k + ((t0 + r) * H + h) * K + cv * C::VEC)
+                                               : z;
+    }
+#pragma unroll
+    for (int it = 0; it < C::ID; ++it) {
+        const int e = tid + it * C::NT;
+        const int rp = e / C::NVD, cv = e % C::NVD;
+        const bool in = dcol0 >= 0 && e < 32 * C::NVD;
+        const int r0 = 2 * rp, r1 = 2 * rp + 1;
+        const int64_t V = a.geo.V;
+        R.da[it] = (in && r0 < c) ? *reinterpret_cast<const u32x4*>(d_o + ((t0 + r0) * H + h) * V + dcol0 + cv * C::VEC) : z;
+        R.db[it] = (in && r1 < c) ? *reinterpret_cast<const u32x4*>(d_o + ((t0 + r1) * H + h) * V + dcol0 + cv * C::VEC) : z;
+    }
+    if (tid < 64) {
+        const int r = tid < c ? tid : c - 1;
+        R.gam = a.gam[(t0 + r) * H + h];
+    }
+}
+
+// Write a row pair of VEC elements transposed: dst[(col0 + e) * ld + r0 .. r0+1] = (A[e], B[e]) * (s0, s1).
+template <typename T>
+__device__ __forceinline__ void put_pair_t(T* dst, int ld, int col0, int r0, const u32x4& A, const u32x4& B,
+                                           float s0 = 1.f, float s1 = 1.f, bool scaled = false);
+template <>
+__device__ __forceinline__ void put_pair_t(bf16_t* dst, int ld, int col0, int r0, const u32x4& A, const u32x4& B,
+                                           float s0, float s1, bool scaled) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        uint32_t lo = (A[j >> 1] >> ((j & 1) * 16)) & 0xFFFFu;
+        uint32_t hi = (B[j >> 1] >> ((j & 1) * 16)) & 0xFFFFu;
+        if (scaled) {
+            lo = f2bf_bits(bf2f((bf16_t)lo) * s0);
+            hi = f2bf_bits(bf2f((bf16_t)hi) * s1);
+        }
+        *reinterpret_cast<uint32_t*>(dst + (col0 + j) * ld + r0) = lo | (hi << 16);
+    }
+}
+template <>
+__device__ __forceinline__ void put_pair_t(float* dst, int ld, int col0, int r0, const u32x4& A, const u32x4& B,
+                                           float s0, float s1, bool scaled) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        float x = __uint_as_float(A[j]), y = __uint_as_float(B[j]);
+        if (scaled) {
+            x *= s0;
+            y *= s1;
+        }
+        *reinterpret_cast<f32x2*>(dst + (col0 + j) * ld + r0) = f32x2{x, y};
+    }
+}
+
+template <typename T, int K, int RT>
+struct RevLds {
+    T* sQ;
+    T* sK;
+    T* sW;   // W^T (bf16) or W (fp32)
+    T* sQt;  // (e^gam Q)^T (bf16)
+    T* sD;   // dO^T (bf16) or dO (fp32)
+    T* sPm;  // P^T [j][r]
+    float* sGam;
+};
+
+template <typename T, int K, int RT>
+__device__ __forceinline__ void rev_stage(const RevRegs<T, K, RT>& R, const RevLds<T, K, RT>& L, float scale) {
+    using C = VCfg<T, K, RT>;
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int it = 0; it < C::IQ; ++it) {
+        const int e = tid + it * C::NT;
+        if (e < 32 * C::NVK) {
+            const int rp = e / C::NVK, cv = e % C::NVK;
+            const int r0 = 2 * rp;
+            *reinterpret_cast<u32x4*>(L.sQ + r0 * C::LD + cv * C::VEC) = R.qa[it];
+            *reinterpret_cast<u32x4*>(L.sQ + (r0 + 1) * C::LD + cv * C::VEC) = R.qb[it];
+            if constexpr (C::kTrans) {
+                put_pair_t(L.sQt, C::LDT, cv * C::VEC, r0, R.qa[it], R.qb[it], scale * fast_exp(R.gq0[it]),
+                           scale * fast_exp(R.gq1[it]), true);
+                put_pair_t(L.sW, C::LDT, cv * C::VEC, r0, R.wa[it], R.wb[it]);
+            } else {
+                *reinterpret_cast<u32x4*>(L.sW + r0 * C::LD + cv * C::VEC) = R.wa[it];
+                *reinterpret_cast<u32x4*>(L.sW + (r0 + 1) * C::LD + cv * C::VEC) = R.wb[it];
+            }
+        }
+    }
+#pragma unroll
+    for (int it = 0; it < C::IK; ++it) {
+        const int e = tid + it * C::NT;
+        if (e < 64 * C::NVK) {
+            const int r = e / C::NVK, cv = e % C::NVK;
+            *reinterpret_cast<u32x4*>(L.sK + r * C::LD + cv * C::VEC) = R.k[it];
+        }
+    }
+#pragma unroll
+    for (int it = 0; it < C::ID; ++it) {
+        const int e = tid + it * C::NT;
+        if (e < 32 * C::NVD) {
+            const int rp = e / C::NVD, cv = e % C::NVD;
+            const int r0 = 2 * rp;
+            if constexpr (C::kTrans) {
+                put_pair_t(L.sD, C::LDT, cv * C::VEC, r0, R.da[it], R.db[it]);
+            } else {
+                *reinterpret_cast<u32x4*>(L.sD + r0 * C::LDD + cv * C::VEC) = R.da[it];
+                *reinterpret_cast<u32x4*>(L.sD + (r0 + 1) * C::LDD + cv * C::VEC) = R.db[it];
+            }
+        }
+    }
+    if (tid < 64) L.sGam[tid] = R.gam;
+}
+
+// dO^T fragment of value column `col` over chunk rows r0..r0+31 (optionally scaled by e^gam_r).
+template <typename T, int K, int RT>
+__device__ __forceinline__ void do_frag(Frag<T>& f, const RevLds<T, K, RT>& L, int col, int r0) {
+    using C = VCfg<T, K, RT>;
+    if constexpr (C::kTrans)
+        frag_row(f, L.sD, C::LDT, col, r0);
+    else
+        frag_col(f, L.sD, C::LDD, col, r0);
+}
+
+template <typename T, int K, int RT, int MODE>
+__global__ __launch_bounds__(RT * 4) void k_reverse(RevArgs a) {
+    using C = VCfg<T, K, RT>;
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    RevLds<T, K, RT> L;
+    L.sQ = reinterpret_cast<T*>(smem + C::off_q);
+    L.sK = reinterpret_cast<T*>(smem + C::off_k);
+    L.sW = reinterpret_cast<T*>(smem + C::off_w);
+    L.sQt = reinterpret_cast<T*>(smem + C::off_qt);
+    L.sD = reinterpret_cast<T*>(smem + C::off_do);
+    L.sPm = reinterpret_cast<T*>(smem + C::off_pm);
+    L.sGam = reinterpret_cast<float*>(smem + C::off_gam);
+
+    const Geo& geo = a.geo;
+    const int64_t gs = blockIdx.x;
+    const int h = blockIdx.y;
+    const int vt = blockIdx.z;
+    const int V = geo.V;
+    const int64_t H = geo.H;
+    SegLoc sg;
+    if (!locate_seg(geo, gs, sg)) return;
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63, ln = lane & 15, gq = lane >> 4;
+    const int row = vt * RT + wave * 16 + ln;
+    const size_t VK = (size_t)V * K;
+
+    f32x4 accG[K / 16];
+    int cbeg = sg.c0, cend = sg.c1;  // processed from cend-1 down to cbeg
+    int mode = 0;
+    const bool last = sg.s == sg.nseg - 1;
+    if (MODE == kRecurPrepass) {
+        mode = a.modes[sg.n * H + h];
+        if (mode == 1) {
+            // warmup: the W chunks after this segment, from a zero adjoint (or from d(final
+            // state) when the window reaches the sequence end)
+            if (last || vt * RT >= V) return;
+            cbeg = sg.c1;
+            cend = min(sg.c1 + a.warmup, sg.nchunks);
+            if (cend == sg.nchunks && a.dsT)
+                load_state<K>(accG, a.dsT + ((size_t)sg.n * H + h) * VK, row);
+            else
+#pragma unroll
+                for (int kt = 0; kt < K / 16; ++kt) accG[kt] = zero4();
+        } else if (mode == 2) {
+            if (sg.s == 0 || vt * RT >= V + K) return;
+#pragma unroll
+            for (int kt = 0; kt < K / 16; ++kt) {
+                f32x4 z = zero4();
+                if (row >= V) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) z[i] = (kt * 16 + gq * 4 + i == row - V) ? 1.f : 0.f;
+                }
+                accG[kt] = z;
+            }
+        } else {
+            return;
+        }
+    } else {
+        if (!last && a.use_cp) {
+            load_state<K>(accG, a.seginit + ((size_t)gs * H + h) * VK, row);
+        } else if (a.dsT) {
+            load_state<K>(accG, a.dsT + ((size_t)sg.n * H + h) * VK, row);
+        } else {
+#pragma unroll
+            for (int kt = 0; kt < K / 16; ++kt) accG[kt] = zero4();
+        }
+    }
+
+    const bool has_do = vt * RT < V;  // M-hat rows of the exact prepass carry no output gradient
+    const int dcol0 = has_do ? vt * RT : -1;
+    RevRegs<T, K, RT> R;
+    if (cbeg < cend) rev_fetch<T, K, RT>(R, a, sg.bos + (int64_t)(cend - 1) * 64, min(64, sg.len - (cend - 1) * 64), h, dcol0);
+    for (int ci = cend - 1; ci >= cbeg; --ci) {
+        const int64_t t0 = sg.bos + (int64_t)ci * 64;
+        if (MODE == kRecurOut) {
+            // adjoint of the state leaving this chunk
+            T* gs_out = reinterpret_cast<T*>(a.gstates) + ((size_t)(sg.choff + ci) * H + h) * VK + (size_t)row * K;
+#pragma unroll
+            for (int kt = 0; kt < K / 16; ++kt) store4(gs_out + kt * 16 + gq * 4, accG[kt]);
+        }
+        lds_sync();
+        rev_stage<T, K, RT>(R, L, a.scale);
+        lds_sync();
+        if (ci - 1 >= cbeg)
+            rev_fetch<T, K, RT>(R, a, t0 - 64, min(64, sg.len - (ci - 1) * 64), h, dcol0);
+
+        Frag<T> gf[K / 32];
+#pragma unroll
+        for (int kb = 0; kb < K / 32; ++kb) frag_acc(gf[kb], accG[2 * kb], accG[2 * kb + 1]);
+        if (has_do) {
+            // P^T[j][r] = e^{gam_r - gam_j} (Q K^T)[r][j] for r >= j, staged row-major by j
+            for (int idx = wave; idx < 12; idx += C::NW) {
+                const int rt = kTriB[idx][0], jt = kTriB[idx][1];
+                f32x4 acc = zero4();
+#pragma unroll
+                for (int kb = 0; kb < (jt <= rt ? K / 32 : 0); ++kb) {
+                    Frag<T> fa, fb;
+                    frag_row(fa, L.sQ, C::LD, rt * 16 + ln, kb * 32);
+                    frag_row(fb, L.sK, C::LD, jt * 16 + ln, kb * 32);
+                    mma(acc, fa, fb);  // (Q K^T) tile: lane holds [r = rt*16+gq*4+i][j = jt*16+ln]
+                }
+                const int j = jt * 16 + ln;
+                const float gj = L.sGam[j];
+                f32x4 v;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int r = rt * 16 + gq * 4 + i;
+                    v[i] = (r >= j) ? a.scale * acc[i] * fast_exp(L.sGam[r] - gj) : 0.f;
+                }
+                store4(L.sPm + j * C::LDP + rt * 16 + gq * 4, v);
+            }
+        }
+        // dDelta tiles (rows j, columns = the wave's adjoint rows): Kt G^T part
+        const float Gm = L.sGam[63];
+        f32x4 accD[4];
+#pragma unroll
+        for (int jt = 0; jt < 4; ++jt) {
+            accD[jt] = zero4();
+#pragma unroll
+            for (int kb = 0; kb < K / 32; ++kb) {
+                Frag<T> fa;
+                frag_row(fa, L.sK, C::LD, jt * 16 + ln, kb * 32);
+                mma(accD[jt], fa, gf[kb]);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) accD[jt][i] *= fast_exp(Gm - L.sGam[jt * 16 + gq * 4 + i]);
+        }
+        lds_sync();  // P^T complete
+        if (has_do) {
+#pragma unroll
+            for (int jt = 0; jt < 4; ++jt) {
+#pragma unroll
+                for (int rb = (jt >> 1); rb < 2; ++rb) {
+                    Frag<T> fa, fb;
+                    frag_row(fa, L.sPm, C::LDP, jt * 16 + ln, rb * 32);
+                    do_frag<T, K, RT>(fb, L, wave * 16 + ln, rb * 32);
+                    mma(accD[jt], fa, fb);
+                }
+            }
+        }
+        // G^T <- e^Gam G^T + (e^gam Q)^T dO - W^T dDelta
+        const float eG = fast_exp(Gm);
+        Frag<T> ddf[2];
+        frag_acc(ddf[0], accD[0], accD[1], -1.f);
+        frag_acc(ddf[1], accD[2], accD[3], -1.f);
+        Frag<T> dof[2];
+        if (has_do) {
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb) {
+                do_frag<T, K, RT>(dof[rb], L, wave * 16 + ln, rb * 32);
+                if constexpr (!C::kTrans) {
+                    // fp32: fold e^gam_r into the dO slots (bf16 folds it into the staged Q^T)
+                    Frag<float>& f = reinterpret_cast<Frag<float>&>(dof[rb]);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        f.lo[e] *= a.scale * fast_exp(L.sGam[rb * 32 + gq * 4 + e]);
+                        f.hi[e] *= a.scale * fast_exp(L.sGam[rb * 32 + 16 + gq * 4 + e]);
+                    }
+                }
+            }
+        }
+#pragma unroll
+        for (int kt = 0; kt < K / 16; ++kt) {
+            accG[kt] *= eG;
+#pragma unroll
+            for (int jb = 0; jb < 2; ++jb) {
+                Frag<T> fa;
+                if constexpr (C::kTrans)
+                    frag_row(fa, L.sW, C::LDT, kt * 16 + ln, jb * 32);
+                else
+                    frag_col(fa, L.sW, C::LD, kt * 16 + ln, jb * 32);
+                mma(accG[kt], fa, ddf[jb]);
+            }
+            if (has_do) {
+#pragma unroll
+                for (int rb = 0; rb < 2; ++rb) {
+                    Frag<T> fa;
+                    if constexpr (C::kTrans)
+                        frag_row(fa, L.sQt, C::LDT, kt * 16 + ln, rb * 32);
+                    else
+                        frag_col(fa, L.sQ, C::LD, kt * 16 + ln, rb * 32);
+                    mma(accG[kt], fa, dof[rb]);
+                }
+            }
+        }
+    }
+
+    if (MODE == kRecurPrepass) {
+        if (mode == 1) {
+            store_state<K>(accG, a.seginit_out + ((size_t)(gs - 0) * H + h) * VK, row);
+        } else {
+            float* P = a.prep + ((size_t)gs * H + h) * (size_t)(V + K) * K;
+            if (row < V) {
+                store_state<K>(accG, P, row);
+            } else if (row < V + K) {
+                const int i = row - V;
+#pragma unroll
+                for (int kt = 0; kt < K / 16; ++kt)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) P[VK + (size_t)(kt * 16 + gq * 4 + e) * K + i] = accG[kt][e];
+            }
+        }
+    } else if (sg.s == 0 && a.ds0) {
+        store_state<K>(accG, a.ds0 + ((size_t)sg.n * H + h) * VK, row);
+    }
+}
+
+template <typename T, int K, int RT, int MODE>
+hipError_t launch_reverse_t(const RevArgs& a, int64_t nsegs_grid, int vtiles, hipStream_t st) {
+    using C = VCfg<T, K, RT>;
+    static_assert(C::total <= 160 * 1024, "LDS budget");
+    auto kern = k_reverse<T, K, RT, MODE>;
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, C::total);
+    if (e != hipSuccess) return e;
+    dim3 grid((unsigned)nsegs_grid, (unsigned)a.geo.H, (unsigned)vtiles);
+    hipLaunchKernelGGL(kern, grid, dim3(C::NT), C::total, st, a);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// State-side per-chunk gradients. One workgroup (4 waves) per (chunk, head); wave w owns
+// chunk rows r = 16w .. 16w+15. Most tiles are held transposed (rows over k or v,
+// columns over the wave's rows r), which makes them A fragments of their transposes and
+// lets every lane write four consecutive columns of its row with one vector store.
+template <typename T, int K, int V>
+struct SCfg {
+    static constexpr int LDK = K + BPad<T>::row;   // [V][K] states, [64][K] q, k, w
+    static constexpr int LDV = V + BPad<T>::row;   // [64][V] dO
+    static constexpr int LDX = 64 + BPad<T>::row;  // [64][64] exchange of L .* dP
+    static constexpr int off_s = 0;
+    static constexpr int off_g = off_s + V * LDK * (int)sizeof(T);
+    static constexpr int off_q = off_g + V * LDK * (int)sizeof(T);
+    static constexpr int off_k = off_q + 64 * LDK * (int)sizeof(T);
+    static constexpr int off_w = off_k + 64 * LDK * (int)sizeof(T);
+    static constexpr int off_d = off_w + 64 * LDK * (int)sizeof(T);
+    static constexpr int off_x = off_d + 64 * LDV * (int)sizeof(T);
+    static constexpr int off_gam = off_x + 64 * LDX * (int)sizeof(T);
+    static constexpr int off_red = off_gam + 256;          // [4][64] fp32 column partials
+    static constexpr int off_row = off_red + 4 * 64 * 4;   // [64] fp32 row parts
+    static constexpr int off_sc = off_row + 256;           // [8] fp32 scalars
+    static constexpr int total = off_sc + 64;
+};
+
+// Copy `rows` rows x D columns of a row-major global matrix (row stride ld_g elements) into
+// LDS (row stride ld_s), zero past `rows`; 256 threads, 16-byte vectors.
+template <typename T, int D>
+__device__ __forceinline__ void copy_rows(T* dst, int ld_s, const T* src, size_t ld_g, int nrows, int rows) {
+    constexpr int VEC = Elem<T>::kVec;
+    constexpr int NV = D / VEC;
+    for (int e = threadIdx.x; e < nrows * NV; e += 256) {
+        const int r = e / NV, cv = e % NV;
+        u32x4 x = u32x4{0u, 0u, 0u, 0u};
+        if (r < rows) x = *reinterpret_cast<const u32x4*>(src + (size_t)r * ld_g + cv * VEC);
+        *reinterpret_cast<u32x4*>(dst + r * ld_s + cv * VEC) = x;
+    }
+}
+
+// Same, multiplying every element by s (used to fold the query scale into dO).
+template <typename T, int D>
+__device__ __forceinline__ void copy_rows_scaled(T* dst, int ld_s, const T* src, size_t ld_g, int nrows, int rows,
+                                                 float s) {
+    if (s == 1.f) {
+        copy_rows<T, D>(dst, ld_s, src, ld_g, nrows, rows);
+        return;
+    }
+    for (int e = threadIdx.x; e < nrows * D / 4; e += 256) {
+        const int r = e / (D / 4), cv = e % (D / 4);
+        f32x4 x = zero4();
+        if (r < rows) {
+            const T* p = src + (size_t)r * ld_g + cv * 4;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) x[i] = Elem<T>::to_f(p[i]) * s;
+        }
+        store4(dst + r * ld_s + cv * 4, x);
+    }
+}
+
+// Negated copy of a fragment.
+__device__ __forceinline__ Frag<bf16_t> neg(const Frag<bf16_t>& f) {
+    Frag<bf16_t> n;
+    n.v = f.v ^ u32x4{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
+    return n;
+}
+__device__ __forceinline__ Frag<float> neg(const Frag<float>& f) {
+    Frag<float> n;
+    n.lo = -f.lo;
+    n.hi = -f.hi;
+    return n;
+}
+
+// Fragment of row `row` of a global row-major matrix, zero when row >= rows.
+template <typename T>
+__device__ __forceinline__ void frag_row_g(Frag<T>& f, const T* base, size_t ld, int row, int rows, int k0) {
+    if (row < rows) {
+        const int gq = (threadIdx.x & 63) >> 4;
+        const T* p = base + (size_t)row * ld + k0 + gq * 4;
+        if constexpr (sizeof(T) == 2) {
+            const u32x2 a = *reinterpret_cast<const u32x2*>(p);
+            const u32x2 b = *reinterpret_cast<const u32x2*>(p + 16);
+            reinterpret_cast<Frag<bf16_t>&>(f).v = u32x4{a.x, a.y, b.x, b.y};
+        } else {
+            reinterpret_cast<Frag<float>&>(f).lo = *reinterpret_cast<const f32x4*>(p);
+            reinterpret_cast<Frag<float>&>(f).hi = *reinterpret_cast<const f32x4*>(p + 16);
+        }
+    } else {
+        if constexpr (sizeof(T) == 2)
+            reinterpret_cast<Frag<bf16_t>&>(f).v = u32x4{0u, 0u, 0u, 0u};
+        else {
+            reinterpret_cast<Frag<float>&>(f).lo = zero4();
+            reinterpret_cast<Frag<float>&>(f).hi = zero4();
+        }
+    }
+}
+
+// Sum over the four lanes that share ln (lane groups gq = 0..3).
+__device__ __forceinline__ float sum_gq(float x) {
+    x += __shfl_xor(x, 16, 64);
+    x += __shfl_xor(x, 32, 64);
+    return x;
+}
+// Sum over the 16 lanes of one lane group (ln = 0..15).
+__device__ __forceinline__ float sum_ln(float x) {
+    x += __shfl_xor(x, 1, 64);
+    x += __shfl_xor(x, 2, 64);
+    x += __shfl_xor(x, 4, 64);
+    x += __shfl_xor(x, 8, 64);
+    return x;
+}
+
+template <typename T, int K, int V>
+__global__ __launch_bounds__(256) void k_bwd_state(BwdChunkArgs a) {
+    using S = SCfg<T, K, V>;
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    T* sS = reinterpret_cast<T*>(smem + S::off_s);
+    T* sG = reinterpret_cast<T*>(smem + S::off_g);
+    T* sQ = reinterpret_cast<T*>(smem + S::off_q);
+    T* sK = reinterpret_cast<T*>(smem + S::off_k);
+    T* sW = reinterpret_cast<T*>(smem + S::off_w);
+    T* sD = reinterpret_cast<T*>(smem + S::off_d);
+    T* sX = reinterpret_cast<T*>(smem + S::off_x);
+    float* sGam = reinterpret_cast<float*>(smem + S::off_gam);
+    float* sRed = reinterpret_cast<float*>(smem + S::off_red);
+    float* sRow = reinterpret_cast<float*>(smem + S::off_row);
+    float* sSc = reinterpret_cast<float*>(smem + S::off_sc);
+
+    const Geo& geo = a.geo;
+    const int64_t gc = blockIdx.x;
+    const int h = blockIdx.y;
+    ChunkLoc L;
+    if (!locate_chunk(geo, gc, L)) return;
+    const int64_t H = geo.H;
+    const int c = L.c;
+    const int64_t t0 = L.t0;
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63, ln = lane & 15, gq = lane >> 4;
+    const int r = wave * 16 + ln;  // this lane's chunk row in "column" roles
+    const size_t VK = (size_t)V * K;
+
+    // ---- stage operands -------------------------------------------------------------
+    copy_rows<T, K>(sS, S::LDK, reinterpret_cast<const T*>(a.hstates) + ((size_t)gc * H + h) * VK, K, V, V);
+    copy_rows<T, K>(sG, S::LDK, reinterpret_cast<const T*>(a.gstates) + ((size_t)gc * H + h) * VK, K, V, V);
+    copy_rows<T, K>(sQ, S::LDK, reinterpret_cast<const T*>(a.q) + (t0 * H + h) * K, (size_t)H * K, 64, c);
+    copy_rows<T, K>(sK, S::LDK, reinterpret_cast<const T*>(a.k) + (t0 * H + h) * K, (size_t)H * K, 64, c);
+    copy_rows<T, K>(sW, S::LDK, reinterpret_cast<const T*>(a.w) + (t0 * H + h) * K, (size_t)H * K, 64, c);
+    // dO enters every product together with the query scale (o = scale S q)
+    copy_rows_scaled<T, V>(sD, S::LDV, reinterpret_cast<const T*>(a.d_o) + (t0 * H + h) * V, (size_t)H * V, 64, c,
+                           a.scale);
+    if (tid < 64) sGam[tid] = a.gam[(t0 + (tid < c ? tid : c - 1)) * H + h];
+    lds_sync();
+
+    const float Gm = sGam[63];
+    const float gr = sGam[r];
+    const T* ug = reinterpret_cast<const T*>(a.u) + (t0 * H + h) * V;  // U rows of this chunk
+    const size_t ldu = (size_t)H * V;
+
+    // ---- P tiles with the wave's rows as keys: PmK[jt] = P^T restricted (rows j, cols r) --
+    f32x4 PmK[4];
+#pragma unroll
+    for (int jt = 0; jt < 4; ++jt) {
+        PmK[jt] = zero4();
+        if (jt >= wave) {
+#pragma unroll
+            for (int kb = 0; kb < K / 32; ++kb) {
+                Frag<T> fa, fb;
+                frag_row(fa, sQ, S::LDK, jt * 16 + ln, kb * 32);
+                frag_row(fb, sK, S::LDK, r, kb * 32);
+                mma(PmK[jt], fa, fb);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int j = jt * 16 + gq * 4 + i;
+            PmK[jt][i] = (j >= r) ? PmK[jt][i] * fast_exp(sGam[j] - gr) : 0.f;
+        }
+    }
+    // ---- Delta^T[v][r] = U[r][v] - (S W^T)[v][r];  dDelta^T = dO^T P + G K~^T ------------
+    f32x4 DT[V / 16], DDT[V / 16];
+    Frag<T> wr[K / 32], kr[K / 32];
+#pragma unroll
+    for (int kb = 0; kb < K / 32; ++kb) {
+        Frag<T> f;
+        frag_row(f, sW, S::LDK, r, kb * 32);
+        wr[kb] = neg(f);
+        frag_row(kr[kb], sK, S::LDK, r, kb * 32);
+    }
+    const float ekt = fast_exp(Gm - gr);
+#pragma unroll
+    for (int vt = 0; vt < V / 16; ++vt) {
+        f32x4 u0 = zero4();
+        if (r < c) {
+            const T* up = ug + (size_t)r * ldu + vt * 16 + gq * 4;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) u0[i] = Elem<T>::to_f(up[i]);
+        }
+        DT[vt] = u0;
+        DDT[vt] = zero4();
+#pragma unroll
+        for (int kb = 0; kb < K / 32; ++kb) {
+            Frag<T> fs, fg;
+            frag_row(fs, sS, S::LDK, vt * 16 + ln, kb * 32);
+            mma(DT[vt], fs, wr[kb]);
+            frag_row(fg, sG, S::LDK, vt * 16 + ln, kb * 32);
+            mma(DDT[vt], fg, kr[kb]);
+        }
+        DDT[vt] *= ekt;
+#pragma unroll
+        for (int jb = 0; jb < 2; ++jb) {
+            Frag<T> fd, fp;
+            frag_col(fd, sD, S::LDV, vt * 16 + ln, jb * 32);  // dO^T row v, slots j
+            frag_acc(fp, PmK[2 * jb], PmK[2 * jb + 1]);
+            mma(DDT[vt], fd, fp);
+        }
+    }
+    // ---- dQt^T, dW^T = -(S^T dDelta^T), dKt^T = G^T Delta^T  (rows k, cols r) ---------
+    f32x4 dQT[K / 16], dWT[K / 16], dKT[K / 16];
+    Frag<T> dor[V / 32], ddf[V / 32], dtf[V / 32];
+#pragma unroll
+    for (int vb = 0; vb < V / 32; ++vb) {
+        frag_row(dor[vb], sD, S::LDV, r, vb * 32);
+        frag_acc(ddf[vb], DDT[2 * vb], DDT[2 * vb + 1], -1.f);
+        frag_acc(dtf[vb], DT[2 * vb], DT[2 * vb + 1]);
+    }
+#pragma unroll
+    for (int kt = 0; kt < K / 16; ++kt) {
+        dQT[kt] = zero4();
+        dWT[kt] = zero4();
+        dKT[kt] = zero4();
+#pragma unroll
+        for (int vb = 0; vb < V / 32; ++vb) {
+            Frag<T> fs, fg;
+            frag_col(fs, sS, S::LDK, kt * 16 + ln, vb * 32);  // S^T row k, slots v
+            mma(dQT[kt], fs, dor[vb]);
+            mma(dWT[kt], fs, ddf[vb]);
+            frag_col(fg, sG, S::LDK, kt * 16 + ln, vb * 32);  // G^T row k, slots v
+            mma(dKT[kt], fg, dtf[vb]);
+        }
+    }
+    // ---- dP^T[j][r] = (U dO^T)[j][r] - (W dQt^T)[j][r];  P with the wave's rows as queries --
+    f32x4 dPT[4], PmQ[4];
+    Frag<T> dqf[K / 32];
+#pragma unroll
+    for (int kb = 0; kb < K / 32; ++kb) frag_acc(dqf[kb], dQT[2 * kb], dQT[2 * kb + 1], -1.f);
+    Frag<T> qr[K / 32];
+#pragma unroll
+    for (int kb = 0; kb < K / 32; ++kb) frag_row(qr[kb], sQ, S::LDK, r, kb * 32);
+#pragma unroll
+    for (int jt = 0; jt < 4; ++jt) {
+        dPT[jt] = zero4();
+        PmQ[jt] = zero4();
+        if (jt <= wave) {
+#pragma unroll
+            for (int vb = 0; vb < V / 32; ++vb) {
+                Frag<T> fu;
+                frag_row_g(fu, ug, ldu, jt * 16 + ln, c, vb * 32);
+                mma(dPT[jt], fu, dor[vb]);
+            }
+#pragma unroll
+            for (int kb = 0; kb < K / 32; ++kb) {
+                Frag<T> fw, fk;
+                frag_row(fw, sW, S::LDK, jt * 16 + ln, kb * 32);
+                mma(dPT[jt], fw, dqf[kb]);
+                frag_row(fk, sK, S::LDK, jt * 16 + ln, kb * 32);
+                mma(PmQ[jt], fk, qr[kb]);
+            }
+        }
+    }
+    // mask, decay, the P terms of d(gam), and L .* dP
+    float drow = 0.f;  // d(gam_r) terms accumulated in this lane (summed over gq below)
+    f32x4 LdP[4];
+#pragma unroll
+    for (int jt = 0; jt < 4; ++jt) {
+        f32x4 colpart;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int j = jt * 16 + gq * 4 + i;
+            const float e = (j <= r) ? fast_exp(gr - sGam[j]) : 0.f;
+            const float p = PmQ[jt][i] * e;
+            const float x = dPT[jt][i] * p;  // dP .* P at (query r, key j)
+            drow += x;
+            colpart[i] = x;
+            LdP[jt][i] = dPT[jt][i] * e;
+        }
+        // column sums over the wave's 16 query rows -> key j
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float s = sum_ln(colpart[i]);
+            if (ln == 0) sRed[wave * 64 + jt * 16 + gq * 4 + i] = -s;
+        }
+    }
+    // d(gam_r) += e^{gam_r} sum_k dQt[r][k] Q[r][k]
+    const float egr = fast_exp(gr);
+    {
+        float acc = 0.f;
+#pragma unroll
+        for (int kt = 0; kt < K / 16; ++kt) {
+            const T* qp = sQ + r * S::LDK + kt * 16 + gq * 4;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc += dQT[kt][i] * Elem<T>::to_f(qp[i]);
+        }
+        drow += egr * acc;
+    }
+    // dq^T = e^{gam_r} dQt^T + K^T (L .* dP)^T
+    Frag<T> lf[2];
+    frag_acc(lf[0], LdP[0], LdP[1]);
+    frag_acc(lf[1], LdP[2], LdP[3]);
+    {
+        T* dq = reinterpret_cast<T*>(a.dq) + ((t0 + r) * H + h) * K;
+#pragma unroll
+        for (int kt = 0; kt < K / 16; ++kt) {
+            f32x4 acc = dQT[kt] * egr;
+#pragma unroll
+            for (int jb = 0; jb < 2; ++jb) {
+                Frag<T> fk;
+                frag_col(fk, sK, S::LDK, kt * 16 + ln, jb * 32);  // K^T row k, slots j
+                mma(acc, fk, lf[jb]);
+            }
+            if (r < c) store4(dq + kt * 16 + gq * 4, acc);
+        }
+    }
+    // exchange L .* dP: sX[key j][query r] = (L .* dP)[r][j]
+#pragma unroll
+    for (int jt = 0; jt < 4; ++jt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sX[(jt * 16 + gq * 4 + i) * S::LDX + r] = Elem<T>::from_f(LdP[jt][i]);
+    // d(gam) from Kt: -e^{Gam-gam_r} sum_k dKt[r][k] K[r][k]; the chunk total gets the sum
+    float ktk = 0.f;
+#pragma unroll
+    for (int kt = 0; kt < K / 16; ++kt) {
+        const T* kp = sK + r * S::LDK + kt * 16 + gq * 4;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ktk += dKT[kt][i] * Elem<T>::to_f(kp[i]);
+    }
+    ktk *= ekt;
+    drow -= ktk;
+    // e^Gam <G, S> over the whole state (each thread a slice)
+    float gs = 0.f;
+    for (int e = tid; e < V * K; e += 256) {
+        const int vv = e / K, kk = e % K;
+        gs += Elem<T>::to_f(sG[vv * S::LDK + kk]) * Elem<T>::to_f(sS[vv * S::LDK + kk]);
+    }
+    {
+        float t = ktk;  // one value per (r, gq); summed over all lanes it is sum_r
+        t = sum_gq(t);
+        t = sum_ln(t);
+        gs = sum_gq(sum_ln(gs));
+        if (lane == 0) {
+            sSc[wave] = t;
+            sSc[4 + wave] = gs;
+        }
+    }
+    drow = sum_gq(drow);
+    if (gq == 0) sRow[r] = drow;
+    lds_sync();
+    // dk part for the wave's rows as keys: e^{Gam-gam_r} dKt^T + Q^T (L .* dP)[:, r]
+    {
+        Frag<T> xf[2];
+        frag_row(xf[0], sX, S::LDX, r, 0);
+        frag_row(xf[1], sX, S::LDX, r, 32);
+        float* dkp = a.dk_part + ((t0 + r) * H + h) * K;
+        float* dwp = a.dw + ((t0 + r) * H + h) * K;
+#pragma unroll
+        for (int kt = 0; kt < K / 16; ++kt) {
+            f32x4 acc = dKT[kt] * ekt;
+#pragma unroll
+            for (int yb = 0; yb < 2; ++yb) {
+                Frag<T> fq;
+                frag_col(fq, sQ, S::LDK, kt * 16 + ln, yb * 32);  // Q^T row k, slots y
+                mma(acc, fq, xf[yb]);
+            }
+            if (r < c) {
+                *reinterpret_cast<f32x4*>(dkp + kt * 16 + gq * 4) = acc;
+                *reinterpret_cast<f32x4*>(dwp + kt * 16 + gq * 4) = dWT[kt];
+            }
+        }
+        float* dup = a.du + ((t0 + r) * H + h) * V;
+        if (r < c) {
+#pragma unroll
+            for (int vt = 0; vt < V / 16; ++vt) *reinterpret_cast<f32x4*>(dup + vt * 16 + gq * 4) = DDT[vt];
+        }
+    }
+    if (tid < 64) {
+        float d = sRow[tid] + sRed[tid] + sRed[64 + tid] + sRed[128 + tid] + sRed[192 + tid];
+        if (tid == c - 1) {
+            const float kt_all = sSc[0] + sSc[1] + sSc[2] + sSc[3];
+            const float gs_all = sSc[4] + sSc[5] + sSc[6] + sSc[7];
+            d += kt_all + fast_exp(Gm) * gs_all;
+        }
+        if (tid < c) a.dgam_part[(t0 + tid) * H + h] = d;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// WY-side per-chunk gradients. One workgroup (4 waves) per (chunk, head); wave w owns rows
+// a = 16w .. 16w+15. Recomputes A and T = (I + A)^{-1} as the intra-chunk kernel does.
+template <typename T, int K, int V>
+struct WCfg {
+    static constexpr int LDK = K + BPad<T>::row;
+    static constexpr int LDV = V + BPad<T>::row;
+    static constexpr int kF = 64 * kLdA * 4;  // one fp32 64x64 matrix
+    static constexpr int off_k = 0;
+    static constexpr int off_v = off_k + 64 * LDK * (int)sizeof(T);
+    static constexpr int off_dw = off_v + 64 * LDV * (int)sizeof(T);
+    static constexpr int off_du = off_dw + 64 * LDK * (int)sizeof(T);
+    static constexpr int off_ar = off_du + 64 * LDV * (int)sizeof(T);  // e^{gam_a-gam_c} k_a.k_c (strict lower)
+    static constexpr int off_t = off_ar + kF;                           // T
+    static constexpr int off_r1 = off_t + kF;                           // A, then dT, then Mx
+    static constexpr int off_r2 = off_r1 + kF;                          // dT T^T
+    static constexpr int off_gam = off_r2 + kF;
+    static constexpr int off_beta = off_gam + 256;
+    static constexpr int off_red = off_beta + 256;  // [4][64]
+    static constexpr int off_row = off_red + 4 * 64 * 4;
+    static constexpr int total = off_row + 256;
+};
+
+// fp32 LDS column fragment converted to the operand type.
+template <typename T>
+__device__ __forceinline__ void frag_col_f32(Frag<T>& f, const float* base, int ld, int col, int k0) {
+    Frag<float> x;
+    frag_col(x, base, ld, col, k0);
+    if constexpr (sizeof(T) == 2) {
+        reinterpret_cast<Frag<bf16_t>&>(f).v =
+            u32x4{pack_bf2(x.lo.x, x.lo.y), pack_bf2(x.lo.z, x.lo.w), pack_bf2(x.hi.x, x.hi.y), pack_bf2(x.hi.z, x.hi.w)};
+    } else {
+        reinterpret_cast<Frag<float>&>(f) = x;
+    }
+}
+
+// fp32 LDS row fragment converted to the operand type.
+template <typename T>
+__device__ __forceinline__ void frag_row_f32cvt(Frag<T>& f, const float* base, int ld, int row, int k0) {
+    Frag<float> x;
+    frag_row(x, base, ld, row, k0);
+    if constexpr (sizeof(T) == 2) {
+        reinterpret_cast<Frag<bf16_t>&>(f).v =
+            u32x4{pack_bf2(x.lo.x, x.lo.y), pack_bf2(x.lo.z, x.lo.w), pack_bf2(x.hi.x, x.hi.y), pack_bf2(x.hi.z, x.hi.w)};
+    } else {
+        reinterpret_cast<Frag<float>&>(f) = x;
+    }
+}
+
+// fp32 rows [64][D] from global into LDS in the operand type.
+template <typename T, int D>
+__device__ __forceinline__ void copy_rows_f32(T* dst, int ld_s, const float* src, size_t ld_g, int rows) {
+    constexpr int NV = D / 4;
+    for (int e = threadIdx.x; e < 64 * NV; e += 256) {
+        const int r = e / NV, cv = e % NV;
+        f32x4 x = zero4();
+        if (r < rows) x = *reinterpret_cast<const f32x4*>(src + (size_t)r * ld_g + cv * 4);
+        store4(dst + r * ld_s + cv * 4, x);
+    }
+}
+
+template <typename T, int K, int V>
+__global__ __launch_bounds__(256) void k_bwd_wy(BwdChunkArgs a) {
+    using S = WCfg<T, K, V>;
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    T* sK = reinterpret_cast<T*>(smem + S::off_k);
+    T* sV = reinterpret_cast<T*>(smem + S::off_v);
+    T* sdW = reinterpret_cast<T*>(smem + S::off_dw);
+    T* sdU = reinterpret_cast<T*>(smem + S::off_du);
+    float* sAr = reinterpret_cast<float*>(smem + S::off_ar);
+    float* sT = reinterpret_cast<float*>(smem + S::off_t);
+    float* sR1 = reinterpret_cast<float*>(smem + S::off_r1);
+    float* sR2 = reinterpret_cast<float*>(smem + S::off_r2);
+    float* sGam = reinterpret_cast<float*>(smem + S::off_gam);
+    float* sBeta = reinterpret_cast<float*>(smem + S::off_beta);
+    float* sRed = reinterpret_cast<float*>(smem + S::off_red);
+    float* sRow = reinterpret_cast<float*>(smem + S::off_row);
+
+    const Geo& geo = a.geo;
+    const int64_t gc = blockIdx.x;
+    const int h = blockIdx.y;
+    ChunkLoc L;
+    if (!locate_chunk(geo, gc, L)) return;
+    const int64_t H = geo.H;
+    const int c = L.c;
+    const int64_t t0 = L.t0;
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63, ln = lane & 15, gq = lane >> 4;
+    const int ra = wave * 16 + ln;  // this lane's row a in "column" roles
+
+    copy_rows<T, K>(sK, S::LDK, reinterpret_cast<const T*>(a.k) + (t0 * H + h) * K, (size_t)H * K, 64, c);
+    copy_rows<T, V>(sV, S::LDV, reinterpret_cast<const T*>(a.v) + (t0 * H + h) * V, (size_t)H * V, 64, c);
+    copy_rows_f32<T, K>(sdW, S::LDK, a.dw + (t0 * H + h) * K, (size_t)H * K, c);
+    copy_rows_f32<T, V>(sdU, S::LDV, a.du + (t0 * H + h) * V, (size_t)H * V, c);
+    if (tid < 64) {
+        const bool in = tid < c;
+        sGam[tid] = a.gam[(t0 + (in ? tid : c - 1)) * H + h];
+        sBeta[tid] = in ? a.beta[(t0 + tid) * H + h] : 0.f;
+    }
+    lds_sync();
+
+    // ---- A (for the inverse) and e^{gam_a - gam_c} k_a.k_c -------------------------------
+    for (int idx = wave; idx < 10; idx += 4) {
+        const int ti = kTriB[idx][0], tj = kTriB[idx][1];
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int kb = 0; kb < K / 32; ++kb) {
+            Frag<T> fa, fb;
+            frag_row(fa, sK, S::LDK, ti * 16 + ln, kb * 32);
+            frag_row(fb, sK, S::LDK, tj * 16 + ln, kb * 32);
+            mma(acc, fb, fa);  // rows j = tj*16.., cols i = ti*16+ln: lane holds (KK)[i][j]
+        }
+        const int i = ti * 16 + ln;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int j = tj * 16 + gq * 4 + e;
+            const float ar = (j < i) ? fast_exp(sGam[i] - sGam[j]) * acc[e] : 0.f;
+            sAr[i * kLdA + j] = ar;
+            sR1[i * kLdA + j] = sBeta[i] * ar;
+        }
+    }
+    lds_sync();
+    tri_inverse64(sR1, sT);
+
+    // ---- dT[a][b] = beta_b e^{gam_b} (dW K^T)[a][b] + beta_b (dU V^T)[a][b], b < a part ----
+    f32x4 dT[4];
+    {
+        Frag<T> wf[K / 32], uf[V / 32];
+#pragma unroll
+        for (int kb = 0; kb < K / 32; ++kb) frag_row(wf[kb], sdW, S::LDK, ra, kb * 32);
+#pragma unroll
+        for (int vb = 0; vb < V / 32; ++vb) frag_row(uf[vb], sdU, S::LDV, ra, vb * 32);
+#pragma unroll
+        for (int bt = 0; bt < 4; ++bt) {
+            f32x4 x = zero4(), y = zero4();
+            if (bt <= wave) {
+#pragma unroll
+                for (int kb = 0; kb < K / 32; ++kb) {
+                    Frag<T> fk;
+                    frag_row(fk, sK, S::LDK, bt * 16 + ln, kb * 32);
+                    mma(x, fk, wf[kb]);  // rows b, cols a: (K dW^T)[b][a]
+                }
+#pragma unroll
+                for (int vb = 0; vb < V / 32; ++vb) {
+                    Frag<T> fv;
+                    frag_row(fv, sV, S::LDV, bt * 16 + ln, vb * 32);
+                    mma(y, fv, uf[vb]);
+                }
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int b = bt * 16 + gq * 4 + e;
+                dT[bt][e] = (b < ra) ? sBeta[b] * (fast_exp(sGam[b]) * x[e] + y[e]) : 0.f;
+            }
+        }
+    }
+    // stage dT (row a, column b) over A, which the inverse no longer needs
+#pragma unroll
+    for (int bt = 0; bt < 4; ++bt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sR1[ra * kLdA + bt * 16 + gq * 4 + e] = dT[bt][e];
+    lds_sync();
+    // ---- Y = dT T^T (fp32): Y[a][c] = sum_b dT[a][b] T[c][b] ---------------------------------
+    {
+        Frag<float> da[2];
+        frag_row(da[0], sR1, kLdA, ra, 0);
+        frag_row(da[1], sR1, kLdA, ra, 32);
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) {
+            f32x4 y = zero4();
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                Frag<float> ft;
+                frag_row(ft, sT, kLdA, ct * 16 + ln, kb * 32);
+                mma(y, ft, da[kb]);  // rows c, cols a: Y^T
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sR2[ra * kLdA + ct * 16 + gq * 4 + e] = y[e];
+        }
+    }
+    lds_sync();
+    // ---- dA[a][c] = -sum_x T[x][a] Y[x][c], strict lower; its consumers ----------------------
+    float dbeta_row = 0.f, dgam_row = 0.f;
+    {
+        Frag<float> ta[2];
+        frag_col(ta[0], sT, kLdA, ra, 0);   // T^T row a, slots x
+        frag_col(ta[1], sT, kLdA, ra, 32);
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) {
+            f32x4 d = zero4();
+            if (ct <= wave) {
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb) {
+                    Frag<float> fy;
+                    frag_col(fy, sR2, kLdA, ct * 16 + ln, kb * 32);  // Y^T row c, slots x
+                    mma(d, fy, ta[kb]);  // rows c, cols a: (T^T Y)^T
+                }
+            }
+            f32x4 colpart;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int cc = ct * 16 + gq * 4 + e;
+                const float dA = (cc < ra) ? -d[e] : 0.f;
+                const float ar = (cc < ra) ? sAr[ra * kLdA + cc] : 0.f;  // upper blocks never written
+                const float av = sBeta[ra] * ar;  // A[a][c]
+                dbeta_row += dA * ar;
+                dgam_row += dA * av;
+                colpart[e] = dA * av;
+                d[e] = dA * sBeta[ra] * ((cc < ra) ? fast_exp(sGam[ra] - sGam[cc]) : 0.f);  // Mx[a][c]
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float s = sum_ln(colpart[e]);
+                if (ln == 0) sRed[wave * 64 + ct * 16 + gq * 4 + e] = -s;
+            }
+            // Mx[a][c] staged in R1: dT was consumed by Y, and R2 (Y) is still being read
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sR1[ra * kLdA + ct * 16 + gq * 4 + e] = d[e];
+        }
+    }
+    lds_sync();
+    // ---- dBk^T = dW^T T, dBv^T = dU^T T (rows k / v, cols a);  dK, dV --------------------
+    Frag<T> tcol[2];
+    frag_col_f32(tcol[0], sT, kLdA, ra, 0);  // T column a, slots x
+    frag_col_f32(tcol[1], sT, kLdA, ra, 32);
+    Frag<T> mrow[2], mcol[2];
+    frag_row_f32cvt(mrow[0], sR1, kLdA, ra, 0);  // Mx row a, slots c
+    frag_row_f32cvt(mrow[1], sR1, kLdA, ra, 32);
+    frag_col_f32(mcol[0], sR1, kLdA, ra, 0);     // Mx column a, slots c
+    frag_col_f32(mcol[1], sR1, kLdA, ra, 32);
+    const float ba = sBeta[ra], ega = fast_exp(sGam[ra]);
+    {
+        T* dkp = reinterpret_cast<T*>(a.dk) + ((t0 + ra) * H + h) * K;
+        const float* dkq = a.dk_part + ((t0 + ra) * H + h) * K;
+#pragma unroll
+        for (int kt = 0; kt < K / 16; ++kt) {
+            f32x4 bk = zero4(), mk = zero4();
+#pragma unroll
+            for (int xb = 0; xb < 2; ++xb) {
+                Frag<T> fw, fk;
+                frag_col(fw, sdW, S::LDK, kt * 16 + ln, xb * 32);  // dW^T row k, slots x
+                mma(bk, fw, tcol[xb]);
+                frag_col(fk, sK, S::LDK, kt * 16 + ln, xb * 32);   // K^T row k, slots c
+                mma(mk, fk, mrow[xb]);
+                mma(mk, fk, mcol[xb]);
+            }
+            // dbeta, dgam from Bk = diag(beta e^gam) K
+            const T* kr = sK + ra * S::LDK + kt * 16 + gq * 4;
+            float s = 0.f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) s += bk[e] * Elem<T>::to_f(kr[e]);
+            dbeta_row += ega * s;
+            dgam_row += ba * ega * s;
+            if (ra < c) {
+                const f32x4 part = *reinterpret_cast<const f32x4*>(dkq + kt * 16 + gq * 4);
+                store4(dkp + kt * 16 + gq * 4, part + mk + bk * (ba * ega));
+            }
+        }
+    }
+    {
+        T* dvp = reinterpret_cast<T*>(a.dv) + ((t0 + ra) * H + h) * V;
+#pragma unroll
+        for (int vt = 0; vt < V / 16; ++vt) {
+            f32x4 bv = zero4();
+#pragma unroll
+            for (int xb = 0; xb < 2; ++xb) {
+                Frag<T> fu;
+                frag_col(fu, sdU, S::LDV, vt * 16 + ln, xb * 32);  // dU^T row v, slots x
+                mma(bv, fu, tcol[xb]);
+            }
+            const T* vr = sV + ra * S::LDV + vt * 16 + gq * 4;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dbeta_row += bv[e] * Elem<T>::to_f(vr[e]);
+            if (ra < c) store4(dvp + vt * 16 + gq * 4, bv * ba);
+        }
+    }
+    dbeta_row = sum_gq(dbeta_row);
+    dgam_row = sum_gq(dgam_row);
+    if (gq == 0) sRow[ra] = dgam_row;
+    if (gq == 0 && ra < c) a.dbeta[(t0 + ra) * H + h] = dbeta_row;
+    lds_sync();
+    // ---- d(gam) total and dg = reverse cumulative sum within the chunk -------------------
+    if (wave == 0) {
+        float d = 0.f;
+        if (lane < c)
+            d = a.dgam_part[(t0 + lane) * H + h] + sRow[lane] + sRed[lane] + sRed[64 + lane] + sRed[128 + lane] +
+                sRed[192 + lane];
+        // suffix sum over lanes lane..63
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const float y = __shfl_down(d, off, 64);
+            if (lane + off < 64) d += y;
+        }
+        if (lane < c) a.dg[(t0 + lane) * H + h] = d;
+    }
+}
+
+template <typename T, int K, int V>
+hipError_t launch_bwd_state_t(const BwdChunkArgs& a, hipStream_t st) {
+    using S = SCfg<T, K, V>;
+    static_assert(S::total <= 160 * 1024, "LDS budget");
+    auto kern = k_bwd_state<T, K, V>;
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, S::total);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kern, dim3((unsigned)a.geo.total_chunks, (unsigned)a.geo.H), dim3(256), S::total, st, a);
+    return hipGetLastError();
+}
+
+template <typename T, int K, int V>
+hipError_t launch_bwd_wy_t(const BwdChunkArgs& a, hipStream_t st) {
+    using S = WCfg<T, K, V>;
+    static_assert(S::total <= 160 * 1024, "LDS budget");
+    auto kern = k_bwd_wy<T, K, V>;
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, S::total);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kern, dim3((unsigned)a.geo.total_chunks, (unsigned)a.geo.H), dim3(256), S::total, st, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_reverse(const RevArgs& a, int dtype, int mode, int64_t nsegs_grid, int vtiles, hipStream_t st) {
+    if (nsegs_grid == 0) return hipSuccess;
+    const int K = a.geo.K;
+    const int RT = recur_rows(a.geo.V, K);
+#define GDN_REV_CASE(TT, KK, RR)                                                                          \
+    if (K == KK && RT == RR) {                                                                            \
+        if (mode == kRecurOut) return launch_reverse_t<TT, KK, RR, kRecurOut>(a, nsegs_grid, vtiles, st);  \
+        if (mode == kRecurPrepass) return launch_reverse_t<TT, KK, RR, kRecurPrepass>(a, nsegs_grid, vtiles, st); \
+    }
+    if (dtype == 0) {
+        GDN_REV_CASE(bf16_t, 64, 64)
+        GDN_REV_CASE(bf16_t, 128, 64)
+        GDN_REV_CASE(bf16_t, 128, 128)
+    } else {
+        GDN_REV_CASE(float, 64, 64)
+        GDN_REV_CASE(float, 128, 64)
+    }
+#undef GDN_REV_CASE
+    return hipErrorInvalidValue;
+}
+
+
+#define GDN_BWD_CASES(FN)                                        \
+    if (dtype == 0) {                                            \
+        if (K == 64 && V == 64) return FN<bf16_t, 64, 64>(a, st);    \
+        if (K == 64 && V == 128) return FN<bf16_t, 64, 128>(a, st);  \
+        if (K == 128 && V == 64) return FN<bf16_t, 128, 64>(a, st);  \
+        if (K == 128 && V == 128) return FN<bf16_t, 128, 128>(a, st); \
+    } else {                                                     \
+        if (K == 64 && V == 64) return FN<float, 64, 64>(a, st);     \
+    }
+
+hipError_t launch_bwd_state(const BwdChunkArgs& a, int dtype, hipStream_t st) {
+    if (a.geo.total_chunks == 0) return hipSuccess;
+    const int K = a.geo.K, V = a.geo.V;
+    GDN_BWD_CASES(launch_bwd_state_t)
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_bwd_wy(const BwdChunkArgs& a, int dtype, hipStream_t st) {
+    if (a.geo.total_chunks == 0) return hipSuccess;
+    const int K = a.geo.K, V = a.geo.V;
+    GDN_BWD_CASES(launch_bwd_wy_t)
+    return hipErrorInvalidValue;
+}
+#undef GDN_BWD_CASES
+
+}  // namespace gdn

@@ -182,6 +182,90 @@ struct SeqInfo {
 };
 
 // ---------------------------------------------------------------------------
+// T = (I + A)^{-1} for a 64x64 strictly lower triangular fp32 A in LDS (leading dimension
+// kLdA), written to T in LDS; 256-thread workgroups. Diagonal 16x16 blocks by forward
+// substitution (wave b, lanes 0..15 = the columns of block b), the strictly upper blocks
+// zeroed, then the off-diagonal blocks level by level (T_ij = -T_ii sum_m A_im T_mj) with
+// fp32 matrix-core products. Starts and ends with the LDS in a consistent state for the
+// whole workgroup (the caller's barrier before, this routine's last barrier after).
+constexpr int kLdA = 68;
+
+// Y = sum_{m=j}^{i-1} A_{i,m} T_{m,j}; T_{i,j} = -T_{i,i} Y   (16x16 blocks, fp32 matrix cores)
+__device__ __forceinline__ void tri_offdiag_block(float* sA, float* sT, int i, int j) {
+    const int lane = threadIdx.x & 63;
+    const int ln = lane & 15, gq = lane >> 4;
+    f32x4 y = zero4();
+    for (int m = j; m < i; ++m) {
+        const f32x4 a = *reinterpret_cast<const f32x4*>(sA + (16 * i + ln) * kLdA + 16 * m + 4 * gq);
+        f32x4 b;
+        b.x = sT[(16 * m + 4 * gq + 0) * kLdA + 16 * j + ln];
+        b.y = sT[(16 * m + 4 * gq + 1) * kLdA + 16 * j + ln];
+        b.z = sT[(16 * m + 4 * gq + 2) * kLdA + 16 * j + ln];
+        b.w = sT[(16 * m + 4 * gq + 3) * kLdA + 16 * j + ln];
+        mma_f32_k16(y, a, b);
+    }
+    // y[s] = Y[4*gq + s][ln] is a B operand as is.
+    const f32x4 a = *reinterpret_cast<const f32x4*>(sT + (16 * i + ln) * kLdA + 16 * i + 4 * gq);
+    f32x4 r = zero4();
+    mma_f32_k16(r, a, y);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) sT[(16 * i + 4 * gq + s) * kLdA + 16 * j + ln] = -r[s];
+}
+
+__device__ __forceinline__ void tri_inverse64(float* sA, float* sT) {
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6;
+    const int lane = tid & 63;
+    const int ln = lane & 15, gq = lane >> 4;
+    // 3a: diagonal blocks by forward substitution (wave b, lanes 0..15 = columns of block b)
+    if (gq == 0) {
+        const int b = wave;
+        const int col = ln;
+        float x[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            float s = (r == col) ? 1.f : 0.f;
+            const float* arow = sA + (16 * b + r) * kLdA + 16 * b;
+#pragma unroll
+            for (int j = 0; j < r; ++j) s -= arow[j] * x[j];
+            x[r] = s;
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sT[(16 * b + r) * kLdA + 16 * b + col] = x[r];
+    }
+    // zero the strictly upper blocks (read by the k32 slices of stage 4)
+    for (int e = tid; e < 6 * 256; e += 256) {
+        const int blk = e >> 8, off = e & 255;
+        const int bi = blk < 3 ? 0 : (blk < 5 ? 1 : 2);
+        const int bj = blk < 3 ? blk + 1 : (blk < 5 ? blk - 1 : 3);
+        sT[(16 * bi + (off >> 4)) * kLdA + 16 * bj + (off & 15)] = 0.f;
+    }
+    lds_sync();
+    if (wave < 3) tri_offdiag_block(sA, sT, wave + 1, wave);
+    lds_sync();
+    if (wave < 2) tri_offdiag_block(sA, sT, wave + 2, wave);
+    lds_sync();
+    if (wave == 0) tri_offdiag_block(sA, sT, 3, 0);
+    lds_sync();
+}
+
+// accS <- row `lrow` of a [rows][K] fp32 state (as S^T tiles)
+template <int K>
+__device__ __forceinline__ void load_state(f32x4 (&accS)[K / 16], const float* src, int lrow) {
+    const int gq = (threadIdx.x & 63) >> 4;
+#pragma unroll
+    for (int kt = 0; kt < K / 16; ++kt)
+        accS[kt] = *reinterpret_cast<const f32x4*>(src + (size_t)lrow * K + kt * 16 + gq * 4);
+}
+template <int K>
+__device__ __forceinline__ void store_state(const f32x4 (&accS)[K / 16], float* dst, int lrow) {
+    const int gq = (threadIdx.x & 63) >> 4;
+#pragma unroll
+    for (int kt = 0; kt < K / 16; ++kt)
+        *reinterpret_cast<f32x4*>(dst + (size_t)lrow * K + kt * 16 + gq * 4) = accS[kt];
+}
+
+// ---------------------------------------------------------------------------
 // LDS staging (256-thread workgroups).
 // Copy `rows` (<= 64) rows of a [.., H, D] tensor for head h into LDS, row-major and/or
 // transposed; rows beyond `rows` are zero.

@@ -32,7 +32,6 @@ template <typename T> struct IntraPad;
 template <> struct IntraPad<bf16_t> { static constexpr int row = 8, tr = 8; };
 template <> struct IntraPad<float> { static constexpr int row = 4, tr = 4; };
 
-constexpr int kLdA = 68;  // fp32 [64][68] for A and T
 
 template <typename T, int K, int V>
 struct IntraSmem {
@@ -62,28 +61,6 @@ struct IntraSmem {
 // Gram tiles (row tile >= column tile) of a 64x64 lower triangle.
 __constant__ int8_t kTri[10][2] = {{0, 0}, {1, 0}, {1, 1}, {2, 0}, {2, 1}, {2, 2},
                                    {3, 0}, {3, 1}, {3, 2}, {3, 3}};
-
-// Y = sum_{m=j}^{i-1} A_{i,m} T_{m,j}; T_{i,j} = -T_{i,i} Y   (16x16 blocks, fp32 matrix cores)
-__device__ __forceinline__ void tri_offdiag_block(float* sA, float* sT, int i, int j) {
-    const int lane = threadIdx.x & 63;
-    const int ln = lane & 15, gq = lane >> 4;
-    f32x4 y = zero4();
-    for (int m = j; m < i; ++m) {
-        const f32x4 a = *reinterpret_cast<const f32x4*>(sA + (16 * i + ln) * kLdA + 16 * m + 4 * gq);
-        f32x4 b;
-        b.x = sT[(16 * m + 4 * gq + 0) * kLdA + 16 * j + ln];
-        b.y = sT[(16 * m + 4 * gq + 1) * kLdA + 16 * j + ln];
-        b.z = sT[(16 * m + 4 * gq + 2) * kLdA + 16 * j + ln];
-        b.w = sT[(16 * m + 4 * gq + 3) * kLdA + 16 * j + ln];
-        mma_f32_k16(y, a, b);
-    }
-    // y[s] = Y[4*gq + s][ln] is a B operand as is.
-    const f32x4 a = *reinterpret_cast<const f32x4*>(sT + (16 * i + ln) * kLdA + 16 * i + 4 * gq);
-    f32x4 r = zero4();
-    mma_f32_k16(r, a, y);
-#pragma unroll
-    for (int s = 0; s < 4; ++s) sT[(16 * i + 4 * gq + s) * kLdA + 16 * j + ln] = -r[s];
-}
 
 template <typename T, int K, int V>
 __global__ __launch_bounds__(kThreads) void k_intra(IntraArgs args) {
@@ -152,35 +129,7 @@ __global__ __launch_bounds__(kThreads) void k_intra(IntraArgs args) {
     lds_sync();
 
     // ---- stage 3: T = (I + A)^{-1} --------------------------------------------------
-    // 3a: diagonal blocks by forward substitution (wave b, lanes 0..15 = columns of block b)
-    if (gq == 0) {
-        const int b = wave;
-        const int col = ln;
-        float x[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            float s = (r == col) ? 1.f : 0.f;
-            const float* arow = sA + (16 * b + r) * kLdA + 16 * b;
-#pragma unroll
-            for (int j = 0; j < r; ++j) s -= arow[j] * x[j];
-            x[r] = s;
-        }
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sT[(16 * b + r) * kLdA + 16 * b + col] = x[r];
-    }
-    // zero the strictly upper blocks (read by the k32 slices of stage 4)
-    for (int e = tid; e < 6 * 256; e += kThreads) {
-        const int blk = e >> 8, off = e & 255;
-        const int bi = blk < 3 ? 0 : (blk < 5 ? 1 : 2);
-        const int bj = blk < 3 ? blk + 1 : (blk < 5 ? blk - 1 : 3);
-        sT[(16 * bi + (off >> 4)) * kLdA + 16 * bj + (off & 15)] = 0.f;
-    }
-    lds_sync();
-    if (wave < 3) tri_offdiag_block(sA, sT, wave + 1, wave);
-    lds_sync();
-    if (wave < 2) tri_offdiag_block(sA, sT, wave + 2, wave);
-    lds_sync();
-    if (wave == 0) tri_offdiag_block(sA, sT, 3, 0);
+    tri_inverse64(sA, sT);
     if (wave == 1) {
         // chunk statistics for the CP decision
         float m = lane < c ? sKK[lane] : 0.f;
@@ -188,7 +137,6 @@ __global__ __launch_bounds__(kThreads) void k_intra(IntraArgs args) {
         for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
         if (lane == 0) args.cstat[gc * H + h] = make_float2(sGam[63], m);
     }
-    lds_sync();
 
     // ---- stage 4: W = T diag(beta e^gam) K, U = T diag(beta) V ------------------------
     const int rt = wave;

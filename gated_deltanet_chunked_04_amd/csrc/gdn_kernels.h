@@ -150,14 +150,60 @@ struct DecideArgs {
     int32_t warmup;
     float log_eps;
     int32_t forced;  // 0 gate test, 1 warmup, 2 exact
+    int32_t reverse; // 1: windows after each segment end (backward adjoint pass)
 };
 
 struct ScanArgs {
     Geo geo;
-    const float* s0;
+    const float* s0;       // forward: initial state; reverse: d(final state) (either may be null)
     const float* prep;
     float* seginit;
     const int32_t* modes;
+    int32_t reverse;       // 1: G_{s-1} = G_s M_s + R_s from the last segment down
+};
+
+struct RevArgs {
+    Geo geo;
+    const void* q;
+    const void* k;
+    const float* gam;
+    const void* w;
+    const void* d_o;
+    const float* dsT;         // [N,H,V,K] or null
+    float* ds0;               // [N,H,V,K] or null: gradient of the initial state
+    const float* seginit;     // [total_segs,H,V,K] adjoint at the end of every segment but the last
+    float* seginit_out;       // prepass: warmup adjoints written here
+    float* prep;              // prepass: [total_segs,H,V+K,K] reverse maps (R rows, then M^T)
+    const int32_t* modes;
+    void* gstates;            // [total_chunks,H,V,K] adjoint of the state leaving every chunk
+    float scale;
+    int32_t warmup;
+    int32_t use_cp;
+};
+
+struct BwdChunkArgs {
+    Geo geo;
+    const void* q;
+    const void* k;
+    const void* v;
+    const float* g;
+    const float* beta;
+    const float* gam;
+    const void* w;
+    const void* u;
+    const void* d_o;
+    const void* hstates;      // [total_chunks,H,V,K] state entering every chunk
+    const void* gstates;      // [total_chunks,H,V,K] adjoint of the state leaving every chunk
+    float* dw;                // [Ttot,H,K] fp32: dL/dW (state side -> WY side)
+    float* du;                // [Ttot,H,V] fp32: dL/dU
+    float* dk_part;           // [Ttot,H,K] fp32: dk terms of the state side
+    float* dgam_part;         // [Ttot,H] fp32: d(gate cumsum) terms of the state side
+    void* dq;
+    void* dk;
+    void* dv;
+    float* dg;
+    float* dbeta;
+    float scale;
 };
 
 struct TableArgs {
@@ -186,5 +232,8 @@ hipError_t launch_decide(const DecideArgs& a, hipStream_t st);
 hipError_t launch_recur(const RecurArgs& a, int dtype, int mode, int64_t nsegs_grid, int vtiles,
                         hipStream_t st);
 hipError_t launch_scan(const ScanArgs& a, int dtype, hipStream_t st);
+hipError_t launch_reverse(const RevArgs& a, int dtype, int mode, int64_t nsegs_grid, int vtiles, hipStream_t st);
+hipError_t launch_bwd_state(const BwdChunkArgs& a, int dtype, hipStream_t st);
+hipError_t launch_bwd_wy(const BwdChunkArgs& a, int dtype, hipStream_t st);
 
 }  // namespace gdn

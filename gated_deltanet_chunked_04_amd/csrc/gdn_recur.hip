@@ -307,22 +307,6 @@ __device__ __forceinline__ void chunk_part2(const RecurArgs& a, const ChunkLds<T
     }
 }
 
-// accS <- row `lrow` of a [rows][K] fp32 state (as S^T tiles)
-template <int K>
-__device__ __forceinline__ void load_state(f32x4 (&accS)[K / 16], const float* src, int lrow) {
-    const int gq = (threadIdx.x & 63) >> 4;
-#pragma unroll
-    for (int kt = 0; kt < K / 16; ++kt)
-        accS[kt] = *reinterpret_cast<const f32x4*>(src + (size_t)lrow * K + kt * 16 + gq * 4);
-}
-template <int K>
-__device__ __forceinline__ void store_state(const f32x4 (&accS)[K / 16], float* dst, int lrow) {
-    const int gq = (threadIdx.x & 63) >> 4;
-#pragma unroll
-    for (int kt = 0; kt < K / 16; ++kt)
-        *reinterpret_cast<f32x4*>(dst + (size_t)lrow * K + kt * 16 + gq * 4) = accS[kt];
-}
-
 template <typename T, int K, int RT, int MODE>
 __global__ __launch_bounds__(RT * 4) void k_recur(RecurArgs a) {
     using C = RCfg<T, K, RT>;
@@ -470,11 +454,18 @@ __global__ __launch_bounds__(kThreads) void k_decide(DecideArgs a) {
     } else {
         bool ok = true;
         for (int s = 1 + lane; s < nseg; s += 64) {
-            const int cb = s * a.geo.seg_len;
-            const int w0 = cb - a.warmup;
-            if (w0 <= 0) continue;  // window reaches the sequence start: exact
+            const int cb = s * a.geo.seg_len;  // first chunk of segment s
+            // forward: the W chunks before segment s; reverse: the W chunks after segment s-1
+            int w0 = cb - a.warmup, w1 = cb;
+            if (a.reverse) {
+                w0 = cb;
+                w1 = cb + a.warmup;
+                if (w1 >= nchunks) continue;  // window reaches the sequence end: exact
+            } else if (w0 <= 0) {
+                continue;  // window reaches the sequence start: exact
+            }
             float sum = 0.f, kk = 0.f;
-            for (int m = w0; m < cb; ++m) {
+            for (int m = w0; m < w1; ++m) {
                 const float2 st = a.cstat[(choff + m) * H + h];
                 sum += st.x;
                 kk = fmaxf(kk, st.y);
@@ -534,8 +525,13 @@ __global__ __launch_bounds__(RT * 4) void k_scan(ScanArgs a) {
         }
         load_state<K>(rreg, P, row);
     };
-    fetch(0);
-    for (int s = 0; s + 1 < nseg; ++s) {
+    // forward: S_{s+1} = S_s M_s + R_s, s = 0 .. nseg-2
+    // reverse: G_{s-1} = G_s M_s + R_s, s = nseg-1 .. 1 (adjoint leaving segment s-1)
+    auto src_of = [&](int step) { return a.reverse ? nseg - 1 - step : step; };
+    fetch(src_of(0));
+    for (int step = 0; step + 1 < nseg; ++step) {
+        const int s = src_of(step);
+        const int dst = a.reverse ? s - 1 : s + 1;
         lds_sync();
 #pragma unroll
         for (int it = 0; it < SC::IM; ++it) {
@@ -549,7 +545,7 @@ __global__ __launch_bounds__(RT * 4) void k_scan(ScanArgs a) {
         f32x4 nx[K / 16];
 #pragma unroll
         for (int kt = 0; kt < K / 16; ++kt) nx[kt] = rreg[kt];
-        if (s + 2 < nseg) fetch(s + 1);
+        if (step + 2 < nseg) fetch(src_of(step + 1));
         Frag<T> sf[K / 32];
 #pragma unroll
         for (int kb = 0; kb < K / 32; ++kb) frag_acc(sf[kb], accS[2 * kb], accS[2 * kb + 1]);
@@ -564,7 +560,7 @@ __global__ __launch_bounds__(RT * 4) void k_scan(ScanArgs a) {
         }
 #pragma unroll
         for (int kt = 0; kt < K / 16; ++kt) accS[kt] = nx[kt];
-        store_state<K>(accS, a.seginit + ((size_t)(segoff + s + 1) * H + h) * VK, row);
+        store_state<K>(accS, a.seginit + ((size_t)(segoff + dst) * H + h) * VK, row);
     }
 }
 
