@@ -1,17 +1,21 @@
 #!/usr/bin/env python
 """Benchmark of the GDN chunked prefill on one MI355X.
 
-A step is one call of the library's forward (gdn_chunk_fwd: intra-chunk kernel,
-CP preprocessing, inter-chunk recurrence) over one batch of synthetic inputs
-that are already resident in HBM. The default workload is batch-1 agentic
-prefill: B=1, H=16, T=32768, dk=dv=128, chunk 64, bf16 q/k/v with fp32 gates,
-AutoCP on.
+A step is one pass of the whole hot path over one batch of synthetic inputs that
+are already resident in HBM: the forward (gdn_chunk_fwd: intra-chunk kernel, CP
+preprocessing, inter-chunk recurrence) followed by the backward (gdn_chunk_bwd:
+recomputation, reverse adjoint pass, per-chunk gradients). The default workload
+is batch-1 agentic prefill: B=1, H=16, T=32768, dk=dv=128, chunk 64, bf16
+q/k/v with fp32 gates and initial state, AutoCP on; the backward's upstream
+gradients are dO ~ N(0,1) (bf16) and d(final state) ~ N(0,0.1).
 
-Prints one JSON line with tokens/s, TFLOP/s, the roofline fraction of the
-dominant kernel (algorithmic bytes over its HIP-event-timed launch duration)
-and the CPU oracle timed on this host's cores.
+Prints one JSON line: tokens/s of the step (and of the forward and backward
+timed alone), TFLOP/s on algorithmic flops, the roofline fraction of the
+step's dominant kernel (algorithmic bytes over its HIP-event-timed launch
+duration) and the CPU oracle timed on this host's cores.
 
-  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--pass both|fwd|bwd]
+                  [--no-cpu-baseline]
 """
 from __future__ import annotations
 
@@ -31,43 +35,67 @@ FP32_PEAK_TFLOPS = 157.3       # dense fp32 MFMA
 
 
 def algorithmic_counts(B, T, H, K, V, esize, N, nseg_total, lengths=None):
-    """Algorithmic bytes and flops of the forward, per kernel, for the whole workload.
+    """Algorithmic bytes and flops per kernel for the whole workload.
 
-    Bytes count each input read once and each output written once:
-      intra      reads k, v, g, beta; writes w, u, the gate cumsum        ((2K+2V) e + 12 per token-head)
-      recur_out  reads q, k, w, u, the gate cumsum; writes o               ((3K+2V) e + 4 per token-head)
-                 + the initial / final states and the sub-sequence entry states
-    Flops per full chunk of C=64 tokens (triangular products at half):
-      intra      Gram C(C-1)K + inverse C(C-1)(C-2)/3 + w,u C(C-1)(K+V)
-      recur_out  3 * 2CKV + C(C+1)(K+V)
+    Bytes count each operand a kernel must read once and each result it writes once
+    (per token-head unless noted; e = input element size):
+      intra        reads k, v, g, beta; writes w, u, gate cumsum            (2K+2V) e + 12
+      recur_out    reads q, k, w, u, gate cumsum; writes o                  (3K+2V) e + 4
+                   + initial / final states and sub-sequence entry states
+      recur_states reads k, w, u, gate cumsum; writes one V x K state per chunk
+      bwd_reverse  reads q, k, w, dO, gate cumsum; writes one V x K adjoint per chunk
+      bwd_state    reads the chunk's state and adjoint, q, k, w, u, dO, gate cumsum;
+                   writes dq and fp32 dW, dU, dk part, d(gate cumsum) part
+      bwd_wy       reads k, v, beta, gate cumsum and the fp32 hand-offs; writes dk, dv, dg, dbeta
+    Flops per chunk of c tokens (C=64; triangular products at half):
+      forward   intra: c(c-1)K + c(c-1)(c-2)/3 + c(c-1)(K+V);  recur: 3*2cKV + c(c+1)(K+V)
+      backward  the reverse-mode products of the chunk map: dQt, dDelta (both terms), dKt,
+                the adjoint update (two terms), dW: 7 * 2cKV; dP, dT, dBk, dBv, the two
+                M products, (L.dP)K, (L.dP)^T Q: c^2 (2V + 2(K+V) + K + V + 2K + 2K);
+                dA = T^T dT T^T: 2 c^3 / 3
     """
     C = 64
-    toks = B * T if lengths is None else sum(lengths)
+    lens = lengths if lengths is not None else [T] * B
+    toks = sum(lens)
     th = toks * H
-    b_intra = th * ((2 * K + 2 * V) * esize + 12)
-    b_recur = th * ((3 * K + 2 * V) * esize + 4) + N * H * V * K * 4 * 2 + max(nseg_total - N, 0) * H * V * K * 4
-    chunks = [((n + C - 1) // C) for n in (lengths if lengths is not None else [T] * B)]
-    f_intra = f_recur = 0.0
-    for n, nch in zip(lengths if lengths is not None else [T] * B, chunks):
-        for j in range(nch):
+    chunks = sum((n + C - 1) // C for n in lens)
+    st = V * K * esize  # one state in the input precision
+    nb = dict(
+        intra=th * ((2 * K + 2 * V) * esize + 12),
+        recur_out=th * ((3 * K + 2 * V) * esize + 4) + N * H * V * K * 4 * 2 + max(nseg_total - N, 0) * H * V * K * 4,
+        recur_states=th * ((2 * K + V) * esize + 4) + chunks * H * st,
+        bwd_reverse=th * ((3 * K + V) * esize + 4) + chunks * H * st,
+        bwd_state=th * ((3 * K + 2 * V) * esize + 4 + esize * K + 4 * (2 * K + V) + 4) + 2 * chunks * H * st,
+        bwd_wy=th * ((K + V) * esize + 8 + 4 * (2 * K + V) + 4 + (K + V) * esize + 8),
+    )
+    f_intra = f_recur = f_bwd = 0.0
+    for n in lens:
+        for j in range((n + C - 1) // C):
             c = min(C, n - j * C)
             f_intra += c * (c - 1) * K + c * (c - 1) * (c - 2) / 3 + c * (c - 1) * (K + V)
             f_recur += 3 * 2 * c * K * V + c * (c + 1) * (K + V)
-    return dict(bytes=dict(intra=b_intra, recur_out=b_recur),
-                flops=dict(intra=f_intra * H, recur_out=f_recur * H), tokens=toks)
+            f_bwd += 7 * 2 * c * K * V + c * c * (2 * V + 2 * (K + V) + K + V + 4 * K) + 2 * c ** 3 / 3
+    return dict(bytes=nb, flops=dict(fwd=(f_intra + f_recur) * H, bwd=f_bwd * H), tokens=toks)
 
 
-def cpu_baseline(inp, tokens):
-    from oracle import default_threads, ref_fwd
+def cpu_baseline(inp, tokens, passes):
+    """The fp64 oracle on this host's cores over the whole workload (every head and token)."""
+    from oracle import default_threads, ref_bwd, ref_fwd
     threads = default_threads()
     t0 = time.perf_counter()
-    ref_fwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], 1.0, inp["initial_state"],
-            cu_seqlens=inp.get("cu_seqlens"), nthreads=threads)
+    if passes in ("both", "fwd"):
+        ref_fwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], 1.0, inp["initial_state"],
+                cu_seqlens=inp.get("cu_seqlens"), nthreads=threads)
+    if passes in ("both", "bwd"):
+        ref_bwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], inp["d_o"], 1.0, inp["initial_state"],
+                inp["d_final_state"], cu_seqlens=inp.get("cu_seqlens"), nthreads=threads)
     dt = time.perf_counter() - t0
-    return {"value": tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "seconds": dt,
-            "sample": "the whole workload's forward (every head and token) through the fp64 token-by-token "
-                      "oracle, OpenMP over sequence x head x 32-row value blocks"}
+    what = {"both": "forward and backward", "fwd": "forward", "bwd": "backward"}[passes]
+    return {"value": round(tokens / dt, 1), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "seconds": round(dt, 3),
+            "sample": f"the whole workload's {what} (every head and token) through the fp64 token-by-token "
+                      "oracle; forward OpenMP over sequence x head x 32-row value blocks, backward over "
+                      "sequence x head"}
 
 
 def main():
@@ -76,6 +104,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="edge_prefill")
+    ap.add_argument("--pass", dest="passes", default="both", choices=["both", "fwd", "bwd"])
     ap.add_argument("--cp", default=None, help="override the workload's CP mode (auto/off/on/exact/warmup)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
@@ -86,6 +115,8 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
+    import dataclasses
+
     import torch
 
     import gated_deltanet_chunked_04_amd as gdn
@@ -93,6 +124,8 @@ def main():
 
     gdn.load_library()
     w = WORKLOADS[args.workload]
+    if args.passes != "fwd" and not w.backward:
+        w = dataclasses.replace(w, backward=True)  # draw dO and d(final state) too
     cp = args.cp or w.cp
     inp = make_inputs(w, seed=0)
     dev = {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
@@ -105,45 +138,69 @@ def main():
     N = B if cu is None else len(lengths)
     desc = gdn.make_desc(q, v, cu_seqlens=cu, cu_seqlens_host=cu_host, cp_mode=cp)
     plan = gdn.gdn_plan(desc)
-    ws = torch.empty(plan["fwd_workspace_bytes"], dtype=torch.uint8, device="cuda")
+    do_fwd = args.passes in ("both", "fwd")
+    do_bwd = args.passes in ("both", "bwd")
+    ws = torch.empty(max(plan["fwd_workspace_bytes"], plan["bwd_workspace_bytes"] if do_bwd else 0),
+                     dtype=torch.uint8, device="cuda")
     o = torch.empty((B, T, H, V), dtype=q.dtype, device="cuda")
     sT = torch.empty((N, H, V, K), dtype=torch.float32, device="cuda")
+    grads = dict(dq=torch.empty_like(q), dk=torch.empty_like(k), dv=torch.empty_like(v), dg=torch.empty_like(g),
+                 dbeta=torch.empty_like(beta), d_initial_state=torch.empty((N, H, V, K), dtype=torch.float32,
+                                                                          device="cuda"))
 
-    def step():
+    def fwd():
         gdn.gdn_chunk_fwd(q, k, v, g, beta, s0, cu_seqlens=cu, cu_seqlens_host=cu_host, cp_mode=cp,
                           workspace=ws, o=o, final_state=sT)
 
+    def bwd():
+        gdn.gdn_chunk_bwd(q, k, v, g, beta, dev["d_o"], s0, dev["d_final_state"], cu_seqlens=cu,
+                          cu_seqlens_host=cu_host, cp_mode=cp, workspace=ws, out=grads)
+
+    def step():
+        if do_fwd:
+            fwd()
+        if do_bwd:
+            bwd()
+
+    def timed(fn, n):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(n):
+            fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / n
+
     for _ in range(args.warmup):
         step()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    ms = timed(step, args.steps)
+    ms_fwd = timed(fwd, args.steps) if do_fwd else None
+    ms_bwd = timed(bwd, args.steps) if do_bwd else None
 
-    # Per-kernel durations: the same steps with every launch bracketed by HIP events on
-    # the launch stream (separate pass, so the events do not perturb ms_per_step).
+    # Per-kernel durations: one more round of steps with every launch bracketed by HIP
+    # events on the launch stream (separate from the timed loops above).
     gdn.gdn_profile_enable(True)
     for _ in range(args.steps):
         step()
     torch.cuda.synchronize()
     kt = gdn.gdn_profile_read()
     gdn.gdn_profile_enable(False)
-    kernels = {name: {"launches": n, "avg_us": 1e3 * tot / n} for name, (n, tot) in kt.items()}
+    # average duration of one launch, and total per step
+    kernels = {name: {"launches": n, "avg_us": 1e3 * tot / n, "per_step_us": 1e3 * tot / args.steps}
+               for name, (n, tot) in kt.items()}
 
     esize = 2 if q.dtype == torch.bfloat16 else 4
     counts = algorithmic_counts(B, T, H, K, V, esize, N, plan["total_segments"], lengths)
     tokens = counts["tokens"]
-    flops_step = sum(counts["flops"].values())
-    dominant = max(("intra", "recur_out"), key=lambda n: kernels.get(n, {"avg_us": 0})["avg_us"])
+    flops_step = (counts["flops"]["fwd"] if do_fwd else 0) + (counts["flops"]["bwd"] if do_bwd else 0)
+    dominant = max((n for n in kernels if n in counts["bytes"]), key=lambda n: kernels[n]["per_step_us"])
     dur_s = kernels[dominant]["avg_us"] * 1e-6
-    achieved = counts["bytes"][dominant] / dur_s / 1e9
+    bytes_per_launch = counts["bytes"][dominant]  # every launch of it covers the whole workload once
+    achieved = bytes_per_launch / dur_s / 1e9
     roofline = {"bound": "hbm", "kernel": dominant, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                "algorithmic_bytes": counts["bytes"][dominant], "avg_launch_us": round(dur_s * 1e6, 2)}
-    tflops = flops_step / (ms * 1e-3) / 1e12
+                "algorithmic_bytes_per_launch": int(bytes_per_launch), "avg_launch_us": round(dur_s * 1e6, 2)}
     peak_mfma = BF16_PEAK_TFLOPS if esize == 2 else FP32_PEAK_TFLOPS
+    tflops = flops_step / (ms * 1e-3) / 1e12
     line = {
         "metric": METRIC,
         "value": round(tokens / (ms * 1e-3), 1),
@@ -157,17 +214,22 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16" if esize == 2 else "f32",
         "data": "synthetic",
-        "config": {"workload": w.name, "pass": "fwd", "B": B, "T": T, "H": H, "K": K, "V": V, "chunk": 64,
-                   "cp": cp, "cp_on": plan["cp_on"], "seg_chunks": plan["seg_chunks"],
+        "config": {"workload": w.name, "pass": args.passes, "B": B, "T": T, "H": H, "K": K, "V": V,
+                   "chunk": 64, "cp": cp, "cp_on": plan["cp_on"], "seg_chunks": plan["seg_chunks"],
                    "segments": plan["total_segments"], "tokens": tokens},
         "tflops": round(tflops, 2),
         "mfma_frac": round(tflops / peak_mfma, 4),
-        "step_hbm_frac": round(sum(counts["bytes"].values()) / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "roofline": roofline,
-        "kernels_us": {n: round(x["avg_us"], 2) for n, x in kernels.items()},
+        "kernels_us_per_step": {n: round(x["per_step_us"], 2) for n, x in kernels.items()},
     }
+    if do_fwd:
+        line["fwd"] = {"ms": round(ms_fwd, 4), "tokens_per_s": round(tokens / (ms_fwd * 1e-3), 1),
+                       "tflops": round(counts["flops"]["fwd"] / (ms_fwd * 1e-3) / 1e12, 2)}
+    if do_bwd:
+        line["bwd"] = {"ms": round(ms_bwd, 4), "tokens_per_s": round(tokens / (ms_bwd * 1e-3), 1),
+                       "tflops": round(counts["flops"]["bwd"] / (ms_bwd * 1e-3) / 1e12, 2)}
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(inp, tokens)
+        line["cpu_baseline"] = cpu_baseline(inp, tokens, args.passes)
     print(json.dumps(line), flush=True)
 
 

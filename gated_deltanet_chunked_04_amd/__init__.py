@@ -150,8 +150,8 @@ def gdn_chunk_fwd(q, k, v, g, beta, initial_state=None, *, scale=1.0, cu_seqlens
 
 def gdn_chunk_bwd(q, k, v, g, beta, d_o, initial_state=None, d_final_state=None, *, scale=1.0,
                   cu_seqlens=None, cu_seqlens_host=None, cp_mode="auto", warmup_chunks=0, seg_chunks=0,
-                  warmup_eps=0.0, workspace=None, need_d_initial_state=True):
-    """Backward. Returns dict(dq, dk, dv, dg, dbeta, d_initial_state)."""
+                  warmup_eps=0.0, workspace=None, need_d_initial_state=True, out=None):
+    """Backward. Returns dict(dq, dk, dv, dg, dbeta, d_initial_state); `out` may hold them preallocated."""
     N = _num_seqs(q, cu_seqlens)
     _check_inputs(q, k, v, g, beta, initial_state, N)
     B, T, H, K = q.shape
@@ -169,10 +169,11 @@ def gdn_chunk_bwd(q, k, v, g, beta, d_o, initial_state=None, d_final_state=None,
     nbytes = ctypes.c_size_t()
     check(lib.gdn_chunk_bwd_workspace_size(desc.ref, ctypes.byref(nbytes)), "gdn_chunk_bwd_workspace_size")
     ws = _workspace(nbytes.value, q.device, workspace)
-    out = dict(dq=torch.empty_like(q), dk=torch.empty_like(k), dv=torch.empty_like(v),
-               dg=torch.empty_like(g), dbeta=torch.empty_like(beta),
-               d_initial_state=(torch.empty((N, H, V, K), dtype=torch.float32, device=q.device)
-                                if need_d_initial_state else None))
+    if out is None:
+        out = dict(dq=torch.empty_like(q), dk=torch.empty_like(k), dv=torch.empty_like(v),
+                   dg=torch.empty_like(g), dbeta=torch.empty_like(beta),
+                   d_initial_state=(torch.empty((N, H, V, K), dtype=torch.float32, device=q.device)
+                                    if need_d_initial_state else None))
     check(lib.gdn_chunk_bwd(desc.ref, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state),
                             _ptr(d_o), _ptr(d_final_state), _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]),
                             _ptr(out["dg"]), _ptr(out["dbeta"]), _ptr(out["d_initial_state"]),
