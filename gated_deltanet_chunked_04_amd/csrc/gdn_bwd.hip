@@ -33,30 +33,23 @@ template <typename T, int K, int RT>
 struct VCfg {
     static constexpr int NW = RT / 16;
     static constexpr int NT = NW * 64;
-    static constexpr bool kTrans = sizeof(T) == 2;  // transposed LDS copies (bf16); fp32 gathers columns
     static constexpr int VEC = Elem<T>::kVec;
-    static constexpr int LD = K + BPad<T>::row;     // row-major q, k, w  [64][K]
-    static constexpr int LDD = RT + BPad<T>::row;   // row-major dO tile  [64][RT]
-    static constexpr int LDT = 64 + BPad<T>::tr;    // transposed copies  [K or RT][64]
-    static constexpr int LDP = 64 + BPad<T>::row;   // P^T                [64][64]
+    static constexpr int LD = K + BPad<T>::row;     // row-major q, scaled q, k, w  [64][K]
+    static constexpr int LDD = RT + BPad<T>::row;   // row-major dO tile            [64][RT]
+    static constexpr int LDP = 64 + BPad<T>::row;   // P^T                          [64][64]
     static constexpr int kMat = 64 * LD * (int)sizeof(T);
-    static constexpr int off_q = 0;                                        // Q  (row-major)
-    static constexpr int off_k = off_q + kMat;                             // K  (row-major)
-    static constexpr int off_w = off_k + kMat;                             // W^T (bf16) / W (fp32)
-    static constexpr int kWBytes = kTrans ? K * LDT * (int)sizeof(T) : kMat;
-    static constexpr int off_qt = off_w + kWBytes;                         // (e^gam Q)^T (bf16 only)
-    static constexpr int kQtBytes = kTrans ? K * LDT * (int)sizeof(T) : 0;
-    static constexpr int off_do = off_qt + kQtBytes;                       // dO^T (bf16) / dO (fp32)
-    static constexpr int kDoBytes = kTrans ? RT * LDT * (int)sizeof(T) : 64 * LDD * (int)sizeof(T);
-    static constexpr int off_pm = off_do + kDoBytes;                       // P^T
+    static constexpr int off_q = 0;                 // Q
+    static constexpr int off_qs = off_q + kMat;     // scale * e^gam_r * Q
+    static constexpr int off_k = off_qs + kMat;     // K
+    static constexpr int off_w = off_k + kMat;      // W
+    static constexpr int off_do = off_w + kMat;     // dO
+    static constexpr int off_pm = off_do + 64 * LDD * (int)sizeof(T);
     static constexpr int off_gam = off_pm + 64 * LDP * (int)sizeof(T);
     static constexpr int total = off_gam + 256;
     static constexpr int NVK = K / VEC;
     static constexpr int NVD = RT / VEC;
-    static constexpr int IQ = (32 * NVK + NT - 1) / NT;   // q row pairs
-    static constexpr int IK = (64 * NVK + NT - 1) / NT;   // k rows
-    static constexpr int IW = (32 * NVK + NT - 1) / NT;   // w row pairs
-    static constexpr int ID = (32 * NVD + NT - 1) / NT;   // dO row pairs
+    static constexpr int IK = (64 * NVK + NT - 1) / NT;   // q, k, w rows
+    static constexpr int ID = (64 * NVD + NT - 1) / NT;   // dO rows
 };
 
 // (row tile, column tile) of the 64x64 product Q K^T whose transpose P^T is staged: the
@@ -67,11 +60,9 @@ __constant__ int8_t kTriB[12][2] = {{0, 0}, {1, 0}, {1, 1}, {2, 0}, {2, 1}, {2, 
 template <typename T, int K, int RT>
 struct RevRegs {
     using C = VCfg<T, K, RT>;
-    u32x4 qa[C::IQ], qb[C::IQ];
-    u32x4 k[C::IK];
-    u32x4 wa[C::IW], wb[C::IW];
-    u32x4 da[C::ID], db[C::ID];
-    float gq0[C::IQ], gq1[C::IQ];  // gate cumsum of the q row pair (scales the transposed copy)
+    u32x4 q[C::IK], k[C::IK], w[C::IK];
+    float gq[C::IK];  // gate cumsum of the q row (scales its copy)
+    u32x4 d[C::ID];
     float gam;
 };
 
@@ -87,34 +78,22 @@ __device__ __forceinline__ void rev_fetch(RevRegs<T, K, RT>& R, const RevArgs& a
     const T* d_o = reinterpret_cast<const T*>(a.d_o);
     const u32x4 z = u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int it = 0; it < C::IQ; ++it) {
-        const int e = tid + it * C::NT;
-        const int rp = e / C::NVK, cv = e % C::NVK;
-        const bool in = e < 32 * C::NVK;
-        const int r0 = 2 * rp, r1 = 2 * rp + 1;
-        R.qa[it] = (in && r0 < c) ? *reinterpret_cast<const u32x4*>(q + ((t0 + r0) * H + h) * K + cv * C::VEC) : z;
-        R.qb[it] = (in && r1 < c) ? *reinterpret_cast<const u32x4*>(q + ((t0 + r1) * H + h) * K + cv * C::VEC) : z;
-        R.gq0[it] = (in && r0 < c) ? a.gam[(t0 + r0) * H + h] : 0.f;
-        R.gq1[it] = (in && r1 < c) ? a.gam[(t0 + r1) * H + h] : 0.f;
-        R.wa[it] = (in && r0 < c) ? *reinterpret_cast<const u32x4*>(w + ((t0 + r0) * H + h) * K + cv * C::VEC) : z;
-        R.wb[it] = (in && r1 < c) ? *reinterpret_cast<const u32x4*>(w + ((t0 + r1) * H + h) * K + cv * C::VEC) : z;
-    }
-#pragma unroll
     for (int it = 0; it < C::IK; ++it) {
         const int e = tid + it * C::NT;
         const int r = e / C::NVK, cv = e % C::NVK;
-        R.k[it] = (e < 64 * C::NVK && r < c) ? *reinterpret_cast<const u32x4*>(k + ((t0 + r) * H + h) * K + cv * C::VEC)
-                                               : z;
+        const bool ok = e < 64 * C::NVK && r < c;
+        const size_t off = ((t0 + r) * H + h) * K + cv * C::VEC;
+        R.q[it] = ok ? *reinterpret_cast<const u32x4*>(q + off) : z;
+        R.k[it] = ok ? *reinterpret_cast<const u32x4*>(k + off) : z;
+        R.w[it] = ok ? *reinterpret_cast<const u32x4*>(w + off) : z;
+        R.gq[it] = ok ? a.gam[(t0 + r) * H + h] : 0.f;
     }
 #pragma unroll
     for (int it = 0; it < C::ID; ++it) {
         const int e = tid + it * C::NT;
-        const int rp = e / C::NVD, cv = e % C::NVD;
-        const bool in = dcol0 >= 0 && e < 32 * C::NVD;
-        const int r0 = 2 * rp, r1 = 2 * rp + 1;
-        const int64_t V = a.geo.V;
-        R.da[it] = (in && r0 < c) ? *reinterpret_cast<const u32x4*>(d_o + ((t0 + r0) * H + h) * V + dcol0 + cv * C::VEC) : z;
-        R.db[it] = (in && r1 < c) ? *reinterpret_cast<const u32x4*>(d_o + ((t0 + r1) * H + h) * V + dcol0 + cv * C::VEC) : z;
+        const int r = e / C::NVD, cv = e % C::NVD;
+        const bool ok = dcol0 >= 0 && e < 64 * C::NVD && r < c;
+        R.d[it] = ok ? *reinterpret_cast<const u32x4*>(d_o + ((t0 + r) * H + h) * a.geo.V + dcol0 + cv * C::VEC) : z;
     }
     if (tid < 64) {
         const int r = tid < c ? tid : c - 1;
@@ -122,45 +101,32 @@ __device__ __forceinline__ void rev_fetch(RevRegs<T, K, RT>& R, const RevArgs& a
     }
 }
 
-// Write a row pair of VEC elements transposed: dst[(col0 + e) * ld + r0 .. r0+1] = (A[e], B[e]) * (s0, s1).
+// 16-byte vector scaled by s (bf16 or fp32 elements).
 template <typename T>
-__device__ __forceinline__ void put_pair_t(T* dst, int ld, int col0, int r0, const u32x4& A, const u32x4& B,
-                                           float s0 = 1.f, float s1 = 1.f, bool scaled = false);
+__device__ __forceinline__ u32x4 scale_vec(const u32x4& x, float s);
 template <>
-__device__ __forceinline__ void put_pair_t(bf16_t* dst, int ld, int col0, int r0, const u32x4& A, const u32x4& B,
-                                           float s0, float s1, bool scaled) {
+__device__ __forceinline__ u32x4 scale_vec<bf16_t>(const u32x4& x, float s) {
+    u32x4 y;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        uint32_t lo = (A[j >> 1] >> ((j & 1) * 16)) & 0xFFFFu;
-        uint32_t hi = (B[j >> 1] >> ((j & 1) * 16)) & 0xFFFFu;
-        if (scaled) {
-            lo = f2bf_bits(bf2f((bf16_t)lo) * s0);
-            hi = f2bf_bits(bf2f((bf16_t)hi) * s1);
-        }
-        *reinterpret_cast<uint32_t*>(dst + (col0 + j) * ld + r0) = lo | (hi << 16);
-    }
+    for (int i = 0; i < 4; ++i)
+        y[i] = pack_bf2(bf2f((bf16_t)(x[i] & 0xFFFFu)) * s, bf2f((bf16_t)(x[i] >> 16)) * s);
+    return y;
 }
 template <>
-__device__ __forceinline__ void put_pair_t(float* dst, int ld, int col0, int r0, const u32x4& A, const u32x4& B,
-                                           float s0, float s1, bool scaled) {
+__device__ __forceinline__ u32x4 scale_vec<float>(const u32x4& x, float s) {
+    u32x4 y;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        float x = __uint_as_float(A[j]), y = __uint_as_float(B[j]);
-        if (scaled) {
-            x *= s0;
-            y *= s1;
-        }
-        *reinterpret_cast<f32x2*>(dst + (col0 + j) * ld + r0) = f32x2{x, y};
-    }
+    for (int i = 0; i < 4; ++i) y[i] = __float_as_uint(__uint_as_float(x[i]) * s);
+    return y;
 }
 
 template <typename T, int K, int RT>
 struct RevLds {
     T* sQ;
+    T* sQs;  // scale * e^gam_r * Q
     T* sK;
-    T* sW;   // W^T (bf16) or W (fp32)
-    T* sQt;  // (e^gam Q)^T (bf16)
-    T* sD;   // dO^T (bf16) or dO (fp32)
+    T* sW;
+    T* sD;   // dO
     T* sPm;  // P^T [j][r]
     float* sGam;
 };
@@ -170,56 +136,26 @@ __device__ __forceinline__ void rev_stage(const RevRegs<T, K, RT>& R, const RevL
     using C = VCfg<T, K, RT>;
     const int tid = threadIdx.x;
 #pragma unroll
-    for (int it = 0; it < C::IQ; ++it) {
-        const int e = tid + it * C::NT;
-        if (e < 32 * C::NVK) {
-            const int rp = e / C::NVK, cv = e % C::NVK;
-            const int r0 = 2 * rp;
-            *reinterpret_cast<u32x4*>(L.sQ + r0 * C::LD + cv * C::VEC) = R.qa[it];
-            *reinterpret_cast<u32x4*>(L.sQ + (r0 + 1) * C::LD + cv * C::VEC) = R.qb[it];
-            if constexpr (C::kTrans) {
-                put_pair_t(L.sQt, C::LDT, cv * C::VEC, r0, R.qa[it], R.qb[it], scale * fast_exp(R.gq0[it]),
-                           scale * fast_exp(R.gq1[it]), true);
-                put_pair_t(L.sW, C::LDT, cv * C::VEC, r0, R.wa[it], R.wb[it]);
-            } else {
-                *reinterpret_cast<u32x4*>(L.sW + r0 * C::LD + cv * C::VEC) = R.wa[it];
-                *reinterpret_cast<u32x4*>(L.sW + (r0 + 1) * C::LD + cv * C::VEC) = R.wb[it];
-            }
-        }
-    }
-#pragma unroll
     for (int it = 0; it < C::IK; ++it) {
         const int e = tid + it * C::NT;
         if (e < 64 * C::NVK) {
             const int r = e / C::NVK, cv = e % C::NVK;
-            *reinterpret_cast<u32x4*>(L.sK + r * C::LD + cv * C::VEC) = R.k[it];
+            const int o = r * C::LD + cv * C::VEC;
+            *reinterpret_cast<u32x4*>(L.sQ + o) = R.q[it];
+            *reinterpret_cast<u32x4*>(L.sQs + o) = scale_vec<T>(R.q[it], scale * fast_exp(R.gq[it]));
+            *reinterpret_cast<u32x4*>(L.sK + o) = R.k[it];
+            *reinterpret_cast<u32x4*>(L.sW + o) = R.w[it];
         }
     }
 #pragma unroll
     for (int it = 0; it < C::ID; ++it) {
         const int e = tid + it * C::NT;
-        if (e < 32 * C::NVD) {
-            const int rp = e / C::NVD, cv = e % C::NVD;
-            const int r0 = 2 * rp;
-            if constexpr (C::kTrans) {
-                put_pair_t(L.sD, C::LDT, cv * C::VEC, r0, R.da[it], R.db[it]);
-            } else {
-                *reinterpret_cast<u32x4*>(L.sD + r0 * C::LDD + cv * C::VEC) = R.da[it];
-                *reinterpret_cast<u32x4*>(L.sD + (r0 + 1) * C::LDD + cv * C::VEC) = R.db[it];
-            }
+        if (e < 64 * C::NVD) {
+            const int r = e / C::NVD, cv = e % C::NVD;
+            *reinterpret_cast<u32x4*>(L.sD + r * C::LDD + cv * C::VEC) = R.d[it];
         }
     }
     if (tid < 64) L.sGam[tid] = R.gam;
-}
-
-// dO^T fragment of value column `col` over chunk rows r0..r0+31 (optionally scaled by e^gam_r).
-template <typename T, int K, int RT>
-__device__ __forceinline__ void do_frag(Frag<T>& f, const RevLds<T, K, RT>& L, int col, int r0) {
-    using C = VCfg<T, K, RT>;
-    if constexpr (C::kTrans)
-        frag_row(f, L.sD, C::LDT, col, r0);
-    else
-        frag_col(f, L.sD, C::LDD, col, r0);
 }
 
 template <typename T, int K, int RT, int MODE>
@@ -228,9 +164,9 @@ __global__ __launch_bounds__(RT * 4) void k_reverse(RevArgs a) {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     RevLds<T, K, RT> L;
     L.sQ = reinterpret_cast<T*>(smem + C::off_q);
+    L.sQs = reinterpret_cast<T*>(smem + C::off_qs);
     L.sK = reinterpret_cast<T*>(smem + C::off_k);
     L.sW = reinterpret_cast<T*>(smem + C::off_w);
-    L.sQt = reinterpret_cast<T*>(smem + C::off_qt);
     L.sD = reinterpret_cast<T*>(smem + C::off_do);
     L.sPm = reinterpret_cast<T*>(smem + C::off_pm);
     L.sGam = reinterpret_cast<float*>(smem + C::off_gam);
@@ -357,7 +293,7 @@ __global__ __launch_bounds__(RT * 4) void k_reverse(RevArgs a) {
                 for (int rb = (jt >> 1); rb < 2; ++rb) {
                     Frag<T> fa, fb;
                     frag_row(fa, L.sPm, C::LDP, jt * 16 + ln, rb * 32);
-                    do_frag<T, K, RT>(fb, L, wave * 16 + ln, rb * 32);
+                    frag_col(fb, L.sD, C::LDD, wave * 16 + ln, rb * 32);  // dO column v, slots r
                     mma(accD[jt], fa, fb);
                 }
             }
@@ -370,18 +306,7 @@ __global__ __launch_bounds__(RT * 4) void k_reverse(RevArgs a) {
         Frag<T> dof[2];
         if (has_do) {
 #pragma unroll
-            for (int rb = 0; rb < 2; ++rb) {
-                do_frag<T, K, RT>(dof[rb], L, wave * 16 + ln, rb * 32);
-                if constexpr (!C::kTrans) {
-                    // fp32: fold e^gam_r into the dO slots (bf16 folds it into the staged Q^T)
-                    Frag<float>& f = reinterpret_cast<Frag<float>&>(dof[rb]);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        f.lo[e] *= a.scale * fast_exp(L.sGam[rb * 32 + gq * 4 + e]);
-                        f.hi[e] *= a.scale * fast_exp(L.sGam[rb * 32 + 16 + gq * 4 + e]);
-                    }
-                }
-            }
+            for (int rb = 0; rb < 2; ++rb) frag_col(dof[rb], L.sD, C::LDD, wave * 16 + ln, rb * 32);
         }
 #pragma unroll
         for (int kt = 0; kt < K / 16; ++kt) {
@@ -389,20 +314,14 @@ __global__ __launch_bounds__(RT * 4) void k_reverse(RevArgs a) {
 #pragma unroll
             for (int jb = 0; jb < 2; ++jb) {
                 Frag<T> fa;
-                if constexpr (C::kTrans)
-                    frag_row(fa, L.sW, C::LDT, kt * 16 + ln, jb * 32);
-                else
-                    frag_col(fa, L.sW, C::LD, kt * 16 + ln, jb * 32);
+                frag_col(fa, L.sW, C::LD, kt * 16 + ln, jb * 32);  // W^T row k, slots j
                 mma(accG[kt], fa, ddf[jb]);
             }
             if (has_do) {
 #pragma unroll
                 for (int rb = 0; rb < 2; ++rb) {
                     Frag<T> fa;
-                    if constexpr (C::kTrans)
-                        frag_row(fa, L.sQt, C::LDT, kt * 16 + ln, rb * 32);
-                    else
-                        frag_col(fa, L.sQ, C::LD, kt * 16 + ln, rb * 32);
+                    frag_col(fa, L.sQs, C::LD, kt * 16 + ln, rb * 32);  // (scale e^gam Q)^T row k, slots r
                     mma(accG[kt], fa, dof[rb]);
                 }
             }
@@ -466,37 +385,44 @@ struct SCfg {
     static constexpr int total = off_sc + 64;
 };
 
-// Copy `rows` rows x D columns of a row-major global matrix (row stride ld_g elements) into
-// LDS (row stride ld_s), zero past `rows`; 256 threads, 16-byte vectors.
-template <typename T, int D>
-__device__ __forceinline__ void copy_rows(T* dst, int ld_s, const T* src, size_t ld_g, int nrows, int rows) {
+// Copy NR rows x D columns of a row-major global matrix (row stride ld_g elements) into
+// LDS (row stride ld_s); rows >= `rows` are zero. 256 threads, 16-byte vectors; every
+// global load of the copy is issued before the first LDS store.
+template <typename T, int D, int NR>
+__device__ __forceinline__ void copy_rows(T* dst, int ld_s, const T* src, size_t ld_g, int rows) {
     constexpr int VEC = Elem<T>::kVec;
     constexpr int NV = D / VEC;
-    for (int e = threadIdx.x; e < nrows * NV; e += 256) {
+    constexpr int IT = NR * NV / 256;
+    static_assert(NR * NV % 256 == 0, "copy shape");
+    u32x4 x[IT];
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+        const int e = threadIdx.x + it * 256;
         const int r = e / NV, cv = e % NV;
-        u32x4 x = u32x4{0u, 0u, 0u, 0u};
-        if (r < rows) x = *reinterpret_cast<const u32x4*>(src + (size_t)r * ld_g + cv * VEC);
-        *reinterpret_cast<u32x4*>(dst + r * ld_s + cv * VEC) = x;
+        x[it] = r < rows ? *reinterpret_cast<const u32x4*>(src + (size_t)r * ld_g + cv * VEC) : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+        const int e = threadIdx.x + it * 256;
+        const int r = e / NV, cv = e % NV;
+        *reinterpret_cast<u32x4*>(dst + r * ld_s + cv * VEC) = x[it];
     }
 }
 
 // Same, multiplying every element by s (used to fold the query scale into dO).
-template <typename T, int D>
-__device__ __forceinline__ void copy_rows_scaled(T* dst, int ld_s, const T* src, size_t ld_g, int nrows, int rows,
-                                                 float s) {
+template <typename T, int D, int NR>
+__device__ __forceinline__ void copy_rows_scaled(T* dst, int ld_s, const T* src, size_t ld_g, int rows, float s) {
     if (s == 1.f) {
-        copy_rows<T, D>(dst, ld_s, src, ld_g, nrows, rows);
+        copy_rows<T, D, NR>(dst, ld_s, src, ld_g, rows);
         return;
     }
-    for (int e = threadIdx.x; e < nrows * D / 4; e += 256) {
-        const int r = e / (D / 4), cv = e % (D / 4);
-        f32x4 x = zero4();
-        if (r < rows) {
-            const T* p = src + (size_t)r * ld_g + cv * 4;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) x[i] = Elem<T>::to_f(p[i]) * s;
-        }
-        store4(dst + r * ld_s + cv * 4, x);
+    constexpr int VEC = Elem<T>::kVec;
+    constexpr int NV = D / VEC;
+    for (int e = threadIdx.x; e < NR * NV; e += 256) {
+        const int r = e / NV, cv = e % NV;
+        u32x4 x = u32x4{0u, 0u, 0u, 0u};
+        if (r < rows) x = scale_vec<T>(*reinterpret_cast<const u32x4*>(src + (size_t)r * ld_g + cv * VEC), s);
+        *reinterpret_cast<u32x4*>(dst + r * ld_s + cv * VEC) = x;
     }
 }
 
@@ -582,14 +508,14 @@ __global__ __launch_bounds__(256) void k_bwd_state(BwdChunkArgs a) {
     const size_t VK = (size_t)V * K;
 
     // ---- stage operands -------------------------------------------------------------
-    copy_rows<T, K>(sS, S::LDK, reinterpret_cast<const T*>(a.hstates) + ((size_t)gc * H + h) * VK, K, V, V);
-    copy_rows<T, K>(sG, S::LDK, reinterpret_cast<const T*>(a.gstates) + ((size_t)gc * H + h) * VK, K, V, V);
-    copy_rows<T, K>(sQ, S::LDK, reinterpret_cast<const T*>(a.q) + (t0 * H + h) * K, (size_t)H * K, 64, c);
-    copy_rows<T, K>(sK, S::LDK, reinterpret_cast<const T*>(a.k) + (t0 * H + h) * K, (size_t)H * K, 64, c);
-    copy_rows<T, K>(sW, S::LDK, reinterpret_cast<const T*>(a.w) + (t0 * H + h) * K, (size_t)H * K, 64, c);
+    copy_rows<T, K, V>(sS, S::LDK, reinterpret_cast<const T*>(a.hstates) + ((size_t)gc * H + h) * VK, K, V);
+    copy_rows<T, K, V>(sG, S::LDK, reinterpret_cast<const T*>(a.gstates) + ((size_t)gc * H + h) * VK, K, V);
+    copy_rows<T, K, 64>(sQ, S::LDK, reinterpret_cast<const T*>(a.q) + (t0 * H + h) * K, (size_t)H * K, c);
+    copy_rows<T, K, 64>(sK, S::LDK, reinterpret_cast<const T*>(a.k) + (t0 * H + h) * K, (size_t)H * K, c);
+    copy_rows<T, K, 64>(sW, S::LDK, reinterpret_cast<const T*>(a.w) + (t0 * H + h) * K, (size_t)H * K, c);
     // dO enters every product together with the query scale (o = scale S q)
-    copy_rows_scaled<T, V>(sD, S::LDV, reinterpret_cast<const T*>(a.d_o) + (t0 * H + h) * V, (size_t)H * V, 64, c,
-                           a.scale);
+    copy_rows_scaled<T, V, 64>(sD, S::LDV, reinterpret_cast<const T*>(a.d_o) + (t0 * H + h) * V, (size_t)H * V, c,
+                               a.scale);
     if (tid < 64) sGam[tid] = a.gam[(t0 + (tid < c ? tid : c - 1)) * H + h];
     lds_sync();
 
@@ -779,9 +705,23 @@ __global__ __launch_bounds__(256) void k_bwd_state(BwdChunkArgs a) {
     drow -= ktk;
     // e^Gam <G, S> over the whole state (each thread a slice)
     float gs = 0.f;
-    for (int e = tid; e < V * K; e += 256) {
-        const int vv = e / K, kk = e % K;
-        gs += Elem<T>::to_f(sG[vv * S::LDK + kk]) * Elem<T>::to_f(sS[vv * S::LDK + kk]);
+    {
+        constexpr int VEC = Elem<T>::kVec;
+#pragma unroll 4
+        for (int e = tid; e < V * K / VEC; e += 256) {
+            const int vv = e / (K / VEC), kk = (e % (K / VEC)) * VEC;
+            const u32x4 xg = *reinterpret_cast<const u32x4*>(sG + vv * S::LDK + kk);
+            const u32x4 xs = *reinterpret_cast<const u32x4*>(sS + vv * S::LDK + kk);
+            if constexpr (sizeof(T) == 2) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    gs += bf2f((bf16_t)(xg[i] & 0xFFFFu)) * bf2f((bf16_t)(xs[i] & 0xFFFFu)) +
+                          bf2f((bf16_t)(xg[i] >> 16)) * bf2f((bf16_t)(xs[i] >> 16));
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) gs += __uint_as_float(xg[i]) * __uint_as_float(xs[i]);
+            }
+        }
     }
     {
         float t = ktk;  // one value per (r, gq); summed over all lanes it is sum_r
@@ -883,15 +823,23 @@ __device__ __forceinline__ void frag_row_f32cvt(Frag<T>& f, const float* base, i
     }
 }
 
-// fp32 rows [64][D] from global into LDS in the operand type.
+// fp32 rows [64][D] from global into LDS in the operand type (loads issued first).
 template <typename T, int D>
 __device__ __forceinline__ void copy_rows_f32(T* dst, int ld_s, const float* src, size_t ld_g, int rows) {
     constexpr int NV = D / 4;
-    for (int e = threadIdx.x; e < 64 * NV; e += 256) {
+    constexpr int IT = 64 * NV / 256;
+    f32x4 x[IT];
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+        const int e = threadIdx.x + it * 256;
         const int r = e / NV, cv = e % NV;
-        f32x4 x = zero4();
-        if (r < rows) x = *reinterpret_cast<const f32x4*>(src + (size_t)r * ld_g + cv * 4);
-        store4(dst + r * ld_s + cv * 4, x);
+        x[it] = r < rows ? *reinterpret_cast<const f32x4*>(src + (size_t)r * ld_g + cv * 4) : zero4();
+    }
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+        const int e = threadIdx.x + it * 256;
+        const int r = e / NV, cv = e % NV;
+        store4(dst + r * ld_s + cv * 4, x[it]);
     }
 }
 
@@ -924,8 +872,8 @@ __global__ __launch_bounds__(256) void k_bwd_wy(BwdChunkArgs a) {
     const int wave = tid >> 6, lane = tid & 63, ln = lane & 15, gq = lane >> 4;
     const int ra = wave * 16 + ln;  // this lane's row a in "column" roles
 
-    copy_rows<T, K>(sK, S::LDK, reinterpret_cast<const T*>(a.k) + (t0 * H + h) * K, (size_t)H * K, 64, c);
-    copy_rows<T, V>(sV, S::LDV, reinterpret_cast<const T*>(a.v) + (t0 * H + h) * V, (size_t)H * V, 64, c);
+    copy_rows<T, K, 64>(sK, S::LDK, reinterpret_cast<const T*>(a.k) + (t0 * H + h) * K, (size_t)H * K, c);
+    copy_rows<T, V, 64>(sV, S::LDV, reinterpret_cast<const T*>(a.v) + (t0 * H + h) * V, (size_t)H * V, c);
     copy_rows_f32<T, K>(sdW, S::LDK, a.dw + (t0 * H + h) * K, (size_t)H * K, c);
     copy_rows_f32<T, V>(sdU, S::LDV, a.du + (t0 * H + h) * V, (size_t)H * V, c);
     if (tid < 64) {
@@ -1171,8 +1119,7 @@ hipError_t launch_reverse(const RevArgs& a, int dtype, int mode, int64_t nsegs_g
         GDN_REV_CASE(bf16_t, 128, 64)
         GDN_REV_CASE(bf16_t, 128, 128)
     } else {
-        GDN_REV_CASE(float, 64, 64)
-        GDN_REV_CASE(float, 128, 64)
+        GDN_REV_CASE(float, 64, 64)  // the fp32 backward supports K = V = 64 only
     }
 #undef GDN_REV_CASE
     return hipErrorInvalidValue;

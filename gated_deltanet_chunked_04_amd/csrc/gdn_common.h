@@ -88,18 +88,31 @@ __device__ __forceinline__ void frag_row(Frag<float>& f, const float* base, int 
     f.hi = *reinterpret_cast<const f32x4*>(p + 16);
 }
 
-// Fragment of column `col` of a row-major matrix over rows k0 .. k0+31
-// (slot kappa -> row k0 + kappa): strided scalar reads.
+// Fragment of column `col` of a row-major matrix over rows k0 .. k0+31 (slot kappa ->
+// row k0 + kappa). `col` must be tile*16 + ln for the calling lane (every lane group reads
+// the 16 consecutive columns of one tile).
 template <typename T>
 __device__ __forceinline__ void frag_col(Frag<T>& f, const T* base, int ld, int col, int k0);
+
+// bf16 from LDS: two ds_read_b64_tr_b16. Within each 16-lane group the instruction treats
+// the 16 lanes' 8-byte reads as the rows of a 16x4 block and returns to lane i the elements
+// (row i/4 + 4m, column i%4), m = 0..3. Pointing lane (ln, gq) at
+// X[k0 + 4gq + ln/4][c0 + 4(ln%4)] therefore hands it X[k0 + 4gq + m][c0 + ln]: slots 0..3;
+// the second read, 16 rows down, gives slots 4..7. (Layout checked on gfx950 with an
+// in-bounds probe.) `base` must point into LDS.
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+__device__ __forceinline__ u32x2 ds_read_tr16(const bf16_t* p) {
+    const s16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(p));
+    return __builtin_bit_cast(u32x2, v);
+}
 template <>
 __device__ __forceinline__ void frag_col(Frag<bf16_t>& f, const bf16_t* base, int ld, int col, int k0) {
-    const int gq = threadIdx.x >> 4 & 3;
-    const bf16_t* p = base + (size_t)(k0 + gq * 4) * ld + col;
-    uint32_t s[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) s[e] = p[(size_t)((e >> 2) * 16 + (e & 3)) * ld];
-    f.v = u32x4{s[0] | s[1] << 16, s[2] | s[3] << 16, s[4] | s[5] << 16, s[6] | s[7] << 16};
+    const int lane = threadIdx.x & 63, ln = lane & 15, gq = lane >> 4;
+    const bf16_t* p = base + (size_t)(k0 + gq * 4 + (ln >> 2)) * ld + (col - ln) + 4 * (ln & 3);
+    const u32x2 a = ds_read_tr16(p);
+    const u32x2 b = ds_read_tr16(p + (size_t)16 * ld);
+    f.v = u32x4{a.x, a.y, b.x, b.y};
 }
 template <>
 __device__ __forceinline__ void frag_col(Frag<float>& f, const float* base, int ld, int col, int k0) {

@@ -14,8 +14,8 @@
 // S_t = exp(g_t) S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T: inside a chunk the
 // per-token corrections delta_r = beta_r (v_r - S'_r k_r) solve (I + A) Delta = U - W S^T.
 //
-// One workgroup (4 waves) per (chunk, head). K is staged twice in LDS: row-major for
-// the Gram matrix and transposed for T*K; V only transposed. The inverse is blocked:
+// One workgroup (4 waves) per (chunk, head). K and V are staged row-major in LDS; T*K
+// and T*V read their columns with LDS transpose loads. The inverse is blocked:
 // 16x16 diagonal blocks by forward substitution, then off-diagonal blocks level by
 // level with fp32 matrix-core products. T stays fp32; the products T*K and T*V run on
 // the matrix cores in the input precision with fp32 accumulation.
@@ -35,27 +35,16 @@ template <> struct IntraPad<float> { static constexpr int row = 4, tr = 4; };
 
 template <typename T, int K, int V>
 struct IntraSmem {
-    static constexpr int LDR = K + IntraPad<T>::row;   // row-major K
-    static constexpr int LDT = 64 + IntraPad<T>::tr;   // transposed K / V
-    static constexpr int kKrmBytes = 64 * LDR * (int)sizeof(T);
-    static constexpr int kTBytes = 64 * kLdA * 4;
-    static constexpr int kUnionBytes = kKrmBytes > kTBytes ? kKrmBytes : kTBytes;
-    static constexpr int kKtBytes = K * LDT * (int)sizeof(T);
-    static constexpr int kVtBytes = V * LDT * (int)sizeof(T);
-    static constexpr int kABytes = 64 * kLdA * 4;
-    static constexpr int off_union = 0;
-    static constexpr int off_kt = off_union + kUnionBytes;
-    static constexpr int off_vt = off_kt + kKtBytes;
-    static constexpr int off_a = off_vt + kVtBytes;
-    static constexpr int off_gam = off_a + kABytes;
+    static constexpr int LDK = K + IntraPad<T>::row;   // row-major K (Gram rows, then the W output)
+    static constexpr int LDV = V + IntraPad<T>::row;   // row-major V (then the U output)
+    static constexpr int off_k = 0;
+    static constexpr int off_v = off_k + 64 * LDK * (int)sizeof(T);
+    static constexpr int off_t = off_v + 64 * LDV * (int)sizeof(T);
+    static constexpr int off_a = off_t + 64 * kLdA * 4;
+    static constexpr int off_gam = off_a + 64 * kLdA * 4;
     static constexpr int off_beta = off_gam + 256;
     static constexpr int off_kk = off_beta + 256;
     static constexpr int total = off_kk + 256;
-    // Output staging reuses the transposed regions: W as [64][K+pad], U as [64][V+pad].
-    static constexpr int LDO_K = K + IntraPad<T>::row;
-    static constexpr int LDO_V = V + IntraPad<T>::row;
-    static_assert(64 * LDO_K * (int)sizeof(T) <= kKtBytes, "W staging does not fit");
-    static_assert(64 * LDO_V * (int)sizeof(T) <= kVtBytes, "U staging does not fit");
 };
 
 // Gram tiles (row tile >= column tile) of a 64x64 lower triangle.
@@ -66,10 +55,9 @@ template <typename T, int K, int V>
 __global__ __launch_bounds__(kThreads) void k_intra(IntraArgs args) {
     using S = IntraSmem<T, K, V>;
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-    T* sKrm = reinterpret_cast<T*>(smem + S::off_union);
-    float* sT = reinterpret_cast<float*>(smem + S::off_union);
-    T* sKt = reinterpret_cast<T*>(smem + S::off_kt);
-    T* sVt = reinterpret_cast<T*>(smem + S::off_vt);
+    T* sK = reinterpret_cast<T*>(smem + S::off_k);
+    T* sV = reinterpret_cast<T*>(smem + S::off_v);
+    float* sT = reinterpret_cast<float*>(smem + S::off_t);
     float* sA = reinterpret_cast<float*>(smem + S::off_a);
     float* sGam = reinterpret_cast<float*>(smem + S::off_gam);
     float* sBeta = reinterpret_cast<float*>(smem + S::off_beta);
@@ -88,8 +76,8 @@ __global__ __launch_bounds__(kThreads) void k_intra(IntraArgs args) {
     const int ln = lane & 15, gq = lane >> 4;
 
     // ---- stage 1: operands into LDS, gate cumsum --------------------------------
-    stage_rows<T, K, true>(reinterpret_cast<const T*>(args.k), L.t0, H, h, c, sKrm, S::LDR, sKt, S::LDT);
-    stage_rows<T, V, false>(reinterpret_cast<const T*>(args.v), L.t0, H, h, c, nullptr, 0, sVt, S::LDT);
+    stage_rows<T, K, true, false>(reinterpret_cast<const T*>(args.k), L.t0, H, h, c, sK, S::LDK, nullptr, 0);
+    stage_rows<T, V, true, false>(reinterpret_cast<const T*>(args.v), L.t0, H, h, c, sV, S::LDV, nullptr, 0);
     if (wave == 0) {
         const bool in = lane < c;
         float x = in ? args.g[(L.t0 + lane) * H + h] : 0.f;
@@ -112,8 +100,8 @@ __global__ __launch_bounds__(kThreads) void k_intra(IntraArgs args) {
 #pragma unroll
         for (int kb = 0; kb < K / 32; ++kb) {
             Frag<T> a, b;
-            frag_row(a, sKrm, S::LDR, ti * 16 + ln, kb * 32);
-            frag_row(b, sKrm, S::LDR, tj * 16 + ln, kb * 32);
+            frag_row(a, sK, S::LDK, ti * 16 + ln, kb * 32);
+            frag_row(b, sK, S::LDK, tj * 16 + ln, kb * 32);
             mma(acc, a, b);
         }
         const int j = tj * 16 + ln;
@@ -179,7 +167,7 @@ __global__ __launch_bounds__(kThreads) void k_intra(IntraArgs args) {
         for (int kb = 0; kb < NKB; ++kb) {
             if (kb < nkb) {
                 Frag<T> b;
-                frag_row(b, sKt, S::LDT, ct * 16 + ln, kb * 32);
+                frag_col(b, sK, S::LDK, ct * 16 + ln, kb * 32);  // K^T row ct*16+ln, slots j
                 mma(accw[ct], b, aw[kb]);
             }
         }
@@ -191,22 +179,23 @@ __global__ __launch_bounds__(kThreads) void k_intra(IntraArgs args) {
         for (int kb = 0; kb < NKB; ++kb) {
             if (kb < nkb) {
                 Frag<T> b;
-                frag_row(b, sVt, S::LDT, ct * 16 + ln, kb * 32);
+                frag_col(b, sV, S::LDV, ct * 16 + ln, kb * 32);  // V^T row ct*16+ln, slots j
                 mma(accu[ct], b, au[kb]);
             }
         }
     }
     lds_sync();
-    T* sWo = sKt;
-    T* sUo = sVt;
+    // outputs staged over K and V, which are no longer read
+    T* sWo = sK;
+    T* sUo = sV;
     const int orow = rt * 16 + ln;
 #pragma unroll
-    for (int ct = 0; ct < K / 16; ++ct) store4(sWo + orow * S::LDO_K + ct * 16 + gq * 4, accw[ct]);
+    for (int ct = 0; ct < K / 16; ++ct) store4(sWo + orow * S::LDK + ct * 16 + gq * 4, accw[ct]);
 #pragma unroll
-    for (int ct = 0; ct < V / 16; ++ct) store4(sUo + orow * S::LDO_V + ct * 16 + gq * 4, accu[ct]);
+    for (int ct = 0; ct < V / 16; ++ct) store4(sUo + orow * S::LDV + ct * 16 + gq * 4, accu[ct]);
     lds_sync();
-    store_rows<T, K>(reinterpret_cast<T*>(args.w), L.t0, H, h, c, sWo, S::LDO_K);
-    store_rows<T, V>(reinterpret_cast<T*>(args.u), L.t0, H, h, c, sUo, S::LDO_V);
+    store_rows<T, K>(reinterpret_cast<T*>(args.w), L.t0, H, h, c, sWo, S::LDK);
+    store_rows<T, V>(reinterpret_cast<T*>(args.u), L.t0, H, h, c, sUo, S::LDV);
 }
 
 template <typename T, int K, int V>

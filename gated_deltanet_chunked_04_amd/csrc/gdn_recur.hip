@@ -42,10 +42,8 @@ template <typename T, int K, int RT>
 struct RCfg {
     static constexpr int NW = RT / 16;
     static constexpr int NT = NW * 64;
-    static constexpr bool kTrans = sizeof(T) == 2;  // transposed K copy (bf16 only)
     static constexpr int VEC = Elem<T>::kVec;
     static constexpr int LD = K + RPad<T>::row;
-    static constexpr int LDT = 64 + RPad<T>::tr;
     static constexpr int LDU = RT + RPad<T>::row;
     static constexpr int LDP = 64 + RPad<T>::row;
     static constexpr int kMat = 64 * LD * (int)sizeof(T);
@@ -54,8 +52,7 @@ struct RCfg {
     static constexpr int off_w = off_k + kMat;
     static constexpr int off_u = off_w + kMat;
     static constexpr int off_pm = off_u + 64 * LDU * (int)sizeof(T);
-    static constexpr int off_kt = off_pm + 64 * LDP * (int)sizeof(T);
-    static constexpr int off_gam = off_kt + (kTrans ? K * LDT * (int)sizeof(T) : 0);
+    static constexpr int off_gam = off_pm + 64 * LDP * (int)sizeof(T);
     static constexpr int total = off_gam + 256;
     // register prefetch: 16-byte vectors per thread
     static constexpr int NVK = K / VEC;                        // vectors per row of q/k/w
@@ -130,7 +127,6 @@ struct ChunkLds {
     T* sW;
     T* sU;
     T* sPm;
-    T* sKt;
     float* sGam;
 };
 
@@ -156,14 +152,6 @@ __device__ __forceinline__ void chunk_stage(const ChunkRegs<T, K, RT, kQ>& R, co
             const u32x4 A = R.ka[it], B = R.kb[it];
             *reinterpret_cast<u32x4*>(L.sK + r0 * C::LD + cv * C::VEC) = A;
             *reinterpret_cast<u32x4*>(L.sK + (r0 + 1) * C::LD + cv * C::VEC) = B;
-            if constexpr (C::kTrans) {
-#pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    const uint32_t lo = (A[j >> 1] >> ((j & 1) * 16)) & 0xFFFFu;
-                    const uint32_t hi = (B[j >> 1] >> ((j & 1) * 16)) & 0xFFFFu;
-                    *reinterpret_cast<uint32_t*>(L.sKt + (cv * 8 + j) * C::LDT + r0) = lo | (hi << 16);
-                }
-            }
         }
     }
 #pragma unroll
@@ -298,10 +286,7 @@ __device__ __forceinline__ void chunk_part2(const RecurArgs& a, const ChunkLds<T
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
             Frag<T> fa;
-            if constexpr (C::kTrans)
-                frag_row(fa, L.sKt, C::LDT, kt * 16 + ln, kb * 32);
-            else
-                frag_col(fa, L.sK, C::LD, kt * 16 + ln, kb * 32);
+            frag_col(fa, L.sK, C::LD, kt * 16 + ln, kb * 32);  // K^T row k, slots j
             mma(accS[kt], fa, dtf[kb]);
         }
     }
@@ -318,7 +303,6 @@ __global__ __launch_bounds__(RT * 4) void k_recur(RecurArgs a) {
     L.sW = reinterpret_cast<T*>(smem + C::off_w);
     L.sU = reinterpret_cast<T*>(smem + C::off_u);
     L.sPm = reinterpret_cast<T*>(smem + C::off_pm);
-    L.sKt = reinterpret_cast<T*>(smem + C::off_kt);
     L.sGam = reinterpret_cast<float*>(smem + C::off_gam);
 
     const Geo& geo = a.geo;
