@@ -44,9 +44,8 @@ def algorithmic_counts(B, T, H, K, V, esize, N, nseg_total, lengths=None):
                    + initial / final states and sub-sequence entry states
       recur_states reads k, w, u, gate cumsum; writes one V x K state per chunk
       bwd_reverse  reads q, k, w, dO, gate cumsum; writes one V x K adjoint per chunk
-      bwd_state    reads the chunk's state and adjoint, q, k, w, u, dO, gate cumsum;
-                   writes dq and fp32 dW, dU, dk part, d(gate cumsum) part
-      bwd_wy       reads k, v, beta, gate cumsum and the fp32 hand-offs; writes dk, dv, dg, dbeta
+      bwd_chunk    reads the chunk's state and adjoint, q, k, v, w, u, dO, gate cumsum, beta;
+                   writes dq, dk, dv, dg, dbeta                 (3K+3V) e + 8 + (2K+V) e + 8
     Flops per chunk of c tokens (C=64; triangular products at half):
       forward   intra: c(c-1)K + c(c-1)(c-2)/3 + c(c-1)(K+V);  recur: 3*2cKV + c(c+1)(K+V)
       backward  the reverse-mode products of the chunk map: dQt, dDelta (both terms), dKt,
@@ -65,8 +64,7 @@ def algorithmic_counts(B, T, H, K, V, esize, N, nseg_total, lengths=None):
         recur_out=th * ((3 * K + 2 * V) * esize + 4) + N * H * V * K * 4 * 2 + max(nseg_total - N, 0) * H * V * K * 4,
         recur_states=th * ((2 * K + V) * esize + 4) + chunks * H * st,
         bwd_reverse=th * ((3 * K + V) * esize + 4) + chunks * H * st,
-        bwd_state=th * ((3 * K + 2 * V) * esize + 4 + esize * K + 4 * (2 * K + V) + 4) + 2 * chunks * H * st,
-        bwd_wy=th * ((K + V) * esize + 8 + 4 * (2 * K + V) + 4 + (K + V) * esize + 8),
+        bwd_chunk=th * ((3 * K + 3 * V) * esize + 8 + (2 * K + V) * esize + 8) + 2 * chunks * H * st,
     )
     f_intra = f_recur = f_bwd = 0.0
     for n in lens:

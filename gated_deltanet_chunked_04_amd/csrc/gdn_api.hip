@@ -44,8 +44,8 @@ struct Plan {
     size_t o_gam = 0, o_w = 0, o_u = 0, o_cstat = 0, o_bos = 0, o_len = 0, o_choff = 0, o_segoff = 0,
            o_ctab = 0, o_stab = 0, o_modes = 0, o_seginit = 0, o_prep = 0, fwd_bytes = 0;
     // backward workspace: the forward's layout, then these
-    size_t o_modes_r = 0, o_seginit_r = 0, o_prep_r = 0, o_h = 0, o_gst = 0, o_dw = 0, o_du = 0, o_dkp = 0,
-           o_dgp = 0, bwd_bytes = 0;
+    size_t o_modes_r = 0, o_seginit_r = 0, o_prep_r = 0, o_h = 0, o_gst = 0, bwd_bytes = 0;
+    int32_t cus = 256;   // compute units (desc->num_cus, else the device's)
     int32_t bwd_ok = 1;  // fp32 backward supports K = V = 64 only (LDS)
 };
 
@@ -99,6 +99,7 @@ gdn_status make_plan(const gdn_desc* d, Plan& p) {
     }
     if (p.total_chunks > INT32_MAX || max_nt > INT32_MAX / 2) return GDN_ERR_UNSUPPORTED;
 
+    p.cus = d->num_cus > 0 ? d->num_cus : query_cus();
     // AutoCP
     const int64_t NH = (int64_t)p.N * d->H;
     bool cp = false;
@@ -115,7 +116,7 @@ gdn_status make_plan(const gdn_desc* d, Plan& p) {
             seg_len = d->seg_chunks;
         } else {
             // One recurrence workgroup per CU at V = K = 128 (8 waves, ~95 KB of LDS), two otherwise.
-            const int cus = d->num_cus > 0 ? d->num_cus : query_cus();
+            const int cus = p.cus;
             const int per_cu = recur_rows((int)d->V, (int)d->K) == 128 ? 1 : 2;
             const int64_t target = (int64_t)per_cu * cus;       // workgroups to aim for
             const int64_t units = NH * vtiles;                   // workgroups per segment layer
@@ -176,10 +177,6 @@ gdn_status make_plan(const gdn_desc* d, Plan& p) {
     }
     p.o_h = take((size_t)p.total_chunks * H * V * K * p.esize);
     p.o_gst = take((size_t)p.total_chunks * H * V * K * p.esize);
-    p.o_dw = take(T * H * K * 4);
-    p.o_du = take(T * H * V * 4);
-    p.o_dkp = take(T * H * K * 4);
-    p.o_dgp = take(T * H * 4);
     p.bwd_bytes = std::max<size_t>(off, kAlign);
     p.bwd_ok = (d->dtype == GDN_DTYPE_BF16) || (d->K == 64 && d->V == 64);
     return GDN_OK;
@@ -220,10 +217,10 @@ Geo make_geo(const gdn_desc* d, const Plan& p, unsigned char* ws) {
 // ---------------------------------------------------------------------------
 // Kernel timing (gdn_profile_enable / gdn_profile_read).
 enum KernelId { kKTables = 0, kKIntra, kKDecide, kKPrepass, kKScan, kKRecurOut, kKRecurStates,
-                kKBwdPrepass, kKBwdScan, kKBwdReverse, kKBwdGrads, kKBwdWy, kKCount };
+                kKBwdPrepass, kKBwdScan, kKBwdReverse, kKBwdChunk, kKCount };
 const char* const kKernelNames[kKCount] = {"tables", "intra", "cp_decide", "cp_prepass", "cp_scan",
                                            "recur_out", "recur_states", "bwd_cp_prepass", "bwd_cp_scan",
-                                           "bwd_reverse", "bwd_state", "bwd_wy"};
+                                           "bwd_reverse", "bwd_chunk"};
 struct Pending {
     int kid;
     hipEvent_t start, stop;
@@ -552,18 +549,14 @@ gdn_status gdn_chunk_bwd(const gdn_desc* desc, const void* q, const void* k, con
     ba.d_o = d_o;
     ba.hstates = ws + p.o_h;
     ba.gstates = ws + p.o_gst;
-    ba.dw = reinterpret_cast<float*>(ws + p.o_dw);
-    ba.du = reinterpret_cast<float*>(ws + p.o_du);
-    ba.dk_part = reinterpret_cast<float*>(ws + p.o_dkp);
-    ba.dgam_part = reinterpret_cast<float*>(ws + p.o_dgp);
     ba.dq = dq;
     ba.dk = dk;
     ba.dv = dv;
     ba.dg = dg;
     ba.dbeta = dbeta;
     ba.scale = desc->scale;
-    GDN_LAUNCH(kKBwdGrads, st, launch_bwd_state(ba, desc->dtype, st));
-    GDN_LAUNCH(kKBwdWy, st, launch_bwd_wy(ba, desc->dtype, st));
+    const int64_t tasks = p.total_chunks * (int64_t)desc->H;
+    GDN_LAUNCH(kKBwdChunk, st, launch_bwd_chunk(ba, desc->dtype, (int)std::min<int64_t>(tasks, p.cus), st));
     return GDN_OK;
 }
 

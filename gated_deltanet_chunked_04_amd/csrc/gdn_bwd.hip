@@ -8,10 +8,10 @@
 //   G_in   = e^Gam G + dO^T diag(e^gam) Q - dDelta^T W      (adjoint entering the chunk)
 // G_in is affine in G with the transposed chunk map, so the same CP scheme as the forward
 // splits the serial chain: warmup windows after each sub-sequence, or exact maps composed
-// from the end. The per-chunk gradients then run in parallel over all chunks:
-//   state side (k_bwd_state): Delta = U - W S^T, dQt = dO S, dP = dO U^T - dQt W^T,
-//     dKt = Delta G, dW = -dDelta S  ->  dq, the P and Kt terms of dk and d(gam), dW, dU
-//   WY side (k_bwd_wy): recompute T = (I + A)^{-1}; dT = dW Bk^T + dU Bv^T,
+// from the end. The per-chunk gradients then run in parallel over all chunks (k_bwd_chunk):
+//   state side: Delta = U - W S^T, dQt = dO S, dP = dO U^T - dQt W^T, dKt = Delta G,
+//     dW = -dDelta S  ->  dq, the P and Kt terms of dk and d(gam), dW, dU
+//   WY side: recompute T = (I + A)^{-1}; dT = dW Bk^T + dU Bv^T,
 //     dA = strict_lower(-T^T dT T^T), dBk = T^T dW, dBv = T^T dU  ->  dk, dv, dbeta, and
 //     dg as the in-chunk reverse cumulative sum of d(gam).
 #include "gdn_common.h"
@@ -362,68 +362,188 @@ hipError_t launch_reverse_t(const RevArgs& a, int64_t nsegs_grid, int vtiles, hi
 }
 
 // ---------------------------------------------------------------------------
-// State-side per-chunk gradients. One workgroup (4 waves) per (chunk, head); wave w owns
-// chunk rows r = 16w .. 16w+15. Most tiles are held transposed (rows over k or v,
-// columns over the wave's rows r), which makes them A fragments of their transposes and
-// lets every lane write four consecutive columns of its row with one vector store.
+// Per-chunk gradients: the state side, then the WY side, in one kernel. A persistent
+// workgroup (4 waves, one per CU) walks the (chunk, head) tasks; the next task's operands
+// travel into registers while the current task computes, so HBM traffic overlaps the
+// work instead of alternating with it. Wave w owns chunk rows r = 16w .. 16w+15. Most
+// tiles are held transposed (rows over k or v, columns over the wave's rows r), which
+// makes them A fragments of their transposes and lets every lane write four consecutive
+// columns of its row with one vector store.
+//
+// LDS: K stays for both sides. The state side holds S, G, Q, W, scale * dO and U (the
+// L .* dP exchange later reuses U). dU is written over dO once the dDelta products are
+// done, dW over S once the S and G products are done; the WY side's four fp32 64x64
+// matrices and V go into the space that is free once the state side ends (the hole
+// between dW and dU first, then from U onwards).
+struct WyPlace {
+    int off[5];  // A-raw, T, R1, R2 (fp32 64x64 each), V
+    int end;
+};
+constexpr WyPlace place_wy(int h0, int h1, int tail, int f32mat, int vmat) {
+    WyPlace p{};
+    int cur = h0, tl = tail;
+    for (int i = 0; i < 5; ++i) {
+        const int s = i < 4 ? f32mat : vmat;
+        if (cur + s <= h1) {
+            p.off[i] = cur;
+            cur += s;
+        } else {
+            p.off[i] = tl;
+            tl += s;
+        }
+    }
+    p.end = tl;
+    return p;
+}
+
 template <typename T, int K, int V>
-struct SCfg {
-    static constexpr int LDK = K + BPad<T>::row;   // [V][K] states, [64][K] q, k, w
-    static constexpr int LDV = V + BPad<T>::row;   // [64][V] dO
-    static constexpr int LDX = 64 + BPad<T>::row;  // [64][64] exchange of L .* dP
-    static constexpr int off_s = 0;
-    static constexpr int off_g = off_s + V * LDK * (int)sizeof(T);
-    static constexpr int off_q = off_g + V * LDK * (int)sizeof(T);
-    static constexpr int off_k = off_q + 64 * LDK * (int)sizeof(T);
-    static constexpr int off_w = off_k + 64 * LDK * (int)sizeof(T);
-    static constexpr int off_d = off_w + 64 * LDK * (int)sizeof(T);
-    static constexpr int off_x = off_d + 64 * LDV * (int)sizeof(T);
-    static constexpr int off_gam = off_x + 64 * LDX * (int)sizeof(T);
-    static constexpr int off_red = off_gam + 256;          // [4][64] fp32 column partials
-    static constexpr int off_row = off_red + 4 * 64 * 4;   // [64] fp32 row parts
-    static constexpr int off_sc = off_row + 256;           // [8] fp32 scalars
+struct BCfg {
+    static constexpr int VEC = Elem<T>::kVec;
+    static constexpr int LDK = K + BPad<T>::row;
+    static constexpr int LDV = V + BPad<T>::row;
+    static constexpr int LDX = 64 + BPad<T>::row;
+    static constexpr int kMK = 64 * LDK * (int)sizeof(T);  // one [64][K] matrix
+    static constexpr int kMV = 64 * LDV * (int)sizeof(T);  // one [64][V] matrix
+    static constexpr int kSt = V * LDK * (int)sizeof(T);   // one [V][K] state
+    static constexpr int kF = 64 * kLdA * 4;               // one fp32 64x64 matrix
+    static constexpr int off_k = 0;
+    // state side
+    static constexpr int off_s = kMK;
+    static constexpr int off_g = off_s + kSt;
+    static constexpr int off_q = off_g + kSt;
+    static constexpr int off_w = off_q + kMK;
+    static constexpr int off_d = off_w + kMK;  // scale * dO, then dU
+    static constexpr int off_u = off_d + kMV;  // U, then the L .* dP exchange
+    static constexpr int off_x = off_u;
+    static constexpr int end_state = off_u + kMV;
+    // WY side
+    static constexpr int off_dw = off_s;
+    static constexpr int off_du = off_d;
+    static constexpr WyPlace wy = place_wy(off_dw + kMK, off_d, off_u, kF, kMV);
+    static constexpr int off_ar = wy.off[0];  // e^{gam_a-gam_c} k_a.k_c (strict lower)
+    static constexpr int off_t = wy.off[1];   // T
+    static constexpr int off_r1 = wy.off[2];  // A, then dT, then Mx
+    static constexpr int off_r2 = wy.off[3];  // dT T^T
+    static constexpr int off_v = wy.off[4];
+    // small arrays after both
+    static constexpr int off_gam = end_state > wy.end ? end_state : wy.end;
+    static constexpr int off_beta = off_gam + 256;
+    static constexpr int off_red = off_beta + 256;  // [4][64] fp32 column partials
+    static constexpr int off_row = off_red + 1024;  // [64] fp32 row parts
+    static constexpr int off_dgs = off_row + 256;   // [64] state-side d(gam)
+    static constexpr int off_sc = off_dgs + 256;    // [8] fp32 scalars
     static constexpr int total = off_sc + 64;
+    static_assert(LDX <= LDV, "the exchange fits over U");
+    static_assert(kMK <= 2 * kSt, "dW fits over S and G");
+    // 16-byte vectors per thread of one task's operands
+    static constexpr int NS = V * (K / VEC) / 256;   // S or G
+    static constexpr int NK = 64 * (K / VEC) / 256;  // q, k, w
+    static constexpr int NV = 64 * (V / VEC) / 256;  // dO, u, v
+    static_assert(NS * 256 == V * (K / VEC) && NK * 256 == 64 * (K / VEC) && NV * 256 == 64 * (V / VEC),
+                  "vector split");
 };
 
-// Copy NR rows x D columns of a row-major global matrix (row stride ld_g elements) into
-// LDS (row stride ld_s); rows >= `rows` are zero. 256 threads, 16-byte vectors; every
-// global load of the copy is issued before the first LDS store.
-template <typename T, int D, int NR>
-__device__ __forceinline__ void copy_rows(T* dst, int ld_s, const T* src, size_t ld_g, int rows) {
-    constexpr int VEC = Elem<T>::kVec;
-    constexpr int NV = D / VEC;
-    constexpr int IT = NR * NV / 256;
-    static_assert(NR * NV % 256 == 0, "copy shape");
-    u32x4 x[IT];
-#pragma unroll
-    for (int it = 0; it < IT; ++it) {
-        const int e = threadIdx.x + it * 256;
-        const int r = e / NV, cv = e % NV;
-        x[it] = r < rows ? *reinterpret_cast<const u32x4*>(src + (size_t)r * ld_g + cv * VEC) : u32x4{0u, 0u, 0u, 0u};
+// One task's operands in registers, in the three groups that are fetched at different
+// points of the previous task: S and G, the chunk rows (q, k, w, dO, u, gate cumsum,
+// beta), and v.
+template <typename T, int K, int V>
+struct BRegs {
+    using C = BCfg<T, K, V>;
+    u32x4 s[C::NS], g[C::NS];
+    u32x4 q[C::NK], k[C::NK], w[C::NK], d[C::NV], u[C::NV];
+    u32x4 v[C::NV];
+    float gam, beta;
+};
+
+struct BTask {
+    int64_t gc;  // global chunk
+    int64_t t0;  // first token (flattened)
+    int h;
+    int c;       // tokens in the chunk
+};
+
+// First valid task at or after t, stepping by the grid; ntasks when there is none.
+__device__ __forceinline__ int64_t bwd_next_task(const Geo& geo, int64_t t, int64_t ntasks, BTask& x) {
+    for (; t < ntasks; t += gridDim.x) {
+        ChunkLoc L;
+        const int64_t gc = t / geo.H;
+        if (locate_chunk(geo, gc, L)) {
+            x.gc = gc;
+            x.t0 = L.t0;
+            x.h = (int)(t - gc * geo.H);
+            x.c = L.c;
+            return t;
+        }
     }
+    return ntasks;
+}
+
+// Rows [0, rows) of a row-major global matrix into registers: 16-byte vector e of the
+// tile goes to thread e % 256, slot e / 256; rows >= rows are zero.
+template <typename T, int D, int N>
+__device__ __forceinline__ void fetch_tile(u32x4 (&x)[N], const T* src, size_t ld_g, int rows) {
+    constexpr int NVR = D / Elem<T>::kVec;
 #pragma unroll
-    for (int it = 0; it < IT; ++it) {
+    for (int it = 0; it < N; ++it) {
         const int e = threadIdx.x + it * 256;
-        const int r = e / NV, cv = e % NV;
-        *reinterpret_cast<u32x4*>(dst + r * ld_s + cv * VEC) = x[it];
+        const int r = e / NVR, cv = e % NVR;
+        x[it] = r < rows ? *reinterpret_cast<const u32x4*>(src + (size_t)r * ld_g + cv * Elem<T>::kVec)
+                         : u32x4{0u, 0u, 0u, 0u};
     }
 }
 
-// Same, multiplying every element by s (used to fold the query scale into dO).
-template <typename T, int D, int NR>
-__device__ __forceinline__ void copy_rows_scaled(T* dst, int ld_s, const T* src, size_t ld_g, int rows, float s) {
-    if (s == 1.f) {
-        copy_rows<T, D, NR>(dst, ld_s, src, ld_g, rows);
-        return;
+// The registers of fetch_tile into a row-major LDS tile (row stride ld_s), scaled by s.
+template <typename T, int D, int N>
+__device__ __forceinline__ void put_tile(T* dst, int ld_s, const u32x4 (&x)[N], float s = 1.f) {
+    constexpr int NVR = D / Elem<T>::kVec;
+#pragma unroll
+    for (int it = 0; it < N; ++it) {
+        const int e = threadIdx.x + it * 256;
+        const int r = e / NVR, cv = e % NVR;
+        *reinterpret_cast<u32x4*>(dst + r * ld_s + cv * Elem<T>::kVec) = s == 1.f ? x[it] : scale_vec<T>(x[it], s);
     }
-    constexpr int VEC = Elem<T>::kVec;
-    constexpr int NV = D / VEC;
-    for (int e = threadIdx.x; e < NR * NV; e += 256) {
-        const int r = e / NV, cv = e % NV;
-        u32x4 x = u32x4{0u, 0u, 0u, 0u};
-        if (r < rows) x = scale_vec<T>(*reinterpret_cast<const u32x4*>(src + (size_t)r * ld_g + cv * VEC), s);
-        *reinterpret_cast<u32x4*>(dst + r * ld_s + cv * VEC) = x;
+}
+
+template <typename T, int K, int V>
+__device__ __forceinline__ void bwd_fetch_states(BRegs<T, K, V>& R, const BwdChunkArgs& a, const BTask& x) {
+    const size_t st = ((size_t)x.gc * a.geo.H + x.h) * (size_t)V * K;
+    fetch_tile<T, K>(R.s, reinterpret_cast<const T*>(a.hstates) + st, K, V);
+    fetch_tile<T, K>(R.g, reinterpret_cast<const T*>(a.gstates) + st, K, V);
+}
+
+template <typename T, int K, int V>
+__device__ __forceinline__ void bwd_fetch_rows(BRegs<T, K, V>& R, const BwdChunkArgs& a, const BTask& x) {
+    const int64_t H = a.geo.H;
+    const size_t ok = ((size_t)x.t0 * H + x.h) * K, ov = ((size_t)x.t0 * H + x.h) * V;
+    fetch_tile<T, K>(R.q, reinterpret_cast<const T*>(a.q) + ok, (size_t)H * K, x.c);
+    fetch_tile<T, K>(R.k, reinterpret_cast<const T*>(a.k) + ok, (size_t)H * K, x.c);
+    fetch_tile<T, K>(R.w, reinterpret_cast<const T*>(a.w) + ok, (size_t)H * K, x.c);
+    fetch_tile<T, V>(R.d, reinterpret_cast<const T*>(a.d_o) + ov, (size_t)H * V, x.c);
+    fetch_tile<T, V>(R.u, reinterpret_cast<const T*>(a.u) + ov, (size_t)H * V, x.c);
+    const int tid = threadIdx.x;
+    if (tid < 64) {
+        const bool in = tid < x.c;
+        R.gam = a.gam[(x.t0 + (in ? tid : x.c - 1)) * H + x.h];
+        R.beta = in ? a.beta[(x.t0 + tid) * H + x.h] : 0.f;
     }
+}
+
+template <typename T, int K, int V>
+__device__ __forceinline__ void bwd_fetch_v(BRegs<T, K, V>& R, const BwdChunkArgs& a, const BTask& x) {
+    fetch_tile<T, V>(R.v, reinterpret_cast<const T*>(a.v) + ((size_t)x.t0 * a.geo.H + x.h) * V,
+                     (size_t)a.geo.H * V, x.c);
+}
+
+// Four consecutive LDS elements as fp32.
+__device__ __forceinline__ f32x4 ld4(const bf16_t* p) {
+    const u32x2 x = *reinterpret_cast<const u32x2*>(p);
+    return f32x4{__uint_as_float(x.x << 16), __uint_as_float(x.x & 0xFFFF0000u), __uint_as_float(x.y << 16),
+                 __uint_as_float(x.y & 0xFFFF0000u)};
+}
+__device__ __forceinline__ f32x4 ld4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
+
+__device__ __forceinline__ float dot4(const f32x4& a, const f32x4& b) {
+    return a[0] * b[0] + a[1] * b[1] + a[2] * b[2] + a[3] * b[3];
 }
 
 // Negated copy of a fragment.
@@ -437,30 +557,6 @@ __device__ __forceinline__ Frag<float> neg(const Frag<float>& f) {
     n.lo = -f.lo;
     n.hi = -f.hi;
     return n;
-}
-
-// Fragment of row `row` of a global row-major matrix, zero when row >= rows.
-template <typename T>
-__device__ __forceinline__ void frag_row_g(Frag<T>& f, const T* base, size_t ld, int row, int rows, int k0) {
-    if (row < rows) {
-        const int gq = (threadIdx.x & 63) >> 4;
-        const T* p = base + (size_t)row * ld + k0 + gq * 4;
-        if constexpr (sizeof(T) == 2) {
-            const u32x2 a = *reinterpret_cast<const u32x2*>(p);
-            const u32x2 b = *reinterpret_cast<const u32x2*>(p + 16);
-            reinterpret_cast<Frag<bf16_t>&>(f).v = u32x4{a.x, a.y, b.x, b.y};
-        } else {
-            reinterpret_cast<Frag<float>&>(f).lo = *reinterpret_cast<const f32x4*>(p);
-            reinterpret_cast<Frag<float>&>(f).hi = *reinterpret_cast<const f32x4*>(p + 16);
-        }
-    } else {
-        if constexpr (sizeof(T) == 2)
-            reinterpret_cast<Frag<bf16_t>&>(f).v = u32x4{0u, 0u, 0u, 0u};
-        else {
-            reinterpret_cast<Frag<float>&>(f).lo = zero4();
-            reinterpret_cast<Frag<float>&>(f).hi = zero4();
-        }
-    }
 }
 
 // Sum over the four lanes that share ln (lane groups gq = 0..3).
@@ -477,325 +573,6 @@ __device__ __forceinline__ float sum_ln(float x) {
     x += __shfl_xor(x, 8, 64);
     return x;
 }
-
-template <typename T, int K, int V>
-__global__ __launch_bounds__(256) void k_bwd_state(BwdChunkArgs a) {
-    using S = SCfg<T, K, V>;
-    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-    T* sS = reinterpret_cast<T*>(smem + S::off_s);
-    T* sG = reinterpret_cast<T*>(smem + S::off_g);
-    T* sQ = reinterpret_cast<T*>(smem + S::off_q);
-    T* sK = reinterpret_cast<T*>(smem + S::off_k);
-    T* sW = reinterpret_cast<T*>(smem + S::off_w);
-    T* sD = reinterpret_cast<T*>(smem + S::off_d);
-    T* sX = reinterpret_cast<T*>(smem + S::off_x);
-    float* sGam = reinterpret_cast<float*>(smem + S::off_gam);
-    float* sRed = reinterpret_cast<float*>(smem + S::off_red);
-    float* sRow = reinterpret_cast<float*>(smem + S::off_row);
-    float* sSc = reinterpret_cast<float*>(smem + S::off_sc);
-
-    const Geo& geo = a.geo;
-    const int64_t gc = blockIdx.x;
-    const int h = blockIdx.y;
-    ChunkLoc L;
-    if (!locate_chunk(geo, gc, L)) return;
-    const int64_t H = geo.H;
-    const int c = L.c;
-    const int64_t t0 = L.t0;
-    const int tid = threadIdx.x;
-    const int wave = tid >> 6, lane = tid & 63, ln = lane & 15, gq = lane >> 4;
-    const int r = wave * 16 + ln;  // this lane's chunk row in "column" roles
-    const size_t VK = (size_t)V * K;
-
-    // ---- stage operands -------------------------------------------------------------
-    copy_rows<T, K, V>(sS, S::LDK, reinterpret_cast<const T*>(a.hstates) + ((size_t)gc * H + h) * VK, K, V);
-    copy_rows<T, K, V>(sG, S::LDK, reinterpret_cast<const T*>(a.gstates) + ((size_t)gc * H + h) * VK, K, V);
-    copy_rows<T, K, 64>(sQ, S::LDK, reinterpret_cast<const T*>(a.q) + (t0 * H + h) * K, (size_t)H * K, c);
-    copy_rows<T, K, 64>(sK, S::LDK, reinterpret_cast<const T*>(a.k) + (t0 * H + h) * K, (size_t)H * K, c);
-    copy_rows<T, K, 64>(sW, S::LDK, reinterpret_cast<const T*>(a.w) + (t0 * H + h) * K, (size_t)H * K, c);
-    // dO enters every product together with the query scale (o = scale S q)
-    copy_rows_scaled<T, V, 64>(sD, S::LDV, reinterpret_cast<const T*>(a.d_o) + (t0 * H + h) * V, (size_t)H * V, c,
-                               a.scale);
-    if (tid < 64) sGam[tid] = a.gam[(t0 + (tid < c ? tid : c - 1)) * H + h];
-    lds_sync();
-
-    const float Gm = sGam[63];
-    const float gr = sGam[r];
-    const T* ug = reinterpret_cast<const T*>(a.u) + (t0 * H + h) * V;  // U rows of this chunk
-    const size_t ldu = (size_t)H * V;
-
-    // ---- P tiles with the wave's rows as keys: PmK[jt] = P^T restricted (rows j, cols r) --
-    f32x4 PmK[4];
-#pragma unroll
-    for (int jt = 0; jt < 4; ++jt) {
-        PmK[jt] = zero4();
-        if (jt >= wave) {
-#pragma unroll
-            for (int kb = 0; kb < K / 32; ++kb) {
-                Frag<T> fa, fb;
-                frag_row(fa, sQ, S::LDK, jt * 16 + ln, kb * 32);
-                frag_row(fb, sK, S::LDK, r, kb * 32);
-                mma(PmK[jt], fa, fb);
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int j = jt * 16 + gq * 4 + i;
-            PmK[jt][i] = (j >= r) ? PmK[jt][i] * fast_exp(sGam[j] - gr) : 0.f;
-        }
-    }
-    // ---- Delta^T[v][r] = U[r][v] - (S W^T)[v][r];  dDelta^T = dO^T P + G K~^T ------------
-    f32x4 DT[V / 16], DDT[V / 16];
-    Frag<T> wr[K / 32], kr[K / 32];
-#pragma unroll
-    for (int kb = 0; kb < K / 32; ++kb) {
-        Frag<T> f;
-        frag_row(f, sW, S::LDK, r, kb * 32);
-        wr[kb] = neg(f);
-        frag_row(kr[kb], sK, S::LDK, r, kb * 32);
-    }
-    const float ekt = fast_exp(Gm - gr);
-#pragma unroll
-    for (int vt = 0; vt < V / 16; ++vt) {
-        f32x4 u0 = zero4();
-        if (r < c) {
-            const T* up = ug + (size_t)r * ldu + vt * 16 + gq * 4;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) u0[i] = Elem<T>::to_f(up[i]);
-        }
-        DT[vt] = u0;
-        DDT[vt] = zero4();
-#pragma unroll
-        for (int kb = 0; kb < K / 32; ++kb) {
-            Frag<T> fs, fg;
-            frag_row(fs, sS, S::LDK, vt * 16 + ln, kb * 32);
-            mma(DT[vt], fs, wr[kb]);
-            frag_row(fg, sG, S::LDK, vt * 16 + ln, kb * 32);
-            mma(DDT[vt], fg, kr[kb]);
-        }
-        DDT[vt] *= ekt;
-#pragma unroll
-        for (int jb = 0; jb < 2; ++jb) {
-            Frag<T> fd, fp;
-            frag_col(fd, sD, S::LDV, vt * 16 + ln, jb * 32);  // dO^T row v, slots j
-            frag_acc(fp, PmK[2 * jb], PmK[2 * jb + 1]);
-            mma(DDT[vt], fd, fp);
-        }
-    }
-    // ---- dQt^T, dW^T = -(S^T dDelta^T), dKt^T = G^T Delta^T  (rows k, cols r) ---------
-    f32x4 dQT[K / 16], dWT[K / 16], dKT[K / 16];
-    Frag<T> dor[V / 32], ddf[V / 32], dtf[V / 32];
-#pragma unroll
-    for (int vb = 0; vb < V / 32; ++vb) {
-        frag_row(dor[vb], sD, S::LDV, r, vb * 32);
-        frag_acc(ddf[vb], DDT[2 * vb], DDT[2 * vb + 1], -1.f);
-        frag_acc(dtf[vb], DT[2 * vb], DT[2 * vb + 1]);
-    }
-#pragma unroll
-    for (int kt = 0; kt < K / 16; ++kt) {
-        dQT[kt] = zero4();
-        dWT[kt] = zero4();
-        dKT[kt] = zero4();
-#pragma unroll
-        for (int vb = 0; vb < V / 32; ++vb) {
-            Frag<T> fs, fg;
-            frag_col(fs, sS, S::LDK, kt * 16 + ln, vb * 32);  // S^T row k, slots v
-            mma(dQT[kt], fs, dor[vb]);
-            mma(dWT[kt], fs, ddf[vb]);
-            frag_col(fg, sG, S::LDK, kt * 16 + ln, vb * 32);  // G^T row k, slots v
-            mma(dKT[kt], fg, dtf[vb]);
-        }
-    }
-    // ---- dP^T[j][r] = (U dO^T)[j][r] - (W dQt^T)[j][r];  P with the wave's rows as queries --
-    f32x4 dPT[4], PmQ[4];
-    Frag<T> dqf[K / 32];
-#pragma unroll
-    for (int kb = 0; kb < K / 32; ++kb) frag_acc(dqf[kb], dQT[2 * kb], dQT[2 * kb + 1], -1.f);
-    Frag<T> qr[K / 32];
-#pragma unroll
-    for (int kb = 0; kb < K / 32; ++kb) frag_row(qr[kb], sQ, S::LDK, r, kb * 32);
-#pragma unroll
-    for (int jt = 0; jt < 4; ++jt) {
-        dPT[jt] = zero4();
-        PmQ[jt] = zero4();
-        if (jt <= wave) {
-#pragma unroll
-            for (int vb = 0; vb < V / 32; ++vb) {
-                Frag<T> fu;
-                frag_row_g(fu, ug, ldu, jt * 16 + ln, c, vb * 32);
-                mma(dPT[jt], fu, dor[vb]);
-            }
-#pragma unroll
-            for (int kb = 0; kb < K / 32; ++kb) {
-                Frag<T> fw, fk;
-                frag_row(fw, sW, S::LDK, jt * 16 + ln, kb * 32);
-                mma(dPT[jt], fw, dqf[kb]);
-                frag_row(fk, sK, S::LDK, jt * 16 + ln, kb * 32);
-                mma(PmQ[jt], fk, qr[kb]);
-            }
-        }
-    }
-    // mask, decay, the P terms of d(gam), and L .* dP
-    float drow = 0.f;  // d(gam_r) terms accumulated in this lane (summed over gq below)
-    f32x4 LdP[4];
-#pragma unroll
-    for (int jt = 0; jt < 4; ++jt) {
-        f32x4 colpart;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int j = jt * 16 + gq * 4 + i;
-            const float e = (j <= r) ? fast_exp(gr - sGam[j]) : 0.f;
-            const float p = PmQ[jt][i] * e;
-            const float x = dPT[jt][i] * p;  // dP .* P at (query r, key j)
-            drow += x;
-            colpart[i] = x;
-            LdP[jt][i] = dPT[jt][i] * e;
-        }
-        // column sums over the wave's 16 query rows -> key j
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float s = sum_ln(colpart[i]);
-            if (ln == 0) sRed[wave * 64 + jt * 16 + gq * 4 + i] = -s;
-        }
-    }
-    // d(gam_r) += e^{gam_r} sum_k dQt[r][k] Q[r][k]
-    const float egr = fast_exp(gr);
-    {
-        float acc = 0.f;
-#pragma unroll
-        for (int kt = 0; kt < K / 16; ++kt) {
-            const T* qp = sQ + r * S::LDK + kt * 16 + gq * 4;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) acc += dQT[kt][i] * Elem<T>::to_f(qp[i]);
-        }
-        drow += egr * acc;
-    }
-    // dq^T = e^{gam_r} dQt^T + K^T (L .* dP)^T
-    Frag<T> lf[2];
-    frag_acc(lf[0], LdP[0], LdP[1]);
-    frag_acc(lf[1], LdP[2], LdP[3]);
-    {
-        T* dq = reinterpret_cast<T*>(a.dq) + ((t0 + r) * H + h) * K;
-#pragma unroll
-        for (int kt = 0; kt < K / 16; ++kt) {
-            f32x4 acc = dQT[kt] * egr;
-#pragma unroll
-            for (int jb = 0; jb < 2; ++jb) {
-                Frag<T> fk;
-                frag_col(fk, sK, S::LDK, kt * 16 + ln, jb * 32);  // K^T row k, slots j
-                mma(acc, fk, lf[jb]);
-            }
-            if (r < c) store4(dq + kt * 16 + gq * 4, acc);
-        }
-    }
-    // exchange L .* dP: sX[key j][query r] = (L .* dP)[r][j]
-#pragma unroll
-    for (int jt = 0; jt < 4; ++jt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sX[(jt * 16 + gq * 4 + i) * S::LDX + r] = Elem<T>::from_f(LdP[jt][i]);
-    // d(gam) from Kt: -e^{Gam-gam_r} sum_k dKt[r][k] K[r][k]; the chunk total gets the sum
-    float ktk = 0.f;
-#pragma unroll
-    for (int kt = 0; kt < K / 16; ++kt) {
-        const T* kp = sK + r * S::LDK + kt * 16 + gq * 4;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) ktk += dKT[kt][i] * Elem<T>::to_f(kp[i]);
-    }
-    ktk *= ekt;
-    drow -= ktk;
-    // e^Gam <G, S> over the whole state (each thread a slice)
-    float gs = 0.f;
-    {
-        constexpr int VEC = Elem<T>::kVec;
-#pragma unroll 4
-        for (int e = tid; e < V * K / VEC; e += 256) {
-            const int vv = e / (K / VEC), kk = (e % (K / VEC)) * VEC;
-            const u32x4 xg = *reinterpret_cast<const u32x4*>(sG + vv * S::LDK + kk);
-            const u32x4 xs = *reinterpret_cast<const u32x4*>(sS + vv * S::LDK + kk);
-            if constexpr (sizeof(T) == 2) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    gs += bf2f((bf16_t)(xg[i] & 0xFFFFu)) * bf2f((bf16_t)(xs[i] & 0xFFFFu)) +
-                          bf2f((bf16_t)(xg[i] >> 16)) * bf2f((bf16_t)(xs[i] >> 16));
-            } else {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) gs += __uint_as_float(xg[i]) * __uint_as_float(xs[i]);
-            }
-        }
-    }
-    {
-        float t = ktk;  // one value per (r, gq); summed over all lanes it is sum_r
-        t = sum_gq(t);
-        t = sum_ln(t);
-        gs = sum_gq(sum_ln(gs));
-        if (lane == 0) {
-            sSc[wave] = t;
-            sSc[4 + wave] = gs;
-        }
-    }
-    drow = sum_gq(drow);
-    if (gq == 0) sRow[r] = drow;
-    lds_sync();
-    // dk part for the wave's rows as keys: e^{Gam-gam_r} dKt^T + Q^T (L .* dP)[:, r]
-    {
-        Frag<T> xf[2];
-        frag_row(xf[0], sX, S::LDX, r, 0);
-        frag_row(xf[1], sX, S::LDX, r, 32);
-        float* dkp = a.dk_part + ((t0 + r) * H + h) * K;
-        float* dwp = a.dw + ((t0 + r) * H + h) * K;
-#pragma unroll
-        for (int kt = 0; kt < K / 16; ++kt) {
-            f32x4 acc = dKT[kt] * ekt;
-#pragma unroll
-            for (int yb = 0; yb < 2; ++yb) {
-                Frag<T> fq;
-                frag_col(fq, sQ, S::LDK, kt * 16 + ln, yb * 32);  // Q^T row k, slots y
-                mma(acc, fq, xf[yb]);
-            }
-            if (r < c) {
-                *reinterpret_cast<f32x4*>(dkp + kt * 16 + gq * 4) = acc;
-                *reinterpret_cast<f32x4*>(dwp + kt * 16 + gq * 4) = dWT[kt];
-            }
-        }
-        float* dup = a.du + ((t0 + r) * H + h) * V;
-        if (r < c) {
-#pragma unroll
-            for (int vt = 0; vt < V / 16; ++vt) *reinterpret_cast<f32x4*>(dup + vt * 16 + gq * 4) = DDT[vt];
-        }
-    }
-    if (tid < 64) {
-        float d = sRow[tid] + sRed[tid] + sRed[64 + tid] + sRed[128 + tid] + sRed[192 + tid];
-        if (tid == c - 1) {
-            const float kt_all = sSc[0] + sSc[1] + sSc[2] + sSc[3];
-            const float gs_all = sSc[4] + sSc[5] + sSc[6] + sSc[7];
-            d += kt_all + fast_exp(Gm) * gs_all;
-        }
-        if (tid < c) a.dgam_part[(t0 + tid) * H + h] = d;
-    }
-}
-
-// ---------------------------------------------------------------------------
-// WY-side per-chunk gradients. One workgroup (4 waves) per (chunk, head); wave w owns rows
-// a = 16w .. 16w+15. Recomputes A and T = (I + A)^{-1} as the intra-chunk kernel does.
-template <typename T, int K, int V>
-struct WCfg {
-    static constexpr int LDK = K + BPad<T>::row;
-    static constexpr int LDV = V + BPad<T>::row;
-    static constexpr int kF = 64 * kLdA * 4;  // one fp32 64x64 matrix
-    static constexpr int off_k = 0;
-    static constexpr int off_v = off_k + 64 * LDK * (int)sizeof(T);
-    static constexpr int off_dw = off_v + 64 * LDV * (int)sizeof(T);
-    static constexpr int off_du = off_dw + 64 * LDK * (int)sizeof(T);
-    static constexpr int off_ar = off_du + 64 * LDV * (int)sizeof(T);  // e^{gam_a-gam_c} k_a.k_c (strict lower)
-    static constexpr int off_t = off_ar + kF;                           // T
-    static constexpr int off_r1 = off_t + kF;                           // A, then dT, then Mx
-    static constexpr int off_r2 = off_r1 + kF;                          // dT T^T
-    static constexpr int off_gam = off_r2 + kF;
-    static constexpr int off_beta = off_gam + 256;
-    static constexpr int off_red = off_beta + 256;  // [4][64]
-    static constexpr int off_row = off_red + 4 * 64 * 4;
-    static constexpr int total = off_row + 256;
-};
 
 // fp32 LDS column fragment converted to the operand type.
 template <typename T>
@@ -823,283 +600,513 @@ __device__ __forceinline__ void frag_row_f32cvt(Frag<T>& f, const float* base, i
     }
 }
 
-// fp32 rows [64][D] from global into LDS in the operand type (loads issued first).
-template <typename T, int D>
-__device__ __forceinline__ void copy_rows_f32(T* dst, int ld_s, const float* src, size_t ld_g, int rows) {
-    constexpr int NV = D / 4;
-    constexpr int IT = 64 * NV / 256;
-    f32x4 x[IT];
-#pragma unroll
-    for (int it = 0; it < IT; ++it) {
-        const int e = threadIdx.x + it * 256;
-        const int r = e / NV, cv = e % NV;
-        x[it] = r < rows ? *reinterpret_cast<const f32x4*>(src + (size_t)r * ld_g + cv * 4) : zero4();
-    }
-#pragma unroll
-    for (int it = 0; it < IT; ++it) {
-        const int e = threadIdx.x + it * 256;
-        const int r = e / NV, cv = e % NV;
-        store4(dst + r * ld_s + cv * 4, x[it]);
-    }
-}
-
 template <typename T, int K, int V>
-__global__ __launch_bounds__(256) void k_bwd_wy(BwdChunkArgs a) {
-    using S = WCfg<T, K, V>;
+__global__ __launch_bounds__(256) void k_bwd_chunk(BwdChunkArgs a) {
+    using C = BCfg<T, K, V>;
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-    T* sK = reinterpret_cast<T*>(smem + S::off_k);
-    T* sV = reinterpret_cast<T*>(smem + S::off_v);
-    T* sdW = reinterpret_cast<T*>(smem + S::off_dw);
-    T* sdU = reinterpret_cast<T*>(smem + S::off_du);
-    float* sAr = reinterpret_cast<float*>(smem + S::off_ar);
-    float* sT = reinterpret_cast<float*>(smem + S::off_t);
-    float* sR1 = reinterpret_cast<float*>(smem + S::off_r1);
-    float* sR2 = reinterpret_cast<float*>(smem + S::off_r2);
-    float* sGam = reinterpret_cast<float*>(smem + S::off_gam);
-    float* sBeta = reinterpret_cast<float*>(smem + S::off_beta);
-    float* sRed = reinterpret_cast<float*>(smem + S::off_red);
-    float* sRow = reinterpret_cast<float*>(smem + S::off_row);
+    T* sK = reinterpret_cast<T*>(smem + C::off_k);
+    T* sS = reinterpret_cast<T*>(smem + C::off_s);
+    T* sG = reinterpret_cast<T*>(smem + C::off_g);
+    T* sQ = reinterpret_cast<T*>(smem + C::off_q);
+    T* sW = reinterpret_cast<T*>(smem + C::off_w);
+    T* sD = reinterpret_cast<T*>(smem + C::off_d);
+    T* sU = reinterpret_cast<T*>(smem + C::off_u);
+    T* sX = reinterpret_cast<T*>(smem + C::off_x);
+    float* sAr = reinterpret_cast<float*>(smem + C::off_ar);
+    float* sT = reinterpret_cast<float*>(smem + C::off_t);
+    float* sR1 = reinterpret_cast<float*>(smem + C::off_r1);
+    float* sR2 = reinterpret_cast<float*>(smem + C::off_r2);
+    T* sV = reinterpret_cast<T*>(smem + C::off_v);
+    T* sdW = reinterpret_cast<T*>(smem + C::off_dw);
+    T* sdU = reinterpret_cast<T*>(smem + C::off_du);
+    float* sGam = reinterpret_cast<float*>(smem + C::off_gam);
+    float* sBeta = reinterpret_cast<float*>(smem + C::off_beta);
+    float* sRed = reinterpret_cast<float*>(smem + C::off_red);
+    float* sRow = reinterpret_cast<float*>(smem + C::off_row);
+    float* sDgs = reinterpret_cast<float*>(smem + C::off_dgs);
+    float* sSc = reinterpret_cast<float*>(smem + C::off_sc);
 
     const Geo& geo = a.geo;
-    const int64_t gc = blockIdx.x;
-    const int h = blockIdx.y;
-    ChunkLoc L;
-    if (!locate_chunk(geo, gc, L)) return;
     const int64_t H = geo.H;
-    const int c = L.c;
-    const int64_t t0 = L.t0;
+    const int64_t ntasks = geo.total_chunks * H;
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63, ln = lane & 15, gq = lane >> 4;
-    const int ra = wave * 16 + ln;  // this lane's row a in "column" roles
+    const int r = wave * 16 + ln;  // this lane's chunk row in "column" roles
 
-    copy_rows<T, K, 64>(sK, S::LDK, reinterpret_cast<const T*>(a.k) + (t0 * H + h) * K, (size_t)H * K, c);
-    copy_rows<T, V, 64>(sV, S::LDV, reinterpret_cast<const T*>(a.v) + (t0 * H + h) * V, (size_t)H * V, c);
-    copy_rows_f32<T, K>(sdW, S::LDK, a.dw + (t0 * H + h) * K, (size_t)H * K, c);
-    copy_rows_f32<T, V>(sdU, S::LDV, a.du + (t0 * H + h) * V, (size_t)H * V, c);
-    if (tid < 64) {
-        const bool in = tid < c;
-        sGam[tid] = a.gam[(t0 + (in ? tid : c - 1)) * H + h];
-        sBeta[tid] = in ? a.beta[(t0 + tid) * H + h] : 0.f;
-    }
-    lds_sync();
+    BTask cur;
+    int64_t t = bwd_next_task(geo, blockIdx.x, ntasks, cur);
+    if (t >= ntasks) return;
+    BRegs<T, K, V> R;  // the next task's operands
+    u32x4 rv[C::NV];    // v of this task
+    bwd_fetch_states(R, a, cur);
+    bwd_fetch_rows(R, a, cur);
+    bwd_fetch_v(R, a, cur);
 
-    // ---- A (for the inverse) and e^{gam_a - gam_c} k_a.k_c -------------------------------
-    for (int idx = wave; idx < 10; idx += 4) {
-        const int ti = kTriB[idx][0], tj = kTriB[idx][1];
-        f32x4 acc = zero4();
-#pragma unroll
-        for (int kb = 0; kb < K / 32; ++kb) {
-            Frag<T> fa, fb;
-            frag_row(fa, sK, S::LDK, ti * 16 + ln, kb * 32);
-            frag_row(fb, sK, S::LDK, tj * 16 + ln, kb * 32);
-            mma(acc, fb, fa);  // rows j = tj*16.., cols i = ti*16+ln: lane holds (KK)[i][j]
+    for (;;) {
+        // ---- stage this task (the previous task's LDS reads are done) ---------------------
+        lds_sync();
+        put_tile<T, K>(sS, C::LDK, R.s);
+        put_tile<T, K>(sG, C::LDK, R.g);
+        put_tile<T, K>(sQ, C::LDK, R.q);
+        put_tile<T, K>(sK, C::LDK, R.k);
+        put_tile<T, K>(sW, C::LDK, R.w);
+        // dO enters every product together with the query scale (o = scale S q)
+        put_tile<T, V>(sD, C::LDV, R.d, a.scale);
+        put_tile<T, V>(sU, C::LDV, R.u);
+        if (tid < 64) {
+            sGam[tid] = R.gam;
+            sBeta[tid] = R.beta;
         }
-        const int i = ti * 16 + ln;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int j = tj * 16 + gq * 4 + e;
-            const float ar = (j < i) ? fast_exp(sGam[i] - sGam[j]) * acc[e] : 0.f;
-            sAr[i * kLdA + j] = ar;
-            sR1[i * kLdA + j] = sBeta[i] * ar;
-        }
-    }
-    lds_sync();
-    tri_inverse64(sR1, sT);
+        for (int i = 0; i < C::NV; ++i) rv[i] = R.v[i];
+        lds_sync();
+        // The last task fetches itself again: unconditional fetches end the previous
+        // operands' live range at the staging above.
+        BTask nxt = cur;
+        const int64_t tn = bwd_next_task(geo, t + gridDim.x, ntasks, nxt);
+        const bool more = tn < ntasks;
+        if (!more) nxt = cur;
 
-    // ---- dT[a][b] = beta_b e^{gam_b} (dW K^T)[a][b] + beta_b (dU V^T)[a][b], b < a part ----
-    f32x4 dT[4];
-    {
-        Frag<T> wf[K / 32], uf[V / 32];
+        const int c = cur.c;
+        const int64_t t0 = cur.t0;
+        const int h = cur.h;
+        const float Gm = sGam[63];
+        const float gr = sGam[r];
+
+        // ================================ state side ===================================
+        // e^Gam <G, S> over the whole state (each thread a slice)
+        float gs = 0.f;
+        {
+            constexpr int VEC = Elem<T>::kVec;
+#pragma unroll 4
+            for (int e = tid; e < V * K / VEC; e += 256) {
+                const int vv = e / (K / VEC), kk = (e % (K / VEC)) * VEC;
 #pragma unroll
-        for (int kb = 0; kb < K / 32; ++kb) frag_row(wf[kb], sdW, S::LDK, ra, kb * 32);
+                for (int i = 0; i < VEC; i += 4)
+                    gs += dot4(ld4(sG + vv * C::LDK + kk + i), ld4(sS + vv * C::LDK + kk + i));
+            }
+        }
+        // ---- P tiles with the wave's rows as keys: PmK[jt] = P^T restricted (rows j, cols r)
+        f32x4 PmK[4];
 #pragma unroll
-        for (int vb = 0; vb < V / 32; ++vb) frag_row(uf[vb], sdU, S::LDV, ra, vb * 32);
-#pragma unroll
-        for (int bt = 0; bt < 4; ++bt) {
-            f32x4 x = zero4(), y = zero4();
-            if (bt <= wave) {
+        for (int jt = 0; jt < 4; ++jt) {
+            PmK[jt] = zero4();
+            if (jt >= wave) {
 #pragma unroll
                 for (int kb = 0; kb < K / 32; ++kb) {
-                    Frag<T> fk;
-                    frag_row(fk, sK, S::LDK, bt * 16 + ln, kb * 32);
-                    mma(x, fk, wf[kb]);  // rows b, cols a: (K dW^T)[b][a]
-                }
-#pragma unroll
-                for (int vb = 0; vb < V / 32; ++vb) {
-                    Frag<T> fv;
-                    frag_row(fv, sV, S::LDV, bt * 16 + ln, vb * 32);
-                    mma(y, fv, uf[vb]);
+                    Frag<T> fa, fb;
+                    frag_row(fa, sQ, C::LDK, jt * 16 + ln, kb * 32);
+                    frag_row(fb, sK, C::LDK, r, kb * 32);
+                    mma(PmK[jt], fa, fb);
                 }
             }
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int b = bt * 16 + gq * 4 + e;
-                dT[bt][e] = (b < ra) ? sBeta[b] * (fast_exp(sGam[b]) * x[e] + y[e]) : 0.f;
+            for (int i = 0; i < 4; ++i) {
+                const int j = jt * 16 + gq * 4 + i;
+                PmK[jt][i] = (j >= r) ? PmK[jt][i] * fast_exp(sGam[j] - gr) : 0.f;
             }
         }
-    }
-    // stage dT (row a, column b) over A, which the inverse no longer needs
+        // ---- Delta^T[v][r] = U[r][v] - (S W^T)[v][r];  dDelta^T = dO^T P + G K~^T ----------
+        f32x4 DT[V / 16], DDT[V / 16];
+        Frag<T> wr[K / 32], kr[K / 32];
 #pragma unroll
-    for (int bt = 0; bt < 4; ++bt)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) sR1[ra * kLdA + bt * 16 + gq * 4 + e] = dT[bt][e];
-    lds_sync();
-    // ---- Y = dT T^T (fp32): Y[a][c] = sum_b dT[a][b] T[c][b] ---------------------------------
-    {
-        Frag<float> da[2];
-        frag_row(da[0], sR1, kLdA, ra, 0);
-        frag_row(da[1], sR1, kLdA, ra, 32);
-#pragma unroll
-        for (int ct = 0; ct < 4; ++ct) {
-            f32x4 y = zero4();
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                Frag<float> ft;
-                frag_row(ft, sT, kLdA, ct * 16 + ln, kb * 32);
-                mma(y, ft, da[kb]);  // rows c, cols a: Y^T
-            }
-#pragma unroll
-            for (int e = 0; e < 4; ++e) sR2[ra * kLdA + ct * 16 + gq * 4 + e] = y[e];
+        for (int kb = 0; kb < K / 32; ++kb) {
+            Frag<T> f;
+            frag_row(f, sW, C::LDK, r, kb * 32);
+            wr[kb] = neg(f);
+            frag_row(kr[kb], sK, C::LDK, r, kb * 32);
         }
-    }
-    lds_sync();
-    // ---- dA[a][c] = -sum_x T[x][a] Y[x][c], strict lower; its consumers ----------------------
-    float dbeta_row = 0.f, dgam_row = 0.f;
-    {
-        Frag<float> ta[2];
-        frag_col(ta[0], sT, kLdA, ra, 0);   // T^T row a, slots x
-        frag_col(ta[1], sT, kLdA, ra, 32);
-#pragma unroll
-        for (int ct = 0; ct < 4; ++ct) {
-            f32x4 d = zero4();
-            if (ct <= wave) {
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb) {
-                    Frag<float> fy;
-                    frag_col(fy, sR2, kLdA, ct * 16 + ln, kb * 32);  // Y^T row c, slots x
-                    mma(d, fy, ta[kb]);  // rows c, cols a: (T^T Y)^T
-                }
-            }
-            f32x4 colpart;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int cc = ct * 16 + gq * 4 + e;
-                const float dA = (cc < ra) ? -d[e] : 0.f;
-                const float ar = (cc < ra) ? sAr[ra * kLdA + cc] : 0.f;  // upper blocks never written
-                const float av = sBeta[ra] * ar;  // A[a][c]
-                dbeta_row += dA * ar;
-                dgam_row += dA * av;
-                colpart[e] = dA * av;
-                d[e] = dA * sBeta[ra] * ((cc < ra) ? fast_exp(sGam[ra] - sGam[cc]) : 0.f);  // Mx[a][c]
-            }
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const float s = sum_ln(colpart[e]);
-                if (ln == 0) sRed[wave * 64 + ct * 16 + gq * 4 + e] = -s;
-            }
-            // Mx[a][c] staged in R1: dT was consumed by Y, and R2 (Y) is still being read
-#pragma unroll
-            for (int e = 0; e < 4; ++e) sR1[ra * kLdA + ct * 16 + gq * 4 + e] = d[e];
-        }
-    }
-    lds_sync();
-    // ---- dBk^T = dW^T T, dBv^T = dU^T T (rows k / v, cols a);  dK, dV --------------------
-    Frag<T> tcol[2];
-    frag_col_f32(tcol[0], sT, kLdA, ra, 0);  // T column a, slots x
-    frag_col_f32(tcol[1], sT, kLdA, ra, 32);
-    Frag<T> mrow[2], mcol[2];
-    frag_row_f32cvt(mrow[0], sR1, kLdA, ra, 0);  // Mx row a, slots c
-    frag_row_f32cvt(mrow[1], sR1, kLdA, ra, 32);
-    frag_col_f32(mcol[0], sR1, kLdA, ra, 0);     // Mx column a, slots c
-    frag_col_f32(mcol[1], sR1, kLdA, ra, 32);
-    const float ba = sBeta[ra], ega = fast_exp(sGam[ra]);
-    {
-        T* dkp = reinterpret_cast<T*>(a.dk) + ((t0 + ra) * H + h) * K;
-        const float* dkq = a.dk_part + ((t0 + ra) * H + h) * K;
-#pragma unroll
-        for (int kt = 0; kt < K / 16; ++kt) {
-            f32x4 bk = zero4(), mk = zero4();
-#pragma unroll
-            for (int xb = 0; xb < 2; ++xb) {
-                Frag<T> fw, fk;
-                frag_col(fw, sdW, S::LDK, kt * 16 + ln, xb * 32);  // dW^T row k, slots x
-                mma(bk, fw, tcol[xb]);
-                frag_col(fk, sK, S::LDK, kt * 16 + ln, xb * 32);   // K^T row k, slots c
-                mma(mk, fk, mrow[xb]);
-                mma(mk, fk, mcol[xb]);
-            }
-            // dbeta, dgam from Bk = diag(beta e^gam) K
-            const T* kr = sK + ra * S::LDK + kt * 16 + gq * 4;
-            float s = 0.f;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) s += bk[e] * Elem<T>::to_f(kr[e]);
-            dbeta_row += ega * s;
-            dgam_row += ba * ega * s;
-            if (ra < c) {
-                const f32x4 part = *reinterpret_cast<const f32x4*>(dkq + kt * 16 + gq * 4);
-                store4(dkp + kt * 16 + gq * 4, part + mk + bk * (ba * ega));
-            }
-        }
-    }
-    {
-        T* dvp = reinterpret_cast<T*>(a.dv) + ((t0 + ra) * H + h) * V;
+        const float ekt = fast_exp(Gm - gr);
 #pragma unroll
         for (int vt = 0; vt < V / 16; ++vt) {
-            f32x4 bv = zero4();
+            DT[vt] = ld4(sU + r * C::LDV + vt * 16 + gq * 4);
+            DDT[vt] = zero4();
 #pragma unroll
-            for (int xb = 0; xb < 2; ++xb) {
-                Frag<T> fu;
-                frag_col(fu, sdU, S::LDV, vt * 16 + ln, xb * 32);  // dU^T row v, slots x
-                mma(bv, fu, tcol[xb]);
+            for (int kb = 0; kb < K / 32; ++kb) {
+                Frag<T> fs, fg;
+                frag_row(fs, sS, C::LDK, vt * 16 + ln, kb * 32);
+                mma(DT[vt], fs, wr[kb]);
+                frag_row(fg, sG, C::LDK, vt * 16 + ln, kb * 32);
+                mma(DDT[vt], fg, kr[kb]);
             }
-            const T* vr = sV + ra * S::LDV + vt * 16 + gq * 4;
+            DDT[vt] *= ekt;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) dbeta_row += bv[e] * Elem<T>::to_f(vr[e]);
-            if (ra < c) store4(dvp + vt * 16 + gq * 4, bv * ba);
+            for (int jb = 0; jb < 2; ++jb) {
+                Frag<T> fd, fp;
+                frag_col(fd, sD, C::LDV, vt * 16 + ln, jb * 32);  // dO^T row v, slots j
+                frag_acc(fp, PmK[2 * jb], PmK[2 * jb + 1]);
+                mma(DDT[vt], fd, fp);
+            }
         }
-    }
-    dbeta_row = sum_gq(dbeta_row);
-    dgam_row = sum_gq(dgam_row);
-    if (gq == 0) sRow[ra] = dgam_row;
-    if (gq == 0 && ra < c) a.dbeta[(t0 + ra) * H + h] = dbeta_row;
-    lds_sync();
-    // ---- d(gam) total and dg = reverse cumulative sum within the chunk -------------------
-    if (wave == 0) {
-        float d = 0.f;
-        if (lane < c)
-            d = a.dgam_part[(t0 + lane) * H + h] + sRow[lane] + sRed[lane] + sRed[64 + lane] + sRed[128 + lane] +
-                sRed[192 + lane];
-        // suffix sum over lanes lane..63
+        // ---- dQt^T, dW^T = -(S^T dDelta^T), dKt^T = G^T Delta^T  (rows k, cols r) --------
+        f32x4 dQT[K / 16], dWT[K / 16], dKT[K / 16];
+        Frag<T> dor[V / 32];
+        {
+            Frag<T> ddf[V / 32], dtf[V / 32];
 #pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const float y = __shfl_down(d, off, 64);
-            if (lane + off < 64) d += y;
+            for (int vb = 0; vb < V / 32; ++vb) {
+                frag_row(dor[vb], sD, C::LDV, r, vb * 32);
+                frag_acc(ddf[vb], DDT[2 * vb], DDT[2 * vb + 1], -1.f);
+                frag_acc(dtf[vb], DT[2 * vb], DT[2 * vb + 1]);
+            }
+            lds_sync();  // every read of dO is done: dU = dDelta (rows r) goes over it
+#pragma unroll
+            for (int vt = 0; vt < V / 16; ++vt)
+                store4(sdU + r * C::LDV + vt * 16 + gq * 4, r < c ? DDT[vt] : zero4());
+#pragma unroll
+            for (int kt = 0; kt < K / 16; ++kt) {
+                dQT[kt] = zero4();
+                dWT[kt] = zero4();
+                dKT[kt] = zero4();
+#pragma unroll
+                for (int vb = 0; vb < V / 32; ++vb) {
+                    Frag<T> fs, fg;
+                    frag_col(fs, sS, C::LDK, kt * 16 + ln, vb * 32);  // S^T row k, slots v
+                    mma(dQT[kt], fs, dor[vb]);
+                    mma(dWT[kt], fs, ddf[vb]);
+                    frag_col(fg, sG, C::LDK, kt * 16 + ln, vb * 32);  // G^T row k, slots v
+                    mma(dKT[kt], fg, dtf[vb]);
+                }
+            }
         }
-        if (lane < c) a.dg[(t0 + lane) * H + h] = d;
+        lds_sync();  // every read of S and G is done: dW (rows r) goes over S
+#pragma unroll
+        for (int kt = 0; kt < K / 16; ++kt) store4(sdW + r * C::LDK + kt * 16 + gq * 4, r < c ? dWT[kt] : zero4());
+        bwd_fetch_rows(R, a, nxt);  // in flight over the rest of this task
+        // ---- dP^T[j][r] = (U dO^T)[j][r] - (W dQt^T)[j][r];  P with the wave's rows as queries
+        f32x4 dPT[4], PmQ[4];
+        {
+            Frag<T> dqf[K / 32], qr[K / 32];
+#pragma unroll
+            for (int kb = 0; kb < K / 32; ++kb) {
+                frag_acc(dqf[kb], dQT[2 * kb], dQT[2 * kb + 1], -1.f);
+                frag_row(qr[kb], sQ, C::LDK, r, kb * 32);
+            }
+#pragma unroll
+            for (int jt = 0; jt < 4; ++jt) {
+                dPT[jt] = zero4();
+                PmQ[jt] = zero4();
+                if (jt <= wave) {
+#pragma unroll
+                    for (int vb = 0; vb < V / 32; ++vb) {
+                        Frag<T> fu;
+                        frag_row(fu, sU, C::LDV, jt * 16 + ln, vb * 32);
+                        mma(dPT[jt], fu, dor[vb]);
+                    }
+#pragma unroll
+                    for (int kb = 0; kb < K / 32; ++kb) {
+                        Frag<T> fw, fk;
+                        frag_row(fw, sW, C::LDK, jt * 16 + ln, kb * 32);
+                        mma(dPT[jt], fw, dqf[kb]);
+                        frag_row(fk, sK, C::LDK, jt * 16 + ln, kb * 32);
+                        mma(PmQ[jt], fk, qr[kb]);
+                    }
+                }
+            }
+        }
+        // mask, decay, the P terms of d(gam), and L .* dP
+        float drow = 0.f;  // d(gam_r) terms accumulated in this lane (summed over gq below)
+        f32x4 LdP[4];
+#pragma unroll
+        for (int jt = 0; jt < 4; ++jt) {
+            f32x4 colpart;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int j = jt * 16 + gq * 4 + i;
+                const float e = (j <= r) ? fast_exp(gr - sGam[j]) : 0.f;
+                const float x = dPT[jt][i] * PmQ[jt][i] * e;  // dP .* P at (query r, key j)
+                drow += x;
+                colpart[i] = x;
+                LdP[jt][i] = dPT[jt][i] * e;
+            }
+            // column sums over the wave's 16 query rows -> key j
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float s = sum_ln(colpart[i]);
+                if (ln == 0) sRed[wave * 64 + jt * 16 + gq * 4 + i] = -s;
+            }
+        }
+        // d(gam_r) += e^{gam_r} sum_k dQt[r][k] Q[r][k]
+        const float egr = fast_exp(gr);
+        {
+            float acc = 0.f;
+#pragma unroll
+            for (int kt = 0; kt < K / 16; ++kt) acc += dot4(dQT[kt], ld4(sQ + r * C::LDK + kt * 16 + gq * 4));
+            drow += egr * acc;
+        }
+        // dq^T = e^{gam_r} dQt^T + K^T (L .* dP)^T
+        {
+            Frag<T> lf[2];
+            frag_acc(lf[0], LdP[0], LdP[1]);
+            frag_acc(lf[1], LdP[2], LdP[3]);
+            T* dq = reinterpret_cast<T*>(a.dq) + ((t0 + r) * H + h) * K;
+#pragma unroll
+            for (int kt = 0; kt < K / 16; ++kt) {
+                f32x4 acc = dQT[kt] * egr;
+#pragma unroll
+                for (int jb = 0; jb < 2; ++jb) {
+                    Frag<T> fk;
+                    frag_col(fk, sK, C::LDK, kt * 16 + ln, jb * 32);  // K^T row k, slots j
+                    mma(acc, fk, lf[jb]);
+                }
+                if (r < c) store4(dq + kt * 16 + gq * 4, acc);
+            }
+        }
+        // d(gam) from Kt: -e^{Gam-gam_r} sum_k dKt[r][k] K[r][k]; the chunk total gets the sum
+        float ktk = 0.f;
+#pragma unroll
+        for (int kt = 0; kt < K / 16; ++kt) ktk += dot4(dKT[kt], ld4(sK + r * C::LDK + kt * 16 + gq * 4));
+        ktk *= ekt;
+        drow -= ktk;
+        {
+            float t1 = sum_ln(sum_gq(ktk));  // one value per (r, gq); summed over all lanes it is sum_r
+            const float g1 = sum_gq(sum_ln(gs));
+            if (lane == 0) {
+                sSc[wave] = t1;
+                sSc[4 + wave] = g1;
+            }
+        }
+        drow = sum_gq(drow);
+        if (gq == 0) sRow[r] = drow;
+        lds_sync();  // every read of U is done: the exchange overwrites it
+        // exchange L .* dP: sX[key j][query r] = (L .* dP)[r][j]
+#pragma unroll
+        for (int jt = 0; jt < 4; ++jt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sX[(jt * 16 + gq * 4 + i) * C::LDX + r] = Elem<T>::from_f(LdP[jt][i]);
+        lds_sync();
+        // dk terms of the state side for the wave's rows as keys: e^{Gam-gam_r} dKt^T + Q^T (L .* dP)[:, r]
+        f32x4 dkpart[K / 16];
+        {
+            Frag<T> xf[2];
+            frag_row(xf[0], sX, C::LDX, r, 0);
+            frag_row(xf[1], sX, C::LDX, r, 32);
+#pragma unroll
+            for (int kt = 0; kt < K / 16; ++kt) {
+                dkpart[kt] = dKT[kt] * ekt;
+#pragma unroll
+                for (int yb = 0; yb < 2; ++yb) {
+                    Frag<T> fq;
+                    frag_col(fq, sQ, C::LDK, kt * 16 + ln, yb * 32);  // Q^T row k, slots y
+                    mma(dkpart[kt], fq, xf[yb]);
+                }
+            }
+        }
+        lds_sync();  // the state side's LDS reads are done: the WY side reuses the space
+
+        // ================================= WY side =====================================
+        if (tid < 64) {
+            float d = sRow[tid] + sRed[tid] + sRed[64 + tid] + sRed[128 + tid] + sRed[192 + tid];
+            if (tid == c - 1) {
+                const float kt_all = sSc[0] + sSc[1] + sSc[2] + sSc[3];
+                const float gs_all = sSc[4] + sSc[5] + sSc[6] + sSc[7];
+                d += kt_all + fast_exp(Gm) * gs_all;
+            }
+            sDgs[tid] = d;
+        }
+        put_tile<T, V>(sV, C::LDV, rv);
+        bwd_fetch_states(R, a, nxt);
+        bwd_fetch_v(R, a, nxt);
+        // ---- A (for the inverse) and e^{gam_a - gam_c} k_a.k_c ------------------------------
+        // (reads only K, gam and beta, which the stores above do not touch)
+        for (int idx = wave; idx < 10; idx += 4) {
+            const int ti = kTriB[idx][0], tj = kTriB[idx][1];
+            f32x4 acc = zero4();
+#pragma unroll
+            for (int kb = 0; kb < K / 32; ++kb) {
+                Frag<T> fa, fb;
+                frag_row(fa, sK, C::LDK, ti * 16 + ln, kb * 32);
+                frag_row(fb, sK, C::LDK, tj * 16 + ln, kb * 32);
+                mma(acc, fb, fa);  // rows j = tj*16.., cols i = ti*16+ln: lane holds (KK)[i][j]
+            }
+            const int i = ti * 16 + ln;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int j = tj * 16 + gq * 4 + e;
+                const float ar = (j < i) ? fast_exp(sGam[i] - sGam[j]) * acc[e] : 0.f;
+                sAr[i * kLdA + j] = ar;
+                sR1[i * kLdA + j] = sBeta[i] * ar;
+            }
+        }
+        lds_sync();
+        tri_inverse64(sR1, sT);
+        const int ra = r;
+        // ---- dT[a][b] = beta_b e^{gam_b} (dW K^T)[a][b] + beta_b (dU V^T)[a][b], b < a part -
+        f32x4 dT[4];
+        {
+            Frag<T> wf[K / 32], uf[V / 32];
+#pragma unroll
+            for (int kb = 0; kb < K / 32; ++kb) frag_row(wf[kb], sdW, C::LDK, ra, kb * 32);
+#pragma unroll
+            for (int vb = 0; vb < V / 32; ++vb) frag_row(uf[vb], sdU, C::LDV, ra, vb * 32);
+#pragma unroll
+            for (int bt = 0; bt < 4; ++bt) {
+                f32x4 x = zero4(), y = zero4();
+                if (bt <= wave) {
+#pragma unroll
+                    for (int kb = 0; kb < K / 32; ++kb) {
+                        Frag<T> fk;
+                        frag_row(fk, sK, C::LDK, bt * 16 + ln, kb * 32);
+                        mma(x, fk, wf[kb]);  // rows b, cols a: (K dW^T)[b][a]
+                    }
+#pragma unroll
+                    for (int vb = 0; vb < V / 32; ++vb) {
+                        Frag<T> fv;
+                        frag_row(fv, sV, C::LDV, bt * 16 + ln, vb * 32);
+                        mma(y, fv, uf[vb]);
+                    }
+                }
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int b = bt * 16 + gq * 4 + e;
+                    dT[bt][e] = (b < ra) ? sBeta[b] * (fast_exp(sGam[b]) * x[e] + y[e]) : 0.f;
+                }
+            }
+        }
+        // stage dT (row a, column b) over A, which the inverse no longer needs
+#pragma unroll
+        for (int bt = 0; bt < 4; ++bt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sR1[ra * kLdA + bt * 16 + gq * 4 + e] = dT[bt][e];
+        lds_sync();
+        // ---- Y = dT T^T (fp32): Y[a][c] = sum_b dT[a][b] T[c][b] -------------------------------
+        {
+            Frag<float> da[2];
+            frag_row(da[0], sR1, kLdA, ra, 0);
+            frag_row(da[1], sR1, kLdA, ra, 32);
+#pragma unroll
+            for (int ct = 0; ct < 4; ++ct) {
+                f32x4 y = zero4();
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb) {
+                    Frag<float> ft;
+                    frag_row(ft, sT, kLdA, ct * 16 + ln, kb * 32);
+                    mma(y, ft, da[kb]);  // rows c, cols a: Y^T
+                }
+#pragma unroll
+                for (int e = 0; e < 4; ++e) sR2[ra * kLdA + ct * 16 + gq * 4 + e] = y[e];
+            }
+        }
+        lds_sync();
+        // ---- dA[a][c] = -sum_x T[x][a] Y[x][c], strict lower; its consumers --------------------
+        float dbeta_row = 0.f, dgam_row = 0.f;
+        {
+            Frag<float> ta[2];
+            frag_col(ta[0], sT, kLdA, ra, 0);  // T^T row a, slots x
+            frag_col(ta[1], sT, kLdA, ra, 32);
+#pragma unroll
+            for (int ct = 0; ct < 4; ++ct) {
+                f32x4 d = zero4();
+                if (ct <= wave) {
+#pragma unroll
+                    for (int kb = 0; kb < 2; ++kb) {
+                        Frag<float> fy;
+                        frag_col(fy, sR2, kLdA, ct * 16 + ln, kb * 32);  // Y^T row c, slots x
+                        mma(d, fy, ta[kb]);  // rows c, cols a: (T^T Y)^T
+                    }
+                }
+                f32x4 colpart;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int cc = ct * 16 + gq * 4 + e;
+                    const float dA = (cc < ra) ? -d[e] : 0.f;
+                    const float ar = (cc < ra) ? sAr[ra * kLdA + cc] : 0.f;  // upper blocks never written
+                    const float av = sBeta[ra] * ar;  // A[a][c]
+                    dbeta_row += dA * ar;
+                    dgam_row += dA * av;
+                    colpart[e] = dA * av;
+                    d[e] = dA * sBeta[ra] * ((cc < ra) ? fast_exp(sGam[ra] - sGam[cc]) : 0.f);  // Mx[a][c]
+                }
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float s = sum_ln(colpart[e]);
+                    if (ln == 0) sRed[wave * 64 + ct * 16 + gq * 4 + e] = -s;
+                }
+                // Mx[a][c] staged in R1: dT was consumed by Y, and R2 (Y) is still being read
+#pragma unroll
+                for (int e = 0; e < 4; ++e) sR1[ra * kLdA + ct * 16 + gq * 4 + e] = d[e];
+            }
+        }
+        lds_sync();
+        // ---- dBk^T = dW^T T, dBv^T = dU^T T (rows k / v, cols a);  dK, dV ----------------------
+        Frag<T> tcol[2];
+        frag_col_f32(tcol[0], sT, kLdA, ra, 0);  // T column a, slots x
+        frag_col_f32(tcol[1], sT, kLdA, ra, 32);
+        Frag<T> mrow[2], mcol[2];
+        frag_row_f32cvt(mrow[0], sR1, kLdA, ra, 0);  // Mx row a, slots c
+        frag_row_f32cvt(mrow[1], sR1, kLdA, ra, 32);
+        frag_col_f32(mcol[0], sR1, kLdA, ra, 0);     // Mx column a, slots c
+        frag_col_f32(mcol[1], sR1, kLdA, ra, 32);
+        const float ba = sBeta[ra], ega = fast_exp(sGam[ra]);
+        {
+            T* dkp = reinterpret_cast<T*>(a.dk) + ((t0 + ra) * H + h) * K;
+#pragma unroll
+            for (int kt = 0; kt < K / 16; ++kt) {
+                f32x4 bk = zero4(), mk = zero4();
+#pragma unroll
+                for (int xb = 0; xb < 2; ++xb) {
+                    Frag<T> fw, fk;
+                    frag_col(fw, sdW, C::LDK, kt * 16 + ln, xb * 32);  // dW^T row k, slots x
+                    mma(bk, fw, tcol[xb]);
+                    frag_col(fk, sK, C::LDK, kt * 16 + ln, xb * 32);   // K^T row k, slots c
+                    mma(mk, fk, mrow[xb]);
+                    mma(mk, fk, mcol[xb]);
+                }
+                // dbeta, dgam from Bk = diag(beta e^gam) K
+                const float s = dot4(bk, ld4(sK + ra * C::LDK + kt * 16 + gq * 4));
+                dbeta_row += ega * s;
+                dgam_row += ba * ega * s;
+                if (ra < c) store4(dkp + kt * 16 + gq * 4, dkpart[kt] + mk + bk * (ba * ega));
+            }
+        }
+        {
+            T* dvp = reinterpret_cast<T*>(a.dv) + ((t0 + ra) * H + h) * V;
+#pragma unroll
+            for (int vt = 0; vt < V / 16; ++vt) {
+                f32x4 bv = zero4();
+#pragma unroll
+                for (int xb = 0; xb < 2; ++xb) {
+                    Frag<T> fu;
+                    frag_col(fu, sdU, C::LDV, vt * 16 + ln, xb * 32);  // dU^T row v, slots x
+                    mma(bv, fu, tcol[xb]);
+                }
+                dbeta_row += dot4(bv, ld4(sV + ra * C::LDV + vt * 16 + gq * 4));
+                if (ra < c) store4(dvp + vt * 16 + gq * 4, bv * ba);
+            }
+        }
+        dbeta_row = sum_gq(dbeta_row);
+        dgam_row = sum_gq(dgam_row);
+        if (gq == 0) sRow[ra] = dgam_row;
+        if (gq == 0 && ra < c) a.dbeta[(t0 + ra) * H + h] = dbeta_row;
+        lds_sync();
+        // ---- d(gam) total and dg = reverse cumulative sum within the chunk --------------------
+        if (wave == 0) {
+            float d = 0.f;
+            if (lane < c)
+                d = sDgs[lane] + sRow[lane] + sRed[lane] + sRed[64 + lane] + sRed[128 + lane] + sRed[192 + lane];
+            // suffix sum over lanes lane..63
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const float y = __shfl_down(d, off, 64);
+                if (lane + off < 64) d += y;
+            }
+            if (lane < c) a.dg[(t0 + lane) * H + h] = d;
+        }
+        if (!more) break;
+        cur = nxt;
+        t = tn;
     }
 }
 
 template <typename T, int K, int V>
-hipError_t launch_bwd_state_t(const BwdChunkArgs& a, hipStream_t st) {
-    using S = SCfg<T, K, V>;
-    static_assert(S::total <= 160 * 1024, "LDS budget");
-    auto kern = k_bwd_state<T, K, V>;
+hipError_t launch_bwd_chunk_t(const BwdChunkArgs& a, int grid, hipStream_t st) {
+    using C = BCfg<T, K, V>;
+    static_assert(C::total <= 160 * 1024, "LDS budget");
+    auto kern = k_bwd_chunk<T, K, V>;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, S::total);
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, C::total);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, dim3((unsigned)a.geo.total_chunks, (unsigned)a.geo.H), dim3(256), S::total, st, a);
-    return hipGetLastError();
-}
-
-template <typename T, int K, int V>
-hipError_t launch_bwd_wy_t(const BwdChunkArgs& a, hipStream_t st) {
-    using S = WCfg<T, K, V>;
-    static_assert(S::total <= 160 * 1024, "LDS budget");
-    auto kern = k_bwd_wy<T, K, V>;
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, S::total);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, dim3((unsigned)a.geo.total_chunks, (unsigned)a.geo.H), dim3(256), S::total, st, a);
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), C::total, st, a);
     return hipGetLastError();
 }
 
@@ -1126,27 +1133,20 @@ hipError_t launch_reverse(const RevArgs& a, int dtype, int mode, int64_t nsegs_g
 }
 
 
-#define GDN_BWD_CASES(FN)                                        \
-    if (dtype == 0) {                                            \
-        if (K == 64 && V == 64) return FN<bf16_t, 64, 64>(a, st);    \
-        if (K == 64 && V == 128) return FN<bf16_t, 64, 128>(a, st);  \
-        if (K == 128 && V == 64) return FN<bf16_t, 128, 64>(a, st);  \
-        if (K == 128 && V == 128) return FN<bf16_t, 128, 128>(a, st); \
-    } else {                                                     \
-        if (K == 64 && V == 64) return FN<float, 64, 64>(a, st);     \
+#define GDN_BWD_CASES(FN)                                              \
+    if (dtype == 0) {                                                  \
+        if (K == 64 && V == 64) return FN<bf16_t, 64, 64>(a, grid, st);    \
+        if (K == 64 && V == 128) return FN<bf16_t, 64, 128>(a, grid, st);  \
+        if (K == 128 && V == 64) return FN<bf16_t, 128, 64>(a, grid, st);  \
+        if (K == 128 && V == 128) return FN<bf16_t, 128, 128>(a, grid, st); \
+    } else {                                                           \
+        if (K == 64 && V == 64) return FN<float, 64, 64>(a, grid, st);     \
     }
 
-hipError_t launch_bwd_state(const BwdChunkArgs& a, int dtype, hipStream_t st) {
-    if (a.geo.total_chunks == 0) return hipSuccess;
+hipError_t launch_bwd_chunk(const BwdChunkArgs& a, int dtype, int grid, hipStream_t st) {
+    if (a.geo.total_chunks == 0 || grid < 1) return hipSuccess;
     const int K = a.geo.K, V = a.geo.V;
-    GDN_BWD_CASES(launch_bwd_state_t)
-    return hipErrorInvalidValue;
-}
-
-hipError_t launch_bwd_wy(const BwdChunkArgs& a, int dtype, hipStream_t st) {
-    if (a.geo.total_chunks == 0) return hipSuccess;
-    const int K = a.geo.K, V = a.geo.V;
-    GDN_BWD_CASES(launch_bwd_wy_t)
+    GDN_BWD_CASES(launch_bwd_chunk_t)
     return hipErrorInvalidValue;
 }
 #undef GDN_BWD_CASES

@@ -194,10 +194,6 @@ struct BwdChunkArgs {
     const void* d_o;
     const void* hstates;      // [total_chunks,H,V,K] state entering every chunk
     const void* gstates;      // [total_chunks,H,V,K] adjoint of the state leaving every chunk
-    float* dw;                // [Ttot,H,K] fp32: dL/dW (state side -> WY side)
-    float* du;                // [Ttot,H,V] fp32: dL/dU
-    float* dk_part;           // [Ttot,H,K] fp32: dk terms of the state side
-    float* dgam_part;         // [Ttot,H] fp32: d(gate cumsum) terms of the state side
     void* dq;
     void* dk;
     void* dv;
@@ -233,7 +229,7 @@ hipError_t launch_recur(const RecurArgs& a, int dtype, int mode, int64_t nsegs_g
                         hipStream_t st);
 hipError_t launch_scan(const ScanArgs& a, int dtype, hipStream_t st);
 hipError_t launch_reverse(const RevArgs& a, int dtype, int mode, int64_t nsegs_grid, int vtiles, hipStream_t st);
-hipError_t launch_bwd_state(const BwdChunkArgs& a, int dtype, hipStream_t st);
-hipError_t launch_bwd_wy(const BwdChunkArgs& a, int dtype, hipStream_t st);
+// grid: persistent workgroups (one per CU; each walks tasks gc * H + h with a grid stride)
+hipError_t launch_bwd_chunk(const BwdChunkArgs& a, int dtype, int grid, hipStream_t st);
 
 }  // namespace gdn
