@@ -44,7 +44,7 @@ struct Plan {
     size_t o_gam = 0, o_w = 0, o_u = 0, o_cstat = 0, o_bos = 0, o_len = 0, o_choff = 0, o_segoff = 0,
            o_ctab = 0, o_stab = 0, o_modes = 0, o_seginit = 0, o_prep = 0, fwd_bytes = 0;
     // backward workspace: the forward's layout, then these
-    size_t o_modes_r = 0, o_seginit_r = 0, o_prep_r = 0, o_h = 0, o_gst = 0, bwd_bytes = 0;
+    size_t o_modes_r = 0, o_seginit_r = 0, o_prep_r = 0, o_h = 0, o_gst = 0, o_tm = 0, bwd_bytes = 0;
     int32_t cus = 256;   // compute units (desc->num_cus, else the device's)
     int32_t bwd_ok = 1;  // fp32 backward supports K = V = 64 only (LDS)
 };
@@ -98,6 +98,8 @@ gdn_status make_plan(const gdn_desc* d, Plan& p) {
         max_nt = p.nt;
     }
     if (p.total_chunks > INT32_MAX || max_nt > INT32_MAX / 2) return GDN_ERR_UNSUPPORTED;
+    // the per-chunk kernels address a 64-row tile of [T, H, D] with 32-bit byte offsets
+    if (d->H * std::max(d->K, d->V) * 64 * 4 >= ((int64_t)1 << 31)) return GDN_ERR_UNSUPPORTED;
 
     p.cus = d->num_cus > 0 ? d->num_cus : query_cus();
     // AutoCP
@@ -177,6 +179,7 @@ gdn_status make_plan(const gdn_desc* d, Plan& p) {
     }
     p.o_h = take((size_t)p.total_chunks * H * V * K * p.esize);
     p.o_gst = take((size_t)p.total_chunks * H * V * K * p.esize);
+    p.o_tm = take((size_t)p.total_chunks * H * 64 * 64 * p.esize);
     p.bwd_bytes = std::max<size_t>(off, kAlign);
     p.bwd_ok = (d->dtype == GDN_DTYPE_BF16) || (d->K == 64 && d->V == 64);
     return GDN_OK;
@@ -286,7 +289,8 @@ gdn_status check_ws(const Plan& p, size_t need, void* ws, size_t bytes) {
 
 // Tables (varlen) + intra-chunk kernel into the given output buffers.
 gdn_status run_intra(const gdn_desc* d, const Plan& p, unsigned char* ws, const void* k, const void* v,
-                     const float* g, const float* beta, float* gam, void* w, void* u, hipStream_t st) {
+                     const float* g, const float* beta, float* gam, void* w, void* u, hipStream_t st,
+                     void* tmat = nullptr) {
     if (p.varlen) {
         TableArgs t{};
         t.cu = d->cu_seqlens;
@@ -313,6 +317,7 @@ gdn_status run_intra(const gdn_desc* d, const Plan& p, unsigned char* ws, const 
     ia.w = w;
     ia.u = u;
     ia.cstat = reinterpret_cast<float2*>(ws + p.o_cstat);
+    ia.tmat = tmat;
     GDN_LAUNCH(kKIntra, st, launch_intra(ia, d->dtype, st));
     return GDN_OK;
 }
@@ -461,7 +466,7 @@ gdn_status gdn_chunk_bwd(const gdn_desc* desc, const void* q, const void* k, con
     void* w = ws + p.o_w;
     void* u = ws + p.o_u;
     // 1. recompute the gate cumsum and the WY factors
-    if ((s = run_intra(desc, p, ws, k, v, g, beta, gam, w, u, st)) != GDN_OK) return s;
+    if ((s = run_intra(desc, p, ws, k, v, g, beta, gam, w, u, st, ws + p.o_tm)) != GDN_OK) return s;
     const int rt = recur_rows((int)desc->V, (int)desc->K);
     const int vtiles = (int)(desc->V / rt);
     const int vktiles = (int)((desc->V + desc->K + rt - 1) / rt);
@@ -549,6 +554,7 @@ gdn_status gdn_chunk_bwd(const gdn_desc* desc, const void* q, const void* k, con
     ba.d_o = d_o;
     ba.hstates = ws + p.o_h;
     ba.gstates = ws + p.o_gst;
+    ba.tmat = ws + p.o_tm;
     ba.dq = dq;
     ba.dk = dk;
     ba.dv = dv;

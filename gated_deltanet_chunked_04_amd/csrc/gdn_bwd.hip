@@ -11,7 +11,7 @@
 // from the end. The per-chunk gradients then run in parallel over all chunks (k_bwd_chunk):
 //   state side: Delta = U - W S^T, dQt = dO S, dP = dO U^T - dQt W^T, dKt = Delta G,
 //     dW = -dDelta S  ->  dq, the P and Kt terms of dk and d(gam), dW, dU
-//   WY side: recompute T = (I + A)^{-1}; dT = dW Bk^T + dU Bv^T,
+//   WY side: with T = (I + A)^{-1} (written by the intra-chunk kernel); dT = dW Bk^T + dU Bv^T,
 //     dA = strict_lower(-T^T dT T^T), dBk = T^T dW, dBv = T^T dU  ->  dk, dv, dbeta, and
 //     dg as the in-chunk reverse cumulative sum of d(gam).
 #include "gdn_common.h"
@@ -180,7 +180,7 @@ __global__ __launch_bounds__(RT * 4) void k_reverse(RevArgs a) {
     SegLoc sg;
     if (!locate_seg(geo, gs, sg)) return;
     const int tid = threadIdx.x;
-    const int wave = tid >> 6, lane = tid & 63, ln = lane & 15, gq = lane >> 4;
+    const int wave = wave_id(), lane = tid & 63, ln = lane & 15, gq = lane >> 4;
     const int row = vt * RT + wave * 16 + ln;
     const size_t VK = (size_t)V * K;
 
@@ -372,18 +372,18 @@ hipError_t launch_reverse_t(const RevArgs& a, int64_t nsegs_grid, int vtiles, hi
 //
 // LDS: K stays for both sides. The state side holds S, G, Q, W, scale * dO and U (the
 // L .* dP exchange later reuses U). dU is written over dO once the dDelta products are
-// done, dW over S once the S and G products are done; the WY side's four fp32 64x64
-// matrices and V go into the space that is free once the state side ends (the hole
+// done, dW over S once the S and G products are done; the WY side's V, T and two 64x64
+// scratch matrices go into the space that is free once the state side ends (the hole
 // between dW and dU first, then from U onwards).
 struct WyPlace {
-    int off[5];  // A-raw, T, R1, R2 (fp32 64x64 each), V
+    int off[4];  // V, T, Y, Mx
     int end;
 };
-constexpr WyPlace place_wy(int h0, int h1, int tail, int f32mat, int vmat) {
+constexpr WyPlace place_wy(int h0, int h1, int tail, int vmat, int xmat) {
     WyPlace p{};
     int cur = h0, tl = tail;
-    for (int i = 0; i < 5; ++i) {
-        const int s = i < 4 ? f32mat : vmat;
+    for (int i = 0; i < 4; ++i) {
+        const int s = i == 0 ? vmat : xmat;
         if (cur + s <= h1) {
             p.off[i] = cur;
             cur += s;
@@ -404,8 +404,8 @@ struct BCfg {
     static constexpr int LDX = 64 + BPad<T>::row;
     static constexpr int kMK = 64 * LDK * (int)sizeof(T);  // one [64][K] matrix
     static constexpr int kMV = 64 * LDV * (int)sizeof(T);  // one [64][V] matrix
+    static constexpr int kMX = 64 * LDX * (int)sizeof(T);  // one [64][64] matrix
     static constexpr int kSt = V * LDK * (int)sizeof(T);   // one [V][K] state
-    static constexpr int kF = 64 * kLdA * 4;               // one fp32 64x64 matrix
     static constexpr int off_k = 0;
     // state side
     static constexpr int off_s = kMK;
@@ -419,12 +419,11 @@ struct BCfg {
     // WY side
     static constexpr int off_dw = off_s;
     static constexpr int off_du = off_d;
-    static constexpr WyPlace wy = place_wy(off_dw + kMK, off_d, off_u, kF, kMV);
-    static constexpr int off_ar = wy.off[0];  // e^{gam_a-gam_c} k_a.k_c (strict lower)
-    static constexpr int off_t = wy.off[1];   // T
-    static constexpr int off_r1 = wy.off[2];  // A, then dT, then Mx
-    static constexpr int off_r2 = wy.off[3];  // dT T^T
-    static constexpr int off_v = wy.off[4];
+    static constexpr WyPlace wy = place_wy(off_dw + kMK, off_d, off_u, kMV, kMX);
+    static constexpr int off_v = wy.off[0];
+    static constexpr int off_tm = wy.off[1];  // T = (I + A)^{-1}
+    static constexpr int off_y = wy.off[2];   // Y = dT T^T
+    static constexpr int off_mx = wy.off[3];  // Mx = dA .* (beta_a e^{gam_a - gam_c})
     // small arrays after both
     static constexpr int off_gam = end_state > wy.end ? end_state : wy.end;
     static constexpr int off_beta = off_gam + 256;
@@ -439,19 +438,20 @@ struct BCfg {
     static constexpr int NS = V * (K / VEC) / 256;   // S or G
     static constexpr int NK = 64 * (K / VEC) / 256;  // q, k, w
     static constexpr int NV = 64 * (V / VEC) / 256;  // dO, u, v
-    static_assert(NS * 256 == V * (K / VEC) && NK * 256 == 64 * (K / VEC) && NV * 256 == 64 * (V / VEC),
+    static constexpr int NX = 64 * (64 / VEC) / 256; // T
+    static_assert(NS * 256 == V * (K / VEC) && NK * 256 == 64 * (K / VEC) && NV * 256 == 64 * (V / VEC) &&
+                      NX * 256 == 64 * (64 / VEC),
                   "vector split");
 };
 
-// One task's operands in registers, in the three groups that are fetched at different
-// points of the previous task: S and G, the chunk rows (q, k, w, dO, u, gate cumsum,
-// beta), and v.
+// One task's operands in registers, in the two groups that are fetched at different
+// points of the previous task: the chunk rows (q, k, w, dO, u, T, gate cumsum, beta),
+// then S, G and v.
 template <typename T, int K, int V>
 struct BRegs {
     using C = BCfg<T, K, V>;
-    u32x4 s[C::NS], g[C::NS];
-    u32x4 q[C::NK], k[C::NK], w[C::NK], d[C::NV], u[C::NV];
-    u32x4 v[C::NV];
+    u32x4 q[C::NK], k[C::NK], w[C::NK], d[C::NV], u[C::NV], t[C::NX];
+    u32x4 s[C::NS], g[C::NS], v[C::NV];
     float gam, beta;
 };
 
@@ -479,16 +479,27 @@ __device__ __forceinline__ int64_t bwd_next_task(const Geo& geo, int64_t t, int6
 }
 
 // Rows [0, rows) of a row-major global matrix into registers: 16-byte vector e of the
-// tile goes to thread e % 256, slot e / 256; rows >= rows are zero.
+// tile goes to thread e % 256, slot e / 256; rows >= rows are zero. Each load is a
+// wave-uniform base plus one 32-bit lane offset shared by all slots (the host bounds a
+// tile's extent below 2 GiB), so no per-slot 64-bit address stays live across the task.
 template <typename T, int D, int N>
 __device__ __forceinline__ void fetch_tile(u32x4 (&x)[N], const T* src, size_t ld_g, int rows) {
-    constexpr int NVR = D / Elem<T>::kVec;
+    constexpr int VEC = Elem<T>::kVec;
+    constexpr int NVR = D / VEC;    // vectors per row
+    constexpr int RPI = 256 / NVR;  // rows per slot
+    static_assert(256 % NVR == 0, "row split");
+    const int r0 = threadIdx.x / NVR, cv = threadIdx.x % NVR;
+    const uint32_t off = ((uint32_t)r0 * (uint32_t)ld_g + (uint32_t)(cv * VEC)) * (uint32_t)sizeof(T);
+    const char* b = reinterpret_cast<const char*>(src);
+    const size_t step = (size_t)RPI * ld_g * sizeof(T);
+    if (rows >= N * RPI) {  // whole tile (wave-uniform)
 #pragma unroll
-    for (int it = 0; it < N; ++it) {
-        const int e = threadIdx.x + it * 256;
-        const int r = e / NVR, cv = e % NVR;
-        x[it] = r < rows ? *reinterpret_cast<const u32x4*>(src + (size_t)r * ld_g + cv * Elem<T>::kVec)
-                         : u32x4{0u, 0u, 0u, 0u};
+        for (int it = 0; it < N; ++it) x[it] = *reinterpret_cast<const u32x4*>(b + it * step + off);
+    } else {
+#pragma unroll
+        for (int it = 0; it < N; ++it)
+            x[it] = r0 + it * RPI < rows ? *reinterpret_cast<const u32x4*>(b + it * step + off)
+                                         : u32x4{0u, 0u, 0u, 0u};
     }
 }
 
@@ -520,6 +531,7 @@ __device__ __forceinline__ void bwd_fetch_rows(BRegs<T, K, V>& R, const BwdChunk
     fetch_tile<T, K>(R.w, reinterpret_cast<const T*>(a.w) + ok, (size_t)H * K, x.c);
     fetch_tile<T, V>(R.d, reinterpret_cast<const T*>(a.d_o) + ov, (size_t)H * V, x.c);
     fetch_tile<T, V>(R.u, reinterpret_cast<const T*>(a.u) + ov, (size_t)H * V, x.c);
+    fetch_tile<T, 64>(R.t, reinterpret_cast<const T*>(a.tmat) + ((size_t)x.gc * H + x.h) * 4096, 64, 64);
     const int tid = threadIdx.x;
     if (tid < 64) {
         const bool in = tid < x.c;
@@ -565,40 +577,6 @@ __device__ __forceinline__ float sum_gq(float x) {
     x += __shfl_xor(x, 32, 64);
     return x;
 }
-// Sum over the 16 lanes of one lane group (ln = 0..15).
-__device__ __forceinline__ float sum_ln(float x) {
-    x += __shfl_xor(x, 1, 64);
-    x += __shfl_xor(x, 2, 64);
-    x += __shfl_xor(x, 4, 64);
-    x += __shfl_xor(x, 8, 64);
-    return x;
-}
-
-// fp32 LDS column fragment converted to the operand type.
-template <typename T>
-__device__ __forceinline__ void frag_col_f32(Frag<T>& f, const float* base, int ld, int col, int k0) {
-    Frag<float> x;
-    frag_col(x, base, ld, col, k0);
-    if constexpr (sizeof(T) == 2) {
-        reinterpret_cast<Frag<bf16_t>&>(f).v =
-            u32x4{pack_bf2(x.lo.x, x.lo.y), pack_bf2(x.lo.z, x.lo.w), pack_bf2(x.hi.x, x.hi.y), pack_bf2(x.hi.z, x.hi.w)};
-    } else {
-        reinterpret_cast<Frag<float>&>(f) = x;
-    }
-}
-
-// fp32 LDS row fragment converted to the operand type.
-template <typename T>
-__device__ __forceinline__ void frag_row_f32cvt(Frag<T>& f, const float* base, int ld, int row, int k0) {
-    Frag<float> x;
-    frag_row(x, base, ld, row, k0);
-    if constexpr (sizeof(T) == 2) {
-        reinterpret_cast<Frag<bf16_t>&>(f).v =
-            u32x4{pack_bf2(x.lo.x, x.lo.y), pack_bf2(x.lo.z, x.lo.w), pack_bf2(x.hi.x, x.hi.y), pack_bf2(x.hi.z, x.hi.w)};
-    } else {
-        reinterpret_cast<Frag<float>&>(f) = x;
-    }
-}
 
 template <typename T, int K, int V>
 __global__ __launch_bounds__(256) void k_bwd_chunk(BwdChunkArgs a) {
@@ -612,10 +590,9 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(BwdChunkArgs a) {
     T* sD = reinterpret_cast<T*>(smem + C::off_d);
     T* sU = reinterpret_cast<T*>(smem + C::off_u);
     T* sX = reinterpret_cast<T*>(smem + C::off_x);
-    float* sAr = reinterpret_cast<float*>(smem + C::off_ar);
-    float* sT = reinterpret_cast<float*>(smem + C::off_t);
-    float* sR1 = reinterpret_cast<float*>(smem + C::off_r1);
-    float* sR2 = reinterpret_cast<float*>(smem + C::off_r2);
+    T* sTm = reinterpret_cast<T*>(smem + C::off_tm);
+    T* sY = reinterpret_cast<T*>(smem + C::off_y);
+    T* sMx = reinterpret_cast<T*>(smem + C::off_mx);
     T* sV = reinterpret_cast<T*>(smem + C::off_v);
     T* sdW = reinterpret_cast<T*>(smem + C::off_dw);
     T* sdU = reinterpret_cast<T*>(smem + C::off_du);
@@ -630,7 +607,7 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(BwdChunkArgs a) {
     const int64_t H = geo.H;
     const int64_t ntasks = geo.total_chunks * H;
     const int tid = threadIdx.x;
-    const int wave = tid >> 6, lane = tid & 63, ln = lane & 15, gq = lane >> 4;
+    const int wave = wave_id(), lane = tid & 63, ln = lane & 15, gq = lane >> 4;
     const int r = wave * 16 + ln;  // this lane's chunk row in "column" roles
 
     BTask cur;
@@ -638,6 +615,7 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(BwdChunkArgs a) {
     if (t >= ntasks) return;
     BRegs<T, K, V> R;  // the next task's operands
     u32x4 rv[C::NV];    // v of this task
+    u32x4 rt[C::NX];    // T of this task
     bwd_fetch_states(R, a, cur);
     bwd_fetch_rows(R, a, cur);
     bwd_fetch_v(R, a, cur);
@@ -659,6 +637,8 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(BwdChunkArgs a) {
         }
 #pragma unroll
         for (int i = 0; i < C::NV; ++i) rv[i] = R.v[i];
+#pragma unroll
+        for (int i = 0; i < C::NX; ++i) rt[i] = R.t[i];
         lds_sync();
         // The last task fetches itself again: unconditional fetches end the previous
         // operands' live range at the staging above.
@@ -772,7 +752,6 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(BwdChunkArgs a) {
         lds_sync();  // every read of S and G is done: dW (rows r) goes over S
 #pragma unroll
         for (int kt = 0; kt < K / 16; ++kt) store4(sdW + r * C::LDK + kt * 16 + gq * 4, r < c ? dWT[kt] : zero4());
-        bwd_fetch_rows(R, a, nxt);  // in flight over the rest of this task
         // ---- dP^T[j][r] = (U dO^T)[j][r] - (W dQt^T)[j][r];  P with the wave's rows as queries
         f32x4 dPT[4], PmQ[4];
         {
@@ -905,35 +884,17 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(BwdChunkArgs a) {
             sDgs[tid] = d;
         }
         put_tile<T, V>(sV, C::LDV, rv);
-        bwd_fetch_states(R, a, nxt);
-        bwd_fetch_v(R, a, nxt);
-        // ---- A (for the inverse) and e^{gam_a - gam_c} k_a.k_c ------------------------------
-        // (reads only K, gam and beta, which the stores above do not touch)
-        for (int idx = wave; idx < 10; idx += 4) {
-            const int ti = kTriB[idx][0], tj = kTriB[idx][1];
-            f32x4 acc = zero4();
-#pragma unroll
-            for (int kb = 0; kb < K / 32; ++kb) {
-                Frag<T> fa, fb;
-                frag_row(fa, sK, C::LDK, ti * 16 + ln, kb * 32);
-                frag_row(fb, sK, C::LDK, tj * 16 + ln, kb * 32);
-                mma(acc, fb, fa);  // rows j = tj*16.., cols i = ti*16+ln: lane holds (KK)[i][j]
-            }
-            const int i = ti * 16 + ln;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int j = tj * 16 + gq * 4 + e;
-                const float ar = (j < i) ? fast_exp(sGam[i] - sGam[j]) * acc[e] : 0.f;
-                sAr[i * kLdA + j] = ar;
-                sR1[i * kLdA + j] = sBeta[i] * ar;
-            }
-        }
+        put_tile<T, 64>(sTm, C::LDX, rt);
         lds_sync();
-        tri_inverse64(sR1, sT);
+        // The next task's operands load over the rest of this one. They are issued late,
+        // where few registers are live, so that nothing spills or waits on them here.
+        bwd_fetch_rows(R, a, nxt);
         const int ra = r;
-        // ---- dT[a][b] = beta_b e^{gam_b} (dW K^T)[a][b] + beta_b (dU V^T)[a][b], b < a part -
-        f32x4 dT[4];
+        // ---- dT[a][b] = beta_b e^{gam_b} (dW K^T)[a][b] + beta_b (dU V^T)[a][b], b < a --------
+        // (tiles rows b, cols a: two of them are a B fragment of dT^T)
+        Frag<T> dtf[2];
         {
+            f32x4 dT[4];
             Frag<T> wf[K / 32], uf[V / 32];
 #pragma unroll
             for (int kb = 0; kb < K / 32; ++kb) frag_row(wf[kb], sdW, C::LDK, ra, kb * 32);
@@ -962,81 +923,84 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(BwdChunkArgs a) {
                     dT[bt][e] = (b < ra) ? sBeta[b] * (fast_exp(sGam[b]) * x[e] + y[e]) : 0.f;
                 }
             }
+            frag_acc(dtf[0], dT[0], dT[1]);
+            frag_acc(dtf[1], dT[2], dT[3]);
         }
-        // stage dT (row a, column b) over A, which the inverse no longer needs
+        // ---- Y = dT T^T: tiles Y^T[c][a] = sum_b T[c][b] dT[a][b] (T[c][b] = 0 for b > c) -----
 #pragma unroll
-        for (int bt = 0; bt < 4; ++bt)
+        for (int ct = 0; ct < 4; ++ct) {
+            f32x4 y = zero4();
 #pragma unroll
-            for (int e = 0; e < 4; ++e) sR1[ra * kLdA + bt * 16 + gq * 4 + e] = dT[bt][e];
-        lds_sync();
-        // ---- Y = dT T^T (fp32): Y[a][c] = sum_b dT[a][b] T[c][b] -------------------------------
-        {
-            Frag<float> da[2];
-            frag_row(da[0], sR1, kLdA, ra, 0);
-            frag_row(da[1], sR1, kLdA, ra, 32);
-#pragma unroll
-            for (int ct = 0; ct < 4; ++ct) {
-                f32x4 y = zero4();
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb) {
-                    Frag<float> ft;
-                    frag_row(ft, sT, kLdA, ct * 16 + ln, kb * 32);
-                    mma(y, ft, da[kb]);  // rows c, cols a: Y^T
+            for (int kb = 0; kb < 2; ++kb) {
+                if (kb == 0 || ct >= 2) {
+                    Frag<T> ft;
+                    frag_row(ft, sTm, C::LDX, ct * 16 + ln, kb * 32);
+                    mma(y, ft, dtf[kb]);
                 }
-#pragma unroll
-                for (int e = 0; e < 4; ++e) sR2[ra * kLdA + ct * 16 + gq * 4 + e] = y[e];
             }
+            store4(sY + ra * C::LDX + ct * 16 + gq * 4, y);  // Y[a][c]
         }
         lds_sync();
-        // ---- dA[a][c] = -sum_x T[x][a] Y[x][c], strict lower; its consumers --------------------
+        // ---- dA[a][c] = -sum_x T[x][a] Y[x][c] for c < a (T[x][a] = 0 for x < a); with the
+        // raw A[a][c] = e^{gam_a - gam_c} k_a.k_c: dbeta, d(gam), and Mx = dA beta_a e^{..}
         float dbeta_row = 0.f, dgam_row = 0.f;
+        Frag<T> ta[2];
+        frag_col(ta[0], sTm, C::LDX, ra, 0);  // T column a, slots x
+        frag_col(ta[1], sTm, C::LDX, ra, 32);
         {
-            Frag<float> ta[2];
-            frag_col(ta[0], sT, kLdA, ra, 0);  // T^T row a, slots x
-            frag_col(ta[1], sT, kLdA, ra, 32);
+            Frag<T> kra[K / 32];
+#pragma unroll
+            for (int kb = 0; kb < K / 32; ++kb) frag_row(kra[kb], sK, C::LDK, ra, kb * 32);
+            const float ba = sBeta[ra], ga = sGam[ra];
 #pragma unroll
             for (int ct = 0; ct < 4; ++ct) {
-                f32x4 d = zero4();
+                f32x4 d = zero4(), kk = zero4();
                 if (ct <= wave) {
 #pragma unroll
                     for (int kb = 0; kb < 2; ++kb) {
-                        Frag<float> fy;
-                        frag_col(fy, sR2, kLdA, ct * 16 + ln, kb * 32);  // Y^T row c, slots x
-                        mma(d, fy, ta[kb]);  // rows c, cols a: (T^T Y)^T
+                        if (kb == 1 || wave < 2) {
+                            Frag<T> fy;
+                            frag_col(fy, sY, C::LDX, ct * 16 + ln, kb * 32);  // Y^T row c, slots x
+                            mma(d, fy, ta[kb]);  // rows c, cols a: (T^T Y)^T
+                        }
+                    }
+#pragma unroll
+                    for (int kb = 0; kb < K / 32; ++kb) {
+                        Frag<T> fk;
+                        frag_row(fk, sK, C::LDK, ct * 16 + ln, kb * 32);
+                        mma(kk, fk, kra[kb]);  // rows c, cols a: k_c . k_a
                     }
                 }
-                f32x4 colpart;
+                f32x4 colpart, mx;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int cc = ct * 16 + gq * 4 + e;
-                    const float dA = (cc < ra) ? -d[e] : 0.f;
-                    const float ar = (cc < ra) ? sAr[ra * kLdA + cc] : 0.f;  // upper blocks never written
-                    const float av = sBeta[ra] * ar;  // A[a][c]
+                    const bool lower = cc < ra;
+                    const float dec = lower ? fast_exp(ga - sGam[cc]) : 0.f;
+                    const float ar = dec * kk[e];  // raw A[a][c]
+                    const float dA = lower ? -d[e] : 0.f;
                     dbeta_row += dA * ar;
-                    dgam_row += dA * av;
-                    colpart[e] = dA * av;
-                    d[e] = dA * sBeta[ra] * ((cc < ra) ? fast_exp(sGam[ra] - sGam[cc]) : 0.f);  // Mx[a][c]
+                    dgam_row += dA * ar * ba;
+                    colpart[e] = dA * ar * ba;
+                    mx[e] = dA * ba * dec;
                 }
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const float s = sum_ln(colpart[e]);
                     if (ln == 0) sRed[wave * 64 + ct * 16 + gq * 4 + e] = -s;
                 }
-                // Mx[a][c] staged in R1: dT was consumed by Y, and R2 (Y) is still being read
-#pragma unroll
-                for (int e = 0; e < 4; ++e) sR1[ra * kLdA + ct * 16 + gq * 4 + e] = d[e];
+                store4(sMx + ra * C::LDX + ct * 16 + gq * 4, mx);  // Mx[a][c]
             }
         }
         lds_sync();
+        bwd_fetch_states(R, a, nxt);
+        bwd_fetch_v(R, a, nxt);
         // ---- dBk^T = dW^T T, dBv^T = dU^T T (rows k / v, cols a);  dK, dV ----------------------
-        Frag<T> tcol[2];
-        frag_col_f32(tcol[0], sT, kLdA, ra, 0);  // T column a, slots x
-        frag_col_f32(tcol[1], sT, kLdA, ra, 32);
         Frag<T> mrow[2], mcol[2];
-        frag_row_f32cvt(mrow[0], sR1, kLdA, ra, 0);  // Mx row a, slots c
-        frag_row_f32cvt(mrow[1], sR1, kLdA, ra, 32);
-        frag_col_f32(mcol[0], sR1, kLdA, ra, 0);     // Mx column a, slots c
-        frag_col_f32(mcol[1], sR1, kLdA, ra, 32);
+        frag_row(mrow[0], sMx, C::LDX, ra, 0);  // Mx row a, slots c
+        frag_row(mrow[1], sMx, C::LDX, ra, 32);
+        frag_col(mcol[0], sMx, C::LDX, ra, 0);  // Mx column a, slots c
+        frag_col(mcol[1], sMx, C::LDX, ra, 32);
         const float ba = sBeta[ra], ega = fast_exp(sGam[ra]);
         {
             T* dkp = reinterpret_cast<T*>(a.dk) + ((t0 + ra) * H + h) * K;
@@ -1047,7 +1011,7 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(BwdChunkArgs a) {
                 for (int xb = 0; xb < 2; ++xb) {
                     Frag<T> fw, fk;
                     frag_col(fw, sdW, C::LDK, kt * 16 + ln, xb * 32);  // dW^T row k, slots x
-                    mma(bk, fw, tcol[xb]);
+                    mma(bk, fw, ta[xb]);
                     frag_col(fk, sK, C::LDK, kt * 16 + ln, xb * 32);   // K^T row k, slots c
                     mma(mk, fk, mrow[xb]);
                     mma(mk, fk, mcol[xb]);
@@ -1068,7 +1032,7 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(BwdChunkArgs a) {
                 for (int xb = 0; xb < 2; ++xb) {
                     Frag<T> fu;
                     frag_col(fu, sdU, C::LDV, vt * 16 + ln, xb * 32);  // dU^T row v, slots x
-                    mma(bv, fu, tcol[xb]);
+                    mma(bv, fu, ta[xb]);
                 }
                 dbeta_row += dot4(bv, ld4(sV + ra * C::LDV + vt * 16 + gq * 4));
                 if (ra < c) store4(dvp + vt * 16 + gq * 4, bv * ba);

@@ -35,18 +35,34 @@ constexpr int kWave = 64;
 
 __device__ __forceinline__ float bf2f(bf16_t x) { return __uint_as_float((uint32_t)x << 16); }
 
-// fp32 -> bf16, round to nearest even (inputs are finite).
-__device__ __forceinline__ uint32_t f2bf_bits(float f) {
-    uint32_t u = __float_as_uint(f);
-    u += 0x7FFFu + ((u >> 16) & 1u);
-    return u >> 16;
-}
-__device__ __forceinline__ bf16_t f2bf(float f) { return (bf16_t)f2bf_bits(f); }
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// fp32 -> bf16, round to nearest even: gfx950's v_cvt_pk_bf16_f32 converts two at once.
 __device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
-    return f2bf_bits(lo) | (f2bf_bits(hi) << 16);
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2_t));
 }
+__device__ __forceinline__ bf16_t f2bf(float f) { return __builtin_bit_cast(bf16_t, (__bf16)f); }
 
 __device__ __forceinline__ float fast_exp(float x) { return __expf(x); }
+
+// Wave index within the workgroup, as a wave-uniform (scalar) value: branches on it
+// stay scalar branches instead of exec-masked ones.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)); }
+
+// Value of the lane that the DPP control kCtrl selects (within a row of 16 lanes).
+template <int kCtrl>
+__device__ __forceinline__ float dpp_f(float x) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), kCtrl, 0xF, 0xF, true));
+}
+// Sum over the 16 lanes of a row; every lane of the row gets the same bits (each step
+// adds two values that the partner lane adds in the other order). Call with all lanes on.
+__device__ __forceinline__ float sum_ln(float x) {
+    x += dpp_f<0xB1>(x);   // quad_perm [1,0,3,2]: lane ^ 1
+    x += dpp_f<0x4E>(x);   // quad_perm [2,3,0,1]: lane ^ 2
+    x += dpp_f<0x141>(x);  // row_half_mirror: quads 0 <-> 1, 2 <-> 3
+    x += dpp_f<0x140>(x);  // row_mirror: halves of the row
+    return x;
+}
 
 // ---------------------------------------------------------------------------
 // Element traits: storage type T in memory (bf16_t or float).
@@ -227,7 +243,7 @@ __device__ __forceinline__ void tri_offdiag_block(float* sA, float* sT, int i, i
 
 __device__ __forceinline__ void tri_inverse64(float* sA, float* sT) {
     const int tid = threadIdx.x;
-    const int wave = tid >> 6;
+    const int wave = wave_id();
     const int lane = tid & 63;
     const int ln = lane & 15, gq = lane >> 4;
     // 3a: diagonal blocks by forward substitution (wave b, lanes 0..15 = columns of block b)

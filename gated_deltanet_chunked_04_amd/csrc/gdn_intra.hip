@@ -18,7 +18,8 @@
 // and T*V read their columns with LDS transpose loads. The inverse is blocked:
 // 16x16 diagonal blocks by forward substitution, then off-diagonal blocks level by
 // level with fp32 matrix-core products. T stays fp32; the products T*K and T*V run on
-// the matrix cores in the input precision with fp32 accumulation.
+// the matrix cores in the input precision with fp32 accumulation. For the backward the
+// kernel also writes T in the input precision.
 #include "gdn_common.h"
 #include "gdn_kernels.h"
 
@@ -71,7 +72,7 @@ __global__ __launch_bounds__(kThreads) void k_intra(IntraArgs args) {
     const int64_t H = geo.H;
     const int c = L.c;
     const int tid = threadIdx.x;
-    const int wave = tid >> 6;
+    const int wave = wave_id();
     const int lane = tid & 63;
     const int ln = lane & 15, gq = lane >> 4;
 
@@ -118,6 +119,13 @@ __global__ __launch_bounds__(kThreads) void k_intra(IntraArgs args) {
 
     // ---- stage 3: T = (I + A)^{-1} --------------------------------------------------
     tri_inverse64(sA, sT);
+    if (args.tmat) {
+        // T for the backward, in the input precision: thread -> row tid/4, 16 columns
+        const int tr = tid >> 2, tc = (tid & 3) * 16;
+        T* dst = reinterpret_cast<T*>(args.tmat) + ((size_t)gc * H + h) * 4096 + tr * 64 + tc;
+#pragma unroll
+        for (int i = 0; i < 16; i += 4) store4(dst + i, *reinterpret_cast<const f32x4*>(sT + tr * kLdA + tc + i));
+    }
     if (wave == 1) {
         // chunk statistics for the CP decision
         float m = lane < c ? sKK[lane] : 0.f;

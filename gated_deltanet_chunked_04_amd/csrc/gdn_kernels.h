@@ -115,6 +115,7 @@ struct IntraArgs {
     void* w;         // [Ttot, H, K]
     void* u;         // [Ttot, H, V]
     float2* cstat;   // [total_chunks, H]: (chunk gate total, max beta*|k|^2)
+    void* tmat;      // [total_chunks, H, 64, 64] T = (I + A)^{-1} row-major, or null (not written)
 };
 
 enum RecurMode : int {
@@ -194,6 +195,7 @@ struct BwdChunkArgs {
     const void* d_o;
     const void* hstates;      // [total_chunks,H,V,K] state entering every chunk
     const void* gstates;      // [total_chunks,H,V,K] adjoint of the state leaving every chunk
+    const void* tmat;         // [total_chunks,H,64,64] T = (I + A)^{-1} of every chunk
     void* dq;
     void* dk;
     void* dv;

@@ -175,7 +175,7 @@ __device__ __forceinline__ void chunk_part1(const ChunkLds<T, K, RT>& L, const f
                                             Frag<T> (&sf)[K / 32], f32x4 (&accD)[4], f32x4 (&accO)[4]) {
     using C = RCfg<T, K, RT>;
     const int tid = threadIdx.x;
-    const int wave = tid >> 6, lane = tid & 63, ln = lane & 15, gq = lane >> 4;
+    const int wave = wave_id(), lane = tid & 63, ln = lane & 15, gq = lane >> 4;
     Frag<T> nsf[K / 32];
 #pragma unroll
     for (int kb = 0; kb < K / 32; ++kb) {
@@ -243,7 +243,7 @@ __device__ __forceinline__ void chunk_part2(const RecurArgs& a, const ChunkLds<T
                                             int vcol0) {
     using C = RCfg<T, K, RT>;
     const int tid = threadIdx.x;
-    const int wave = tid >> 6, lane = tid & 63, ln = lane & 15, gq = lane >> 4;
+    const int wave = wave_id(), lane = tid & 63, ln = lane & 15, gq = lane >> 4;
     if (kOut) {
         Frag<T> df[2];
         frag_acc(df[0], accD[0], accD[1]);
@@ -314,7 +314,7 @@ __global__ __launch_bounds__(RT * 4) void k_recur(RecurArgs a) {
     SegLoc sg;
     if (!locate_seg(geo, gs, sg)) return;
     const int tid = threadIdx.x;
-    const int wave = tid >> 6, lane = tid & 63, ln = lane & 15, gq = lane >> 4;
+    const int wave = wave_id(), lane = tid & 63, ln = lane & 15, gq = lane >> 4;
     const int row = vt * RT + wave * 16 + ln;  // this lane's state row (value row, or V + M row)
     const size_t VK = (size_t)V * K;
 
@@ -422,7 +422,7 @@ hipError_t launch_recur_t(const RecurArgs& a, int64_t nsegs_grid, int vtiles, hi
 // token map exp(g)(I - beta k k^T) has spectral norm <= exp(g), so a wrong state at
 // the window start is damped by at least exp(window gate sum)).
 __global__ __launch_bounds__(kThreads) void k_decide(DecideArgs a) {
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int wave = wave_id(), lane = threadIdx.x & 63;
     const int64_t p = (int64_t)blockIdx.x * 4 + wave;
     const int H = a.geo.H;
     if (p >= (int64_t)a.geo.N * H) return;
@@ -487,7 +487,7 @@ __global__ __launch_bounds__(RT * 4) void k_scan(ScanArgs a) {
     seq_segs(a.geo, n, nseg, segoff, nchunks, choff);
     if (nseg < 2) return;
     const int tid = threadIdx.x;
-    const int wave = tid >> 6, lane = tid & 63, ln = lane & 15;
+    const int wave = wave_id(), lane = tid & 63, ln = lane & 15;
     const int row = vt * RT + wave * 16 + ln;
     const size_t VK = (size_t)V * K;
     const size_t PS = (size_t)(V + K) * K;  // floats per (segment, head) map
