@@ -318,7 +318,7 @@ gdn_status run_intra(const gdn_desc* d, const Plan& p, unsigned char* ws, const 
     ia.u = u;
     ia.cstat = reinterpret_cast<float2*>(ws + p.o_cstat);
     ia.tmat = tmat;
-    GDN_LAUNCH(kKIntra, st, launch_intra(ia, d->dtype, st));
+    GDN_LAUNCH(kKIntra, st, launch_intra(ia, d->dtype, p.cus, st));
     return GDN_OK;
 }
 

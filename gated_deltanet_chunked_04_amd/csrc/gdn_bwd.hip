@@ -101,25 +101,6 @@ __device__ __forceinline__ void rev_fetch(RevRegs<T, K, RT>& R, const RevArgs& a
     }
 }
 
-// 16-byte vector scaled by s (bf16 or fp32 elements).
-template <typename T>
-__device__ __forceinline__ u32x4 scale_vec(const u32x4& x, float s);
-template <>
-__device__ __forceinline__ u32x4 scale_vec<bf16_t>(const u32x4& x, float s) {
-    u32x4 y;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-        y[i] = pack_bf2(bf2f((bf16_t)(x[i] & 0xFFFFu)) * s, bf2f((bf16_t)(x[i] >> 16)) * s);
-    return y;
-}
-template <>
-__device__ __forceinline__ u32x4 scale_vec<float>(const u32x4& x, float s) {
-    u32x4 y;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) y[i] = __float_as_uint(__uint_as_float(x[i]) * s);
-    return y;
-}
-
 template <typename T, int K, int RT>
 struct RevLds {
     T* sQ;
@@ -455,75 +436,15 @@ struct BRegs {
     float gam, beta;
 };
 
-struct BTask {
-    int64_t gc;  // global chunk
-    int64_t t0;  // first token (flattened)
-    int h;
-    int c;       // tokens in the chunk
-};
-
-// First valid task at or after t, stepping by the grid; ntasks when there is none.
-__device__ __forceinline__ int64_t bwd_next_task(const Geo& geo, int64_t t, int64_t ntasks, BTask& x) {
-    for (; t < ntasks; t += gridDim.x) {
-        ChunkLoc L;
-        const int64_t gc = t / geo.H;
-        if (locate_chunk(geo, gc, L)) {
-            x.gc = gc;
-            x.t0 = L.t0;
-            x.h = (int)(t - gc * geo.H);
-            x.c = L.c;
-            return t;
-        }
-    }
-    return ntasks;
-}
-
-// Rows [0, rows) of a row-major global matrix into registers: 16-byte vector e of the
-// tile goes to thread e % 256, slot e / 256; rows >= rows are zero. Each load is a
-// wave-uniform base plus one 32-bit lane offset shared by all slots (the host bounds a
-// tile's extent below 2 GiB), so no per-slot 64-bit address stays live across the task.
-template <typename T, int D, int N>
-__device__ __forceinline__ void fetch_tile(u32x4 (&x)[N], const T* src, size_t ld_g, int rows) {
-    constexpr int VEC = Elem<T>::kVec;
-    constexpr int NVR = D / VEC;    // vectors per row
-    constexpr int RPI = 256 / NVR;  // rows per slot
-    static_assert(256 % NVR == 0, "row split");
-    const int r0 = threadIdx.x / NVR, cv = threadIdx.x % NVR;
-    const uint32_t off = ((uint32_t)r0 * (uint32_t)ld_g + (uint32_t)(cv * VEC)) * (uint32_t)sizeof(T);
-    const char* b = reinterpret_cast<const char*>(src);
-    const size_t step = (size_t)RPI * ld_g * sizeof(T);
-    if (rows >= N * RPI) {  // whole tile (wave-uniform)
-#pragma unroll
-        for (int it = 0; it < N; ++it) x[it] = *reinterpret_cast<const u32x4*>(b + it * step + off);
-    } else {
-#pragma unroll
-        for (int it = 0; it < N; ++it)
-            x[it] = r0 + it * RPI < rows ? *reinterpret_cast<const u32x4*>(b + it * step + off)
-                                         : u32x4{0u, 0u, 0u, 0u};
-    }
-}
-
-// The registers of fetch_tile into a row-major LDS tile (row stride ld_s), scaled by s.
-template <typename T, int D, int N>
-__device__ __forceinline__ void put_tile(T* dst, int ld_s, const u32x4 (&x)[N], float s = 1.f) {
-    constexpr int NVR = D / Elem<T>::kVec;
-#pragma unroll
-    for (int it = 0; it < N; ++it) {
-        const int e = threadIdx.x + it * 256;
-        const int r = e / NVR, cv = e % NVR;
-        *reinterpret_cast<u32x4*>(dst + r * ld_s + cv * Elem<T>::kVec) = s == 1.f ? x[it] : scale_vec<T>(x[it], s);
-    }
-}
-
 template <typename T, int K, int V>
-__device__ __forceinline__ void bwd_fetch_states(BRegs<T, K, V>& R, const BwdChunkArgs& a, const BTask& x) {
+__device__ __forceinline__ void bwd_fetch_states(BRegs<T, K, V>& R, const BwdChunkArgs& a, const ChunkTask& x) {
     const size_t st = ((size_t)x.gc * a.geo.H + x.h) * (size_t)V * K;
     fetch_tile<T, K>(R.s, reinterpret_cast<const T*>(a.hstates) + st, K, V);
     fetch_tile<T, K>(R.g, reinterpret_cast<const T*>(a.gstates) + st, K, V);
 }
 
 template <typename T, int K, int V>
-__device__ __forceinline__ void bwd_fetch_rows(BRegs<T, K, V>& R, const BwdChunkArgs& a, const BTask& x) {
+__device__ __forceinline__ void bwd_fetch_rows(BRegs<T, K, V>& R, const BwdChunkArgs& a, const ChunkTask& x) {
     const int64_t H = a.geo.H;
     const size_t ok = ((size_t)x.t0 * H + x.h) * K, ov = ((size_t)x.t0 * H + x.h) * V;
     fetch_tile<T, K>(R.q, reinterpret_cast<const T*>(a.q) + ok, (size_t)H * K, x.c);
@@ -541,7 +462,7 @@ __device__ __forceinline__ void bwd_fetch_rows(BRegs<T, K, V>& R, const BwdChunk
 }
 
 template <typename T, int K, int V>
-__device__ __forceinline__ void bwd_fetch_v(BRegs<T, K, V>& R, const BwdChunkArgs& a, const BTask& x) {
+__device__ __forceinline__ void bwd_fetch_v(BRegs<T, K, V>& R, const BwdChunkArgs& a, const ChunkTask& x) {
     fetch_tile<T, V>(R.v, reinterpret_cast<const T*>(a.v) + ((size_t)x.t0 * a.geo.H + x.h) * V,
                      (size_t)a.geo.H * V, x.c);
 }
@@ -610,8 +531,8 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(BwdChunkArgs a) {
     const int wave = wave_id(), lane = tid & 63, ln = lane & 15, gq = lane >> 4;
     const int r = wave * 16 + ln;  // this lane's chunk row in "column" roles
 
-    BTask cur;
-    int64_t t = bwd_next_task(geo, blockIdx.x, ntasks, cur);
+    ChunkTask cur;
+    int64_t t = next_chunk_task(geo, blockIdx.x, ntasks, cur);
     if (t >= ntasks) return;
     BRegs<T, K, V> R;  // the next task's operands
     u32x4 rv[C::NV];    // v of this task
@@ -642,8 +563,8 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(BwdChunkArgs a) {
         lds_sync();
         // The last task fetches itself again: unconditional fetches end the previous
         // operands' live range at the staging above.
-        BTask nxt = cur;
-        const int64_t tn = bwd_next_task(geo, t + gridDim.x, ntasks, nxt);
+        ChunkTask nxt = cur;
+        const int64_t tn = next_chunk_task(geo, t + gridDim.x, ntasks, nxt);
         const bool more = tn < ntasks;
         if (!more) nxt = cur;
 

@@ -295,42 +295,61 @@ __device__ __forceinline__ void store_state(const f32x4 (&accS)[K / 16], float* 
 }
 
 // ---------------------------------------------------------------------------
-// LDS staging (256-thread workgroups).
-// Copy `rows` (<= 64) rows of a [.., H, D] tensor for head h into LDS, row-major and/or
-// transposed; rows beyond `rows` are zero.
-template <typename T, int D, bool kRowMajor, bool kTrans = true>
-__device__ __forceinline__ void stage_rows(const T* __restrict__ src, int64_t t0, int64_t H, int h,
-                                           int rows, T* rm, int ldr, T* tr, int ldt) {
+// Tile movement for 256-thread workgroups.
+
+// 16-byte vector scaled by s (bf16 or fp32 elements).
+template <typename T>
+__device__ __forceinline__ u32x4 scale_vec(const u32x4& x, float s);
+template <>
+__device__ __forceinline__ u32x4 scale_vec<bf16_t>(const u32x4& x, float s) {
+    u32x4 y;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        y[i] = pack_bf2(__uint_as_float(x[i] << 16) * s, __uint_as_float(x[i] & 0xFFFF0000u) * s);
+    return y;
+}
+template <>
+__device__ __forceinline__ u32x4 scale_vec<float>(const u32x4& x, float s) {
+    u32x4 y;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) y[i] = __float_as_uint(__uint_as_float(x[i]) * s);
+    return y;
+}
+
+// Rows [0, rows) of a row-major global matrix into registers: 16-byte vector e of the
+// tile goes to thread e % 256, slot e / 256; rows >= rows are zero. Each load is a
+// wave-uniform base plus one 32-bit lane offset shared by all slots (the host bounds a
+// tile's extent below 2 GiB), so no per-slot 64-bit address stays live.
+template <typename T, int D, int N>
+__device__ __forceinline__ void fetch_tile(u32x4 (&x)[N], const T* src, size_t ld_g, int rows) {
     constexpr int VEC = Elem<T>::kVec;
-    constexpr int NV = D / VEC;          // vectors per row
-    constexpr int UNITS = 32 * NV;       // (row pair, vector)
-    const int tid = threadIdx.x;
+    constexpr int NVR = D / VEC;    // vectors per row
+    constexpr int RPI = 256 / NVR;  // rows per slot
+    static_assert(256 % NVR == 0, "row split");
+    const int r0 = threadIdx.x / NVR, cv = threadIdx.x % NVR;
+    const uint32_t off = ((uint32_t)r0 * (uint32_t)ld_g + (uint32_t)(cv * VEC)) * (uint32_t)sizeof(T);
+    const char* b = reinterpret_cast<const char*>(src);
+    const size_t step = (size_t)RPI * ld_g * sizeof(T);
+    if (rows >= N * RPI) {  // whole tile (wave-uniform)
 #pragma unroll
-    for (int it = 0; it < UNITS / 256; ++it) {
-        const int u = tid + it * 256;
-        const int cv = u % NV;
-        const int rp = u / NV;
-        const int r0 = 2 * rp, r1 = 2 * rp + 1;
-        u32x4 a = u32x4{0u, 0u, 0u, 0u}, b = u32x4{0u, 0u, 0u, 0u};
-        if (r0 < rows) a = *reinterpret_cast<const u32x4*>(src + ((t0 + r0) * H + h) * D + cv * VEC);
-        if (r1 < rows) b = *reinterpret_cast<const u32x4*>(src + ((t0 + r1) * H + h) * D + cv * VEC);
-        if (kRowMajor) {
-            *reinterpret_cast<u32x4*>(rm + r0 * ldr + cv * VEC) = a;
-            *reinterpret_cast<u32x4*>(rm + r1 * ldr + cv * VEC) = b;
-        }
-        if constexpr (!kTrans) {
-        } else if constexpr (sizeof(T) == 2) {
+        for (int it = 0; it < N; ++it) x[it] = *reinterpret_cast<const u32x4*>(b + it * step + off);
+    } else {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const uint32_t lo = (a[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu;
-                const uint32_t hi = (b[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu;
-                *reinterpret_cast<uint32_t*>(tr + (cv * VEC + e) * ldt + r0) = lo | (hi << 16);
-            }
-        } else {
+        for (int it = 0; it < N; ++it)
+            x[it] = r0 + it * RPI < rows ? *reinterpret_cast<const u32x4*>(b + it * step + off)
+                                         : u32x4{0u, 0u, 0u, 0u};
+    }
+}
+
+// The registers of fetch_tile into a row-major LDS tile (row stride ld_s), scaled by s.
+template <typename T, int D, int N>
+__device__ __forceinline__ void put_tile(T* dst, int ld_s, const u32x4 (&x)[N], float s = 1.f) {
+    constexpr int NVR = D / Elem<T>::kVec;
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                *reinterpret_cast<u32x2*>(tr + (cv * VEC + e) * ldt + r0) = u32x2{a[e], b[e]};
-        }
+    for (int it = 0; it < N; ++it) {
+        const int e = threadIdx.x + it * 256;
+        const int r = e / NVR, cv = e % NVR;
+        *reinterpret_cast<u32x4*>(dst + r * ld_s + cv * Elem<T>::kVec) = s == 1.f ? x[it] : scale_vec<T>(x[it], s);
     }
 }
 

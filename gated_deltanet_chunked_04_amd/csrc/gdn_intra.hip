@@ -23,6 +23,8 @@
 #include "gdn_common.h"
 #include "gdn_kernels.h"
 
+#include <algorithm>
+
 namespace gdn {
 
 namespace {
@@ -52,6 +54,32 @@ struct IntraSmem {
 __constant__ int8_t kTri[10][2] = {{0, 0}, {1, 0}, {1, 1}, {2, 0}, {2, 1}, {2, 2},
                                    {3, 0}, {3, 1}, {3, 2}, {3, 3}};
 
+// One task's inputs in registers (fetched while the previous task computes).
+template <typename T, int K, int V>
+struct IntraRegs {
+    static constexpr int VEC = Elem<T>::kVec;
+    static constexpr int NK = 64 * (K / VEC) / 256;
+    static constexpr int NV = 64 * (V / VEC) / 256;
+    u32x4 k[NK], v[NV];
+    float g, beta;  // lanes 0..63 of wave 0
+};
+
+template <typename T, int K, int V>
+__device__ __forceinline__ void intra_fetch(IntraRegs<T, K, V>& R, const IntraArgs& a, const ChunkTask& x) {
+    const int64_t H = a.geo.H;
+    fetch_tile<T, K>(R.k, reinterpret_cast<const T*>(a.k) + ((size_t)x.t0 * H + x.h) * K, (size_t)H * K, x.c);
+    fetch_tile<T, V>(R.v, reinterpret_cast<const T*>(a.v) + ((size_t)x.t0 * H + x.h) * V, (size_t)H * V, x.c);
+    const int tid = threadIdx.x;
+    if (tid < 64) {
+        const bool in = tid < x.c;
+        const int64_t i = (x.t0 + (in ? tid : 0)) * H + x.h;
+        R.g = in ? a.g[i] : 0.f;
+        R.beta = in ? a.beta[i] : 0.f;
+    }
+}
+
+// Persistent: each workgroup walks (chunk, head) tasks with a grid stride; the next
+// task's k, v, g and beta load into registers while the current task computes.
 template <typename T, int K, int V>
 __global__ __launch_bounds__(kThreads) void k_intra(IntraArgs args) {
     using S = IntraSmem<T, K, V>;
@@ -65,167 +93,186 @@ __global__ __launch_bounds__(kThreads) void k_intra(IntraArgs args) {
     float* sKK = reinterpret_cast<float*>(smem + S::off_kk);
 
     const Geo& geo = args.geo;
-    const int64_t gc = blockIdx.x;
-    const int h = blockIdx.y;
-    ChunkLoc L;
-    if (!locate_chunk(geo, gc, L)) return;
     const int64_t H = geo.H;
-    const int c = L.c;
+    const int64_t ntasks = geo.total_chunks * H;
     const int tid = threadIdx.x;
     const int wave = wave_id();
     const int lane = tid & 63;
     const int ln = lane & 15, gq = lane >> 4;
 
-    // ---- stage 1: operands into LDS, gate cumsum --------------------------------
-    stage_rows<T, K, true, false>(reinterpret_cast<const T*>(args.k), L.t0, H, h, c, sK, S::LDK, nullptr, 0);
-    stage_rows<T, V, true, false>(reinterpret_cast<const T*>(args.v), L.t0, H, h, c, sV, S::LDV, nullptr, 0);
-    if (wave == 0) {
-        const bool in = lane < c;
-        float x = in ? args.g[(L.t0 + lane) * H + h] : 0.f;
-        const float b = in ? args.beta[(L.t0 + lane) * H + h] : 0.f;
+    ChunkTask cur;
+    int64_t t = next_chunk_task(geo, blockIdx.x, ntasks, cur);
+    if (t >= ntasks) return;
+    IntraRegs<T, K, V> R;
+    intra_fetch(R, args, cur);
+    for (;;) {
+        // ---- stage 1: operands into LDS, gate cumsum --------------------------------
+        lds_sync();  // the previous task's LDS reads are done
+        put_tile<T, K>(sK, S::LDK, R.k);
+        put_tile<T, V>(sV, S::LDV, R.v);
+        const float g_in = R.g, b_in = R.beta;
+        // the last task fetches itself again: the fetch stays unconditional
+        ChunkTask nxt = cur;
+        const int64_t tn = next_chunk_task(geo, t + gridDim.x, ntasks, nxt);
+        const bool more = tn < ntasks;
+        if (!more) nxt = cur;
+        intra_fetch(R, args, nxt);
+        const int64_t gc = cur.gc;
+        const int h = cur.h;
+        const int c = cur.c;
+        const int64_t t0 = cur.t0;
+        if (wave == 0) {
+            const bool in = lane < c;
+            float x = g_in;
 #pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const float y = __shfl_up(x, off, 64);
-            if (lane >= off) x += y;
+            for (int off = 1; off < 64; off <<= 1) {
+                const float y = __shfl_up(x, off, 64);
+                if (lane >= off) x += y;
+            }
+            sGam[lane] = x;   // rows past the chunk end carry the chunk total
+            sBeta[lane] = b_in;
+            if (in) args.gam[(t0 + lane) * H + h] = x;
         }
-        sGam[lane] = x;   // rows past the chunk end carry the chunk total
-        sBeta[lane] = b;
-        if (in) args.gam[(L.t0 + lane) * H + h] = x;
-    }
-    lds_sync();
+        lds_sync();
 
-    // ---- stage 2: A = strict_lower(diag(beta) (D .* K K^T)) -----------------------
-    for (int idx = wave; idx < 10; idx += 4) {
-        const int ti = kTri[idx][0], tj = kTri[idx][1];
-        f32x4 acc = zero4();
+        // ---- stage 2: A = strict_lower(diag(beta) (D .* K K^T)) -----------------------
+        for (int idx = wave; idx < 10; idx += 4) {
+            const int ti = kTri[idx][0], tj = kTri[idx][1];
+            f32x4 acc = zero4();
 #pragma unroll
-        for (int kb = 0; kb < K / 32; ++kb) {
-            Frag<T> a, b;
-            frag_row(a, sK, S::LDK, ti * 16 + ln, kb * 32);
-            frag_row(b, sK, S::LDK, tj * 16 + ln, kb * 32);
-            mma(acc, a, b);
-        }
-        const int j = tj * 16 + ln;
-        const float gj = sGam[j];
+            for (int kb = 0; kb < K / 32; ++kb) {
+                Frag<T> a, b;
+                frag_row(a, sK, S::LDK, ti * 16 + ln, kb * 32);
+                frag_row(b, sK, S::LDK, tj * 16 + ln, kb * 32);
+                mma(acc, a, b);
+            }
+            const int j = tj * 16 + ln;
+            const float gj = sGam[j];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = ti * 16 + gq * 4 + i;
-            const float val = (j < r) ? sBeta[r] * fast_exp(sGam[r] - gj) * acc[i] : 0.f;
-            sA[r * kLdA + j] = val;
-            if (r == j) sKK[r] = sBeta[r] * acc[i];
-        }
-    }
-    lds_sync();
-
-    // ---- stage 3: T = (I + A)^{-1} --------------------------------------------------
-    tri_inverse64(sA, sT);
-    if (args.tmat) {
-        // T for the backward, in the input precision: thread -> row tid/4, 16 columns
-        const int tr = tid >> 2, tc = (tid & 3) * 16;
-        T* dst = reinterpret_cast<T*>(args.tmat) + ((size_t)gc * H + h) * 4096 + tr * 64 + tc;
-#pragma unroll
-        for (int i = 0; i < 16; i += 4) store4(dst + i, *reinterpret_cast<const f32x4*>(sT + tr * kLdA + tc + i));
-    }
-    if (wave == 1) {
-        // chunk statistics for the CP decision
-        float m = lane < c ? sKK[lane] : 0.f;
-#pragma unroll
-        for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
-        if (lane == 0) args.cstat[gc * H + h] = make_float2(sGam[63], m);
-    }
-
-    // ---- stage 4: W = T diag(beta e^gam) K, U = T diag(beta) V ------------------------
-    const int rt = wave;
-    constexpr int NKB = 2;  // k32 slices over the 64 chunk rows
-    Frag<T> aw[NKB], au[NKB];
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-        Frag<float> tf;
-        frag_row(tf, sT, kLdA, rt * 16 + ln, kb * 32);
-        float fw[8], fu[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int j = kb * 32 + (e >> 2) * 16 + gq * 4 + (e & 3);
-            const float tv = e < 4 ? tf.lo[e] : tf.hi[e - 4];
-            const float bj = sBeta[j];
-            fu[e] = tv * bj;
-            fw[e] = fu[e] * fast_exp(sGam[j]);
-        }
-        if constexpr (sizeof(T) == 2) {
-            aw[kb].v = u32x4{pack_bf2(fw[0], fw[1]), pack_bf2(fw[2], fw[3]), pack_bf2(fw[4], fw[5]),
-                             pack_bf2(fw[6], fw[7])};
-            au[kb].v = u32x4{pack_bf2(fu[0], fu[1]), pack_bf2(fu[2], fu[3]), pack_bf2(fu[4], fu[5]),
-                             pack_bf2(fu[6], fu[7])};
-        } else {
-            reinterpret_cast<Frag<float>&>(aw[kb]).lo = f32x4{fw[0], fw[1], fw[2], fw[3]};
-            reinterpret_cast<Frag<float>&>(aw[kb]).hi = f32x4{fw[4], fw[5], fw[6], fw[7]};
-            reinterpret_cast<Frag<float>&>(au[kb]).lo = f32x4{fu[0], fu[1], fu[2], fu[3]};
-            reinterpret_cast<Frag<float>&>(au[kb]).hi = f32x4{fu[4], fu[5], fu[6], fu[7]};
-        }
-    }
-    const int nkb = (rt >> 1) + 1;  // T[r][j] = 0 for j > r
-    // Transposed tiles: with A = rows of K^T (V^T) and B = the scaled rows of T, accw[ct]
-    // holds W^T[ct*16 + gq*4 + i][rt*16 + ln], i.e. four consecutive columns of row
-    // rt*16 + ln, which each lane stages with one vector store.
-    f32x4 accw[K / 16], accu[V / 16];
-#pragma unroll
-    for (int ct = 0; ct < K / 16; ++ct) {
-        accw[ct] = zero4();
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
-            if (kb < nkb) {
-                Frag<T> b;
-                frag_col(b, sK, S::LDK, ct * 16 + ln, kb * 32);  // K^T row ct*16+ln, slots j
-                mma(accw[ct], b, aw[kb]);
+            for (int i = 0; i < 4; ++i) {
+                const int r = ti * 16 + gq * 4 + i;
+                const float val = (j < r) ? sBeta[r] * fast_exp(sGam[r] - gj) * acc[i] : 0.f;
+                sA[r * kLdA + j] = val;
+                if (r == j) sKK[r] = sBeta[r] * acc[i];
             }
         }
-    }
+        lds_sync();
+
+        // ---- stage 3: T = (I + A)^{-1} --------------------------------------------------
+        tri_inverse64(sA, sT);
+        if (args.tmat) {
+            // T for the backward, in the input precision: thread -> row tid/4, 16 columns
+            const int tr = tid >> 2, tc = (tid & 3) * 16;
+            T* dst = reinterpret_cast<T*>(args.tmat) + ((size_t)gc * H + h) * 4096 + tr * 64 + tc;
 #pragma unroll
-    for (int ct = 0; ct < V / 16; ++ct) {
-        accu[ct] = zero4();
+            for (int i = 0; i < 16; i += 4) store4(dst + i, *reinterpret_cast<const f32x4*>(sT + tr * kLdA + tc + i));
+        }
+        if (wave == 1) {
+            // chunk statistics for the CP decision
+            float m = lane < c ? sKK[lane] : 0.f;
+#pragma unroll
+            for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+            if (lane == 0) args.cstat[gc * H + h] = make_float2(sGam[63], m);
+        }
+
+        // ---- stage 4: W = T diag(beta e^gam) K, U = T diag(beta) V ------------------------
+        const int rt = wave;
+        constexpr int NKB = 2;  // k32 slices over the 64 chunk rows
+        Frag<T> aw[NKB], au[NKB];
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
-            if (kb < nkb) {
-                Frag<T> b;
-                frag_col(b, sV, S::LDV, ct * 16 + ln, kb * 32);  // V^T row ct*16+ln, slots j
-                mma(accu[ct], b, au[kb]);
+            Frag<float> tf;
+            frag_row(tf, sT, kLdA, rt * 16 + ln, kb * 32);
+            float fw[8], fu[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int j = kb * 32 + (e >> 2) * 16 + gq * 4 + (e & 3);
+                const float tv = e < 4 ? tf.lo[e] : tf.hi[e - 4];
+                const float bj = sBeta[j];
+                fu[e] = tv * bj;
+                fw[e] = fu[e] * fast_exp(sGam[j]);
+            }
+            if constexpr (sizeof(T) == 2) {
+                aw[kb].v = u32x4{pack_bf2(fw[0], fw[1]), pack_bf2(fw[2], fw[3]), pack_bf2(fw[4], fw[5]),
+                                 pack_bf2(fw[6], fw[7])};
+                au[kb].v = u32x4{pack_bf2(fu[0], fu[1]), pack_bf2(fu[2], fu[3]), pack_bf2(fu[4], fu[5]),
+                                 pack_bf2(fu[6], fu[7])};
+            } else {
+                reinterpret_cast<Frag<float>&>(aw[kb]).lo = f32x4{fw[0], fw[1], fw[2], fw[3]};
+                reinterpret_cast<Frag<float>&>(aw[kb]).hi = f32x4{fw[4], fw[5], fw[6], fw[7]};
+                reinterpret_cast<Frag<float>&>(au[kb]).lo = f32x4{fu[0], fu[1], fu[2], fu[3]};
+                reinterpret_cast<Frag<float>&>(au[kb]).hi = f32x4{fu[4], fu[5], fu[6], fu[7]};
             }
         }
+        const int nkb = (rt >> 1) + 1;  // T[r][j] = 0 for j > r
+        // Transposed tiles: with A = rows of K^T (V^T) and B = the scaled rows of T, accw[ct]
+        // holds W^T[ct*16 + gq*4 + i][rt*16 + ln], i.e. four consecutive columns of row
+        // rt*16 + ln, which each lane stages with one vector store.
+        f32x4 accw[K / 16], accu[V / 16];
+#pragma unroll
+        for (int ct = 0; ct < K / 16; ++ct) {
+            accw[ct] = zero4();
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) {
+                if (kb < nkb) {
+                    Frag<T> b;
+                    frag_col(b, sK, S::LDK, ct * 16 + ln, kb * 32);  // K^T row ct*16+ln, slots j
+                    mma(accw[ct], b, aw[kb]);
+                }
+            }
+        }
+#pragma unroll
+        for (int ct = 0; ct < V / 16; ++ct) {
+            accu[ct] = zero4();
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) {
+                if (kb < nkb) {
+                    Frag<T> b;
+                    frag_col(b, sV, S::LDV, ct * 16 + ln, kb * 32);  // V^T row ct*16+ln, slots j
+                    mma(accu[ct], b, au[kb]);
+                }
+            }
+        }
+        lds_sync();
+        // outputs staged over K and V, which are no longer read
+        T* sWo = sK;
+        T* sUo = sV;
+        const int orow = rt * 16 + ln;
+#pragma unroll
+        for (int ct = 0; ct < K / 16; ++ct) store4(sWo + orow * S::LDK + ct * 16 + gq * 4, accw[ct]);
+#pragma unroll
+        for (int ct = 0; ct < V / 16; ++ct) store4(sUo + orow * S::LDV + ct * 16 + gq * 4, accu[ct]);
+        lds_sync();
+        store_rows<T, K>(reinterpret_cast<T*>(args.w), t0, H, h, c, sWo, S::LDK);
+        store_rows<T, V>(reinterpret_cast<T*>(args.u), t0, H, h, c, sUo, S::LDV);
+        if (!more) break;
+        cur = nxt;
+        t = tn;
     }
-    lds_sync();
-    // outputs staged over K and V, which are no longer read
-    T* sWo = sK;
-    T* sUo = sV;
-    const int orow = rt * 16 + ln;
-#pragma unroll
-    for (int ct = 0; ct < K / 16; ++ct) store4(sWo + orow * S::LDK + ct * 16 + gq * 4, accw[ct]);
-#pragma unroll
-    for (int ct = 0; ct < V / 16; ++ct) store4(sUo + orow * S::LDV + ct * 16 + gq * 4, accu[ct]);
-    lds_sync();
-    store_rows<T, K>(reinterpret_cast<T*>(args.w), L.t0, H, h, c, sWo, S::LDK);
-    store_rows<T, V>(reinterpret_cast<T*>(args.u), L.t0, H, h, c, sUo, S::LDV);
 }
 
 template <typename T, int K, int V>
-hipError_t launch_intra_t(const IntraArgs& a, hipStream_t st) {
+hipError_t launch_intra_t(const IntraArgs& a, int cus, hipStream_t st) {
     using S = IntraSmem<T, K, V>;
     static_assert(S::total <= 160 * 1024, "LDS budget");
     auto kern = k_intra<T, K, V>;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, S::total);
     if (e != hipSuccess) return e;
-    dim3 grid((unsigned)a.geo.total_chunks, (unsigned)a.geo.H);
-    hipLaunchKernelGGL(kern, grid, dim3(kThreads), S::total, st, a);
+    // as many workgroups as fit on the chip at once (LDS-bound), at most one per task
+    const int64_t per_cu = std::max(1, (160 * 1024) / S::total);
+    const int64_t grid = std::min<int64_t>(a.geo.total_chunks * a.geo.H, per_cu * std::max(cus, 1));
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kThreads), S::total, st, a);
     return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_intra(const IntraArgs& a, int dtype, hipStream_t st) {
+hipError_t launch_intra(const IntraArgs& a, int dtype, int cus, hipStream_t st) {
     if (a.geo.total_chunks == 0) return hipSuccess;
     const int K = a.geo.K, V = a.geo.V;
 #define GDN_INTRA_CASE(TT, KK, VV) \
-    if (K == KK && V == VV) return launch_intra_t<TT, KK, VV>(a, st);
+    if (K == KK && V == VV) return launch_intra_t<TT, KK, VV>(a, cus, st);
     if (dtype == 0) {
         GDN_INTRA_CASE(bf16_t, 64, 64)
         GDN_INTRA_CASE(bf16_t, 64, 128)

@@ -52,6 +52,30 @@ __device__ __forceinline__ bool locate_chunk(const Geo& g, int64_t gc, ChunkLoc&
     return L.c > 0;
 }
 
+// (chunk, head) tasks of the persistent per-chunk kernels: task t is chunk t / H, head t % H.
+struct ChunkTask {
+    int64_t gc;  // global chunk
+    int64_t t0;  // first token (flattened)
+    int h;
+    int c;       // tokens in the chunk
+};
+
+// First valid task at or after t, stepping by the grid; ntasks when there is none.
+__device__ __forceinline__ int64_t next_chunk_task(const Geo& geo, int64_t t, int64_t ntasks, ChunkTask& x) {
+    for (; t < ntasks; t += gridDim.x) {
+        ChunkLoc L;
+        const int64_t gc = t / geo.H;
+        if (locate_chunk(geo, gc, L)) {
+            x.gc = gc;
+            x.t0 = L.t0;
+            x.h = (int)(t - gc * geo.H);
+            x.c = L.c;
+            return t;
+        }
+    }
+    return ntasks;
+}
+
 struct SegLoc {
     int32_t n, s, c0, c1;  // sequence, segment index, chunk range [c0, c1) in the sequence
     int32_t nseg;          // segments of this sequence
@@ -225,7 +249,7 @@ __host__ __device__ constexpr int recur_rows(int V, int K) { return (V == 128 &&
 
 // Launchers (return hipGetLastError of the launch).
 hipError_t launch_tables(const TableArgs& a, hipStream_t st);
-hipError_t launch_intra(const IntraArgs& a, int dtype, hipStream_t st);
+hipError_t launch_intra(const IntraArgs& a, int dtype, int cus, hipStream_t st);  // persistent grid
 hipError_t launch_decide(const DecideArgs& a, hipStream_t st);
 hipError_t launch_recur(const RecurArgs& a, int dtype, int mode, int64_t nsegs_grid, int vtiles,
                         hipStream_t st);
