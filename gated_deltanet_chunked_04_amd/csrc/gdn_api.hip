@@ -44,7 +44,8 @@ struct Plan {
     size_t o_gam = 0, o_w = 0, o_u = 0, o_cstat = 0, o_bos = 0, o_len = 0, o_choff = 0, o_segoff = 0,
            o_ctab = 0, o_stab = 0, o_modes = 0, o_seginit = 0, o_prep = 0, fwd_bytes = 0;
     // backward workspace: the forward's layout, then these
-    size_t o_modes_r = 0, o_seginit_r = 0, o_prep_r = 0, o_h = 0, o_gst = 0, o_tm = 0, bwd_bytes = 0;
+    size_t o_modes_r = 0, o_seginit_r = 0, o_prep_r = 0, o_h = 0, o_gst = 0, o_tm = 0, o_dl = 0, o_ddl = 0,
+           bwd_bytes = 0;
     int32_t cus = 256;   // compute units (desc->num_cus, else the device's)
     int32_t bwd_ok = 1;  // fp32 backward supports K = V = 64 only (LDS)
 };
@@ -180,6 +181,8 @@ gdn_status make_plan(const gdn_desc* d, Plan& p) {
     p.o_h = take((size_t)p.total_chunks * H * V * K * p.esize);
     p.o_gst = take((size_t)p.total_chunks * H * V * K * p.esize);
     p.o_tm = take((size_t)p.total_chunks * H * 64 * 64 * p.esize);
+    p.o_dl = take(T * H * V * p.esize);
+    p.o_ddl = take(T * H * V * p.esize);
     p.bwd_bytes = std::max<size_t>(off, kAlign);
     p.bwd_ok = (d->dtype == GDN_DTYPE_BF16) || (d->K == 64 && d->V == 64);
     return GDN_OK;
@@ -485,6 +488,7 @@ gdn_status gdn_chunk_bwd(const gdn_desc* desc, const void* q, const void* k, con
     int32_t* modes = reinterpret_cast<int32_t*>(ws + p.o_modes);
     ra.modes = modes;
     ra.hstates = ws + p.o_h;
+    ra.delta = ws + p.o_dl;
     if (p.cp_on) {
         float* seginit = reinterpret_cast<float*>(ws + p.o_seginit);
         float* prep = reinterpret_cast<float*>(ws + p.o_prep);
@@ -515,6 +519,7 @@ gdn_status gdn_chunk_bwd(const gdn_desc* desc, const void* q, const void* k, con
     va.dsT = d_final_state;
     va.ds0 = d_initial_state;
     va.gstates = ws + p.o_gst;
+    va.ddelta = ws + p.o_ddl;
     va.scale = desc->scale;
     va.warmup = p.W;
     va.use_cp = p.cp_on;
@@ -549,9 +554,9 @@ gdn_status gdn_chunk_bwd(const gdn_desc* desc, const void* q, const void* k, con
     ba.g = g;
     ba.beta = beta;
     ba.gam = gam;
-    ba.w = w;
-    ba.u = u;
     ba.d_o = d_o;
+    ba.delta = ws + p.o_dl;
+    ba.ddelta = ws + p.o_ddl;
     ba.hstates = ws + p.o_h;
     ba.gstates = ws + p.o_gst;
     ba.tmat = ws + p.o_tm;

@@ -44,7 +44,8 @@ struct VCfg {
     static constexpr int off_w = off_k + kMat;      // W
     static constexpr int off_do = off_w + kMat;     // dO
     static constexpr int off_pm = off_do + 64 * LDD * (int)sizeof(T);
-    static constexpr int off_gam = off_pm + 64 * LDP * (int)sizeof(T);
+    static constexpr int off_dd = off_pm + 64 * LDP * (int)sizeof(T);   // dDelta tile [64][RT]
+    static constexpr int off_gam = off_dd + 64 * LDD * (int)sizeof(T);
     static constexpr int total = off_gam + 256;
     static constexpr int NVK = K / VEC;
     static constexpr int NVD = RT / VEC;
@@ -151,6 +152,7 @@ __global__ __launch_bounds__(RT * 4) void k_reverse(RevArgs a) {
     L.sD = reinterpret_cast<T*>(smem + C::off_do);
     L.sPm = reinterpret_cast<T*>(smem + C::off_pm);
     L.sGam = reinterpret_cast<float*>(smem + C::off_gam);
+    T* sDd = reinterpret_cast<T*>(smem + C::off_dd);
 
     const Geo& geo = a.geo;
     const int64_t gs = blockIdx.x;
@@ -220,6 +222,9 @@ __global__ __launch_bounds__(RT * 4) void k_reverse(RevArgs a) {
             for (int kt = 0; kt < K / 16; ++kt) store4(gs_out + kt * 16 + gq * 4, accG[kt]);
         }
         lds_sync();
+        if (MODE == kRecurOut && a.ddelta && ci < cend - 1)
+            flush_tile<T, RT, C::NT>(reinterpret_cast<T*>(a.ddelta) + ((t0 + 64) * H + h) * V + vt * RT,
+                                     (size_t)H * V, min(64, sg.len - (ci + 1) * 64), sDd, C::LDD);
         rev_stage<T, K, RT>(R, L, a.scale);
         lds_sync();
         if (ci - 1 >= cbeg)
@@ -279,6 +284,15 @@ __global__ __launch_bounds__(RT * 4) void k_reverse(RevArgs a) {
                 }
             }
         }
+        if (MODE == kRecurOut && a.ddelta) {
+            // dDelta (= dU) for the per-chunk gradients, staged [64][RT] by row j and
+            // written out after the next chunk's first barrier
+#pragma unroll
+            for (int jt = 0; jt < 4; ++jt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    sDd[(jt * 16 + gq * 4 + i) * C::LDD + wave * 16 + ln] = Elem<T>::from_f(accD[jt][i]);
+        }
         // G^T <- e^Gam G^T + (e^gam Q)^T dO - W^T dDelta
         const float eG = fast_exp(Gm);
         Frag<T> ddf[2];
@@ -309,6 +323,11 @@ __global__ __launch_bounds__(RT * 4) void k_reverse(RevArgs a) {
         }
     }
 
+    if (MODE == kRecurOut && a.ddelta && cbeg < cend) {
+        lds_sync();
+        flush_tile<T, RT, C::NT>(reinterpret_cast<T*>(a.ddelta) + ((sg.bos + (int64_t)cbeg * 64) * H + h) * V + vt * RT,
+                                 (size_t)H * V, min(64, sg.len - cbeg * 64), sDd, C::LDD);
+    }
     if (MODE == kRecurPrepass) {
         if (mode == 1) {
             store_state<K>(accG, a.seginit_out + ((size_t)(gs - 0) * H + h) * VK, row);
@@ -346,16 +365,23 @@ hipError_t launch_reverse_t(const RevArgs& a, int64_t nsegs_grid, int vtiles, hi
 // Per-chunk gradients: the state side, then the WY side, in one kernel. A persistent
 // workgroup (4 waves, one per CU) walks the (chunk, head) tasks; the next task's operands
 // travel into registers while the current task computes, so HBM traffic overlaps the
-// work instead of alternating with it. Wave w owns chunk rows r = 16w .. 16w+15. Most
-// tiles are held transposed (rows over k or v, columns over the wave's rows r), which
-// makes them A fragments of their transposes and lets every lane write four consecutive
-// columns of its row with one vector store.
+// work instead of alternating with it.
 //
-// LDS: K stays for both sides. The state side holds S, G, Q, W, scale * dO and U (the
-// L .* dP exchange later reuses U). dU is written over dO once the dDelta products are
-// done, dW over S once the S and G products are done; the WY side's V, T and two 64x64
-// scratch matrices go into the space that is free once the state side ends (the hole
-// between dW and dU first, then from U onwards).
+// Delta = U - W S^T comes from the state pass and dDelta (= dU) from the reverse pass,
+// both of which form them anyway; with them, every state-side product contracts over
+// the value dimension:
+//   dQt = dO S, dW = -dDelta S     (S read as column slices: wave w owns k in [K/4 w, K/4 (w+1)))
+//   dKt = Delta G, dP = dO Delta^T (wave w owns chunk rows r = 16w .. 16w+15)
+// so no partial sums cross waves and S is read from LDS once per task. Most tiles are
+// held transposed (rows over k or chunk rows, columns over r), which makes them A
+// fragments of their transposes and lets every lane write four consecutive columns of
+// its row with one vector store.
+//
+// LDS: K stays for both sides. The state side holds S, G, Q, scale * dO, Delta and dDelta
+// (the L .* dP exchange later goes over Delta). dDelta is the WY side's dU as it stands;
+// dW goes over S once the state side ends, and V, T and two 64x64 scratch matrices of
+// the WY side go into the rest of that space (the hole between dW and dDelta first, then
+// past dDelta).
 struct WyPlace {
     int off[4];  // V, T, Y, Mx
     int end;
@@ -392,15 +418,14 @@ struct BCfg {
     static constexpr int off_s = kMK;
     static constexpr int off_g = off_s + kSt;
     static constexpr int off_q = off_g + kSt;
-    static constexpr int off_w = off_q + kMK;
-    static constexpr int off_d = off_w + kMK;  // scale * dO, then dU
-    static constexpr int off_u = off_d + kMV;  // U, then the L .* dP exchange
-    static constexpr int off_x = off_u;
-    static constexpr int end_state = off_u + kMV;
+    static constexpr int off_d = off_q + kMK;    // scale * dO
+    static constexpr int off_dl = off_d + kMV;   // Delta, then the L .* dP exchange
+    static constexpr int off_x = off_dl;
+    static constexpr int off_dd = off_dl + kMV;  // dDelta (the WY side's dU)
+    static constexpr int end_state = off_dd + kMV;
     // WY side
     static constexpr int off_dw = off_s;
-    static constexpr int off_du = off_d;
-    static constexpr WyPlace wy = place_wy(off_dw + kMK, off_d, off_u, kMV, kMX);
+    static constexpr WyPlace wy = place_wy(off_dw + kMK, off_dd, end_state, kMV, kMX);
     static constexpr int off_v = wy.off[0];
     static constexpr int off_tm = wy.off[1];  // T = (I + A)^{-1}
     static constexpr int off_y = wy.off[2];   // Y = dT T^T
@@ -410,61 +435,63 @@ struct BCfg {
     static constexpr int off_beta = off_gam + 256;
     static constexpr int off_red = off_beta + 256;  // [4][64] fp32 column partials
     static constexpr int off_row = off_red + 1024;  // [64] fp32 row parts
-    static constexpr int off_dgs = off_row + 256;   // [64] state-side d(gam)
+    static constexpr int off_qd = off_row + 256;    // [4][64] e^gam dQt . Q partials over k slices
+    static constexpr int off_dgs = off_qd + 1024;   // [64] state-side d(gam)
     static constexpr int off_sc = off_dgs + 256;    // [8] fp32 scalars
     static constexpr int total = off_sc + 64;
-    static_assert(LDX <= LDV, "the exchange fits over U");
-    static_assert(kMK <= 2 * kSt, "dW fits over S and G");
+    static_assert(LDX <= LDV, "the exchange fits over Delta");
+    static_assert(kMK <= kSt, "dW fits over S");
     // 16-byte vectors per thread of one task's operands
-    static constexpr int NS = V * (K / VEC) / 256;   // S or G
-    static constexpr int NK = 64 * (K / VEC) / 256;  // q, k, w
-    static constexpr int NV = 64 * (V / VEC) / 256;  // dO, u, v
-    static constexpr int NX = 64 * (64 / VEC) / 256; // T
+    static constexpr int NS = V * (K / VEC) / 256;    // S or G
+    static constexpr int NK = 64 * (K / VEC) / 256;   // q, k
+    static constexpr int NV = 64 * (V / VEC) / 256;   // dO, Delta, dDelta, v
+    static constexpr int NX = 64 * (64 / VEC) / 256;  // T
     static_assert(NS * 256 == V * (K / VEC) && NK * 256 == 64 * (K / VEC) && NV * 256 == 64 * (V / VEC) &&
                       NX * 256 == 64 * (64 / VEC),
                   "vector split");
 };
 
 // One task's operands in registers, in the two groups that are fetched at different
-// points of the previous task: the chunk rows (q, k, w, dO, u, T, gate cumsum, beta),
-// then S, G and v.
+// points of the previous task: the chunk rows (q, k, dO, Delta, dDelta, T, gate cumsum,
+// beta), then S, G and v.
 template <typename T, int K, int V>
 struct BRegs {
     using C = BCfg<T, K, V>;
-    u32x4 q[C::NK], k[C::NK], w[C::NK], d[C::NV], u[C::NV], t[C::NX];
+    u32x4 q[C::NK], k[C::NK], d[C::NV], dl[C::NV], dd[C::NV], t[C::NX];
     u32x4 s[C::NS], g[C::NS], v[C::NV];
     float gam, beta;
 };
 
-template <typename T, int K, int V>
-__device__ __forceinline__ void bwd_fetch_states(BRegs<T, K, V>& R, const BwdChunkArgs& a, const ChunkTask& x) {
-    const size_t st = ((size_t)x.gc * a.geo.H + x.h) * (size_t)V * K;
-    fetch_tile<T, K>(R.s, reinterpret_cast<const T*>(a.hstates) + st, K, V);
-    fetch_tile<T, K>(R.g, reinterpret_cast<const T*>(a.gstates) + st, K, V);
-}
-
-template <typename T, int K, int V>
-__device__ __forceinline__ void bwd_fetch_rows(BRegs<T, K, V>& R, const BwdChunkArgs& a, const ChunkTask& x) {
+// The next task's operands travel in small groups issued at different points of the
+// current task's WY side: a burst of all of them would stall the issuing waves on the
+// CU's load queue instead of draining behind the matrix work.
+template <int kGroup, typename T, int K, int V>
+__device__ __forceinline__ void bwd_fetch(BRegs<T, K, V>& R, const BwdChunkArgs& a, const ChunkTask& x) {
     const int64_t H = a.geo.H;
     const size_t ok = ((size_t)x.t0 * H + x.h) * K, ov = ((size_t)x.t0 * H + x.h) * V;
-    fetch_tile<T, K>(R.q, reinterpret_cast<const T*>(a.q) + ok, (size_t)H * K, x.c);
-    fetch_tile<T, K>(R.k, reinterpret_cast<const T*>(a.k) + ok, (size_t)H * K, x.c);
-    fetch_tile<T, K>(R.w, reinterpret_cast<const T*>(a.w) + ok, (size_t)H * K, x.c);
-    fetch_tile<T, V>(R.d, reinterpret_cast<const T*>(a.d_o) + ov, (size_t)H * V, x.c);
-    fetch_tile<T, V>(R.u, reinterpret_cast<const T*>(a.u) + ov, (size_t)H * V, x.c);
-    fetch_tile<T, 64>(R.t, reinterpret_cast<const T*>(a.tmat) + ((size_t)x.gc * H + x.h) * 4096, 64, 64);
-    const int tid = threadIdx.x;
-    if (tid < 64) {
-        const bool in = tid < x.c;
-        R.gam = a.gam[(x.t0 + (in ? tid : x.c - 1)) * H + x.h];
-        R.beta = in ? a.beta[(x.t0 + tid) * H + x.h] : 0.f;
+    const size_t st = ((size_t)x.gc * H + x.h) * (size_t)V * K;
+    if constexpr (kGroup == 0) {
+        fetch_tile<T, K>(R.q, reinterpret_cast<const T*>(a.q) + ok, (size_t)H * K, x.c);
+        fetch_tile<T, K>(R.k, reinterpret_cast<const T*>(a.k) + ok, (size_t)H * K, x.c);
+        const int tid = threadIdx.x;
+        if (tid < 64) {
+            const bool in = tid < x.c;
+            R.gam = a.gam[(x.t0 + (in ? tid : x.c - 1)) * H + x.h];
+            R.beta = in ? a.beta[(x.t0 + tid) * H + x.h] : 0.f;
+        }
+    } else if constexpr (kGroup == 1) {
+        fetch_tile<T, V>(R.d, reinterpret_cast<const T*>(a.d_o) + ov, (size_t)H * V, x.c);
+        fetch_tile<T, 64>(R.t, reinterpret_cast<const T*>(a.tmat) + ((size_t)x.gc * H + x.h) * 4096, 64, 64);
+    } else if constexpr (kGroup == 2) {
+        fetch_tile<T, V>(R.dl, reinterpret_cast<const T*>(a.delta) + ov, (size_t)H * V, x.c);
+        fetch_tile<T, V>(R.dd, reinterpret_cast<const T*>(a.ddelta) + ov, (size_t)H * V, x.c);
+    } else if constexpr (kGroup == 3) {
+        fetch_tile<T, K>(R.s, reinterpret_cast<const T*>(a.hstates) + st, K, V);
+    } else if constexpr (kGroup == 4) {
+        fetch_tile<T, K>(R.g, reinterpret_cast<const T*>(a.gstates) + st, K, V);
+    } else {
+        fetch_tile<T, V>(R.v, reinterpret_cast<const T*>(a.v) + ov, (size_t)H * V, x.c);
     }
-}
-
-template <typename T, int K, int V>
-__device__ __forceinline__ void bwd_fetch_v(BRegs<T, K, V>& R, const BwdChunkArgs& a, const ChunkTask& x) {
-    fetch_tile<T, V>(R.v, reinterpret_cast<const T*>(a.v) + ((size_t)x.t0 * a.geo.H + x.h) * V,
-                     (size_t)a.geo.H * V, x.c);
 }
 
 // Four consecutive LDS elements as fp32.
@@ -507,20 +534,20 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(BwdChunkArgs a) {
     T* sS = reinterpret_cast<T*>(smem + C::off_s);
     T* sG = reinterpret_cast<T*>(smem + C::off_g);
     T* sQ = reinterpret_cast<T*>(smem + C::off_q);
-    T* sW = reinterpret_cast<T*>(smem + C::off_w);
     T* sD = reinterpret_cast<T*>(smem + C::off_d);
-    T* sU = reinterpret_cast<T*>(smem + C::off_u);
+    T* sDl = reinterpret_cast<T*>(smem + C::off_dl);
     T* sX = reinterpret_cast<T*>(smem + C::off_x);
+    T* sdU = reinterpret_cast<T*>(smem + C::off_dd);
+    T* sdW = reinterpret_cast<T*>(smem + C::off_dw);
+    T* sV = reinterpret_cast<T*>(smem + C::off_v);
     T* sTm = reinterpret_cast<T*>(smem + C::off_tm);
     T* sY = reinterpret_cast<T*>(smem + C::off_y);
     T* sMx = reinterpret_cast<T*>(smem + C::off_mx);
-    T* sV = reinterpret_cast<T*>(smem + C::off_v);
-    T* sdW = reinterpret_cast<T*>(smem + C::off_dw);
-    T* sdU = reinterpret_cast<T*>(smem + C::off_du);
     float* sGam = reinterpret_cast<float*>(smem + C::off_gam);
     float* sBeta = reinterpret_cast<float*>(smem + C::off_beta);
     float* sRed = reinterpret_cast<float*>(smem + C::off_red);
     float* sRow = reinterpret_cast<float*>(smem + C::off_row);
+    float* sQd = reinterpret_cast<float*>(smem + C::off_qd);
     float* sDgs = reinterpret_cast<float*>(smem + C::off_dgs);
     float* sSc = reinterpret_cast<float*>(smem + C::off_sc);
 
@@ -530,6 +557,7 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(BwdChunkArgs a) {
     const int tid = threadIdx.x;
     const int wave = wave_id(), lane = tid & 63, ln = lane & 15, gq = lane >> 4;
     const int r = wave * 16 + ln;  // this lane's chunk row in "column" roles
+    constexpr int KW = K / 64;     // k tiles (of 16) per wave in the column-split products
 
     ChunkTask cur;
     int64_t t = next_chunk_task(geo, blockIdx.x, ntasks, cur);
@@ -537,9 +565,12 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(BwdChunkArgs a) {
     BRegs<T, K, V> R;  // the next task's operands
     u32x4 rv[C::NV];    // v of this task
     u32x4 rt[C::NX];    // T of this task
-    bwd_fetch_states(R, a, cur);
-    bwd_fetch_rows(R, a, cur);
-    bwd_fetch_v(R, a, cur);
+    bwd_fetch<0>(R, a, cur);
+    bwd_fetch<1>(R, a, cur);
+    bwd_fetch<2>(R, a, cur);
+    bwd_fetch<3>(R, a, cur);
+    bwd_fetch<4>(R, a, cur);
+    bwd_fetch<5>(R, a, cur);
 
     for (;;) {
         // ---- stage this task (the previous task's LDS reads are done) ---------------------
@@ -548,10 +579,10 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(BwdChunkArgs a) {
         put_tile<T, K>(sG, C::LDK, R.g);
         put_tile<T, K>(sQ, C::LDK, R.q);
         put_tile<T, K>(sK, C::LDK, R.k);
-        put_tile<T, K>(sW, C::LDK, R.w);
         // dO enters every product together with the query scale (o = scale S q)
         put_tile<T, V>(sD, C::LDV, R.d, a.scale);
-        put_tile<T, V>(sU, C::LDV, R.u);
+        put_tile<T, V>(sDl, C::LDV, R.dl);
+        put_tile<T, V>(sdU, C::LDV, R.dd);
         if (tid < 64) {
             sGam[tid] = R.gam;
             sBeta[tid] = R.beta;
@@ -573,8 +604,9 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(BwdChunkArgs a) {
         const int h = cur.h;
         const float Gm = sGam[63];
         const float gr = sGam[r];
+        const float ekt = fast_exp(Gm - gr);
 
-        // ================================ state side ===================================
+        // ======================= state side, rows r of this wave =======================
         // e^Gam <G, S> over the whole state (each thread a slice)
         float gs = 0.f;
         {
@@ -587,101 +619,14 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(BwdChunkArgs a) {
                     gs += dot4(ld4(sG + vv * C::LDK + kk + i), ld4(sS + vv * C::LDK + kk + i));
             }
         }
-        // ---- P tiles with the wave's rows as keys: PmK[jt] = P^T restricted (rows j, cols r)
-        f32x4 PmK[4];
-#pragma unroll
-        for (int jt = 0; jt < 4; ++jt) {
-            PmK[jt] = zero4();
-            if (jt >= wave) {
-#pragma unroll
-                for (int kb = 0; kb < K / 32; ++kb) {
-                    Frag<T> fa, fb;
-                    frag_row(fa, sQ, C::LDK, jt * 16 + ln, kb * 32);
-                    frag_row(fb, sK, C::LDK, r, kb * 32);
-                    mma(PmK[jt], fa, fb);
-                }
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int j = jt * 16 + gq * 4 + i;
-                PmK[jt][i] = (j >= r) ? PmK[jt][i] * fast_exp(sGam[j] - gr) : 0.f;
-            }
-        }
-        // ---- Delta^T[v][r] = U[r][v] - (S W^T)[v][r];  dDelta^T = dO^T P + G K~^T ----------
-        f32x4 DT[V / 16], DDT[V / 16];
-        Frag<T> wr[K / 32], kr[K / 32];
-#pragma unroll
-        for (int kb = 0; kb < K / 32; ++kb) {
-            Frag<T> f;
-            frag_row(f, sW, C::LDK, r, kb * 32);
-            wr[kb] = neg(f);
-            frag_row(kr[kb], sK, C::LDK, r, kb * 32);
-        }
-        const float ekt = fast_exp(Gm - gr);
-#pragma unroll
-        for (int vt = 0; vt < V / 16; ++vt) {
-            DT[vt] = ld4(sU + r * C::LDV + vt * 16 + gq * 4);
-            DDT[vt] = zero4();
-#pragma unroll
-            for (int kb = 0; kb < K / 32; ++kb) {
-                Frag<T> fs, fg;
-                frag_row(fs, sS, C::LDK, vt * 16 + ln, kb * 32);
-                mma(DT[vt], fs, wr[kb]);
-                frag_row(fg, sG, C::LDK, vt * 16 + ln, kb * 32);
-                mma(DDT[vt], fg, kr[kb]);
-            }
-            DDT[vt] *= ekt;
-#pragma unroll
-            for (int jb = 0; jb < 2; ++jb) {
-                Frag<T> fd, fp;
-                frag_col(fd, sD, C::LDV, vt * 16 + ln, jb * 32);  // dO^T row v, slots j
-                frag_acc(fp, PmK[2 * jb], PmK[2 * jb + 1]);
-                mma(DDT[vt], fd, fp);
-            }
-        }
-        // ---- dQt^T, dW^T = -(S^T dDelta^T), dKt^T = G^T Delta^T  (rows k, cols r) --------
-        f32x4 dQT[K / 16], dWT[K / 16], dKT[K / 16];
-        Frag<T> dor[V / 32];
-        {
-            Frag<T> ddf[V / 32], dtf[V / 32];
-#pragma unroll
-            for (int vb = 0; vb < V / 32; ++vb) {
-                frag_row(dor[vb], sD, C::LDV, r, vb * 32);
-                frag_acc(ddf[vb], DDT[2 * vb], DDT[2 * vb + 1], -1.f);
-                frag_acc(dtf[vb], DT[2 * vb], DT[2 * vb + 1]);
-            }
-            lds_sync();  // every read of dO is done: dU = dDelta (rows r) goes over it
-#pragma unroll
-            for (int vt = 0; vt < V / 16; ++vt)
-                store4(sdU + r * C::LDV + vt * 16 + gq * 4, r < c ? DDT[vt] : zero4());
-#pragma unroll
-            for (int kt = 0; kt < K / 16; ++kt) {
-                dQT[kt] = zero4();
-                dWT[kt] = zero4();
-                dKT[kt] = zero4();
-#pragma unroll
-                for (int vb = 0; vb < V / 32; ++vb) {
-                    Frag<T> fs, fg;
-                    frag_col(fs, sS, C::LDK, kt * 16 + ln, vb * 32);  // S^T row k, slots v
-                    mma(dQT[kt], fs, dor[vb]);
-                    mma(dWT[kt], fs, ddf[vb]);
-                    frag_col(fg, sG, C::LDK, kt * 16 + ln, vb * 32);  // G^T row k, slots v
-                    mma(dKT[kt], fg, dtf[vb]);
-                }
-            }
-        }
-        lds_sync();  // every read of S and G is done: dW (rows r) goes over S
-#pragma unroll
-        for (int kt = 0; kt < K / 16; ++kt) store4(sdW + r * C::LDK + kt * 16 + gq * 4, r < c ? dWT[kt] : zero4());
-        // ---- dP^T[j][r] = (U dO^T)[j][r] - (W dQt^T)[j][r];  P with the wave's rows as queries
+        // ---- P (rows j, cols r) and dP^T[j][r] = sum_v Delta[j][v] dO[r][v], j-tiles <= wave
         f32x4 dPT[4], PmQ[4];
         {
-            Frag<T> dqf[K / 32], qr[K / 32];
+            Frag<T> qr[K / 32], dor[V / 32];
 #pragma unroll
-            for (int kb = 0; kb < K / 32; ++kb) {
-                frag_acc(dqf[kb], dQT[2 * kb], dQT[2 * kb + 1], -1.f);
-                frag_row(qr[kb], sQ, C::LDK, r, kb * 32);
-            }
+            for (int kb = 0; kb < K / 32; ++kb) frag_row(qr[kb], sQ, C::LDK, r, kb * 32);
+#pragma unroll
+            for (int vb = 0; vb < V / 32; ++vb) frag_row(dor[vb], sD, C::LDV, r, vb * 32);
 #pragma unroll
             for (int jt = 0; jt < 4; ++jt) {
                 dPT[jt] = zero4();
@@ -689,18 +634,33 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(BwdChunkArgs a) {
                 if (jt <= wave) {
 #pragma unroll
                     for (int vb = 0; vb < V / 32; ++vb) {
-                        Frag<T> fu;
-                        frag_row(fu, sU, C::LDV, jt * 16 + ln, vb * 32);
-                        mma(dPT[jt], fu, dor[vb]);
+                        Frag<T> fd;
+                        frag_row(fd, sDl, C::LDV, jt * 16 + ln, vb * 32);
+                        mma(dPT[jt], fd, dor[vb]);
                     }
 #pragma unroll
                     for (int kb = 0; kb < K / 32; ++kb) {
-                        Frag<T> fw, fk;
-                        frag_row(fw, sW, C::LDK, jt * 16 + ln, kb * 32);
-                        mma(dPT[jt], fw, dqf[kb]);
+                        Frag<T> fk;
                         frag_row(fk, sK, C::LDK, jt * 16 + ln, kb * 32);
                         mma(PmQ[jt], fk, qr[kb]);
                     }
+                }
+            }
+        }
+        // ---- dKt^T[k][r] = sum_v G[v][k] Delta[r][v]  (rows k, cols r) -------------------------
+        f32x4 dKT[K / 16];
+        {
+            Frag<T> dtr[V / 32];
+#pragma unroll
+            for (int vb = 0; vb < V / 32; ++vb) frag_row(dtr[vb], sDl, C::LDV, r, vb * 32);
+#pragma unroll
+            for (int kt = 0; kt < K / 16; ++kt) {
+                dKT[kt] = zero4();
+#pragma unroll
+                for (int vb = 0; vb < V / 32; ++vb) {
+                    Frag<T> fg;
+                    frag_col(fg, sG, C::LDK, kt * 16 + ln, vb * 32);  // G^T row k, slots v
+                    mma(dKT[kt], fg, dtr[vb]);
                 }
             }
         }
@@ -726,32 +686,6 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(BwdChunkArgs a) {
                 if (ln == 0) sRed[wave * 64 + jt * 16 + gq * 4 + i] = -s;
             }
         }
-        // d(gam_r) += e^{gam_r} sum_k dQt[r][k] Q[r][k]
-        const float egr = fast_exp(gr);
-        {
-            float acc = 0.f;
-#pragma unroll
-            for (int kt = 0; kt < K / 16; ++kt) acc += dot4(dQT[kt], ld4(sQ + r * C::LDK + kt * 16 + gq * 4));
-            drow += egr * acc;
-        }
-        // dq^T = e^{gam_r} dQt^T + K^T (L .* dP)^T
-        {
-            Frag<T> lf[2];
-            frag_acc(lf[0], LdP[0], LdP[1]);
-            frag_acc(lf[1], LdP[2], LdP[3]);
-            T* dq = reinterpret_cast<T*>(a.dq) + ((t0 + r) * H + h) * K;
-#pragma unroll
-            for (int kt = 0; kt < K / 16; ++kt) {
-                f32x4 acc = dQT[kt] * egr;
-#pragma unroll
-                for (int jb = 0; jb < 2; ++jb) {
-                    Frag<T> fk;
-                    frag_col(fk, sK, C::LDK, kt * 16 + ln, jb * 32);  // K^T row k, slots j
-                    mma(acc, fk, lf[jb]);
-                }
-                if (r < c) store4(dq + kt * 16 + gq * 4, acc);
-            }
-        }
         // d(gam) from Kt: -e^{Gam-gam_r} sum_k dKt[r][k] K[r][k]; the chunk total gets the sum
         float ktk = 0.f;
 #pragma unroll
@@ -759,7 +693,7 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(BwdChunkArgs a) {
         ktk *= ekt;
         drow -= ktk;
         {
-            float t1 = sum_ln(sum_gq(ktk));  // one value per (r, gq); summed over all lanes it is sum_r
+            const float t1 = sum_ln(sum_gq(ktk));  // one value per (r, gq); summed over all lanes it is sum_r
             const float g1 = sum_gq(sum_ln(gs));
             if (lane == 0) {
                 sSc[wave] = t1;
@@ -768,35 +702,104 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(BwdChunkArgs a) {
         }
         drow = sum_gq(drow);
         if (gq == 0) sRow[r] = drow;
-        lds_sync();  // every read of U is done: the exchange overwrites it
-        // exchange L .* dP: sX[key j][query r] = (L .* dP)[r][j]
+        lds_sync();  // every read of Delta is done: the exchange overwrites it
+        // exchange L .* dP: sX[query r][key j]
 #pragma unroll
-        for (int jt = 0; jt < 4; ++jt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) sX[(jt * 16 + gq * 4 + i) * C::LDX + r] = Elem<T>::from_f(LdP[jt][i]);
+        for (int jt = 0; jt < 4; ++jt) store4(sX + r * C::LDX + jt * 16 + gq * 4, LdP[jt]);
         lds_sync();
-        // dk terms of the state side for the wave's rows as keys: e^{Gam-gam_r} dKt^T + Q^T (L .* dP)[:, r]
+        // dk terms of the state side for the wave's rows as keys y = r:
+        // e^{Gam-gam_y} dKt^T + Q^T (L .* dP)[:, y]
         f32x4 dkpart[K / 16];
         {
-            Frag<T> xf[2];
-            frag_row(xf[0], sX, C::LDX, r, 0);
-            frag_row(xf[1], sX, C::LDX, r, 32);
+            Frag<T> xc[2];
+            frag_col(xc[0], sX, C::LDX, r, 0);  // (L .* dP) column y, slots r'
+            frag_col(xc[1], sX, C::LDX, r, 32);
 #pragma unroll
             for (int kt = 0; kt < K / 16; ++kt) {
                 dkpart[kt] = dKT[kt] * ekt;
 #pragma unroll
                 for (int yb = 0; yb < 2; ++yb) {
                     Frag<T> fq;
-                    frag_col(fq, sQ, C::LDK, kt * 16 + ln, yb * 32);  // Q^T row k, slots y
-                    mma(dkpart[kt], fq, xf[yb]);
+                    frag_col(fq, sQ, C::LDK, kt * 16 + ln, yb * 32);  // Q^T row k, slots r'
+                    mma(dkpart[kt], fq, xc[yb]);
                 }
             }
         }
-        lds_sync();  // the state side's LDS reads are done: the WY side reuses the space
+        // ============ state side, k tiles kw*KW .. of this wave, all chunk rows =============
+        // dQt^T[k][r] = sum_v S[v][k] dO[r][v],  dW^T[k][r] = -sum_v S[v][k] dDelta[r][v]
+        {
+            const int k0 = wave * (K / 4);
+            f32x4 dQT[KW][4], dWT[KW][4];
+            Frag<T> sfc[KW][V / 32];
+#pragma unroll
+            for (int j = 0; j < KW; ++j)
+#pragma unroll
+                for (int vb = 0; vb < V / 32; ++vb)
+                    frag_col(sfc[j][vb], sS, C::LDK, k0 + j * 16 + ln, vb * 32);  // S^T row k, slots v
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                Frag<T> fdo[V / 32], fdd[V / 32];
+#pragma unroll
+                for (int vb = 0; vb < V / 32; ++vb) {
+                    frag_row(fdo[vb], sD, C::LDV, rr * 16 + ln, vb * 32);
+                    Frag<T> f;
+                    frag_row(f, sdU, C::LDV, rr * 16 + ln, vb * 32);
+                    fdd[vb] = neg(f);
+                }
+#pragma unroll
+                for (int j = 0; j < KW; ++j) {
+                    dQT[j][rr] = zero4();
+                    dWT[j][rr] = zero4();
+#pragma unroll
+                    for (int vb = 0; vb < V / 32; ++vb) {
+                        mma(dQT[j][rr], sfc[j][vb], fdo[vb]);
+                        mma(dWT[j][rr], sfc[j][vb], fdd[vb]);
+                    }
+                }
+            }
+            // dq^T = e^{gam_r} dQt^T + K^T (L .* dP)^T, and e^{gam_r} sum_k dQt[r][k] Q[r][k]
+            // over this wave's k slice
+            Frag<T> kc[KW][2];
+#pragma unroll
+            for (int j = 0; j < KW; ++j) {
+                frag_col(kc[j][0], sK, C::LDK, k0 + j * 16 + ln, 0);  // K^T row k, slots j'
+                frag_col(kc[j][1], sK, C::LDK, k0 + j * 16 + ln, 32);
+            }
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                const int row = rr * 16 + ln;
+                const float eg = fast_exp(sGam[row]);
+                Frag<T> xr[2];
+                frag_row(xr[0], sX, C::LDX, row, 0);  // (L .* dP) row r, slots j'
+                frag_row(xr[1], sX, C::LDX, row, 32);
+                T* dq = reinterpret_cast<T*>(a.dq) + ((t0 + row) * H + h) * K + k0;
+                float qd = 0.f;
+#pragma unroll
+                for (int j = 0; j < KW; ++j) {
+                    qd += dot4(dQT[j][rr], ld4(sQ + row * C::LDK + k0 + j * 16 + gq * 4));
+                    f32x4 acc = dQT[j][rr] * eg;
+                    mma(acc, kc[j][0], xr[0]);
+                    mma(acc, kc[j][1], xr[1]);
+                    if (row < c) store4(dq + j * 16 + gq * 4, acc);
+                }
+                qd = sum_gq(qd) * eg;
+                if (gq == 0) sQd[wave * 64 + row] = qd;
+            }
+            lds_sync();  // the state side's LDS reads are done: the WY side reuses the space
+            // dW (rows r) in the operand type, over S
+#pragma unroll
+            for (int j = 0; j < KW; ++j)
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr) {
+                    const int row = rr * 16 + ln;
+                    store4(sdW + row * C::LDK + k0 + j * 16 + gq * 4, row < c ? dWT[j][rr] : zero4());
+                }
+        }
 
         // ================================= WY side =====================================
         if (tid < 64) {
-            float d = sRow[tid] + sRed[tid] + sRed[64 + tid] + sRed[128 + tid] + sRed[192 + tid];
+            float d = sRow[tid] + sRed[tid] + sRed[64 + tid] + sRed[128 + tid] + sRed[192 + tid] + sQd[tid] +
+                      sQd[64 + tid] + sQd[128 + tid] + sQd[192 + tid];
             if (tid == c - 1) {
                 const float kt_all = sSc[0] + sSc[1] + sSc[2] + sSc[3];
                 const float gs_all = sSc[4] + sSc[5] + sSc[6] + sSc[7];
@@ -807,9 +810,9 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(BwdChunkArgs a) {
         put_tile<T, V>(sV, C::LDV, rv);
         put_tile<T, 64>(sTm, C::LDX, rt);
         lds_sync();
-        // The next task's operands load over the rest of this one. They are issued late,
-        // where few registers are live, so that nothing spills or waits on them here.
-        bwd_fetch_rows(R, a, nxt);
+        // The next task's operands load over the rest of this one, issued late (where few
+        // registers are live, so that nothing spills or waits on them) and in groups.
+        bwd_fetch<0>(R, a, nxt);
         const int ra = r;
         // ---- dT[a][b] = beta_b e^{gam_b} (dW K^T)[a][b] + beta_b (dU V^T)[a][b], b < a --------
         // (tiles rows b, cols a: two of them are a B fragment of dT^T)
@@ -847,6 +850,7 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(BwdChunkArgs a) {
             frag_acc(dtf[0], dT[0], dT[1]);
             frag_acc(dtf[1], dT[2], dT[3]);
         }
+        bwd_fetch<1>(R, a, nxt);
         // ---- Y = dT T^T: tiles Y^T[c][a] = sum_b T[c][b] dT[a][b] (T[c][b] = 0 for b > c) -----
 #pragma unroll
         for (int ct = 0; ct < 4; ++ct) {
@@ -862,6 +866,7 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(BwdChunkArgs a) {
             store4(sY + ra * C::LDX + ct * 16 + gq * 4, y);  // Y[a][c]
         }
         lds_sync();
+        bwd_fetch<2>(R, a, nxt);
         // ---- dA[a][c] = -sum_x T[x][a] Y[x][c] for c < a (T[x][a] = 0 for x < a); with the
         // raw A[a][c] = e^{gam_a - gam_c} k_a.k_c: dbeta, d(gam), and Mx = dA beta_a e^{..}
         float dbeta_row = 0.f, dgam_row = 0.f;
@@ -914,8 +919,7 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(BwdChunkArgs a) {
             }
         }
         lds_sync();
-        bwd_fetch_states(R, a, nxt);
-        bwd_fetch_v(R, a, nxt);
+        bwd_fetch<3>(R, a, nxt);
         // ---- dBk^T = dW^T T, dBv^T = dU^T T (rows k / v, cols a);  dK, dV ----------------------
         Frag<T> mrow[2], mcol[2];
         frag_row(mrow[0], sMx, C::LDX, ra, 0);  // Mx row a, slots c
@@ -945,6 +949,7 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(BwdChunkArgs a) {
             }
         }
         {
+            bwd_fetch<4>(R, a, nxt);
             T* dvp = reinterpret_cast<T*>(a.dv) + ((t0 + ra) * H + h) * V;
 #pragma unroll
             for (int vt = 0; vt < V / 16; ++vt) {
@@ -959,6 +964,7 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(BwdChunkArgs a) {
                 if (ra < c) store4(dvp + vt * 16 + gq * 4, bv * ba);
             }
         }
+        bwd_fetch<5>(R, a, nxt);
         dbeta_row = sum_gq(dbeta_row);
         dgam_row = sum_gq(dgam_row);
         if (gq == 0) sRow[ra] = dgam_row;

@@ -353,6 +353,23 @@ __device__ __forceinline__ void put_tile(T* dst, int ld_s, const u32x4 (&x)[N], 
     }
 }
 
+// Store rows [0, rows) of a [64][D] row-major LDS tile (row stride ld) to rows t0.. of a
+// row-major global matrix with row stride ld_g elements; nt threads, 16-byte vectors.
+template <typename T, int D, int NT>
+__device__ __forceinline__ void flush_tile(T* dst, size_t ld_g, int rows, const T* sm, int ld) {
+    constexpr int VEC = Elem<T>::kVec;
+    constexpr int NV = D / VEC;
+    static_assert((64 * NV) % NT == 0, "flush split");
+#pragma unroll
+    for (int it = 0; it < 64 * NV / NT; ++it) {
+        const int u = threadIdx.x + it * NT;
+        const int r = u / NV, cv = u % NV;
+        if (r < rows)
+            *reinterpret_cast<u32x4*>(dst + (size_t)r * ld_g + cv * VEC) =
+                *reinterpret_cast<const u32x4*>(sm + r * ld + cv * VEC);
+    }
+}
+
 // Store a [64][D] row-major LDS tile (rows < rows) to a [.., H, D] tensor.
 template <typename T, int D>
 __device__ __forceinline__ void store_rows(T* __restrict__ dst, int64_t t0, int64_t H, int h, int rows,

@@ -163,6 +163,7 @@ struct RecurArgs {
     float* prep;              // prepass: [total_segs,H,V+K,K] exact maps (R rows, then M^T)
     const int32_t* modes;     // [N,H] 0 none, 1 warmup, 2 exact
     void* hstates;            // kRecurStates: [total_chunks,H,V,K] entry state of every chunk
+    void* delta;              // kRecurStates: [Ttot,H,V] Delta = U - W S^T of every chunk, or null
     float scale;
     int32_t warmup;           // W chunks
     int32_t use_cp;           // segments >= 1 read seginit
@@ -201,6 +202,7 @@ struct RevArgs {
     float* prep;              // prepass: [total_segs,H,V+K,K] reverse maps (R rows, then M^T)
     const int32_t* modes;
     void* gstates;            // [total_chunks,H,V,K] adjoint of the state leaving every chunk
+    void* ddelta;             // kRecurOut: [Ttot,H,V] dL/dDelta of every chunk, or null
     float scale;
     int32_t warmup;
     int32_t use_cp;
@@ -214,9 +216,9 @@ struct BwdChunkArgs {
     const float* g;
     const float* beta;
     const float* gam;
-    const void* w;
-    const void* u;
     const void* d_o;
+    const void* delta;        // [Ttot,H,V] Delta = U - W S^T (from the state pass)
+    const void* ddelta;       // [Ttot,H,V] dL/dDelta = dU (from the reverse pass)
     const void* hstates;      // [total_chunks,H,V,K] state entering every chunk
     const void* gstates;      // [total_chunks,H,V,K] adjoint of the state leaving every chunk
     const void* tmat;         // [total_chunks,H,64,64] T = (I + A)^{-1} of every chunk

@@ -54,6 +54,7 @@ struct RCfg {
     static constexpr int off_pm = off_u + 64 * LDU * (int)sizeof(T);
     static constexpr int off_gam = off_pm + 64 * LDP * (int)sizeof(T);
     static constexpr int total = off_gam + 256;
+    static_assert(64 * LDU <= 64 * LD, "the q tile holds a [64][RT] Delta tile");
     // register prefetch: 16-byte vectors per thread
     static constexpr int NVK = K / VEC;                        // vectors per row of q/k/w
     static constexpr int NVU = RT / VEC;                       // vectors per row of the u tile
@@ -370,6 +371,9 @@ __global__ __launch_bounds__(RT * 4) void k_recur(RecurArgs a) {
             for (int kt = 0; kt < K / 16; ++kt) store4(hs + kt * 16 + gq * 4, accS[kt]);
         }
         lds_sync();  // previous chunk's LDS reads are done
+        if (MODE == kRecurStates && a.delta && ci > cbeg)
+            flush_tile<T, RT, C::NT>(reinterpret_cast<T*>(a.delta) + ((t0 - 64) * H + h) * V + vt * RT,
+                                     (size_t)H * V, 64, L.sQ, C::LDU);
         chunk_stage<T, K, RT, kOut>(R, L);
         lds_sync();
         if (ci + 1 < cend)
@@ -377,10 +381,25 @@ __global__ __launch_bounds__(RT * 4) void k_recur(RecurArgs a) {
         Frag<T> sf[K / 32];
         f32x4 accD[4], accO[4];
         chunk_part1<T, K, RT, kOut>(L, accS, sf, accD, accO);
+        if (MODE == kRecurStates && a.delta) {
+            // Delta for the backward, staged over the unused q tile ([64][RT], row j) and
+            // written out after the next chunk's first barrier
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    L.sQ[(rt * 16 + gq * 4 + i) * C::LDU + wave * 16 + ln] = Elem<T>::from_f(accD[rt][i]);
+        }
         if (kOut) lds_sync();  // P tiles complete
         chunk_part2<T, K, RT, kOut>(a, L, accS, accD, accO, t0, c, h, vt * RT);
     }
 
+    if (MODE == kRecurStates && a.delta && cbeg < cend) {
+        lds_sync();
+        const int cl = cend - 1;
+        flush_tile<T, RT, C::NT>(reinterpret_cast<T*>(a.delta) + ((sg.bos + (int64_t)cl * 64) * H + h) * V + vt * RT,
+                                 (size_t)H * V, min(64, sg.len - cl * 64), L.sQ, C::LDU);
+    }
     if (MODE == kRecurPrepass) {
         if (mode == 1) {
             store_state<K>(accS, a.seginit_out + ((size_t)gs * H + h) * VK, row);
