@@ -53,10 +53,6 @@ struct VCfg {
     static constexpr int ID = (64 * NVD + NT - 1) / NT;   // dO rows
 };
 
-// (row tile, column tile) of the 64x64 product Q K^T whose transpose P^T is staged: the
-// 10 tiles with r >= j plus the two zero tiles read inside the k32 slices of P^T dO.
-__constant__ int8_t kTriB[12][2] = {{0, 0}, {1, 0}, {1, 1}, {2, 0}, {2, 1}, {2, 2},
-                                    {3, 0}, {3, 1}, {3, 2}, {3, 3}, {0, 1}, {2, 3}};
 
 template <typename T, int K, int RT>
 struct RevRegs {
@@ -211,9 +207,14 @@ __global__ __launch_bounds__(RT * 4) void k_reverse(RevArgs a) {
 
     const bool has_do = vt * RT < V;  // M-hat rows of the exact prepass carry no output gradient
     const int dcol0 = has_do ? vt * RT : -1;
-    RevRegs<T, K, RT> R;
-    if (cbeg < cend) rev_fetch<T, K, RT>(R, a, sg.bos + (int64_t)(cend - 1) * 64, min(64, sg.len - (cend - 1) * 64), h, dcol0);
-    for (int ci = cend - 1; ci >= cbeg; --ci) {
+    // Operands travel two chunks ahead of use, in two register buffers that alternate.
+    RevRegs<T, K, RT> R0, R1;
+    auto fetch0 = [&](RevRegs<T, K, RT>& R, int cn) {
+        rev_fetch<T, K, RT>(R, a, sg.bos + (int64_t)cn * 64, min(64, sg.len - cn * 64), h, dcol0);
+    };
+    if (cbeg < cend) fetch0(R0, cend - 1);
+    if (cbeg < cend - 1) fetch0(R1, cend - 2);
+    auto step = [&](RevRegs<T, K, RT>& R, const int ci) {
         const int64_t t0 = sg.bos + (int64_t)ci * 64;
         if (MODE == kRecurOut) {
             // adjoint of the state leaving this chunk
@@ -227,8 +228,11 @@ __global__ __launch_bounds__(RT * 4) void k_reverse(RevArgs a) {
                                      (size_t)H * V, min(64, sg.len - (ci + 1) * 64), sDd, C::LDD);
         rev_stage<T, K, RT>(R, L, a.scale);
         lds_sync();
-        if (ci - 1 >= cbeg)
-            rev_fetch<T, K, RT>(R, a, t0 - 64, min(64, sg.len - (ci - 1) * 64), h, dcol0);
+        // two chunks ahead: this buffer's next chunk (the first chunk again past the start)
+        {
+            const int cn = max(ci - 2, cbeg);
+            rev_fetch<T, K, RT>(R, a, sg.bos + (int64_t)cn * 64, min(64, sg.len - cn * 64), h, dcol0);
+        }
 
         Frag<T> gf[K / 32];
 #pragma unroll
@@ -236,7 +240,7 @@ __global__ __launch_bounds__(RT * 4) void k_reverse(RevArgs a) {
         if (has_do) {
             // P^T[j][r] = e^{gam_r - gam_j} (Q K^T)[r][j] for r >= j, staged row-major by j
             for (int idx = wave; idx < 12; idx += C::NW) {
-                const int rt = kTriB[idx][0], jt = kTriB[idx][1];
+                const int rt = tri_row(idx), jt = tri_col(idx);
                 f32x4 acc = zero4();
 #pragma unroll
                 for (int kb = 0; kb < (jt <= rt ? K / 32 : 0); ++kb) {
@@ -321,6 +325,10 @@ __global__ __launch_bounds__(RT * 4) void k_reverse(RevArgs a) {
                 }
             }
         }
+        };
+    for (int ci = cend - 1; ci >= cbeg; ci -= 2) {
+        step(R0, ci);
+        if (ci - 1 >= cbeg) step(R1, ci - 1);
     }
 
     if (MODE == kRecurOut && a.ddelta && cbeg < cend) {

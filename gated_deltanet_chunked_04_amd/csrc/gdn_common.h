@@ -45,6 +45,19 @@ __device__ __forceinline__ bf16_t f2bf(float f) { return __builtin_bit_cast(bf16
 
 __device__ __forceinline__ float fast_exp(float x) { return __expf(x); }
 
+// (row tile, column tile) of tile idx of a 64x64 matrix in 16x16 tiles, in the order
+// (0,0) (1,0) (1,1) (2,0) (2,1) (2,2) (3,0) (3,1) (3,2) (3,3): the lower triangle; then
+// (0,1) and (2,3), the upper tiles that fall inside the k32 slices of a product with
+// the triangle. Arithmetic rather than a table: a table lookup is a global load, and
+// waiting on it would also wait on every load in flight.
+__device__ __forceinline__ int tri_row(int idx) {
+    return idx < 1 ? 0 : idx < 3 ? 1 : idx < 6 ? 2 : idx < 10 ? 3 : (idx == 10 ? 0 : 2);
+}
+__device__ __forceinline__ int tri_col(int idx) {
+    const int ti = tri_row(idx);
+    return idx < 10 ? idx - ti * (ti + 1) / 2 : (idx == 10 ? 1 : 3);
+}
+
 // Wave index within the workgroup, as a wave-uniform (scalar) value: branches on it
 // stay scalar branches instead of exec-masked ones.
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)); }
@@ -317,16 +330,16 @@ __device__ __forceinline__ u32x4 scale_vec<float>(const u32x4& x, float s) {
 }
 
 // Rows [0, rows) of a row-major global matrix into registers: 16-byte vector e of the
-// tile goes to thread e % 256, slot e / 256; rows >= rows are zero. Each load is a
-// wave-uniform base plus one 32-bit lane offset shared by all slots (the host bounds a
-// tile's extent below 2 GiB), so no per-slot 64-bit address stays live.
-template <typename T, int D, int N>
+// tile goes to thread e % NT, slot e / NT (NT threads); rows >= rows are zero. Each load
+// is a wave-uniform base plus one 32-bit lane offset shared by all slots (the host bounds
+// a tile's extent below 2 GiB), so no per-slot 64-bit address stays live.
+template <typename T, int D, int N, int NT = 256>
 __device__ __forceinline__ void fetch_tile(u32x4 (&x)[N], const T* src, size_t ld_g, int rows) {
     constexpr int VEC = Elem<T>::kVec;
-    constexpr int NVR = D / VEC;    // vectors per row
-    constexpr int RPI = 256 / NVR;  // rows per slot
-    static_assert(256 % NVR == 0, "row split");
-    const int r0 = threadIdx.x / NVR, cv = threadIdx.x % NVR;
+    constexpr int NVR = D / VEC;   // vectors per row
+    constexpr int RPI = NT / NVR;  // rows per slot
+    static_assert(NT % NVR == 0, "row split");
+    const int r0 = (int)threadIdx.x / NVR, cv = (int)threadIdx.x % NVR;
     const uint32_t off = ((uint32_t)r0 * (uint32_t)ld_g + (uint32_t)(cv * VEC)) * (uint32_t)sizeof(T);
     const char* b = reinterpret_cast<const char*>(src);
     const size_t step = (size_t)RPI * ld_g * sizeof(T);
@@ -342,12 +355,12 @@ __device__ __forceinline__ void fetch_tile(u32x4 (&x)[N], const T* src, size_t l
 }
 
 // The registers of fetch_tile into a row-major LDS tile (row stride ld_s), scaled by s.
-template <typename T, int D, int N>
+template <typename T, int D, int N, int NT = 256>
 __device__ __forceinline__ void put_tile(T* dst, int ld_s, const u32x4 (&x)[N], float s = 1.f) {
     constexpr int NVR = D / Elem<T>::kVec;
 #pragma unroll
     for (int it = 0; it < N; ++it) {
-        const int e = threadIdx.x + it * 256;
+        const int e = (int)threadIdx.x + it * NT;
         const int r = e / NVR, cv = e % NVR;
         *reinterpret_cast<u32x4*>(dst + r * ld_s + cv * Elem<T>::kVec) = s == 1.f ? x[it] : scale_vec<T>(x[it], s);
     }

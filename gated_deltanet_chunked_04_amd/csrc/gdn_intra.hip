@@ -50,9 +50,6 @@ struct IntraSmem {
     static constexpr int total = off_kk + 256;
 };
 
-// Gram tiles (row tile >= column tile) of a 64x64 lower triangle.
-__constant__ int8_t kTri[10][2] = {{0, 0}, {1, 0}, {1, 1}, {2, 0}, {2, 1}, {2, 2},
-                                   {3, 0}, {3, 1}, {3, 2}, {3, 3}};
 
 // One task's inputs in registers (fetched while the previous task computes).
 template <typename T, int K, int V>
@@ -137,7 +134,7 @@ __global__ __launch_bounds__(kThreads) void k_intra(IntraArgs args) {
 
         // ---- stage 2: A = strict_lower(diag(beta) (D .* K K^T)) -----------------------
         for (int idx = wave; idx < 10; idx += 4) {
-            const int ti = kTri[idx][0], tj = kTri[idx][1];
+            const int ti = tri_row(idx), tj = tri_col(idx);
             f32x4 acc = zero4();
 #pragma unroll
             for (int kb = 0; kb < K / 32; ++kb) {

@@ -58,66 +58,44 @@ struct RCfg {
     // register prefetch: 16-byte vectors per thread
     static constexpr int NVK = K / VEC;                        // vectors per row of q/k/w
     static constexpr int NVU = RT / VEC;                       // vectors per row of the u tile
-    static constexpr int IQ = (64 * NVK + NT - 1) / NT;        // q, w rows
-    static constexpr int IK = (32 * NVK + NT - 1) / NT;        // k row pairs
-    static constexpr int IU = (64 * NVU + NT - 1) / NT;        // u rows
+    static constexpr int IQ = 64 * NVK / NT;                   // q, w, k rows
+    static constexpr int IU = 64 * NVU / NT;                   // u rows
+    static_assert(IQ * NT == 64 * NVK && IU * NT == 64 * NVU, "tile split");
 };
 
-// (row tile, column tile) of the 64x64 P matrix: the 10 lower tiles plus the two upper
-// tiles (0,1) and (2,3) that fall inside the k32 slices read by P*Delta (written as zero).
-__constant__ int8_t kTriR[12][2] = {{0, 0}, {1, 0}, {1, 1}, {2, 0}, {2, 1}, {2, 2},
-                                    {3, 0}, {3, 1}, {3, 2}, {3, 3}, {0, 1}, {2, 3}};
 
-// One chunk's operands in registers (loaded one chunk ahead of use).
+// One chunk's operands in registers (loaded ahead of use), fetched in three pieces at
+// different points of the step so that the loads drain behind the work.
 template <typename T, int K, int RT, bool kQ>
 struct ChunkRegs {
     using C = RCfg<T, K, RT>;
     u32x4 q[kQ ? C::IQ : 1];
     u32x4 w[C::IQ];
-    u32x4 ka[C::IK], kb[C::IK];
+    u32x4 k[C::IQ];
     u32x4 u[C::IU];
     float gam;
 };
 
-template <typename T, int K, int RT, bool kQ>
+template <int kPart, typename T, int K, int RT, bool kQ>
 __device__ __forceinline__ void chunk_fetch(ChunkRegs<T, K, RT, kQ>& R, const RecurArgs& a, int64_t t0, int c, int h,
                                             int ucol0) {
     using C = RCfg<T, K, RT>;
-    const int tid = threadIdx.x;
     const int64_t H = a.geo.H;
-    const T* q = reinterpret_cast<const T*>(a.q);
-    const T* k = reinterpret_cast<const T*>(a.k);
-    const T* w = reinterpret_cast<const T*>(a.w);
-    const T* u = reinterpret_cast<const T*>(a.u);
-    const u32x4 z = u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int it = 0; it < C::IQ; ++it) {
-        const int e = tid + it * C::NT;
-        const int r = e / C::NVK, cv = e % C::NVK;
-        const bool ok = e < 64 * C::NVK && r < c;
-        const size_t off = ((t0 + r) * H + h) * K + cv * C::VEC;
-        if (kQ) R.q[it] = ok ? *reinterpret_cast<const u32x4*>(q + off) : z;
-        R.w[it] = ok ? *reinterpret_cast<const u32x4*>(w + off) : z;
-    }
-#pragma unroll
-    for (int it = 0; it < C::IK; ++it) {
-        const int e = tid + it * C::NT;
-        const int rp = e / C::NVK, cv = e % C::NVK;
-        const bool in = e < 32 * C::NVK;
-        const int r0 = 2 * rp, r1 = 2 * rp + 1;
-        R.ka[it] = (in && r0 < c) ? *reinterpret_cast<const u32x4*>(k + ((t0 + r0) * H + h) * K + cv * C::VEC) : z;
-        R.kb[it] = (in && r1 < c) ? *reinterpret_cast<const u32x4*>(k + ((t0 + r1) * H + h) * K + cv * C::VEC) : z;
-    }
-#pragma unroll
-    for (int it = 0; it < C::IU; ++it) {
-        const int e = tid + it * C::NT;
-        const int r = e / C::NVU, cv = e % C::NVU;
-        const bool ok = ucol0 >= 0 && e < 64 * C::NVU && r < c;
-        R.u[it] = ok ? *reinterpret_cast<const u32x4*>(u + ((t0 + r) * H + h) * a.geo.V + ucol0 + cv * C::VEC) : z;
-    }
-    if (tid < 64) {
-        const int r = tid < c ? tid : c - 1;  // rows past the chunk end carry the chunk total
-        R.gam = a.gam[(t0 + r) * H + h];
+    const size_t ok = ((size_t)t0 * H + h) * K;
+    if constexpr (kPart == 0) {
+        if constexpr (kQ) fetch_tile<T, K, C::IQ, C::NT>(R.q, reinterpret_cast<const T*>(a.q) + ok, (size_t)H * K, c);
+        fetch_tile<T, K, C::IQ, C::NT>(R.w, reinterpret_cast<const T*>(a.w) + ok, (size_t)H * K, c);
+    } else if constexpr (kPart == 1) {
+        fetch_tile<T, K, C::IQ, C::NT>(R.k, reinterpret_cast<const T*>(a.k) + ok, (size_t)H * K, c);
+    } else {
+        // the M rows of the exact prepass (ucol0 < 0) have no u columns
+        fetch_tile<T, RT, C::IU, C::NT>(R.u, reinterpret_cast<const T*>(a.u) + ((size_t)t0 * H + h) * a.geo.V + max(ucol0, 0),
+                                        (size_t)H * a.geo.V, ucol0 >= 0 ? c : 0);
+        const int tid = threadIdx.x;
+        if (tid < 64) {
+            const int r = tid < c ? tid : c - 1;  // rows past the chunk end carry the chunk total
+            R.gam = a.gam[(t0 + r) * H + h];
+        }
     }
 }
 
@@ -134,36 +112,11 @@ struct ChunkLds {
 template <typename T, int K, int RT, bool kQ>
 __device__ __forceinline__ void chunk_stage(const ChunkRegs<T, K, RT, kQ>& R, const ChunkLds<T, K, RT>& L) {
     using C = RCfg<T, K, RT>;
-    const int tid = threadIdx.x;
-#pragma unroll
-    for (int it = 0; it < C::IQ; ++it) {
-        const int e = tid + it * C::NT;
-        if (e < 64 * C::NVK) {
-            const int r = e / C::NVK, cv = e % C::NVK;
-            if (kQ) *reinterpret_cast<u32x4*>(L.sQ + r * C::LD + cv * C::VEC) = R.q[it];
-            *reinterpret_cast<u32x4*>(L.sW + r * C::LD + cv * C::VEC) = R.w[it];
-        }
-    }
-#pragma unroll
-    for (int it = 0; it < C::IK; ++it) {
-        const int e = tid + it * C::NT;
-        if (e < 32 * C::NVK) {
-            const int rp = e / C::NVK, cv = e % C::NVK;
-            const int r0 = 2 * rp;
-            const u32x4 A = R.ka[it], B = R.kb[it];
-            *reinterpret_cast<u32x4*>(L.sK + r0 * C::LD + cv * C::VEC) = A;
-            *reinterpret_cast<u32x4*>(L.sK + (r0 + 1) * C::LD + cv * C::VEC) = B;
-        }
-    }
-#pragma unroll
-    for (int it = 0; it < C::IU; ++it) {
-        const int e = tid + it * C::NT;
-        if (e < 64 * C::NVU) {
-            const int r = e / C::NVU, cv = e % C::NVU;
-            *reinterpret_cast<u32x4*>(L.sU + r * C::LDU + cv * C::VEC) = R.u[it];
-        }
-    }
-    if (tid < 64) L.sGam[tid] = R.gam;
+    if constexpr (kQ) put_tile<T, K, C::IQ, C::NT>(L.sQ, C::LD, R.q);
+    put_tile<T, K, C::IQ, C::NT>(L.sW, C::LD, R.w);
+    put_tile<T, K, C::IQ, C::NT>(L.sK, C::LD, R.k);
+    put_tile<T, RT, C::IU, C::NT>(L.sU, C::LDU, R.u);
+    if (threadIdx.x < 64) L.sGam[threadIdx.x] = R.gam;
 }
 
 // One chunk of the recurrence for this wave's 16 state rows (columns of S^T).
@@ -183,58 +136,84 @@ __device__ __forceinline__ void chunk_part1(const ChunkLds<T, K, RT>& L, const f
         frag_acc(sf[kb], accS[2 * kb], accS[2 * kb + 1]);
         frag_acc(nsf[kb], accS[2 * kb], accS[2 * kb + 1], -1.f);
     }
+    // Independent accumulators are updated side by side (k32 slice outer, tiles inner) and
+    // each slice's fragments are loaded before its products, so neither the matrix-core
+    // latency nor the LDS latency sits on a chain of dependent products.
     if (kOut) {
-        for (int idx = wave; idx < 12; idx += C::NW) {
-            const int rt = kTriR[idx][0], jt = kTriR[idx][1];
-            f32x4 acc = zero4();
+        // this wave's P tiles (rows r of Q, columns j of K), at most NPT of them
+        constexpr int NPT = (12 + C::NW - 1) / C::NW;
+        f32x4 pacc[NPT];
+        int prt[NPT], pjt[NPT];
+        bool pon[NPT], pmm[NPT];
 #pragma unroll
-            for (int kb = 0; kb < (jt <= rt ? K / 32 : 0); ++kb) {
-                Frag<T> fa, fb;
-                frag_row(fa, L.sK, C::LD, jt * 16 + ln, kb * 32);
-                frag_row(fb, L.sQ, C::LD, rt * 16 + ln, kb * 32);
-                mma(acc, fa, fb);
-            }
-            // acc[i] = (Q K^T)[r = rt*16+ln][j = jt*16+gq*4+i]
-            const int r = rt * 16 + ln;
-            const float gr = L.sGam[r];
-            f32x4 v;
+        for (int m = 0; m < NPT; ++m) {
+            const int idx = wave + m * C::NW;
+            pon[m] = idx < 12;
+            prt[m] = pon[m] ? tri_row(idx) : 0;
+            pjt[m] = pon[m] ? tri_col(idx) : 0;
+            pmm[m] = pon[m] && pjt[m] <= prt[m];
+            pacc[m] = zero4();
+        }
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int j = jt * 16 + gq * 4 + i;
-                v[i] = (j <= r) ? acc[i] * fast_exp(gr - L.sGam[j]) : 0.f;
+        for (int kb = 0; kb < K / 32; ++kb) {
+            Frag<T> fa[NPT], fb[NPT];
+#pragma unroll
+            for (int m = 0; m < NPT; ++m) {
+                if (pmm[m]) {
+                    frag_row(fa[m], L.sK, C::LD, pjt[m] * 16 + ln, kb * 32);
+                    frag_row(fb[m], L.sQ, C::LD, prt[m] * 16 + ln, kb * 32);
+                }
             }
-            store4(L.sPm + r * C::LDP + jt * 16 + gq * 4, v);
+#pragma unroll
+            for (int m = 0; m < NPT; ++m)
+                if (pmm[m]) mma(pacc[m], fa[m], fb[m]);
+        }
+#pragma unroll
+        for (int m = 0; m < NPT; ++m) {
+            if (pon[m]) {
+                // pacc[i] = (Q K^T)[r = rt*16+ln][j = jt*16+gq*4+i]
+                const int r = prt[m] * 16 + ln;
+                const float gr = L.sGam[r];
+                const f32x4 gj = *reinterpret_cast<const f32x4*>(L.sGam + pjt[m] * 16 + gq * 4);
+                f32x4 v;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int j = pjt[m] * 16 + gq * 4 + i;
+                    v[i] = (j <= r) ? pacc[m][i] * fast_exp(gr - gj[i]) : 0.f;
+                }
+                store4(L.sPm + r * C::LDP + pjt[m] * 16 + gq * 4, v);
+            }
         }
     }
-    // Delta = U - W S^T  (rows j of the chunk, columns = the wave's state rows)
+    // Delta = U - W S^T  (rows j of the chunk, columns = the wave's state rows), and
+    // O^T tiles: accO[rt][i] = O^T[v = wave*16 + gq*4 + i][r = rt*16 + ln]. The S^T
+    // accumulators are an A fragment of S and the Delta accumulators an A fragment of
+    // Delta^T, so O^T = S Q^T diag(e^gam) + Delta^T P^T needs no data movement, and each
+    // lane ends up with four consecutive value columns of one token row.
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
             accD[rt][i] = Elem<T>::to_f(L.sU[(rt * 16 + gq * 4 + i) * C::LDU + wave * 16 + ln]);
-#pragma unroll
-        for (int kb = 0; kb < K / 32; ++kb) {
-            Frag<T> fa;
-            frag_row(fa, L.sW, C::LD, rt * 16 + ln, kb * 32);
-            mma(accD[rt], fa, nsf[kb]);
-        }
+        if (kOut) accO[rt] = zero4();
     }
-    // O^T tiles: accO[rt][i] = O^T[v = wave*16 + gq*4 + i][r = rt*16 + ln]. The S^T
-    // accumulators are an A fragment of S and the Delta accumulators an A fragment of
-    // Delta^T, so O^T = S Q^T diag(e^gam) + Delta^T P^T needs no data movement, and each
-    // lane ends up with four consecutive value columns of one token row.
-    if (kOut) {
+#pragma unroll
+    for (int kb = 0; kb < K / 32; ++kb) {
+        Frag<T> fw[4], fq[4];
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) {
-            accO[rt] = zero4();
-#pragma unroll
-            for (int kb = 0; kb < K / 32; ++kb) {
-                Frag<T> fb;
-                frag_row(fb, L.sQ, C::LD, rt * 16 + ln, kb * 32);
-                mma(accO[rt], sf[kb], fb);
-            }
-            accO[rt] *= fast_exp(L.sGam[rt * 16 + ln]);
+            frag_row(fw[rt], L.sW, C::LD, rt * 16 + ln, kb * 32);
+            if (kOut) frag_row(fq[rt], L.sQ, C::LD, rt * 16 + ln, kb * 32);
         }
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+            mma(accD[rt], fw[rt], nsf[kb]);
+            if (kOut) mma(accO[rt], sf[kb], fq[rt]);
+        }
+    }
+    if (kOut) {
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) accO[rt] *= fast_exp(L.sGam[rt * 16 + ln]);
     }
 }
 
@@ -250,13 +229,12 @@ __device__ __forceinline__ void chunk_part2(const RecurArgs& a, const ChunkLds<T
         frag_acc(df[0], accD[0], accD[1]);
         frag_acc(df[1], accD[2], accD[3]);
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt) {
+        for (int kb = 0; kb < 2; ++kb) {
+            Frag<T> fb[4];
 #pragma unroll
-            for (int kb = 0; kb <= (rt >> 1); ++kb) {
-                Frag<T> fb;
-                frag_row(fb, L.sPm, C::LDP, rt * 16 + ln, kb * 32);
-                mma(accO[rt], df[kb], fb);
-            }
+            for (int rt = 2 * kb; rt < 4; ++rt) frag_row(fb[rt], L.sPm, C::LDP, rt * 16 + ln, kb * 32);
+#pragma unroll
+            for (int rt = 2 * kb; rt < 4; ++rt) mma(accO[rt], df[kb], fb[rt]);
         }
         T* o = reinterpret_cast<T*>(a.o);
         const int64_t H = a.geo.H;
@@ -273,23 +251,25 @@ __device__ __forceinline__ void chunk_part2(const RecurArgs& a, const ChunkLds<T
     Frag<T> dtf[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
+        const f32x4 g0 = *reinterpret_cast<const f32x4*>(L.sGam + kb * 32 + gq * 4);
+        const f32x4 g1 = *reinterpret_cast<const f32x4*>(L.sGam + kb * 32 + 16 + gq * 4);
         f32x4 r0, r1;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            r0[i] = fast_exp(G - L.sGam[kb * 32 + gq * 4 + i]);
-            r1[i] = fast_exp(G - L.sGam[kb * 32 + 16 + gq * 4 + i]);
+            r0[i] = fast_exp(G - g0[i]);
+            r1[i] = fast_exp(G - g1[i]);
         }
         frag_acc_rows(dtf[kb], accD[2 * kb], accD[2 * kb + 1], r0, r1);
     }
 #pragma unroll
-    for (int kt = 0; kt < K / 16; ++kt) {
-        accS[kt] *= eG;
+    for (int kt = 0; kt < K / 16; ++kt) accS[kt] *= eG;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            Frag<T> fa;
-            frag_col(fa, L.sK, C::LD, kt * 16 + ln, kb * 32);  // K^T row k, slots j
-            mma(accS[kt], fa, dtf[kb]);
-        }
+    for (int kb = 0; kb < 2; ++kb) {
+        Frag<T> fa[K / 16];
+#pragma unroll
+        for (int kt = 0; kt < K / 16; ++kt) frag_col(fa[kt], L.sK, C::LD, kt * 16 + ln, kb * 32);  // K^T row k, slots j
+#pragma unroll
+        for (int kt = 0; kt < K / 16; ++kt) mma(accS[kt], fa[kt], dtf[kb]);
     }
 }
 
@@ -359,9 +339,16 @@ __global__ __launch_bounds__(RT * 4) void k_recur(RecurArgs a) {
     }
 
     const int ucol0 = (vt * RT < V) ? vt * RT : -1;
-    ChunkRegs<T, K, RT, kOut> R;
-    if (cbeg < cend) chunk_fetch<T, K, RT, kOut>(R, a, sg.bos + (int64_t)cbeg * 64, min(64, sg.len - cbeg * 64), h, ucol0);
-    for (int ci = cbeg; ci < cend; ++ci) {
+    // Operands travel two chunks ahead of use, in two register buffers that alternate.
+    ChunkRegs<T, K, RT, kOut> R0, R1;
+    auto fetch0 = [&](ChunkRegs<T, K, RT, kOut>& R, int cn) {
+        chunk_fetch<0>(R, a, sg.bos + (int64_t)cn * 64, min(64, sg.len - cn * 64), h, ucol0);
+        chunk_fetch<1>(R, a, sg.bos + (int64_t)cn * 64, min(64, sg.len - cn * 64), h, ucol0);
+        chunk_fetch<2>(R, a, sg.bos + (int64_t)cn * 64, min(64, sg.len - cn * 64), h, ucol0);
+    };
+    if (cbeg < cend) fetch0(R0, cbeg);
+    if (cbeg + 1 < cend) fetch0(R1, cbeg + 1);
+    auto step = [&](ChunkRegs<T, K, RT, kOut>& R, const int ci) {
         const int64_t t0 = sg.bos + (int64_t)ci * 64;
         const int c = min(64, sg.len - ci * 64);
         if (MODE == kRecurStates) {
@@ -376,8 +363,12 @@ __global__ __launch_bounds__(RT * 4) void k_recur(RecurArgs a) {
                                      (size_t)H * V, 64, L.sQ, C::LDU);
         chunk_stage<T, K, RT, kOut>(R, L);
         lds_sync();
-        if (ci + 1 < cend)
-            chunk_fetch<T, K, RT, kOut>(R, a, t0 + 64, min(64, sg.len - (ci + 1) * 64), h, ucol0);
+        // two chunks ahead: this buffer's next chunk (the last chunk again past the end),
+        // in three pieces over the step
+        const int cn = min(ci + 2, cend - 1);
+        const int64_t tn = sg.bos + (int64_t)cn * 64;
+        const int cnn = min(64, sg.len - cn * 64);
+        chunk_fetch<0>(R, a, tn, cnn, h, ucol0);
         Frag<T> sf[K / 32];
         f32x4 accD[4], accO[4];
         chunk_part1<T, K, RT, kOut>(L, accS, sf, accD, accO);
@@ -390,8 +381,14 @@ __global__ __launch_bounds__(RT * 4) void k_recur(RecurArgs a) {
                 for (int i = 0; i < 4; ++i)
                     L.sQ[(rt * 16 + gq * 4 + i) * C::LDU + wave * 16 + ln] = Elem<T>::from_f(accD[rt][i]);
         }
+        chunk_fetch<1>(R, a, tn, cnn, h, ucol0);
         if (kOut) lds_sync();  // P tiles complete
         chunk_part2<T, K, RT, kOut>(a, L, accS, accD, accO, t0, c, h, vt * RT);
+        chunk_fetch<2>(R, a, tn, cnn, h, ucol0);
+        };
+    for (int ci = cbeg; ci < cend; ci += 2) {
+        step(R0, ci);
+        if (ci + 1 < cend) step(R1, ci + 1);
     }
 
     if (MODE == kRecurStates && a.delta && cbeg < cend) {
