@@ -215,6 +215,26 @@ __device__ __forceinline__ void store4(bf16_t* p, const f32x4& x) {
 }
 __device__ __forceinline__ void store4(float* p, const f32x4& x) { *reinterpret_cast<f32x4*>(p) = x; }
 
+// Four fp32 values in the storage type, as the register image one vector store writes.
+template <typename T> struct Pack4;
+template <> struct Pack4<bf16_t> {
+    typedef u32x2 type;
+    __device__ static type make(const f32x4& x) { return u32x2{pack_bf2(x.x, x.y), pack_bf2(x.z, x.w)}; }
+};
+template <> struct Pack4<float> {
+    typedef f32x4 type;
+    __device__ static type make(const f32x4& x) { return x; }
+};
+
+// Holds x in its registers up to this point. A vector store reads its data registers
+// late, and the wait that protects them retires every older memory operation too (the
+// counter is in order); holding a store's data until the next point that waits for
+// loads anyway keeps that wait from landing on prefetches still in flight.
+template <typename X>
+__device__ __forceinline__ void hold(const X& x) {
+    asm volatile("" : : "v"(x));
+}
+
 // ---------------------------------------------------------------------------
 // Sequence / chunk bookkeeping shared by the kernels.
 struct SeqInfo {

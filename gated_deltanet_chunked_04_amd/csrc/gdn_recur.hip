@@ -220,7 +220,7 @@ __device__ __forceinline__ void chunk_part1(const ChunkLds<T, K, RT>& L, const f
 template <typename T, int K, int RT, bool kOut>
 __device__ __forceinline__ void chunk_part2(const RecurArgs& a, const ChunkLds<T, K, RT>& L, f32x4 (&accS)[K / 16],
                                             f32x4 (&accD)[4], f32x4 (&accO)[4], int64_t t0, int c, int h,
-                                            int vcol0) {
+                                            int vcol0, typename Pack4<T>::type (&okeep)[4]) {
     using C = RCfg<T, K, RT>;
     const int tid = threadIdx.x;
     const int wave = wave_id(), lane = tid & 63, ln = lane & 15, gq = lane >> 4;
@@ -240,9 +240,13 @@ __device__ __forceinline__ void chunk_part2(const RecurArgs& a, const ChunkLds<T
         const int64_t H = a.geo.H;
         const int V = a.geo.V;
 #pragma unroll
+        for (int rt = 0; rt < 4; ++rt) okeep[rt] = Pack4<T>::make(accO[rt] * a.scale);
+#pragma unroll
         for (int rt = 0; rt < 4; ++rt) {
             const int r = rt * 16 + ln;
-            if (r < c) store4(o + ((t0 + r) * H + h) * V + vcol0 + wave * 16 + gq * 4, accO[rt] * a.scale);
+            if (r < c)
+                *reinterpret_cast<typename Pack4<T>::type*>(o + ((t0 + r) * H + h) * V + vcol0 + wave * 16 + gq * 4) =
+                    okeep[rt];
         }
     }
     // S^T <- e^Gam S^T + K^T diag(e^{Gam-gam}) Delta
@@ -339,33 +343,68 @@ __global__ __launch_bounds__(RT * 4) void k_recur(RecurArgs a) {
     }
 
     const int ucol0 = (vt * RT < V) ? vt * RT : -1;
-    // Operands travel two chunks ahead of use, in two register buffers that alternate.
+    // Operands are fetched in three pieces issued over each step. Store data is held until
+    // the next chunk's staging (see hold()), which waits for the step's loads anyway.
+    typedef typename Pack4<T>::type PV;
+    constexpr int NFL = 64 * (RT / C::VEC) / C::NT;  // Delta flush vectors per thread
+    PV okeep[4], hkeep[K / 16];
+    u32x4 fkeep[NFL];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) okeep[i] = PV{};
+#pragma unroll
+    for (int i = 0; i < K / 16; ++i) hkeep[i] = PV{};
+#pragma unroll
+    for (int i = 0; i < NFL; ++i) fkeep[i] = u32x4{0u, 0u, 0u, 0u};
+    // The states and output passes prefetch one chunk ahead; the prepass, which has little
+    // work per chunk to cover the loads, two chunks ahead in two alternating buffers.
+    constexpr int kDepth = MODE == kRecurPrepass ? 2 : 1;
     ChunkRegs<T, K, RT, kOut> R0, R1;
-    auto fetch0 = [&](ChunkRegs<T, K, RT, kOut>& R, int cn) {
-        chunk_fetch<0>(R, a, sg.bos + (int64_t)cn * 64, min(64, sg.len - cn * 64), h, ucol0);
-        chunk_fetch<1>(R, a, sg.bos + (int64_t)cn * 64, min(64, sg.len - cn * 64), h, ucol0);
-        chunk_fetch<2>(R, a, sg.bos + (int64_t)cn * 64, min(64, sg.len - cn * 64), h, ucol0);
+    auto fetch_all = [&](ChunkRegs<T, K, RT, kOut>& R, int cn) {
+        const int64_t tb = sg.bos + (int64_t)cn * 64;
+        const int cb = min(64, sg.len - cn * 64);
+        chunk_fetch<0>(R, a, tb, cb, h, ucol0);
+        chunk_fetch<1>(R, a, tb, cb, h, ucol0);
+        chunk_fetch<2>(R, a, tb, cb, h, ucol0);
     };
-    if (cbeg < cend) fetch0(R0, cbeg);
-    if (cbeg + 1 < cend) fetch0(R1, cbeg + 1);
+    if (cbeg < cend) fetch_all(R0, cbeg);
+    if (kDepth == 2 && cbeg + 1 < cend) fetch_all(R1, cbeg + 1);
     auto step = [&](ChunkRegs<T, K, RT, kOut>& R, const int ci) {
         const int64_t t0 = sg.bos + (int64_t)ci * 64;
         const int c = min(64, sg.len - ci * 64);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) hold(okeep[i]);
+#pragma unroll
+        for (int i = 0; i < K / 16; ++i) hold(hkeep[i]);
+#pragma unroll
+        for (int i = 0; i < NFL; ++i) hold(fkeep[i]);
         if (MODE == kRecurStates) {
             // entry state of this chunk, in the input precision
             T* hs = reinterpret_cast<T*>(a.hstates) + ((size_t)(sg.choff + ci) * H + h) * VK + (size_t)row * K;
 #pragma unroll
-            for (int kt = 0; kt < K / 16; ++kt) store4(hs + kt * 16 + gq * 4, accS[kt]);
+            for (int kt = 0; kt < K / 16; ++kt) hkeep[kt] = Pack4<T>::make(accS[kt]);
+#pragma unroll
+            for (int kt = 0; kt < K / 16; ++kt) *reinterpret_cast<PV*>(hs + kt * 16 + gq * 4) = hkeep[kt];
         }
         lds_sync();  // previous chunk's LDS reads are done
-        if (MODE == kRecurStates && a.delta && ci > cbeg)
-            flush_tile<T, RT, C::NT>(reinterpret_cast<T*>(a.delta) + ((t0 - 64) * H + h) * V + vt * RT,
-                                     (size_t)H * V, 64, L.sQ, C::LDU);
+        if (MODE == kRecurStates && a.delta && ci > cbeg) {
+            // the previous chunk's Delta, staged over the q tile
+            T* dst = reinterpret_cast<T*>(a.delta) + ((t0 - 64) * H + h) * V + vt * RT;
+            constexpr int NV = RT / C::VEC;
+#pragma unroll
+            for (int it = 0; it < NFL; ++it) {
+                const int u = (int)threadIdx.x + it * C::NT;
+                fkeep[it] = *reinterpret_cast<const u32x4*>(L.sQ + (u / NV) * C::LDU + (u % NV) * C::VEC);
+            }
+#pragma unroll
+            for (int it = 0; it < NFL; ++it) {
+                const int u = (int)threadIdx.x + it * C::NT;
+                *reinterpret_cast<u32x4*>(dst + (size_t)(u / NV) * H * V + (u % NV) * C::VEC) = fkeep[it];
+            }
+        }
         chunk_stage<T, K, RT, kOut>(R, L);
         lds_sync();
-        // two chunks ahead: this buffer's next chunk (the last chunk again past the end),
-        // in three pieces over the step
-        const int cn = min(ci + 2, cend - 1);
+        // operands kDepth chunks ahead (the last chunk again past the end), in three pieces
+        const int cn = min(ci + kDepth, cend - 1);
         const int64_t tn = sg.bos + (int64_t)cn * 64;
         const int cnn = min(64, sg.len - cn * 64);
         chunk_fetch<0>(R, a, tn, cnn, h, ucol0);
@@ -383,12 +422,16 @@ __global__ __launch_bounds__(RT * 4) void k_recur(RecurArgs a) {
         }
         chunk_fetch<1>(R, a, tn, cnn, h, ucol0);
         if (kOut) lds_sync();  // P tiles complete
-        chunk_part2<T, K, RT, kOut>(a, L, accS, accD, accO, t0, c, h, vt * RT);
+        chunk_part2<T, K, RT, kOut>(a, L, accS, accD, accO, t0, c, h, vt * RT, okeep);
         chunk_fetch<2>(R, a, tn, cnn, h, ucol0);
-        };
-    for (int ci = cbeg; ci < cend; ci += 2) {
-        step(R0, ci);
-        if (ci + 1 < cend) step(R1, ci + 1);
+    };
+    if constexpr (kDepth == 2) {
+        for (int ci = cbeg; ci < cend; ci += 2) {
+            step(R0, ci);
+            if (ci + 1 < cend) step(R1, ci + 1);
+        }
+    } else {
+        for (int ci = cbeg; ci < cend; ++ci) step(R0, ci);
     }
 
     if (MODE == kRecurStates && a.delta && cbeg < cend) {
