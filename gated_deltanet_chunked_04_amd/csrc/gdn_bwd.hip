@@ -49,8 +49,9 @@ struct VCfg {
     static constexpr int total = off_gam + 256;
     static constexpr int NVK = K / VEC;
     static constexpr int NVD = RT / VEC;
-    static constexpr int IK = (64 * NVK + NT - 1) / NT;   // q, k, w rows
-    static constexpr int ID = (64 * NVD + NT - 1) / NT;   // dO rows
+    static constexpr int IK = 64 * NVK / NT;   // q, k, w rows
+    static constexpr int ID = 64 * NVD / NT;   // dO rows
+    static_assert(IK * NT == 64 * NVK && ID * NT == 64 * NVD, "tile split");
 };
 
 
@@ -63,38 +64,35 @@ struct RevRegs {
     float gam;
 };
 
-template <typename T, int K, int RT>
+// One chunk's operands in three pieces, issued at different points of a step.
+template <int kPart, typename T, int K, int RT>
 __device__ __forceinline__ void rev_fetch(RevRegs<T, K, RT>& R, const RevArgs& a, int64_t t0, int c, int h,
                                           int dcol0) {
     using C = VCfg<T, K, RT>;
-    const int tid = threadIdx.x;
     const int64_t H = a.geo.H;
-    const T* q = reinterpret_cast<const T*>(a.q);
-    const T* k = reinterpret_cast<const T*>(a.k);
-    const T* w = reinterpret_cast<const T*>(a.w);
-    const T* d_o = reinterpret_cast<const T*>(a.d_o);
-    const u32x4 z = u32x4{0u, 0u, 0u, 0u};
+    const size_t ok = ((size_t)t0 * H + h) * K;
+    if constexpr (kPart == 0) {
+        fetch_tile<T, K, C::IK, C::NT>(R.q, reinterpret_cast<const T*>(a.q) + ok, (size_t)H * K, c);
+        fetch_tile<T, K, C::IK, C::NT>(R.k, reinterpret_cast<const T*>(a.k) + ok, (size_t)H * K, c);
+        // gate cumsum of each q row this thread holds (rows r0 + it * NT / NVK)
+        const int r0 = (int)threadIdx.x / C::NVK;
 #pragma unroll
-    for (int it = 0; it < C::IK; ++it) {
-        const int e = tid + it * C::NT;
-        const int r = e / C::NVK, cv = e % C::NVK;
-        const bool ok = e < 64 * C::NVK && r < c;
-        const size_t off = ((t0 + r) * H + h) * K + cv * C::VEC;
-        R.q[it] = ok ? *reinterpret_cast<const u32x4*>(q + off) : z;
-        R.k[it] = ok ? *reinterpret_cast<const u32x4*>(k + off) : z;
-        R.w[it] = ok ? *reinterpret_cast<const u32x4*>(w + off) : z;
-        R.gq[it] = ok ? a.gam[(t0 + r) * H + h] : 0.f;
-    }
-#pragma unroll
-    for (int it = 0; it < C::ID; ++it) {
-        const int e = tid + it * C::NT;
-        const int r = e / C::NVD, cv = e % C::NVD;
-        const bool ok = dcol0 >= 0 && e < 64 * C::NVD && r < c;
-        R.d[it] = ok ? *reinterpret_cast<const u32x4*>(d_o + ((t0 + r) * H + h) * a.geo.V + dcol0 + cv * C::VEC) : z;
-    }
-    if (tid < 64) {
-        const int r = tid < c ? tid : c - 1;
-        R.gam = a.gam[(t0 + r) * H + h];
+        for (int it = 0; it < C::IK; ++it) {
+            const int r = r0 + it * (C::NT / C::NVK);
+            R.gq[it] = a.gam[(t0 + min(r, c - 1)) * H + h];
+        }
+    } else if constexpr (kPart == 1) {
+        fetch_tile<T, K, C::IK, C::NT>(R.w, reinterpret_cast<const T*>(a.w) + ok, (size_t)H * K, c);
+    } else {
+        // the M-hat rows of the exact prepass (dcol0 < 0) have no output gradient
+        fetch_tile<T, RT, C::ID, C::NT>(R.d, reinterpret_cast<const T*>(a.d_o) + ((size_t)t0 * H + h) * a.geo.V +
+                                                 max(dcol0, 0),
+                                        (size_t)H * a.geo.V, dcol0 >= 0 ? c : 0);
+        const int tid = threadIdx.x;
+        if (tid < 64) {
+            const int r = tid < c ? tid : c - 1;
+            R.gam = a.gam[(t0 + r) * H + h];
+        }
     }
 }
 
@@ -112,28 +110,17 @@ struct RevLds {
 template <typename T, int K, int RT>
 __device__ __forceinline__ void rev_stage(const RevRegs<T, K, RT>& R, const RevLds<T, K, RT>& L, float scale) {
     using C = VCfg<T, K, RT>;
-    const int tid = threadIdx.x;
+    put_tile<T, K, C::IK, C::NT>(L.sQ, C::LD, R.q);
+    put_tile<T, K, C::IK, C::NT>(L.sK, C::LD, R.k);
+    put_tile<T, K, C::IK, C::NT>(L.sW, C::LD, R.w);
 #pragma unroll
     for (int it = 0; it < C::IK; ++it) {
-        const int e = tid + it * C::NT;
-        if (e < 64 * C::NVK) {
-            const int r = e / C::NVK, cv = e % C::NVK;
-            const int o = r * C::LD + cv * C::VEC;
-            *reinterpret_cast<u32x4*>(L.sQ + o) = R.q[it];
-            *reinterpret_cast<u32x4*>(L.sQs + o) = scale_vec<T>(R.q[it], scale * fast_exp(R.gq[it]));
-            *reinterpret_cast<u32x4*>(L.sK + o) = R.k[it];
-            *reinterpret_cast<u32x4*>(L.sW + o) = R.w[it];
-        }
+        const int e = (int)threadIdx.x + it * C::NT;
+        const int r = e / C::NVK, cv = e % C::NVK;
+        *reinterpret_cast<u32x4*>(L.sQs + r * C::LD + cv * C::VEC) = scale_vec<T>(R.q[it], scale * fast_exp(R.gq[it]));
     }
-#pragma unroll
-    for (int it = 0; it < C::ID; ++it) {
-        const int e = tid + it * C::NT;
-        if (e < 64 * C::NVD) {
-            const int r = e / C::NVD, cv = e % C::NVD;
-            *reinterpret_cast<u32x4*>(L.sD + r * C::LDD + cv * C::VEC) = R.d[it];
-        }
-    }
-    if (tid < 64) L.sGam[tid] = R.gam;
+    put_tile<T, RT, C::ID, C::NT>(L.sD, C::LDD, R.d);
+    if (threadIdx.x < 64) L.sGam[threadIdx.x] = R.gam;
 }
 
 template <typename T, int K, int RT, int MODE>
@@ -207,85 +194,146 @@ __global__ __launch_bounds__(RT * 4) void k_reverse(RevArgs a) {
 
     const bool has_do = vt * RT < V;  // M-hat rows of the exact prepass carry no output gradient
     const int dcol0 = has_do ? vt * RT : -1;
-    // Operands travel two chunks ahead of use, in two register buffers that alternate.
+    // Operands are fetched in three pieces over each step: one chunk ahead in the output
+    // pass, two (alternating buffers) in the prepass, which has little work per chunk.
+    // Store data is held until the next chunk's staging (see hold()).
+    constexpr int kDepth = MODE == kRecurPrepass ? 2 : 1;
+    typedef typename Pack4<T>::type PV;
+    constexpr int NFL = 64 * (RT / C::VEC) / C::NT;  // dDelta flush vectors per thread
+    PV gkeep[K / 16];
+    u32x4 fkeep[NFL];
+#pragma unroll
+    for (int i = 0; i < K / 16; ++i) gkeep[i] = PV{};
+#pragma unroll
+    for (int i = 0; i < NFL; ++i) fkeep[i] = u32x4{0u, 0u, 0u, 0u};
     RevRegs<T, K, RT> R0, R1;
-    auto fetch0 = [&](RevRegs<T, K, RT>& R, int cn) {
-        rev_fetch<T, K, RT>(R, a, sg.bos + (int64_t)cn * 64, min(64, sg.len - cn * 64), h, dcol0);
+    auto fetch_all = [&](RevRegs<T, K, RT>& R, int cn) {
+        const int64_t tb = sg.bos + (int64_t)cn * 64;
+        const int cb = min(64, sg.len - cn * 64);
+        rev_fetch<0>(R, a, tb, cb, h, dcol0);
+        rev_fetch<1>(R, a, tb, cb, h, dcol0);
+        rev_fetch<2>(R, a, tb, cb, h, dcol0);
     };
-    if (cbeg < cend) fetch0(R0, cend - 1);
-    if (cbeg < cend - 1) fetch0(R1, cend - 2);
+    if (cbeg < cend) fetch_all(R0, cend - 1);
+    if (kDepth == 2 && cbeg < cend - 1) fetch_all(R1, cend - 2);
+    constexpr int NPT = (12 + C::NW - 1) / C::NW;  // P^T tiles per wave
     auto step = [&](RevRegs<T, K, RT>& R, const int ci) {
         const int64_t t0 = sg.bos + (int64_t)ci * 64;
+#pragma unroll
+        for (int i = 0; i < K / 16; ++i) hold(gkeep[i]);
+#pragma unroll
+        for (int i = 0; i < NFL; ++i) hold(fkeep[i]);
         if (MODE == kRecurOut) {
             // adjoint of the state leaving this chunk
             T* gs_out = reinterpret_cast<T*>(a.gstates) + ((size_t)(sg.choff + ci) * H + h) * VK + (size_t)row * K;
 #pragma unroll
-            for (int kt = 0; kt < K / 16; ++kt) store4(gs_out + kt * 16 + gq * 4, accG[kt]);
+            for (int kt = 0; kt < K / 16; ++kt) gkeep[kt] = Pack4<T>::make(accG[kt]);
+#pragma unroll
+            for (int kt = 0; kt < K / 16; ++kt) *reinterpret_cast<PV*>(gs_out + kt * 16 + gq * 4) = gkeep[kt];
         }
         lds_sync();
-        if (MODE == kRecurOut && a.ddelta && ci < cend - 1)
-            flush_tile<T, RT, C::NT>(reinterpret_cast<T*>(a.ddelta) + ((t0 + 64) * H + h) * V + vt * RT,
-                                     (size_t)H * V, min(64, sg.len - (ci + 1) * 64), sDd, C::LDD);
+        if (MODE == kRecurOut && a.ddelta && ci < cend - 1) {
+            // the previous (later) chunk's dDelta
+            T* dst = reinterpret_cast<T*>(a.ddelta) + ((t0 + 64) * H + h) * V + vt * RT;
+            const int cp = min(64, sg.len - (ci + 1) * 64);
+            constexpr int NV = RT / C::VEC;
+#pragma unroll
+            for (int it = 0; it < NFL; ++it) {
+                const int u = (int)threadIdx.x + it * C::NT;
+                fkeep[it] = *reinterpret_cast<const u32x4*>(sDd + (u / NV) * C::LDD + (u % NV) * C::VEC);
+            }
+#pragma unroll
+            for (int it = 0; it < NFL; ++it) {
+                const int u = (int)threadIdx.x + it * C::NT;
+                if (u / NV < cp) *reinterpret_cast<u32x4*>(dst + (size_t)(u / NV) * H * V + (u % NV) * C::VEC) = fkeep[it];
+            }
+        }
         rev_stage<T, K, RT>(R, L, a.scale);
         lds_sync();
-        // two chunks ahead: this buffer's next chunk (the first chunk again past the start)
-        {
-            const int cn = max(ci - 2, cbeg);
-            rev_fetch<T, K, RT>(R, a, sg.bos + (int64_t)cn * 64, min(64, sg.len - cn * 64), h, dcol0);
-        }
+        const int cn = max(ci - kDepth, cbeg);
+        const int64_t tn = sg.bos + (int64_t)cn * 64;
+        const int cnn = min(64, sg.len - cn * 64);
+        rev_fetch<0>(R, a, tn, cnn, h, dcol0);
 
         Frag<T> gf[K / 32];
 #pragma unroll
         for (int kb = 0; kb < K / 32; ++kb) frag_acc(gf[kb], accG[2 * kb], accG[2 * kb + 1]);
+        // Independent accumulators are updated side by side (k32 slice outer, tiles inner)
+        // and each slice's fragments are loaded before its products.
         if (has_do) {
             // P^T[j][r] = e^{gam_r - gam_j} (Q K^T)[r][j] for r >= j, staged row-major by j
-            for (int idx = wave; idx < 12; idx += C::NW) {
-                const int rt = tri_row(idx), jt = tri_col(idx);
-                f32x4 acc = zero4();
+            f32x4 pacc[NPT];
+            int prt[NPT], pjt[NPT];
+            bool pon[NPT], pmm[NPT];
 #pragma unroll
-                for (int kb = 0; kb < (jt <= rt ? K / 32 : 0); ++kb) {
-                    Frag<T> fa, fb;
-                    frag_row(fa, L.sQ, C::LD, rt * 16 + ln, kb * 32);
-                    frag_row(fb, L.sK, C::LD, jt * 16 + ln, kb * 32);
-                    mma(acc, fa, fb);  // (Q K^T) tile: lane holds [r = rt*16+gq*4+i][j = jt*16+ln]
-                }
-                const int j = jt * 16 + ln;
-                const float gj = L.sGam[j];
-                f32x4 v;
+            for (int m = 0; m < NPT; ++m) {
+                const int idx = wave + m * C::NW;
+                pon[m] = idx < 12;
+                prt[m] = pon[m] ? tri_row(idx) : 0;
+                pjt[m] = pon[m] ? tri_col(idx) : 0;
+                pmm[m] = pon[m] && pjt[m] <= prt[m];
+                pacc[m] = zero4();
+            }
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int r = rt * 16 + gq * 4 + i;
-                    v[i] = (r >= j) ? a.scale * acc[i] * fast_exp(L.sGam[r] - gj) : 0.f;
+            for (int kb = 0; kb < K / 32; ++kb) {
+                Frag<T> fa[NPT], fb[NPT];
+#pragma unroll
+                for (int m = 0; m < NPT; ++m) {
+                    if (pmm[m]) {
+                        frag_row(fa[m], L.sQ, C::LD, prt[m] * 16 + ln, kb * 32);
+                        frag_row(fb[m], L.sK, C::LD, pjt[m] * 16 + ln, kb * 32);
+                    }
                 }
-                store4(L.sPm + j * C::LDP + rt * 16 + gq * 4, v);
+#pragma unroll
+                for (int m = 0; m < NPT; ++m)
+                    if (pmm[m]) mma(pacc[m], fa[m], fb[m]);  // lane holds [r = rt*16+gq*4+i][j = jt*16+ln]
+            }
+#pragma unroll
+            for (int m = 0; m < NPT; ++m) {
+                if (pon[m]) {
+                    const int j = pjt[m] * 16 + ln;
+                    const float gj = L.sGam[j];
+                    const f32x4 gr = *reinterpret_cast<const f32x4*>(L.sGam + prt[m] * 16 + gq * 4);
+                    f32x4 v;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int r = prt[m] * 16 + gq * 4 + i;
+                        v[i] = (r >= j) ? a.scale * pacc[m][i] * fast_exp(gr[i] - gj) : 0.f;
+                    }
+                    store4(L.sPm + j * C::LDP + prt[m] * 16 + gq * 4, v);
+                }
             }
         }
         // dDelta tiles (rows j, columns = the wave's adjoint rows): Kt G^T part
         const float Gm = L.sGam[63];
         f32x4 accD[4];
 #pragma unroll
-        for (int jt = 0; jt < 4; ++jt) {
-            accD[jt] = zero4();
+        for (int jt = 0; jt < 4; ++jt) accD[jt] = zero4();
 #pragma unroll
-            for (int kb = 0; kb < K / 32; ++kb) {
-                Frag<T> fa;
-                frag_row(fa, L.sK, C::LD, jt * 16 + ln, kb * 32);
-                mma(accD[jt], fa, gf[kb]);
-            }
+        for (int kb = 0; kb < K / 32; ++kb) {
+            Frag<T> fa[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) accD[jt][i] *= fast_exp(Gm - L.sGam[jt * 16 + gq * 4 + i]);
+            for (int jt = 0; jt < 4; ++jt) frag_row(fa[jt], L.sK, C::LD, jt * 16 + ln, kb * 32);
+#pragma unroll
+            for (int jt = 0; jt < 4; ++jt) mma(accD[jt], fa[jt], gf[kb]);
         }
+#pragma unroll
+        for (int jt = 0; jt < 4; ++jt) {
+            const f32x4 gj = *reinterpret_cast<const f32x4*>(L.sGam + jt * 16 + gq * 4);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) accD[jt][i] *= fast_exp(Gm - gj[i]);
+        }
+        rev_fetch<1>(R, a, tn, cnn, h, dcol0);
         lds_sync();  // P^T complete
         if (has_do) {
 #pragma unroll
-            for (int jt = 0; jt < 4; ++jt) {
+            for (int rb = 0; rb < 2; ++rb) {
+                Frag<T> fb, fa[4];
+                frag_col(fb, L.sD, C::LDD, wave * 16 + ln, rb * 32);  // dO column v, slots r
 #pragma unroll
-                for (int rb = (jt >> 1); rb < 2; ++rb) {
-                    Frag<T> fa, fb;
-                    frag_row(fa, L.sPm, C::LDP, jt * 16 + ln, rb * 32);
-                    frag_col(fb, L.sD, C::LDD, wave * 16 + ln, rb * 32);  // dO column v, slots r
-                    mma(accD[jt], fa, fb);
-                }
+                for (int jt = 0; jt <= 2 * rb + 1; ++jt) frag_row(fa[jt], L.sPm, C::LDP, jt * 16 + ln, rb * 32);
+#pragma unroll
+                for (int jt = 0; jt <= 2 * rb + 1; ++jt) mma(accD[jt], fa[jt], fb);
             }
         }
         if (MODE == kRecurOut && a.ddelta) {
@@ -308,27 +356,32 @@ __global__ __launch_bounds__(RT * 4) void k_reverse(RevArgs a) {
             for (int rb = 0; rb < 2; ++rb) frag_col(dof[rb], L.sD, C::LDD, wave * 16 + ln, rb * 32);
         }
 #pragma unroll
-        for (int kt = 0; kt < K / 16; ++kt) {
-            accG[kt] *= eG;
+        for (int kt = 0; kt < K / 16; ++kt) accG[kt] *= eG;
 #pragma unroll
-            for (int jb = 0; jb < 2; ++jb) {
-                Frag<T> fa;
-                frag_col(fa, L.sW, C::LD, kt * 16 + ln, jb * 32);  // W^T row k, slots j
-                mma(accG[kt], fa, ddf[jb]);
-            }
+        for (int jb = 0; jb < 2; ++jb) {
+            Frag<T> fw[K / 16];
+#pragma unroll
+            for (int kt = 0; kt < K / 16; ++kt) frag_col(fw[kt], L.sW, C::LD, kt * 16 + ln, jb * 32);  // W^T row k, slots j
+#pragma unroll
+            for (int kt = 0; kt < K / 16; ++kt) mma(accG[kt], fw[kt], ddf[jb]);
             if (has_do) {
+                Frag<T> fq[K / 16];
 #pragma unroll
-                for (int rb = 0; rb < 2; ++rb) {
-                    Frag<T> fa;
-                    frag_col(fa, L.sQs, C::LD, kt * 16 + ln, rb * 32);  // (scale e^gam Q)^T row k, slots r
-                    mma(accG[kt], fa, dof[rb]);
-                }
+                for (int kt = 0; kt < K / 16; ++kt)
+                    frag_col(fq[kt], L.sQs, C::LD, kt * 16 + ln, jb * 32);  // (scale e^gam Q)^T row k, slots r
+#pragma unroll
+                for (int kt = 0; kt < K / 16; ++kt) mma(accG[kt], fq[kt], dof[jb]);
             }
         }
-        };
-    for (int ci = cend - 1; ci >= cbeg; ci -= 2) {
-        step(R0, ci);
-        if (ci - 1 >= cbeg) step(R1, ci - 1);
+        rev_fetch<2>(R, a, tn, cnn, h, dcol0);
+    };
+    if constexpr (kDepth == 2) {
+        for (int ci = cend - 1; ci >= cbeg; ci -= 2) {
+            step(R0, ci);
+            if (ci - 1 >= cbeg) step(R1, ci - 1);
+        }
+    } else {
+        for (int ci = cend - 1; ci >= cbeg; --ci) step(R0, ci);
     }
 
     if (MODE == kRecurOut && a.ddelta && cbeg < cend) {
