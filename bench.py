@@ -40,12 +40,16 @@ def algorithmic_counts(B, T, H, K, V, esize, N, nseg_total, lengths=None):
     Bytes count each operand a kernel must read once and each result it writes once
     (per token-head unless noted; e = input element size):
       intra        reads k, v, g, beta; writes w, u, gate cumsum            (2K+2V) e + 12
+                   (the backward's launch also writes T = (I+A)^-1: + 64 e)
       recur_out    reads q, k, w, u, gate cumsum; writes o                  (3K+2V) e + 4
                    + initial / final states and sub-sequence entry states
-      recur_states reads k, w, u, gate cumsum; writes one V x K state per chunk
-      bwd_reverse  reads q, k, w, dO, gate cumsum; writes one V x K adjoint per chunk
-      bwd_chunk    reads the chunk's state and adjoint, q, k, v, w, u, dO, gate cumsum, beta;
-                   writes dq, dk, dv, dg, dbeta                 (3K+3V) e + 8 + (2K+V) e + 8
+      recur_states reads k, w, u, gate cumsum; writes Delta               (2K+2V) e + 4
+                   + one V x K state per chunk
+      bwd_reverse  reads q, k, w, dO, gate cumsum; writes dDelta          (3K+2V) e + 4
+                   + one V x K adjoint per chunk
+      bwd_chunk    reads q, k, v, dO, Delta, dDelta, T, gate cumsum, beta and the chunk's
+                   state and adjoint; writes dq, dk, dv, dg, dbeta
+                                                  (2K+4V+64) e + 8 + (2K+V) e + 8 + 2 V K e / 64
     Flops per chunk of c tokens (C=64; triangular products at half):
       forward   intra: c(c-1)K + c(c-1)(c-2)/3 + c(c-1)(K+V);  recur: 3*2cKV + c(c+1)(K+V)
       backward  the reverse-mode products of the chunk map: dQt, dDelta (both terms), dKt,
@@ -62,9 +66,9 @@ def algorithmic_counts(B, T, H, K, V, esize, N, nseg_total, lengths=None):
     nb = dict(
         intra=th * ((2 * K + 2 * V) * esize + 12),
         recur_out=th * ((3 * K + 2 * V) * esize + 4) + N * H * V * K * 4 * 2 + max(nseg_total - N, 0) * H * V * K * 4,
-        recur_states=th * ((2 * K + V) * esize + 4) + chunks * H * st,
-        bwd_reverse=th * ((3 * K + V) * esize + 4) + chunks * H * st,
-        bwd_chunk=th * ((3 * K + 3 * V) * esize + 8 + (2 * K + V) * esize + 8) + 2 * chunks * H * st,
+        recur_states=th * ((2 * K + 2 * V) * esize + 4) + chunks * H * st,
+        bwd_reverse=th * ((3 * K + 2 * V) * esize + 4) + chunks * H * st,
+        bwd_chunk=th * ((2 * K + 4 * V + 64) * esize + 8 + (2 * K + V) * esize + 8) + 2 * chunks * H * st,
     )
     f_intra = f_recur = f_bwd = 0.0
     for n in lens:
@@ -74,6 +78,46 @@ def algorithmic_counts(B, T, H, K, V, esize, N, nseg_total, lengths=None):
             f_recur += 3 * 2 * c * K * V + c * (c + 1) * (K + V)
             f_bwd += 7 * 2 * c * K * V + c * c * (2 * V + 2 * (K + V) + K + V + 4 * K) + 2 * c ** 3 / 3
     return dict(bytes=nb, flops=dict(fwd=(f_intra + f_recur) * H, bwd=f_bwd * H), tokens=toks)
+
+
+# Source files that define each kernel (plus the shared headers): a traffic figure measured
+# with hardware counters holds only for the sources it was measured on.
+KERNEL_SOURCES = {
+    "intra": ["gdn_intra.hip"], "cp_decide": ["gdn_recur.hip"], "cp_prepass": ["gdn_recur.hip"],
+    "cp_scan": ["gdn_recur.hip"], "recur_out": ["gdn_recur.hip"], "recur_states": ["gdn_recur.hip"],
+    "bwd_cp_prepass": ["gdn_bwd.hip"], "bwd_cp_scan": ["gdn_recur.hip"], "bwd_reverse": ["gdn_bwd.hip"],
+    "bwd_chunk": ["gdn_bwd.hip"],
+}
+
+
+def kernel_source_hash(kernel):
+    import hashlib
+    csrc = os.path.join(ROOT, "gated_deltanet_chunked_04_amd", "csrc")
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel] + ["gdn_common.h", "gdn_kernels.h"]:
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch from the counter summary in profiles/, or None.
+
+    profiles/<kernel>_<workload>_traffic.md carries a line
+      traffic: kernel=<k> workload=<w> sources=<hash> bytes_per_launch=<n>
+    written from two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) scaled by a copy of known
+    size; it counts only while the kernel's sources hash to the recorded value."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.md")
+    if not os.path.exists(path) or kernel not in KERNEL_SOURCES:
+        return None
+    with open(path) as fh:
+        for line in fh:
+            if line.startswith("traffic:"):
+                kv = dict(x.split("=", 1) for x in line.split()[1:])
+                if kv.get("kernel") == kernel and kv.get("workload") == workload and \
+                        kv.get("sources") == kernel_source_hash(kernel):
+                    return int(kv["bytes_per_launch"])
+    return None
 
 
 def cpu_baseline(inp, tokens, passes):
@@ -105,6 +149,9 @@ def main():
     ap.add_argument("--pass", dest="passes", default="both", choices=["both", "fwd", "bwd"])
     ap.add_argument("--cp", default=None, help="override the workload's CP mode (auto/off/on/exact/warmup)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="also run one device-to-device copy of this many MiB (a reference for HBM "
+                         "byte counters taken with rocprofv3 --pmc)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -168,6 +215,16 @@ def main():
         torch.cuda.synchronize()
         return (time.perf_counter() - t0) * 1e3 / n
 
+    if args.copy_calibration > 0:
+        # a plain copy of known size: its FETCH_SIZE / WRITE_SIZE read per dispatch calibrate
+        # the same counters for the kernels
+        src = torch.empty(args.copy_calibration << 20, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
     for _ in range(args.warmup):
         step()
     ms = timed(step, args.steps)
@@ -195,7 +252,8 @@ def main():
     bytes_per_launch = counts["bytes"][dominant]  # every launch of it covers the whole workload once
     achieved = bytes_per_launch / dur_s / 1e9
     roofline = {"bound": "hbm", "kernel": dominant, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": measured_traffic(dominant, w.name),
                 "algorithmic_bytes_per_launch": int(bytes_per_launch), "avg_launch_us": round(dur_s * 1e6, 2)}
     peak_mfma = BF16_PEAK_TFLOPS if esize == 2 else FP32_PEAK_TFLOPS
     tflops = flops_step / (ms * 1e-3) / 1e12
