@@ -557,9 +557,9 @@ __global__ __launch_bounds__(RT * 4) void k_scan(ScanArgs a) {
 #pragma unroll
         for (int kt = 0; kt < K / 16; ++kt) accS[kt] = zero4();
 
-    f32x4 mreg[SC::IM];
-    f32x4 rreg[K / 16];
-    auto fetch = [&](int s) {
+    // maps two steps ahead, in two register buffers that alternate
+    f32x4 mA[SC::IM], rA[K / 16], mB[SC::IM], rB[K / 16];
+    auto fetch = [&](f32x4 (&mreg)[SC::IM], f32x4 (&rreg)[K / 16], int s) {
         const float* P = a.prep + ((size_t)(segoff + s) * H + h) * PS;
 #pragma unroll
         for (int it = 0; it < SC::IM; ++it) {
@@ -571,8 +571,10 @@ __global__ __launch_bounds__(RT * 4) void k_scan(ScanArgs a) {
     // forward: S_{s+1} = S_s M_s + R_s, s = 0 .. nseg-2
     // reverse: G_{s-1} = G_s M_s + R_s, s = nseg-1 .. 1 (adjoint leaving segment s-1)
     auto src_of = [&](int step) { return a.reverse ? nseg - 1 - step : step; };
-    fetch(src_of(0));
-    for (int step = 0; step + 1 < nseg; ++step) {
+    const int nsteps = nseg - 1;
+    fetch(mA, rA, src_of(0));
+    if (nsteps > 1) fetch(mB, rB, src_of(1));
+    auto one = [&](f32x4 (&mreg)[SC::IM], f32x4 (&rreg)[K / 16], int step) {
         const int s = src_of(step);
         const int dst = a.reverse ? s - 1 : s + 1;
         lds_sync();
@@ -588,22 +590,26 @@ __global__ __launch_bounds__(RT * 4) void k_scan(ScanArgs a) {
         f32x4 nx[K / 16];
 #pragma unroll
         for (int kt = 0; kt < K / 16; ++kt) nx[kt] = rreg[kt];
-        if (step + 2 < nseg) fetch(src_of(step + 1));
+        // this buffer's next map (the last one again past the end)
+        fetch(mreg, rreg, src_of(min(step + 2, nsteps - 1)));
         Frag<T> sf[K / 32];
 #pragma unroll
         for (int kb = 0; kb < K / 32; ++kb) frag_acc(sf[kb], accS[2 * kb], accS[2 * kb + 1]);
 #pragma unroll
-        for (int kt = 0; kt < K / 16; ++kt) {
+        for (int kb = 0; kb < K / 32; ++kb) {
+            Frag<T> fa[K / 16];
 #pragma unroll
-            for (int kb = 0; kb < K / 32; ++kb) {
-                Frag<T> fa;
-                frag_row(fa, sM, SC::LDM, kt * 16 + ln, kb * 32);  // rows of M^T
-                mma(nx[kt], fa, sf[kb]);
-            }
+            for (int kt = 0; kt < K / 16; ++kt) frag_row(fa[kt], sM, SC::LDM, kt * 16 + ln, kb * 32);  // rows of M^T
+#pragma unroll
+            for (int kt = 0; kt < K / 16; ++kt) mma(nx[kt], fa[kt], sf[kb]);
         }
 #pragma unroll
         for (int kt = 0; kt < K / 16; ++kt) accS[kt] = nx[kt];
         store_state<K>(accS, a.seginit + ((size_t)(segoff + dst) * H + h) * VK, row);
+    };
+    for (int step = 0; step < nsteps; step += 2) {
+        one(mA, rA, step);
+        if (step + 1 < nsteps) one(mB, rB, step + 1);
     }
 }
 
