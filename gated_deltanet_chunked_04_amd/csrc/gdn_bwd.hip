@@ -688,24 +688,28 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(BwdChunkArgs a) {
             for (int kb = 0; kb < K / 32; ++kb) frag_row(qr[kb], sQ, C::LDK, r, kb * 32);
 #pragma unroll
             for (int vb = 0; vb < V / 32; ++vb) frag_row(dor[vb], sD, C::LDV, r, vb * 32);
+            // all four j tiles (the mask below zeroes j > r): one straight block of
+            // independent products instead of a branch per tile
 #pragma unroll
             for (int jt = 0; jt < 4; ++jt) {
                 dPT[jt] = zero4();
                 PmQ[jt] = zero4();
-                if (jt <= wave) {
+            }
 #pragma unroll
-                    for (int vb = 0; vb < V / 32; ++vb) {
-                        Frag<T> fd;
-                        frag_row(fd, sDl, C::LDV, jt * 16 + ln, vb * 32);
-                        mma(dPT[jt], fd, dor[vb]);
-                    }
+            for (int vb = 0; vb < V / 32; ++vb) {
+                Frag<T> fd[4];
 #pragma unroll
-                    for (int kb = 0; kb < K / 32; ++kb) {
-                        Frag<T> fk;
-                        frag_row(fk, sK, C::LDK, jt * 16 + ln, kb * 32);
-                        mma(PmQ[jt], fk, qr[kb]);
-                    }
-                }
+                for (int jt = 0; jt < 4; ++jt) frag_row(fd[jt], sDl, C::LDV, jt * 16 + ln, vb * 32);
+#pragma unroll
+                for (int jt = 0; jt < 4; ++jt) mma(dPT[jt], fd[jt], dor[vb]);
+            }
+#pragma unroll
+            for (int kb = 0; kb < K / 32; ++kb) {
+                Frag<T> fk[4];
+#pragma unroll
+                for (int jt = 0; jt < 4; ++jt) frag_row(fk[jt], sK, C::LDK, jt * 16 + ln, kb * 32);
+#pragma unroll
+                for (int jt = 0; jt < 4; ++jt) mma(PmQ[jt], fk[jt], qr[kb]);
             }
         }
         // ---- dKt^T[k][r] = sum_v G[v][k] Delta[r][v]  (rows k, cols r) -------------------------
@@ -715,14 +719,14 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(BwdChunkArgs a) {
 #pragma unroll
             for (int vb = 0; vb < V / 32; ++vb) frag_row(dtr[vb], sDl, C::LDV, r, vb * 32);
 #pragma unroll
-            for (int kt = 0; kt < K / 16; ++kt) {
-                dKT[kt] = zero4();
+            for (int kt = 0; kt < K / 16; ++kt) dKT[kt] = zero4();
 #pragma unroll
-                for (int vb = 0; vb < V / 32; ++vb) {
-                    Frag<T> fg;
-                    frag_col(fg, sG, C::LDK, kt * 16 + ln, vb * 32);  // G^T row k, slots v
-                    mma(dKT[kt], fg, dtr[vb]);
-                }
+            for (int vb = 0; vb < V / 32; ++vb) {
+                Frag<T> fg[K / 16];
+#pragma unroll
+                for (int kt = 0; kt < K / 16; ++kt) frag_col(fg[kt], sG, C::LDK, kt * 16 + ln, vb * 32);  // G^T row k, slots v
+#pragma unroll
+                for (int kt = 0; kt < K / 16; ++kt) mma(dKT[kt], fg[kt], dtr[vb]);
             }
         }
         // mask, decay, the P terms of d(gam), and L .* dP
@@ -885,27 +889,37 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(BwdChunkArgs a) {
             for (int kb = 0; kb < K / 32; ++kb) frag_row(wf[kb], sdW, C::LDK, ra, kb * 32);
 #pragma unroll
             for (int vb = 0; vb < V / 32; ++vb) frag_row(uf[vb], sdU, C::LDV, ra, vb * 32);
+            // all four b tiles (the mask below zeroes b >= a)
+            f32x4 x[4], y[4];
 #pragma unroll
             for (int bt = 0; bt < 4; ++bt) {
-                f32x4 x = zero4(), y = zero4();
-                if (bt <= wave) {
+                x[bt] = zero4();
+                y[bt] = zero4();
+            }
 #pragma unroll
-                    for (int kb = 0; kb < K / 32; ++kb) {
-                        Frag<T> fk;
-                        frag_row(fk, sK, C::LDK, bt * 16 + ln, kb * 32);
-                        mma(x, fk, wf[kb]);  // rows b, cols a: (K dW^T)[b][a]
-                    }
+            for (int kb = 0; kb < K / 32; ++kb) {
+                Frag<T> fk[4];
 #pragma unroll
-                    for (int vb = 0; vb < V / 32; ++vb) {
-                        Frag<T> fv;
-                        frag_row(fv, sV, C::LDV, bt * 16 + ln, vb * 32);
-                        mma(y, fv, uf[vb]);
-                    }
-                }
+                for (int bt = 0; bt < 4; ++bt) frag_row(fk[bt], sK, C::LDK, bt * 16 + ln, kb * 32);
+#pragma unroll
+                for (int bt = 0; bt < 4; ++bt) mma(x[bt], fk[bt], wf[kb]);  // rows b, cols a: (K dW^T)[b][a]
+            }
+#pragma unroll
+            for (int vb = 0; vb < V / 32; ++vb) {
+                Frag<T> fv[4];
+#pragma unroll
+                for (int bt = 0; bt < 4; ++bt) frag_row(fv[bt], sV, C::LDV, bt * 16 + ln, vb * 32);
+#pragma unroll
+                for (int bt = 0; bt < 4; ++bt) mma(y[bt], fv[bt], uf[vb]);
+            }
+#pragma unroll
+            for (int bt = 0; bt < 4; ++bt) {
+                const f32x4 gb = *reinterpret_cast<const f32x4*>(sGam + bt * 16 + gq * 4);
+                const f32x4 bb = *reinterpret_cast<const f32x4*>(sBeta + bt * 16 + gq * 4);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int b = bt * 16 + gq * 4 + e;
-                    dT[bt][e] = (b < ra) ? sBeta[b] * (fast_exp(sGam[b]) * x[e] + y[e]) : 0.f;
+                    dT[bt][e] = (b < ra) ? bb[e] * (fast_exp(gb[e]) * x[bt][e] + y[bt][e]) : 0.f;
                 }
             }
             frag_acc(dtf[0], dT[0], dT[1]);
@@ -913,18 +927,20 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(BwdChunkArgs a) {
         }
         bwd_fetch<1>(R, a, nxt);
         // ---- Y = dT T^T: tiles Y^T[c][a] = sum_b T[c][b] dT[a][b] (T[c][b] = 0 for b > c) -----
+        {
+            f32x4 y[4];
 #pragma unroll
-        for (int ct = 0; ct < 4; ++ct) {
-            f32x4 y = zero4();
+            for (int ct = 0; ct < 4; ++ct) y[ct] = zero4();
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
-                if (kb == 0 || ct >= 2) {
-                    Frag<T> ft;
-                    frag_row(ft, sTm, C::LDX, ct * 16 + ln, kb * 32);
-                    mma(y, ft, dtf[kb]);
-                }
+                Frag<T> ft[4];
+#pragma unroll
+                for (int ct = 0; ct < 4; ++ct) frag_row(ft[ct], sTm, C::LDX, ct * 16 + ln, kb * 32);
+#pragma unroll
+                for (int ct = 0; ct < 4; ++ct) mma(y[ct], ft[ct], dtf[kb]);
             }
-            store4(sY + ra * C::LDX + ct * 16 + gq * 4, y);  // Y[a][c]
+#pragma unroll
+            for (int ct = 0; ct < 4; ++ct) store4(sY + ra * C::LDX + ct * 16 + gq * 4, y[ct]);  // Y[a][c]
         }
         lds_sync();
         bwd_fetch<2>(R, a, nxt);
@@ -939,25 +955,32 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(BwdChunkArgs a) {
 #pragma unroll
             for (int kb = 0; kb < K / 32; ++kb) frag_row(kra[kb], sK, C::LDK, ra, kb * 32);
             const float ba = sBeta[ra], ga = sGam[ra];
+            // all four c tiles (the mask below zeroes c >= a)
+            f32x4 dd[4], kkk[4];
 #pragma unroll
             for (int ct = 0; ct < 4; ++ct) {
-                f32x4 d = zero4(), kk = zero4();
-                if (ct <= wave) {
+                dd[ct] = zero4();
+                kkk[ct] = zero4();
+            }
 #pragma unroll
-                    for (int kb = 0; kb < 2; ++kb) {
-                        if (kb == 1 || wave < 2) {
-                            Frag<T> fy;
-                            frag_col(fy, sY, C::LDX, ct * 16 + ln, kb * 32);  // Y^T row c, slots x
-                            mma(d, fy, ta[kb]);  // rows c, cols a: (T^T Y)^T
-                        }
-                    }
+            for (int kb = 0; kb < 2; ++kb) {
+                Frag<T> fy[4];
 #pragma unroll
-                    for (int kb = 0; kb < K / 32; ++kb) {
-                        Frag<T> fk;
-                        frag_row(fk, sK, C::LDK, ct * 16 + ln, kb * 32);
-                        mma(kk, fk, kra[kb]);  // rows c, cols a: k_c . k_a
-                    }
-                }
+                for (int ct = 0; ct < 4; ++ct) frag_col(fy[ct], sY, C::LDX, ct * 16 + ln, kb * 32);  // Y^T row c, slots x
+#pragma unroll
+                for (int ct = 0; ct < 4; ++ct) mma(dd[ct], fy[ct], ta[kb]);  // rows c, cols a: (T^T Y)^T
+            }
+#pragma unroll
+            for (int kb = 0; kb < K / 32; ++kb) {
+                Frag<T> fk[4];
+#pragma unroll
+                for (int ct = 0; ct < 4; ++ct) frag_row(fk[ct], sK, C::LDK, ct * 16 + ln, kb * 32);
+#pragma unroll
+                for (int ct = 0; ct < 4; ++ct) mma(kkk[ct], fk[ct], kra[kb]);  // rows c, cols a: k_c . k_a
+            }
+#pragma unroll
+            for (int ct = 0; ct < 4; ++ct) {
+                const f32x4 d = dd[ct], kk = kkk[ct];
                 f32x4 colpart, mx;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {

@@ -279,18 +279,20 @@ __device__ __forceinline__ void tri_inverse64(float* sA, float* sT) {
     const int wave = wave_id();
     const int lane = tid & 63;
     const int ln = lane & 15, gq = lane >> 4;
-    // 3a: diagonal blocks by forward substitution (wave b, lanes 0..15 = columns of block b)
+    // 3a: diagonal blocks by forward substitution (wave b, lanes 0..15 = columns of block b),
+    // column-oriented: once x_j is final it updates every later row, so the dependent chain
+    // is 15 fused multiply-adds long instead of one per product
     if (gq == 0) {
         const int b = wave;
         const int col = ln;
+        const float* ablk = sA + (16 * b) * kLdA + 16 * b;
         float x[16];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            float s = (r == col) ? 1.f : 0.f;
-            const float* arow = sA + (16 * b + r) * kLdA + 16 * b;
+        for (int r = 0; r < 16; ++r) x[r] = (r == col) ? 1.f : 0.f;
 #pragma unroll
-            for (int j = 0; j < r; ++j) s -= arow[j] * x[j];
-            x[r] = s;
+        for (int j = 0; j < 15; ++j) {
+#pragma unroll
+            for (int r = j + 1; r < 16; ++r) x[r] -= ablk[r * kLdA + j] * x[j];
         }
 #pragma unroll
         for (int r = 0; r < 16; ++r) sT[(16 * b + r) * kLdA + 16 * b + col] = x[r];

@@ -133,24 +133,48 @@ __global__ __launch_bounds__(kThreads) void k_intra(IntraArgs args) {
         lds_sync();
 
         // ---- stage 2: A = strict_lower(diag(beta) (D .* K K^T)) -----------------------
-        for (int idx = wave; idx < 10; idx += 4) {
-            const int ti = tri_row(idx), tj = tri_col(idx);
-            f32x4 acc = zero4();
+        // this wave's lower tiles (wave, wave + 4, wave + 8), their k32 products side by side
+        {
+            constexpr int NTT = 3;
+            f32x4 acc[NTT];
+            int ti[NTT], tj[NTT];
+            bool on[NTT];
+            // (waves with two tiles recompute the last one instead of branching; only the
+            // stores are skipped, so the products form one straight block)
+#pragma unroll
+            for (int m = 0; m < NTT; ++m) {
+                const int idx = wave + 4 * m;
+                on[m] = idx < 10;
+                ti[m] = tri_row(min(idx, 9));
+                tj[m] = tri_col(min(idx, 9));
+                acc[m] = zero4();
+            }
 #pragma unroll
             for (int kb = 0; kb < K / 32; ++kb) {
-                Frag<T> a, b;
-                frag_row(a, sK, S::LDK, ti * 16 + ln, kb * 32);
-                frag_row(b, sK, S::LDK, tj * 16 + ln, kb * 32);
-                mma(acc, a, b);
-            }
-            const int j = tj * 16 + ln;
-            const float gj = sGam[j];
+                Frag<T> fa[NTT], fb[NTT];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = ti * 16 + gq * 4 + i;
-                const float val = (j < r) ? sBeta[r] * fast_exp(sGam[r] - gj) * acc[i] : 0.f;
-                sA[r * kLdA + j] = val;
-                if (r == j) sKK[r] = sBeta[r] * acc[i];
+                for (int m = 0; m < NTT; ++m) {
+                    frag_row(fa[m], sK, S::LDK, ti[m] * 16 + ln, kb * 32);
+                    frag_row(fb[m], sK, S::LDK, tj[m] * 16 + ln, kb * 32);
+                }
+#pragma unroll
+                for (int m = 0; m < NTT; ++m) mma(acc[m], fa[m], fb[m]);
+            }
+#pragma unroll
+            for (int m = 0; m < NTT; ++m) {
+                if (on[m]) {
+                    const int j = tj[m] * 16 + ln;
+                    const float gj = sGam[j];
+                    const f32x4 gr = *reinterpret_cast<const f32x4*>(sGam + ti[m] * 16 + gq * 4);
+                    const f32x4 br = *reinterpret_cast<const f32x4*>(sBeta + ti[m] * 16 + gq * 4);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int r = ti[m] * 16 + gq * 4 + i;
+                        const float val = (j < r) ? br[i] * fast_exp(gr[i] - gj) * acc[m][i] : 0.f;
+                        sA[r * kLdA + j] = val;
+                        if (r == j) sKK[r] = br[i] * acc[m][i];
+                    }
+                }
             }
         }
         lds_sync();
