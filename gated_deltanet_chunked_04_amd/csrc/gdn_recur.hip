@@ -734,15 +734,14 @@ hipError_t launch_decide(const DecideArgs& a, hipStream_t st) {
 hipError_t launch_scan(const ScanArgs& a, int dtype, hipStream_t st) {
     if (a.geo.N == 0) return hipSuccess;
     const int K = a.geo.K;
-    const int RT = recur_rows(a.geo.V, K);
+    // 64 state rows per workgroup whatever the recurrence uses: the scan is a serial chain
+    // per sequence-head, and more workgroups per head shorten each link
     if (dtype == 0) {
-        if (K == 64 && RT == 64) return launch_scan_t<bf16_t, 64, 64>(a, st);
-        if (K == 128 && RT == 64) return launch_scan_t<bf16_t, 128, 64>(a, st);
-        if (K == 128 && RT == 128) return launch_scan_t<bf16_t, 128, 128>(a, st);
+        if (K == 64) return launch_scan_t<bf16_t, 64, 64>(a, st);
+        if (K == 128) return launch_scan_t<bf16_t, 128, 64>(a, st);
     } else {
-        if (K == 64 && RT == 64) return launch_scan_t<float, 64, 64>(a, st);
-        if (K == 128 && RT == 64) return launch_scan_t<float, 128, 64>(a, st);
-        if (K == 128 && RT == 128) return launch_scan_t<float, 128, 128>(a, st);
+        if (K == 64) return launch_scan_t<float, 64, 64>(a, st);
+        if (K == 128) return launch_scan_t<float, 128, 64>(a, st);
     }
     return hipErrorInvalidValue;
 }
