@@ -12,7 +12,10 @@ gradients are dO ~ N(0,1) (bf16) and d(final state) ~ N(0,0.1).
 Prints one JSON line: tokens/s of the step (and of the forward and backward
 timed alone), TFLOP/s on algorithmic flops, the roofline fraction of the
 step's dominant kernel (algorithmic bytes over its HIP-event-timed launch
-duration) and the CPU oracle timed on this host's cores.
+duration) and the CPU oracle timed on this host's cores. The headline step
+recomputes the forward's intra-chunk results in the backward; "keep_forward"
+reports the opt-in variant whose backward starts from the forward's kept
+workspace instead (more memory held between the passes, less backward work).
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--pass both|fwd|bwd]
                   [--no-cpu-baseline]
@@ -207,6 +210,14 @@ def main():
         if do_bwd:
             bwd()
 
+    def step_keep():
+        # the opt-in variant: the forward keeps W, U, T, the gate cumsum and the CP entry
+        # states in the workspace (which covers both layouts) and the backward starts from them
+        gdn.gdn_chunk_fwd(q, k, v, g, beta, s0, cu_seqlens=cu, cu_seqlens_host=cu_host, cp_mode=cp,
+                          workspace=ws, o=o, final_state=sT, keep_for_backward=True)
+        gdn.gdn_chunk_bwd(q, k, v, g, beta, dev["d_o"], s0, dev["d_final_state"], cu_seqlens=cu,
+                          cu_seqlens_host=cu_host, cp_mode=cp, workspace=ws, out=grads, reuse_forward=True)
+
     def timed(fn, n):
         torch.cuda.synchronize()
         t0 = time.perf_counter()
@@ -230,6 +241,10 @@ def main():
     ms = timed(step, args.steps)
     ms_fwd = timed(fwd, args.steps) if do_fwd else None
     ms_bwd = timed(bwd, args.steps) if do_bwd else None
+    ms_keep = None
+    if do_fwd and do_bwd:
+        step_keep()
+        ms_keep = timed(step_keep, args.steps)
 
     # Per-kernel durations: one more round of steps with every launch bracketed by HIP
     # events on the launch stream (separate from the timed loops above).
@@ -284,6 +299,9 @@ def main():
     if do_bwd:
         line["bwd"] = {"ms": round(ms_bwd, 4), "tokens_per_s": round(tokens / (ms_bwd * 1e-3), 1),
                        "tflops": round(counts["flops"]["bwd"] / (ms_bwd * 1e-3) / 1e12, 2)}
+    if ms_keep is not None:
+        line["keep_forward"] = {"ms_per_step": round(ms_keep, 4),
+                                "tokens_per_s": round(tokens / (ms_keep * 1e-3), 1)}
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(inp, tokens, args.passes)
     print(json.dumps(line), flush=True)

@@ -8,6 +8,8 @@ missing they raise instead of computing anything elsewhere.
   gdn_plan(...)               host-side plan (AutoCP decision, sub-sequence length, workspace)
   gdn_chunk_fwd(...)          O and the final state
   gdn_chunk_bwd(...)          gradients of <dO, O> + <dS_T, S_T>
+  gdn_workspace(...)          one buffer that serves a forward that keeps its intermediates
+                              and the backward that reuses them
   gdn_intra_chunk(...)        the intra-chunk kernel alone (gate cumsum, w, u)
   gdn_cp_modes(...)           per sequence-head CP decision (0 none, 1 warmup, 2 exact)
   chunk_gated_delta_rule(...) autograd wrapper over gdn_chunk_fwd / gdn_chunk_bwd
@@ -20,10 +22,11 @@ from typing import Optional
 import numpy as np
 import torch
 
-from ._abi import (CP_MODES, EXPORTS, GDN_DTYPE_BF16, GDN_DTYPE_FP32, GdnDesc, GdnError,  # noqa: F401
-                   GdnKernelTime, GdnPlanInfo, check, load_library, status_string)
+from ._abi import (CP_MODES, EXPORTS, GDN_DTYPE_BF16, GDN_DTYPE_FP32, GDN_FLAG_KEEP_FORWARD,  # noqa: F401
+                   GDN_FLAG_REUSE_FORWARD, GdnDesc, GdnError, GdnKernelTime, GdnPlanInfo, check,
+                   load_library, status_string)
 
-__all__ = ["gdn_plan", "gdn_chunk_fwd", "gdn_chunk_bwd", "gdn_intra_chunk", "gdn_cp_modes",
+__all__ = ["gdn_plan", "gdn_chunk_fwd", "gdn_chunk_bwd", "gdn_workspace", "gdn_intra_chunk", "gdn_cp_modes",
            "gdn_profile_enable", "gdn_profile_read", "chunk_gated_delta_rule", "load_library",
            "make_desc", "GdnError"]
 
@@ -40,7 +43,7 @@ class Desc:
     """A gdn_desc plus the host objects its pointers refer to."""
 
     def __init__(self, B, T, H, K, V, dtype, *, scale=1.0, cu_seqlens=None, cu_seqlens_host=None,
-                 cp_mode="auto", warmup_chunks=0, seg_chunks=0, warmup_eps=0.0, num_cus=0):
+                 cp_mode="auto", warmup_chunks=0, seg_chunks=0, warmup_eps=0.0, num_cus=0, flags=0):
         d = GdnDesc()
         d.B, d.T, d.H, d.K, d.V = int(B), int(T), int(H), int(K), int(V)
         d.chunk = 64
@@ -71,6 +74,7 @@ class Desc:
         d.seg_chunks = int(seg_chunks)
         d.warmup_eps = float(warmup_eps)
         d.num_cus = int(num_cus)
+        d.flags = int(flags)
         self.c = d
 
     @property
@@ -87,6 +91,22 @@ def gdn_plan(desc: Desc) -> dict:
     info = GdnPlanInfo()
     check(load_library().gdn_plan(desc.ref, ctypes.byref(info)), "gdn_plan")
     return {f: getattr(info, f) for f, _ in GdnPlanInfo._fields_}
+
+
+def gdn_workspace(q, v, *, cu_seqlens=None, cu_seqlens_host=None, cp_mode="auto", warmup_chunks=0,
+                  seg_chunks=0, warmup_eps=0.0):
+    """A workspace large enough for gdn_chunk_fwd(keep_for_backward=True) and for
+    gdn_chunk_bwd(reuse_forward=True) with the same shapes and options."""
+    kw = dict(cu_seqlens=cu_seqlens, cu_seqlens_host=cu_seqlens_host, cp_mode=cp_mode,
+              warmup_chunks=warmup_chunks, seg_chunks=seg_chunks, warmup_eps=warmup_eps)
+    lib = load_library()
+    f, b = ctypes.c_size_t(), ctypes.c_size_t()
+    # the descriptors stay referenced through the calls: they own the host copy of cu_seqlens
+    dk = make_desc(q, v, flags=GDN_FLAG_KEEP_FORWARD, **kw)
+    dr = make_desc(q, v, flags=GDN_FLAG_REUSE_FORWARD, **kw)
+    check(lib.gdn_chunk_fwd_workspace_size(dk.ref, ctypes.byref(f)), "gdn_chunk_fwd_workspace_size")
+    check(lib.gdn_chunk_bwd_workspace_size(dr.ref, ctypes.byref(b)), "gdn_chunk_bwd_workspace_size")
+    return torch.empty(max(f.value, b.value, 256), dtype=torch.uint8, device=q.device)
 
 
 def _workspace(nbytes: int, device, workspace=None):
@@ -123,13 +143,21 @@ def _num_seqs(q, cu_seqlens):
 
 def gdn_chunk_fwd(q, k, v, g, beta, initial_state=None, *, scale=1.0, cu_seqlens=None,
                   cu_seqlens_host=None, output_final_state=True, cp_mode="auto", warmup_chunks=0,
-                  seg_chunks=0, warmup_eps=0.0, workspace=None, o=None, final_state=None):
-    """Forward. Returns (o, final_state or None). Runs on the current stream."""
+                  seg_chunks=0, warmup_eps=0.0, workspace=None, o=None, final_state=None,
+                  keep_for_backward=False):
+    """Forward. Returns (o, final_state or None). Runs on the current stream.
+
+    keep_for_backward=True leaves the intra-chunk results (gate cumsum, W, U, T), the CP
+    decisions and the sub-sequence entry states in `workspace` (required; see gdn_workspace),
+    so that gdn_chunk_bwd(reuse_forward=True) on the same inputs and options skips recomputing them.
+    """
     N = _num_seqs(q, cu_seqlens)
     _check_inputs(q, k, v, g, beta, initial_state, N)
+    if keep_for_backward and workspace is None:
+        raise ValueError("keep_for_backward needs a caller-owned workspace (gdn_workspace)")
     desc = make_desc(q, v, scale=scale, cu_seqlens=cu_seqlens, cu_seqlens_host=cu_seqlens_host,
                      cp_mode=cp_mode, warmup_chunks=warmup_chunks, seg_chunks=seg_chunks,
-                     warmup_eps=warmup_eps)
+                     warmup_eps=warmup_eps, flags=GDN_FLAG_KEEP_FORWARD if keep_for_backward else 0)
     lib = load_library()
     nbytes = ctypes.c_size_t()
     check(lib.gdn_chunk_fwd_workspace_size(desc.ref, ctypes.byref(nbytes)), "gdn_chunk_fwd_workspace_size")
@@ -150,8 +178,13 @@ def gdn_chunk_fwd(q, k, v, g, beta, initial_state=None, *, scale=1.0, cu_seqlens
 
 def gdn_chunk_bwd(q, k, v, g, beta, d_o, initial_state=None, d_final_state=None, *, scale=1.0,
                   cu_seqlens=None, cu_seqlens_host=None, cp_mode="auto", warmup_chunks=0, seg_chunks=0,
-                  warmup_eps=0.0, workspace=None, need_d_initial_state=True, out=None):
-    """Backward. Returns dict(dq, dk, dv, dg, dbeta, d_initial_state); `out` may hold them preallocated."""
+                  warmup_eps=0.0, workspace=None, need_d_initial_state=True, out=None,
+                  reuse_forward=False):
+    """Backward. Returns dict(dq, dk, dv, dg, dbeta, d_initial_state); `out` may hold them preallocated.
+
+    reuse_forward=True takes the forward's intermediates from `workspace`, which must be the buffer a
+    gdn_chunk_fwd(keep_for_backward=True) call on the same inputs and options wrote, untouched since.
+    """
     N = _num_seqs(q, cu_seqlens)
     _check_inputs(q, k, v, g, beta, initial_state, N)
     B, T, H, K = q.shape
@@ -162,9 +195,11 @@ def gdn_chunk_bwd(q, k, v, g, beta, d_o, initial_state=None, d_final_state=None,
                                       or d_final_state.dtype != torch.float32
                                       or not d_final_state.is_contiguous()):
         raise ValueError("d_final_state must be contiguous fp32 [N,H,V,K]")
+    if reuse_forward and workspace is None:
+        raise ValueError("reuse_forward needs the forward's workspace")
     desc = make_desc(q, v, scale=scale, cu_seqlens=cu_seqlens, cu_seqlens_host=cu_seqlens_host,
                      cp_mode=cp_mode, warmup_chunks=warmup_chunks, seg_chunks=seg_chunks,
-                     warmup_eps=warmup_eps)
+                     warmup_eps=warmup_eps, flags=GDN_FLAG_REUSE_FORWARD if reuse_forward else 0)
     lib = load_library()
     nbytes = ctypes.c_size_t()
     check(lib.gdn_chunk_bwd_workspace_size(desc.ref, ctypes.byref(nbytes)), "gdn_chunk_bwd_workspace_size")
@@ -230,29 +265,39 @@ def gdn_profile_read() -> dict:
 
 class _GDNFunction(torch.autograd.Function):
     @staticmethod
-    def forward(ctx, q, k, v, g, beta, initial_state, scale, cu_seqlens, cp_mode):
+    def forward(ctx, q, k, v, g, beta, initial_state, scale, cu_seqlens, cp_mode, keep):
+        ws = gdn_workspace(q, v, cu_seqlens=cu_seqlens, cp_mode=cp_mode) if keep else None
         o, sT = gdn_chunk_fwd(q, k, v, g, beta, initial_state, scale=scale, cu_seqlens=cu_seqlens,
-                              cp_mode=cp_mode)
+                              cp_mode=cp_mode, workspace=ws, keep_for_backward=keep)
         ctx.save_for_backward(q, k, v, g, beta, initial_state, cu_seqlens)
         ctx.scale = scale
         ctx.cp_mode = cp_mode
+        ctx.ws = ws
         return o, sT
 
     @staticmethod
     def backward(ctx, d_o, d_sT):
         q, k, v, g, beta, s0, cu = ctx.saved_tensors
+        ws, ctx.ws = ctx.ws, None
         gr = gdn_chunk_bwd(q, k, v, g, beta, d_o.contiguous(), s0,
                            None if d_sT is None else d_sT.contiguous(), scale=ctx.scale,
-                           cu_seqlens=cu, cp_mode=ctx.cp_mode, need_d_initial_state=s0 is not None)
-        return (gr["dq"], gr["dk"], gr["dv"], gr["dg"], gr["dbeta"], gr["d_initial_state"], None, None, None)
+                           cu_seqlens=cu, cp_mode=ctx.cp_mode, need_d_initial_state=s0 is not None,
+                           workspace=ws, reuse_forward=ws is not None)
+        return (gr["dq"], gr["dk"], gr["dv"], gr["dg"], gr["dbeta"], gr["d_initial_state"],
+                None, None, None, None)
 
 
 def chunk_gated_delta_rule(q, k, v, g, beta, scale: float = 1.0, initial_state=None,
-                           output_final_state: bool = True, cu_seqlens=None, cp_mode: str = "auto"):
+                           output_final_state: bool = True, cu_seqlens=None, cp_mode: str = "auto",
+                           keep_intermediates: bool = False):
     """High-level call: (o, final_state) with autograd through gdn_chunk_bwd.
 
     q, k: [B,T,H,K]; v: [B,T,H,V] (bf16 or fp32); g (natural-log decay) and beta: [B,T,H] fp32;
     initial_state: [N,H,V,K] fp32 or None; cu_seqlens: int32 [N+1] device tensor (B must be 1).
+    keep_intermediates=True holds the forward's workspace (W, U, T, gate cumsum, CP entry states)
+    until the backward, which then skips recomputing them: more memory, less backward time.
     """
-    o, sT = _GDNFunction.apply(q, k, v, g, beta, initial_state, scale, cu_seqlens, cp_mode)
+    o, sT = _GDNFunction.apply(q, k, v, g, beta, initial_state, scale, cu_seqlens, cp_mode,
+                               bool(keep_intermediates and torch.is_grad_enabled()
+                                    and any(x.requires_grad for x in (q, k, v, g, beta))))
     return (o, sT) if output_final_state else (o, None)

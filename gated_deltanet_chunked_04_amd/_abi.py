@@ -15,6 +15,8 @@ LIB_PATH = os.path.join(HERE, "libgdn.so")
 GDN_OK, GDN_ERR_INVALID_ARG, GDN_ERR_UNSUPPORTED, GDN_ERR_WORKSPACE, GDN_ERR_HIP = range(5)
 GDN_DTYPE_BF16, GDN_DTYPE_FP32 = 0, 1
 CP_MODES = {"auto": 0, "off": 1, "on": 2, "exact": 3, "warmup": 4}
+GDN_FLAG_KEEP_FORWARD, GDN_FLAG_REUSE_FORWARD = 1, 2
+GDN_ABI_VERSION = 2
 
 # Declared entry points of include/gdn.h (checked by the ABI test).
 EXPORTS = ("gdn_abi_version", "gdn_status_string", "gdn_plan", "gdn_chunk_fwd_workspace_size",
@@ -31,7 +33,7 @@ class GdnDesc(ctypes.Structure):
         ("cu_seqlens", ctypes.c_void_p), ("cu_seqlens_host", ctypes.c_void_p),
         ("cp_mode", ctypes.c_int32), ("warmup_chunks", ctypes.c_int32),
         ("seg_chunks", ctypes.c_int32), ("warmup_eps", ctypes.c_float),
-        ("num_cus", ctypes.c_int32), ("reserved", ctypes.c_int32 * 7),
+        ("num_cus", ctypes.c_int32), ("flags", ctypes.c_int32), ("reserved", ctypes.c_int32 * 6),
     ]
 
 
@@ -90,6 +92,8 @@ def load_library(path: str = LIB_PATH):
     lib.gdn_profile_enable.argtypes = [i32]
     lib.gdn_profile_read.restype = i32
     lib.gdn_profile_read.argtypes = [ctypes.POINTER(GdnKernelTime), i32]
+    if lib.gdn_abi_version() != GDN_ABI_VERSION:
+        raise RuntimeError(f"libgdn.so ABI version {lib.gdn_abi_version()} != {GDN_ABI_VERSION}: rebuild it")
     _LIB = lib
     return lib
 

@@ -60,8 +60,9 @@ int query_cus() {
 
 gdn_status make_plan(const gdn_desc* d, Plan& p) {
     if (!d) return GDN_ERR_INVALID_ARG;
-    for (int i = 0; i < 7; ++i)
+    for (int i = 0; i < 6; ++i)
         if (d->reserved[i] != 0) return GDN_ERR_INVALID_ARG;
+    if (d->flags & ~(GDN_FLAG_KEEP_FORWARD | GDN_FLAG_REUSE_FORWARD)) return GDN_ERR_INVALID_ARG;
     if (d->B < 1 || d->T < 0 || d->H < 1 || d->K < 1 || d->V < 1) return GDN_ERR_INVALID_ARG;
     if (!(d->chunk == 0 || d->chunk == 64)) return GDN_ERR_UNSUPPORTED;
     if (!(d->K == 64 || d->K == 128) || !(d->V == 64 || d->V == 128)) return GDN_ERR_UNSUPPORTED;
@@ -171,7 +172,10 @@ gdn_status make_plan(const gdn_desc* d, Plan& p) {
         p.o_seginit = take((size_t)p.total_segs * H * V * K * 4);
         p.o_prep = take((size_t)p.total_segs * H * (V + K) * K * 4);
     }
-    p.fwd_bytes = std::max<size_t>(off, kAlign);
+    // T = (I + A)^{-1} per chunk: written by the forward when it keeps its intermediates,
+    // always by the backward (which reads it); the same offset in both layouts
+    p.o_tm = take((size_t)p.total_chunks * H * 64 * 64 * p.esize);
+    p.fwd_bytes = std::max<size_t>((d->flags & GDN_FLAG_KEEP_FORWARD) ? off : p.o_tm, kAlign);
     // backward workspace continues after the forward's
     if (p.cp_on) {
         p.o_modes_r = take((size_t)p.N * H * 4);
@@ -180,7 +184,6 @@ gdn_status make_plan(const gdn_desc* d, Plan& p) {
     }
     p.o_h = take((size_t)p.total_chunks * H * V * K * p.esize);
     p.o_gst = take((size_t)p.total_chunks * H * V * K * p.esize);
-    p.o_tm = take((size_t)p.total_chunks * H * 64 * 64 * p.esize);
     p.o_dl = take(T * H * V * p.esize);
     p.o_ddl = take(T * H * V * p.esize);
     p.bwd_bytes = std::max<size_t>(off, kAlign);
@@ -401,7 +404,10 @@ gdn_status gdn_chunk_fwd(const gdn_desc* desc, const void* q, const void* k, con
     float* gam = reinterpret_cast<float*>(ws + p.o_gam);
     void* w = ws + p.o_w;
     void* u = ws + p.o_u;
-    if ((s = run_intra(desc, p, ws, k, v, g, beta, gam, w, u, st)) != GDN_OK) return s;
+    // with GDN_FLAG_KEEP_FORWARD the intra pass also leaves T for the backward
+    if ((s = run_intra(desc, p, ws, k, v, g, beta, gam, w, u, st,
+                       (desc->flags & GDN_FLAG_KEEP_FORWARD) ? ws + p.o_tm : nullptr)) != GDN_OK)
+        return s;
 
     RecurArgs ra{};
     memset(&ra, 0, sizeof(ra));
@@ -468,8 +474,9 @@ gdn_status gdn_chunk_bwd(const gdn_desc* desc, const void* q, const void* k, con
     float* gam = reinterpret_cast<float*>(ws + p.o_gam);
     void* w = ws + p.o_w;
     void* u = ws + p.o_u;
-    // 1. recompute the gate cumsum and the WY factors
-    if ((s = run_intra(desc, p, ws, k, v, g, beta, gam, w, u, st, ws + p.o_tm)) != GDN_OK) return s;
+    // 1. the forward's intra-chunk pass (kept by a GDN_FLAG_KEEP_FORWARD forward, or recomputed)
+    const bool reuse = (desc->flags & GDN_FLAG_REUSE_FORWARD) != 0;
+    if (!reuse && (s = run_intra(desc, p, ws, k, v, g, beta, gam, w, u, st, ws + p.o_tm)) != GDN_OK) return s;
     const int rt = recur_rows((int)desc->V, (int)desc->K);
     const int vtiles = (int)(desc->V / rt);
     const int vktiles = (int)((desc->V + desc->K + rt - 1) / rt);
@@ -489,7 +496,10 @@ gdn_status gdn_chunk_bwd(const gdn_desc* desc, const void* q, const void* k, con
     ra.modes = modes;
     ra.hstates = ws + p.o_h;
     ra.delta = ws + p.o_dl;
-    if (p.cp_on) {
+    if (p.cp_on && reuse) {
+        // the forward's CP decisions and sub-sequence entry states
+        ra.seginit = reinterpret_cast<float*>(ws + p.o_seginit);
+    } else if (p.cp_on) {
         float* seginit = reinterpret_cast<float*>(ws + p.o_seginit);
         float* prep = reinterpret_cast<float*>(ws + p.o_prep);
         if ((s = run_decide(desc, p, ws, modes, st)) != GDN_OK) return s;

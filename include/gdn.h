@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 1
+#define GDN_ABI_VERSION 2
 
 typedef enum gdn_status {
     GDN_OK = 0,
@@ -80,6 +80,19 @@ typedef enum gdn_cp_mode {
     GDN_CP_WARMUP = 4  /* CP, warmup for every sequence-head (caller asserts fast decay) */
 } gdn_cp_mode;
 
+/* desc->flags: keeping the forward's intermediates for the backward of a training step.
+ * GDN_FLAG_KEEP_FORWARD    gdn_chunk_fwd leaves in its workspace what the backward
+ *                          recomputes otherwise: the chunk gate cumsums, w, u, T = (I+A)^-1,
+ *                          the CP decisions and the sub-sequence entry states (the
+ *                          forward workspace then includes room for T).
+ * GDN_FLAG_REUSE_FORWARD   gdn_chunk_bwd starts from them instead of recomputing the
+ *                          intra-chunk pass and the forward CP preprocessing. The caller
+ *                          guarantees that the same workspace last held a KEEP_FORWARD
+ *                          forward of the same inputs and descriptor (flags aside), with
+ *                          no other call on it since except REUSE_FORWARD backwards. */
+#define GDN_FLAG_KEEP_FORWARD 1
+#define GDN_FLAG_REUSE_FORWARD 2
+
 /* Problem descriptor. Zero-initialise, then fill. */
 typedef struct gdn_desc {
     int64_t B, T, H, K, V;          /* batch, tokens per row (packed total if varlen), heads, key dim, value dim */
@@ -94,7 +107,8 @@ typedef struct gdn_desc {
     int32_t seg_chunks;             /* CP sub-sequence length in chunks (0 = chosen from the CU count) */
     float warmup_eps;               /* warmup acceptance: exp(window gate sum) <= eps (0 = 1e-4 bf16, 1e-6 fp32) */
     int32_t num_cus;                /* compute units to plan for (0 = query the current device) */
-    int32_t reserved[7];            /* must be zero */
+    int32_t flags;                  /* GDN_FLAG_* (0 = none) */
+    int32_t reserved[6];            /* must be zero */
 } gdn_desc;
 
 /* Host-side plan of a call (filled by gdn_plan; no device work). */
@@ -135,6 +149,7 @@ gdn_status gdn_chunk_fwd_workspace_size(const gdn_desc* desc, size_t* bytes);
  *   o                : output [B,T,H,V]
  *   final_state      : output [N,H,V,K] fp32, or NULL (not written)
  *   workspace        : device scratch of at least gdn_chunk_fwd_workspace_size bytes, 256-byte aligned
+ *                      (with GDN_FLAG_KEEP_FORWARD, the one the backward will receive)
  *   stream           : hipStream_t (NULL = default stream)
  * Returns GDN_OK once all work is enqueued. */
 gdn_status gdn_chunk_fwd(const gdn_desc* desc, const void* q, const void* k, const void* v,
@@ -153,7 +168,8 @@ gdn_status gdn_chunk_bwd_workspace_size(const gdn_desc* desc, size_t* bytes);
  *   dq, dk, dv      : outputs, same layouts and dtype as q, k, v
  *   dg, dbeta       : outputs [B,T,H] fp32 (dg is with respect to the raw per-token g)
  *   d_initial_state : output [N,H,V,K] fp32, or NULL (not written)
- * The forward is recomputed inside; nothing from gdn_chunk_fwd is reused. */
+ * The forward is recomputed inside, unless desc->flags has GDN_FLAG_REUSE_FORWARD (then the
+ * intra-chunk pass and the forward CP preprocessing come from the workspace; see above). */
 gdn_status gdn_chunk_bwd(const gdn_desc* desc, const void* q, const void* k, const void* v,
                          const float* g, const float* beta, const float* initial_state,
                          const void* d_o, const float* d_final_state,

@@ -34,7 +34,7 @@ def test_exports_every_declared_symbol(lib):
     assert set(declared) == set(_abi.EXPORTS)
     for name in declared:
         assert hasattr(lib, name), name
-    assert lib.gdn_abi_version() == 1
+    assert lib.gdn_abi_version() == _abi.GDN_ABI_VERSION == 2
 
 
 def test_status_strings(lib):
@@ -122,6 +122,11 @@ def test_argument_errors(lib):
     d2 = desc()
     d2.c.reserved[3] = 1
     assert lib.gdn_plan(d2.ref, ctypes.byref(out)) == 1
+    # unknown flag bits
+    for bad_flag in (4, 8, 1 << 30, -1):
+        d2 = desc()
+        d2.c.flags = bad_flag
+        assert lib.gdn_plan(d2.ref, ctypes.byref(out)) == 1, bad_flag
     # varlen with B != 1, or without the host copy
     d2 = desc(B=2)
     d2.c.cu_seqlens = 0x1000
@@ -152,5 +157,28 @@ def test_call_errors_before_launch(lib):
     assert lib.gdn_chunk_fwd(d.ref, p, p, p, p, p, None, p, None, None, nb, None) == 3
     assert lib.gdn_chunk_fwd(d.ref, p, p, p, p, p, None, p, None, p, ctypes.c_size_t(nb.value - 1), None) == 3
     assert lib.gdn_chunk_fwd(d.ref, p, p, p, p, p, None, p, None, ctypes.c_void_p(0x1010), nb, None) == 3
+    # a forward that keeps its intermediates for the backward needs the larger workspace
+    keep = desc(T=256, H=2, flags=_abi.GDN_FLAG_KEEP_FORWARD)
+    assert lib.gdn_chunk_fwd(keep.ref, p, p, p, p, p, None, p, None, p, nb, None) == 3
     assert lib.gdn_intra_chunk(d.ref, p, p, p, p, None, p, p, p, nb, None) == 1
     assert lib.gdn_cp_modes(d.ref, p, p, p, p, None, p, nb, None) == 1
+
+
+@pytest.mark.parametrize("kw", [dict(), dict(B=1, H=64, T=4096), dict(T=1000, H=2, K=64, V=64, dtype=torch.float32)])
+def test_keep_forward_workspace(kw):
+    """A forward that keeps its intermediates needs more workspace (T per chunk, C x C in the
+    input dtype), laid out where the backward reads it; the backward's size does not depend on
+    the flags, and covers the kept forward's."""
+    base = plan(**kw)
+    keep = plan(flags=_abi.GDN_FLAG_KEEP_FORWARD, **kw)
+    reuse = plan(flags=_abi.GDN_FLAG_REUSE_FORWARD, **kw)
+    both = plan(flags=_abi.GDN_FLAG_KEEP_FORWARD | _abi.GDN_FLAG_REUSE_FORWARD, **kw)
+    H = kw.get("H", 16)
+    esize = 4 if kw.get("dtype") == torch.float32 else 2
+    tm = base["total_chunks"] * H * 64 * 64 * esize
+    assert keep["fwd_workspace_bytes"] >= base["fwd_workspace_bytes"] + tm
+    assert keep["fwd_workspace_bytes"] <= base["fwd_workspace_bytes"] + tm + 256
+    for p in (keep, reuse, both):
+        assert p["bwd_workspace_bytes"] == base["bwd_workspace_bytes"]
+        assert p["cp_on"] == base["cp_on"] and p["total_segments"] == base["total_segments"]
+    assert base["bwd_workspace_bytes"] >= keep["fwd_workspace_bytes"]

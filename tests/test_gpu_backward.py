@@ -139,3 +139,57 @@ def test_backward_workload_16k(gpu_lib, cp):
     ref = oracle_bwd(inp, heads=heads)
     errs = compare({n: out[n].cpu() for n in NAMES}, ref, 1e-2, heads=heads)
     print(f"cp={cp} " + " ".join(f"{n}={e:.2e}" for n, e in errs.items()), flush=True)
+
+
+REUSE_CASES = [
+    (torch.float32, 64, 64, "off", {}, None),
+    (torch.float32, 64, 64, "exact", dict(seg_chunks=3), None),
+    (torch.bfloat16, 128, 128, "exact", dict(seg_chunks=3), None),
+    (torch.bfloat16, 128, 128, "warmup", dict(seg_chunks=4, warmup_chunks=3), None),
+    (torch.bfloat16, 128, 128, "auto", {}, None),
+    (torch.bfloat16, 128, 128, "exact", dict(seg_chunks=2), [1, 63, 64, 65, 0, 700, 1500, 129]),
+    (torch.bfloat16, 64, 128, "off", {}, [300, 0, 1000]),
+]
+
+
+@pytest.mark.parametrize("dtype,K,V,cp,kw,lengths", REUSE_CASES)
+def test_backward_reuses_forward(gpu_lib, dtype, K, V, cp, kw, lengths):
+    """A backward that starts from a kept forward's workspace gives the recomputing backward's
+    gradients bit for bit (same kernels on the same inputs), and keeping changes no forward output."""
+    gdn = gpu_lib
+    if lengths is None:
+        inp = with_grads(small_inputs(B=2, T=1000, H=2, K=K, V=V, dtype=dtype, seed=15))
+    else:
+        inp = with_grads(small_inputs(H=3, K=K, V=V, dtype=dtype, lengths=lengths, seed=15))
+    d = to_dev(inp)
+    opts = dict(scale=0.8, cu_seqlens=d.get("cu_seqlens"), cp_mode=cp, **kw)
+    args = (d["q"], d["k"], d["v"], d["g"], d["beta"])
+    o0, s0 = gdn.gdn_chunk_fwd(*args, d["initial_state"], **opts)
+    ws = gdn.gdn_workspace(d["q"], d["v"], **{n: x for n, x in opts.items() if n != "scale"})
+    ws.fill_(0xA5)  # nothing the backward reads may come from outside what the forward wrote
+    o1, s1 = gdn.gdn_chunk_fwd(*args, d["initial_state"], workspace=ws, keep_for_backward=True, **opts)
+    assert torch.equal(o0, o1) and torch.equal(s0, s1)
+    ref = gdn.gdn_chunk_bwd(*args, d["d_o"], d["initial_state"], d["d_final_state"], **opts)
+    got = gdn.gdn_chunk_bwd(*args, d["d_o"], d["initial_state"], d["d_final_state"], workspace=ws,
+                            reuse_forward=True, **opts)
+    torch.cuda.synchronize()
+    for n in NAMES:
+        assert torch.equal(got[n], ref[n]), n
+    # and against the oracle
+    compare(got, oracle_bwd(inp, scale=0.8), tol_for(dtype))
+
+
+def test_autograd_wrapper_keep_intermediates(gpu_lib):
+    inp = with_grads(small_inputs(B=1, T=2000, H=3, K=128, V=128, dtype=torch.bfloat16, seed=16))
+    d = to_dev(inp)
+    grads = []
+    for keep in (False, True):
+        leaves = {n: d[n].clone().requires_grad_(True) for n in ("q", "k", "v", "g", "beta", "initial_state")}
+        o, sT = gpu_lib.chunk_gated_delta_rule(leaves["q"], leaves["k"], leaves["v"], leaves["g"],
+                                               leaves["beta"], initial_state=leaves["initial_state"],
+                                               cp_mode="exact", keep_intermediates=keep)
+        loss = (o.float() * d["d_o"].float()).sum() + (sT * d["d_final_state"]).sum()
+        loss.backward()
+        grads.append({n: x.grad for n, x in leaves.items()})
+    for n in grads[0]:
+        assert torch.equal(grads[0][n], grads[1][n]), n
