@@ -268,11 +268,11 @@ struct ProfScope {
         if (!p.on) return;
         a = p.get();
         b = p.get();
-        if (a && b) hipEventRecord(a, st);
+        if (a && b) (void)hipEventRecord(a, st);
     }
     ~ProfScope() {
         if (!a || !b) return;
-        hipEventRecord(b, st);
+        (void)hipEventRecord(b, st);
         Profiler& p = profiler();
         std::lock_guard<std::mutex> g(p.mu);
         p.pending.push_back(Pending{kid, a, b});
@@ -285,6 +285,39 @@ struct ProfScope {
         hipError_t e_ = (call);           \
         if (e_ != hipSuccess) return GDN_ERR_HIP; \
     } while (0)
+
+// A second stream per device, for the backward's two independent recurrences, with the
+// two events that fork it from and join it to the caller's stream. Created on first use
+// with the default priority and kept until the process ends. The caller holds side_mutex()
+// from the fork to the join, so that concurrent callers do not interleave event records.
+struct SideStream {
+    hipStream_t s = nullptr;
+    hipEvent_t fork = nullptr, join = nullptr;
+};
+constexpr int kMaxDevices = 64;
+std::mutex& side_mutex() {
+    static std::mutex m;
+    return m;
+}
+gdn_status side_stream(hipStream_t st, SideStream& out) {
+    static SideStream per_dev[kMaxDevices];
+    int dev = -1, cur = -1;
+    if (hipStreamGetDevice(st, &dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return GDN_ERR_HIP;
+    SideStream& x = per_dev[dev];
+    if (!x.s) {
+        if (hipGetDevice(&cur) != hipSuccess) return GDN_ERR_HIP;
+        if (cur != dev && hipSetDevice(dev) != hipSuccess) return GDN_ERR_HIP;
+        SideStream y;
+        bool ok = hipStreamCreateWithFlags(&y.s, hipStreamNonBlocking) == hipSuccess &&
+                  hipEventCreateWithFlags(&y.fork, hipEventDisableTiming) == hipSuccess &&
+                  hipEventCreateWithFlags(&y.join, hipEventDisableTiming) == hipSuccess;
+        if (cur != dev && hipSetDevice(cur) != hipSuccess) ok = false;
+        if (!ok) return GDN_ERR_HIP;  // (a partial set is not kept)
+        x = y;
+    }
+    out = x;
+    return GDN_OK;
+}
 
 gdn_status check_ws(const Plan& p, size_t need, void* ws, size_t bytes) {
     if (!ws || bytes < need) return GDN_ERR_WORKSPACE;
@@ -480,6 +513,15 @@ gdn_status gdn_chunk_bwd(const gdn_desc* desc, const void* q, const void* k, con
     const int rt = recur_rows((int)desc->V, (int)desc->K);
     const int vtiles = (int)(desc->V / rt);
     const int vktiles = (int)((desc->V + desc->K + rt - 1) / rt);
+    // The forward states pass (2) and the reverse adjoint pass (3) read only what the intra
+    // pass wrote and write disjoint workspace regions: (3) runs on a second stream, forked
+    // from the caller's after (1) and joined to it before (4).
+    std::lock_guard<std::mutex> side_lock(side_mutex());
+    SideStream side;
+    if ((s = side_stream(st, side)) != GDN_OK) return s;
+    hipStream_t st2 = side.s;
+    if (hipEventRecord(side.fork, st) != hipSuccess || hipStreamWaitEvent(st2, side.fork, 0) != hipSuccess)
+        return GDN_ERR_HIP;
     // 2. chunk-entry states, with the forward's CP
     RecurArgs ra{};
     memset(&ra, 0, sizeof(ra));
@@ -518,6 +560,9 @@ gdn_status gdn_chunk_bwd(const gdn_desc* desc, const void* q, const void* k, con
     }
     GDN_LAUNCH(kKRecurStates, st, launch_recur(ra, desc->dtype, kRecurStates, p.total_segs, vtiles, st));
     // 3. reverse adjoint pass, with CP mirrored (windows and scan from the sequence end)
+    const gdn_status sr = [&]() -> gdn_status {
+    gdn_status s = GDN_OK;
+    hipStream_t st = st2;
     RevArgs va;
     memset(&va, 0, sizeof(va));
     va.geo = ra.geo;
@@ -554,6 +599,12 @@ gdn_status gdn_chunk_bwd(const gdn_desc* desc, const void* q, const void* k, con
         va.seginit = seginit_r;
     }
     GDN_LAUNCH(kKBwdReverse, st, launch_reverse(va, desc->dtype, kRecurOut, p.total_segs, vtiles, st));
+    return GDN_OK;
+    }();
+    // join, also after a failed launch on the side stream
+    if (hipEventRecord(side.join, st2) != hipSuccess || hipStreamWaitEvent(st, side.join, 0) != hipSuccess)
+        return GDN_ERR_HIP;
+    if (sr != GDN_OK) return sr;
     // 4. per-chunk gradients
     BwdChunkArgs ba;
     memset(&ba, 0, sizeof(ba));

@@ -22,8 +22,8 @@ namespace gdn {
 namespace {
 
 template <typename T> struct BPad;
-template <> struct BPad<bf16_t> { static constexpr int row = 8, tr = 8; };
-template <> struct BPad<float> { static constexpr int row = 4, tr = 4; };
+template <> struct BPad<bf16_t> { static constexpr int row = 8; };
+template <> struct BPad<float> { static constexpr int row = 4; };
 
 // ---------------------------------------------------------------------------
 // Reverse adjoint recurrence. RT adjoint rows (value rows, or V + M-hat rows in the

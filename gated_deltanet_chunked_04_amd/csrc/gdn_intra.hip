@@ -32,8 +32,8 @@ namespace {
 constexpr int kThreads = 256;
 
 template <typename T> struct IntraPad;
-template <> struct IntraPad<bf16_t> { static constexpr int row = 8, tr = 8; };
-template <> struct IntraPad<float> { static constexpr int row = 4, tr = 4; };
+template <> struct IntraPad<bf16_t> { static constexpr int row = 8; };
+template <> struct IntraPad<float> { static constexpr int row = 4; };
 
 
 template <typename T, int K, int V>

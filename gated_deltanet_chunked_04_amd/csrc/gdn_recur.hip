@@ -34,8 +34,8 @@ namespace {
 constexpr int kThreads = 256;  // decision / table kernels
 
 template <typename T> struct RPad;
-template <> struct RPad<bf16_t> { static constexpr int row = 8, tr = 8; };
-template <> struct RPad<float> { static constexpr int row = 4, tr = 4; };
+template <> struct RPad<bf16_t> { static constexpr int row = 8; };
+template <> struct RPad<float> { static constexpr int row = 4; };
 
 // RT state rows per workgroup (one wave per 16 rows), chunk operands staged in LDS.
 template <typename T, int K, int RT>
@@ -408,6 +408,11 @@ __global__ __launch_bounds__(RT * 4) void k_recur(RecurArgs a) {
         const int64_t tn = sg.bos + (int64_t)cn * 64;
         const int cnn = min(64, sg.len - cn * 64);
         chunk_fetch<0>(R, a, tn, cnn, h, ucol0);
+        // the states pass has the least work per step to cover the loads: all pieces at once
+        if constexpr (MODE == kRecurStates) {
+            chunk_fetch<1>(R, a, tn, cnn, h, ucol0);
+            chunk_fetch<2>(R, a, tn, cnn, h, ucol0);
+        }
         Frag<T> sf[K / 32];
         f32x4 accD[4], accO[4];
         chunk_part1<T, K, RT, kOut>(L, accS, sf, accD, accO);
@@ -420,10 +425,10 @@ __global__ __launch_bounds__(RT * 4) void k_recur(RecurArgs a) {
                 for (int i = 0; i < 4; ++i)
                     L.sQ[(rt * 16 + gq * 4 + i) * C::LDU + wave * 16 + ln] = Elem<T>::from_f(accD[rt][i]);
         }
-        chunk_fetch<1>(R, a, tn, cnn, h, ucol0);
+        if constexpr (MODE != kRecurStates) chunk_fetch<1>(R, a, tn, cnn, h, ucol0);
         if (kOut) lds_sync();  // P tiles complete
         chunk_part2<T, K, RT, kOut>(a, L, accS, accD, accO, t0, c, h, vt * RT, okeep);
-        chunk_fetch<2>(R, a, tn, cnn, h, ucol0);
+        if constexpr (MODE != kRecurStates) chunk_fetch<2>(R, a, tn, cnn, h, ucol0);
     };
     if constexpr (kDepth == 2) {
         for (int ci = cbeg; ci < cend; ci += 2) {

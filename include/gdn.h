@@ -169,7 +169,11 @@ gdn_status gdn_chunk_bwd_workspace_size(const gdn_desc* desc, size_t* bytes);
  *   dg, dbeta       : outputs [B,T,H] fp32 (dg is with respect to the raw per-token g)
  *   d_initial_state : output [N,H,V,K] fp32, or NULL (not written)
  * The forward is recomputed inside, unless desc->flags has GDN_FLAG_REUSE_FORWARD (then the
- * intra-chunk pass and the forward CP preprocessing come from the workspace; see above). */
+ * intra-chunk pass and the forward CP preprocessing come from the workspace; see above).
+ * The reverse adjoint pass runs on a second stream of the library's (one per device, made on
+ * the first call with the default priority), forked from `stream` and joined back to it
+ * before the per-chunk gradients: work enqueued on `stream` afterwards sees every output.
+ * Concurrent calls from several host threads are serialised while they enqueue. */
 gdn_status gdn_chunk_bwd(const gdn_desc* desc, const void* q, const void* k, const void* v,
                          const float* g, const float* beta, const float* initial_state,
                          const void* d_o, const float* d_final_state,
