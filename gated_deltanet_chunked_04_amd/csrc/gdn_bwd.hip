@@ -581,11 +581,7 @@ __device__ __forceinline__ Frag<float> neg(const Frag<float>& f) {
 }
 
 // Sum over the four lanes that share ln (lane groups gq = 0..3).
-__device__ __forceinline__ float sum_gq(float x) {
-    x += __shfl_xor(x, 16, 64);
-    x += __shfl_xor(x, 32, 64);
-    return x;
-}
+__device__ __forceinline__ float sum_gq(float x) { return sum_rows(x); }
 
 template <typename T, int K, int V>
 __global__ __launch_bounds__(256) void k_bwd_chunk(BwdChunkArgs a) {
@@ -735,10 +731,11 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(BwdChunkArgs a) {
 #pragma unroll
         for (int jt = 0; jt < 4; ++jt) {
             f32x4 colpart;
+            const f32x4 gj = ld4(sGam + jt * 16 + gq * 4);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int j = jt * 16 + gq * 4 + i;
-                const float e = (j <= r) ? fast_exp(gr - sGam[j]) : 0.f;
+                const float e = (j <= r) ? fast_exp(gr - gj[i]) : 0.f;
                 const float x = dPT[jt][i] * PmQ[jt][i] * e;  // dP .* P at (query r, key j)
                 drow += x;
                 colpart[i] = x;
@@ -981,12 +978,13 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(BwdChunkArgs a) {
 #pragma unroll
             for (int ct = 0; ct < 4; ++ct) {
                 const f32x4 d = dd[ct], kk = kkk[ct];
+                const f32x4 gc = ld4(sGam + ct * 16 + gq * 4);
                 f32x4 colpart, mx;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int cc = ct * 16 + gq * 4 + e;
                     const bool lower = cc < ra;
-                    const float dec = lower ? fast_exp(ga - sGam[cc]) : 0.f;
+                    const float dec = lower ? fast_exp(ga - gc[e]) : 0.f;
                     const float ar = dec * kk[e];  // raw A[a][c]
                     const float dA = lower ? -d[e] : 0.f;
                     dbeta_row += dA * ar;
@@ -1056,16 +1054,12 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(BwdChunkArgs a) {
         lds_sync();
         // ---- d(gam) total and dg = reverse cumulative sum within the chunk --------------------
         if (wave == 0) {
+            // suffix sum over the chunk's rows: a prefix scan over the lanes in reversed order
+            const int i = 63 - lane;
             float d = 0.f;
-            if (lane < c)
-                d = sDgs[lane] + sRow[lane] + sRed[lane] + sRed[64 + lane] + sRed[128 + lane] + sRed[192 + lane];
-            // suffix sum over lanes lane..63
-#pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                const float y = __shfl_down(d, off, 64);
-                if (lane + off < 64) d += y;
-            }
-            if (lane < c) a.dg[(t0 + lane) * H + h] = d;
+            if (i < c) d = sDgs[i] + sRow[i] + sRed[i] + sRed[64 + i] + sRed[128 + i] + sRed[192 + i];
+            d = wave_prefix_sum(d);
+            if (i < c) a.dg[(t0 + i) * H + h] = d;
         }
         if (!more) break;
         cur = nxt;

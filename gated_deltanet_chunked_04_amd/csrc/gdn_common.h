@@ -77,6 +77,47 @@ __device__ __forceinline__ float sum_ln(float x) {
     return x;
 }
 
+// DPP move with zero fill where the source lane is outside the row.
+template <int kCtrl>
+__device__ __forceinline__ float dpp_z(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), kCtrl, 0xF, 0xF, false));
+}
+// Inclusive prefix sum over the 64 lanes (lane l gets x_0 + ... + x_l): a Hillis-Steele scan
+// within each 16-lane row by DPP row shifts, then the totals of the rows below from lane
+// reads. Call with all lanes on.
+__device__ __forceinline__ float wave_prefix_sum(float x) {
+    x += dpp_z<0x111>(x);  // row_shr:1
+    x += dpp_z<0x112>(x);  // row_shr:2
+    x += dpp_z<0x114>(x);  // row_shr:4
+    x += dpp_z<0x118>(x);  // row_shr:8
+    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 15));
+    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 31));
+    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 47));
+    const int row = (int)(threadIdx.x & 63) >> 4;
+    const float below = row == 0 ? 0.f : (row == 1 ? r0 : (row == 2 ? r0 + r1 : (r0 + r1) + r2));
+    return x + below;
+}
+// Maximum over the 64 lanes, returned to every lane. Call with all lanes on.
+__device__ __forceinline__ float wave_max(float x) {
+    x = fmaxf(x, dpp_f<0xB1>(x));
+    x = fmaxf(x, dpp_f<0x4E>(x));
+    x = fmaxf(x, dpp_f<0x141>(x));
+    x = fmaxf(x, dpp_f<0x140>(x));
+    const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 0));
+    const float b = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 16));
+    const float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 32));
+    const float d = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 48));
+    return fmaxf(fmaxf(a, b), fmaxf(c, d));
+}
+// Sum over the four lanes ln, ln + 16, ln + 32, ln + 48 (one per row) with the gfx950 row
+// swaps (no LDS traffic); the four lanes get the same bits. Call with all lanes on.
+__device__ __forceinline__ float sum_rows(float x) {
+    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    const float y = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 // ---------------------------------------------------------------------------
 // Element traits: storage type T in memory (bf16_t or float).
 template <typename T> struct Elem;

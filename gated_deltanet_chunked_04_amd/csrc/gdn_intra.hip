@@ -120,12 +120,7 @@ __global__ __launch_bounds__(kThreads) void k_intra(IntraArgs args) {
         const int64_t t0 = cur.t0;
         if (wave == 0) {
             const bool in = lane < c;
-            float x = g_in;
-#pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                const float y = __shfl_up(x, off, 64);
-                if (lane >= off) x += y;
-            }
+            const float x = wave_prefix_sum(g_in);
             sGam[lane] = x;   // rows past the chunk end carry the chunk total
             sBeta[lane] = b_in;
             if (in) args.gam[(t0 + lane) * H + h] = x;
@@ -190,9 +185,7 @@ __global__ __launch_bounds__(kThreads) void k_intra(IntraArgs args) {
         }
         if (wave == 1) {
             // chunk statistics for the CP decision
-            float m = lane < c ? sKK[lane] : 0.f;
-#pragma unroll
-            for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+            const float m = wave_max(lane < c ? sKK[lane] : 0.f);
             if (lane == 0) args.cstat[gc * H + h] = make_float2(sGam[63], m);
         }
 
