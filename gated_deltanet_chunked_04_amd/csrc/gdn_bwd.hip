@@ -632,8 +632,6 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(BwdChunkArgs a) {
     for (;;) {
         // ---- stage this task (the previous task's LDS reads are done) ---------------------
         lds_sync();
-        put_tile<T, K>(sS, C::LDK, R.s);
-        put_tile<T, K>(sG, C::LDK, R.g);
         put_tile<T, K>(sQ, C::LDK, R.q);
         put_tile<T, K>(sK, C::LDK, R.k);
         // dO enters every product together with the query scale (o = scale S q)
@@ -664,18 +662,6 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(BwdChunkArgs a) {
         const float ekt = fast_exp(Gm - gr);
 
         // ======================= state side, rows r of this wave =======================
-        // e^Gam <G, S> over the whole state (each thread a slice)
-        float gs = 0.f;
-        {
-            constexpr int VEC = Elem<T>::kVec;
-#pragma unroll 4
-            for (int e = tid; e < V * K / VEC; e += 256) {
-                const int vv = e / (K / VEC), kk = (e % (K / VEC)) * VEC;
-#pragma unroll
-                for (int i = 0; i < VEC; i += 4)
-                    gs += dot4(ld4(sG + vv * C::LDK + kk + i), ld4(sS + vv * C::LDK + kk + i));
-            }
-        }
         // ---- P (rows j, cols r) and dP^T[j][r] = sum_v Delta[j][v] dO[r][v], j-tiles <= wave
         f32x4 dPT[4], PmQ[4];
         {
@@ -706,6 +692,23 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(BwdChunkArgs a) {
                 for (int jt = 0; jt < 4; ++jt) frag_row(fk[jt], sK, C::LDK, jt * 16 + ln, kb * 32);
 #pragma unroll
                 for (int jt = 0; jt < 4; ++jt) mma(PmQ[jt], fk[jt], qr[kb]);
+            }
+        }
+        // S and G are fetched last in the previous task and staged only here, so that their
+        // registers are free over that task's WY side and their loads land behind the products above
+        put_tile<T, K>(sS, C::LDK, R.s);
+        put_tile<T, K>(sG, C::LDK, R.g);
+        lds_sync();
+        // e^Gam <G, S> over the whole state (each thread a slice)
+        float gs = 0.f;
+        {
+            constexpr int VEC = Elem<T>::kVec;
+#pragma unroll 4
+            for (int e = tid; e < V * K / VEC; e += 256) {
+                const int vv = e / (K / VEC), kk = (e % (K / VEC)) * VEC;
+#pragma unroll
+                for (int i = 0; i < VEC; i += 4)
+                    gs += dot4(ld4(sG + vv * C::LDK + kk + i), ld4(sS + vv * C::LDK + kk + i));
             }
         }
         // ---- dKt^T[k][r] = sum_v G[v][k] Delta[r][v]  (rows k, cols r) -------------------------
@@ -1001,7 +1004,6 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(BwdChunkArgs a) {
             }
         }
         lds_sync();
-        bwd_fetch<3>(R, a, nxt);
         // ---- dBk^T = dW^T T, dBv^T = dU^T T (rows k / v, cols a);  dK, dV ----------------------
         Frag<T> mrow[2], mcol[2];
         frag_row(mrow[0], sMx, C::LDX, ra, 0);  // Mx row a, slots c
@@ -1031,7 +1033,6 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(BwdChunkArgs a) {
             }
         }
         {
-            bwd_fetch<4>(R, a, nxt);
             T* dvp = reinterpret_cast<T*>(a.dv) + ((t0 + ra) * H + h) * V;
 #pragma unroll
             for (int vt = 0; vt < V / 16; ++vt) {
@@ -1047,6 +1048,8 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(BwdChunkArgs a) {
             }
         }
         bwd_fetch<5>(R, a, nxt);
+        bwd_fetch<3>(R, a, nxt);
+        bwd_fetch<4>(R, a, nxt);
         dbeta_row = sum_gq(dbeta_row);
         dgam_row = sum_gq(dgam_row);
         if (gq == 0) sRow[ra] = dgam_row;
