@@ -444,13 +444,13 @@ hipError_t launch_reverse_t(const RevArgs& a, int64_t nsegs_grid, int vtiles, hi
 // the WY side go into the rest of that space (the hole between dW and dDelta first, then
 // past dDelta).
 struct WyPlace {
-    int off[4];  // V, T, Y, Mx
+    int off[5];  // V, T, Y, Mx, dT
     int end;
 };
 constexpr WyPlace place_wy(int h0, int h1, int tail, int vmat, int xmat) {
     WyPlace p{};
     int cur = h0, tl = tail;
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 5; ++i) {
         const int s = i == 0 ? vmat : xmat;
         if (cur + s <= h1) {
             p.off[i] = cur;
@@ -491,24 +491,27 @@ struct BCfg {
     static constexpr int off_tm = wy.off[1];  // T = (I + A)^{-1}
     static constexpr int off_y = wy.off[2];   // Y = dT T^T
     static constexpr int off_mx = wy.off[3];  // Mx = dA .* (beta_a e^{gam_a - gam_c})
+    static constexpr int off_dt = wy.off[4];  // dT, exchanged between the two wave halves
     // small arrays after both
     static constexpr int off_gam = end_state > wy.end ? end_state : wy.end;
     static constexpr int off_beta = off_gam + 256;
     static constexpr int off_red = off_beta + 256;  // [4][64] fp32 column partials
-    static constexpr int off_row = off_red + 1024;  // [64] fp32 row parts
-    static constexpr int off_qd = off_row + 256;    // [4][64] e^gam dQt . Q partials over k slices
+    static constexpr int off_row = off_red + 1024;  // [2][64] fp32 row parts (one per wave half)
+    static constexpr int off_qd = off_row + 512;    // [4][64] e^gam dQt . Q partials over k slices
     static constexpr int off_dgs = off_qd + 1024;   // [64] state-side d(gam)
-    static constexpr int off_sc = off_dgs + 256;    // [8] fp32 scalars
-    static constexpr int total = off_sc + 64;
+    static constexpr int off_sc = off_dgs + 256;    // [16] fp32 scalars (two per wave)
+    static constexpr int off_db = off_sc + 64;      // [2][64] fp32 dbeta parts (one per wave half)
+    static constexpr int total = off_db + 512;
     static_assert(LDX <= LDV, "the exchange fits over Delta");
     static_assert(kMK <= kSt, "dW fits over S");
-    // 16-byte vectors per thread of one task's operands
-    static constexpr int NS = V * (K / VEC) / 256;    // S or G
-    static constexpr int NK = 64 * (K / VEC) / 256;   // q, k
-    static constexpr int NV = 64 * (V / VEC) / 256;   // dO, Delta, dDelta, v
-    static constexpr int NX = 64 * (64 / VEC) / 256;  // T
-    static_assert(NS * 256 == V * (K / VEC) && NK * 256 == 64 * (K / VEC) && NV * 256 == 64 * (V / VEC) &&
-                      NX * 256 == 64 * (64 / VEC),
+    // eight waves; 16-byte vectors per thread of one task's operands
+    static constexpr int NT = 512;
+    static constexpr int NS = V * (K / VEC) / NT;    // S or G
+    static constexpr int NK = 64 * (K / VEC) / NT;   // q, k
+    static constexpr int NV = 64 * (V / VEC) / NT;   // dO, Delta, dDelta, v
+    static constexpr int NX = 64 * (64 / VEC) / NT;  // T
+    static_assert(NS * NT == V * (K / VEC) && NK * NT == 64 * (K / VEC) && NV * NT == 64 * (V / VEC) &&
+                      NX * NT == 64 * (64 / VEC),
                   "vector split");
 };
 
@@ -518,8 +521,8 @@ struct BCfg {
 template <typename T, int K, int V>
 struct BRegs {
     using C = BCfg<T, K, V>;
-    u32x4 q[C::NK], k[C::NK], d[C::NV], dl[C::NV], dd[C::NV], t[C::NX];
-    u32x4 s[C::NS], g[C::NS], v[C::NV];
+    u32x4 q[C::NK], k[C::NK], d[C::NV], dl[C::NV], dd[C::NV];
+    u32x4 s[C::NS], g[C::NS];
     float gam, beta;
 };
 
@@ -528,12 +531,13 @@ struct BRegs {
 // CU's load queue instead of draining behind the matrix work.
 template <int kGroup, typename T, int K, int V>
 __device__ __forceinline__ void bwd_fetch(BRegs<T, K, V>& R, const BwdChunkArgs& a, const ChunkTask& x) {
+    using C = BCfg<T, K, V>;
     const int64_t H = a.geo.H;
     const size_t ok = ((size_t)x.t0 * H + x.h) * K, ov = ((size_t)x.t0 * H + x.h) * V;
     const size_t st = ((size_t)x.gc * H + x.h) * (size_t)V * K;
     if constexpr (kGroup == 0) {
-        fetch_tile<T, K>(R.q, reinterpret_cast<const T*>(a.q) + ok, (size_t)H * K, x.c);
-        fetch_tile<T, K>(R.k, reinterpret_cast<const T*>(a.k) + ok, (size_t)H * K, x.c);
+        fetch_tile<T, K, C::NK, C::NT>(R.q, reinterpret_cast<const T*>(a.q) + ok, (size_t)H * K, x.c);
+        fetch_tile<T, K, C::NK, C::NT>(R.k, reinterpret_cast<const T*>(a.k) + ok, (size_t)H * K, x.c);
         const int tid = threadIdx.x;
         if (tid < 64) {
             const bool in = tid < x.c;
@@ -541,18 +545,31 @@ __device__ __forceinline__ void bwd_fetch(BRegs<T, K, V>& R, const BwdChunkArgs&
             R.beta = in ? a.beta[(x.t0 + tid) * H + x.h] : 0.f;
         }
     } else if constexpr (kGroup == 1) {
-        fetch_tile<T, V>(R.d, reinterpret_cast<const T*>(a.d_o) + ov, (size_t)H * V, x.c);
-        fetch_tile<T, 64>(R.t, reinterpret_cast<const T*>(a.tmat) + ((size_t)x.gc * H + x.h) * 4096, 64, 64);
+        fetch_tile<T, V, C::NV, C::NT>(R.d, reinterpret_cast<const T*>(a.d_o) + ov, (size_t)H * V, x.c);
     } else if constexpr (kGroup == 2) {
-        fetch_tile<T, V>(R.dl, reinterpret_cast<const T*>(a.delta) + ov, (size_t)H * V, x.c);
-        fetch_tile<T, V>(R.dd, reinterpret_cast<const T*>(a.ddelta) + ov, (size_t)H * V, x.c);
+        fetch_tile<T, V, C::NV, C::NT>(R.dl, reinterpret_cast<const T*>(a.delta) + ov, (size_t)H * V, x.c);
+        fetch_tile<T, V, C::NV, C::NT>(R.dd, reinterpret_cast<const T*>(a.ddelta) + ov, (size_t)H * V, x.c);
     } else if constexpr (kGroup == 3) {
-        fetch_tile<T, K>(R.s, reinterpret_cast<const T*>(a.hstates) + st, K, V);
-    } else if constexpr (kGroup == 4) {
-        fetch_tile<T, K>(R.g, reinterpret_cast<const T*>(a.gstates) + st, K, V);
+        fetch_tile<T, K, C::NS, C::NT>(R.s, reinterpret_cast<const T*>(a.hstates) + st, K, V);
     } else {
-        fetch_tile<T, V>(R.v, reinterpret_cast<const T*>(a.v) + ov, (size_t)H * V, x.c);
+        fetch_tile<T, K, C::NS, C::NT>(R.g, reinterpret_cast<const T*>(a.gstates) + st, K, V);
     }
+}
+
+// v and T of the task being processed, loaded during its state side for its WY side.
+template <typename T, int K, int V>
+struct VTRegs {
+    using C = BCfg<T, K, V>;
+    u32x4 v[C::NV], t[C::NX];
+};
+template <typename T, int K, int V>
+__device__ __forceinline__ void bwd_fetch_vt(VTRegs<T, K, V>& R, const BwdChunkArgs& a, const ChunkTask& x) {
+    using C = BCfg<T, K, V>;
+    const int64_t H = a.geo.H;
+    fetch_tile<T, V, C::NV, C::NT>(R.v, reinterpret_cast<const T*>(a.v) + ((size_t)x.t0 * H + x.h) * V,
+                                   (size_t)H * V, x.c);
+    fetch_tile<T, 64, C::NX, C::NT>(R.t, reinterpret_cast<const T*>(a.tmat) + ((size_t)x.gc * H + x.h) * 4096, 64,
+                                    64);
 }
 
 // Four consecutive LDS elements as fp32.
@@ -584,68 +601,78 @@ __device__ __forceinline__ Frag<float> neg(const Frag<float>& f) {
 __device__ __forceinline__ float sum_gq(float x) { return sum_rows(x); }
 
 template <typename T, int K, int V>
-__global__ __launch_bounds__(256) void k_bwd_chunk(BwdChunkArgs a) {
+__global__ __launch_bounds__(512) void k_bwd_chunk(BwdChunkArgs a) {
     using C = BCfg<T, K, V>;
+    constexpr int NT = C::NT;
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-    T* sK = reinterpret_cast<T*>(smem + C::off_k);
-    T* sS = reinterpret_cast<T*>(smem + C::off_s);
-    T* sG = reinterpret_cast<T*>(smem + C::off_g);
-    T* sQ = reinterpret_cast<T*>(smem + C::off_q);
-    T* sD = reinterpret_cast<T*>(smem + C::off_d);
-    T* sDl = reinterpret_cast<T*>(smem + C::off_dl);
-    T* sX = reinterpret_cast<T*>(smem + C::off_x);
-    T* sdU = reinterpret_cast<T*>(smem + C::off_dd);
-    T* sdW = reinterpret_cast<T*>(smem + C::off_dw);
-    T* sV = reinterpret_cast<T*>(smem + C::off_v);
-    T* sTm = reinterpret_cast<T*>(smem + C::off_tm);
-    T* sY = reinterpret_cast<T*>(smem + C::off_y);
-    T* sMx = reinterpret_cast<T*>(smem + C::off_mx);
-    float* sGam = reinterpret_cast<float*>(smem + C::off_gam);
-    float* sBeta = reinterpret_cast<float*>(smem + C::off_beta);
-    float* sRed = reinterpret_cast<float*>(smem + C::off_red);
-    float* sRow = reinterpret_cast<float*>(smem + C::off_row);
-    float* sQd = reinterpret_cast<float*>(smem + C::off_qd);
-    float* sDgs = reinterpret_cast<float*>(smem + C::off_dgs);
-    float* sSc = reinterpret_cast<float*>(smem + C::off_sc);
 
     const Geo& geo = a.geo;
     const int64_t H = geo.H;
     const int64_t ntasks = geo.total_chunks * H;
     const int tid = threadIdx.x;
     const int wave = wave_id(), lane = tid & 63, ln = lane & 15, gq = lane >> 4;
-    const int r = wave * 16 + ln;  // this lane's chunk row in "column" roles
-    constexpr int KW = K / 64;     // k tiles (of 16) per wave in the column-split products
+    // Waves w and w + 4 share the chunk rows 16w .. 16w+15 in the row-split products and
+    // split the tiles along the other dimension: half hf takes the j, c, b tiles 2hf, 2hf+1,
+    // the k tiles hf*K/32 .., the v tiles hf*V/32 .. and, in the column-split products,
+    // the row tiles 2hf, 2hf+1 of its k slice.
+    const int w = wave & 3, hf = wave >> 2;
+    const int r = w * 16 + ln;     // this lane's chunk row in "column" roles
+    constexpr int KW = K / 64;     // k tiles (of 16) per k slice in the column-split products
+    constexpr int KH = K / 32;     // k tiles per half
+    constexpr int VH = V / 32;     // v tiles per half
 
     ChunkTask cur;
     int64_t t = next_chunk_task(geo, blockIdx.x, ntasks, cur);
     if (t >= ntasks) return;
     BRegs<T, K, V> R;  // the next task's operands
-    u32x4 rv[C::NV];    // v of this task
-    u32x4 rt[C::NX];    // T of this task
+    VTRegs<T, K, V> RV;  // v and T of this task
     bwd_fetch<0>(R, a, cur);
     bwd_fetch<1>(R, a, cur);
     bwd_fetch<2>(R, a, cur);
     bwd_fetch<3>(R, a, cur);
     bwd_fetch<4>(R, a, cur);
-    bwd_fetch<5>(R, a, cur);
 
     for (;;) {
+        // The LDS pointers are formed anew each task from an offset the compiler cannot see
+        // through (it is zero): otherwise it hoists every per-lane LDS address out of the
+        // loop and keeps dozens of them live (and spilled) across the whole task.
+        int zero_off = 0;
+        asm volatile("" : "+s"(zero_off));
+        unsigned char* sm = smem + zero_off;
+        T* sK = reinterpret_cast<T*>(sm + C::off_k);
+        T* sS = reinterpret_cast<T*>(sm + C::off_s);
+        T* sG = reinterpret_cast<T*>(sm + C::off_g);
+        T* sQ = reinterpret_cast<T*>(sm + C::off_q);
+        T* sD = reinterpret_cast<T*>(sm + C::off_d);
+        T* sDl = reinterpret_cast<T*>(sm + C::off_dl);
+        T* sX = reinterpret_cast<T*>(sm + C::off_x);
+        T* sdU = reinterpret_cast<T*>(sm + C::off_dd);
+        T* sdW = reinterpret_cast<T*>(sm + C::off_dw);
+        T* sV = reinterpret_cast<T*>(sm + C::off_v);
+        T* sTm = reinterpret_cast<T*>(sm + C::off_tm);
+        T* sY = reinterpret_cast<T*>(sm + C::off_y);
+        T* sMx = reinterpret_cast<T*>(sm + C::off_mx);
+        T* sDT = reinterpret_cast<T*>(sm + C::off_dt);
+        float* sGam = reinterpret_cast<float*>(sm + C::off_gam);
+        float* sBeta = reinterpret_cast<float*>(sm + C::off_beta);
+        float* sRed = reinterpret_cast<float*>(sm + C::off_red);
+        float* sRow = reinterpret_cast<float*>(sm + C::off_row);
+        float* sQd = reinterpret_cast<float*>(sm + C::off_qd);
+        float* sDgs = reinterpret_cast<float*>(sm + C::off_dgs);
+        float* sSc = reinterpret_cast<float*>(sm + C::off_sc);
+        float* sDb = reinterpret_cast<float*>(sm + C::off_db);
         // ---- stage this task (the previous task's LDS reads are done) ---------------------
         lds_sync();
-        put_tile<T, K>(sQ, C::LDK, R.q);
-        put_tile<T, K>(sK, C::LDK, R.k);
+        put_tile<T, K, C::NK, NT>(sQ, C::LDK, R.q);
+        put_tile<T, K, C::NK, NT>(sK, C::LDK, R.k);
         // dO enters every product together with the query scale (o = scale S q)
-        put_tile<T, V>(sD, C::LDV, R.d, a.scale);
-        put_tile<T, V>(sDl, C::LDV, R.dl);
-        put_tile<T, V>(sdU, C::LDV, R.dd);
+        put_tile<T, V, C::NV, NT>(sD, C::LDV, R.d, a.scale);
+        put_tile<T, V, C::NV, NT>(sDl, C::LDV, R.dl);
+        put_tile<T, V, C::NV, NT>(sdU, C::LDV, R.dd);
         if (tid < 64) {
             sGam[tid] = R.gam;
             sBeta[tid] = R.beta;
         }
-#pragma unroll
-        for (int i = 0; i < C::NV; ++i) rv[i] = R.v[i];
-#pragma unroll
-        for (int i = 0; i < C::NX; ++i) rt[i] = R.t[i];
         lds_sync();
         // The last task fetches itself again: unconditional fetches end the previous
         // operands' live range at the staging above.
@@ -662,99 +689,101 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(BwdChunkArgs a) {
         const float ekt = fast_exp(Gm - gr);
 
         // ======================= state side, rows r of this wave =======================
-        // ---- P (rows j, cols r) and dP^T[j][r] = sum_v Delta[j][v] dO[r][v], j-tiles <= wave
-        f32x4 dPT[4], PmQ[4];
+        // ---- P (rows j, cols r) and dP^T[j][r] = sum_v Delta[j][v] dO[r][v], this half's j tiles
+        f32x4 dPT[2], PmQ[2];
         {
             Frag<T> qr[K / 32], dor[V / 32];
 #pragma unroll
             for (int kb = 0; kb < K / 32; ++kb) frag_row(qr[kb], sQ, C::LDK, r, kb * 32);
 #pragma unroll
             for (int vb = 0; vb < V / 32; ++vb) frag_row(dor[vb], sD, C::LDV, r, vb * 32);
-            // all four j tiles (the mask below zeroes j > r): one straight block of
-            // independent products instead of a branch per tile
+            // both j tiles (the mask below zeroes j > r): one straight block of independent
+            // products instead of a branch per tile
 #pragma unroll
-            for (int jt = 0; jt < 4; ++jt) {
-                dPT[jt] = zero4();
-                PmQ[jt] = zero4();
+            for (int m = 0; m < 2; ++m) {
+                dPT[m] = zero4();
+                PmQ[m] = zero4();
             }
 #pragma unroll
             for (int vb = 0; vb < V / 32; ++vb) {
-                Frag<T> fd[4];
+                Frag<T> fd[2];
 #pragma unroll
-                for (int jt = 0; jt < 4; ++jt) frag_row(fd[jt], sDl, C::LDV, jt * 16 + ln, vb * 32);
+                for (int m = 0; m < 2; ++m) frag_row(fd[m], sDl, C::LDV, (2 * hf + m) * 16 + ln, vb * 32);
 #pragma unroll
-                for (int jt = 0; jt < 4; ++jt) mma(dPT[jt], fd[jt], dor[vb]);
+                for (int m = 0; m < 2; ++m) mma(dPT[m], fd[m], dor[vb]);
             }
 #pragma unroll
             for (int kb = 0; kb < K / 32; ++kb) {
-                Frag<T> fk[4];
+                Frag<T> fk[2];
 #pragma unroll
-                for (int jt = 0; jt < 4; ++jt) frag_row(fk[jt], sK, C::LDK, jt * 16 + ln, kb * 32);
+                for (int m = 0; m < 2; ++m) frag_row(fk[m], sK, C::LDK, (2 * hf + m) * 16 + ln, kb * 32);
 #pragma unroll
-                for (int jt = 0; jt < 4; ++jt) mma(PmQ[jt], fk[jt], qr[kb]);
+                for (int m = 0; m < 2; ++m) mma(PmQ[m], fk[m], qr[kb]);
             }
         }
         // S and G are fetched last in the previous task and staged only here, so that their
         // registers are free over that task's WY side and their loads land behind the products above
-        put_tile<T, K>(sS, C::LDK, R.s);
-        put_tile<T, K>(sG, C::LDK, R.g);
+        put_tile<T, K, C::NS, NT>(sS, C::LDK, R.s);
+        put_tile<T, K, C::NS, NT>(sG, C::LDK, R.g);
         lds_sync();
         // e^Gam <G, S> over the whole state (each thread a slice)
         float gs = 0.f;
         {
             constexpr int VEC = Elem<T>::kVec;
 #pragma unroll 4
-            for (int e = tid; e < V * K / VEC; e += 256) {
+            for (int e = tid; e < V * K / VEC; e += NT) {
                 const int vv = e / (K / VEC), kk = (e % (K / VEC)) * VEC;
 #pragma unroll
                 for (int i = 0; i < VEC; i += 4)
                     gs += dot4(ld4(sG + vv * C::LDK + kk + i), ld4(sS + vv * C::LDK + kk + i));
             }
         }
-        // ---- dKt^T[k][r] = sum_v G[v][k] Delta[r][v]  (rows k, cols r) -------------------------
-        f32x4 dKT[K / 16];
+        // ---- dKt^T[k][r] = sum_v G[v][k] Delta[r][v]  (rows k of this half, cols r) ------------
+        f32x4 dKT[KH];
         {
             Frag<T> dtr[V / 32];
 #pragma unroll
             for (int vb = 0; vb < V / 32; ++vb) frag_row(dtr[vb], sDl, C::LDV, r, vb * 32);
 #pragma unroll
-            for (int kt = 0; kt < K / 16; ++kt) dKT[kt] = zero4();
+            for (int i = 0; i < KH; ++i) dKT[i] = zero4();
 #pragma unroll
             for (int vb = 0; vb < V / 32; ++vb) {
-                Frag<T> fg[K / 16];
+                Frag<T> fg[KH];
 #pragma unroll
-                for (int kt = 0; kt < K / 16; ++kt) frag_col(fg[kt], sG, C::LDK, kt * 16 + ln, vb * 32);  // G^T row k, slots v
+                for (int i = 0; i < KH; ++i)
+                    frag_col(fg[i], sG, C::LDK, (hf * KH + i) * 16 + ln, vb * 32);  // G^T row k, slots v
 #pragma unroll
-                for (int kt = 0; kt < K / 16; ++kt) mma(dKT[kt], fg[kt], dtr[vb]);
+                for (int i = 0; i < KH; ++i) mma(dKT[i], fg[i], dtr[vb]);
             }
         }
         // mask, decay, the P terms of d(gam), and L .* dP
         float drow = 0.f;  // d(gam_r) terms accumulated in this lane (summed over gq below)
-        f32x4 LdP[4];
+        f32x4 LdP[2];
 #pragma unroll
-        for (int jt = 0; jt < 4; ++jt) {
+        for (int m = 0; m < 2; ++m) {
+            const int jt = 2 * hf + m;
             f32x4 colpart;
             const f32x4 gj = ld4(sGam + jt * 16 + gq * 4);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int j = jt * 16 + gq * 4 + i;
                 const float e = (j <= r) ? fast_exp(gr - gj[i]) : 0.f;
-                const float x = dPT[jt][i] * PmQ[jt][i] * e;  // dP .* P at (query r, key j)
+                const float x = dPT[m][i] * PmQ[m][i] * e;  // dP .* P at (query r, key j)
                 drow += x;
                 colpart[i] = x;
-                LdP[jt][i] = dPT[jt][i] * e;
+                LdP[m][i] = dPT[m][i] * e;
             }
-            // column sums over the wave's 16 query rows -> key j
+            // column sums over the wave's 16 query rows -> key j (each key belongs to one half)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const float s = sum_ln(colpart[i]);
-                if (ln == 0) sRed[wave * 64 + jt * 16 + gq * 4 + i] = -s;
+                if (ln == 0) sRed[w * 64 + jt * 16 + gq * 4 + i] = -s;
             }
         }
         // d(gam) from Kt: -e^{Gam-gam_r} sum_k dKt[r][k] K[r][k]; the chunk total gets the sum
         float ktk = 0.f;
 #pragma unroll
-        for (int kt = 0; kt < K / 16; ++kt) ktk += dot4(dKT[kt], ld4(sK + r * C::LDK + kt * 16 + gq * 4));
+        for (int i = 0; i < KH; ++i) ktk += dot4(dKT[i], ld4(sK + r * C::LDK + (hf * KH + i) * 16 + gq * 4));
         ktk *= ekt;
         drow -= ktk;
         {
@@ -762,39 +791,39 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(BwdChunkArgs a) {
             const float g1 = sum_gq(sum_ln(gs));
             if (lane == 0) {
                 sSc[wave] = t1;
-                sSc[4 + wave] = g1;
+                sSc[8 + wave] = g1;
             }
         }
         drow = sum_gq(drow);
-        if (gq == 0) sRow[r] = drow;
+        if (gq == 0) sRow[hf * 64 + r] = drow;
         lds_sync();  // every read of Delta is done: the exchange overwrites it
         // exchange L .* dP: sX[query r][key j]
 #pragma unroll
-        for (int jt = 0; jt < 4; ++jt) store4(sX + r * C::LDX + jt * 16 + gq * 4, LdP[jt]);
+        for (int m = 0; m < 2; ++m) store4(sX + r * C::LDX + (2 * hf + m) * 16 + gq * 4, LdP[m]);
         lds_sync();
-        // dk terms of the state side for the wave's rows as keys y = r:
+        // dk terms of the state side for the wave's rows as keys y = r, this half's k tiles:
         // e^{Gam-gam_y} dKt^T + Q^T (L .* dP)[:, y]
-        f32x4 dkpart[K / 16];
+        f32x4 dkpart[KH];
         {
             Frag<T> xc[2];
             frag_col(xc[0], sX, C::LDX, r, 0);  // (L .* dP) column y, slots r'
             frag_col(xc[1], sX, C::LDX, r, 32);
 #pragma unroll
-            for (int kt = 0; kt < K / 16; ++kt) {
-                dkpart[kt] = dKT[kt] * ekt;
+            for (int i = 0; i < KH; ++i) {
+                dkpart[i] = dKT[i] * ekt;
 #pragma unroll
                 for (int yb = 0; yb < 2; ++yb) {
                     Frag<T> fq;
-                    frag_col(fq, sQ, C::LDK, kt * 16 + ln, yb * 32);  // Q^T row k, slots r'
-                    mma(dkpart[kt], fq, xc[yb]);
+                    frag_col(fq, sQ, C::LDK, (hf * KH + i) * 16 + ln, yb * 32);  // Q^T row k, slots r'
+                    mma(dkpart[i], fq, xc[yb]);
                 }
             }
         }
-        // ============ state side, k tiles kw*KW .. of this wave, all chunk rows =============
+        // ======= state side, k slice w (KW tiles), row tiles 2hf, 2hf+1 of the chunk =======
         // dQt^T[k][r] = sum_v S[v][k] dO[r][v],  dW^T[k][r] = -sum_v S[v][k] dDelta[r][v]
         {
-            const int k0 = wave * (K / 4);
-            f32x4 dQT[KW][4], dWT[KW][4];
+            const int k0 = w * (K / 4);
+            f32x4 dQT[KW][2], dWT[KW][2];
             Frag<T> sfc[KW][V / 32];
 #pragma unroll
             for (int j = 0; j < KW; ++j)
@@ -802,7 +831,8 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(BwdChunkArgs a) {
                 for (int vb = 0; vb < V / 32; ++vb)
                     frag_col(sfc[j][vb], sS, C::LDK, k0 + j * 16 + ln, vb * 32);  // S^T row k, slots v
 #pragma unroll
-            for (int rr = 0; rr < 4; ++rr) {
+            for (int m = 0; m < 2; ++m) {
+                const int rr = 2 * hf + m;
                 Frag<T> fdo[V / 32], fdd[V / 32];
 #pragma unroll
                 for (int vb = 0; vb < V / 32; ++vb) {
@@ -813,15 +843,18 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(BwdChunkArgs a) {
                 }
 #pragma unroll
                 for (int j = 0; j < KW; ++j) {
-                    dQT[j][rr] = zero4();
-                    dWT[j][rr] = zero4();
+                    dQT[j][m] = zero4();
+                    dWT[j][m] = zero4();
 #pragma unroll
                     for (int vb = 0; vb < V / 32; ++vb) {
-                        mma(dQT[j][rr], sfc[j][vb], fdo[vb]);
-                        mma(dWT[j][rr], sfc[j][vb], fdd[vb]);
+                        mma(dQT[j][m], sfc[j][vb], fdo[vb]);
+                        mma(dWT[j][m], sfc[j][vb], fdd[vb]);
                     }
                 }
             }
+            // v and T of this task for the WY side: late enough to add no registers to the
+            // products above, early enough for the loads to land before the WY staging
+            bwd_fetch_vt(RV, a, cur);
             // dq^T = e^{gam_r} dQt^T + K^T (L .* dP)^T, and e^{gam_r} sum_k dQt[r][k] Q[r][k]
             // over this wave's k slice
             Frag<T> kc[KW][2];
@@ -831,8 +864,8 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(BwdChunkArgs a) {
                 frag_col(kc[j][1], sK, C::LDK, k0 + j * 16 + ln, 32);
             }
 #pragma unroll
-            for (int rr = 0; rr < 4; ++rr) {
-                const int row = rr * 16 + ln;
+            for (int m = 0; m < 2; ++m) {
+                const int row = (2 * hf + m) * 16 + ln;
                 const float eg = fast_exp(sGam[row]);
                 Frag<T> xr[2];
                 frag_row(xr[0], sX, C::LDX, row, 0);  // (L .* dP) row r, slots j'
@@ -841,111 +874,120 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(BwdChunkArgs a) {
                 float qd = 0.f;
 #pragma unroll
                 for (int j = 0; j < KW; ++j) {
-                    qd += dot4(dQT[j][rr], ld4(sQ + row * C::LDK + k0 + j * 16 + gq * 4));
-                    f32x4 acc = dQT[j][rr] * eg;
+                    qd += dot4(dQT[j][m], ld4(sQ + row * C::LDK + k0 + j * 16 + gq * 4));
+                    f32x4 acc = dQT[j][m] * eg;
                     mma(acc, kc[j][0], xr[0]);
                     mma(acc, kc[j][1], xr[1]);
                     if (row < c) store4(dq + j * 16 + gq * 4, acc);
                 }
                 qd = sum_gq(qd) * eg;
-                if (gq == 0) sQd[wave * 64 + row] = qd;
+                if (gq == 0) sQd[w * 64 + row] = qd;
             }
             lds_sync();  // the state side's LDS reads are done: the WY side reuses the space
             // dW (rows r) in the operand type, over S
 #pragma unroll
             for (int j = 0; j < KW; ++j)
 #pragma unroll
-                for (int rr = 0; rr < 4; ++rr) {
-                    const int row = rr * 16 + ln;
-                    store4(sdW + row * C::LDK + k0 + j * 16 + gq * 4, row < c ? dWT[j][rr] : zero4());
+                for (int m = 0; m < 2; ++m) {
+                    const int row = (2 * hf + m) * 16 + ln;
+                    store4(sdW + row * C::LDK + k0 + j * 16 + gq * 4, row < c ? dWT[j][m] : zero4());
                 }
         }
 
         // ================================= WY side =====================================
         if (tid < 64) {
-            float d = sRow[tid] + sRed[tid] + sRed[64 + tid] + sRed[128 + tid] + sRed[192 + tid] + sQd[tid] +
-                      sQd[64 + tid] + sQd[128 + tid] + sQd[192 + tid];
+            float d = sRow[tid] + sRow[64 + tid] + sRed[tid] + sRed[64 + tid] + sRed[128 + tid] + sRed[192 + tid] +
+                      sQd[tid] + sQd[64 + tid] + sQd[128 + tid] + sQd[192 + tid];
             if (tid == c - 1) {
-                const float kt_all = sSc[0] + sSc[1] + sSc[2] + sSc[3];
-                const float gs_all = sSc[4] + sSc[5] + sSc[6] + sSc[7];
+                float kt_all = 0.f, gs_all = 0.f;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    kt_all += sSc[i];
+                    gs_all += sSc[8 + i];
+                }
                 d += kt_all + fast_exp(Gm) * gs_all;
             }
             sDgs[tid] = d;
         }
-        put_tile<T, V>(sV, C::LDV, rv);
-        put_tile<T, 64>(sTm, C::LDX, rt);
+        put_tile<T, V, C::NV, NT>(sV, C::LDV, RV.v);
+        put_tile<T, 64, C::NX, NT>(sTm, C::LDX, RV.t);
         lds_sync();
         // The next task's operands load over the rest of this one, issued late (where few
         // registers are live, so that nothing spills or waits on them) and in groups.
         bwd_fetch<0>(R, a, nxt);
         const int ra = r;
-        // ---- dT[a][b] = beta_b e^{gam_b} (dW K^T)[a][b] + beta_b (dU V^T)[a][b], b < a --------
-        // (tiles rows b, cols a: two of them are a B fragment of dT^T)
-        Frag<T> dtf[2];
+        // ---- dT[a][b] = beta_b e^{gam_b} (dW K^T)[a][b] + beta_b (dU V^T)[a][b], b < a, this
+        // half's b tiles (rows b, cols a), exchanged through LDS as dT[a][b]
         {
-            f32x4 dT[4];
             Frag<T> wf[K / 32], uf[V / 32];
 #pragma unroll
             for (int kb = 0; kb < K / 32; ++kb) frag_row(wf[kb], sdW, C::LDK, ra, kb * 32);
 #pragma unroll
             for (int vb = 0; vb < V / 32; ++vb) frag_row(uf[vb], sdU, C::LDV, ra, vb * 32);
-            // all four b tiles (the mask below zeroes b >= a)
-            f32x4 x[4], y[4];
+            // both b tiles (the mask below zeroes b >= a)
+            f32x4 x[2], y[2];
 #pragma unroll
-            for (int bt = 0; bt < 4; ++bt) {
-                x[bt] = zero4();
-                y[bt] = zero4();
+            for (int m = 0; m < 2; ++m) {
+                x[m] = zero4();
+                y[m] = zero4();
             }
 #pragma unroll
             for (int kb = 0; kb < K / 32; ++kb) {
-                Frag<T> fk[4];
+                Frag<T> fk[2];
 #pragma unroll
-                for (int bt = 0; bt < 4; ++bt) frag_row(fk[bt], sK, C::LDK, bt * 16 + ln, kb * 32);
+                for (int m = 0; m < 2; ++m) frag_row(fk[m], sK, C::LDK, (2 * hf + m) * 16 + ln, kb * 32);
 #pragma unroll
-                for (int bt = 0; bt < 4; ++bt) mma(x[bt], fk[bt], wf[kb]);  // rows b, cols a: (K dW^T)[b][a]
+                for (int m = 0; m < 2; ++m) mma(x[m], fk[m], wf[kb]);  // rows b, cols a: (K dW^T)[b][a]
             }
 #pragma unroll
             for (int vb = 0; vb < V / 32; ++vb) {
-                Frag<T> fv[4];
+                Frag<T> fv[2];
 #pragma unroll
-                for (int bt = 0; bt < 4; ++bt) frag_row(fv[bt], sV, C::LDV, bt * 16 + ln, vb * 32);
+                for (int m = 0; m < 2; ++m) frag_row(fv[m], sV, C::LDV, (2 * hf + m) * 16 + ln, vb * 32);
 #pragma unroll
-                for (int bt = 0; bt < 4; ++bt) mma(y[bt], fv[bt], uf[vb]);
+                for (int m = 0; m < 2; ++m) mma(y[m], fv[m], uf[vb]);
             }
 #pragma unroll
-            for (int bt = 0; bt < 4; ++bt) {
-                const f32x4 gb = *reinterpret_cast<const f32x4*>(sGam + bt * 16 + gq * 4);
-                const f32x4 bb = *reinterpret_cast<const f32x4*>(sBeta + bt * 16 + gq * 4);
+            for (int m = 0; m < 2; ++m) {
+                const int bt = 2 * hf + m;
+                const f32x4 gb = ld4(sGam + bt * 16 + gq * 4);
+                const f32x4 bb = ld4(sBeta + bt * 16 + gq * 4);
+                f32x4 dT;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int b = bt * 16 + gq * 4 + e;
-                    dT[bt][e] = (b < ra) ? bb[e] * (fast_exp(gb[e]) * x[bt][e] + y[bt][e]) : 0.f;
+                    dT[e] = (b < ra) ? bb[e] * (fast_exp(gb[e]) * x[m][e] + y[m][e]) : 0.f;
                 }
+                store4(sDT + ra * C::LDX + bt * 16 + gq * 4, dT);  // dT[a][b]
             }
-            frag_acc(dtf[0], dT[0], dT[1]);
-            frag_acc(dtf[1], dT[2], dT[3]);
         }
+        lds_sync();
         bwd_fetch<1>(R, a, nxt);
-        // ---- Y = dT T^T: tiles Y^T[c][a] = sum_b T[c][b] dT[a][b] (T[c][b] = 0 for b > c) -----
+        // ---- Y = dT T^T: tiles Y^T[c][a] = sum_b T[c][b] dT[a][b] (T[c][b] = 0 for b > c),
+        // this half's c tiles -------------------------------------------------------------------
         {
-            f32x4 y[4];
+            Frag<T> dtf[2];
+            frag_row(dtf[0], sDT, C::LDX, ra, 0);  // dT row a, slots b
+            frag_row(dtf[1], sDT, C::LDX, ra, 32);
+            f32x4 y[2];
 #pragma unroll
-            for (int ct = 0; ct < 4; ++ct) y[ct] = zero4();
+            for (int m = 0; m < 2; ++m) y[m] = zero4();
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
-                Frag<T> ft[4];
+                Frag<T> ft[2];
 #pragma unroll
-                for (int ct = 0; ct < 4; ++ct) frag_row(ft[ct], sTm, C::LDX, ct * 16 + ln, kb * 32);
+                for (int m = 0; m < 2; ++m) frag_row(ft[m], sTm, C::LDX, (2 * hf + m) * 16 + ln, kb * 32);
 #pragma unroll
-                for (int ct = 0; ct < 4; ++ct) mma(y[ct], ft[ct], dtf[kb]);
+                for (int m = 0; m < 2; ++m) mma(y[m], ft[m], dtf[kb]);
             }
 #pragma unroll
-            for (int ct = 0; ct < 4; ++ct) store4(sY + ra * C::LDX + ct * 16 + gq * 4, y[ct]);  // Y[a][c]
+            for (int m = 0; m < 2; ++m) store4(sY + ra * C::LDX + (2 * hf + m) * 16 + gq * 4, y[m]);  // Y[a][c]
         }
         lds_sync();
         bwd_fetch<2>(R, a, nxt);
         // ---- dA[a][c] = -sum_x T[x][a] Y[x][c] for c < a (T[x][a] = 0 for x < a); with the
-        // raw A[a][c] = e^{gam_a - gam_c} k_a.k_c: dbeta, d(gam), and Mx = dA beta_a e^{..}
+        // raw A[a][c] = e^{gam_a - gam_c} k_a.k_c: dbeta, d(gam), and Mx = dA beta_a e^{..},
+        // this half's c tiles
         float dbeta_row = 0.f, dgam_row = 0.f;
         Frag<T> ta[2];
         frag_col(ta[0], sTm, C::LDX, ra, 0);  // T column a, slots x
@@ -955,32 +997,33 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(BwdChunkArgs a) {
 #pragma unroll
             for (int kb = 0; kb < K / 32; ++kb) frag_row(kra[kb], sK, C::LDK, ra, kb * 32);
             const float ba = sBeta[ra], ga = sGam[ra];
-            // all four c tiles (the mask below zeroes c >= a)
-            f32x4 dd[4], kkk[4];
+            f32x4 dd[2], kkk[2];
 #pragma unroll
-            for (int ct = 0; ct < 4; ++ct) {
-                dd[ct] = zero4();
-                kkk[ct] = zero4();
+            for (int m = 0; m < 2; ++m) {
+                dd[m] = zero4();
+                kkk[m] = zero4();
             }
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
-                Frag<T> fy[4];
+                Frag<T> fy[2];
 #pragma unroll
-                for (int ct = 0; ct < 4; ++ct) frag_col(fy[ct], sY, C::LDX, ct * 16 + ln, kb * 32);  // Y^T row c, slots x
+                for (int m = 0; m < 2; ++m)
+                    frag_col(fy[m], sY, C::LDX, (2 * hf + m) * 16 + ln, kb * 32);  // Y^T row c, slots x
 #pragma unroll
-                for (int ct = 0; ct < 4; ++ct) mma(dd[ct], fy[ct], ta[kb]);  // rows c, cols a: (T^T Y)^T
+                for (int m = 0; m < 2; ++m) mma(dd[m], fy[m], ta[kb]);  // rows c, cols a: (T^T Y)^T
             }
 #pragma unroll
             for (int kb = 0; kb < K / 32; ++kb) {
-                Frag<T> fk[4];
+                Frag<T> fk[2];
 #pragma unroll
-                for (int ct = 0; ct < 4; ++ct) frag_row(fk[ct], sK, C::LDK, ct * 16 + ln, kb * 32);
+                for (int m = 0; m < 2; ++m) frag_row(fk[m], sK, C::LDK, (2 * hf + m) * 16 + ln, kb * 32);
 #pragma unroll
-                for (int ct = 0; ct < 4; ++ct) mma(kkk[ct], fk[ct], kra[kb]);  // rows c, cols a: k_c . k_a
+                for (int m = 0; m < 2; ++m) mma(kkk[m], fk[m], kra[kb]);  // rows c, cols a: k_c . k_a
             }
 #pragma unroll
-            for (int ct = 0; ct < 4; ++ct) {
-                const f32x4 d = dd[ct], kk = kkk[ct];
+            for (int m = 0; m < 2; ++m) {
+                const int ct = 2 * hf + m;
+                const f32x4 d = dd[m], kk = kkk[m];
                 const f32x4 gc = ld4(sGam + ct * 16 + gq * 4);
                 f32x4 colpart, mx;
 #pragma unroll
@@ -998,13 +1041,13 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(BwdChunkArgs a) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const float s = sum_ln(colpart[e]);
-                    if (ln == 0) sRed[wave * 64 + ct * 16 + gq * 4 + e] = -s;
+                    if (ln == 0) sRed[w * 64 + ct * 16 + gq * 4 + e] = -s;
                 }
                 store4(sMx + ra * C::LDX + ct * 16 + gq * 4, mx);  // Mx[a][c]
             }
         }
         lds_sync();
-        // ---- dBk^T = dW^T T, dBv^T = dU^T T (rows k / v, cols a);  dK, dV ----------------------
+        // ---- dBk^T = dW^T T, dBv^T = dU^T T (rows k / v, cols a);  dK, dV, this half's tiles ---
         Frag<T> mrow[2], mcol[2];
         frag_row(mrow[0], sMx, C::LDX, ra, 0);  // Mx row a, slots c
         frag_row(mrow[1], sMx, C::LDX, ra, 32);
@@ -1014,7 +1057,8 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(BwdChunkArgs a) {
         {
             T* dkp = reinterpret_cast<T*>(a.dk) + ((t0 + ra) * H + h) * K;
 #pragma unroll
-            for (int kt = 0; kt < K / 16; ++kt) {
+            for (int i = 0; i < KH; ++i) {
+                const int kt = hf * KH + i;
                 f32x4 bk = zero4(), mk = zero4();
 #pragma unroll
                 for (int xb = 0; xb < 2; ++xb) {
@@ -1029,13 +1073,14 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(BwdChunkArgs a) {
                 const float s = dot4(bk, ld4(sK + ra * C::LDK + kt * 16 + gq * 4));
                 dbeta_row += ega * s;
                 dgam_row += ba * ega * s;
-                if (ra < c) store4(dkp + kt * 16 + gq * 4, dkpart[kt] + mk + bk * (ba * ega));
+                if (ra < c) store4(dkp + kt * 16 + gq * 4, dkpart[i] + mk + bk * (ba * ega));
             }
         }
         {
             T* dvp = reinterpret_cast<T*>(a.dv) + ((t0 + ra) * H + h) * V;
 #pragma unroll
-            for (int vt = 0; vt < V / 16; ++vt) {
+            for (int i = 0; i < VH; ++i) {
+                const int vt = hf * VH + i;
                 f32x4 bv = zero4();
 #pragma unroll
                 for (int xb = 0; xb < 2; ++xb) {
@@ -1047,22 +1092,26 @@ __global__ __launch_bounds__(256) void k_bwd_chunk(BwdChunkArgs a) {
                 if (ra < c) store4(dvp + vt * 16 + gq * 4, bv * ba);
             }
         }
-        bwd_fetch<5>(R, a, nxt);
         bwd_fetch<3>(R, a, nxt);
         bwd_fetch<4>(R, a, nxt);
         dbeta_row = sum_gq(dbeta_row);
         dgam_row = sum_gq(dgam_row);
-        if (gq == 0) sRow[ra] = dgam_row;
-        if (gq == 0 && ra < c) a.dbeta[(t0 + ra) * H + h] = dbeta_row;
+        if (gq == 0) {
+            sRow[hf * 64 + ra] = dgam_row;
+            sDb[hf * 64 + ra] = dbeta_row;
+        }
         lds_sync();
-        // ---- d(gam) total and dg = reverse cumulative sum within the chunk --------------------
+        // ---- dbeta, and d(gam) total with dg = reverse cumulative sum within the chunk ---------
         if (wave == 0) {
             // suffix sum over the chunk's rows: a prefix scan over the lanes in reversed order
             const int i = 63 - lane;
             float d = 0.f;
-            if (i < c) d = sDgs[i] + sRow[i] + sRed[i] + sRed[64 + i] + sRed[128 + i] + sRed[192 + i];
+            if (i < c)
+                d = sDgs[i] + sRow[i] + sRow[64 + i] + sRed[i] + sRed[64 + i] + sRed[128 + i] + sRed[192 + i];
             d = wave_prefix_sum(d);
             if (i < c) a.dg[(t0 + i) * H + h] = d;
+        } else if (wave == 1) {
+            if (lane < c) a.dbeta[(t0 + lane) * H + h] = sDb[lane] + sDb[64 + lane];
         }
         if (!more) break;
         cur = nxt;
@@ -1078,7 +1127,7 @@ hipError_t launch_bwd_chunk_t(const BwdChunkArgs& a, int grid, hipStream_t st) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, C::total);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), C::total, st, a);
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(C::NT), C::total, st, a);
     return hipGetLastError();
 }
 

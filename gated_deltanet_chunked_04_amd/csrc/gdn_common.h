@@ -435,14 +435,21 @@ template <typename T, int D, int NT>
 __device__ __forceinline__ void flush_tile(T* dst, size_t ld_g, int rows, const T* sm, int ld) {
     constexpr int VEC = Elem<T>::kVec;
     constexpr int NV = D / VEC;
+    constexpr int N = 64 * NV / NT;
     static_assert((64 * NV) % NT == 0, "flush split");
+    // all LDS reads first; a full tile (the wave-uniform common case) stores with no branch
+    // per row, so the reads are not serialised behind per-row branches
+    u32x4 x[N];
 #pragma unroll
-    for (int it = 0; it < 64 * NV / NT; ++it) {
+    for (int it = 0; it < N; ++it) {
+        const int u = threadIdx.x + it * NT;
+        x[it] = *reinterpret_cast<const u32x4*>(sm + (u / NV) * ld + (u % NV) * VEC);
+    }
+#pragma unroll
+    for (int it = 0; it < N; ++it) {
         const int u = threadIdx.x + it * NT;
         const int r = u / NV, cv = u % NV;
-        if (r < rows)
-            *reinterpret_cast<u32x4*>(dst + (size_t)r * ld_g + cv * VEC) =
-                *reinterpret_cast<const u32x4*>(sm + r * ld + cv * VEC);
+        if (rows >= 64 || r < rows) *reinterpret_cast<u32x4*>(dst + (size_t)r * ld_g + cv * VEC) = x[it];
     }
 }
 
@@ -454,14 +461,18 @@ __device__ __forceinline__ void store_rows(T* __restrict__ dst, int64_t t0, int6
     constexpr int NV = D / VEC;
     constexpr int UNITS = 64 * NV;
     const int tid = threadIdx.x;
+    u32x4 x[UNITS / 256];
+#pragma unroll
+    for (int it = 0; it < UNITS / 256; ++it) {
+        const int u = tid + it * 256;
+        x[it] = *reinterpret_cast<const u32x4*>(sm + (u / NV) * ld + (u % NV) * VEC);
+    }
 #pragma unroll
     for (int it = 0; it < UNITS / 256; ++it) {
         const int u = tid + it * 256;
         const int cv = u % NV;
         const int r = u / NV;
-        if (r < rows)
-            *reinterpret_cast<u32x4*>(dst + ((t0 + r) * H + h) * D + cv * VEC) =
-                *reinterpret_cast<const u32x4*>(sm + r * ld + cv * VEC);
+        if (rows >= 64 || r < rows) *reinterpret_cast<u32x4*>(dst + ((t0 + r) * H + h) * D + cv * VEC) = x[it];
     }
 }
 

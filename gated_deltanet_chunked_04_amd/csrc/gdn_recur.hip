@@ -241,10 +241,11 @@ __device__ __forceinline__ void chunk_part2(const RecurArgs& a, const ChunkLds<T
         const int V = a.geo.V;
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) okeep[rt] = Pack4<T>::make(accO[rt] * a.scale);
+        // a full chunk (the wave-uniform common case) stores with no branch per row
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) {
             const int r = rt * 16 + ln;
-            if (r < c)
+            if (c == 64 || r < c)
                 *reinterpret_cast<typename Pack4<T>::type*>(o + ((t0 + r) * H + h) * V + vcol0 + wave * 16 + gq * 4) =
                     okeep[rt];
         }
