@@ -192,6 +192,25 @@ __device__ __forceinline__ void frag_col(Frag<float>& f, const float* base, int 
     f.hi = f32x4{p[(size_t)16 * ld], p[(size_t)17 * ld], p[(size_t)18 * ld], p[(size_t)19 * ld]};
 }
 
+// Rows k0 + 4gq .. k0 + 4gq + 3 of column `col` (= tile*16 + ln for the calling lane) of a
+// row-major LDS matrix, as fp32: one transpose read in bf16 (slot m of the read is row
+// k0 + 4gq + m, as in frag_col).
+template <typename T>
+__device__ __forceinline__ f32x4 col4(const T* base, int ld, int col, int k0);
+template <>
+__device__ __forceinline__ f32x4 col4(const bf16_t* base, int ld, int col, int k0) {
+    const int lane = threadIdx.x & 63, ln = lane & 15, gq = lane >> 4;
+    const u32x2 a = ds_read_tr16(base + (size_t)(k0 + gq * 4 + (ln >> 2)) * ld + (col - ln) + 4 * (ln & 3));
+    return f32x4{__uint_as_float(a.x << 16), __uint_as_float(a.x & 0xFFFF0000u), __uint_as_float(a.y << 16),
+                 __uint_as_float(a.y & 0xFFFF0000u)};
+}
+template <>
+__device__ __forceinline__ f32x4 col4(const float* base, int ld, int col, int k0) {
+    const int gq = threadIdx.x >> 4 & 3;
+    const float* p = base + (size_t)(k0 + gq * 4) * ld + col;
+    return f32x4{p[0], p[(size_t)ld], p[(size_t)2 * ld], p[(size_t)3 * ld]};
+}
+
 // Fragment from two fp32 accumulator tiles (rows k0..k0+15 and k0+16..k0+31 of X),
 // each element multiplied by s; as a B fragment of X, or an A fragment of X^T.
 __device__ __forceinline__ void frag_acc(Frag<bf16_t>& f, const f32x4& t0, const f32x4& t1, float s = 1.f) {

@@ -81,6 +81,7 @@ template <typename T, int K, int V>
 __global__ __launch_bounds__(kThreads) void k_intra(IntraArgs args) {
     using S = IntraSmem<T, K, V>;
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+
     T* sK = reinterpret_cast<T*>(smem + S::off_k);
     T* sV = reinterpret_cast<T*>(smem + S::off_v);
     float* sT = reinterpret_cast<float*>(smem + S::off_t);
@@ -149,26 +150,28 @@ __global__ __launch_bounds__(kThreads) void k_intra(IntraArgs args) {
                 Frag<T> fa[NTT], fb[NTT];
 #pragma unroll
                 for (int m = 0; m < NTT; ++m) {
-                    frag_row(fa[m], sK, S::LDK, ti[m] * 16 + ln, kb * 32);
-                    frag_row(fb[m], sK, S::LDK, tj[m] * 16 + ln, kb * 32);
+                    frag_row(fa[m], sK, S::LDK, tj[m] * 16 + ln, kb * 32);
+                    frag_row(fb[m], sK, S::LDK, ti[m] * 16 + ln, kb * 32);
                 }
 #pragma unroll
                 for (int m = 0; m < NTT; ++m) mma(acc[m], fa[m], fb[m]);
             }
+            // acc[m][i] = k_j . k_r with j = tj*16 + gq*4 + i, r = ti*16 + ln: four consecutive
+            // columns of row r, one vector store
 #pragma unroll
             for (int m = 0; m < NTT; ++m) {
                 if (on[m]) {
-                    const int j = tj[m] * 16 + ln;
-                    const float gj = sGam[j];
-                    const f32x4 gr = *reinterpret_cast<const f32x4*>(sGam + ti[m] * 16 + gq * 4);
-                    const f32x4 br = *reinterpret_cast<const f32x4*>(sBeta + ti[m] * 16 + gq * 4);
+                    const int r = ti[m] * 16 + ln;
+                    const float gr = sGam[r], br = sBeta[r];
+                    const f32x4 gj = *reinterpret_cast<const f32x4*>(sGam + tj[m] * 16 + gq * 4);
+                    f32x4 val;
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        const int r = ti[m] * 16 + gq * 4 + i;
-                        const float val = (j < r) ? br[i] * fast_exp(gr[i] - gj) * acc[m][i] : 0.f;
-                        sA[r * kLdA + j] = val;
-                        if (r == j) sKK[r] = br[i] * acc[m][i];
+                        const int j = tj[m] * 16 + gq * 4 + i;
+                        val[i] = (j < r) ? br * fast_exp(gr - gj[i]) * acc[m][i] : 0.f;
+                        if (r == j) sKK[r] = br * acc[m][i];
                     }
+                    *reinterpret_cast<f32x4*>(sA + r * kLdA + tj[m] * 16 + gq * 4) = val;
                 }
             }
         }
@@ -198,13 +201,18 @@ __global__ __launch_bounds__(kThreads) void k_intra(IntraArgs args) {
             Frag<float> tf;
             frag_row(tf, sT, kLdA, rt * 16 + ln, kb * 32);
             float fw[8], fu[8];
+            // slots 0..3: columns kb*32 + gq*4 + e; slots 4..7: 16 further
+            const f32x4 b0 = *reinterpret_cast<const f32x4*>(sBeta + kb * 32 + gq * 4);
+            const f32x4 b1 = *reinterpret_cast<const f32x4*>(sBeta + kb * 32 + 16 + gq * 4);
+            const f32x4 g0 = *reinterpret_cast<const f32x4*>(sGam + kb * 32 + gq * 4);
+            const f32x4 g1 = *reinterpret_cast<const f32x4*>(sGam + kb * 32 + 16 + gq * 4);
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const int j = kb * 32 + (e >> 2) * 16 + gq * 4 + (e & 3);
                 const float tv = e < 4 ? tf.lo[e] : tf.hi[e - 4];
-                const float bj = sBeta[j];
+                const float bj = e < 4 ? b0[e] : b1[e - 4];
+                const float gjv = e < 4 ? g0[e] : g1[e - 4];
                 fu[e] = tv * bj;
-                fw[e] = fu[e] * fast_exp(sGam[j]);
+                fw[e] = fu[e] * fast_exp(gjv);
             }
             if constexpr (sizeof(T) == 2) {
                 aw[kb].v = u32x4{pack_bf2(fw[0], fw[1]), pack_bf2(fw[2], fw[3]), pack_bf2(fw[4], fw[5]),

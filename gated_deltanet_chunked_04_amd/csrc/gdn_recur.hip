@@ -192,9 +192,7 @@ __device__ __forceinline__ void chunk_part1(const ChunkLds<T, K, RT>& L, const f
     // lane ends up with four consecutive value columns of one token row.
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            accD[rt][i] = Elem<T>::to_f(L.sU[(rt * 16 + gq * 4 + i) * C::LDU + wave * 16 + ln]);
+        accD[rt] = col4(L.sU, C::LDU, wave * 16 + ln, rt * 16);
         if (kOut) accO[rt] = zero4();
     }
 #pragma unroll
