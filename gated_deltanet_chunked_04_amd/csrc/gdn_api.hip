@@ -362,9 +362,10 @@ gdn_status run_intra(const gdn_desc* d, const Plan& p, unsigned char* ws, const 
 }
 
 gdn_status run_decide(const gdn_desc* d, const Plan& p, unsigned char* ws, int32_t* modes, hipStream_t st,
-                      int reverse = 0) {
+                      int reverse = 0, int32_t* modes_r = nullptr) {
     DecideArgs da{};
     da.reverse = reverse;
+    da.modes_r = modes_r;
     da.geo = make_geo(d, p, ws);
     da.cstat = reinterpret_cast<const float2*>(ws + p.o_cstat);
     da.modes = modes;
@@ -516,6 +517,15 @@ gdn_status gdn_chunk_bwd(const gdn_desc* desc, const void* q, const void* k, con
     // The forward states pass (2) and the reverse adjoint pass (3) read only what the intra
     // pass wrote and write disjoint workspace regions: (3) runs on a second stream, forked
     // from the caller's after (1) and joined to it before (4).
+    // both CP decisions (forward windows for the state pass, windows after each segment for
+    // the adjoint pass) in one launch ahead of the fork
+    int32_t* modes = reinterpret_cast<int32_t*>(ws + p.o_modes);
+    int32_t* modes_r = p.cp_on ? reinterpret_cast<int32_t*>(ws + p.o_modes_r) : nullptr;
+    if (p.cp_on) {
+        if (reuse) s = run_decide(desc, p, ws, modes_r, st, 1);
+        else s = run_decide(desc, p, ws, modes, st, 0, modes_r);
+        if (s != GDN_OK) return s;
+    }
     std::lock_guard<std::mutex> side_lock(side_mutex());
     SideStream side;
     if ((s = side_stream(st, side)) != GDN_OK) return s;
@@ -534,7 +544,6 @@ gdn_status gdn_chunk_bwd(const gdn_desc* desc, const void* q, const void* k, con
     ra.scale = desc->scale;
     ra.warmup = p.W;
     ra.use_cp = p.cp_on;
-    int32_t* modes = reinterpret_cast<int32_t*>(ws + p.o_modes);
     ra.modes = modes;
     ra.hstates = ws + p.o_h;
     ra.delta = ws + p.o_dl;
@@ -544,7 +553,6 @@ gdn_status gdn_chunk_bwd(const gdn_desc* desc, const void* q, const void* k, con
     } else if (p.cp_on) {
         float* seginit = reinterpret_cast<float*>(ws + p.o_seginit);
         float* prep = reinterpret_cast<float*>(ws + p.o_prep);
-        if ((s = run_decide(desc, p, ws, modes, st)) != GDN_OK) return s;
         ra.seginit_out = seginit;
         ra.prep = prep;
         GDN_LAUNCH(kKPrepass, st, launch_recur(ra, desc->dtype, kRecurPrepass, p.total_segs, vktiles, st));
@@ -579,10 +587,8 @@ gdn_status gdn_chunk_bwd(const gdn_desc* desc, const void* q, const void* k, con
     va.warmup = p.W;
     va.use_cp = p.cp_on;
     if (p.cp_on) {
-        int32_t* modes_r = reinterpret_cast<int32_t*>(ws + p.o_modes_r);
         float* seginit_r = reinterpret_cast<float*>(ws + p.o_seginit_r);
         float* prep_r = reinterpret_cast<float*>(ws + p.o_prep_r);
-        if ((s = run_decide(desc, p, ws, modes_r, st, 1)) != GDN_OK) return s;
         va.modes = modes_r;
         va.seginit_out = seginit_r;
         va.prep = prep_r;

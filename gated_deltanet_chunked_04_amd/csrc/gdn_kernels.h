@@ -177,6 +177,7 @@ struct DecideArgs {
     float log_eps;
     int32_t forced;  // 0 gate test, 1 warmup, 2 exact
     int32_t reverse; // 1: windows after each segment end (backward adjoint pass)
+    int32_t* modes_r;  // optional second output: the reverse decision, from the same launch
 };
 
 struct ScanArgs {

@@ -493,35 +493,41 @@ __global__ __launch_bounds__(kThreads) void k_decide(DecideArgs a) {
     int32_t nseg, nchunks;
     int64_t segoff, choff;
     seq_segs(a.geo, n, nseg, segoff, nchunks, choff);
-    int mode;
-    if (nseg <= 1) {
-        mode = 0;
-    } else if (a.forced) {
-        mode = a.forced;
-    } else {
-        bool ok = true;
-        for (int s = 1 + lane; s < nseg; s += 64) {
-            const int cb = s * a.geo.seg_len;  // first chunk of segment s
-            // forward: the W chunks before segment s; reverse: the W chunks after segment s-1
-            int w0 = cb - a.warmup, w1 = cb;
-            if (a.reverse) {
-                w0 = cb;
-                w1 = cb + a.warmup;
-                if (w1 >= nchunks) continue;  // window reaches the sequence end: exact
-            } else if (w0 <= 0) {
-                continue;  // window reaches the sequence start: exact
+    // a.modes gets the decision for a.reverse's direction; a.modes_r, if given, the reverse one
+    for (int dir = 0; dir < 2; ++dir) {
+        int32_t* out = dir == 0 ? a.modes : a.modes_r;
+        if (!out) continue;
+        const bool rev = dir == 0 ? a.reverse != 0 : true;
+        int mode;
+        if (nseg <= 1) {
+            mode = 0;
+        } else if (a.forced) {
+            mode = a.forced;
+        } else {
+            bool ok = true;
+            for (int s = 1 + lane; s < nseg; s += 64) {
+                const int cb = s * a.geo.seg_len;  // first chunk of segment s
+                // forward: the W chunks before segment s; reverse: the W chunks after segment s-1
+                int w0 = cb - a.warmup, w1 = cb;
+                if (rev) {
+                    w0 = cb;
+                    w1 = cb + a.warmup;
+                    if (w1 >= nchunks) continue;  // window reaches the sequence end: exact
+                } else if (w0 <= 0) {
+                    continue;  // window reaches the sequence start: exact
+                }
+                float sum = 0.f, kk = 0.f;
+                for (int m = w0; m < w1; ++m) {
+                    const float2 st = a.cstat[(choff + m) * H + h];
+                    sum += st.x;
+                    kk = fmaxf(kk, st.y);
+                }
+                ok = ok && (sum <= a.log_eps) && (kk <= 2.f);
             }
-            float sum = 0.f, kk = 0.f;
-            for (int m = w0; m < w1; ++m) {
-                const float2 st = a.cstat[(choff + m) * H + h];
-                sum += st.x;
-                kk = fmaxf(kk, st.y);
-            }
-            ok = ok && (sum <= a.log_eps) && (kk <= 2.f);
+            mode = __all(ok) ? 1 : 2;
         }
-        mode = __all(ok) ? 1 : 2;
+        if (lane == 0) out[p] = mode;
     }
-    if (lane == 0) a.modes[p] = mode;
 }
 
 // ---------------------------------------------------------------------------
