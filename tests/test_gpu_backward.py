@@ -193,3 +193,52 @@ def test_autograd_wrapper_keep_intermediates(gpu_lib):
         grads.append({n: x.grad for n, x in leaves.items()})
     for n in grads[0]:
         assert torch.equal(grads[0][n], grads[1][n]), n
+
+
+def test_backward_on_side_streams_and_threads(gpu_lib):
+    """The backward forks its reverse pass onto a library stream and joins it back to the
+    caller's: results on a non-default caller stream, and from two host threads calling at
+    once on two streams, equal the serial default-stream results bit for bit."""
+    import threading
+    gdn = gpu_lib
+    inps = [to_dev(with_grads(small_inputs(B=1, T=3000, H=2, K=128, V=128, dtype=torch.bfloat16, seed=s)))
+            for s in (21, 22)]
+    opts = dict(cp_mode="exact", seg_chunks=8)
+
+    def run(d):
+        return gdn.gdn_chunk_bwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["d_o"], d["initial_state"],
+                                 d["d_final_state"], **opts)
+
+    ref = [run(d) for d in inps]
+    torch.cuda.synchronize()
+    # a caller stream other than the default one; outputs read on that stream after the call
+    s1 = torch.cuda.Stream()
+    with torch.cuda.stream(s1):
+        got = run(inps[0])
+        copies = {n: got[n].clone() for n in NAMES}
+    s1.synchronize()
+    for n in NAMES:
+        assert torch.equal(copies[n], ref[0][n]), n
+    # two host threads, two streams, at once
+    outs = [None, None]
+    errs = []
+
+    def worker(i):
+        try:
+            st = torch.cuda.Stream()
+            with torch.cuda.stream(st):
+                o = run(inps[i])
+                outs[i] = {n: o[n].clone() for n in NAMES}
+            st.synchronize()
+        except Exception as e:  # surfaced below
+            errs.append(e)
+
+    th = [threading.Thread(target=worker, args=(i,)) for i in range(2)]
+    for x in th:
+        x.start()
+    for x in th:
+        x.join()
+    assert not errs, errs
+    for i in range(2):
+        for n in NAMES:
+            assert torch.equal(outs[i][n], ref[i][n]), (i, n)
