@@ -292,6 +292,15 @@ def main():
         "mfma_frac": round(tflops / peak_mfma, 4),
         "roofline": roofline,
         "kernels_us_per_step": {n: round(x["per_step_us"], 2) for n, x in kernels.items()},
+        # every kernel with a byte model against the HBM roofline (HIP-event launch durations;
+        # the backward's reverse chain runs beside its state chain on a second stream, so
+        # those durations include shared time, and k_intra's average mixes the forward launch
+        # with the backward's, which also writes T: priced here at the forward's bytes)
+        "kernels_roofline": {
+            n: {"avg_launch_us": round(kernels[n]["avg_us"], 2), "algorithmic_bytes": int(b),
+                "GB/s": round(b / (kernels[n]["avg_us"] * 1e-6) / 1e9, 1),
+                "frac": round(b / (kernels[n]["avg_us"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+            for n, b in counts["bytes"].items() if n in kernels},
     }
     if do_fwd:
         line["fwd"] = {"ms": round(ms_fwd, 4), "tokens_per_s": round(tokens / (ms_fwd * 1e-3), 1),

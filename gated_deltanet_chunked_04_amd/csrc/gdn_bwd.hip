@@ -397,11 +397,13 @@ __global__ __launch_bounds__(RT * 4) void k_reverse(RevArgs a) {
             if (row < V) {
                 store_state<K>(accG, P, row);
             } else if (row < V + K) {
+                // M^T in the input precision after the R rows, as the forward's prepass
                 const int i = row - V;
+                T* Mt = reinterpret_cast<T*>(P + VK);
 #pragma unroll
                 for (int kt = 0; kt < K / 16; ++kt)
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) P[VK + (size_t)(kt * 16 + gq * 4 + e) * K + i] = accG[kt][e];
+                    for (int e = 0; e < 4; ++e) Mt[(size_t)(kt * 16 + gq * 4 + e) * K + i] = Elem<T>::from_f(accG[kt][e]);
             }
         }
     } else if (sg.s == 0 && a.ds0) {

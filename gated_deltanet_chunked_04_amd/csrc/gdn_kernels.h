@@ -160,7 +160,8 @@ struct RecurArgs {
     float* sT;                // [N,H,V,K] or null
     const float* seginit;     // [total_segs,H,V,K] initial state of every segment (s >= 1)
     float* seginit_out;       // prepass: warmup states written here
-    float* prep;              // prepass: [total_segs,H,V+K,K] exact maps (R rows, then M^T)
+    float* prep;              // prepass: exact maps per [total_segs,H]: R rows [V][K] fp32, then M^T
+                              // [K][K] in the input precision, in a (V+K) x K fp32 slot
     const int32_t* modes;     // [N,H] 0 none, 1 warmup, 2 exact
     void* hstates;            // kRecurStates: [total_chunks,H,V,K] entry state of every chunk
     void* delta;              // kRecurStates: [Ttot,H,V] Delta = U - W S^T of every chunk, or null
@@ -200,7 +201,7 @@ struct RevArgs {
     float* ds0;               // [N,H,V,K] or null: gradient of the initial state
     const float* seginit;     // [total_segs,H,V,K] adjoint at the end of every segment but the last
     float* seginit_out;       // prepass: warmup adjoints written here
-    float* prep;              // prepass: [total_segs,H,V+K,K] reverse maps (R rows, then M^T)
+    float* prep;              // prepass: reverse maps, laid out as the forward's
     const int32_t* modes;
     void* gstates;            // [total_chunks,H,V,K] adjoint of the state leaving every chunk
     void* ddelta;             // kRecurOut: [Ttot,H,V] dL/dDelta of every chunk, or null

@@ -452,12 +452,14 @@ __global__ __launch_bounds__(RT * 4) void k_recur(RecurArgs a) {
             if (row < V) {
                 store_state<K>(accS, P, row);
             } else if (row < V + K) {
-                // M^T[k][i] at P + V*K + k*K + i, i = row - V
+                // M^T[k][i] at element k*K + i of a [K][K] matrix in the input precision (the
+                // scan's matrix-core operand precision) after the R rows, i = row - V
                 const int i = row - V;
+                T* Mt = reinterpret_cast<T*>(P + VK);
 #pragma unroll
                 for (int kt = 0; kt < K / 16; ++kt)
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) P[VK + (size_t)(kt * 16 + gq * 4 + e) * K + i] = accS[kt][e];
+                    for (int e = 0; e < 4; ++e) Mt[(size_t)(kt * 16 + gq * 4 + e) * K + i] = Elem<T>::from_f(accS[kt][e]);
             }
         }
     } else if (sg.s == sg.nseg - 1 && a.sT) {
@@ -539,7 +541,8 @@ template <typename T, int K, int RT>
 struct ScanCfg {
     static constexpr int NT = RT * 4;
     static constexpr int LDM = K + RPad<T>::row;
-    static constexpr int IM = (K * K / 4 + NT - 1) / NT;  // fp32x4 vectors of M^T per thread
+    static constexpr int VEC = Elem<T>::kVec;
+    static constexpr int IM = (K * K / VEC + NT - 1) / NT;  // 16-byte vectors of M^T per thread
     static constexpr int total = K * LDM * (int)sizeof(T);
 };
 
@@ -568,13 +571,16 @@ __global__ __launch_bounds__(RT * 4) void k_scan(ScanArgs a) {
         for (int kt = 0; kt < K / 16; ++kt) accS[kt] = zero4();
 
     // maps two steps ahead, in two register buffers that alternate
-    f32x4 mA[SC::IM], rA[K / 16], mB[SC::IM], rB[K / 16];
-    auto fetch = [&](f32x4 (&mreg)[SC::IM], f32x4 (&rreg)[K / 16], int s) {
+    u32x4 mA[SC::IM], mB[SC::IM];
+    f32x4 rA[K / 16], rB[K / 16];
+    auto fetch = [&](u32x4 (&mreg)[SC::IM], f32x4 (&rreg)[K / 16], int s) {
         const float* P = a.prep + ((size_t)(segoff + s) * H + h) * PS;
+        const T* Mt = reinterpret_cast<const T*>(P + VK);
 #pragma unroll
         for (int it = 0; it < SC::IM; ++it) {
             const int e = tid + it * SC::NT;
-            mreg[it] = e < K * K / 4 ? *reinterpret_cast<const f32x4*>(P + VK + (size_t)e * 4) : zero4();
+            mreg[it] = e < K * K / SC::VEC ? *reinterpret_cast<const u32x4*>(Mt + (size_t)e * SC::VEC)
+                                           : u32x4{0u, 0u, 0u, 0u};
         }
         load_state<K>(rreg, P, row);
     };
@@ -584,16 +590,16 @@ __global__ __launch_bounds__(RT * 4) void k_scan(ScanArgs a) {
     const int nsteps = nseg - 1;
     fetch(mA, rA, src_of(0));
     if (nsteps > 1) fetch(mB, rB, src_of(1));
-    auto one = [&](f32x4 (&mreg)[SC::IM], f32x4 (&rreg)[K / 16], int step) {
+    auto one = [&](u32x4 (&mreg)[SC::IM], f32x4 (&rreg)[K / 16], int step) {
         const int s = src_of(step);
         const int dst = a.reverse ? s - 1 : s + 1;
         lds_sync();
 #pragma unroll
         for (int it = 0; it < SC::IM; ++it) {
             const int e = tid + it * SC::NT;
-            if (e < K * K / 4) {
-                const int r = (e * 4) / K, cc = (e * 4) % K;
-                store4(sM + r * SC::LDM + cc, mreg[it]);
+            if (e < K * K / SC::VEC) {
+                const int r = (e * SC::VEC) / K, cc = (e * SC::VEC) % K;
+                *reinterpret_cast<u32x4*>(sM + r * SC::LDM + cc) = mreg[it];
             }
         }
         lds_sync();
