@@ -141,6 +141,33 @@ def test_backward_workload_16k(gpu_lib, cp):
     print(f"cp={cp} " + " ".join(f"{n}={e:.2e}" for n, e in errs.items()), flush=True)
 
 
+def test_backward_edge_prefill_32k(gpu_lib):
+    """The benchmarked step's backward: B=1, H=16, T=32768, bf16, AutoCP (on: 16 sub-sequences,
+    heads in warmup and exact modes), through the same calls bench.py times (the forward keeping
+    its workspace, the backward reusing it, and the recomputing backward); sampled heads against
+    the oracle, the two backwards bit for bit."""
+    import dataclasses
+    from gdn_inputs import WORKLOADS
+    gdn = gpu_lib
+    inp = make_inputs(dataclasses.replace(WORKLOADS["edge_prefill"], backward=True), seed=0)
+    d = to_dev(inp)
+    args = (d["q"], d["k"], d["v"], d["g"], d["beta"])
+    modes = gdn.gdn_cp_modes(d["k"], d["v"], d["g"], d["beta"]).cpu()
+    assert set(modes.flatten().tolist()) == {1, 2}, modes  # both CP kinds at this workload
+    ref = gdn.gdn_chunk_bwd(*args, d["d_o"], d["initial_state"], d["d_final_state"])
+    ws = gdn.gdn_workspace(d["q"], d["v"])
+    gdn.gdn_chunk_fwd(*args, d["initial_state"], workspace=ws, keep_for_backward=True)
+    got = gdn.gdn_chunk_bwd(*args, d["d_o"], d["initial_state"], d["d_final_state"], workspace=ws,
+                            reuse_forward=True)
+    torch.cuda.synchronize()
+    for n in NAMES:
+        assert torch.equal(got[n], ref[n]), n
+    # one warmup head and one exact head
+    heads = [int((modes[0] == 1).nonzero()[0]), int((modes[0] == 2).nonzero()[0])]
+    errs = compare({n: ref[n].cpu() for n in NAMES}, oracle_bwd(inp, heads=heads), 1e-2, heads=heads)
+    print(f"heads={heads} " + " ".join(f"{n}={e:.2e}" for n, e in errs.items()), flush=True)
+
+
 REUSE_CASES = [
     (torch.float32, 64, 64, "off", {}, None),
     (torch.float32, 64, 64, "exact", dict(seg_chunks=3), None),
