@@ -324,6 +324,9 @@ __global__ __launch_bounds__(RT * 4) void k_reverse(RevArgs a) {
             for (int i = 0; i < 4; ++i) accD[jt][i] *= fast_exp(Gm - gj[i]);
         }
         rev_fetch<1>(R, a, tn, cnn, h, dcol0);
+        // dO and the gate cumsum too: every chunk's loads land together in one burst across the
+        // chip, so the last piece needs most of a step to arrive
+        rev_fetch<2>(R, a, tn, cnn, h, dcol0);
         lds_sync();  // P^T complete
         if (has_do) {
 #pragma unroll
@@ -373,7 +376,6 @@ __global__ __launch_bounds__(RT * 4) void k_reverse(RevArgs a) {
                 for (int kt = 0; kt < K / 16; ++kt) mma(accG[kt], fq[kt], dof[jb]);
             }
         }
-        rev_fetch<2>(R, a, tn, cnn, h, dcol0);
     };
     if constexpr (kDepth == 2) {
         for (int ci = cend - 1; ci >= cbeg; ci -= 2) {
