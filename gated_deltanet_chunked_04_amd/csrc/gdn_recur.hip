@@ -424,10 +424,14 @@ __global__ __launch_bounds__(RT * 4) void k_recur(RecurArgs a) {
                 for (int i = 0; i < 4; ++i)
                     L.sQ[(rt * 16 + gq * 4 + i) * C::LDU + wave * 16 + ln] = Elem<T>::from_f(accD[rt][i]);
         }
-        if constexpr (MODE != kRecurStates) chunk_fetch<1>(R, a, tn, cnn, h, ucol0);
+        if constexpr (MODE != kRecurStates) {
+            // u and the gate cumsum too: every chunk's loads land together in one burst across
+            // the chip, so the last piece needs most of a step to arrive
+            chunk_fetch<1>(R, a, tn, cnn, h, ucol0);
+            chunk_fetch<2>(R, a, tn, cnn, h, ucol0);
+        }
         if (kOut) lds_sync();  // P tiles complete
         chunk_part2<T, K, RT, kOut>(a, L, accS, accD, accO, t0, c, h, vt * RT, okeep);
-        if constexpr (MODE != kRecurStates) chunk_fetch<2>(R, a, tn, cnn, h, ucol0);
     };
     if constexpr (kDepth == 2) {
         for (int ci = cbeg; ci < cend; ci += 2) {
