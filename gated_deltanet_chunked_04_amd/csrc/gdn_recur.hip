@@ -136,39 +136,64 @@ __device__ __forceinline__ void chunk_part1(const ChunkLds<T, K, RT>& L, const f
         frag_acc(sf[kb], accS[2 * kb], accS[2 * kb + 1]);
         frag_acc(nsf[kb], accS[2 * kb], accS[2 * kb + 1], -1.f);
     }
-    // Independent accumulators are updated side by side (k32 slice outer, tiles inner) and
-    // each slice's fragments are loaded before its products, so neither the matrix-core
-    // latency nor the LDS latency sits on a chain of dependent products.
-    if (kOut) {
-        // this wave's P tiles (rows r of Q, columns j of K), at most NPT of them
+    // bf16 with 128 state rows: one pass over the k32 slices serves the P tiles and O with the
+    // same Q fragments; elsewhere (more registers per fragment, or fewer waves) the P tiles
+    // take a pass of their own.
+    if constexpr (sizeof(T) == 2 && RT == 128) {
+        // This wave's P tiles (rows r of Q, columns j of K; at most NPT of them), Delta = U - W S^T
+        // (rows j of the chunk, columns = the wave's state rows) and the O^T tiles
+        // accO[rt][i] = O^T[v = wave*16 + gq*4 + i][r = rt*16 + ln] in one pass over the k32
+        // slices, so each slice's Q fragments serve both the P tiles and O. The S^T accumulators
+        // are an A fragment of S and the Delta accumulators an A fragment of Delta^T, so
+        // O^T = S Q^T diag(e^gam) + Delta^T P^T needs no data movement, and each lane ends up
+        // with four consecutive value columns of one token row.
         constexpr int NPT = (12 + C::NW - 1) / C::NW;
         f32x4 pacc[NPT];
         int prt[NPT], pjt[NPT];
         bool pon[NPT], pmm[NPT];
-#pragma unroll
+    #pragma unroll
         for (int m = 0; m < NPT; ++m) {
             const int idx = wave + m * C::NW;
-            pon[m] = idx < 12;
+            pon[m] = kOut && idx < 12;
             prt[m] = pon[m] ? tri_row(idx) : 0;
             pjt[m] = pon[m] ? tri_col(idx) : 0;
             pmm[m] = pon[m] && pjt[m] <= prt[m];
             pacc[m] = zero4();
         }
-#pragma unroll
+    #pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+            accD[rt] = col4(L.sU, C::LDU, wave * 16 + ln, rt * 16);
+            if (kOut) accO[rt] = zero4();
+        }
+    #pragma unroll
         for (int kb = 0; kb < K / 32; ++kb) {
-            Frag<T> fa[NPT], fb[NPT];
-#pragma unroll
+            Frag<T> fw[4], fq[4], fa[NPT];
+    #pragma unroll
+            for (int rt = 0; rt < 4; ++rt) {
+                frag_row(fw[rt], L.sW, C::LD, rt * 16 + ln, kb * 32);
+                if (kOut) frag_row(fq[rt], L.sQ, C::LD, rt * 16 + ln, kb * 32);
+            }
+    #pragma unroll
+            for (int m = 0; m < NPT; ++m)
+                if (pmm[m]) frag_row(fa[m], L.sK, C::LD, pjt[m] * 16 + ln, kb * 32);
+    #pragma unroll
+            for (int rt = 0; rt < 4; ++rt) {
+                mma(accD[rt], fw[rt], nsf[kb]);
+                if (kOut) mma(accO[rt], sf[kb], fq[rt]);
+            }
+    #pragma unroll
             for (int m = 0; m < NPT; ++m) {
                 if (pmm[m]) {
-                    frag_row(fa[m], L.sK, C::LD, pjt[m] * 16 + ln, kb * 32);
-                    frag_row(fb[m], L.sQ, C::LD, prt[m] * 16 + ln, kb * 32);
+                    // the Q rows of this tile: one of the slice's fragments above (wave-uniform pick)
+                    Frag<T> fb = fq[0];
+                    if (prt[m] == 1) fb = fq[1];
+                    if (prt[m] == 2) fb = fq[2];
+                    if (prt[m] == 3) fb = fq[3];
+                    mma(pacc[m], fa[m], fb);
                 }
             }
-#pragma unroll
-            for (int m = 0; m < NPT; ++m)
-                if (pmm[m]) mma(pacc[m], fa[m], fb[m]);
         }
-#pragma unroll
+    #pragma unroll
         for (int m = 0; m < NPT; ++m) {
             if (pon[m]) {
                 // pacc[i] = (Q K^T)[r = rt*16+ln][j = jt*16+gq*4+i]
@@ -176,7 +201,7 @@ __device__ __forceinline__ void chunk_part1(const ChunkLds<T, K, RT>& L, const f
                 const float gr = L.sGam[r];
                 const f32x4 gj = *reinterpret_cast<const f32x4*>(L.sGam + pjt[m] * 16 + gq * 4);
                 f32x4 v;
-#pragma unroll
+    #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int j = pjt[m] * 16 + gq * 4 + i;
                     v[i] = (j <= r) ? pacc[m][i] * fast_exp(gr - gj[i]) : 0.f;
@@ -184,29 +209,79 @@ __device__ __forceinline__ void chunk_part1(const ChunkLds<T, K, RT>& L, const f
                 store4(L.sPm + r * C::LDP + pjt[m] * 16 + gq * 4, v);
             }
         }
-    }
-    // Delta = U - W S^T  (rows j of the chunk, columns = the wave's state rows), and
-    // O^T tiles: accO[rt][i] = O^T[v = wave*16 + gq*4 + i][r = rt*16 + ln]. The S^T
-    // accumulators are an A fragment of S and the Delta accumulators an A fragment of
-    // Delta^T, so O^T = S Q^T diag(e^gam) + Delta^T P^T needs no data movement, and each
-    // lane ends up with four consecutive value columns of one token row.
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt) {
-        accD[rt] = col4(L.sU, C::LDU, wave * 16 + ln, rt * 16);
-        if (kOut) accO[rt] = zero4();
-    }
-#pragma unroll
-    for (int kb = 0; kb < K / 32; ++kb) {
-        Frag<T> fw[4], fq[4];
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt) {
-            frag_row(fw[rt], L.sW, C::LD, rt * 16 + ln, kb * 32);
-            if (kOut) frag_row(fq[rt], L.sQ, C::LD, rt * 16 + ln, kb * 32);
+    } else {
+        // Independent accumulators are updated side by side (k32 slice outer, tiles inner) and
+        // each slice's fragments are loaded before its products, so neither the matrix-core
+        // latency nor the LDS latency sits on a chain of dependent products.
+        if (kOut) {
+            // this wave's P tiles (rows r of Q, columns j of K), at most NPT of them
+            constexpr int NPT = (12 + C::NW - 1) / C::NW;
+            f32x4 pacc[NPT];
+            int prt[NPT], pjt[NPT];
+            bool pon[NPT], pmm[NPT];
+    #pragma unroll
+            for (int m = 0; m < NPT; ++m) {
+                const int idx = wave + m * C::NW;
+                pon[m] = idx < 12;
+                prt[m] = pon[m] ? tri_row(idx) : 0;
+                pjt[m] = pon[m] ? tri_col(idx) : 0;
+                pmm[m] = pon[m] && pjt[m] <= prt[m];
+                pacc[m] = zero4();
+            }
+    #pragma unroll
+            for (int kb = 0; kb < K / 32; ++kb) {
+                Frag<T> fa[NPT], fb[NPT];
+    #pragma unroll
+                for (int m = 0; m < NPT; ++m) {
+                    if (pmm[m]) {
+                        frag_row(fa[m], L.sK, C::LD, pjt[m] * 16 + ln, kb * 32);
+                        frag_row(fb[m], L.sQ, C::LD, prt[m] * 16 + ln, kb * 32);
+                    }
+                }
+    #pragma unroll
+                for (int m = 0; m < NPT; ++m)
+                    if (pmm[m]) mma(pacc[m], fa[m], fb[m]);
+            }
+    #pragma unroll
+            for (int m = 0; m < NPT; ++m) {
+                if (pon[m]) {
+                    // pacc[i] = (Q K^T)[r = rt*16+ln][j = jt*16+gq*4+i]
+                    const int r = prt[m] * 16 + ln;
+                    const float gr = L.sGam[r];
+                    const f32x4 gj = *reinterpret_cast<const f32x4*>(L.sGam + pjt[m] * 16 + gq * 4);
+                    f32x4 v;
+    #pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int j = pjt[m] * 16 + gq * 4 + i;
+                        v[i] = (j <= r) ? pacc[m][i] * fast_exp(gr - gj[i]) : 0.f;
+                    }
+                    store4(L.sPm + r * C::LDP + pjt[m] * 16 + gq * 4, v);
+                }
+            }
         }
-#pragma unroll
+        // Delta = U - W S^T  (rows j of the chunk, columns = the wave's state rows), and
+        // O^T tiles: accO[rt][i] = O^T[v = wave*16 + gq*4 + i][r = rt*16 + ln]. The S^T
+        // accumulators are an A fragment of S and the Delta accumulators an A fragment of
+        // Delta^T, so O^T = S Q^T diag(e^gam) + Delta^T P^T needs no data movement, and each
+        // lane ends up with four consecutive value columns of one token row.
+    #pragma unroll
         for (int rt = 0; rt < 4; ++rt) {
-            mma(accD[rt], fw[rt], nsf[kb]);
-            if (kOut) mma(accO[rt], sf[kb], fq[rt]);
+            accD[rt] = col4(L.sU, C::LDU, wave * 16 + ln, rt * 16);
+            if (kOut) accO[rt] = zero4();
+        }
+    #pragma unroll
+        for (int kb = 0; kb < K / 32; ++kb) {
+            Frag<T> fw[4], fq[4];
+    #pragma unroll
+            for (int rt = 0; rt < 4; ++rt) {
+                frag_row(fw[rt], L.sW, C::LD, rt * 16 + ln, kb * 32);
+                if (kOut) frag_row(fq[rt], L.sQ, C::LD, rt * 16 + ln, kb * 32);
+            }
+    #pragma unroll
+            for (int rt = 0; rt < 4; ++rt) {
+                mma(accD[rt], fw[rt], nsf[kb]);
+                if (kOut) mma(accO[rt], sf[kb], fq[rt]);
+            }
         }
     }
     if (kOut) {
