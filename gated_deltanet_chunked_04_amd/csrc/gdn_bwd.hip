@@ -258,35 +258,50 @@ __global__ __launch_bounds__(RT * 4) void k_reverse(RevArgs a) {
         Frag<T> gf[K / 32];
 #pragma unroll
         for (int kb = 0; kb < K / 32; ++kb) frag_acc(gf[kb], accG[2 * kb], accG[2 * kb + 1]);
-        // Independent accumulators are updated side by side (k32 slice outer, tiles inner)
-        // and each slice's fragments are loaded before its products.
-        if (has_do) {
-            // P^T[j][r] = e^{gam_r - gam_j} (Q K^T)[r][j] for r >= j, staged row-major by j
+        const float Gm = L.sGam[63];
+        f32x4 accD[4];
+#pragma unroll
+        for (int jt = 0; jt < 4; ++jt) accD[jt] = zero4();
+        if constexpr (sizeof(T) == 2 && RT == 128) {
+            // P^T[j][r] = e^{gam_r - gam_j} (Q K^T)[r][j] for r >= j (this wave's tiles, staged
+            // row-major by j; none for the M rows of the exact prepass) and the Kt G^T part of the
+            // dDelta tiles (rows j, columns = the wave's adjoint rows). Independent accumulators are
+            // updated side by side (k32 slice outer, tiles inner) and each slice's fragments are
+            // loaded before its products.
             f32x4 pacc[NPT];
             int prt[NPT], pjt[NPT];
             bool pon[NPT], pmm[NPT];
 #pragma unroll
             for (int m = 0; m < NPT; ++m) {
                 const int idx = wave + m * C::NW;
-                pon[m] = idx < 12;
+                pon[m] = has_do && idx < 12;
                 prt[m] = pon[m] ? tri_row(idx) : 0;
                 pjt[m] = pon[m] ? tri_col(idx) : 0;
                 pmm[m] = pon[m] && pjt[m] <= prt[m];
                 pacc[m] = zero4();
             }
+            // bf16 with 128 adjoint rows: the P^T tiles take their K rows from the same k32
+            // fragments as dDelta, in one pass
 #pragma unroll
             for (int kb = 0; kb < K / 32; ++kb) {
-                Frag<T> fa[NPT], fb[NPT];
+                Frag<T> fk[4], fq[NPT];
+#pragma unroll
+                for (int jt = 0; jt < 4; ++jt) frag_row(fk[jt], L.sK, C::LD, jt * 16 + ln, kb * 32);
+#pragma unroll
+                for (int m = 0; m < NPT; ++m)
+                    if (pmm[m]) frag_row(fq[m], L.sQ, C::LD, prt[m] * 16 + ln, kb * 32);
+#pragma unroll
+                for (int jt = 0; jt < 4; ++jt) mma(accD[jt], fk[jt], gf[kb]);
 #pragma unroll
                 for (int m = 0; m < NPT; ++m) {
                     if (pmm[m]) {
-                        frag_row(fa[m], L.sQ, C::LD, prt[m] * 16 + ln, kb * 32);
-                        frag_row(fb[m], L.sK, C::LD, pjt[m] * 16 + ln, kb * 32);
+                        Frag<T> fb = fk[0];  // wave-uniform pick of the tile's K rows
+                        if (pjt[m] == 1) fb = fk[1];
+                        if (pjt[m] == 2) fb = fk[2];
+                        if (pjt[m] == 3) fb = fk[3];
+                        mma(pacc[m], fq[m], fb);  // lane holds [r = rt*16+gq*4+i][j = jt*16+ln]
                     }
                 }
-#pragma unroll
-                for (int m = 0; m < NPT; ++m)
-                    if (pmm[m]) mma(pacc[m], fa[m], fb[m]);  // lane holds [r = rt*16+gq*4+i][j = jt*16+ln]
             }
 #pragma unroll
             for (int m = 0; m < NPT; ++m) {
@@ -303,19 +318,62 @@ __global__ __launch_bounds__(RT * 4) void k_reverse(RevArgs a) {
                     store4(L.sPm + j * C::LDP + prt[m] * 16 + gq * 4, v);
                 }
             }
-        }
-        // dDelta tiles (rows j, columns = the wave's adjoint rows): Kt G^T part
-        const float Gm = L.sGam[63];
-        f32x4 accD[4];
+        } else {
+            // Independent accumulators are updated side by side (k32 slice outer, tiles inner)
+            // and each slice's fragments are loaded before its products.
+            if (has_do) {
+                // P^T[j][r] = e^{gam_r - gam_j} (Q K^T)[r][j] for r >= j, staged row-major by j
+                f32x4 pacc[NPT];
+                int prt[NPT], pjt[NPT];
+                bool pon[NPT], pmm[NPT];
 #pragma unroll
-        for (int jt = 0; jt < 4; ++jt) accD[jt] = zero4();
+                for (int m = 0; m < NPT; ++m) {
+                    const int idx = wave + m * C::NW;
+                    pon[m] = idx < 12;
+                    prt[m] = pon[m] ? tri_row(idx) : 0;
+                    pjt[m] = pon[m] ? tri_col(idx) : 0;
+                    pmm[m] = pon[m] && pjt[m] <= prt[m];
+                    pacc[m] = zero4();
+                }
 #pragma unroll
-        for (int kb = 0; kb < K / 32; ++kb) {
-            Frag<T> fa[4];
+                for (int kb = 0; kb < K / 32; ++kb) {
+                    Frag<T> fa[NPT], fb[NPT];
 #pragma unroll
-            for (int jt = 0; jt < 4; ++jt) frag_row(fa[jt], L.sK, C::LD, jt * 16 + ln, kb * 32);
+                    for (int m = 0; m < NPT; ++m) {
+                        if (pmm[m]) {
+                            frag_row(fa[m], L.sQ, C::LD, prt[m] * 16 + ln, kb * 32);
+                            frag_row(fb[m], L.sK, C::LD, pjt[m] * 16 + ln, kb * 32);
+                        }
+                    }
 #pragma unroll
-            for (int jt = 0; jt < 4; ++jt) mma(accD[jt], fa[jt], gf[kb]);
+                    for (int m = 0; m < NPT; ++m)
+                        if (pmm[m]) mma(pacc[m], fa[m], fb[m]);  // lane holds [r = rt*16+gq*4+i][j = jt*16+ln]
+                }
+#pragma unroll
+                for (int m = 0; m < NPT; ++m) {
+                    if (pon[m]) {
+                        const int j = pjt[m] * 16 + ln;
+                        const float gj = L.sGam[j];
+                        const f32x4 gr = *reinterpret_cast<const f32x4*>(L.sGam + prt[m] * 16 + gq * 4);
+                        f32x4 v;
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const int r = prt[m] * 16 + gq * 4 + i;
+                            v[i] = (r >= j) ? a.scale * pacc[m][i] * fast_exp(gr[i] - gj) : 0.f;
+                        }
+                        store4(L.sPm + j * C::LDP + prt[m] * 16 + gq * 4, v);
+                    }
+                }
+            }
+            // dDelta tiles (rows j, columns = the wave's adjoint rows): Kt G^T part
+#pragma unroll
+            for (int kb = 0; kb < K / 32; ++kb) {
+                Frag<T> fa[4];
+#pragma unroll
+                for (int jt = 0; jt < 4; ++jt) frag_row(fa[jt], L.sK, C::LD, jt * 16 + ln, kb * 32);
+#pragma unroll
+                for (int jt = 0; jt < 4; ++jt) mma(accD[jt], fa[jt], gf[kb]);
+            }
         }
 #pragma unroll
         for (int jt = 0; jt < 4; ++jt) {
@@ -324,9 +382,10 @@ __global__ __launch_bounds__(RT * 4) void k_reverse(RevArgs a) {
             for (int i = 0; i < 4; ++i) accD[jt][i] *= fast_exp(Gm - gj[i]);
         }
         rev_fetch<1>(R, a, tn, cnn, h, dcol0);
-        // dO and the gate cumsum too: every chunk's loads land together in one burst across the
-        // chip, so the last piece needs most of a step to arrive
-        rev_fetch<2>(R, a, tn, cnn, h, dcol0);
+        // bf16: dO and the gate cumsum too (every chunk's loads land together in one burst
+        // across the chip, so the last piece needs most of a step to arrive); fp32, whose
+        // operands take twice the registers, at the end of the step
+        if constexpr (sizeof(T) == 2) rev_fetch<2>(R, a, tn, cnn, h, dcol0);
         lds_sync();  // P^T complete
         if (has_do) {
 #pragma unroll
@@ -376,6 +435,7 @@ __global__ __launch_bounds__(RT * 4) void k_reverse(RevArgs a) {
                 for (int kt = 0; kt < K / 16; ++kt) mma(accG[kt], fq[kt], dof[jb]);
             }
         }
+        if constexpr (sizeof(T) != 2) rev_fetch<2>(R, a, tn, cnn, h, dcol0);
     };
     if constexpr (kDepth == 2) {
         for (int ci = cend - 1; ci >= cbeg; ci -= 2) {

@@ -151,7 +151,7 @@ __device__ __forceinline__ void chunk_part1(const ChunkLds<T, K, RT>& L, const f
         f32x4 pacc[NPT];
         int prt[NPT], pjt[NPT];
         bool pon[NPT], pmm[NPT];
-    #pragma unroll
+#pragma unroll
         for (int m = 0; m < NPT; ++m) {
             const int idx = wave + m * C::NW;
             pon[m] = kOut && idx < 12;
@@ -160,28 +160,28 @@ __device__ __forceinline__ void chunk_part1(const ChunkLds<T, K, RT>& L, const f
             pmm[m] = pon[m] && pjt[m] <= prt[m];
             pacc[m] = zero4();
         }
-    #pragma unroll
+#pragma unroll
         for (int rt = 0; rt < 4; ++rt) {
             accD[rt] = col4(L.sU, C::LDU, wave * 16 + ln, rt * 16);
             if (kOut) accO[rt] = zero4();
         }
-    #pragma unroll
+#pragma unroll
         for (int kb = 0; kb < K / 32; ++kb) {
             Frag<T> fw[4], fq[4], fa[NPT];
-    #pragma unroll
+#pragma unroll
             for (int rt = 0; rt < 4; ++rt) {
                 frag_row(fw[rt], L.sW, C::LD, rt * 16 + ln, kb * 32);
                 if (kOut) frag_row(fq[rt], L.sQ, C::LD, rt * 16 + ln, kb * 32);
             }
-    #pragma unroll
+#pragma unroll
             for (int m = 0; m < NPT; ++m)
                 if (pmm[m]) frag_row(fa[m], L.sK, C::LD, pjt[m] * 16 + ln, kb * 32);
-    #pragma unroll
+#pragma unroll
             for (int rt = 0; rt < 4; ++rt) {
                 mma(accD[rt], fw[rt], nsf[kb]);
                 if (kOut) mma(accO[rt], sf[kb], fq[rt]);
             }
-    #pragma unroll
+#pragma unroll
             for (int m = 0; m < NPT; ++m) {
                 if (pmm[m]) {
                     // the Q rows of this tile: one of the slice's fragments above (wave-uniform pick)
@@ -193,7 +193,7 @@ __device__ __forceinline__ void chunk_part1(const ChunkLds<T, K, RT>& L, const f
                 }
             }
         }
-    #pragma unroll
+#pragma unroll
         for (int m = 0; m < NPT; ++m) {
             if (pon[m]) {
                 // pacc[i] = (Q K^T)[r = rt*16+ln][j = jt*16+gq*4+i]
@@ -201,7 +201,7 @@ __device__ __forceinline__ void chunk_part1(const ChunkLds<T, K, RT>& L, const f
                 const float gr = L.sGam[r];
                 const f32x4 gj = *reinterpret_cast<const f32x4*>(L.sGam + pjt[m] * 16 + gq * 4);
                 f32x4 v;
-    #pragma unroll
+#pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int j = pjt[m] * 16 + gq * 4 + i;
                     v[i] = (j <= r) ? pacc[m][i] * fast_exp(gr - gj[i]) : 0.f;
@@ -219,7 +219,7 @@ __device__ __forceinline__ void chunk_part1(const ChunkLds<T, K, RT>& L, const f
             f32x4 pacc[NPT];
             int prt[NPT], pjt[NPT];
             bool pon[NPT], pmm[NPT];
-    #pragma unroll
+#pragma unroll
             for (int m = 0; m < NPT; ++m) {
                 const int idx = wave + m * C::NW;
                 pon[m] = idx < 12;
@@ -228,21 +228,21 @@ __device__ __forceinline__ void chunk_part1(const ChunkLds<T, K, RT>& L, const f
                 pmm[m] = pon[m] && pjt[m] <= prt[m];
                 pacc[m] = zero4();
             }
-    #pragma unroll
+#pragma unroll
             for (int kb = 0; kb < K / 32; ++kb) {
                 Frag<T> fa[NPT], fb[NPT];
-    #pragma unroll
+#pragma unroll
                 for (int m = 0; m < NPT; ++m) {
                     if (pmm[m]) {
                         frag_row(fa[m], L.sK, C::LD, pjt[m] * 16 + ln, kb * 32);
                         frag_row(fb[m], L.sQ, C::LD, prt[m] * 16 + ln, kb * 32);
                     }
                 }
-    #pragma unroll
+#pragma unroll
                 for (int m = 0; m < NPT; ++m)
                     if (pmm[m]) mma(pacc[m], fa[m], fb[m]);
             }
-    #pragma unroll
+#pragma unroll
             for (int m = 0; m < NPT; ++m) {
                 if (pon[m]) {
                     // pacc[i] = (Q K^T)[r = rt*16+ln][j = jt*16+gq*4+i]
@@ -250,7 +250,7 @@ __device__ __forceinline__ void chunk_part1(const ChunkLds<T, K, RT>& L, const f
                     const float gr = L.sGam[r];
                     const f32x4 gj = *reinterpret_cast<const f32x4*>(L.sGam + pjt[m] * 16 + gq * 4);
                     f32x4 v;
-    #pragma unroll
+#pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         const int j = pjt[m] * 16 + gq * 4 + i;
                         v[i] = (j <= r) ? pacc[m][i] * fast_exp(gr - gj[i]) : 0.f;
@@ -264,20 +264,20 @@ __device__ __forceinline__ void chunk_part1(const ChunkLds<T, K, RT>& L, const f
         // accumulators are an A fragment of S and the Delta accumulators an A fragment of
         // Delta^T, so O^T = S Q^T diag(e^gam) + Delta^T P^T needs no data movement, and each
         // lane ends up with four consecutive value columns of one token row.
-    #pragma unroll
+#pragma unroll
         for (int rt = 0; rt < 4; ++rt) {
             accD[rt] = col4(L.sU, C::LDU, wave * 16 + ln, rt * 16);
             if (kOut) accO[rt] = zero4();
         }
-    #pragma unroll
+#pragma unroll
         for (int kb = 0; kb < K / 32; ++kb) {
             Frag<T> fw[4], fq[4];
-    #pragma unroll
+#pragma unroll
             for (int rt = 0; rt < 4; ++rt) {
                 frag_row(fw[rt], L.sW, C::LD, rt * 16 + ln, kb * 32);
                 if (kOut) frag_row(fq[rt], L.sQ, C::LD, rt * 16 + ln, kb * 32);
             }
-    #pragma unroll
+#pragma unroll
             for (int rt = 0; rt < 4; ++rt) {
                 mma(accD[rt], fw[rt], nsf[kb]);
                 if (kOut) mma(accO[rt], sf[kb], fq[rt]);
