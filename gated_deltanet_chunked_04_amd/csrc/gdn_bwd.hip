@@ -488,16 +488,18 @@ hipError_t launch_reverse_t(const RevArgs& a, int64_t nsegs_grid, int vtiles, hi
 
 // ---------------------------------------------------------------------------
 // Per-chunk gradients: the state side, then the WY side, in one kernel. A persistent
-// workgroup (4 waves, one per CU) walks the (chunk, head) tasks; the next task's operands
+// workgroup (8 waves, one per CU) walks the (chunk, head) tasks; the next task's operands
 // travel into registers while the current task computes, so HBM traffic overlaps the
 // work instead of alternating with it.
 //
 // Delta = U - W S^T comes from the state pass and dDelta (= dU) from the reverse pass,
 // both of which form them anyway; with them, every state-side product contracts over
 // the value dimension:
-//   dQt = dO S, dW = -dDelta S     (S read as column slices: wave w owns k in [K/4 w, K/4 (w+1)))
-//   dKt = Delta G, dP = dO Delta^T (wave w owns chunk rows r = 16w .. 16w+15)
-// so no partial sums cross waves and S is read from LDS once per task. Most tiles are
+//   dQt = dO S, dW = -dDelta S     (S read as column slices: waves w, w+4 own k in
+//                                   [K/4 w, K/4 (w+1)) and split the chunk-row tiles)
+//   dKt = Delta G, dP = dO Delta^T (waves w, w+4 own chunk rows r = 16w .. 16w+15 and split
+//                                   the tiles along the other dimension)
+// so no partial sums over k cross waves. Most tiles are
 // held transposed (rows over k or chunk rows, columns over r), which makes them A
 // fragments of their transposes and lets every lane write four consecutive columns of
 // its row with one vector store.

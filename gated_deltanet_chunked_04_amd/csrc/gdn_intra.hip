@@ -14,7 +14,8 @@
 // S_t = exp(g_t) S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T: inside a chunk the
 // per-token corrections delta_r = beta_r (v_r - S'_r k_r) solve (I + A) Delta = U - W S^T.
 //
-// One workgroup (4 waves) per (chunk, head). K and V are staged row-major in LDS; T*K
+// Persistent workgroups of 4 waves, two per CU, each taking one (chunk, head) at a time.
+// K and V are staged row-major in LDS; T*K
 // and T*V read their columns with LDS transpose loads. The inverse is blocked:
 // 16x16 diagonal blocks by forward substitution, then off-diagonal blocks level by
 // level with fp32 matrix-core products. T stays fp32; the products T*K and T*V run on

@@ -20,8 +20,8 @@
 //     M matrix"); then scan S_{s+1} = S_s M_s + R~_s across segments.
 // A per sequence-head decision kernel picks between them from the chunk gate totals.
 //
-// Workgroup layout: 256 threads = 4 waves; a workgroup owns 64 value rows of one
-// sequence-head segment, wave w owns 16 of them. The state is kept in registers as
+// Workgroup layout: a workgroup owns RT value rows of one sequence-head segment (128 rows,
+// 8 waves, at V = K = 128; 64 rows, 4 waves, otherwise), wave w owns 16 of them. The state is kept in registers as
 // fp32 accumulator tiles of S^T (K/16 tiles per wave), which feed the matrix cores
 // directly as B operands (see gdn_common.h); it is never written to LDS.
 #include "gdn_common.h"
