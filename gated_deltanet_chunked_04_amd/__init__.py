@@ -148,8 +148,9 @@ def gdn_chunk_fwd(q, k, v, g, beta, initial_state=None, *, scale=1.0, cu_seqlens
     """Forward. Returns (o, final_state or None). Runs on the current stream.
 
     keep_for_backward=True leaves the intra-chunk results (gate cumsum, W, U, T), the CP
-    decisions and the sub-sequence entry states in `workspace` (required; see gdn_workspace),
-    so that gdn_chunk_bwd(reuse_forward=True) on the same inputs and options skips recomputing them.
+    decisions, the sub-sequence entry states, every chunk's entry state and Delta in `workspace`
+    (required; see gdn_workspace), so that gdn_chunk_bwd(reuse_forward=True) on the same inputs
+    and options skips recomputing them.
     """
     N = _num_seqs(q, cu_seqlens)
     _check_inputs(q, k, v, g, beta, initial_state, N)
@@ -294,8 +295,9 @@ def chunk_gated_delta_rule(q, k, v, g, beta, scale: float = 1.0, initial_state=N
 
     q, k: [B,T,H,K]; v: [B,T,H,V] (bf16 or fp32); g (natural-log decay) and beta: [B,T,H] fp32;
     initial_state: [N,H,V,K] fp32 or None; cu_seqlens: int32 [N+1] device tensor (B must be 1).
-    keep_intermediates=True holds the forward's workspace (W, U, T, gate cumsum, CP entry states)
-    until the backward, which then skips recomputing them: more memory, less backward time.
+    keep_intermediates=True holds the forward's workspace (W, U, T, gate cumsum, CP entry states,
+    chunk states and Delta) until the backward, which then skips recomputing them: more memory,
+    less backward time.
     """
     o, sT = _GDNFunction.apply(q, k, v, g, beta, initial_state, scale, cu_seqlens, cp_mode,
                                bool(keep_intermediates and torch.is_grad_enabled()

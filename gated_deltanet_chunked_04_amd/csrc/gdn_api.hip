@@ -172,9 +172,12 @@ gdn_status make_plan(const gdn_desc* d, Plan& p) {
         p.o_seginit = take((size_t)p.total_segs * H * V * K * 4);
         p.o_prep = take((size_t)p.total_segs * H * (V + K) * K * 4);
     }
-    // T = (I + A)^{-1} per chunk: written by the forward when it keeps its intermediates,
-    // always by the backward (which reads it); the same offset in both layouts
+    // T = (I + A)^{-1} per chunk, the chunk-entry states h and Delta = U - W S^T: written by
+    // the forward when it keeps its intermediates, always by the backward (which reads them);
+    // the same offsets in both layouts
     p.o_tm = take((size_t)p.total_chunks * H * 64 * 64 * p.esize);
+    p.o_h = take((size_t)p.total_chunks * H * V * K * p.esize);
+    p.o_dl = take(T * H * V * p.esize);
     p.fwd_bytes = std::max<size_t>((d->flags & GDN_FLAG_KEEP_FORWARD) ? off : p.o_tm, kAlign);
     // backward workspace continues after the forward's
     if (p.cp_on) {
@@ -182,9 +185,7 @@ gdn_status make_plan(const gdn_desc* d, Plan& p) {
         p.o_seginit_r = take((size_t)p.total_segs * H * V * K * 4);
         p.o_prep_r = take((size_t)p.total_segs * H * (V + K) * K * 4);
     }
-    p.o_h = take((size_t)p.total_chunks * H * V * K * p.esize);
     p.o_gst = take((size_t)p.total_chunks * H * V * K * p.esize);
-    p.o_dl = take(T * H * V * p.esize);
     p.o_ddl = take(T * H * V * p.esize);
     p.bwd_bytes = std::max<size_t>(off, kAlign);
     p.bwd_ok = (d->dtype == GDN_DTYPE_BF16) || (d->K == 64 && d->V == 64);
@@ -477,7 +478,13 @@ gdn_status gdn_chunk_fwd(const gdn_desc* desc, const void* q, const void* k, con
         GDN_LAUNCH(kKScan, st, launch_scan(sa, desc->dtype, st));
         ra.seginit = seginit;
     }
-    GDN_LAUNCH(kKRecurOut, st, launch_recur(ra, desc->dtype, kRecurOut, p.total_segs,
+    // a forward that keeps its intermediates also records h and Delta (where a backward exists)
+    const bool rec = (desc->flags & GDN_FLAG_KEEP_FORWARD) && p.bwd_ok;
+    if (rec) {
+        ra.hstates = ws + p.o_h;
+        ra.delta = ws + p.o_dl;
+    }
+    GDN_LAUNCH(kKRecurOut, st, launch_recur(ra, desc->dtype, rec ? kRecurOutRec : kRecurOut, p.total_segs,
                                             (int)(desc->V / recur_rows((int)desc->V, (int)desc->K)), st));
     return GDN_OK;
 }
@@ -532,7 +539,7 @@ gdn_status gdn_chunk_bwd(const gdn_desc* desc, const void* q, const void* k, con
     hipStream_t st2 = side.s;
     if (hipEventRecord(side.fork, st) != hipSuccess || hipStreamWaitEvent(st2, side.fork, 0) != hipSuccess)
         return GDN_ERR_HIP;
-    // 2. chunk-entry states, with the forward's CP
+    // 2. chunk-entry states and Delta, with the forward's CP (kept by the forward when reused)
     RecurArgs ra{};
     memset(&ra, 0, sizeof(ra));
     ra.geo = make_geo(desc, p, ws);
@@ -547,10 +554,7 @@ gdn_status gdn_chunk_bwd(const gdn_desc* desc, const void* q, const void* k, con
     ra.modes = modes;
     ra.hstates = ws + p.o_h;
     ra.delta = ws + p.o_dl;
-    if (p.cp_on && reuse) {
-        // the forward's CP decisions and sub-sequence entry states
-        ra.seginit = reinterpret_cast<float*>(ws + p.o_seginit);
-    } else if (p.cp_on) {
+    if (!reuse && p.cp_on) {
         float* seginit = reinterpret_cast<float*>(ws + p.o_seginit);
         float* prep = reinterpret_cast<float*>(ws + p.o_prep);
         ra.seginit_out = seginit;
@@ -566,7 +570,7 @@ gdn_status gdn_chunk_bwd(const gdn_desc* desc, const void* q, const void* k, con
         GDN_LAUNCH(kKScan, st, launch_scan(sa, desc->dtype, st));
         ra.seginit = seginit;
     }
-    GDN_LAUNCH(kKRecurStates, st, launch_recur(ra, desc->dtype, kRecurStates, p.total_segs, vtiles, st));
+    if (!reuse) GDN_LAUNCH(kKRecurStates, st, launch_recur(ra, desc->dtype, kRecurStates, p.total_segs, vtiles, st));
     // 3. reverse adjoint pass, with CP mirrored (windows and scan from the sequence end)
     const gdn_status sr = [&]() -> gdn_status {
     gdn_status s = GDN_OK;

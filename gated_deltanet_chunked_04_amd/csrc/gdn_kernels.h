@@ -145,7 +145,8 @@ struct IntraArgs {
 enum RecurMode : int {
     kRecurOut = 0,      // outputs O (and the final state) for each segment
     kRecurPrepass = 1,  // CP preprocessing: warmup windows and exact (R, M) segment maps
-    kRecurStates = 2    // chunk-entry states for the backward (h), no output
+    kRecurStates = 2,   // chunk-entry states for the backward (h), no output
+    kRecurOutRec = 3    // the output pass recording h and Delta too (a forward that keeps them)
 };
 
 struct RecurArgs {
@@ -163,8 +164,8 @@ struct RecurArgs {
     float* prep;              // prepass: exact maps per [total_segs,H]: R rows [V][K] fp32, then M^T
                               // [K][K] in the input precision, in a (V+K) x K fp32 slot
     const int32_t* modes;     // [N,H] 0 none, 1 warmup, 2 exact
-    void* hstates;            // kRecurStates: [total_chunks,H,V,K] entry state of every chunk
-    void* delta;              // kRecurStates: [Ttot,H,V] Delta = U - W S^T of every chunk, or null
+    void* hstates;            // kRecurStates, kRecurOutRec: [total_chunks,H,V,K] entry state of every chunk
+    void* delta;              // same modes: [Ttot,H,V] Delta = U - W S^T of every chunk, or null
     float scale;
     int32_t warmup;           // W chunks
     int32_t use_cp;           // segments >= 1 read seginit

@@ -354,7 +354,9 @@ __device__ __forceinline__ void chunk_part2(const RecurArgs& a, const ChunkLds<T
 template <typename T, int K, int RT, int MODE>
 __global__ __launch_bounds__(RT * 4) void k_recur(RecurArgs a) {
     using C = RCfg<T, K, RT>;
-    constexpr bool kOut = MODE == kRecurOut;
+    constexpr bool kOut = MODE == kRecurOut || MODE == kRecurOutRec;
+    // records each chunk's entry state and Delta for the backward
+    constexpr bool kRec = MODE == kRecurStates || MODE == kRecurOutRec;
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     ChunkLds<T, K, RT> L;
     L.sQ = reinterpret_cast<T*>(smem + C::off_q);
@@ -451,7 +453,7 @@ __global__ __launch_bounds__(RT * 4) void k_recur(RecurArgs a) {
         for (int i = 0; i < K / 16; ++i) hold(hkeep[i]);
 #pragma unroll
         for (int i = 0; i < NFL; ++i) hold(fkeep[i]);
-        if (MODE == kRecurStates) {
+        if (kRec) {
             // entry state of this chunk, in the input precision
             T* hs = reinterpret_cast<T*>(a.hstates) + ((size_t)(sg.choff + ci) * H + h) * VK + (size_t)row * K;
 #pragma unroll
@@ -460,7 +462,7 @@ __global__ __launch_bounds__(RT * 4) void k_recur(RecurArgs a) {
             for (int kt = 0; kt < K / 16; ++kt) *reinterpret_cast<PV*>(hs + kt * 16 + gq * 4) = hkeep[kt];
         }
         lds_sync();  // previous chunk's LDS reads are done
-        if (MODE == kRecurStates && a.delta && ci > cbeg) {
+        if (kRec && a.delta && ci > cbeg) {
             // the previous chunk's Delta, staged over the q tile
             T* dst = reinterpret_cast<T*>(a.delta) + ((t0 - 64) * H + h) * V + vt * RT;
             constexpr int NV = RT / C::VEC;
@@ -475,6 +477,8 @@ __global__ __launch_bounds__(RT * 4) void k_recur(RecurArgs a) {
                 *reinterpret_cast<u32x4*>(dst + (size_t)(u / NV) * H * V + (u % NV) * C::VEC) = fkeep[it];
             }
         }
+        // (the output pass stages q over the tile just read: every wave's reads first)
+        if (MODE == kRecurOutRec && a.delta) lds_sync();
         chunk_stage<T, K, RT, kOut>(R, L);
         lds_sync();
         // operands kDepth chunks ahead (the last chunk again past the end), in three pieces
@@ -505,7 +509,15 @@ __global__ __launch_bounds__(RT * 4) void k_recur(RecurArgs a) {
             chunk_fetch<1>(R, a, tn, cnn, h, ucol0);
             chunk_fetch<2>(R, a, tn, cnn, h, ucol0);
         }
-        if (kOut) lds_sync();  // P tiles complete
+        if (kOut) lds_sync();  // P tiles complete (and every read of the q tile)
+        if (MODE == kRecurOutRec && a.delta) {
+            // Delta, staged over the q tile as in the states pass
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    L.sQ[(rt * 16 + gq * 4 + i) * C::LDU + wave * 16 + ln] = Elem<T>::from_f(accD[rt][i]);
+        }
         chunk_part2<T, K, RT, kOut>(a, L, accS, accD, accO, t0, c, h, vt * RT, okeep);
     };
     if constexpr (kDepth == 2) {
@@ -517,7 +529,7 @@ __global__ __launch_bounds__(RT * 4) void k_recur(RecurArgs a) {
         for (int ci = cbeg; ci < cend; ++ci) step(R0, ci);
     }
 
-    if (MODE == kRecurStates && a.delta && cbeg < cend) {
+    if (kRec && a.delta && cbeg < cend) {
         lds_sync();
         const int cl = cend - 1;
         flush_tile<T, RT, C::NT>(reinterpret_cast<T*>(a.delta) + ((sg.bos + (int64_t)cl * 64) * H + h) * V + vt * RT,
@@ -803,6 +815,7 @@ hipError_t launch_recur(const RecurArgs& a, int dtype, int mode, int64_t nsegs_g
 #define GDN_RECUR_CASE(TT, KK, RR)                                                                         \
     if (K == KK && RT == RR) {                                                                             \
         if (mode == kRecurOut) return launch_recur_t<TT, KK, RR, kRecurOut>(a, nsegs_grid, vtiles, st);     \
+        if (mode == kRecurOutRec) return launch_recur_t<TT, KK, RR, kRecurOutRec>(a, nsegs_grid, vtiles, st); \
         if (mode == kRecurPrepass) return launch_recur_t<TT, KK, RR, kRecurPrepass>(a, nsegs_grid, vtiles, st); \
         if (mode == kRecurStates) return launch_recur_t<TT, KK, RR, kRecurStates>(a, nsegs_grid, vtiles, st); \
     }

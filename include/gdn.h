@@ -83,10 +83,12 @@ typedef enum gdn_cp_mode {
 /* desc->flags: keeping the forward's intermediates for the backward of a training step.
  * GDN_FLAG_KEEP_FORWARD    gdn_chunk_fwd leaves in its workspace what the backward
  *                          recomputes otherwise: the chunk gate cumsums, w, u, T = (I+A)^-1,
- *                          the CP decisions and the sub-sequence entry states (the
- *                          forward workspace then includes room for T).
+ *                          the CP decisions, the sub-sequence entry states, every chunk's
+ *                          entry state and Delta = U - W S^T (the forward workspace then
+ *                          includes room for T, the states and Delta).
  * GDN_FLAG_REUSE_FORWARD   gdn_chunk_bwd starts from them instead of recomputing the
- *                          intra-chunk pass and the forward CP preprocessing. The caller
+ *                          intra-chunk pass, the forward CP preprocessing and the chunk-state
+ *                          pass. The caller
  *                          guarantees that the same workspace last held a KEEP_FORWARD
  *                          forward of the same inputs and descriptor (flags aside), with
  *                          no other call on it since except REUSE_FORWARD backwards. */

@@ -167,17 +167,21 @@ def test_call_errors_before_launch(lib):
 @pytest.mark.parametrize("kw", [dict(), dict(B=1, H=64, T=4096), dict(T=1000, H=2, K=64, V=64, dtype=torch.float32)])
 def test_keep_forward_workspace(kw):
     """A forward that keeps its intermediates needs more workspace (T per chunk, C x C in the
-    input dtype), laid out where the backward reads it; the backward's size does not depend on
-    the flags, and covers the kept forward's."""
+    input dtype; the chunk-entry states and Delta), laid out where the backward reads it; the
+    backward's size does not depend on the flags, and covers the kept forward's."""
     base = plan(**kw)
     keep = plan(flags=_abi.GDN_FLAG_KEEP_FORWARD, **kw)
     reuse = plan(flags=_abi.GDN_FLAG_REUSE_FORWARD, **kw)
     both = plan(flags=_abi.GDN_FLAG_KEEP_FORWARD | _abi.GDN_FLAG_REUSE_FORWARD, **kw)
     H = kw.get("H", 16)
+    K, V = kw.get("K", 128), kw.get("V", 128)
     esize = 4 if kw.get("dtype") == torch.float32 else 2
-    tm = base["total_chunks"] * H * 64 * 64 * esize
-    assert keep["fwd_workspace_bytes"] >= base["fwd_workspace_bytes"] + tm
-    assert keep["fwd_workspace_bytes"] <= base["fwd_workspace_bytes"] + tm + 256
+    tokens = kw.get("B", 1) * kw.get("T", 32768)
+    # T = (I+A)^-1 per chunk, one V x K state per chunk and Delta per token, each 256-byte aligned
+    kept = [base["total_chunks"] * H * 64 * 64 * esize, base["total_chunks"] * H * V * K * esize,
+            tokens * H * V * esize]
+    extra = sum(-(-b // 256) * 256 for b in kept)
+    assert base["fwd_workspace_bytes"] + extra - 256 <= keep["fwd_workspace_bytes"] <= base["fwd_workspace_bytes"] + extra
     for p in (keep, reuse, both):
         assert p["bwd_workspace_bytes"] == base["bwd_workspace_bytes"]
         assert p["cp_on"] == base["cp_on"] and p["total_segments"] == base["total_segments"]
