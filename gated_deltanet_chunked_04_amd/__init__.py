@@ -43,7 +43,8 @@ class Desc:
     """A gdn_desc plus the host objects its pointers refer to."""
 
     def __init__(self, B, T, H, K, V, dtype, *, scale=1.0, cu_seqlens=None, cu_seqlens_host=None,
-                 cp_mode="auto", warmup_chunks=0, seg_chunks=0, warmup_eps=0.0, num_cus=0, flags=0):
+                 cp_mode="auto", warmup_chunks=0, seg_chunks=0, warmup_eps=0.0, num_cus=0, flags=0,
+                 warmup_max_chunks=0):
         d = GdnDesc()
         d.B, d.T, d.H, d.K, d.V = int(B), int(T), int(H), int(K), int(V)
         d.chunk = 64
@@ -71,6 +72,7 @@ class Desc:
             d.cu_seqlens_host = hc.ctypes.data
         d.cp_mode = CP_MODES[cp_mode] if isinstance(cp_mode, str) else int(cp_mode)
         d.warmup_chunks = int(warmup_chunks)
+        d.warmup_max_chunks = int(warmup_max_chunks)
         d.seg_chunks = int(seg_chunks)
         d.warmup_eps = float(warmup_eps)
         d.num_cus = int(num_cus)
@@ -94,11 +96,12 @@ def gdn_plan(desc: Desc) -> dict:
 
 
 def gdn_workspace(q, v, *, cu_seqlens=None, cu_seqlens_host=None, cp_mode="auto", warmup_chunks=0,
-                  seg_chunks=0, warmup_eps=0.0):
+                  seg_chunks=0, warmup_eps=0.0, warmup_max_chunks=0):
     """A workspace large enough for gdn_chunk_fwd(keep_for_backward=True) and for
     gdn_chunk_bwd(reuse_forward=True) with the same shapes and options."""
     kw = dict(cu_seqlens=cu_seqlens, cu_seqlens_host=cu_seqlens_host, cp_mode=cp_mode,
-              warmup_chunks=warmup_chunks, seg_chunks=seg_chunks, warmup_eps=warmup_eps)
+              warmup_chunks=warmup_chunks, seg_chunks=seg_chunks, warmup_eps=warmup_eps,
+              warmup_max_chunks=warmup_max_chunks)
     lib = load_library()
     f, b = ctypes.c_size_t(), ctypes.c_size_t()
     # the descriptors stay referenced through the calls: they own the host copy of cu_seqlens
@@ -143,7 +146,7 @@ def _num_seqs(q, cu_seqlens):
 
 def gdn_chunk_fwd(q, k, v, g, beta, initial_state=None, *, scale=1.0, cu_seqlens=None,
                   cu_seqlens_host=None, output_final_state=True, cp_mode="auto", warmup_chunks=0,
-                  seg_chunks=0, warmup_eps=0.0, workspace=None, o=None, final_state=None,
+                  seg_chunks=0, warmup_eps=0.0, warmup_max_chunks=0, workspace=None, o=None, final_state=None,
                   keep_for_backward=False):
     """Forward. Returns (o, final_state or None). Runs on the current stream.
 
@@ -158,7 +161,8 @@ def gdn_chunk_fwd(q, k, v, g, beta, initial_state=None, *, scale=1.0, cu_seqlens
         raise ValueError("keep_for_backward needs a caller-owned workspace (gdn_workspace)")
     desc = make_desc(q, v, scale=scale, cu_seqlens=cu_seqlens, cu_seqlens_host=cu_seqlens_host,
                      cp_mode=cp_mode, warmup_chunks=warmup_chunks, seg_chunks=seg_chunks,
-                     warmup_eps=warmup_eps, flags=GDN_FLAG_KEEP_FORWARD if keep_for_backward else 0)
+                     warmup_eps=warmup_eps, warmup_max_chunks=warmup_max_chunks,
+                     flags=GDN_FLAG_KEEP_FORWARD if keep_for_backward else 0)
     lib = load_library()
     nbytes = ctypes.c_size_t()
     check(lib.gdn_chunk_fwd_workspace_size(desc.ref, ctypes.byref(nbytes)), "gdn_chunk_fwd_workspace_size")
@@ -179,7 +183,7 @@ def gdn_chunk_fwd(q, k, v, g, beta, initial_state=None, *, scale=1.0, cu_seqlens
 
 def gdn_chunk_bwd(q, k, v, g, beta, d_o, initial_state=None, d_final_state=None, *, scale=1.0,
                   cu_seqlens=None, cu_seqlens_host=None, cp_mode="auto", warmup_chunks=0, seg_chunks=0,
-                  warmup_eps=0.0, workspace=None, need_d_initial_state=True, out=None,
+                  warmup_eps=0.0, warmup_max_chunks=0, workspace=None, need_d_initial_state=True, out=None,
                   reuse_forward=False):
     """Backward. Returns dict(dq, dk, dv, dg, dbeta, d_initial_state); `out` may hold them preallocated.
 
@@ -200,7 +204,8 @@ def gdn_chunk_bwd(q, k, v, g, beta, d_o, initial_state=None, d_final_state=None,
         raise ValueError("reuse_forward needs the forward's workspace")
     desc = make_desc(q, v, scale=scale, cu_seqlens=cu_seqlens, cu_seqlens_host=cu_seqlens_host,
                      cp_mode=cp_mode, warmup_chunks=warmup_chunks, seg_chunks=seg_chunks,
-                     warmup_eps=warmup_eps, flags=GDN_FLAG_REUSE_FORWARD if reuse_forward else 0)
+                     warmup_eps=warmup_eps, warmup_max_chunks=warmup_max_chunks,
+                     flags=GDN_FLAG_REUSE_FORWARD if reuse_forward else 0)
     lib = load_library()
     nbytes = ctypes.c_size_t()
     check(lib.gdn_chunk_bwd_workspace_size(desc.ref, ctypes.byref(nbytes)), "gdn_chunk_bwd_workspace_size")
@@ -235,11 +240,12 @@ def gdn_intra_chunk(k, v, g, beta, *, cu_seqlens=None, cu_seqlens_host=None):
 
 
 def gdn_cp_modes(k, v, g, beta, *, cu_seqlens=None, cu_seqlens_host=None, cp_mode="auto",
-                 warmup_chunks=0, seg_chunks=0, warmup_eps=0.0):
+                 warmup_chunks=0, seg_chunks=0, warmup_eps=0.0, warmup_max_chunks=0):
     """Per sequence-head CP decision [N, H] int32: 0 no split, 1 warmup, 2 exact."""
     N = _num_seqs(k, cu_seqlens)
     desc = make_desc(k, v, cu_seqlens=cu_seqlens, cu_seqlens_host=cu_seqlens_host, cp_mode=cp_mode,
-                     warmup_chunks=warmup_chunks, seg_chunks=seg_chunks, warmup_eps=warmup_eps)
+                     warmup_chunks=warmup_chunks, seg_chunks=seg_chunks, warmup_eps=warmup_eps,
+              warmup_max_chunks=warmup_max_chunks)
     lib = load_library()
     nbytes = ctypes.c_size_t()
     check(lib.gdn_chunk_fwd_workspace_size(desc.ref, ctypes.byref(nbytes)), "gdn_chunk_fwd_workspace_size")

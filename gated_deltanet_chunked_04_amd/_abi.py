@@ -16,7 +16,7 @@ GDN_OK, GDN_ERR_INVALID_ARG, GDN_ERR_UNSUPPORTED, GDN_ERR_WORKSPACE, GDN_ERR_HIP
 GDN_DTYPE_BF16, GDN_DTYPE_FP32 = 0, 1
 CP_MODES = {"auto": 0, "off": 1, "on": 2, "exact": 3, "warmup": 4}
 GDN_FLAG_KEEP_FORWARD, GDN_FLAG_REUSE_FORWARD = 1, 2
-GDN_ABI_VERSION = 2
+GDN_ABI_VERSION = 3
 
 # Declared entry points of include/gdn.h (checked by the ABI test).
 EXPORTS = ("gdn_abi_version", "gdn_status_string", "gdn_plan", "gdn_chunk_fwd_workspace_size",
@@ -33,14 +33,16 @@ class GdnDesc(ctypes.Structure):
         ("cu_seqlens", ctypes.c_void_p), ("cu_seqlens_host", ctypes.c_void_p),
         ("cp_mode", ctypes.c_int32), ("warmup_chunks", ctypes.c_int32),
         ("seg_chunks", ctypes.c_int32), ("warmup_eps", ctypes.c_float),
-        ("num_cus", ctypes.c_int32), ("flags", ctypes.c_int32), ("reserved", ctypes.c_int32 * 6),
+        ("num_cus", ctypes.c_int32), ("flags", ctypes.c_int32), ("warmup_max_chunks", ctypes.c_int32),
+        ("reserved", ctypes.c_int32 * 5),
     ]
 
 
 class GdnPlanInfo(ctypes.Structure):
     _fields_ = [
         ("num_seqs", ctypes.c_int32), ("cp_on", ctypes.c_int32), ("seg_chunks", ctypes.c_int32),
-        ("warmup_chunks", ctypes.c_int32), ("warmup_eps", ctypes.c_float), ("v_tiles", ctypes.c_int32),
+        ("warmup_chunks", ctypes.c_int32), ("warmup_max_chunks", ctypes.c_int32),
+        ("warmup_eps", ctypes.c_float), ("v_tiles", ctypes.c_int32),
         ("max_len", ctypes.c_int64), ("total_chunks", ctypes.c_int64),
         ("total_segments", ctypes.c_int64),
         ("fwd_workspace_bytes", ctypes.c_size_t), ("bwd_workspace_bytes", ctypes.c_size_t),

@@ -22,11 +22,13 @@ namespace {
 
 constexpr size_t kAlign = 256;
 constexpr int kDefaultWarmup = 8;
+constexpr int kMaxWindowSpan = 64;  // candidate warmup windows W .. W + 63 (one 64-bit mask)
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 struct Plan {
     int32_t N = 0;
+    int64_t H = 0;
     int32_t varlen = 0;
     int64_t Ttot = 0;
     int64_t max_len = 0;
@@ -37,6 +39,7 @@ struct Plan {
     int32_t nseg = 1;      // uniform: segments per sequence
     int64_t total_segs = 0;
     int32_t W = kDefaultWarmup;
+    int32_t Wmax = kDefaultWarmup;
     float eps = 1e-4f;
     int32_t forced = 0;
     int32_t esize = 2;
@@ -60,7 +63,7 @@ int query_cus() {
 
 gdn_status make_plan(const gdn_desc* d, Plan& p) {
     if (!d) return GDN_ERR_INVALID_ARG;
-    for (int i = 0; i < 6; ++i)
+    for (int i = 0; i < 5; ++i)
         if (d->reserved[i] != 0) return GDN_ERR_INVALID_ARG;
     if (d->flags & ~(GDN_FLAG_KEEP_FORWARD | GDN_FLAG_REUSE_FORWARD)) return GDN_ERR_INVALID_ARG;
     if (d->B < 1 || d->T < 0 || d->H < 1 || d->K < 1 || d->V < 1) return GDN_ERR_INVALID_ARG;
@@ -70,11 +73,15 @@ gdn_status make_plan(const gdn_desc* d, Plan& p) {
     if (!isfinite(d->scale)) return GDN_ERR_INVALID_ARG;
     if (d->cp_mode < GDN_CP_AUTO || d->cp_mode > GDN_CP_WARMUP) return GDN_ERR_INVALID_ARG;
     if (d->warmup_chunks < 0 || d->warmup_chunks > 16) return GDN_ERR_INVALID_ARG;
+    if (d->warmup_max_chunks < 0) return GDN_ERR_INVALID_ARG;
     if (d->seg_chunks < 0 || d->num_cus < 0) return GDN_ERR_INVALID_ARG;
     if (!(d->warmup_eps >= 0.f && d->warmup_eps < 1.f)) return GDN_ERR_INVALID_ARG;
     if (d->H > 65535) return GDN_ERR_UNSUPPORTED;
     p.esize = d->dtype == GDN_DTYPE_BF16 ? 2 : 4;
+    p.H = d->H;
     p.W = d->warmup_chunks ? d->warmup_chunks : kDefaultWarmup;
+    if (d->warmup_max_chunks && (d->warmup_max_chunks < p.W || d->warmup_max_chunks > p.W + kMaxWindowSpan - 1))
+        return GDN_ERR_INVALID_ARG;
     p.eps = d->warmup_eps > 0.f ? d->warmup_eps : (d->dtype == GDN_DTYPE_BF16 ? 1e-4f : 1e-6f);
     p.Ttot = d->B * d->T;
     int64_t max_nt = 0;
@@ -134,6 +141,12 @@ gdn_status make_plan(const gdn_desc* d, Plan& p) {
     }
     p.cp_on = cp ? 1 : 0;
     p.seg_len = (int32_t)seg_len;
+    // A sequence-head whose gates do not meet the warmup bound over W chunks may take a longer
+    // window, by default up to one sub-sequence: the warmup then still costs less than the
+    // exact correction (a (V+K)-row pass over the whole sub-sequence plus the segment scan).
+    p.Wmax = d->warmup_max_chunks
+                 ? d->warmup_max_chunks
+                 : (int32_t)std::min<int64_t>(std::max<int64_t>(seg_len, p.W), p.W + kMaxWindowSpan - 1);
     if (p.varlen) {
         p.total_segs = 0;
         const int32_t* cu = d->cu_seqlens_host;
@@ -159,7 +172,7 @@ gdn_status make_plan(const gdn_desc* d, Plan& p) {
     p.o_w = take(T * H * K * p.esize);
     p.o_u = take(T * H * V * p.esize);
     p.o_cstat = take((size_t)p.total_chunks * H * 8);
-    p.o_modes = take((size_t)p.N * H * 4);
+    p.o_modes = take((size_t)p.N * H * 8);  // CP modes [N,H], then warmup windows [N,H]
     if (p.varlen) {
         p.o_bos = take((size_t)p.N * 8);
         p.o_len = take((size_t)p.N * 4);
@@ -181,7 +194,7 @@ gdn_status make_plan(const gdn_desc* d, Plan& p) {
     p.fwd_bytes = std::max<size_t>((d->flags & GDN_FLAG_KEEP_FORWARD) ? off : p.o_tm, kAlign);
     // backward workspace continues after the forward's
     if (p.cp_on) {
-        p.o_modes_r = take((size_t)p.N * H * 4);
+        p.o_modes_r = take((size_t)p.N * H * 8);
         p.o_seginit_r = take((size_t)p.total_segs * H * V * K * 4);
         p.o_prep_r = take((size_t)p.total_segs * H * (V + K) * K * 4);
     }
@@ -362,15 +375,22 @@ gdn_status run_intra(const gdn_desc* d, const Plan& p, unsigned char* ws, const 
     return GDN_OK;
 }
 
-gdn_status run_decide(const gdn_desc* d, const Plan& p, unsigned char* ws, int32_t* modes, hipStream_t st,
-                      int reverse = 0, int32_t* modes_r = nullptr) {
+// Each modes array [N,H] of the workspace is followed by the warmup windows [N,H] of the
+// same decision.
+int32_t* windows_of(const Plan& p, int32_t* modes) { return modes ? modes + (size_t)p.N * p.H : nullptr; }
+
+gdn_status run_decide(const gdn_desc* d, const Plan& p, unsigned char* ws, int32_t* modes, int32_t* wins,
+                      hipStream_t st, int reverse = 0, int32_t* modes_r = nullptr) {
     DecideArgs da{};
     da.reverse = reverse;
     da.modes_r = modes_r;
+    da.wins_r = windows_of(p, modes_r);
     da.geo = make_geo(d, p, ws);
     da.cstat = reinterpret_cast<const float2*>(ws + p.o_cstat);
     da.modes = modes;
+    da.wins = wins;
     da.warmup = p.W;
+    da.warmup_max = p.Wmax;
     da.log_eps = logf(p.eps);
     da.forced = p.forced;
     GDN_LAUNCH(kKDecide, st, launch_decide(da, st));
@@ -407,6 +427,7 @@ gdn_status gdn_plan(const gdn_desc* desc, gdn_plan_info* out) {
     out->cp_on = p.cp_on;
     out->seg_chunks = p.seg_len;
     out->warmup_chunks = p.W;
+    out->warmup_max_chunks = p.Wmax;
     out->warmup_eps = p.eps;
     out->v_tiles = (int32_t)(desc->V / recur_rows((int)desc->V, (int)desc->K));
     out->max_len = p.max_len;
@@ -456,14 +477,14 @@ gdn_status gdn_chunk_fwd(const gdn_desc* desc, const void* q, const void* k, con
     ra.o = o;
     ra.sT = final_state;
     ra.scale = desc->scale;
-    ra.warmup = p.W;
     ra.use_cp = p.cp_on;
     int32_t* modes = reinterpret_cast<int32_t*>(ws + p.o_modes);
     ra.modes = modes;
+    ra.wins = windows_of(p, modes);
     if (p.cp_on) {
         float* seginit = reinterpret_cast<float*>(ws + p.o_seginit);
         float* prep = reinterpret_cast<float*>(ws + p.o_prep);
-        if ((s = run_decide(desc, p, ws, modes, st)) != GDN_OK) return s;
+        if ((s = run_decide(desc, p, ws, modes, windows_of(p, modes), st)) != GDN_OK) return s;
         ra.seginit_out = seginit;
         ra.prep = prep;
         const int rt = recur_rows((int)desc->V, (int)desc->K);
@@ -529,8 +550,8 @@ gdn_status gdn_chunk_bwd(const gdn_desc* desc, const void* q, const void* k, con
     int32_t* modes = reinterpret_cast<int32_t*>(ws + p.o_modes);
     int32_t* modes_r = p.cp_on ? reinterpret_cast<int32_t*>(ws + p.o_modes_r) : nullptr;
     if (p.cp_on) {
-        if (reuse) s = run_decide(desc, p, ws, modes_r, st, 1);
-        else s = run_decide(desc, p, ws, modes, st, 0, modes_r);
+        if (reuse) s = run_decide(desc, p, ws, modes_r, windows_of(p, modes_r), st, 1);
+        else s = run_decide(desc, p, ws, modes, windows_of(p, modes), st, 0, modes_r);
         if (s != GDN_OK) return s;
     }
     std::lock_guard<std::mutex> side_lock(side_mutex());
@@ -549,9 +570,9 @@ gdn_status gdn_chunk_bwd(const gdn_desc* desc, const void* q, const void* k, con
     ra.u = u;
     ra.s0 = initial_state;
     ra.scale = desc->scale;
-    ra.warmup = p.W;
     ra.use_cp = p.cp_on;
     ra.modes = modes;
+    ra.wins = windows_of(p, modes);
     ra.hstates = ws + p.o_h;
     ra.delta = ws + p.o_dl;
     if (!reuse && p.cp_on) {
@@ -588,12 +609,12 @@ gdn_status gdn_chunk_bwd(const gdn_desc* desc, const void* q, const void* k, con
     va.gstates = ws + p.o_gst;
     va.ddelta = ws + p.o_ddl;
     va.scale = desc->scale;
-    va.warmup = p.W;
     va.use_cp = p.cp_on;
     if (p.cp_on) {
         float* seginit_r = reinterpret_cast<float*>(ws + p.o_seginit_r);
         float* prep_r = reinterpret_cast<float*>(ws + p.o_prep_r);
         va.modes = modes_r;
+        va.wins = windows_of(p, modes_r);
         va.seginit_out = seginit_r;
         va.prep = prep_r;
         GDN_LAUNCH(kKBwdPrepass, st, launch_reverse(va, desc->dtype, kRecurPrepass, p.total_segs, vktiles, st));
@@ -666,7 +687,7 @@ gdn_status gdn_cp_modes(const gdn_desc* desc, const void* k, const void* v, cons
     if ((s = run_intra(desc, p, ws, k, v, g, beta, reinterpret_cast<float*>(ws + p.o_gam), ws + p.o_w,
                        ws + p.o_u, st)) != GDN_OK)
         return s;
-    return run_decide(desc, p, ws, modes_out, st);
+    return run_decide(desc, p, ws, modes_out, windows_of(p, reinterpret_cast<int32_t*>(ws + p.o_modes)), st);
 }
 
 gdn_status gdn_profile_enable(int enable) {

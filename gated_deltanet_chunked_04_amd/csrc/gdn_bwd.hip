@@ -157,11 +157,11 @@ __global__ __launch_bounds__(RT * 4) void k_reverse(RevArgs a) {
     if (MODE == kRecurPrepass) {
         mode = a.modes[sg.n * H + h];
         if (mode == 1) {
-            // warmup: the W chunks after this segment, from a zero adjoint (or from d(final
+            // warmup: the chunks of the window after this segment, from a zero adjoint (or from d(final
             // state) when the window reaches the sequence end)
             if (last || vt * RT >= V) return;
             cbeg = sg.c1;
-            cend = min(sg.c1 + a.warmup, sg.nchunks);
+            cend = min(sg.c1 + a.wins[sg.n * H + h], sg.nchunks);
             if (cend == sg.nchunks && a.dsT)
                 load_state<K>(accG, a.dsT + ((size_t)sg.n * H + h) * VK, row);
             else

@@ -387,7 +387,7 @@ __global__ __launch_bounds__(RT * 4) void k_recur(RecurArgs a) {
         if (mode == 1) {
             if (sg.s == 0 || vt * RT >= V) return;
             cend = sg.c0;
-            cbeg = max(0, sg.c0 - a.warmup);
+            cbeg = max(0, sg.c0 - a.wins[sg.n * H + h]);
             if (cbeg == 0 && a.s0)
                 load_state<K>(accS, a.s0 + ((size_t)sg.n * H + h) * VK, row);
             else
@@ -572,11 +572,14 @@ hipError_t launch_recur_t(const RecurArgs& a, int64_t nsegs_grid, int vtiles, hi
 }
 
 // ---------------------------------------------------------------------------
-// CP decision: one wave per sequence-head. Warmup is accepted when, for every segment
-// boundary whose window does not reach the sequence start, the gate sum over the W
-// chunks before it is <= log(eps) and beta |k|^2 <= 2 on those chunks (then every
-// token map exp(g)(I - beta k k^T) has spectral norm <= exp(g), so a wrong state at
-// the window start is damped by at least exp(window gate sum)).
+// CP decision: one wave per sequence-head. Warmup over a window of w chunks is accepted
+// when, for every segment boundary whose window does not reach the sequence start, the
+// gate sum over the w chunks before it is <= log(eps) and beta |k|^2 <= 2 on those chunks
+// (then every token map exp(g)(I - beta k k^T) has spectral norm <= exp(g), so a wrong
+// state at the window start is damped by at least exp(window gate sum)). The window is the
+// shortest w in [W, Wmax] accepted at every boundary; with none, the exact correction.
+// Each lane walks the chunks before its boundaries once and sets bit w - W of a mask for
+// every accepted w; the wave ANDs the masks.
 __global__ __launch_bounds__(kThreads) void k_decide(DecideArgs a) {
     const int wave = wave_id(), lane = threadIdx.x & 63;
     const int64_t p = (int64_t)blockIdx.x * 4 + wave;
@@ -586,40 +589,74 @@ __global__ __launch_bounds__(kThreads) void k_decide(DecideArgs a) {
     int32_t nseg, nchunks;
     int64_t segoff, choff;
     seq_segs(a.geo, n, nseg, segoff, nchunks, choff);
+    const int W = a.warmup, span = a.warmup_max - a.warmup + 1;  // 1 .. 64 candidate windows
+    const uint64_t all = span >= 64 ? ~0ull : ((1ull << span) - 1);
     // a.modes gets the decision for a.reverse's direction; a.modes_r, if given, the reverse one
     for (int dir = 0; dir < 2; ++dir) {
         int32_t* out = dir == 0 ? a.modes : a.modes_r;
+        int32_t* wout = dir == 0 ? a.wins : a.wins_r;
         if (!out) continue;
         const bool rev = dir == 0 ? a.reverse != 0 : true;
-        int mode;
+        int mode, win = W;
         if (nseg <= 1) {
             mode = 0;
         } else if (a.forced) {
             mode = a.forced;
         } else {
-            bool ok = true;
+            uint64_t pass = all;
             for (int s = 1 + lane; s < nseg; s += 64) {
                 const int cb = s * a.geo.seg_len;  // first chunk of segment s
-                // forward: the W chunks before segment s; reverse: the W chunks after segment s-1
-                int w0 = cb - a.warmup, w1 = cb;
-                if (rev) {
-                    w0 = cb;
-                    w1 = cb + a.warmup;
-                    if (w1 >= nchunks) continue;  // window reaches the sequence end: exact
-                } else if (w0 <= 0) {
-                    continue;  // window reaches the sequence start: exact
-                }
+                // forward: the chunks before segment s; reverse: the chunks from segment s on
+                // (after segment s-1). A window that reaches the sequence start (end) runs
+                // from the known state there: exact.
+                const int avail = rev ? nchunks - cb : cb;
+                uint64_t m = 0;
                 float sum = 0.f, kk = 0.f;
-                for (int m = w0; m < w1; ++m) {
-                    const float2 st = a.cstat[(choff + m) * H + h];
-                    sum += st.x;
-                    kk = fmaxf(kk, st.y);
+                for (int w0 = 0; w0 < a.warmup_max; w0 += 8) {
+                    float2 st[8];
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) {
+                        const int w = w0 + j + 1;
+                        const int idx = rev ? cb + w - 1 : cb - w;
+                        st[j] = (w < avail && w <= a.warmup_max) ? a.cstat[(choff + idx) * H + h] : make_float2(0.f, 0.f);
+                    }
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) {
+                        const int w = w0 + j + 1;
+                        if (w > a.warmup_max) break;
+                        if (w >= avail) {
+                            // this and every longer window start at the sequence start (end)
+                            if (w <= W) m = all;
+                            else m |= all & (~0ull << (w - W));
+                            break;
+                        }
+                        sum += st[j].x;
+                        kk = fmaxf(kk, st[j].y);
+                        if (w >= W && sum <= a.log_eps && kk <= 2.f) m |= 1ull << (w - W);
+                    }
+                    if (w0 + 8 >= avail) break;
                 }
-                ok = ok && (sum <= a.log_eps) && (kk <= 2.f);
+                pass &= m;
             }
-            mode = __all(ok) ? 1 : 2;
+            // AND over the wave
+            uint32_t lo = (uint32_t)pass, hi = (uint32_t)(pass >> 32);
+#pragma unroll
+            for (int off = 32; off >= 1; off >>= 1) {
+                lo &= (uint32_t)__shfl_xor((int)lo, off);
+                hi &= (uint32_t)__shfl_xor((int)hi, off);
+            }
+            pass = ((uint64_t)hi << 32) | lo;
+            if (pass) {
+                mode = 1;
+                win = W + __builtin_ctzll(pass);
+            } else {
+                mode = 2;
+            }
         }
-        if (lane == 0) out[p] = mode;
+        if (lane == 0) {
+            out[p] = mode;
+            if (wout) wout[p] = win;
+        }
     }
 }
 

@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 2
+#define GDN_ABI_VERSION 3
 
 typedef enum gdn_status {
     GDN_OK = 0,
@@ -110,7 +110,12 @@ typedef struct gdn_desc {
     float warmup_eps;               /* warmup acceptance: exp(window gate sum) <= eps (0 = 1e-4 bf16, 1e-6 fp32) */
     int32_t num_cus;                /* compute units to plan for (0 = query the current device) */
     int32_t flags;                  /* GDN_FLAG_* (0 = none) */
-    int32_t reserved[6];            /* must be zero */
+    int32_t warmup_max_chunks;      /* longest warmup window a sequence-head may take when
+                                       warmup_chunks do not meet the acceptance bound (AUTO, ON):
+                                       warmup_chunks..warmup_chunks+63, or 0 = the sub-sequence
+                                       length (at least warmup_chunks, at most warmup_chunks+63);
+                                       equal to warmup_chunks keeps one fixed window */
+    int32_t reserved[5];            /* must be zero */
 } gdn_desc;
 
 /* Host-side plan of a call (filled by gdn_plan; no device work). */
@@ -118,7 +123,8 @@ typedef struct gdn_plan_info {
     int32_t num_seqs;               /* N */
     int32_t cp_on;                  /* 1 if the call splits sequences into sub-sequences */
     int32_t seg_chunks;             /* chunks per sub-sequence (the last one may be shorter) */
-    int32_t warmup_chunks;          /* warmup window W in chunks */
+    int32_t warmup_chunks;          /* warmup window W in chunks (the shortest one taken) */
+    int32_t warmup_max_chunks;      /* longest warmup window a sequence-head may take */
     float warmup_eps;               /* warmup acceptance threshold */
     int32_t v_tiles;                /* value-row tiles per sequence-head in the recurrence kernel */
     int64_t max_len;                /* longest sequence, tokens */
@@ -196,7 +202,9 @@ gdn_status gdn_intra_chunk(const gdn_desc* desc, const void* k, const void* v,
                            void* workspace, size_t workspace_bytes, void* stream);
 
 /* CP decision per sequence-head, as the forward would take it:
- * modes_out [N, H] int32 (device): 0 = no split needed, 1 = warmup, 2 = exact.
+ * modes_out [N, H] int32 (device): 0 = no split needed, 1 = warmup (over the shortest
+ * window from warmup_chunks to warmup_max_chunks that meets the acceptance bound at every
+ * sub-sequence start), 2 = exact.
  * Uses the forward workspace; runs the intra-chunk kernel to get the gates. */
 gdn_status gdn_cp_modes(const gdn_desc* desc, const void* k, const void* v,
                         const float* g, const float* beta, int32_t* modes_out,

@@ -51,6 +51,15 @@ def small_inputs(B=2, T=1000, H=2, K=128, V=128, dtype=torch.bfloat16, seed=0, i
     return dict(q=q, k=k, v=v, g=g, beta=beta, initial_state=s0, cu_seqlens=cu)
 
 
+def mid_decay_inputs(T=8192, seed=5):
+    """Two heads: head 0 with the workloads' gates (fast decay), head 1 with a constant
+    log-decay of -0.6 per 64-token chunk, whose window sum passes log(1e-4) = -9.21 at 16
+    chunks (-9.6) but not at 15 (-9.0)."""
+    inp = small_inputs(B=1, T=T, H=2, seed=seed)
+    inp["g"][:, :, 1] = -0.6 / 64
+    return inp
+
+
 def oracle(inp, scale=1.0, heads=None, rows=None):
     """Oracle forward on (optionally) a subset of heads and value rows."""
     q, k, v, g, beta, s0 = (inp[x] for x in ("q", "k", "v", "g", "beta", "initial_state"))

@@ -34,7 +34,7 @@ def test_exports_every_declared_symbol(lib):
     assert set(declared) == set(_abi.EXPORTS)
     for name in declared:
         assert hasattr(lib, name), name
-    assert lib.gdn_abi_version() == _abi.GDN_ABI_VERSION == 2
+    assert lib.gdn_abi_version() == _abi.GDN_ABI_VERSION == 3
 
 
 def test_status_strings(lib):
@@ -89,6 +89,12 @@ def test_workload_plans():
     assert plan(seg_chunks=100)["seg_chunks"] == 100
     assert plan()["warmup_chunks"] == 8
     assert plan(warmup_chunks=6)["warmup_chunks"] == 6
+    # longer warmup windows: up to one sub-sequence by default, at most W + 63 chunks
+    assert plan()["warmup_max_chunks"] == 32
+    assert plan(B=1, H=8, T=262144)["warmup_max_chunks"] == 71
+    assert plan(warmup_max_chunks=8)["warmup_max_chunks"] == 8
+    assert plan(warmup_chunks=6, warmup_max_chunks=69)["warmup_max_chunks"] == 69
+    assert plan(seg_chunks=4)["warmup_max_chunks"] == 8
 
 
 def test_varlen_plan():
@@ -113,7 +119,8 @@ def test_argument_errors(lib):
     d = desc()
     out = _abi.GdnPlanInfo()
     bad = [("K", 96), ("V", 32), ("H", 0), ("B", 0), ("T", -1), ("chunk", 32), ("dtype", 7),
-           ("cp_mode", 9), ("warmup_chunks", 17), ("warmup_eps", 1.5)]
+           ("cp_mode", 9), ("warmup_chunks", 17), ("warmup_eps", 1.5), ("warmup_max_chunks", -1),
+           ("warmup_max_chunks", 7), ("warmup_max_chunks", 72)]
     codes = {"K": 2, "V": 2, "chunk": 2}
     for field, val in bad:
         d2 = desc()

@@ -9,7 +9,7 @@ import pytest
 import torch
 
 from gdn_inputs import make_inputs
-from gpu_helpers import check, small_inputs, to_dev, tol_for
+from gpu_helpers import check, mid_decay_inputs, small_inputs, to_dev, tol_for
 from oracle import ref_bwd
 
 pytestmark = pytest.mark.gpu
@@ -269,3 +269,16 @@ def test_backward_on_side_streams_and_threads(gpu_lib):
     for i in range(2):
         for n in NAMES:
             assert torch.equal(outs[i][n], ref[i][n]), (i, n)
+
+
+def test_backward_longer_warmup_window(gpu_lib):
+    """The reverse CP on a head that needs a 16-chunk window (constant log-decay of -0.6
+    per chunk): with the longer window allowed (warmup) and capped at 8 chunks (exact), all
+    six gradients match the oracle."""
+    inp = with_grads(mid_decay_inputs())
+    d = to_dev(inp)
+    ref = oracle_bwd(inp)
+    for extra in ({}, dict(warmup_max_chunks=8)):
+        out = gpu_bwd(d, cp_mode="on", seg_chunks=32, **extra)
+        print(extra, compare(out, ref, 1e-2), flush=True)
+

@@ -8,7 +8,7 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_helpers import check, gpu_fwd, oracle, rel_l2, small_inputs, to_dev, tol_for  # noqa: F401
+from gpu_helpers import check, gpu_fwd, mid_decay_inputs, oracle, rel_l2, small_inputs, to_dev, tol_for  # noqa: F401
 from oracle.chunked import chunked_fwd
 
 pytestmark = pytest.mark.gpu
@@ -115,3 +115,29 @@ def test_cp_modes_decision(gpu_lib):
     o, sT = gpu_fwd(d, cp_mode="on", seg_chunks=32)
     check(o, o_ref, 1e-2)
     check(sT, s_ref, 1e-2)
+
+
+def test_cp_longer_warmup_window(gpu_lib):
+    """A head that fails the warmup bound over 8 chunks takes a longer window that meets
+    it (here 16 chunks) when allowed, the exact correction when the cap is below that; every
+    variant matches the oracle."""
+    inp = mid_decay_inputs()
+    d = to_dev(inp)
+    kw = dict(cp_mode="on", seg_chunks=32)
+
+    def modes(**extra):
+        m = gpu_lib.gdn_cp_modes(d["k"], d["v"], d["g"], d["beta"], **kw, **extra)
+        torch.cuda.synchronize()
+        return m.cpu().tolist()
+
+    assert modes() == [[1, 1]]
+    assert modes(warmup_max_chunks=16) == [[1, 1]]
+    assert modes(warmup_max_chunks=15) == [[1, 2]]
+    assert modes(warmup_max_chunks=8) == [[1, 2]]
+    o_ref, s_ref = oracle(inp)
+    for extra in ({}, dict(warmup_max_chunks=15), dict(warmup_chunks=6, warmup_max_chunks=69)):
+        o, sT = gpu_fwd(d, **kw, **extra)
+        e_o = check(o, o_ref, 1e-2, f"o {extra}")
+        e_s = check(sT, s_ref, 1e-2, f"final_state {extra}")
+        print(f"{extra} rel_l2 o={e_o:.2e} final={e_s:.2e}", flush=True)
+
