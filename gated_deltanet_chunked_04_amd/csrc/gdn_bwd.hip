@@ -459,8 +459,9 @@ __global__ __launch_bounds__(RT * 4) void k_reverse(RevArgs a) {
             if (row < V) {
                 store_state<K>(accG, P, row);
             } else if (row < V + K) {
-                // M^T in the input precision after the R rows, as the forward's prepass
-                const int i = row - V;
+                // M^T in the input precision after the R rows, rows in fragment order, as the
+                // forward's prepass
+                const int i = frag_pos(row - V);
                 T* Mt = reinterpret_cast<T*>(P + VK);
 #pragma unroll
                 for (int kt = 0; kt < K / 16; ++kt)

@@ -286,6 +286,26 @@ template <> struct Pack4<float> {
     __device__ static type make(const f32x4& x) { return x; }
 };
 
+// Fragment order within each 32-column block: the column of slot e of lane group gq,
+// (e / 4) * 16 + gq * 4 + e % 4, goes to position gq * 8 + e, so the eight slots of a row
+// fragment are contiguous (one 16-byte load in bf16). Column c of a row -> its position.
+__device__ __forceinline__ int frag_pos(int c) {
+    return (c & ~31) | (((c >> 2) & 3) << 3) | (((c >> 4) & 1) << 2) | (c & 3);
+}
+
+// Row fragment of a matrix stored in fragment order (see frag_pos): row `row`, columns
+// k0 .. k0+31 (k0 a multiple of 32). Any address space.
+__device__ __forceinline__ void frag_row_fo(Frag<bf16_t>& f, const bf16_t* base, int ld, int row, int k0) {
+    const int gq = threadIdx.x >> 4 & 3;
+    f.v = *reinterpret_cast<const u32x4*>(base + (size_t)row * ld + k0 + gq * 8);
+}
+__device__ __forceinline__ void frag_row_fo(Frag<float>& f, const float* base, int ld, int row, int k0) {
+    const int gq = threadIdx.x >> 4 & 3;
+    const float* p = base + (size_t)row * ld + k0 + gq * 8;
+    f.lo = *reinterpret_cast<const f32x4*>(p);
+    f.hi = *reinterpret_cast<const f32x4*>(p + 4);
+}
+
 // Holds x in its registers up to this point. A vector store reads its data registers
 // late, and the wait that protects them retires every older memory operation too (the
 // counter is in order); holding a store's data until the next point that waits for

@@ -543,9 +543,10 @@ __global__ __launch_bounds__(RT * 4) void k_recur(RecurArgs a) {
             if (row < V) {
                 store_state<K>(accS, P, row);
             } else if (row < V + K) {
-                // M^T[k][i] at element k*K + i of a [K][K] matrix in the input precision (the
-                // scan's matrix-core operand precision) after the R rows, i = row - V
-                const int i = row - V;
+                // M^T[k][i], i = row - V, as a [K][K] matrix in the input precision (the
+                // scan's matrix-core operand precision) after the R rows, each row in fragment
+                // order (frag_pos) so that the scan loads its A fragments directly
+                const int i = frag_pos(row - V);
                 T* Mt = reinterpret_cast<T*>(P + VK);
 #pragma unroll
                 for (int kt = 0; kt < K / 16; ++kt)
@@ -662,23 +663,42 @@ __global__ __launch_bounds__(kThreads) void k_decide(DecideArgs a) {
 
 // ---------------------------------------------------------------------------
 // Exact CP: S_{s+1} = S_s M_s + R~_s across segments, for sequence-heads in mode 2.
-// Grid (N, H, V/RT); the state rows live in S^T accumulators as in k_recur. Segment s's
-// M^T is staged in LDS (in the matrix-core operand precision) while segment s+1's map
-// is already in flight into registers.
-template <typename T, int K, int RT>
+// Grid (N, H, V/16): a workgroup carries 16 state rows through the segments of one
+// sequence-head. A link is bound by the vector-memory throughput of its CU (every
+// workgroup reads the whole M^T), so the rows are spread thin over many CUs: at 16 rows a
+// link moves 48 KB per CU (M^T 32 KB, R~ 8 KB, the new state 8 KB) against 96 KB at 64
+// rows. Wave w owns the output columns [w K/4, (w+1) K/4) of the 16 rows, as
+// accumulator tiles of S^T: (S M)^T = M^T S^T, with the wave's rows of M^T as A fragments
+// loaded straight from global memory (the prepasses store M^T in fragment order) and the
+// state, staged in LDS once per link in the matrix-core operand precision, as the B
+// operand of every wave. Maps and R~ rows travel four links ahead in four register
+// buffers; the new state is stored before the next fetch is issued and its registers
+// alternate between links, so no link waits for its own stores.
+template <typename T, int K>
 struct ScanCfg {
-    static constexpr int NT = RT * 4;
-    static constexpr int LDM = K + RPad<T>::row;
-    static constexpr int VEC = Elem<T>::kVec;
-    static constexpr int IM = (K * K / VEC + NT - 1) / NT;  // 16-byte vectors of M^T per thread
-    static constexpr int total = K * LDM * (int)sizeof(T);
+    static constexpr int RT = 16;                       // state rows per workgroup
+    static constexpr int NRT = RT / 16;                 // row tiles
+    static constexpr int NT = 256;
+    static constexpr int KW = K / 64;                   // 16-column tiles per wave
+    static constexpr int NKB = K / 32;                  // k32 slices
+    static constexpr int LDS_ = K + RPad<T>::row;       // staged state row
+    static constexpr int total = RT * LDS_ * (int)sizeof(T);
 };
 
-template <typename T, int K, int RT>
-__global__ __launch_bounds__(RT * 4) void k_scan(ScanArgs a) {
-    using SC = ScanCfg<T, K, RT>;
+template <typename T, int K>
+struct ScanMap {
+    using SC = ScanCfg<T, K>;
+    Frag<T> m[SC::KW][SC::NKB];  // M^T rows (w KW + j) * 16 + ln, k32 slice kb
+    f32x4 r[SC::NRT][SC::KW];    // R~[rt*16 + ln][(w KW + j) * 16 + gq*4 ..]
+};
+
+template <typename T, int K>
+__global__ __launch_bounds__(256) void k_scan(ScanArgs a) {
+    using SC = ScanCfg<T, K>;
+    constexpr int KW = SC::KW;
+    constexpr int NRT = SC::NRT;
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-    T* sM = reinterpret_cast<T*>(smem);
+    T* sS = reinterpret_cast<T*>(smem);
     const int n = blockIdx.x, h = blockIdx.y, vt = blockIdx.z;
     const int H = a.geo.H, V = a.geo.V;
     if (a.modes[(int64_t)n * H + h] != 2) return;
@@ -687,84 +707,115 @@ __global__ __launch_bounds__(RT * 4) void k_scan(ScanArgs a) {
     seq_segs(a.geo, n, nseg, segoff, nchunks, choff);
     if (nseg < 2) return;
     const int tid = threadIdx.x;
-    const int wave = wave_id(), lane = tid & 63, ln = lane & 15;
-    const int row = vt * RT + wave * 16 + ln;
+    const int wave = wave_id(), lane = tid & 63, ln = lane & 15, gq = lane >> 4;
+    const int row0 = vt * SC::RT;  // first state row of the workgroup
+    const int col0 = wave * KW * 16;
     const size_t VK = (size_t)V * K;
     const size_t PS = (size_t)(V + K) * K;  // floats per (segment, head) map
-    f32x4 accS[K / 16];
-    if (a.s0)
-        load_state<K>(accS, a.s0 + ((size_t)n * H + h) * VK, row);
-    else
-#pragma unroll
-        for (int kt = 0; kt < K / 16; ++kt) accS[kt] = zero4();
 
-    // maps two steps ahead, in two register buffers that alternate
-    u32x4 mA[SC::IM], mB[SC::IM];
-    f32x4 rA[K / 16], rB[K / 16];
-    auto fetch = [&](u32x4 (&mreg)[SC::IM], f32x4 (&rreg)[K / 16], int s) {
+    // stage a state held as accumulator tiles: row rt*16 + ln, columns col0 + j*16 + gq*4 ..
+    auto stage = [&](const f32x4 (&x)[NRT][KW]) {
+#pragma unroll
+        for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+            for (int j = 0; j < KW; ++j)
+                *reinterpret_cast<typename Pack4<T>::type*>(sS + (rt * 16 + ln) * SC::LDS_ + col0 + j * 16 + gq * 4) =
+                    Pack4<T>::make(x[rt][j]);
+    };
+    auto tile_off = [&](int rt, int j) { return (size_t)(row0 + rt * 16 + ln) * K + col0 + j * 16 + gq * 4; };
+    {
+        f32x4 s0[NRT][KW];
+#pragma unroll
+        for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+            for (int j = 0; j < KW; ++j)
+                s0[rt][j] = a.s0 ? *reinterpret_cast<const f32x4*>(a.s0 + ((size_t)n * H + h) * VK + tile_off(rt, j))
+                                 : zero4();
+        stage(s0);
+    }
+    auto fetch = [&](ScanMap<T, K>& M, int s) {
         const float* P = a.prep + ((size_t)(segoff + s) * H + h) * PS;
         const T* Mt = reinterpret_cast<const T*>(P + VK);
 #pragma unroll
-        for (int it = 0; it < SC::IM; ++it) {
-            const int e = tid + it * SC::NT;
-            mreg[it] = e < K * K / SC::VEC ? *reinterpret_cast<const u32x4*>(Mt + (size_t)e * SC::VEC)
-                                           : u32x4{0u, 0u, 0u, 0u};
-        }
-        load_state<K>(rreg, P, row);
+        for (int j = 0; j < KW; ++j)
+#pragma unroll
+            for (int kb = 0; kb < SC::NKB; ++kb) frag_row_fo(M.m[j][kb], Mt, K, col0 + j * 16 + ln, kb * 32);
+#pragma unroll
+        for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+            for (int j = 0; j < KW; ++j) M.r[rt][j] = *reinterpret_cast<const f32x4*>(P + tile_off(rt, j));
     };
     // forward: S_{s+1} = S_s M_s + R_s, s = 0 .. nseg-2
     // reverse: G_{s-1} = G_s M_s + R_s, s = nseg-1 .. 1 (adjoint leaving segment s-1)
     auto src_of = [&](int step) { return a.reverse ? nseg - 1 - step : step; };
     const int nsteps = nseg - 1;
-    fetch(mA, rA, src_of(0));
-    if (nsteps > 1) fetch(mB, rB, src_of(1));
-    auto one = [&](u32x4 (&mreg)[SC::IM], f32x4 (&rreg)[K / 16], int step) {
+    constexpr int kDepth = 4;
+    ScanMap<T, K> mb[kDepth];
+    f32x4 accA[NRT][KW], accB[NRT][KW];
+#pragma unroll
+    for (int i = 0; i < kDepth; ++i) fetch(mb[i], src_of(min(i, nsteps - 1)));
+    lds_sync();  // initial state staged
+    auto one = [&](ScanMap<T, K>& M, f32x4 (&acc)[NRT][KW], const f32x4 (&other)[NRT][KW], int step) {
         const int s = src_of(step);
         const int dst = a.reverse ? s - 1 : s + 1;
-        lds_sync();
 #pragma unroll
-        for (int it = 0; it < SC::IM; ++it) {
-            const int e = tid + it * SC::NT;
-            if (e < K * K / SC::VEC) {
-                const int r = (e * SC::VEC) / K, cc = (e * SC::VEC) % K;
-                *reinterpret_cast<u32x4*>(sM + r * SC::LDM + cc) = mreg[it];
-            }
+        for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+            for (int j = 0; j < KW; ++j) acc[rt][j] = M.r[rt][j];
+#pragma unroll
+        for (int kb = 0; kb < SC::NKB; ++kb) {
+            Frag<T> b[NRT];
+#pragma unroll
+            for (int rt = 0; rt < NRT; ++rt) frag_row(b[rt], sS, SC::LDS_, rt * 16 + ln, kb * 32);  // rows of S
+#pragma unroll
+            for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+                for (int j = 0; j < KW; ++j) mma(acc[rt][j], M.m[j][kb], b[rt]);
         }
-        lds_sync();
-        f32x4 nx[K / 16];
+        lds_sync();  // every wave's reads of the staged state are done
+        stage(acc);
+        float* out = a.seginit + ((size_t)(segoff + dst) * H + h) * VK;
 #pragma unroll
-        for (int kt = 0; kt < K / 16; ++kt) nx[kt] = rreg[kt];
-        // this buffer's next map (the last one again past the end)
-        fetch(mreg, rreg, src_of(min(step + 2, nsteps - 1)));
-        Frag<T> sf[K / 32];
+        for (int rt = 0; rt < NRT; ++rt)
 #pragma unroll
-        for (int kb = 0; kb < K / 32; ++kb) frag_acc(sf[kb], accS[2 * kb], accS[2 * kb + 1]);
+            for (int j = 0; j < KW; ++j) *reinterpret_cast<f32x4*>(out + tile_off(rt, j)) = acc[rt][j];
+        // the previous link's stored state stays in its registers until here, so this
+        // link's products never waited for those stores
 #pragma unroll
-        for (int kb = 0; kb < K / 32; ++kb) {
-            Frag<T> fa[K / 16];
+        for (int rt = 0; rt < NRT; ++rt)
 #pragma unroll
-            for (int kt = 0; kt < K / 16; ++kt) frag_row(fa[kt], sM, SC::LDM, kt * 16 + ln, kb * 32);  // rows of M^T
-#pragma unroll
-            for (int kt = 0; kt < K / 16; ++kt) mma(nx[kt], fa[kt], sf[kb]);
-        }
-#pragma unroll
-        for (int kt = 0; kt < K / 16; ++kt) accS[kt] = nx[kt];
-        store_state<K>(accS, a.seginit + ((size_t)(segoff + dst) * H + h) * VK, row);
+            for (int j = 0; j < KW; ++j) hold(other[rt][j]);
+        // this buffer's next map (the last one again past the end), after the stores
+        fetch(M, src_of(min(step + kDepth, nsteps - 1)));
+        lds_sync();  // the new state is staged
     };
-    for (int step = 0; step < nsteps; step += 2) {
-        one(mA, rA, step);
-        if (step + 1 < nsteps) one(mB, rB, step + 1);
+#pragma unroll
+    for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+        for (int j = 0; j < KW; ++j) accB[rt][j] = zero4();
+    // whole groups of links without branches (a link skipped inside the loop would leave the
+    // compiler unsure how many loads are newer than the next map's, and it would wait for
+    // all of them), then the rest
+    int step = 0;
+    for (; step + kDepth <= nsteps; step += kDepth) {
+        one(mb[0], accA, accB, step);
+        one(mb[1], accB, accA, step + 1);
+        one(mb[2], accA, accB, step + 2);
+        one(mb[3], accB, accA, step + 3);
     }
+    if (step < nsteps) one(mb[0], accA, accB, step);
+    if (step + 1 < nsteps) one(mb[1], accB, accA, step + 1);
+    if (step + 2 < nsteps) one(mb[2], accA, accB, step + 2);
 }
 
-template <typename T, int K, int RT>
+template <typename T, int K>
 hipError_t launch_scan_t(const ScanArgs& a, hipStream_t st) {
-    using SC = ScanCfg<T, K, RT>;
-    auto kern = k_scan<T, K, RT>;
+    using SC = ScanCfg<T, K>;
+    auto kern = k_scan<T, K>;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, SC::total);
     if (e != hipSuccess) return e;
-    dim3 grid((unsigned)a.geo.N, (unsigned)a.geo.H, (unsigned)(a.geo.V / RT));
+    dim3 grid((unsigned)a.geo.N, (unsigned)a.geo.H, (unsigned)(a.geo.V / SC::RT));
     hipLaunchKernelGGL(kern, grid, dim3(SC::NT), SC::total, st, a);
     return hipGetLastError();
 }
@@ -879,14 +930,14 @@ hipError_t launch_decide(const DecideArgs& a, hipStream_t st) {
 hipError_t launch_scan(const ScanArgs& a, int dtype, hipStream_t st) {
     if (a.geo.N == 0) return hipSuccess;
     const int K = a.geo.K;
-    // 64 state rows per workgroup whatever the recurrence uses: the scan is a serial chain
+    // 16 state rows per workgroup whatever the recurrence uses: the scan is a serial chain
     // per sequence-head, and more workgroups per head shorten each link
     if (dtype == 0) {
-        if (K == 64) return launch_scan_t<bf16_t, 64, 64>(a, st);
-        if (K == 128) return launch_scan_t<bf16_t, 128, 64>(a, st);
+        if (K == 64) return launch_scan_t<bf16_t, 64>(a, st);
+        if (K == 128) return launch_scan_t<bf16_t, 128>(a, st);
     } else {
-        if (K == 64) return launch_scan_t<float, 64, 64>(a, st);
-        if (K == 128) return launch_scan_t<float, 128, 64>(a, st);
+        if (K == 64) return launch_scan_t<float, 64>(a, st);
+        if (K == 128) return launch_scan_t<float, 128>(a, st);
     }
     return hipErrorInvalidValue;
 }
