@@ -214,8 +214,6 @@ __global__ __launch_bounds__(RT * 4) void k_reverse(RevArgs a) {
         rev_fetch<1>(R, a, tb, cb, h, dcol0);
         rev_fetch<2>(R, a, tb, cb, h, dcol0);
     };
-    if (cbeg < cend) fetch_all(R0, cend - 1);
-    if (kDepth == 2 && cbeg < cend - 1) fetch_all(R1, cend - 2);
     constexpr int NPT = (12 + C::NW - 1) / C::NW;  // P^T tiles per wave
     auto step = [&](RevRegs<T, K, RT>& R, const int ci) {
         const int64_t t0 = sg.bos + (int64_t)ci * 64;
@@ -402,10 +400,7 @@ __global__ __launch_bounds__(RT * 4) void k_reverse(RevArgs a) {
             // dDelta (= dU) for the per-chunk gradients, staged [64][RT] by row j and
             // written out after the next chunk's first barrier
 #pragma unroll
-            for (int jt = 0; jt < 4; ++jt)
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    sDd[(jt * 16 + gq * 4 + i) * C::LDD + wave * 16 + ln] = Elem<T>::from_f(accD[jt][i]);
+            for (int jt = 0; jt < 4; ++jt) put_col4(sDd + (jt * 16 + gq * 4) * C::LDD + wave * 16 + ln, C::LDD, accD[jt]);
         }
         // G^T <- e^Gam G^T + (e^gam Q)^T dO - W^T dDelta
         const float eG = fast_exp(Gm);
@@ -437,12 +432,24 @@ __global__ __launch_bounds__(RT * 4) void k_reverse(RevArgs a) {
         }
         if constexpr (sizeof(T) != 2) rev_fetch<2>(R, a, tn, cnn, h, dcol0);
     };
+    // the entering adjoint may come from a load: wait for it before any prefetch
+#pragma unroll
+    for (int kt = 0; kt < K / 16; ++kt) hold(accG[kt]);
     if constexpr (kDepth == 2) {
-        for (int ci = cend - 1; ci >= cbeg; ci -= 2) {
-            step(R0, ci);
-            if (ci - 1 >= cbeg) step(R1, ci - 1);
+        // pairs of chunks without a branch between them (see the forward recurrence), then
+        // the first chunk
+        if (cbeg < cend) {
+            fetch_all(R0, cend - 1);
+            fetch_all(R1, max(cend - 2, cbeg));
         }
+        int ci = cend - 1;
+        for (; ci - 1 >= cbeg; ci -= 2) {
+            step(R0, ci);
+            step(R1, ci - 1);
+        }
+        if (ci >= cbeg) step(R0, ci);
     } else {
+        if (cbeg < cend) fetch_all(R0, cend - 1);
         for (int ci = cend - 1; ci >= cbeg; --ci) step(R0, ci);
     }
 

@@ -456,6 +456,20 @@ __device__ __forceinline__ void fetch_tile(u32x4 (&x)[N], const T* src, size_t l
     }
 }
 
+// Four accumulator elements into rows r .. r+3 of one LDS column (p points at row r; row
+// stride ld), one scalar store each. The compiler fuses adjacent fp32 LDS stores into
+// ds_write2_b32 and, in some register allocations, encodes the first offset divided by 4
+// once too often, which puts one element in the wrong place; in fp32 an empty asm statement
+// with a memory clobber between the stores keeps them apart.
+template <typename T>
+__device__ __forceinline__ void put_col4(T* p, int ld, const f32x4& x) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        p[i * ld] = Elem<T>::from_f(x[i]);
+        if constexpr (sizeof(T) == 4) asm volatile("" ::: "memory");
+    }
+}
+
 // The registers of fetch_tile into a row-major LDS tile (row stride ld_s), scaled by s.
 template <typename T, int D, int N, int NT = 256>
 __device__ __forceinline__ void put_tile(T* dst, int ld_s, const u32x4 (&x)[N], float s = 1.f) {

@@ -442,8 +442,6 @@ __global__ __launch_bounds__(RT * 4) void k_recur(RecurArgs a) {
         chunk_fetch<1>(R, a, tb, cb, h, ucol0);
         chunk_fetch<2>(R, a, tb, cb, h, ucol0);
     };
-    if (cbeg < cend) fetch_all(R0, cbeg);
-    if (kDepth == 2 && cbeg + 1 < cend) fetch_all(R1, cbeg + 1);
     auto step = [&](ChunkRegs<T, K, RT, kOut>& R, const int ci) {
         const int64_t t0 = sg.bos + (int64_t)ci * 64;
         const int c = min(64, sg.len - ci * 64);
@@ -498,10 +496,7 @@ __global__ __launch_bounds__(RT * 4) void k_recur(RecurArgs a) {
             // Delta for the backward, staged over the unused q tile ([64][RT], row j) and
             // written out after the next chunk's first barrier
 #pragma unroll
-            for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    L.sQ[(rt * 16 + gq * 4 + i) * C::LDU + wave * 16 + ln] = Elem<T>::from_f(accD[rt][i]);
+            for (int rt = 0; rt < 4; ++rt) put_col4(L.sQ + (rt * 16 + gq * 4) * C::LDU + wave * 16 + ln, C::LDU, accD[rt]);
         }
         if constexpr (MODE != kRecurStates) {
             // u and the gate cumsum too: every chunk's loads land together in one burst across
@@ -513,19 +508,30 @@ __global__ __launch_bounds__(RT * 4) void k_recur(RecurArgs a) {
         if (MODE == kRecurOutRec && a.delta) {
             // Delta, staged over the q tile as in the states pass
 #pragma unroll
-            for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    L.sQ[(rt * 16 + gq * 4 + i) * C::LDU + wave * 16 + ln] = Elem<T>::from_f(accD[rt][i]);
+            for (int rt = 0; rt < 4; ++rt) put_col4(L.sQ + (rt * 16 + gq * 4) * C::LDU + wave * 16 + ln, C::LDU, accD[rt]);
         }
         chunk_part2<T, K, RT, kOut>(a, L, accS, accD, accO, t0, c, h, vt * RT, okeep);
     };
+    // the entering state may come from a load: wait for it here, before any prefetch, so the
+    // loop never sees a load into the state registers in flight
+#pragma unroll
+    for (int kt = 0; kt < K / 16; ++kt) hold(accS[kt]);
     if constexpr (kDepth == 2) {
-        for (int ci = cbeg; ci < cend; ci += 2) {
-            step(R0, ci);
-            if (ci + 1 < cend) step(R1, ci + 1);
+        // pairs of chunks without a branch between them (a step skipped inside the loop would
+        // leave the compiler unsure how many loads are newer than the next chunk's, and it
+        // would wait for all of them), then the last chunk
+        if (cbeg < cend) {
+            fetch_all(R0, cbeg);
+            fetch_all(R1, min(cbeg + 1, cend - 1));
         }
+        int ci = cbeg;
+        for (; ci + 2 <= cend; ci += 2) {
+            step(R0, ci);
+            step(R1, ci + 1);
+        }
+        if (ci < cend) step(R0, ci);
     } else {
+        if (cbeg < cend) fetch_all(R0, cbeg);
         for (int ci = cbeg; ci < cend; ++ci) step(R0, ci);
     }
 
@@ -613,29 +619,34 @@ __global__ __launch_bounds__(kThreads) void k_decide(DecideArgs a) {
                 const int avail = rev ? nchunks - cb : cb;
                 uint64_t m = 0;
                 float sum = 0.f, kk = 0.f;
-                for (int w0 = 0; w0 < a.warmup_max; w0 += 8) {
-                    float2 st[8];
+                // the window's statistics in batches of 32 independent loads (one batch up to the
+                // default longest window of one 32-chunk sub-sequence)
+                for (int w0 = 0; w0 < a.warmup_max; w0 += 32) {
+                    float2 st[32];
 #pragma unroll
-                    for (int j = 0; j < 8; ++j) {
+                    for (int j = 0; j < 32; ++j) {
                         const int w = w0 + j + 1;
-                        const int idx = rev ? cb + w - 1 : cb - w;
-                        st[j] = (w < avail && w <= a.warmup_max) ? a.cstat[(choff + idx) * H + h] : make_float2(0.f, 0.f);
+                        // unconditional loads (no branch between them), clamped into the sequence;
+                        // entries past the window are not used
+                        const int idx = rev ? min(cb + w - 1, nchunks - 1) : max(cb - w, 0);
+                        st[j] = a.cstat[(choff + idx) * H + h];
                     }
+                    // (no break inside: the loop unrolls and st stays in registers)
 #pragma unroll
-                    for (int j = 0; j < 8; ++j) {
+                    for (int j = 0; j < 32; ++j) {
                         const int w = w0 + j + 1;
-                        if (w > a.warmup_max) break;
-                        if (w >= avail) {
-                            // this and every longer window start at the sequence start (end)
-                            if (w <= W) m = all;
-                            else m |= all & (~0ull << (w - W));
-                            break;
+                        if (w <= a.warmup_max && w - 1 < avail) {
+                            if (w >= avail) {
+                                // this and every longer window start at the sequence start (end)
+                                m |= w <= W ? all : (all & (~0ull << (w - W)));
+                            } else {
+                                sum += st[j].x;
+                                kk = fmaxf(kk, st[j].y);
+                                if (w >= W && sum <= a.log_eps && kk <= 2.f) m |= 1ull << (w - W);
+                            }
                         }
-                        sum += st[j].x;
-                        kk = fmaxf(kk, st[j].y);
-                        if (w >= W && sum <= a.log_eps && kk <= 2.f) m |= 1ull << (w - W);
                     }
-                    if (w0 + 8 >= avail) break;
+                    if (w0 + 32 >= avail) break;
                 }
                 pass &= m;
             }
