@@ -470,6 +470,28 @@ __device__ __forceinline__ void put_col4(T* p, int ld, const f32x4& x) {
     }
 }
 
+// The registers of fetch_tile into an LDS tile whose rows are in fragment order (see
+// frag_pos), read back with frag_row_fo: one 16-byte LDS read per bf16 row fragment instead
+// of two 8-byte ones. A 16-byte vector holds 4 (fp32) or 8 (bf16) consecutive columns;
+// each run of 4 stays contiguous in fragment order.
+template <typename T, int D, int N, int NT = 256>
+__device__ __forceinline__ void put_tile_fo(T* dst, int ld_s, const u32x4 (&x)[N]) {
+    constexpr int VEC = Elem<T>::kVec;
+    constexpr int NVR = D / VEC;
+#pragma unroll
+    for (int it = 0; it < N; ++it) {
+        const int e = (int)threadIdx.x + it * NT;
+        const int r = e / NVR, c0 = (e % NVR) * VEC;
+        T* row = dst + r * ld_s;
+        if constexpr (sizeof(T) == 2) {
+            *reinterpret_cast<u32x2*>(row + frag_pos(c0)) = u32x2{x[it].x, x[it].y};
+            *reinterpret_cast<u32x2*>(row + frag_pos(c0 + 4)) = u32x2{x[it].z, x[it].w};
+        } else {
+            *reinterpret_cast<u32x4*>(row + frag_pos(c0)) = x[it];
+        }
+    }
+}
+
 // The registers of fetch_tile into a row-major LDS tile (row stride ld_s), scaled by s.
 template <typename T, int D, int N, int NT = 256>
 __device__ __forceinline__ void put_tile(T* dst, int ld_s, const u32x4 (&x)[N], float s = 1.f) {

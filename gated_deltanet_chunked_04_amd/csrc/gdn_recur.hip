@@ -112,8 +112,9 @@ struct ChunkLds {
 template <typename T, int K, int RT, bool kQ>
 __device__ __forceinline__ void chunk_stage(const ChunkRegs<T, K, RT, kQ>& R, const ChunkLds<T, K, RT>& L) {
     using C = RCfg<T, K, RT>;
-    if constexpr (kQ) put_tile<T, K, C::IQ, C::NT>(L.sQ, C::LD, R.q);
-    put_tile<T, K, C::IQ, C::NT>(L.sW, C::LD, R.w);
+    // q and w rows in fragment order: every wave reads them as row fragments only
+    if constexpr (kQ) put_tile_fo<T, K, C::IQ, C::NT>(L.sQ, C::LD, R.q);
+    put_tile_fo<T, K, C::IQ, C::NT>(L.sW, C::LD, R.w);
     put_tile<T, K, C::IQ, C::NT>(L.sK, C::LD, R.k);
     put_tile<T, RT, C::IU, C::NT>(L.sU, C::LDU, R.u);
     if (threadIdx.x < 64) L.sGam[threadIdx.x] = R.gam;
@@ -170,8 +171,8 @@ __device__ __forceinline__ void chunk_part1(const ChunkLds<T, K, RT>& L, const f
             Frag<T> fw[4], fq[4], fa[NPT];
 #pragma unroll
             for (int rt = 0; rt < 4; ++rt) {
-                frag_row(fw[rt], L.sW, C::LD, rt * 16 + ln, kb * 32);
-                if (kOut) frag_row(fq[rt], L.sQ, C::LD, rt * 16 + ln, kb * 32);
+                frag_row_fo(fw[rt], L.sW, C::LD, rt * 16 + ln, kb * 32);
+                if (kOut) frag_row_fo(fq[rt], L.sQ, C::LD, rt * 16 + ln, kb * 32);
             }
 #pragma unroll
             for (int m = 0; m < NPT; ++m)
@@ -235,7 +236,7 @@ __device__ __forceinline__ void chunk_part1(const ChunkLds<T, K, RT>& L, const f
                 for (int m = 0; m < NPT; ++m) {
                     if (pmm[m]) {
                         frag_row(fa[m], L.sK, C::LD, pjt[m] * 16 + ln, kb * 32);
-                        frag_row(fb[m], L.sQ, C::LD, prt[m] * 16 + ln, kb * 32);
+                        frag_row_fo(fb[m], L.sQ, C::LD, prt[m] * 16 + ln, kb * 32);
                     }
                 }
 #pragma unroll
@@ -274,8 +275,8 @@ __device__ __forceinline__ void chunk_part1(const ChunkLds<T, K, RT>& L, const f
             Frag<T> fw[4], fq[4];
 #pragma unroll
             for (int rt = 0; rt < 4; ++rt) {
-                frag_row(fw[rt], L.sW, C::LD, rt * 16 + ln, kb * 32);
-                if (kOut) frag_row(fq[rt], L.sQ, C::LD, rt * 16 + ln, kb * 32);
+                frag_row_fo(fw[rt], L.sW, C::LD, rt * 16 + ln, kb * 32);
+                if (kOut) frag_row_fo(fq[rt], L.sQ, C::LD, rt * 16 + ln, kb * 32);
             }
 #pragma unroll
             for (int rt = 0; rt < 4; ++rt) {
