@@ -110,8 +110,9 @@ struct RevLds {
 template <typename T, int K, int RT>
 __device__ __forceinline__ void rev_stage(const RevRegs<T, K, RT>& R, const RevLds<T, K, RT>& L, float scale) {
     using C = VCfg<T, K, RT>;
-    put_tile<T, K, C::IK, C::NT>(L.sQ, C::LD, R.q);
-    put_tile<T, K, C::IK, C::NT>(L.sK, C::LD, R.k);
+    // q and k rows in fragment order (read as row fragments only); w row-major (read transposed)
+    put_tile_fo<T, K, C::IK, C::NT>(L.sQ, C::LD, R.q);
+    put_tile_fo<T, K, C::IK, C::NT>(L.sK, C::LD, R.k);
     put_tile<T, K, C::IK, C::NT>(L.sW, C::LD, R.w);
 #pragma unroll
     for (int it = 0; it < C::IK; ++it) {
@@ -284,10 +285,10 @@ __global__ __launch_bounds__(RT * 4) void k_reverse(RevArgs a) {
             for (int kb = 0; kb < K / 32; ++kb) {
                 Frag<T> fk[4], fq[NPT];
 #pragma unroll
-                for (int jt = 0; jt < 4; ++jt) frag_row(fk[jt], L.sK, C::LD, jt * 16 + ln, kb * 32);
+                for (int jt = 0; jt < 4; ++jt) frag_row_fo(fk[jt], L.sK, C::LD, jt * 16 + ln, kb * 32);
 #pragma unroll
                 for (int m = 0; m < NPT; ++m)
-                    if (pmm[m]) frag_row(fq[m], L.sQ, C::LD, prt[m] * 16 + ln, kb * 32);
+                    if (pmm[m]) frag_row_fo(fq[m], L.sQ, C::LD, prt[m] * 16 + ln, kb * 32);
 #pragma unroll
                 for (int jt = 0; jt < 4; ++jt) mma(accD[jt], fk[jt], gf[kb]);
 #pragma unroll
@@ -313,7 +314,7 @@ __global__ __launch_bounds__(RT * 4) void k_reverse(RevArgs a) {
                         const int r = prt[m] * 16 + gq * 4 + i;
                         v[i] = (r >= j) ? a.scale * pacc[m][i] * fast_exp(gr[i] - gj) : 0.f;
                     }
-                    store4(L.sPm + j * C::LDP + prt[m] * 16 + gq * 4, v);
+                    store4(L.sPm + j * C::LDP + frag_pos(prt[m] * 16 + gq * 4), v);  // fragment order
                 }
             }
         } else {
@@ -339,8 +340,8 @@ __global__ __launch_bounds__(RT * 4) void k_reverse(RevArgs a) {
 #pragma unroll
                     for (int m = 0; m < NPT; ++m) {
                         if (pmm[m]) {
-                            frag_row(fa[m], L.sQ, C::LD, prt[m] * 16 + ln, kb * 32);
-                            frag_row(fb[m], L.sK, C::LD, pjt[m] * 16 + ln, kb * 32);
+                            frag_row_fo(fa[m], L.sQ, C::LD, prt[m] * 16 + ln, kb * 32);
+                            frag_row_fo(fb[m], L.sK, C::LD, pjt[m] * 16 + ln, kb * 32);
                         }
                     }
 #pragma unroll
@@ -359,7 +360,7 @@ __global__ __launch_bounds__(RT * 4) void k_reverse(RevArgs a) {
                             const int r = prt[m] * 16 + gq * 4 + i;
                             v[i] = (r >= j) ? a.scale * pacc[m][i] * fast_exp(gr[i] - gj) : 0.f;
                         }
-                        store4(L.sPm + j * C::LDP + prt[m] * 16 + gq * 4, v);
+                        store4(L.sPm + j * C::LDP + frag_pos(prt[m] * 16 + gq * 4), v);  // fragment order
                     }
                 }
             }
@@ -368,7 +369,7 @@ __global__ __launch_bounds__(RT * 4) void k_reverse(RevArgs a) {
             for (int kb = 0; kb < K / 32; ++kb) {
                 Frag<T> fa[4];
 #pragma unroll
-                for (int jt = 0; jt < 4; ++jt) frag_row(fa[jt], L.sK, C::LD, jt * 16 + ln, kb * 32);
+                for (int jt = 0; jt < 4; ++jt) frag_row_fo(fa[jt], L.sK, C::LD, jt * 16 + ln, kb * 32);
 #pragma unroll
                 for (int jt = 0; jt < 4; ++jt) mma(accD[jt], fa[jt], gf[kb]);
             }
@@ -391,7 +392,7 @@ __global__ __launch_bounds__(RT * 4) void k_reverse(RevArgs a) {
                 Frag<T> fb, fa[4];
                 frag_col(fb, L.sD, C::LDD, wave * 16 + ln, rb * 32);  // dO column v, slots r
 #pragma unroll
-                for (int jt = 0; jt <= 2 * rb + 1; ++jt) frag_row(fa[jt], L.sPm, C::LDP, jt * 16 + ln, rb * 32);
+                for (int jt = 0; jt <= 2 * rb + 1; ++jt) frag_row_fo(fa[jt], L.sPm, C::LDP, jt * 16 + ln, rb * 32);
 #pragma unroll
                 for (int jt = 0; jt <= 2 * rb + 1; ++jt) mma(accD[jt], fa[jt], fb);
             }

@@ -207,7 +207,7 @@ __device__ __forceinline__ void chunk_part1(const ChunkLds<T, K, RT>& L, const f
                     const int j = pjt[m] * 16 + gq * 4 + i;
                     v[i] = (j <= r) ? pacc[m][i] * fast_exp(gr - gj[i]) : 0.f;
                 }
-                store4(L.sPm + r * C::LDP + pjt[m] * 16 + gq * 4, v);
+                store4(L.sPm + r * C::LDP + frag_pos(pjt[m] * 16 + gq * 4), v);  // fragment order
             }
         }
     } else {
@@ -256,7 +256,7 @@ __device__ __forceinline__ void chunk_part1(const ChunkLds<T, K, RT>& L, const f
                         const int j = pjt[m] * 16 + gq * 4 + i;
                         v[i] = (j <= r) ? pacc[m][i] * fast_exp(gr - gj[i]) : 0.f;
                     }
-                    store4(L.sPm + r * C::LDP + pjt[m] * 16 + gq * 4, v);
+                    store4(L.sPm + r * C::LDP + frag_pos(pjt[m] * 16 + gq * 4), v);  // fragment order
                 }
             }
         }
@@ -306,7 +306,7 @@ __device__ __forceinline__ void chunk_part2(const RecurArgs& a, const ChunkLds<T
         for (int kb = 0; kb < 2; ++kb) {
             Frag<T> fb[4];
 #pragma unroll
-            for (int rt = 2 * kb; rt < 4; ++rt) frag_row(fb[rt], L.sPm, C::LDP, rt * 16 + ln, kb * 32);
+            for (int rt = 2 * kb; rt < 4; ++rt) frag_row_fo(fb[rt], L.sPm, C::LDP, rt * 16 + ln, kb * 32);
 #pragma unroll
             for (int rt = 2 * kb; rt < 4; ++rt) mma(accO[rt], df[kb], fb[rt]);
         }
