@@ -741,8 +741,9 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(BwdChunkArgs a) {
         put_tile<T, K, C::NK, NT>(sQ, C::LDK, R.q);
         put_tile<T, K, C::NK, NT>(sK, C::LDK, R.k);
         // dO enters every product together with the query scale (o = scale S q)
-        put_tile<T, V, C::NV, NT>(sD, C::LDV, R.d, a.scale);
-        put_tile<T, V, C::NV, NT>(sDl, C::LDV, R.dl);
+        // scale * dO and Delta are read as row fragments only: rows in fragment order
+        put_tile_fo<T, V, C::NV, NT>(sD, C::LDV, R.d, a.scale);
+        put_tile_fo<T, V, C::NV, NT>(sDl, C::LDV, R.dl);
         put_tile<T, V, C::NV, NT>(sdU, C::LDV, R.dd);
         if (tid < 64) {
             sGam[tid] = R.gam;
@@ -771,7 +772,7 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(BwdChunkArgs a) {
 #pragma unroll
             for (int kb = 0; kb < K / 32; ++kb) frag_row(qr[kb], sQ, C::LDK, r, kb * 32);
 #pragma unroll
-            for (int vb = 0; vb < V / 32; ++vb) frag_row(dor[vb], sD, C::LDV, r, vb * 32);
+            for (int vb = 0; vb < V / 32; ++vb) frag_row_fo(dor[vb], sD, C::LDV, r, vb * 32);
             // both j tiles (the mask below zeroes j > r): one straight block of independent
             // products instead of a branch per tile
 #pragma unroll
@@ -783,7 +784,7 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(BwdChunkArgs a) {
             for (int vb = 0; vb < V / 32; ++vb) {
                 Frag<T> fd[2];
 #pragma unroll
-                for (int m = 0; m < 2; ++m) frag_row(fd[m], sDl, C::LDV, (2 * hf + m) * 16 + ln, vb * 32);
+                for (int m = 0; m < 2; ++m) frag_row_fo(fd[m], sDl, C::LDV, (2 * hf + m) * 16 + ln, vb * 32);
 #pragma unroll
                 for (int m = 0; m < 2; ++m) mma(dPT[m], fd[m], dor[vb]);
             }
@@ -818,7 +819,7 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(BwdChunkArgs a) {
         {
             Frag<T> dtr[V / 32];
 #pragma unroll
-            for (int vb = 0; vb < V / 32; ++vb) frag_row(dtr[vb], sDl, C::LDV, r, vb * 32);
+            for (int vb = 0; vb < V / 32; ++vb) frag_row_fo(dtr[vb], sDl, C::LDV, r, vb * 32);
 #pragma unroll
             for (int i = 0; i < KH; ++i) dKT[i] = zero4();
 #pragma unroll
@@ -911,7 +912,7 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(BwdChunkArgs a) {
                 Frag<T> fdo[V / 32], fdd[V / 32];
 #pragma unroll
                 for (int vb = 0; vb < V / 32; ++vb) {
-                    frag_row(fdo[vb], sD, C::LDV, rr * 16 + ln, vb * 32);
+                    frag_row_fo(fdo[vb], sD, C::LDV, rr * 16 + ln, vb * 32);
                     Frag<T> f;
                     frag_row(f, sdU, C::LDV, rr * 16 + ln, vb * 32);
                     fdd[vb] = neg(f);
@@ -984,7 +985,7 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(BwdChunkArgs a) {
             }
             sDgs[tid] = d;
         }
-        put_tile<T, V, C::NV, NT>(sV, C::LDV, RV.v);
+        put_tile_fo<T, V, C::NV, NT>(sV, C::LDV, RV.v);  // fragment order
         put_tile<T, 64, C::NX, NT>(sTm, C::LDX, RV.t);
         lds_sync();
         // The next task's operands load over the rest of this one, issued late (where few
@@ -1018,7 +1019,7 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(BwdChunkArgs a) {
             for (int vb = 0; vb < V / 32; ++vb) {
                 Frag<T> fv[2];
 #pragma unroll
-                for (int m = 0; m < 2; ++m) frag_row(fv[m], sV, C::LDV, (2 * hf + m) * 16 + ln, vb * 32);
+                for (int m = 0; m < 2; ++m) frag_row_fo(fv[m], sV, C::LDV, (2 * hf + m) * 16 + ln, vb * 32);
 #pragma unroll
                 for (int m = 0; m < 2; ++m) mma(y[m], fv[m], uf[vb]);
             }
@@ -1033,7 +1034,7 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(BwdChunkArgs a) {
                     const int b = bt * 16 + gq * 4 + e;
                     dT[e] = (b < ra) ? bb[e] * (fast_exp(gb[e]) * x[m][e] + y[m][e]) : 0.f;
                 }
-                store4(sDT + ra * C::LDX + bt * 16 + gq * 4, dT);  // dT[a][b]
+                store4(sDT + ra * C::LDX + frag_pos(bt * 16 + gq * 4), dT);  // dT[a][b], fragment order
             }
         }
         lds_sync();
@@ -1042,8 +1043,8 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(BwdChunkArgs a) {
         // this half's c tiles -------------------------------------------------------------------
         {
             Frag<T> dtf[2];
-            frag_row(dtf[0], sDT, C::LDX, ra, 0);  // dT row a, slots b
-            frag_row(dtf[1], sDT, C::LDX, ra, 32);
+            frag_row_fo(dtf[0], sDT, C::LDX, ra, 0);  // dT row a, slots b
+            frag_row_fo(dtf[1], sDT, C::LDX, ra, 32);
             f32x4 y[2];
 #pragma unroll
             for (int m = 0; m < 2; ++m) y[m] = zero4();
@@ -1163,7 +1164,7 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(BwdChunkArgs a) {
                     frag_col(fu, sdU, C::LDV, vt * 16 + ln, xb * 32);  // dU^T row v, slots x
                     mma(bv, fu, ta[xb]);
                 }
-                dbeta_row += dot4(bv, ld4(sV + ra * C::LDV + vt * 16 + gq * 4));
+                dbeta_row += dot4(bv, ld4(sV + ra * C::LDV + frag_pos(vt * 16 + gq * 4)));
                 if (ra < c) store4(dvp + vt * 16 + gq * 4, bv * ba);
             }
         }

@@ -475,7 +475,7 @@ __device__ __forceinline__ void put_col4(T* p, int ld, const f32x4& x) {
 // of two 8-byte ones. A 16-byte vector holds 4 (fp32) or 8 (bf16) consecutive columns;
 // each run of 4 stays contiguous in fragment order.
 template <typename T, int D, int N, int NT = 256>
-__device__ __forceinline__ void put_tile_fo(T* dst, int ld_s, const u32x4 (&x)[N]) {
+__device__ __forceinline__ void put_tile_fo(T* dst, int ld_s, const u32x4 (&x)[N], float s = 1.f) {
     constexpr int VEC = Elem<T>::kVec;
     constexpr int NVR = D / VEC;
 #pragma unroll
@@ -483,11 +483,12 @@ __device__ __forceinline__ void put_tile_fo(T* dst, int ld_s, const u32x4 (&x)[N
         const int e = (int)threadIdx.x + it * NT;
         const int r = e / NVR, c0 = (e % NVR) * VEC;
         T* row = dst + r * ld_s;
+        const u32x4 y = s == 1.f ? x[it] : scale_vec<T>(x[it], s);
         if constexpr (sizeof(T) == 2) {
-            *reinterpret_cast<u32x2*>(row + frag_pos(c0)) = u32x2{x[it].x, x[it].y};
-            *reinterpret_cast<u32x2*>(row + frag_pos(c0 + 4)) = u32x2{x[it].z, x[it].w};
+            *reinterpret_cast<u32x2*>(row + frag_pos(c0)) = u32x2{y.x, y.y};
+            *reinterpret_cast<u32x2*>(row + frag_pos(c0 + 4)) = u32x2{y.z, y.w};
         } else {
-            *reinterpret_cast<u32x4*>(row + frag_pos(c0)) = x[it];
+            *reinterpret_cast<u32x4*>(row + frag_pos(c0)) = y;
         }
     }
 }
