@@ -470,6 +470,23 @@ __device__ __forceinline__ void put_col4(T* p, int ld, const f32x4& x) {
     }
 }
 
+// frag_col of a tile stored in fragment order (see frag_pos): every run of four
+// consecutive columns that a transpose read takes stays contiguous there, so only the
+// column address changes.
+__device__ __forceinline__ void frag_col_fo(Frag<bf16_t>& f, const bf16_t* base, int ld, int col, int k0) {
+    const int lane = threadIdx.x & 63, ln = lane & 15, gq = lane >> 4;
+    const bf16_t* p = base + (size_t)(k0 + gq * 4 + (ln >> 2)) * ld + frag_pos((col - ln) + 4 * (ln & 3));
+    const u32x2 a = ds_read_tr16(p);
+    const u32x2 b = ds_read_tr16(p + (size_t)16 * ld);
+    f.v = u32x4{a.x, a.y, b.x, b.y};
+}
+__device__ __forceinline__ void frag_col_fo(Frag<float>& f, const float* base, int ld, int col, int k0) {
+    const int gq = threadIdx.x >> 4 & 3;
+    const float* p = base + (size_t)(k0 + gq * 4) * ld + frag_pos(col);
+    f.lo = f32x4{p[0], p[(size_t)ld], p[(size_t)2 * ld], p[(size_t)3 * ld]};
+    f.hi = f32x4{p[(size_t)16 * ld], p[(size_t)17 * ld], p[(size_t)18 * ld], p[(size_t)19 * ld]};
+}
+
 // The registers of fetch_tile into an LDS tile whose rows are in fragment order (see
 // frag_pos), read back with frag_row_fo: one 16-byte LDS read per bf16 row fragment instead
 // of two 8-byte ones. A 16-byte vector holds 4 (fp32) or 8 (bf16) consecutive columns;

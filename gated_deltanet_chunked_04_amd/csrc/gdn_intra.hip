@@ -15,8 +15,8 @@
 // per-token corrections delta_r = beta_r (v_r - S'_r k_r) solve (I + A) Delta = U - W S^T.
 //
 // Persistent workgroups of 4 waves, two per CU, each taking one (chunk, head) at a time.
-// K and V are staged row-major in LDS; T*K
-// and T*V read their columns with LDS transpose loads. The inverse is blocked:
+// K is staged in LDS with its rows in fragment order (one 16-byte read per row fragment
+// of the Gram tiles), V row-major; T*K and T*V read their columns with LDS transpose loads. The inverse is blocked:
 // 16x16 diagonal blocks by forward substitution, then off-diagonal blocks level by
 // level with fp32 matrix-core products. T stays fp32; the products T*K and T*V run on
 // the matrix cores in the input precision with fp32 accumulation. For the backward the
@@ -39,7 +39,7 @@ template <> struct IntraPad<float> { static constexpr int row = 4; };
 
 template <typename T, int K, int V>
 struct IntraSmem {
-    static constexpr int LDK = K + IntraPad<T>::row;   // row-major K (Gram rows, then the W output)
+    static constexpr int LDK = K + IntraPad<T>::row;   // K in fragment order (Gram rows), then the W output
     static constexpr int LDV = V + IntraPad<T>::row;   // row-major V (then the U output)
     static constexpr int off_k = 0;
     static constexpr int off_v = off_k + 64 * LDK * (int)sizeof(T);
@@ -107,7 +107,7 @@ __global__ __launch_bounds__(kThreads) void k_intra(IntraArgs args) {
     for (;;) {
         // ---- stage 1: operands into LDS, gate cumsum --------------------------------
         lds_sync();  // the previous task's LDS reads are done
-        put_tile<T, K>(sK, S::LDK, R.k);
+        put_tile_fo<T, K>(sK, S::LDK, R.k);  // fragment order (read as rows and transposed)
         put_tile<T, V>(sV, S::LDV, R.v);
         const float g_in = R.g, b_in = R.beta;
         // the last task fetches itself again: the fetch stays unconditional
@@ -151,8 +151,8 @@ __global__ __launch_bounds__(kThreads) void k_intra(IntraArgs args) {
                 Frag<T> fa[NTT], fb[NTT];
 #pragma unroll
                 for (int m = 0; m < NTT; ++m) {
-                    frag_row(fa[m], sK, S::LDK, tj[m] * 16 + ln, kb * 32);
-                    frag_row(fb[m], sK, S::LDK, ti[m] * 16 + ln, kb * 32);
+                    frag_row_fo(fa[m], sK, S::LDK, tj[m] * 16 + ln, kb * 32);
+                    frag_row_fo(fb[m], sK, S::LDK, ti[m] * 16 + ln, kb * 32);
                 }
 #pragma unroll
                 for (int m = 0; m < NTT; ++m) mma(acc[m], fa[m], fb[m]);
@@ -239,7 +239,7 @@ __global__ __launch_bounds__(kThreads) void k_intra(IntraArgs args) {
             for (int kb = 0; kb < NKB; ++kb) {
                 if (kb < nkb) {
                     Frag<T> b;
-                    frag_col(b, sK, S::LDK, ct * 16 + ln, kb * 32);  // K^T row ct*16+ln, slots j
+                    frag_col_fo(b, sK, S::LDK, ct * 16 + ln, kb * 32);  // K^T row ct*16+ln, slots j
                     mma(accw[ct], b, aw[kb]);
                 }
             }

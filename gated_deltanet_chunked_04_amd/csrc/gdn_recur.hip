@@ -112,7 +112,9 @@ struct ChunkLds {
 template <typename T, int K, int RT, bool kQ>
 __device__ __forceinline__ void chunk_stage(const ChunkRegs<T, K, RT, kQ>& R, const ChunkLds<T, K, RT>& L) {
     using C = RCfg<T, K, RT>;
-    // q and w rows in fragment order: every wave reads them as row fragments only
+    // q and w rows in fragment order: every wave reads them as row fragments only (k stays
+    // row-major: the prepass and the state pass read it only transposed, and for the output
+    // pass's few P-tile rows fragment order did not pay for its split staging writes)
     if constexpr (kQ) put_tile_fo<T, K, C::IQ, C::NT>(L.sQ, C::LD, R.q);
     put_tile_fo<T, K, C::IQ, C::NT>(L.sW, C::LD, R.w);
     put_tile<T, K, C::IQ, C::NT>(L.sK, C::LD, R.k);
