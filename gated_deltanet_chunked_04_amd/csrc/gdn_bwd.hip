@@ -513,7 +513,10 @@ hipError_t launch_reverse_t(const RevArgs& a, int64_t nsegs_grid, int vtiles, hi
 // fragments of their transposes and lets every lane write four consecutive columns of
 // its row with one vector store.
 //
-// LDS: K stays for both sides. The state side holds S, G, Q, scale * dO, Delta and dDelta
+// LDS: every tile that is read as row fragments (all but S, G and Y) is stored with its
+// rows in fragment order (frag_pos): one 16-byte read per bf16 row fragment, and the
+// transposed reads of the same tiles go through frag_col_fo. K stays for both sides. The
+// state side holds S, G, Q, scale * dO, Delta and dDelta
 // (the L .* dP exchange later goes over Delta). dDelta is the WY side's dU as it stands;
 // dW goes over S once the state side ends, and V, T and two 64x64 scratch matrices of
 // the WY side go into the rest of that space (the hole between dW and dDelta first, then
@@ -738,13 +741,13 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(BwdChunkArgs a) {
         float* sDb = reinterpret_cast<float*>(sm + C::off_db);
         // ---- stage this task (the previous task's LDS reads are done) ---------------------
         lds_sync();
-        put_tile<T, K, C::NK, NT>(sQ, C::LDK, R.q);
-        put_tile<T, K, C::NK, NT>(sK, C::LDK, R.k);
+        put_tile_fo<T, K, C::NK, NT>(sQ, C::LDK, R.q);
+        put_tile_fo<T, K, C::NK, NT>(sK, C::LDK, R.k);
         // dO enters every product together with the query scale (o = scale S q)
         // scale * dO and Delta are read as row fragments only: rows in fragment order
         put_tile_fo<T, V, C::NV, NT>(sD, C::LDV, R.d, a.scale);
         put_tile_fo<T, V, C::NV, NT>(sDl, C::LDV, R.dl);
-        put_tile<T, V, C::NV, NT>(sdU, C::LDV, R.dd);
+        put_tile_fo<T, V, C::NV, NT>(sdU, C::LDV, R.dd);
         if (tid < 64) {
             sGam[tid] = R.gam;
             sBeta[tid] = R.beta;
@@ -770,7 +773,7 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(BwdChunkArgs a) {
         {
             Frag<T> qr[K / 32], dor[V / 32];
 #pragma unroll
-            for (int kb = 0; kb < K / 32; ++kb) frag_row(qr[kb], sQ, C::LDK, r, kb * 32);
+            for (int kb = 0; kb < K / 32; ++kb) frag_row_fo(qr[kb], sQ, C::LDK, r, kb * 32);
 #pragma unroll
             for (int vb = 0; vb < V / 32; ++vb) frag_row_fo(dor[vb], sD, C::LDV, r, vb * 32);
             // both j tiles (the mask below zeroes j > r): one straight block of independent
@@ -792,7 +795,7 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(BwdChunkArgs a) {
             for (int kb = 0; kb < K / 32; ++kb) {
                 Frag<T> fk[2];
 #pragma unroll
-                for (int m = 0; m < 2; ++m) frag_row(fk[m], sK, C::LDK, (2 * hf + m) * 16 + ln, kb * 32);
+                for (int m = 0; m < 2; ++m) frag_row_fo(fk[m], sK, C::LDK, (2 * hf + m) * 16 + ln, kb * 32);
 #pragma unroll
                 for (int m = 0; m < 2; ++m) mma(PmQ[m], fk[m], qr[kb]);
             }
@@ -859,7 +862,7 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(BwdChunkArgs a) {
         // d(gam) from Kt: -e^{Gam-gam_r} sum_k dKt[r][k] K[r][k]; the chunk total gets the sum
         float ktk = 0.f;
 #pragma unroll
-        for (int i = 0; i < KH; ++i) ktk += dot4(dKT[i], ld4(sK + r * C::LDK + (hf * KH + i) * 16 + gq * 4));
+        for (int i = 0; i < KH; ++i) ktk += dot4(dKT[i], ld4(sK + r * C::LDK + frag_pos((hf * KH + i) * 16 + gq * 4)));
         ktk *= ekt;
         drow -= ktk;
         {
@@ -875,22 +878,22 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(BwdChunkArgs a) {
         lds_sync();  // every read of Delta is done: the exchange overwrites it
         // exchange L .* dP: sX[query r][key j]
 #pragma unroll
-        for (int m = 0; m < 2; ++m) store4(sX + r * C::LDX + (2 * hf + m) * 16 + gq * 4, LdP[m]);
+        for (int m = 0; m < 2; ++m) store4(sX + r * C::LDX + frag_pos((2 * hf + m) * 16 + gq * 4), LdP[m]);
         lds_sync();
         // dk terms of the state side for the wave's rows as keys y = r, this half's k tiles:
         // e^{Gam-gam_y} dKt^T + Q^T (L .* dP)[:, y]
         f32x4 dkpart[KH];
         {
             Frag<T> xc[2];
-            frag_col(xc[0], sX, C::LDX, r, 0);  // (L .* dP) column y, slots r'
-            frag_col(xc[1], sX, C::LDX, r, 32);
+            frag_col_fo(xc[0], sX, C::LDX, r, 0);  // (L .* dP) column y, slots r'
+            frag_col_fo(xc[1], sX, C::LDX, r, 32);
 #pragma unroll
             for (int i = 0; i < KH; ++i) {
                 dkpart[i] = dKT[i] * ekt;
 #pragma unroll
                 for (int yb = 0; yb < 2; ++yb) {
                     Frag<T> fq;
-                    frag_col(fq, sQ, C::LDK, (hf * KH + i) * 16 + ln, yb * 32);  // Q^T row k, slots r'
+                    frag_col_fo(fq, sQ, C::LDK, (hf * KH + i) * 16 + ln, yb * 32);  // Q^T row k, slots r'
                     mma(dkpart[i], fq, xc[yb]);
                 }
             }
@@ -914,7 +917,7 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(BwdChunkArgs a) {
                 for (int vb = 0; vb < V / 32; ++vb) {
                     frag_row_fo(fdo[vb], sD, C::LDV, rr * 16 + ln, vb * 32);
                     Frag<T> f;
-                    frag_row(f, sdU, C::LDV, rr * 16 + ln, vb * 32);
+                    frag_row_fo(f, sdU, C::LDV, rr * 16 + ln, vb * 32);
                     fdd[vb] = neg(f);
                 }
 #pragma unroll
@@ -936,21 +939,21 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(BwdChunkArgs a) {
             Frag<T> kc[KW][2];
 #pragma unroll
             for (int j = 0; j < KW; ++j) {
-                frag_col(kc[j][0], sK, C::LDK, k0 + j * 16 + ln, 0);  // K^T row k, slots j'
-                frag_col(kc[j][1], sK, C::LDK, k0 + j * 16 + ln, 32);
+                frag_col_fo(kc[j][0], sK, C::LDK, k0 + j * 16 + ln, 0);  // K^T row k, slots j'
+                frag_col_fo(kc[j][1], sK, C::LDK, k0 + j * 16 + ln, 32);
             }
 #pragma unroll
             for (int m = 0; m < 2; ++m) {
                 const int row = (2 * hf + m) * 16 + ln;
                 const float eg = fast_exp(sGam[row]);
                 Frag<T> xr[2];
-                frag_row(xr[0], sX, C::LDX, row, 0);  // (L .* dP) row r, slots j'
-                frag_row(xr[1], sX, C::LDX, row, 32);
+                frag_row_fo(xr[0], sX, C::LDX, row, 0);  // (L .* dP) row r, slots j'
+                frag_row_fo(xr[1], sX, C::LDX, row, 32);
                 T* dq = reinterpret_cast<T*>(a.dq) + ((t0 + row) * H + h) * K + k0;
                 float qd = 0.f;
 #pragma unroll
                 for (int j = 0; j < KW; ++j) {
-                    qd += dot4(dQT[j][m], ld4(sQ + row * C::LDK + k0 + j * 16 + gq * 4));
+                    qd += dot4(dQT[j][m], ld4(sQ + row * C::LDK + frag_pos(k0 + j * 16 + gq * 4)));
                     f32x4 acc = dQT[j][m] * eg;
                     mma(acc, kc[j][0], xr[0]);
                     mma(acc, kc[j][1], xr[1]);
@@ -966,7 +969,7 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(BwdChunkArgs a) {
 #pragma unroll
                 for (int m = 0; m < 2; ++m) {
                     const int row = (2 * hf + m) * 16 + ln;
-                    store4(sdW + row * C::LDK + k0 + j * 16 + gq * 4, row < c ? dWT[j][m] : zero4());
+                    store4(sdW + row * C::LDK + frag_pos(k0 + j * 16 + gq * 4), row < c ? dWT[j][m] : zero4());
                 }
         }
 
@@ -986,7 +989,7 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(BwdChunkArgs a) {
             sDgs[tid] = d;
         }
         put_tile_fo<T, V, C::NV, NT>(sV, C::LDV, RV.v);  // fragment order
-        put_tile<T, 64, C::NX, NT>(sTm, C::LDX, RV.t);
+        put_tile_fo<T, 64, C::NX, NT>(sTm, C::LDX, RV.t);
         lds_sync();
         // The next task's operands load over the rest of this one, issued late (where few
         // registers are live, so that nothing spills or waits on them) and in groups.
@@ -997,9 +1000,9 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(BwdChunkArgs a) {
         {
             Frag<T> wf[K / 32], uf[V / 32];
 #pragma unroll
-            for (int kb = 0; kb < K / 32; ++kb) frag_row(wf[kb], sdW, C::LDK, ra, kb * 32);
+            for (int kb = 0; kb < K / 32; ++kb) frag_row_fo(wf[kb], sdW, C::LDK, ra, kb * 32);
 #pragma unroll
-            for (int vb = 0; vb < V / 32; ++vb) frag_row(uf[vb], sdU, C::LDV, ra, vb * 32);
+            for (int vb = 0; vb < V / 32; ++vb) frag_row_fo(uf[vb], sdU, C::LDV, ra, vb * 32);
             // both b tiles (the mask below zeroes b >= a)
             f32x4 x[2], y[2];
 #pragma unroll
@@ -1011,7 +1014,7 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(BwdChunkArgs a) {
             for (int kb = 0; kb < K / 32; ++kb) {
                 Frag<T> fk[2];
 #pragma unroll
-                for (int m = 0; m < 2; ++m) frag_row(fk[m], sK, C::LDK, (2 * hf + m) * 16 + ln, kb * 32);
+                for (int m = 0; m < 2; ++m) frag_row_fo(fk[m], sK, C::LDK, (2 * hf + m) * 16 + ln, kb * 32);
 #pragma unroll
                 for (int m = 0; m < 2; ++m) mma(x[m], fk[m], wf[kb]);  // rows b, cols a: (K dW^T)[b][a]
             }
@@ -1052,7 +1055,7 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(BwdChunkArgs a) {
             for (int kb = 0; kb < 2; ++kb) {
                 Frag<T> ft[2];
 #pragma unroll
-                for (int m = 0; m < 2; ++m) frag_row(ft[m], sTm, C::LDX, (2 * hf + m) * 16 + ln, kb * 32);
+                for (int m = 0; m < 2; ++m) frag_row_fo(ft[m], sTm, C::LDX, (2 * hf + m) * 16 + ln, kb * 32);
 #pragma unroll
                 for (int m = 0; m < 2; ++m) mma(y[m], ft[m], dtf[kb]);
             }
@@ -1066,12 +1069,12 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(BwdChunkArgs a) {
         // this half's c tiles
         float dbeta_row = 0.f, dgam_row = 0.f;
         Frag<T> ta[2];
-        frag_col(ta[0], sTm, C::LDX, ra, 0);  // T column a, slots x
-        frag_col(ta[1], sTm, C::LDX, ra, 32);
+        frag_col_fo(ta[0], sTm, C::LDX, ra, 0);  // T column a, slots x
+        frag_col_fo(ta[1], sTm, C::LDX, ra, 32);
         {
             Frag<T> kra[K / 32];
 #pragma unroll
-            for (int kb = 0; kb < K / 32; ++kb) frag_row(kra[kb], sK, C::LDK, ra, kb * 32);
+            for (int kb = 0; kb < K / 32; ++kb) frag_row_fo(kra[kb], sK, C::LDK, ra, kb * 32);
             const float ba = sBeta[ra], ga = sGam[ra];
             f32x4 dd[2], kkk[2];
 #pragma unroll
@@ -1092,7 +1095,7 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(BwdChunkArgs a) {
             for (int kb = 0; kb < K / 32; ++kb) {
                 Frag<T> fk[2];
 #pragma unroll
-                for (int m = 0; m < 2; ++m) frag_row(fk[m], sK, C::LDK, (2 * hf + m) * 16 + ln, kb * 32);
+                for (int m = 0; m < 2; ++m) frag_row_fo(fk[m], sK, C::LDK, (2 * hf + m) * 16 + ln, kb * 32);
 #pragma unroll
                 for (int m = 0; m < 2; ++m) mma(kkk[m], fk[m], kra[kb]);  // rows c, cols a: k_c . k_a
             }
@@ -1119,16 +1122,16 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(BwdChunkArgs a) {
                     const float s = sum_ln(colpart[e]);
                     if (ln == 0) sRed[w * 64 + ct * 16 + gq * 4 + e] = -s;
                 }
-                store4(sMx + ra * C::LDX + ct * 16 + gq * 4, mx);  // Mx[a][c]
+                store4(sMx + ra * C::LDX + frag_pos(ct * 16 + gq * 4), mx);  // Mx[a][c]
             }
         }
         lds_sync();
         // ---- dBk^T = dW^T T, dBv^T = dU^T T (rows k / v, cols a);  dK, dV, this half's tiles ---
         Frag<T> mrow[2], mcol[2];
-        frag_row(mrow[0], sMx, C::LDX, ra, 0);  // Mx row a, slots c
-        frag_row(mrow[1], sMx, C::LDX, ra, 32);
-        frag_col(mcol[0], sMx, C::LDX, ra, 0);  // Mx column a, slots c
-        frag_col(mcol[1], sMx, C::LDX, ra, 32);
+        frag_row_fo(mrow[0], sMx, C::LDX, ra, 0);  // Mx row a, slots c
+        frag_row_fo(mrow[1], sMx, C::LDX, ra, 32);
+        frag_col_fo(mcol[0], sMx, C::LDX, ra, 0);  // Mx column a, slots c
+        frag_col_fo(mcol[1], sMx, C::LDX, ra, 32);
         const float ba = sBeta[ra], ega = fast_exp(sGam[ra]);
         {
             T* dkp = reinterpret_cast<T*>(a.dk) + ((t0 + ra) * H + h) * K;
@@ -1139,14 +1142,14 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(BwdChunkArgs a) {
 #pragma unroll
                 for (int xb = 0; xb < 2; ++xb) {
                     Frag<T> fw, fk;
-                    frag_col(fw, sdW, C::LDK, kt * 16 + ln, xb * 32);  // dW^T row k, slots x
+                    frag_col_fo(fw, sdW, C::LDK, kt * 16 + ln, xb * 32);  // dW^T row k, slots x
                     mma(bk, fw, ta[xb]);
-                    frag_col(fk, sK, C::LDK, kt * 16 + ln, xb * 32);   // K^T row k, slots c
+                    frag_col_fo(fk, sK, C::LDK, kt * 16 + ln, xb * 32);   // K^T row k, slots c
                     mma(mk, fk, mrow[xb]);
                     mma(mk, fk, mcol[xb]);
                 }
                 // dbeta, dgam from Bk = diag(beta e^gam) K
-                const float s = dot4(bk, ld4(sK + ra * C::LDK + kt * 16 + gq * 4));
+                const float s = dot4(bk, ld4(sK + ra * C::LDK + frag_pos(kt * 16 + gq * 4)));
                 dbeta_row += ega * s;
                 dgam_row += ba * ega * s;
                 if (ra < c) store4(dkp + kt * 16 + gq * 4, dkpart[i] + mk + bk * (ba * ega));
@@ -1161,7 +1164,7 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(BwdChunkArgs a) {
 #pragma unroll
                 for (int xb = 0; xb < 2; ++xb) {
                     Frag<T> fu;
-                    frag_col(fu, sdU, C::LDV, vt * 16 + ln, xb * 32);  // dU^T row v, slots x
+                    frag_col_fo(fu, sdU, C::LDV, vt * 16 + ln, xb * 32);  // dU^T row v, slots x
                     mma(bv, fu, ta[xb]);
                 }
                 dbeta_row += dot4(bv, ld4(sV + ra * C::LDV + frag_pos(vt * 16 + gq * 4)));
