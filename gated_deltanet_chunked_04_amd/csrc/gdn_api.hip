@@ -594,7 +594,6 @@ gdn_status gdn_chunk_bwd(const gdn_desc* desc, const void* q, const void* k, con
     if (!reuse) GDN_LAUNCH(kKRecurStates, st, launch_recur(ra, desc->dtype, kRecurStates, p.total_segs, vtiles, st));
     // 3. reverse adjoint pass, with CP mirrored (windows and scan from the sequence end)
     const gdn_status sr = [&]() -> gdn_status {
-    gdn_status s = GDN_OK;
     hipStream_t st = st2;
     RevArgs va;
     memset(&va, 0, sizeof(va));
