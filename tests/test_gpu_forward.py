@@ -39,6 +39,8 @@ CASES = [
     (torch.float32, 64, 64, "exact", dict(seg_chunks=3)),
     (torch.float32, 64, 64, "warmup", dict(seg_chunks=4, warmup_chunks=6)),
     (torch.float32, 128, 128, "exact", dict(seg_chunks=5)),
+    (torch.float32, 128, 64, "exact", dict(seg_chunks=3)),
+    (torch.float32, 64, 128, "warmup", dict(seg_chunks=4, warmup_chunks=3)),
     (torch.bfloat16, 128, 128, "off", {}),
     (torch.bfloat16, 128, 128, "exact", dict(seg_chunks=3)),
     (torch.bfloat16, 128, 128, "warmup", dict(seg_chunks=4, warmup_chunks=3)),
