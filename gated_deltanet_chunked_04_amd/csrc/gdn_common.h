@@ -326,11 +326,23 @@ struct SeqInfo {
 // ---------------------------------------------------------------------------
 // T = (I + A)^{-1} for a 64x64 strictly lower triangular fp32 A in LDS (leading dimension
 // kLdA), written to T in LDS; 256-thread workgroups. Diagonal 16x16 blocks by forward
-// substitution (wave b, lanes 0..15 = the columns of block b), the strictly upper blocks
-// zeroed, then the off-diagonal blocks level by level (T_ij = -T_ii sum_m A_im T_mj) with
+// substitution (wave b, lanes 0..15 = the columns of block b), then the off-diagonal
+// blocks level by level (T_ij = -T_ii sum_m A_im T_mj) with
 // fp32 matrix-core products. Starts and ends with the LDS in a consistent state for the
-// whole workgroup (the caller's barrier before, this routine's last barrier after).
+// whole workgroup (the caller's barrier before, this routine's last barrier after). Writes
+// only the diagonal and strictly lower blocks of T: the caller zeroes the strictly upper
+// blocks once (tri_zero_upper64), since nothing writes them afterwards.
 constexpr int kLdA = 68;
+
+// Zero the strictly upper 16x16 blocks of a 64x64 fp32 T in LDS (256 threads).
+__device__ __forceinline__ void tri_zero_upper64(float* sT) {
+    for (int e = (int)threadIdx.x; e < 6 * 256; e += 256) {
+        const int blk = e >> 8, off = e & 255;
+        const int bi = blk < 3 ? 0 : (blk < 5 ? 1 : 2);
+        const int bj = blk < 3 ? blk + 1 : (blk < 5 ? blk - 1 : 3);
+        sT[(16 * bi + (off >> 4)) * kLdA + 16 * bj + (off & 15)] = 0.f;
+    }
+}
 
 // Y = sum_{m=j}^{i-1} A_{i,m} T_{m,j}; T_{i,j} = -T_{i,i} Y   (16x16 blocks, fp32 matrix cores)
 __device__ __forceinline__ void tri_offdiag_block(float* sA, float* sT, int i, int j) {
@@ -376,13 +388,6 @@ __device__ __forceinline__ void tri_inverse64(float* sA, float* sT) {
         }
 #pragma unroll
         for (int r = 0; r < 16; ++r) sT[(16 * b + r) * kLdA + 16 * b + col] = x[r];
-    }
-    // zero the strictly upper blocks (read by the k32 slices of stage 4)
-    for (int e = tid; e < 6 * 256; e += 256) {
-        const int blk = e >> 8, off = e & 255;
-        const int bi = blk < 3 ? 0 : (blk < 5 ? 1 : 2);
-        const int bj = blk < 3 ? blk + 1 : (blk < 5 ? blk - 1 : 3);
-        sT[(16 * bi + (off >> 4)) * kLdA + 16 * bj + (off & 15)] = 0.f;
     }
     lds_sync();
     if (wave < 3) tri_offdiag_block(sA, sT, wave + 1, wave);

@@ -104,6 +104,9 @@ __global__ __launch_bounds__(kThreads) void k_intra(IntraArgs args) {
     if (t >= ntasks) return;
     IntraRegs<T, K, V> R;
     intra_fetch(R, args, cur);
+    // the strictly upper blocks of T stay zero for every task (read by the k32 slices of
+    // stage 4 and written out with T): zeroed once, before the loop's first barrier
+    tri_zero_upper64(sT);
     for (;;) {
         // ---- stage 1: operands into LDS, gate cumsum --------------------------------
         lds_sync();  // the previous task's LDS reads are done
