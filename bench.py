@@ -143,6 +143,39 @@ def cpu_baseline(inp, tokens, passes):
                       "sequence x head"}
 
 
+def decode_bench(gdn, H, K, V, dtype, reps=50):
+    """The recurrent form after a prefill (gdn_recurrent_fwd), one token per call with the state
+    updated in place: a batch of 64 sequences (priced against the HBM roofline: the call reads
+    and writes every state once, plus q, k, v, g, beta and o) and a single sequence (latency).
+    HIP-event timing over `reps` calls on the current stream."""
+    import torch
+    out = {}
+    for B in (64, 1):
+        gen = torch.Generator().manual_seed(5)
+        q = torch.nn.functional.normalize(torch.randn((B, 1, H, K), generator=gen), dim=-1).to(dtype).cuda()
+        k = torch.nn.functional.normalize(torch.randn((B, 1, H, K), generator=gen), dim=-1).to(dtype).cuda()
+        v = torch.randn((B, 1, H, V), generator=gen).to(dtype).cuda()
+        g = (-torch.nn.functional.softplus(torch.randn((B, 1, H), generator=gen)) * 0.1).cuda()
+        beta = torch.sigmoid(torch.randn((B, 1, H), generator=gen)).cuda()
+        state = (torch.randn((B, H, V, K), generator=gen) * 0.1).cuda()
+        o = torch.empty_like(v)
+        for _ in range(5):
+            gdn.gdn_recurrent_fwd(q, k, v, g, beta, state, state_out=state, o=o)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            gdn.gdn_recurrent_fwd(q, k, v, g, beta, state, state_out=state, o=o)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        es = q.element_size()
+        nbytes = B * H * (2 * V * K * 4 + (2 * K + 2 * V) * es + 8)
+        out[f"B{B}"] = {"H": H, "K": K, "V": V, "tokens_per_call": B, "us_per_call": round(us, 2),
+                        "tokens_per_s": round(B / (us * 1e-6), 1), "GB/s": round(nbytes / (us * 1e-6) / 1e9, 1),
+                        "hbm_frac": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -311,6 +344,7 @@ def main():
     if ms_keep is not None:
         line["keep_forward"] = {"ms_per_step": round(ms_keep, 4),
                                 "tokens_per_s": round(tokens / (ms_keep * 1e-3), 1)}
+    line["decode"] = decode_bench(gdn, H, K, V, q.dtype)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(inp, tokens, args.passes)
     print(json.dumps(line), flush=True)

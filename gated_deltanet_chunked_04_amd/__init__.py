@@ -12,6 +12,7 @@ missing they raise instead of computing anything elsewhere.
                               and the backward that reuses them
   gdn_intra_chunk(...)        the intra-chunk kernel alone (gate cumsum, w, u)
   gdn_cp_modes(...)           per sequence-head CP decision (0 none, 1 warmup, 2 exact)
+  gdn_recurrent_fwd(...)      token-by-token form from a given state (decoding after a prefill)
   chunk_gated_delta_rule(...) autograd wrapper over gdn_chunk_fwd / gdn_chunk_bwd
 """
 from __future__ import annotations
@@ -27,7 +28,7 @@ from ._abi import (CP_MODES, EXPORTS, GDN_DTYPE_BF16, GDN_DTYPE_FP32, GDN_FLAG_K
                    load_library, status_string)
 
 __all__ = ["gdn_plan", "gdn_chunk_fwd", "gdn_chunk_bwd", "gdn_workspace", "gdn_intra_chunk", "gdn_cp_modes",
-           "gdn_profile_enable", "gdn_profile_read", "chunk_gated_delta_rule", "load_library",
+           "gdn_recurrent_fwd", "gdn_profile_enable", "gdn_profile_read", "chunk_gated_delta_rule", "load_library",
            "make_desc", "GdnError"]
 
 
@@ -254,6 +255,30 @@ def gdn_cp_modes(k, v, g, beta, *, cu_seqlens=None, cu_seqlens_host=None, cp_mod
     check(lib.gdn_cp_modes(desc.ref, _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(modes), _ptr(ws),
                            ctypes.c_size_t(ws.numel()), _stream()), "gdn_cp_modes")
     return modes
+
+
+def gdn_recurrent_fwd(q, k, v, g, beta, state=None, *, scale=1.0, state_out=None, o=None):
+    """Recurrent form (decode): the gated delta rule token by token from `state`.
+
+    q, k [B,T,H,K], v [B,T,H,V], g, beta [B,T,H] as in gdn_chunk_fwd (no cu_seqlens); state
+    [B,H,V,K] fp32 or None (zeros), e.g. the final state of gdn_chunk_fwd. Returns (o,
+    state_out); state_out may be `state` itself (updated in place). Runs on the current stream.
+    """
+    B, T, H, K = q.shape
+    V = v.shape[-1]
+    _check_inputs(q, k, v, g, beta, state, B)
+    if state_out is None:
+        state_out = torch.empty((B, H, V, K), dtype=torch.float32, device=q.device)
+    elif (tuple(state_out.shape) != (B, H, V, K) or state_out.dtype != torch.float32
+          or not state_out.is_contiguous() or state_out.device != q.device):
+        raise ValueError(f"state_out: expected contiguous fp32 {(B, H, V, K)} on {q.device}")
+    if o is None:
+        o = torch.empty((B, T, H, V), dtype=q.dtype, device=q.device)
+    desc = make_desc(q, v, scale=scale)
+    check(load_library().gdn_recurrent_fwd(desc.ref, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                           _ptr(state), _ptr(state_out), _ptr(o), _stream()),
+          "gdn_recurrent_fwd")
+    return o, state_out
 
 
 def gdn_profile_enable(enable: bool = True) -> None:

@@ -16,12 +16,12 @@ GDN_OK, GDN_ERR_INVALID_ARG, GDN_ERR_UNSUPPORTED, GDN_ERR_WORKSPACE, GDN_ERR_HIP
 GDN_DTYPE_BF16, GDN_DTYPE_FP32 = 0, 1
 CP_MODES = {"auto": 0, "off": 1, "on": 2, "exact": 3, "warmup": 4}
 GDN_FLAG_KEEP_FORWARD, GDN_FLAG_REUSE_FORWARD = 1, 2
-GDN_ABI_VERSION = 3
+GDN_ABI_VERSION = 4
 
 # Declared entry points of include/gdn.h (checked by the ABI test).
 EXPORTS = ("gdn_abi_version", "gdn_status_string", "gdn_plan", "gdn_chunk_fwd_workspace_size",
            "gdn_chunk_fwd", "gdn_chunk_bwd_workspace_size", "gdn_chunk_bwd", "gdn_intra_chunk",
-           "gdn_cp_modes", "gdn_profile_enable", "gdn_profile_read")
+           "gdn_cp_modes", "gdn_recurrent_fwd", "gdn_profile_enable", "gdn_profile_read")
 
 
 class GdnDesc(ctypes.Structure):
@@ -90,6 +90,8 @@ def load_library(path: str = LIB_PATH):
     lib.gdn_intra_chunk.argtypes = [dp] + [vp] * 7 + [vp, sz, vp]
     lib.gdn_cp_modes.restype = i32
     lib.gdn_cp_modes.argtypes = [dp] + [vp] * 5 + [vp, sz, vp]
+    lib.gdn_recurrent_fwd.restype = i32
+    lib.gdn_recurrent_fwd.argtypes = [dp] + [vp] * 8 + [vp]
     lib.gdn_profile_enable.restype = i32
     lib.gdn_profile_enable.argtypes = [i32]
     lib.gdn_profile_read.restype = i32

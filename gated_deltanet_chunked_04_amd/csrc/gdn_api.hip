@@ -240,10 +240,10 @@ Geo make_geo(const gdn_desc* d, const Plan& p, unsigned char* ws) {
 // ---------------------------------------------------------------------------
 // Kernel timing (gdn_profile_enable / gdn_profile_read).
 enum KernelId { kKTables = 0, kKIntra, kKDecide, kKPrepass, kKScan, kKRecurOut, kKRecurStates,
-                kKBwdPrepass, kKBwdScan, kKBwdReverse, kKBwdChunk, kKCount };
+                kKBwdPrepass, kKBwdScan, kKBwdReverse, kKBwdChunk, kKDecode, kKCount };
 const char* const kKernelNames[kKCount] = {"tables", "intra", "cp_decide", "cp_prepass", "cp_scan",
                                            "recur_out", "recur_states", "bwd_cp_prepass", "bwd_cp_scan",
-                                           "bwd_reverse", "bwd_chunk"};
+                                           "bwd_reverse", "bwd_chunk", "recurrent"};
 struct Pending {
     int kid;
     hipEvent_t start, stop;
@@ -659,6 +659,36 @@ gdn_status gdn_chunk_bwd(const gdn_desc* desc, const void* q, const void* k, con
     ba.scale = desc->scale;
     const int64_t tasks = p.total_chunks * (int64_t)desc->H;
     GDN_LAUNCH(kKBwdChunk, st, launch_bwd_chunk(ba, desc->dtype, (int)std::min<int64_t>(tasks, p.cus), st));
+    return GDN_OK;
+}
+
+gdn_status gdn_recurrent_fwd(const gdn_desc* desc, const void* q, const void* k, const void* v, const float* g,
+                             const float* beta, const float* state_in, float* state_out, void* o, void* stream) {
+    if (!desc) return GDN_ERR_INVALID_ARG;
+    for (int i = 0; i < 5; ++i)
+        if (desc->reserved[i] != 0) return GDN_ERR_INVALID_ARG;
+    if (desc->cu_seqlens || desc->cu_seqlens_host || desc->flags) return GDN_ERR_INVALID_ARG;
+    if (desc->B < 1 || desc->T < 0 || desc->H < 1 || desc->K < 1 || desc->V < 1) return GDN_ERR_INVALID_ARG;
+    if (!(desc->K == 64 || desc->K == 128) || !(desc->V == 64 || desc->V == 128)) return GDN_ERR_UNSUPPORTED;
+    if (desc->dtype != GDN_DTYPE_BF16 && desc->dtype != GDN_DTYPE_FP32) return GDN_ERR_INVALID_ARG;
+    if (!isfinite(desc->scale)) return GDN_ERR_INVALID_ARG;
+    if (desc->B > INT32_MAX || desc->H > 65535) return GDN_ERR_UNSUPPORTED;
+    if (!state_out || (desc->T > 0 && (!q || !k || !v || !g || !beta || !o))) return GDN_ERR_INVALID_ARG;
+    DecodeArgs da{};
+    da.q = q;
+    da.k = k;
+    da.v = v;
+    da.g = g;
+    da.beta = beta;
+    da.s_in = state_in;
+    da.s_out = state_out;
+    da.o = o;
+    da.B = desc->B;
+    da.T = desc->T;
+    da.H = desc->H;
+    da.scale = desc->scale;
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    GDN_LAUNCH(kKDecode, st, launch_decode(da, desc->dtype, (int)desc->K, (int)desc->V, st));
     return GDN_OK;
 }
 

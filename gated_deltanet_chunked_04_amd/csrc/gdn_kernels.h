@@ -266,4 +266,19 @@ hipError_t launch_reverse(const RevArgs& a, int dtype, int mode, int64_t nsegs_g
 // grid: persistent workgroups (one per CU; each walks tasks gc * H + h with a grid stride)
 hipError_t launch_bwd_chunk(const BwdChunkArgs& a, int dtype, int grid, hipStream_t st);
 
+// Recurrent form (decode): T tokens of B sequences from a given state.
+struct DecodeArgs {
+    const void* q;            // [B,T,H,K]
+    const void* k;            // [B,T,H,K]
+    const void* v;            // [B,T,H,V]
+    const float* g;           // [B,T,H]
+    const float* beta;        // [B,T,H]
+    const float* s_in;        // [B,H,V,K] or null (zeros)
+    float* s_out;             // [B,H,V,K] (may be s_in)
+    void* o;                  // [B,T,H,V]
+    int64_t B, T, H;
+    float scale;
+};
+hipError_t launch_decode(const DecodeArgs& a, int dtype, int K, int V, hipStream_t st);
+
 }  // namespace gdn

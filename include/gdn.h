@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 3
+#define GDN_ABI_VERSION 4
 
 typedef enum gdn_status {
     GDN_OK = 0,
@@ -188,6 +188,22 @@ gdn_status gdn_chunk_bwd(const gdn_desc* desc, const void* q, const void* k, con
                          void* dq, void* dk, void* dv, float* dg, float* dbeta,
                          float* d_initial_state,
                          void* workspace, size_t workspace_bytes, void* stream);
+
+/* Recurrent form: the gated delta rule token by token from a given state, for decoding
+ * after a prefill (the pages' interface continues a call from the previous one's state,
+ * ollai.cn article, "how to use"). Every sequence b has desc->T tokens (T >= 0; a decoder
+ * passes 1 or a few); no cu_seqlens, no CP, no workspace, desc->flags 0.
+ *   q, k [B,T,H,K]; v, o [B,T,H,V] (desc->dtype); g, beta [B,T,H] fp32 (layouts above)
+ *   state_in  : [B,H,V,K] fp32 state entering the first token, or NULL (zeros); typically
+ *               the final_state of gdn_chunk_fwd or of the previous call
+ *   state_out : [B,H,V,K] fp32 state after the last token (required); may be state_in
+ *               itself (updated in place)
+ * One workgroup per (sequence, head) keeps its state in registers across the T tokens; the
+ * state is read and written once per call. Same status codes as the calls above (K, V not
+ * in {64,128}: GDN_ERR_UNSUPPORTED). */
+gdn_status gdn_recurrent_fwd(const gdn_desc* desc, const void* q, const void* k, const void* v,
+                             const float* g, const float* beta, const float* state_in,
+                             float* state_out, void* o, void* stream);
 
 /* Intra-chunk step alone (the first fused kernel): chunk-local cumulative gate
  * sum and the WY factors, for kernel-level checks. With gam the chunk-local

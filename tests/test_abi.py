@@ -34,7 +34,7 @@ def test_exports_every_declared_symbol(lib):
     assert set(declared) == set(_abi.EXPORTS)
     for name in declared:
         assert hasattr(lib, name), name
-    assert lib.gdn_abi_version() == _abi.GDN_ABI_VERSION == 3
+    assert lib.gdn_abi_version() == _abi.GDN_ABI_VERSION == 4
 
 
 def test_status_strings(lib):
@@ -169,6 +169,22 @@ def test_call_errors_before_launch(lib):
     assert lib.gdn_chunk_fwd(keep.ref, p, p, p, p, p, None, p, None, p, nb, None) == 3
     assert lib.gdn_intra_chunk(d.ref, p, p, p, p, None, p, p, p, nb, None) == 1
     assert lib.gdn_cp_modes(d.ref, p, p, p, p, None, p, nb, None) == 1
+
+
+def test_recurrent_errors_before_launch(lib):
+    """The recurrent (decode) entry point checks its arguments on the host."""
+    p = ctypes.c_void_p(0x1000)
+    d = desc(T=1, H=2)
+    assert lib.gdn_recurrent_fwd(d.ref, p, p, p, p, p, None, None, p, None) == 1  # no state_out
+    assert lib.gdn_recurrent_fwd(d.ref, None, p, p, p, p, None, p, p, None) == 1  # no q with T > 0
+    for field, val, code in (("K", 96, 2), ("V", 32, 2), ("B", 0, 1), ("T", -1, 1), ("dtype", 5, 1),
+                             ("flags", 1, 1)):
+        d2 = desc(T=1, H=2)
+        setattr(d2.c, field, val)
+        assert lib.gdn_recurrent_fwd(d2.ref, p, p, p, p, p, None, p, p, None) == code, field
+    d2 = desc(T=1, H=2)
+    d2.c.cu_seqlens = 0x1000  # no packed sequences in the recurrent form
+    assert lib.gdn_recurrent_fwd(d2.ref, p, p, p, p, p, None, p, p, None) == 1
 
 
 @pytest.mark.parametrize("kw", [dict(), dict(B=1, H=64, T=4096), dict(T=1000, H=2, K=64, V=64, dtype=torch.float32)])
