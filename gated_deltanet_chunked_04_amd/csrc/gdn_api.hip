@@ -71,7 +71,7 @@ gdn_status make_plan(const gdn_desc* d, Plan& p) {
     if (!(d->K == 64 || d->K == 128) || !(d->V == 64 || d->V == 128)) return GDN_ERR_UNSUPPORTED;
     if (d->dtype != GDN_DTYPE_BF16 && d->dtype != GDN_DTYPE_FP32) return GDN_ERR_INVALID_ARG;
     if (!isfinite(d->scale)) return GDN_ERR_INVALID_ARG;
-    if (d->cp_mode < GDN_CP_AUTO || d->cp_mode > GDN_CP_WARMUP) return GDN_ERR_INVALID_ARG;
+    if (d->cp_mode < GDN_CP_AUTO || d->cp_mode > GDN_CP_PAGES) return GDN_ERR_INVALID_ARG;
     if (d->warmup_chunks < 0 || d->warmup_chunks > 16) return GDN_ERR_INVALID_ARG;
     if (d->warmup_max_chunks < 0) return GDN_ERR_INVALID_ARG;
     if (d->seg_chunks < 0 || d->num_cus < 0) return GDN_ERR_INVALID_ARG;
@@ -111,26 +111,31 @@ gdn_status make_plan(const gdn_desc* d, Plan& p) {
     if (d->H * std::max(d->K, d->V) * 64 * 4 >= ((int64_t)1 << 31)) return GDN_ERR_UNSUPPORTED;
 
     p.cus = d->num_cus > 0 ? d->num_cus : query_cus();
-    // AutoCP
+    // AutoCP. The recurrence runs one workgroup per (sequence-head, row tile, sub-sequence):
+    // one per CU at V = K = 128 (8 waves, ~95 KB of LDS), two otherwise.
     const int64_t NH = (int64_t)p.N * d->H;
+    const int vtiles = (int)(d->V / recur_rows((int)d->V, (int)d->K));
+    const int per_cu = recur_rows((int)d->V, (int)d->K) == 128 ? 1 : 2;
+    const int64_t target = (int64_t)per_cu * p.cus;  // workgroups to aim for
+    const int64_t units = NH * vtiles;                // workgroups per sub-sequence layer
     bool cp = false;
     switch (d->cp_mode) {
-        case GDN_CP_AUTO: cp = (NH <= 40) || (NH <= 56 && p.max_len >= 8192); break;
+        case GDN_CP_AUTO:
+            // split when the grid would fill at most half of the slots without it and the longest
+            // sequence spans two sub-sequences of the minimum length (measured on this part:
+            // N*H = 64 at 8K tokens, forward 0.67 -> 0.34 ms; the pages' rule keeps it off there)
+            cp = 2 * units <= target && max_nt >= 32;
+            break;
+        case GDN_CP_PAGES: cp = (NH <= 40) || (NH <= 56 && p.max_len >= 8192); break;
         case GDN_CP_OFF: cp = false; break;
         default: cp = true; break;
     }
     p.forced = d->cp_mode == GDN_CP_WARMUP ? 1 : (d->cp_mode == GDN_CP_EXACT ? 2 : 0);
-    const int vtiles = (int)(d->V / recur_rows((int)d->V, (int)d->K));
     int64_t seg_len = std::max<int64_t>(max_nt, 1);
     if (cp) {
         if (d->seg_chunks > 0) {
             seg_len = d->seg_chunks;
         } else {
-            // One recurrence workgroup per CU at V = K = 128 (8 waves, ~95 KB of LDS), two otherwise.
-            const int cus = p.cus;
-            const int per_cu = recur_rows((int)d->V, (int)d->K) == 128 ? 1 : 2;
-            const int64_t target = (int64_t)per_cu * cus;       // workgroups to aim for
-            const int64_t units = NH * vtiles;                   // workgroups per segment layer
             const int64_t want = std::max<int64_t>(1, target / std::max<int64_t>(units, 1));
             seg_len = std::max<int64_t>(16, (max_nt + want - 1) / want);
         }

@@ -33,8 +33,10 @@
  * w and u, an optional intra-card context-parallel (CP) preprocessing step
  * gives every sub-sequence its initial state, and an inter-chunk recurrence
  * kernel produces O and the final state. CP turns on by itself for small
- * batch x heads ("AutoCP": B*H <= 40, or B*H <= 56 with seq_len >= 8192) and
- * picks per sequence-head either the exact correction or a sliding-window
+ * batch x heads ("AutoCP"; the pages' thresholds, B*H <= 40 or B*H <= 56 with
+ * seq_len >= 8192, were tuned for a 132-SM part: here the default turns CP on when
+ * the recurrence would otherwise leave compute units idle, GDN_CP_PAGES keeps the
+ * pages' rule) and picks per sequence-head either the exact correction or a sliding-window
  * warmup of a few chunks where the gate decay makes the warmup exact within
  * tolerance ("gate-driven" warmup, "core advantages").
  *
@@ -57,7 +59,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 4
+#define GDN_ABI_VERSION 5
 
 typedef enum gdn_status {
     GDN_OK = 0,
@@ -73,11 +75,16 @@ typedef enum gdn_dtype {
 } gdn_dtype;
 
 typedef enum gdn_cp_mode {
-    GDN_CP_AUTO = 0,   /* shape rule decides; per sequence-head gate test picks warmup or exact */
+    GDN_CP_AUTO = 0,   /* CP when the recurrence would leave compute units idle without it: the
+                          sequence-heads' row tiles fill at most half of its workgroup slots
+                          and the longest sequence spans two sub-sequences of 16 chunks or
+                          more; per sequence-head gate test picks warmup or exact */
     GDN_CP_OFF = 1,    /* one serial pass per sequence-head */
     GDN_CP_ON = 2,     /* CP regardless of the shape rule; per sequence-head gate test */
     GDN_CP_EXACT = 3,  /* CP, exact correction for every sequence-head */
-    GDN_CP_WARMUP = 4  /* CP, warmup for every sequence-head (caller asserts fast decay) */
+    GDN_CP_WARMUP = 4, /* CP, warmup for every sequence-head (caller asserts fast decay) */
+    GDN_CP_PAGES = 5   /* the pages' AutoCP thresholds, tuned for a 132-SM part: CP iff
+                          N*H <= 40, or N*H <= 56 and the longest sequence >= 8192 tokens */
 } gdn_cp_mode;
 
 /* desc->flags: keeping the forward's intermediates for the backward of a training step.

@@ -3,7 +3,11 @@ header declares, plans as the AutoCP rule says and rejects bad arguments before
 touching the device.
 
 AutoCP rule (FlashQLA pages, ollai.cn article, "core advantages"): CP turns on
-when batch x heads <= 40, or batch x heads <= 56 with seq_len >= 8192.
+when batch x heads <= 40, or batch x heads <= 56 with seq_len >= 8192. Those
+thresholds were set for a 132-SM part; the default here turns CP on when the
+recurrence grid (one workgroup per sequence-head and row tile) fills at most half
+of its slots on the chip (one workgroup per CU at K = V = 128, two otherwise) and
+the longest sequence spans 32 chunks or more. cp_mode="pages" keeps the pages' rule.
 """
 import ctypes
 import os
@@ -34,7 +38,7 @@ def test_exports_every_declared_symbol(lib):
     assert set(declared) == set(_abi.EXPORTS)
     for name in declared:
         assert hasattr(lib, name), name
-    assert lib.gdn_abi_version() == _abi.GDN_ABI_VERSION == 4
+    assert lib.gdn_abi_version() == _abi.GDN_ABI_VERSION == 5
 
 
 def test_status_strings(lib):
@@ -52,16 +56,7 @@ def plan(**kw):
     return gdn.gdn_plan(desc(**kw))
 
 
-@pytest.mark.parametrize("B,H,T,on", [
-    (1, 40, 100000, True), (1, 41, 100000, True), (1, 41, 8191, False), (1, 41, 8192, True),
-    (1, 56, 8192, True), (1, 57, 8192, False), (8, 5, 20000, True), (8, 6, 20000, True),
-    (8, 7, 20000, True), (8, 8, 20000, False), (2, 20, 4096, True), (1, 40, 4096, True),
-])
-def test_autocp_rule(B, H, T, on):
-    p = plan(B=B, H=H, T=T)
-    # CP only splits when a sequence is longer than one sub-sequence
-    rule = (B * H <= 40) or (B * H <= 56 and T >= 8192)
-    assert rule == on
+def check_cp_plan(p, B, T, rule):
     if not rule:
         assert p["cp_on"] == 0
         assert p["total_segments"] == B
@@ -73,6 +68,38 @@ def test_autocp_rule(B, H, T, on):
             assert p["total_segments"] == B * -(-nt // p["seg_chunks"])
 
 
+@pytest.mark.parametrize("B,H,T,on", [
+    (1, 40, 100000, True), (1, 41, 100000, True), (1, 41, 8191, False), (1, 41, 8192, True),
+    (1, 56, 8192, True), (1, 57, 8192, False), (8, 5, 20000, True), (8, 6, 20000, True),
+    (8, 7, 20000, True), (8, 8, 20000, False), (2, 20, 4096, True), (1, 40, 4096, True),
+])
+def test_autocp_pages_rule(B, H, T, on):
+    p = plan(B=B, H=H, T=T, cp_mode="pages")
+    # CP only splits when a sequence is longer than one sub-sequence
+    rule = (B * H <= 40) or (B * H <= 56 and T >= 8192)
+    assert rule == on
+    check_cp_plan(p, B, T, rule)
+
+
+@pytest.mark.parametrize("B,H,T,K,V,cus,on", [
+    (1, 16, 32768, 128, 128, 256, True), (4, 16, 8192, 128, 128, 256, True),
+    (4, 32, 8192, 128, 128, 256, True), (1, 129, 8192, 128, 128, 256, False),
+    (16, 16, 4096, 128, 128, 256, False), (1, 64, 2048, 128, 128, 256, True),
+    (1, 64, 1985, 128, 128, 256, True), (1, 64, 1984, 128, 128, 256, False),
+    (1, 256, 8192, 64, 64, 256, True), (1, 257, 8192, 64, 64, 256, False),
+    (1, 128, 8192, 64, 128, 256, True), (1, 129, 8192, 64, 128, 256, False),
+    (1, 256, 8192, 128, 64, 256, True), (1, 257, 8192, 128, 64, 256, False),
+    (1, 66, 8192, 128, 128, 132, True), (1, 67, 8192, 128, 128, 132, False),
+])
+def test_autocp_rule(B, H, T, K, V, cus, on):
+    p = plan(B=B, H=H, T=T, K=K, V=V, num_cus=cus)
+    per_cu = 1 if K == V == 128 else 2
+    vtiles = 1 if (K == V == 128 or V == 64) else 2
+    rule = 2 * B * H * vtiles <= per_cu * cus and (T + 63) // 64 >= 32
+    assert rule == on
+    check_cp_plan(p, B, T, rule)
+
+
 def test_workload_plans():
     # batch-1 agentic prefill: 16 heads x 512 chunks -> CP on, 16 sub-sequences of 32 chunks
     p = plan(B=1, H=16, T=32768)
@@ -80,8 +107,8 @@ def test_workload_plans():
     # one TP8 shard of a 256K prompt
     p = plan(B=1, H=8, T=262144)
     assert p["cp_on"] == 1 and p["seg_chunks"] == 128 and p["total_segments"] == 32
-    # tiny case: CP by rule but a single sub-sequence
-    p = plan(B=1, H=2, T=256, K=64, V=64, dtype=torch.float32)
+    # tiny case: CP by the pages' rule but a single sub-sequence
+    p = plan(B=1, H=2, T=256, K=64, V=64, dtype=torch.float32, cp_mode="pages")
     assert p["cp_on"] == 0 and p["total_chunks"] == 4
     # forced modes always split long sequences, off never does
     assert plan(B=4, H=32, T=32768, cp_mode="exact")["cp_on"] == 1
@@ -110,7 +137,7 @@ def test_varlen_plan():
     assert p["num_seqs"] == 5
     assert p["total_chunks"] == sum((n + 63) // 64 for n in lens)
     assert p["max_len"] == 20000
-    assert p["cp_on"] == 1  # N*H = 20 <= 40
+    assert p["cp_on"] == 1  # N*H = 20: 20 of 256 recurrence slots
     segs = sum(max(1, -(-((n + 63) // 64) // p["seg_chunks"])) for n in lens)
     assert p["total_segments"] == segs
 
@@ -119,7 +146,7 @@ def test_argument_errors(lib):
     d = desc()
     out = _abi.GdnPlanInfo()
     bad = [("K", 96), ("V", 32), ("H", 0), ("B", 0), ("T", -1), ("chunk", 32), ("dtype", 7),
-           ("cp_mode", 9), ("warmup_chunks", 17), ("warmup_eps", 1.5), ("warmup_max_chunks", -1),
+           ("cp_mode", 6), ("warmup_chunks", 17), ("warmup_eps", 1.5), ("warmup_max_chunks", -1),
            ("warmup_max_chunks", 7), ("warmup_max_chunks", 72)]
     codes = {"K": 2, "V": 2, "chunk": 2}
     for field, val in bad:

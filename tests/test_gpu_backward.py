@@ -282,3 +282,16 @@ def test_backward_longer_warmup_window(gpu_lib):
         out = gpu_bwd(d, cp_mode="on", seg_chunks=32, **extra)
         print(extra, compare(out, ref, 1e-2), flush=True)
 
+
+
+def test_backward_autocp_fills_idle_units(gpu_lib):
+    """The backward under the default AutoCP at N*H = 48 and 2560 tokens (CP on here, off by the
+    pages' thresholds), one slowly decaying head in exact mode; sampled heads against the oracle."""
+    gdn = gpu_lib
+    inp = with_grads(small_inputs(B=2, T=2560, H=24, seed=19))
+    inp["g"][:, :, 5] = -0.3 / 64  # -4.8 over a 16-chunk window: exact
+    d = to_dev(inp)
+    assert gdn.gdn_plan(gdn.make_desc(d["q"], d["v"]))["cp_on"] == 1
+    out = gpu_bwd(d)
+    heads = [0, 5, 23]
+    compare({n: out[n].cpu() for n in NAMES}, oracle_bwd(inp, heads=heads), 1e-2, heads=heads)

@@ -8,7 +8,7 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_helpers import check, gpu_fwd, mid_decay_inputs, oracle, rel_l2, small_inputs, to_dev, tol_for  # noqa: F401
+from gpu_helpers import BF16_TOL, check, gpu_fwd, mid_decay_inputs, oracle, rel_l2, small_inputs, to_dev, tol_for  # noqa: F401
 from oracle.chunked import chunked_fwd
 
 pytestmark = pytest.mark.gpu
@@ -143,3 +143,25 @@ def test_cp_longer_warmup_window(gpu_lib):
         e_s = check(sT, s_ref, 1e-2, f"final_state {extra}")
         print(f"{extra} rel_l2 o={e_o:.2e} final={e_s:.2e}", flush=True)
 
+
+
+def test_autocp_fills_idle_units(gpu_lib):
+    """Default AutoCP at a shape the pages' thresholds leave serial: N*H = 48 (> 40) at 2560
+    tokens fills 48 of the 256 recurrence slots, so CP is on; one head decays slowly enough to
+    take the exact correction. Sampled heads against the oracle, all heads against CP off."""
+    gdn = gpu_lib
+    inp = small_inputs(B=2, T=2560, H=24, seed=9)
+    inp["g"][:, :, 5] = -0.3 / 64  # -4.8 over a 16-chunk window: exact
+    d = to_dev(inp)
+    assert gdn.gdn_plan(gdn.make_desc(d["q"], d["v"]))["cp_on"] == 1
+    assert gdn.gdn_plan(gdn.make_desc(d["q"], d["v"], cp_mode="pages"))["cp_on"] == 0
+    modes = gdn.gdn_cp_modes(d["k"], d["v"], d["g"], d["beta"]).cpu()
+    assert set(modes.flatten().tolist()) == {1, 2}, modes
+    o, sT = gpu_fwd(d)
+    heads = [0, 5, 23]
+    o_ref, s_ref = oracle(inp, heads=heads)
+    check(o[:, :, heads], o_ref, BF16_TOL, "o")
+    check(sT[:, heads], s_ref, BF16_TOL, "final_state")
+    o2, s2 = gpu_fwd(d, cp_mode="pages")
+    check(o, o2.double().cpu(), BF16_TOL, "o vs serial")
+    check(sT, s2.double().cpu(), BF16_TOL, "final_state vs serial")
