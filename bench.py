@@ -15,7 +15,8 @@ step's dominant kernel (algorithmic bytes over its HIP-event-timed launch
 duration) and the CPU oracle timed on this host's cores. The headline step
 recomputes the forward's intra-chunk results in the backward; "keep_forward"
 reports the opt-in variant whose backward starts from the forward's kept
-workspace instead (more memory held between the passes, less backward work).
+workspace instead (more memory held between the passes, less backward work);
+"qk_l2norm" the same step on raw q and k, normalised inside the library.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--pass both|fwd|bwd]
                   [--no-cpu-baseline]
@@ -176,6 +177,47 @@ def decode_bench(gdn, H, K, V, dtype, reps=50):
     return out
 
 
+def l2norm_leg(gdn, dev, cu, cu_host, cp, timed, steps):
+    """The same step with the q/k L2 normalisation inside the library (GDN_FLAG_QK_L2NORM):
+    its time, and the two normalisation kernels against the HBM roofline. The forward kernel
+    reads and writes every q and k row once (4 row passes); the backward one reads the raw
+    rows and the gradients and writes the gradients (6 row passes)."""
+    import torch
+    q, k, v, g, beta, s0 = (dev[x] for x in ("q", "k", "v", "g", "beta", "initial_state"))
+    kw = dict(cu_seqlens=cu, cu_seqlens_host=cu_host, cp_mode=cp, qk_l2norm=True)
+    ws = gdn.gdn_workspace(q, v, **kw)
+    o = torch.empty_like(v)
+    B, T, H, K = q.shape
+    N = B if cu is None else int(cu.numel()) - 1
+    sT = torch.empty((N, H, v.shape[-1], K), dtype=torch.float32, device=q.device)
+    grads = dict(dq=torch.empty_like(q), dk=torch.empty_like(k), dv=torch.empty_like(v),
+                 dg=torch.empty_like(g), dbeta=torch.empty_like(beta),
+                 d_initial_state=torch.empty_like(sT))
+
+    def step():
+        gdn.gdn_chunk_fwd(q, k, v, g, beta, s0, workspace=ws, o=o, final_state=sT, **kw)
+        gdn.gdn_chunk_bwd(q, k, v, g, beta, dev["d_o"], s0, dev["d_final_state"], workspace=ws,
+                          out=grads, **kw)
+
+    step()
+    ms = timed(step, steps)
+    gdn.gdn_profile_enable(True)
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    kt = gdn.gdn_profile_read()
+    gdn.gdn_profile_enable(False)
+    row_bytes = q.numel() * q.element_size()  # all q rows (and as many k rows)
+    out = {"ms_per_step": round(ms, 4), "kernels": {}}
+    for name, passes in (("qk_l2norm", 4), ("qk_l2norm_bwd", 6)):
+        n, tot = kt[name]
+        us = 1e3 * tot / n
+        gbs = passes * row_bytes / (us * 1e-6) / 1e9
+        out["kernels"][name] = {"avg_launch_us": round(us, 2), "algorithmic_bytes": passes * row_bytes,
+                                "GB/s": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4)}
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -278,6 +320,7 @@ def main():
     if do_fwd and do_bwd:
         step_keep()
         ms_keep = timed(step_keep, args.steps)
+    l2 = l2norm_leg(gdn, dev, cu, cu_host, cp, timed, args.steps) if (do_fwd and do_bwd) else None
 
     # Per-kernel durations: one more round of steps with every launch bracketed by HIP
     # events on the launch stream (separate from the timed loops above).
@@ -344,6 +387,9 @@ def main():
     if ms_keep is not None:
         line["keep_forward"] = {"ms_per_step": round(ms_keep, 4),
                                 "tokens_per_s": round(tokens / (ms_keep * 1e-3), 1)}
+    if l2 is not None:
+        l2["overhead_ms"] = round(l2["ms_per_step"] - ms, 4)
+        line["qk_l2norm"] = l2
     line["decode"] = decode_bench(gdn, H, K, V, q.dtype)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(inp, tokens, args.passes)

@@ -24,7 +24,7 @@ import numpy as np
 import torch
 
 from ._abi import (CP_MODES, EXPORTS, GDN_DTYPE_BF16, GDN_DTYPE_FP32, GDN_FLAG_KEEP_FORWARD,  # noqa: F401
-                   GDN_FLAG_REUSE_FORWARD, GdnDesc, GdnError, GdnKernelTime, GdnPlanInfo, check,
+                   GDN_FLAG_QK_L2NORM, GDN_FLAG_REUSE_FORWARD, GdnDesc, GdnError, GdnKernelTime, GdnPlanInfo, check,
                    load_library, status_string)
 
 __all__ = ["gdn_plan", "gdn_chunk_fwd", "gdn_chunk_bwd", "gdn_workspace", "gdn_intra_chunk", "gdn_cp_modes",
@@ -45,7 +45,7 @@ class Desc:
 
     def __init__(self, B, T, H, K, V, dtype, *, scale=1.0, cu_seqlens=None, cu_seqlens_host=None,
                  cp_mode="auto", warmup_chunks=0, seg_chunks=0, warmup_eps=0.0, num_cus=0, flags=0,
-                 warmup_max_chunks=0):
+                 warmup_max_chunks=0, qk_l2norm=False):
         d = GdnDesc()
         d.B, d.T, d.H, d.K, d.V = int(B), int(T), int(H), int(K), int(V)
         d.chunk = 64
@@ -77,7 +77,7 @@ class Desc:
         d.seg_chunks = int(seg_chunks)
         d.warmup_eps = float(warmup_eps)
         d.num_cus = int(num_cus)
-        d.flags = int(flags)
+        d.flags = int(flags) | (GDN_FLAG_QK_L2NORM if qk_l2norm else 0)
         self.c = d
 
     @property
@@ -97,12 +97,12 @@ def gdn_plan(desc: Desc) -> dict:
 
 
 def gdn_workspace(q, v, *, cu_seqlens=None, cu_seqlens_host=None, cp_mode="auto", warmup_chunks=0,
-                  seg_chunks=0, warmup_eps=0.0, warmup_max_chunks=0):
+                  seg_chunks=0, warmup_eps=0.0, warmup_max_chunks=0, qk_l2norm=False):
     """A workspace large enough for gdn_chunk_fwd(keep_for_backward=True) and for
     gdn_chunk_bwd(reuse_forward=True) with the same shapes and options."""
     kw = dict(cu_seqlens=cu_seqlens, cu_seqlens_host=cu_seqlens_host, cp_mode=cp_mode,
               warmup_chunks=warmup_chunks, seg_chunks=seg_chunks, warmup_eps=warmup_eps,
-              warmup_max_chunks=warmup_max_chunks)
+              warmup_max_chunks=warmup_max_chunks, qk_l2norm=qk_l2norm)
     lib = load_library()
     f, b = ctypes.c_size_t(), ctypes.c_size_t()
     # the descriptors stay referenced through the calls: they own the host copy of cu_seqlens
@@ -148,8 +148,11 @@ def _num_seqs(q, cu_seqlens):
 def gdn_chunk_fwd(q, k, v, g, beta, initial_state=None, *, scale=1.0, cu_seqlens=None,
                   cu_seqlens_host=None, output_final_state=True, cp_mode="auto", warmup_chunks=0,
                   seg_chunks=0, warmup_eps=0.0, warmup_max_chunks=0, workspace=None, o=None, final_state=None,
-                  keep_for_backward=False):
+                  keep_for_backward=False, qk_l2norm=False):
     """Forward. Returns (o, final_state or None). Runs on the current stream.
+
+    qk_l2norm=True takes raw q and k and runs the path on their rows scaled to
+    x / sqrt(sum x^2 + 1e-6) (normalised inside the library, into the workspace).
 
     keep_for_backward=True leaves the intra-chunk results (gate cumsum, W, U, T), the CP
     decisions, the sub-sequence entry states, every chunk's entry state and Delta in `workspace`
@@ -162,7 +165,7 @@ def gdn_chunk_fwd(q, k, v, g, beta, initial_state=None, *, scale=1.0, cu_seqlens
         raise ValueError("keep_for_backward needs a caller-owned workspace (gdn_workspace)")
     desc = make_desc(q, v, scale=scale, cu_seqlens=cu_seqlens, cu_seqlens_host=cu_seqlens_host,
                      cp_mode=cp_mode, warmup_chunks=warmup_chunks, seg_chunks=seg_chunks,
-                     warmup_eps=warmup_eps, warmup_max_chunks=warmup_max_chunks,
+                     warmup_eps=warmup_eps, warmup_max_chunks=warmup_max_chunks, qk_l2norm=qk_l2norm,
                      flags=GDN_FLAG_KEEP_FORWARD if keep_for_backward else 0)
     lib = load_library()
     nbytes = ctypes.c_size_t()
@@ -185,8 +188,11 @@ def gdn_chunk_fwd(q, k, v, g, beta, initial_state=None, *, scale=1.0, cu_seqlens
 def gdn_chunk_bwd(q, k, v, g, beta, d_o, initial_state=None, d_final_state=None, *, scale=1.0,
                   cu_seqlens=None, cu_seqlens_host=None, cp_mode="auto", warmup_chunks=0, seg_chunks=0,
                   warmup_eps=0.0, warmup_max_chunks=0, workspace=None, need_d_initial_state=True, out=None,
-                  reuse_forward=False):
+                  reuse_forward=False, qk_l2norm=False):
     """Backward. Returns dict(dq, dk, dv, dg, dbeta, d_initial_state); `out` may hold them preallocated.
+
+    qk_l2norm=True: the forward normalised q and k (see gdn_chunk_fwd); dq and dk are with respect
+    to the raw q and k.
 
     reuse_forward=True takes the forward's intermediates from `workspace`, which must be the buffer a
     gdn_chunk_fwd(keep_for_backward=True) call on the same inputs and options wrote, untouched since.
@@ -205,7 +211,7 @@ def gdn_chunk_bwd(q, k, v, g, beta, d_o, initial_state=None, d_final_state=None,
         raise ValueError("reuse_forward needs the forward's workspace")
     desc = make_desc(q, v, scale=scale, cu_seqlens=cu_seqlens, cu_seqlens_host=cu_seqlens_host,
                      cp_mode=cp_mode, warmup_chunks=warmup_chunks, seg_chunks=seg_chunks,
-                     warmup_eps=warmup_eps, warmup_max_chunks=warmup_max_chunks,
+                     warmup_eps=warmup_eps, warmup_max_chunks=warmup_max_chunks, qk_l2norm=qk_l2norm,
                      flags=GDN_FLAG_REUSE_FORWARD if reuse_forward else 0)
     lib = load_library()
     nbytes = ctypes.c_size_t()
@@ -224,10 +230,11 @@ def gdn_chunk_bwd(q, k, v, g, beta, d_o, initial_state=None, d_final_state=None,
     return out
 
 
-def gdn_intra_chunk(k, v, g, beta, *, cu_seqlens=None, cu_seqlens_host=None):
-    """The intra-chunk kernel alone: returns (gam [B,T,H] fp32, w [B,T,H,K], u [B,T,H,V])."""
+def gdn_intra_chunk(k, v, g, beta, *, cu_seqlens=None, cu_seqlens_host=None, qk_l2norm=False):
+    """The intra-chunk kernel alone: returns (gam [B,T,H] fp32, w [B,T,H,K], u [B,T,H,V]).
+    qk_l2norm=True normalises the k rows first."""
     B, T, H, K = k.shape
-    desc = make_desc(k, v, cu_seqlens=cu_seqlens, cu_seqlens_host=cu_seqlens_host)
+    desc = make_desc(k, v, cu_seqlens=cu_seqlens, cu_seqlens_host=cu_seqlens_host, qk_l2norm=qk_l2norm)
     lib = load_library()
     nbytes = ctypes.c_size_t()
     check(lib.gdn_chunk_fwd_workspace_size(desc.ref, ctypes.byref(nbytes)), "gdn_chunk_fwd_workspace_size")
@@ -241,12 +248,12 @@ def gdn_intra_chunk(k, v, g, beta, *, cu_seqlens=None, cu_seqlens_host=None):
 
 
 def gdn_cp_modes(k, v, g, beta, *, cu_seqlens=None, cu_seqlens_host=None, cp_mode="auto",
-                 warmup_chunks=0, seg_chunks=0, warmup_eps=0.0, warmup_max_chunks=0):
+                 warmup_chunks=0, seg_chunks=0, warmup_eps=0.0, warmup_max_chunks=0, qk_l2norm=False):
     """Per sequence-head CP decision [N, H] int32: 0 no split, 1 warmup, 2 exact."""
     N = _num_seqs(k, cu_seqlens)
     desc = make_desc(k, v, cu_seqlens=cu_seqlens, cu_seqlens_host=cu_seqlens_host, cp_mode=cp_mode,
                      warmup_chunks=warmup_chunks, seg_chunks=seg_chunks, warmup_eps=warmup_eps,
-              warmup_max_chunks=warmup_max_chunks)
+                     warmup_max_chunks=warmup_max_chunks, qk_l2norm=qk_l2norm)
     lib = load_library()
     nbytes = ctypes.c_size_t()
     check(lib.gdn_chunk_fwd_workspace_size(desc.ref, ctypes.byref(nbytes)), "gdn_chunk_fwd_workspace_size")
@@ -297,13 +304,14 @@ def gdn_profile_read() -> dict:
 
 class _GDNFunction(torch.autograd.Function):
     @staticmethod
-    def forward(ctx, q, k, v, g, beta, initial_state, scale, cu_seqlens, cp_mode, keep):
-        ws = gdn_workspace(q, v, cu_seqlens=cu_seqlens, cp_mode=cp_mode) if keep else None
+    def forward(ctx, q, k, v, g, beta, initial_state, scale, cu_seqlens, cp_mode, keep, l2):
+        ws = gdn_workspace(q, v, cu_seqlens=cu_seqlens, cp_mode=cp_mode, qk_l2norm=l2) if keep else None
         o, sT = gdn_chunk_fwd(q, k, v, g, beta, initial_state, scale=scale, cu_seqlens=cu_seqlens,
-                              cp_mode=cp_mode, workspace=ws, keep_for_backward=keep)
+                              cp_mode=cp_mode, workspace=ws, keep_for_backward=keep, qk_l2norm=l2)
         ctx.save_for_backward(q, k, v, g, beta, initial_state, cu_seqlens)
         ctx.scale = scale
         ctx.cp_mode = cp_mode
+        ctx.l2 = l2
         ctx.ws = ws
         return o, sT
 
@@ -314,23 +322,25 @@ class _GDNFunction(torch.autograd.Function):
         gr = gdn_chunk_bwd(q, k, v, g, beta, d_o.contiguous(), s0,
                            None if d_sT is None else d_sT.contiguous(), scale=ctx.scale,
                            cu_seqlens=cu, cp_mode=ctx.cp_mode, need_d_initial_state=s0 is not None,
-                           workspace=ws, reuse_forward=ws is not None)
+                           workspace=ws, reuse_forward=ws is not None, qk_l2norm=ctx.l2)
         return (gr["dq"], gr["dk"], gr["dv"], gr["dg"], gr["dbeta"], gr["d_initial_state"],
-                None, None, None, None)
+                None, None, None, None, None)
 
 
 def chunk_gated_delta_rule(q, k, v, g, beta, scale: float = 1.0, initial_state=None,
                            output_final_state: bool = True, cu_seqlens=None, cp_mode: str = "auto",
-                           keep_intermediates: bool = False):
+                           keep_intermediates: bool = False, qk_l2norm: bool = False):
     """High-level call: (o, final_state) with autograd through gdn_chunk_bwd.
 
     q, k: [B,T,H,K]; v: [B,T,H,V] (bf16 or fp32); g (natural-log decay) and beta: [B,T,H] fp32;
     initial_state: [N,H,V,K] fp32 or None; cu_seqlens: int32 [N+1] device tensor (B must be 1).
     keep_intermediates=True holds the forward's workspace (W, U, T, gate cumsum, CP entry states,
     chunk states and Delta) until the backward, which then skips recomputing them: more memory,
-    less backward time.
+    less backward time. qk_l2norm=True normalises q and k rows inside the library
+    (x / sqrt(sum x^2 + 1e-6)); gradients flow to the raw q and k.
     """
     o, sT = _GDNFunction.apply(q, k, v, g, beta, initial_state, scale, cu_seqlens, cp_mode,
                                bool(keep_intermediates and torch.is_grad_enabled()
-                                    and any(x.requires_grad for x in (q, k, v, g, beta))))
+                                    and any(x.requires_grad for x in (q, k, v, g, beta))),
+                               bool(qk_l2norm))
     return (o, sT) if output_final_state else (o, None)

@@ -15,7 +15,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build", "gdn")
 LIB = os.path.join(HERE, "libgdn.so")
-SOURCES = ["gdn_api.hip", "gdn_intra.hip", "gdn_recur.hip", "gdn_bwd.hip", "gdn_decode.hip"]
+SOURCES = ["gdn_api.hip", "gdn_intra.hip", "gdn_recur.hip", "gdn_bwd.hip", "gdn_decode.hip", "gdn_norm.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",

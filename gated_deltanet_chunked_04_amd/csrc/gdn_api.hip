@@ -16,6 +16,7 @@
 
 #include "../../include/gdn.h"
 #include "gdn_kernels.h"
+#include "gdn_norm.h"
 
 namespace gdn {
 namespace {
@@ -44,7 +45,7 @@ struct Plan {
     int32_t forced = 0;
     int32_t esize = 2;
     // forward workspace
-    size_t o_gam = 0, o_w = 0, o_u = 0, o_cstat = 0, o_bos = 0, o_len = 0, o_choff = 0, o_segoff = 0,
+    size_t o_qn = 0, o_kn = 0, o_gam = 0, o_w = 0, o_u = 0, o_cstat = 0, o_bos = 0, o_len = 0, o_choff = 0, o_segoff = 0,
            o_ctab = 0, o_stab = 0, o_modes = 0, o_seginit = 0, o_prep = 0, fwd_bytes = 0;
     // backward workspace: the forward's layout, then these
     size_t o_modes_r = 0, o_seginit_r = 0, o_prep_r = 0, o_h = 0, o_gst = 0, o_tm = 0, o_dl = 0, o_ddl = 0,
@@ -65,7 +66,8 @@ gdn_status make_plan(const gdn_desc* d, Plan& p) {
     if (!d) return GDN_ERR_INVALID_ARG;
     for (int i = 0; i < 5; ++i)
         if (d->reserved[i] != 0) return GDN_ERR_INVALID_ARG;
-    if (d->flags & ~(GDN_FLAG_KEEP_FORWARD | GDN_FLAG_REUSE_FORWARD)) return GDN_ERR_INVALID_ARG;
+    if (d->flags & ~(GDN_FLAG_KEEP_FORWARD | GDN_FLAG_REUSE_FORWARD | GDN_FLAG_QK_L2NORM))
+        return GDN_ERR_INVALID_ARG;
     if (d->B < 1 || d->T < 0 || d->H < 1 || d->K < 1 || d->V < 1) return GDN_ERR_INVALID_ARG;
     if (!(d->chunk == 0 || d->chunk == 64)) return GDN_ERR_UNSUPPORTED;
     if (!(d->K == 64 || d->K == 128) || !(d->V == 64 || d->V == 128)) return GDN_ERR_UNSUPPORTED;
@@ -173,6 +175,10 @@ gdn_status make_plan(const gdn_desc* d, Plan& p) {
         off = align_up(off + bytes);
         return o;
     };
+    if (d->flags & GDN_FLAG_QK_L2NORM) {  // normalised q and k, first: the same offsets in both layouts
+        p.o_qn = take(T * H * K * p.esize);
+        p.o_kn = take(T * H * K * p.esize);
+    }
     p.o_gam = take(T * H * 4);
     p.o_w = take(T * H * K * p.esize);
     p.o_u = take(T * H * V * p.esize);
@@ -245,10 +251,11 @@ Geo make_geo(const gdn_desc* d, const Plan& p, unsigned char* ws) {
 // ---------------------------------------------------------------------------
 // Kernel timing (gdn_profile_enable / gdn_profile_read).
 enum KernelId { kKTables = 0, kKIntra, kKDecide, kKPrepass, kKScan, kKRecurOut, kKRecurStates,
-                kKBwdPrepass, kKBwdScan, kKBwdReverse, kKBwdChunk, kKDecode, kKCount };
+                kKBwdPrepass, kKBwdScan, kKBwdReverse, kKBwdChunk, kKDecode, kKL2Norm, kKL2NormBwd, kKCount };
 const char* const kKernelNames[kKCount] = {"tables", "intra", "cp_decide", "cp_prepass", "cp_scan",
                                            "recur_out", "recur_states", "bwd_cp_prepass", "bwd_cp_scan",
-                                           "bwd_reverse", "bwd_chunk", "recurrent"};
+                                           "bwd_reverse", "bwd_chunk", "recurrent", "qk_l2norm",
+                                           "qk_l2norm_bwd"};
 struct Pending {
     int kid;
     hipEvent_t start, stop;
@@ -342,6 +349,25 @@ gdn_status check_ws(const Plan& p, size_t need, void* ws, size_t bytes) {
     if (!ws || bytes < need) return GDN_ERR_WORKSPACE;
     if (reinterpret_cast<uintptr_t>(ws) % kAlign) return GDN_ERR_WORKSPACE;
     (void)p;
+    return GDN_OK;
+}
+
+// With GDN_FLAG_QK_L2NORM: normalise the q rows (when q is given) and the k rows into the
+// workspace and point q and k at the normalised copies; a no-op otherwise.
+gdn_status run_l2norm(const gdn_desc* d, const Plan& p, unsigned char* ws, const void*& q, const void*& k,
+                      hipStream_t st) {
+    if (!(d->flags & GDN_FLAG_QK_L2NORM)) return GDN_OK;
+    const int64_t rows = p.Ttot * (int64_t)d->H;
+    NormArgs na{};
+    na.x0 = q;
+    na.y0 = ws + p.o_qn;
+    na.rows0 = q ? rows : 0;
+    na.x1 = k;
+    na.y1 = ws + p.o_kn;
+    na.rows1 = rows;
+    if (rows > 0) GDN_LAUNCH(kKL2Norm, st, launch_l2norm(na, d->dtype, (int)d->K, false, st));
+    if (q) q = ws + p.o_qn;
+    k = ws + p.o_kn;
     return GDN_OK;
 }
 
@@ -465,6 +491,7 @@ gdn_status gdn_chunk_fwd(const gdn_desc* desc, const void* q, const void* k, con
     float* gam = reinterpret_cast<float*>(ws + p.o_gam);
     void* w = ws + p.o_w;
     void* u = ws + p.o_u;
+    if ((s = run_l2norm(desc, p, ws, q, k, st)) != GDN_OK) return s;
     // with GDN_FLAG_KEEP_FORWARD the intra pass also leaves T for the backward
     if ((s = run_intra(desc, p, ws, k, v, g, beta, gam, w, u, st,
                        (desc->flags & GDN_FLAG_KEEP_FORWARD) ? ws + p.o_tm : nullptr)) != GDN_OK)
@@ -541,8 +568,19 @@ gdn_status gdn_chunk_bwd(const gdn_desc* desc, const void* q, const void* k, con
     float* gam = reinterpret_cast<float*>(ws + p.o_gam);
     void* w = ws + p.o_w;
     void* u = ws + p.o_u;
-    // 1. the forward's intra-chunk pass (kept by a GDN_FLAG_KEEP_FORWARD forward, or recomputed)
+    // 1. the forward's intra-chunk pass (kept by a GDN_FLAG_KEEP_FORWARD forward, or recomputed),
+    // on the normalised q and k with GDN_FLAG_QK_L2NORM (kept too, at the same offsets)
     const bool reuse = (desc->flags & GDN_FLAG_REUSE_FORWARD) != 0;
+    const void* q_raw = q;
+    const void* k_raw = k;
+    if (desc->flags & GDN_FLAG_QK_L2NORM) {
+        if (reuse) {
+            q = ws + p.o_qn;
+            k = ws + p.o_kn;
+        } else if ((s = run_l2norm(desc, p, ws, q, k, st)) != GDN_OK) {
+            return s;
+        }
+    }
     if (!reuse && (s = run_intra(desc, p, ws, k, v, g, beta, gam, w, u, st, ws + p.o_tm)) != GDN_OK) return s;
     const int rt = recur_rows((int)desc->V, (int)desc->K);
     const int vtiles = (int)(desc->V / rt);
@@ -664,6 +702,16 @@ gdn_status gdn_chunk_bwd(const gdn_desc* desc, const void* q, const void* k, con
     ba.scale = desc->scale;
     const int64_t tasks = p.total_chunks * (int64_t)desc->H;
     GDN_LAUNCH(kKBwdChunk, st, launch_bwd_chunk(ba, desc->dtype, (int)std::min<int64_t>(tasks, p.cus), st));
+    // 5. dq and dk back through the normalisation to the raw rows, in place
+    if ((desc->flags & GDN_FLAG_QK_L2NORM) && p.Ttot > 0) {
+        NormArgs na{};
+        na.x0 = q_raw;
+        na.y0 = dq;
+        na.x1 = k_raw;
+        na.y1 = dk;
+        na.rows0 = na.rows1 = p.Ttot * (int64_t)desc->H;
+        GDN_LAUNCH(kKL2NormBwd, st, launch_l2norm(na, desc->dtype, (int)desc->K, true, st));
+    }
     return GDN_OK;
 }
 
@@ -706,7 +754,10 @@ gdn_status gdn_intra_chunk(const gdn_desc* desc, const void* k, const void* v, c
     if (p.Ttot > 0 && (!k || !v || !g || !beta || !gam_out || !w_out || !u_out)) return GDN_ERR_INVALID_ARG;
     if ((s = check_ws(p, p.fwd_bytes, workspace, workspace_bytes)) != GDN_OK) return s;
     unsigned char* ws = static_cast<unsigned char*>(workspace);
-    return run_intra(desc, p, ws, k, v, g, beta, gam_out, w_out, u_out, reinterpret_cast<hipStream_t>(stream));
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    const void* no_q = nullptr;
+    if ((s = run_l2norm(desc, p, ws, no_q, k, st)) != GDN_OK) return s;
+    return run_intra(desc, p, ws, k, v, g, beta, gam_out, w_out, u_out, st);
 }
 
 gdn_status gdn_cp_modes(const gdn_desc* desc, const void* k, const void* v, const float* g, const float* beta,
@@ -718,6 +769,8 @@ gdn_status gdn_cp_modes(const gdn_desc* desc, const void* k, const void* v, cons
     if ((s = check_ws(p, p.fwd_bytes, workspace, workspace_bytes)) != GDN_OK) return s;
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     unsigned char* ws = static_cast<unsigned char*>(workspace);
+    const void* no_q = nullptr;
+    if ((s = run_l2norm(desc, p, ws, no_q, k, st)) != GDN_OK) return s;
     if ((s = run_intra(desc, p, ws, k, v, g, beta, reinterpret_cast<float*>(ws + p.o_gam), ws + p.o_w,
                        ws + p.o_u, st)) != GDN_OK)
         return s;

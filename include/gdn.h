@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 5
+#define GDN_ABI_VERSION 6
 
 typedef enum gdn_status {
     GDN_OK = 0,
@@ -101,6 +101,18 @@ typedef enum gdn_cp_mode {
  *                          no other call on it since except REUSE_FORWARD backwards. */
 #define GDN_FLAG_KEEP_FORWARD 1
 #define GDN_FLAG_REUSE_FORWARD 2
+
+/* GDN_FLAG_QK_L2NORM: q and k are raw; the path first scales every row of K values (one token,
+ * one head) to x / sqrt(sum x^2 + 1e-6) and runs on those rows, the preprocessing the pages place
+ * ahead of the fused kernels (edge.aivizor.me community post, its account of the chunked-prefill
+ * pipeline) with the unit-norm q and k their workloads use. The normalised copies live at the
+ * start of the workspace (2 x T x H x K values in the input dtype more, in both layouts).
+ * gdn_chunk_bwd then returns dq and dk with respect to the raw q and k:
+ * dx = r (dxhat - xhat (xhat . dxhat)), r = (sum x^2 + 1e-6)^(-1/2). With
+ * GDN_FLAG_REUSE_FORWARD the normalised copies come from the kept forward, which must have had
+ * this flag too. gdn_intra_chunk and gdn_cp_modes normalise k. Not accepted by
+ * gdn_recurrent_fwd. */
+#define GDN_FLAG_QK_L2NORM 4
 
 /* Problem descriptor. Zero-initialise, then fill. */
 typedef struct gdn_desc {

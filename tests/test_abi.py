@@ -38,7 +38,7 @@ def test_exports_every_declared_symbol(lib):
     assert set(declared) == set(_abi.EXPORTS)
     for name in declared:
         assert hasattr(lib, name), name
-    assert lib.gdn_abi_version() == _abi.GDN_ABI_VERSION == 5
+    assert lib.gdn_abi_version() == _abi.GDN_ABI_VERSION == 6
 
 
 def test_status_strings(lib):
@@ -157,7 +157,7 @@ def test_argument_errors(lib):
     d2.c.reserved[3] = 1
     assert lib.gdn_plan(d2.ref, ctypes.byref(out)) == 1
     # unknown flag bits
-    for bad_flag in (4, 8, 1 << 30, -1):
+    for bad_flag in (8, 16, 1 << 30, -1):
         d2 = desc()
         d2.c.flags = bad_flag
         assert lib.gdn_plan(d2.ref, ctypes.byref(out)) == 1, bad_flag
@@ -205,7 +205,7 @@ def test_recurrent_errors_before_launch(lib):
     assert lib.gdn_recurrent_fwd(d.ref, p, p, p, p, p, None, None, p, None) == 1  # no state_out
     assert lib.gdn_recurrent_fwd(d.ref, None, p, p, p, p, None, p, p, None) == 1  # no q with T > 0
     for field, val, code in (("K", 96, 2), ("V", 32, 2), ("B", 0, 1), ("T", -1, 1), ("dtype", 5, 1),
-                             ("flags", 1, 1)):
+                             ("flags", 1, 1), ("flags", _abi.GDN_FLAG_QK_L2NORM, 1)):
         d2 = desc(T=1, H=2)
         setattr(d2.c, field, val)
         assert lib.gdn_recurrent_fwd(d2.ref, p, p, p, p, p, None, p, p, None) == code, field
@@ -236,3 +236,23 @@ def test_keep_forward_workspace(kw):
         assert p["bwd_workspace_bytes"] == base["bwd_workspace_bytes"]
         assert p["cp_on"] == base["cp_on"] and p["total_segments"] == base["total_segments"]
     assert base["bwd_workspace_bytes"] >= keep["fwd_workspace_bytes"]
+
+
+@pytest.mark.parametrize("kw", [dict(), dict(B=2, H=4, T=1000, K=64, V=128), dict(T=300, H=3, K=64, V=64, dtype=torch.float32)])
+def test_qk_l2norm_workspace(kw):
+    """The q/k normalisation keeps two normalised copies (T x H x K values each, input dtype) at
+    the start of both workspace layouts and changes nothing else in the plan."""
+    base = plan(**kw)
+    l2 = plan(flags=_abi.GDN_FLAG_QK_L2NORM, **kw)
+    esize = 4 if kw.get("dtype") == torch.float32 else 2
+    rows = kw.get("B", 1) * kw.get("T", 32768) * kw.get("H", 16)
+    extra = 2 * (-(-(rows * kw.get("K", 128) * esize) // 256) * 256)
+    assert l2["fwd_workspace_bytes"] == base["fwd_workspace_bytes"] + extra
+    assert l2["bwd_workspace_bytes"] == base["bwd_workspace_bytes"] + extra
+    for f in ("cp_on", "seg_chunks", "total_segments", "warmup_chunks", "warmup_max_chunks"):
+        assert l2[f] == base[f], f
+    both = plan(flags=_abi.GDN_FLAG_QK_L2NORM | _abi.GDN_FLAG_KEEP_FORWARD, **kw)
+    assert both["fwd_workspace_bytes"] <= l2["bwd_workspace_bytes"]
+    # the Python keyword sets the same bit
+    assert gdn.gdn_plan(desc(qk_l2norm=True, **kw)) == l2
+
