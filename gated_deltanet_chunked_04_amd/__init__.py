@@ -264,12 +264,13 @@ def gdn_cp_modes(k, v, g, beta, *, cu_seqlens=None, cu_seqlens_host=None, cp_mod
     return modes
 
 
-def gdn_recurrent_fwd(q, k, v, g, beta, state=None, *, scale=1.0, state_out=None, o=None):
+def gdn_recurrent_fwd(q, k, v, g, beta, state=None, *, scale=1.0, state_out=None, o=None, qk_l2norm=False):
     """Recurrent form (decode): the gated delta rule token by token from `state`.
 
     q, k [B,T,H,K], v [B,T,H,V], g, beta [B,T,H] as in gdn_chunk_fwd (no cu_seqlens); state
     [B,H,V,K] fp32 or None (zeros), e.g. the final state of gdn_chunk_fwd. Returns (o,
     state_out); state_out may be `state` itself (updated in place). Runs on the current stream.
+    qk_l2norm=True takes raw q and k rows and normalises them as gdn_chunk_fwd(qk_l2norm=True) does.
     """
     B, T, H, K = q.shape
     V = v.shape[-1]
@@ -281,7 +282,7 @@ def gdn_recurrent_fwd(q, k, v, g, beta, state=None, *, scale=1.0, state_out=None
         raise ValueError(f"state_out: expected contiguous fp32 {(B, H, V, K)} on {q.device}")
     if o is None:
         o = torch.empty((B, T, H, V), dtype=q.dtype, device=q.device)
-    desc = make_desc(q, v, scale=scale)
+    desc = make_desc(q, v, scale=scale, qk_l2norm=qk_l2norm)
     check(load_library().gdn_recurrent_fwd(desc.ref, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
                                            _ptr(state), _ptr(state_out), _ptr(o), _stream()),
           "gdn_recurrent_fwd")

@@ -720,7 +720,7 @@ gdn_status gdn_recurrent_fwd(const gdn_desc* desc, const void* q, const void* k,
     if (!desc) return GDN_ERR_INVALID_ARG;
     for (int i = 0; i < 5; ++i)
         if (desc->reserved[i] != 0) return GDN_ERR_INVALID_ARG;
-    if (desc->cu_seqlens || desc->cu_seqlens_host || desc->flags) return GDN_ERR_INVALID_ARG;
+    if (desc->cu_seqlens || desc->cu_seqlens_host || (desc->flags & ~GDN_FLAG_QK_L2NORM)) return GDN_ERR_INVALID_ARG;
     if (desc->B < 1 || desc->T < 0 || desc->H < 1 || desc->K < 1 || desc->V < 1) return GDN_ERR_INVALID_ARG;
     if (!(desc->K == 64 || desc->K == 128) || !(desc->V == 64 || desc->V == 128)) return GDN_ERR_UNSUPPORTED;
     if (desc->dtype != GDN_DTYPE_BF16 && desc->dtype != GDN_DTYPE_FP32) return GDN_ERR_INVALID_ARG;
@@ -741,7 +741,10 @@ gdn_status gdn_recurrent_fwd(const gdn_desc* desc, const void* q, const void* k,
     da.H = desc->H;
     da.scale = desc->scale;
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-    GDN_LAUNCH(kKDecode, st, launch_decode(da, desc->dtype, (int)desc->K, (int)desc->V, st));
+    if (desc->flags & GDN_FLAG_QK_L2NORM)
+        GDN_LAUNCH(kKDecode, st, launch_decode_qk_l2norm(da, desc->dtype, (int)desc->K, (int)desc->V, st));
+    else
+        GDN_LAUNCH(kKDecode, st, launch_decode(da, desc->dtype, (int)desc->K, (int)desc->V, st));
     return GDN_OK;
 }
 

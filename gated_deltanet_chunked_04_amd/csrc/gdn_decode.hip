@@ -11,14 +11,18 @@
 // state element on the vector ALUs (matrix-vector products: nothing for the matrix cores); a
 // call moves the state through HBM twice, so short calls are bound by that traffic and by the
 // launch.
+// With the q/k L2 normalisation (kL2) the rows k_t, q_t enter as k_t r_k, q_t r_q, r = (sum x^2 +
+// eps)^(-1/2): each thread sums the squares over the 64 columns it reads anyway and the row's
+// threads add their halves, so d = r_k (S k_t), the write uses u r_k k_t and o scales by r_q.
 #include "gdn_common.h"
 #include "gdn_kernels.h"
+#include "gdn_norm.h"
 
 namespace gdn {
 
 namespace {
 
-template <typename T, int K, int V>
+template <typename T, int K, int V, bool kL2>
 __global__ __launch_bounds__(V * K / 64) void k_decode(DecodeArgs a) {
     constexpr int TPR = K / 64;  // threads per state row
     __shared__ __attribute__((aligned(16))) float sk[K];
@@ -49,15 +53,22 @@ __global__ __launch_bounds__(V * K / 64) void k_decode(DecodeArgs a) {
         const float be = a.beta[tok];
         const float vi = Elem<T>::to_f(v[tok * V + row]);
         // d = (S k)_row over this thread's columns, then across the row's threads
-        float d = 0.f;
+        float d = 0.f, ssk = 0.f;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             const f32x4 kk = *reinterpret_cast<const f32x4*>(sk + c0 + 4 * i);
             d += s[i][0] * kk[0] + s[i][1] * kk[1] + s[i][2] * kk[2] + s[i][3] * kk[3];
+            if constexpr (kL2) ssk += kk[0] * kk[0] + kk[1] * kk[1] + kk[2] * kk[2] + kk[3] * kk[3];
         }
         if constexpr (TPR == 2) d += __shfl_xor(d, 1);
-        const float u = be * (vi - al * d);
-        float od = 0.f;
+        float rk = 1.f;
+        if constexpr (kL2) {
+            if constexpr (TPR == 2) ssk += __shfl_xor(ssk, 1);
+            rk = 1.f / sqrtf(ssk + kL2Eps);
+            d *= rk;
+        }
+        const float u = be * (vi - al * d) * rk;  // the write adds u k_t^T, k_t = rk * (staged row)
+        float od = 0.f, ssq = 0.f;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             const f32x4 kk = *reinterpret_cast<const f32x4*>(sk + c0 + 4 * i);
@@ -66,24 +77,28 @@ __global__ __launch_bounds__(V * K / 64) void k_decode(DecodeArgs a) {
             for (int e = 0; e < 4; ++e) {
                 s[i][e] = al * s[i][e] + u * kk[e];
                 od += s[i][e] * qq[e];
+                if constexpr (kL2) ssq += qq[e] * qq[e];
             }
         }
         if constexpr (TPR == 2) od += __shfl_xor(od, 1);
+        if constexpr (kL2) {
+            if constexpr (TPR == 2) ssq += __shfl_xor(ssq, 1);
+            od *= 1.f / sqrtf(ssq + kL2Eps);
+        }
         if (tid % TPR == 0) o[tok * V + row] = Elem<T>::from_f(a.scale * od);
     }
 #pragma unroll
     for (int i = 0; i < 16; ++i) *reinterpret_cast<f32x4*>(a.s_out + soff + 4 * i) = s[i];
 }
 
-}  // namespace
-
-hipError_t launch_decode(const DecodeArgs& a, int dtype, int K, int V, hipStream_t st) {
+template <bool kL2>
+hipError_t launch_decode_t(const DecodeArgs& a, int dtype, int K, int V, hipStream_t st) {
     if (a.B == 0 || a.H == 0) return hipSuccess;
     const dim3 grid((unsigned)a.B, (unsigned)a.H);
-#define GDN_DECODE_CASE(TT, KK, VV)                                                      \
-    if (K == KK && V == VV) {                                                            \
-        hipLaunchKernelGGL((k_decode<TT, KK, VV>), grid, dim3(VV * KK / 64), 0, st, a); \
-        return hipGetLastError();                                                        \
+#define GDN_DECODE_CASE(TT, KK, VV)                                                           \
+    if (K == KK && V == VV) {                                                                 \
+        hipLaunchKernelGGL((k_decode<TT, KK, VV, kL2>), grid, dim3(VV * KK / 64), 0, st, a); \
+        return hipGetLastError();                                                             \
     }
     if (dtype == 0) {
         GDN_DECODE_CASE(bf16_t, 64, 64)
@@ -98,6 +113,16 @@ hipError_t launch_decode(const DecodeArgs& a, int dtype, int K, int V, hipStream
     }
 #undef GDN_DECODE_CASE
     return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_decode(const DecodeArgs& a, int dtype, int K, int V, hipStream_t st) {
+    return launch_decode_t<false>(a, dtype, K, V, st);
+}
+
+hipError_t launch_decode_qk_l2norm(const DecodeArgs& a, int dtype, int K, int V, hipStream_t st) {
+    return launch_decode_t<true>(a, dtype, K, V, st);
 }
 
 }  // namespace gdn

@@ -25,4 +25,8 @@ struct NormArgs {
 
 hipError_t launch_l2norm(const NormArgs& a, int dtype, int K, bool backward, hipStream_t st);
 
+// The recurrent form (gdn_decode.hip) on raw q and k rows, normalised in the kernel.
+struct DecodeArgs;
+hipError_t launch_decode_qk_l2norm(const DecodeArgs& a, int dtype, int K, int V, hipStream_t st);
+
 }  // namespace gdn

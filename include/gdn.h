@@ -110,8 +110,8 @@ typedef enum gdn_cp_mode {
  * gdn_chunk_bwd then returns dq and dk with respect to the raw q and k:
  * dx = r (dxhat - xhat (xhat . dxhat)), r = (sum x^2 + 1e-6)^(-1/2). With
  * GDN_FLAG_REUSE_FORWARD the normalised copies come from the kept forward, which must have had
- * this flag too. gdn_intra_chunk and gdn_cp_modes normalise k. Not accepted by
- * gdn_recurrent_fwd. */
+ * this flag too. gdn_intra_chunk and gdn_cp_modes normalise k; gdn_recurrent_fwd normalises q
+ * and k inside its kernel (fp32 rows, not rounded to the input dtype). */
 #define GDN_FLAG_QK_L2NORM 4
 
 /* Problem descriptor. Zero-initialise, then fill. */
@@ -211,7 +211,8 @@ gdn_status gdn_chunk_bwd(const gdn_desc* desc, const void* q, const void* k, con
 /* Recurrent form: the gated delta rule token by token from a given state, for decoding
  * after a prefill (the pages' interface continues a call from the previous one's state,
  * ollai.cn article, "how to use"). Every sequence b has desc->T tokens (T >= 0; a decoder
- * passes 1 or a few); no cu_seqlens, no CP, no workspace, desc->flags 0.
+ * passes 1 or a few); no cu_seqlens, no CP, no workspace; desc->flags 0 or GDN_FLAG_QK_L2NORM
+ * (raw q and k, normalised per token as in gdn_chunk_fwd).
  *   q, k [B,T,H,K]; v, o [B,T,H,V] (desc->dtype); g, beta [B,T,H] fp32 (layouts above)
  *   state_in  : [B,H,V,K] fp32 state entering the first token, or NULL (zeros); typically
  *               the final_state of gdn_chunk_fwd or of the previous call

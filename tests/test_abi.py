@@ -205,7 +205,7 @@ def test_recurrent_errors_before_launch(lib):
     assert lib.gdn_recurrent_fwd(d.ref, p, p, p, p, p, None, None, p, None) == 1  # no state_out
     assert lib.gdn_recurrent_fwd(d.ref, None, p, p, p, p, None, p, p, None) == 1  # no q with T > 0
     for field, val, code in (("K", 96, 2), ("V", 32, 2), ("B", 0, 1), ("T", -1, 1), ("dtype", 5, 1),
-                             ("flags", 1, 1), ("flags", _abi.GDN_FLAG_QK_L2NORM, 1)):
+                             ("flags", 1, 1), ("flags", 2, 1), ("flags", 8, 1)):
         d2 = desc(T=1, H=2)
         setattr(d2.c, field, val)
         assert lib.gdn_recurrent_fwd(d2.ref, p, p, p, p, p, None, p, p, None) == code, field

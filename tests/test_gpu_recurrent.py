@@ -95,3 +95,50 @@ def test_batch_decode_step(gpu_lib):
     o_ref, s_ref = oracle(inp)
     check(o, o_ref, 1e-2, "o")
     check(sT, s_ref, 1e-2, "state")
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("KV", [(64, 64), (128, 128), (64, 128), (128, 64)])
+def test_recurrent_qk_l2norm(gpu_lib, dtype, KV):
+    """Raw q and k (rows of norms 0.2-4, one all-zero row) normalised inside the decode kernel:
+    against the oracle's composition of the normalisation with the rule."""
+    from oracle import ref_fwd_l2
+    K, V = KV
+    inp = small_inputs(B=3, T=5, H=2, K=K, V=V, dtype=dtype, seed=24)
+    gen = torch.Generator().manual_seed(25)
+    for n in ("q", "k"):
+        x = torch.randn(inp[n].shape, generator=gen) * (0.2 + 3.8 * torch.rand(inp[n].shape[:-1] + (1,), generator=gen))
+        x[1, 2, 0] = 0.0
+        inp[n] = x.to(dtype)
+    d = to_dev(inp)
+    o, sT = gpu_lib.gdn_recurrent_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["initial_state"], scale=0.8,
+                                      qk_l2norm=True)
+    torch.cuda.synchronize()
+    o_ref, s_ref = ref_fwd_l2(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], 0.8, inp["initial_state"])
+    tol = tol_for(dtype)
+    check(o, o_ref, tol, "o")
+    check(sT, s_ref, tol, "state")
+
+
+def test_decode_continues_l2norm_prefill(gpu_lib):
+    """A prefill with the q/k normalisation inside the library, continued token by token with it:
+    the oracle over all tokens."""
+    from oracle import ref_fwd_l2
+    T0, T1 = 700, 8
+    inp = small_inputs(B=2, T=T0 + T1, H=2, K=128, V=128, seed=26)
+    gen = torch.Generator().manual_seed(27)
+    for n in ("q", "k"):
+        x = torch.randn(inp[n].shape, generator=gen) * (0.2 + 3.8 * torch.rand(inp[n].shape[:-1] + (1,), generator=gen))
+        inp[n] = x.to(torch.bfloat16)
+    d = to_dev(inp)
+    pre = slice_tokens(d, 0, T0)
+    o_pre, s_pre = gpu_lib.gdn_chunk_fwd(pre["q"], pre["k"], pre["v"], pre["g"], pre["beta"], d["initial_state"],
+                                         qk_l2norm=True)
+    dec = slice_tokens(d, T0, T0 + T1)
+    o_dec, s_dec = gpu_lib.gdn_recurrent_fwd(dec["q"], dec["k"], dec["v"], dec["g"], dec["beta"], s_pre,
+                                             qk_l2norm=True)
+    torch.cuda.synchronize()
+    o_ref, s_ref = ref_fwd_l2(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], 1.0, inp["initial_state"])
+    check(o_pre, o_ref[:, :T0], 1e-2, "prefill o")
+    check(o_dec, o_ref[:, T0:], 1e-2, "decode o")
+    check(s_dec, s_ref, 1e-2, "decode state")
