@@ -3,9 +3,11 @@
 //
 // AutoCP rule (FlashQLA pages, ollai.cn article, "core advantages", AutoCP item): split
 // sequences inside the card only when batch x heads <= 40, or batch x heads <= 56 and the
-// sequence is at least 8192 tokens long. "batch" is read as the number of sequences and
-// "seq_len" as the longest one. The pages tuned these thresholds on a 132-SM GPU; they are
-// kept as the default and the sub-sequence length is chosen from this device's CU count.
+// sequence is at least 8192 tokens long ("batch" read as the number of sequences, "seq_len"
+// as the longest one). Those thresholds were tuned on a 132-SM GPU and are kept as
+// GDN_CP_PAGES; the default decides what they stand for on this device: whether the serial
+// recurrence would leave compute units idle (make_plan). The sub-sequence length is chosen
+// from the CU count either way.
 #include <math.h>
 #include <stdlib.h>
 #include <string.h>

@@ -160,7 +160,7 @@ int gdn_abi_version(void);
 const char* gdn_status_string(gdn_status status);
 
 /* Validate `desc` and fill `out` with the plan the calls below would use:
- * whether CP is on (the pages' AutoCP rule, "core advantages"), sub-sequence
+ * whether CP is on (AutoCP, "core advantages"; see gdn_cp_mode), sub-sequence
  * length, warmup window and workspace sizes. Host only: reads
  * cu_seqlens_host, never cu_seqlens; queries the device CU count only when
  * desc->num_cus == 0. */
