@@ -223,3 +223,30 @@ def test_l2norm_edge_prefill_32k(gpu_lib):
     e_o = check(o[..., rows], o_ref, 1e-2, "o")
     e_s = check(sT[:, :, rows], s_ref, 1e-2, "final_state")
     print(f"l2norm edge_prefill rel_l2 o={e_o:.2e} final={e_s:.2e}", flush=True)
+
+
+def test_l2norm_backward_edge_prefill_32k(gpu_lib):
+    """The 32K step's backward (B=1, H=16, T=32768, bf16, AutoCP on: warmup and exact heads) with
+    raw q and k (unit rows times a per-row factor in [0.25, 4]) and the normalisation inside the
+    library; one warmup head and one exact head against the oracle, every token."""
+    import dataclasses
+    from gdn_inputs import WORKLOADS
+    gdn = gpu_lib
+    inp = make_inputs(dataclasses.replace(WORKLOADS["edge_prefill"], backward=True), seed=0)
+    gen = torch.Generator().manual_seed(98)
+    for n in ("q", "k"):
+        x = inp[n].float()
+        inp[n] = (x * (0.25 + 3.75 * torch.rand(x.shape[:-1] + (1,), generator=gen))).to(torch.bfloat16)
+    d = to_dev(inp)
+    modes = gdn.gdn_cp_modes(d["k"], d["v"], d["g"], d["beta"], qk_l2norm=True).cpu()
+    assert set(modes.flatten().tolist()) == {1, 2}, modes
+    out = bwd(gdn, d)
+    heads = [int((modes[0] == 1).nonzero()[0]), int((modes[0] == 2).nonzero()[0])]
+    x = {n: inp[n][:, :, heads] for n in ("q", "k", "v", "g", "beta", "d_o")}
+    ref = ref_bwd_l2(x["q"], x["k"], x["v"], x["g"], x["beta"], x["d_o"], 1.0, inp["initial_state"][:, heads],
+                     inp["d_final_state"][:, heads])
+    errs = {}
+    for n in NAMES:
+        got = out[n][:, heads] if n == "d_initial_state" else out[n][:, :, heads]
+        errs[n] = check(got, ref[n], 1e-2, n)
+    print(f"l2norm backward heads={heads} " + " ".join(f"{n}={e:.2e}" for n, e in errs.items()), flush=True)
