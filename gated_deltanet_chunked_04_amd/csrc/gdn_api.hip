@@ -354,29 +354,30 @@ gdn_status check_ws(const Plan& p, size_t need, void* ws, size_t bytes) {
     return GDN_OK;
 }
 
-// With GDN_FLAG_QK_L2NORM: normalise the q rows (when q is given) and the k rows into the
-// workspace and point q and k at the normalised copies; a no-op otherwise.
-gdn_status run_l2norm(const gdn_desc* d, const Plan& p, unsigned char* ws, const void*& q, const void*& k,
-                      hipStream_t st) {
+// With GDN_FLAG_QK_L2NORM: normalise the q rows into the workspace and point q at the copy
+// (the intra-chunk kernel normalises the k rows as it stages them and writes theirs); a no-op
+// otherwise.
+gdn_status run_l2norm_q(const gdn_desc* d, const Plan& p, unsigned char* ws, const void*& q, hipStream_t st) {
     if (!(d->flags & GDN_FLAG_QK_L2NORM)) return GDN_OK;
     const int64_t rows = p.Ttot * (int64_t)d->H;
     NormArgs na{};
     na.x0 = q;
     na.y0 = ws + p.o_qn;
-    na.rows0 = q ? rows : 0;
-    na.x1 = k;
-    na.y1 = ws + p.o_kn;
-    na.rows1 = rows;
+    na.rows0 = rows;
     if (rows > 0) GDN_LAUNCH(kKL2Norm, st, launch_l2norm(na, d->dtype, (int)d->K, false, st));
-    if (q) q = ws + p.o_qn;
-    k = ws + p.o_kn;
+    q = ws + p.o_qn;
     return GDN_OK;
+}
+
+// Where the intra-chunk kernel writes the normalised k rows (GDN_FLAG_QK_L2NORM), else null.
+void* kn_of(const gdn_desc* d, const Plan& p, unsigned char* ws) {
+    return (d->flags & GDN_FLAG_QK_L2NORM) ? ws + p.o_kn : nullptr;
 }
 
 // Tables (varlen) + intra-chunk kernel into the given output buffers.
 gdn_status run_intra(const gdn_desc* d, const Plan& p, unsigned char* ws, const void* k, const void* v,
                      const float* g, const float* beta, float* gam, void* w, void* u, hipStream_t st,
-                     void* tmat = nullptr) {
+                     void* tmat = nullptr, void* kn = nullptr) {
     if (p.varlen) {
         TableArgs t{};
         t.cu = d->cu_seqlens;
@@ -404,6 +405,7 @@ gdn_status run_intra(const gdn_desc* d, const Plan& p, unsigned char* ws, const 
     ia.u = u;
     ia.cstat = reinterpret_cast<float2*>(ws + p.o_cstat);
     ia.tmat = tmat;
+    ia.kn = kn;
     GDN_LAUNCH(kKIntra, st, launch_intra(ia, d->dtype, p.cus, st));
     return GDN_OK;
 }
@@ -493,11 +495,14 @@ gdn_status gdn_chunk_fwd(const gdn_desc* desc, const void* q, const void* k, con
     float* gam = reinterpret_cast<float*>(ws + p.o_gam);
     void* w = ws + p.o_w;
     void* u = ws + p.o_u;
-    if ((s = run_l2norm(desc, p, ws, q, k, st)) != GDN_OK) return s;
-    // with GDN_FLAG_KEEP_FORWARD the intra pass also leaves T for the backward
+    if ((s = run_l2norm_q(desc, p, ws, q, st)) != GDN_OK) return s;
+    // with GDN_FLAG_KEEP_FORWARD the intra pass also leaves T for the backward; with
+    // GDN_FLAG_QK_L2NORM it normalises k and the later kernels read its copy
+    void* kn = kn_of(desc, p, ws);
     if ((s = run_intra(desc, p, ws, k, v, g, beta, gam, w, u, st,
-                       (desc->flags & GDN_FLAG_KEEP_FORWARD) ? ws + p.o_tm : nullptr)) != GDN_OK)
+                       (desc->flags & GDN_FLAG_KEEP_FORWARD) ? ws + p.o_tm : nullptr, kn)) != GDN_OK)
         return s;
+    if (kn) k = kn;
 
     RecurArgs ra{};
     memset(&ra, 0, sizeof(ra));
@@ -575,15 +580,13 @@ gdn_status gdn_chunk_bwd(const gdn_desc* desc, const void* q, const void* k, con
     const bool reuse = (desc->flags & GDN_FLAG_REUSE_FORWARD) != 0;
     const void* q_raw = q;
     const void* k_raw = k;
-    if (desc->flags & GDN_FLAG_QK_L2NORM) {
-        if (reuse) {
-            q = ws + p.o_qn;
-            k = ws + p.o_kn;
-        } else if ((s = run_l2norm(desc, p, ws, q, k, st)) != GDN_OK) {
-            return s;
-        }
+    void* kn = kn_of(desc, p, ws);
+    if (kn) {
+        if (reuse) q = ws + p.o_qn;
+        else if ((s = run_l2norm_q(desc, p, ws, q, st)) != GDN_OK) return s;
     }
-    if (!reuse && (s = run_intra(desc, p, ws, k, v, g, beta, gam, w, u, st, ws + p.o_tm)) != GDN_OK) return s;
+    if (!reuse && (s = run_intra(desc, p, ws, k, v, g, beta, gam, w, u, st, ws + p.o_tm, kn)) != GDN_OK) return s;
+    if (kn) k = kn;
     const int rt = recur_rows((int)desc->V, (int)desc->K);
     const int vtiles = (int)(desc->V / rt);
     const int vktiles = (int)((desc->V + desc->K + rt - 1) / rt);
@@ -760,9 +763,7 @@ gdn_status gdn_intra_chunk(const gdn_desc* desc, const void* k, const void* v, c
     if ((s = check_ws(p, p.fwd_bytes, workspace, workspace_bytes)) != GDN_OK) return s;
     unsigned char* ws = static_cast<unsigned char*>(workspace);
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-    const void* no_q = nullptr;
-    if ((s = run_l2norm(desc, p, ws, no_q, k, st)) != GDN_OK) return s;
-    return run_intra(desc, p, ws, k, v, g, beta, gam_out, w_out, u_out, st);
+    return run_intra(desc, p, ws, k, v, g, beta, gam_out, w_out, u_out, st, nullptr, kn_of(desc, p, ws));
 }
 
 gdn_status gdn_cp_modes(const gdn_desc* desc, const void* k, const void* v, const float* g, const float* beta,
@@ -774,10 +775,8 @@ gdn_status gdn_cp_modes(const gdn_desc* desc, const void* k, const void* v, cons
     if ((s = check_ws(p, p.fwd_bytes, workspace, workspace_bytes)) != GDN_OK) return s;
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     unsigned char* ws = static_cast<unsigned char*>(workspace);
-    const void* no_q = nullptr;
-    if ((s = run_l2norm(desc, p, ws, no_q, k, st)) != GDN_OK) return s;
     if ((s = run_intra(desc, p, ws, k, v, g, beta, reinterpret_cast<float*>(ws + p.o_gam), ws + p.o_w,
-                       ws + p.o_u, st)) != GDN_OK)
+                       ws + p.o_u, st, nullptr, kn_of(desc, p, ws))) != GDN_OK)
         return s;
     return run_decide(desc, p, ws, modes_out, windows_of(p, reinterpret_cast<int32_t*>(ws + p.o_modes)), st);
 }

@@ -23,6 +23,7 @@
 // kernel also writes T in the input precision.
 #include "gdn_common.h"
 #include "gdn_kernels.h"
+#include "gdn_norm.h"
 
 #include <algorithm>
 
@@ -76,9 +77,50 @@ __device__ __forceinline__ void intra_fetch(IntraRegs<T, K, V>& R, const IntraAr
     }
 }
 
+// Sum of squares of one 16-byte vector's elements.
+__device__ __forceinline__ float sumsq_vec(const u32x4& x, bf16_t) {
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float lo = __uint_as_float(x[i] << 16), hi = __uint_as_float(x[i] & 0xFFFF0000u);
+        s = fmaf(hi, hi, fmaf(lo, lo, s));
+    }
+    return s;
+}
+__device__ __forceinline__ float sumsq_vec(const u32x4& x, float) {
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s = fmaf(__uint_as_float(x[i]), __uint_as_float(x[i]), s);
+    return s;
+}
+
+// The q/k L2 normalisation of the fetched k rows, in registers: fetch_tile puts each row's
+// K / VEC vectors in that many consecutive lanes of one wave, so a row's sum of squares
+// takes log2 of that many cross-lane adds; x / sqrt(sum x^2 + eps), rounded to the input
+// dtype (rows past the chunk end are zero and stay zero). The rows inside the chunk go to
+// kn for the kernels that read k after this one.
+template <typename T, int K, int N>
+__device__ __forceinline__ void normalise_k(u32x4 (&x)[N], T* kn, size_t ld_g, int rows) {
+    constexpr int VEC = Elem<T>::kVec;
+    constexpr int NVR = K / VEC;
+    constexpr int RPI = kThreads / NVR;
+    static_assert(kThreads == 256 && 64 % NVR == 0, "the fetch_tile mapping of this kernel");
+    const int r0 = (int)threadIdx.x / NVR, cv = (int)threadIdx.x % NVR;
+#pragma unroll
+    for (int it = 0; it < N; ++it) {
+        float ss = sumsq_vec(x[it], T{});
+#pragma unroll
+        for (int o = NVR / 2; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
+        x[it] = scale_vec<T>(x[it], 1.f / sqrtf(ss + kL2Eps));
+        const int r = r0 + it * RPI;
+        if (r < rows) *reinterpret_cast<u32x4*>(kn + (size_t)r * ld_g + cv * VEC) = x[it];
+    }
+}
+
 // Persistent: each workgroup walks (chunk, head) tasks with a grid stride; the next
-// task's k, v, g and beta load into registers while the current task computes.
-template <typename T, int K, int V>
+// task's k, v, g and beta load into registers while the current task computes. With kL2
+// the k rows arrive raw and are normalised before staging (and written out once).
+template <typename T, int K, int V, bool kL2>
 __global__ __launch_bounds__(kThreads) void k_intra(IntraArgs args) {
     using S = IntraSmem<T, K, V>;
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -110,6 +152,9 @@ __global__ __launch_bounds__(kThreads) void k_intra(IntraArgs args) {
     for (;;) {
         // ---- stage 1: operands into LDS, gate cumsum --------------------------------
         lds_sync();  // the previous task's LDS reads are done
+        if constexpr (kL2)
+            normalise_k<T, K>(R.k, reinterpret_cast<T*>(args.kn) + ((size_t)cur.t0 * H + cur.h) * K, (size_t)H * K,
+                              cur.c);
         put_tile_fo<T, K>(sK, S::LDK, R.k);  // fragment order (read as rows and transposed)
         put_tile<T, V>(sV, S::LDV, R.v);
         const float g_in = R.g, b_in = R.beta;
@@ -281,7 +326,7 @@ template <typename T, int K, int V>
 hipError_t launch_intra_t(const IntraArgs& a, int cus, hipStream_t st) {
     using S = IntraSmem<T, K, V>;
     static_assert(S::total <= 160 * 1024, "LDS budget");
-    auto kern = k_intra<T, K, V>;
+    auto kern = a.kn ? k_intra<T, K, V, true> : k_intra<T, K, V, false>;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, S::total);
     if (e != hipSuccess) return e;

@@ -140,6 +140,8 @@ struct IntraArgs {
     void* u;         // [Ttot, H, V]
     float2* cstat;   // [total_chunks, H]: (chunk gate total, max beta*|k|^2)
     void* tmat;      // [total_chunks, H, 64, 64] T = (I + A)^{-1} row-major, or null (not written)
+    void* kn;        // [Ttot, H, K]: k is raw, its rows are normalised in the kernel and written
+                     // here for the later kernels (the q/k L2 normalisation), or null
 };
 
 enum RecurMode : int {
