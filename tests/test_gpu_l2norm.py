@@ -250,3 +250,20 @@ def test_l2norm_backward_edge_prefill_32k(gpu_lib):
         got = out[n][:, heads] if n == "d_initial_state" else out[n][:, :, heads]
         errs[n] = check(got, ref[n], 1e-2, n)
     print(f"l2norm backward heads={heads} " + " ".join(f"{n}={e:.2e}" for n, e in errs.items()), flush=True)
+
+
+@pytest.mark.parametrize("l2", [False, True])
+def test_no_tokens(gpu_lib, l2):
+    """T = 0: the forward returns the initial state as the final state, the backward passes
+    d(final state) through to d(initial state) and every other output is empty."""
+    gdn = gpu_lib
+    inp = with_grads(small_inputs(B=2, T=0, H=2, K=128, V=64, seed=39))
+    d = to_dev(inp)
+    o, sT = gdn.gdn_chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["initial_state"], qk_l2norm=l2)
+    out = gdn.gdn_chunk_bwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["d_o"], d["initial_state"],
+                            d["d_final_state"], qk_l2norm=l2)
+    torch.cuda.synchronize()
+    assert o.shape == (2, 0, 2, 64) and torch.equal(sT, d["initial_state"])
+    assert torch.equal(out["d_initial_state"], d["d_final_state"])
+    for n in ("dq", "dk", "dv", "dg", "dbeta"):
+        assert out[n].numel() == 0, n
