@@ -179,10 +179,10 @@ def decode_bench(gdn, H, K, V, dtype, reps=50):
 
 def l2norm_leg(gdn, dev, cu, cu_host, cp, timed, steps):
     """The same step with the q/k L2 normalisation inside the library (GDN_FLAG_QK_L2NORM):
-    its time, and the two normalisation kernels against the HBM roofline. The forward kernel
-    reads and writes every q row once (2 row passes; the intra-chunk kernel normalises k as it
-    stages it and writes the normalised rows); the backward one reads the raw q and k rows and
-    their gradients and writes the gradients (6 row passes of q's size)."""
+    its time, and the reverse-mode kernel against the HBM roofline (it reads the raw q and k
+    rows and their gradients and writes the gradients: 6 row passes of q's size). The forward
+    normalisation has no kernel of its own: the kernels that stage q and k normalise the rows
+    there (the intra-chunk kernel also writes the normalised k rows once)."""
     import torch
     q, k, v, g, beta, s0 = (dev[x] for x in ("q", "k", "v", "g", "beta", "initial_state"))
     kw = dict(cu_seqlens=cu, cu_seqlens_host=cu_host, cp_mode=cp, qk_l2norm=True)
@@ -210,7 +210,7 @@ def l2norm_leg(gdn, dev, cu, cu_host, cp, timed, steps):
     gdn.gdn_profile_enable(False)
     row_bytes = q.numel() * q.element_size()  # all q rows (and as many k rows)
     out = {"ms_per_step": round(ms, 4), "kernels": {}}
-    for name, passes in (("qk_l2norm", 2), ("qk_l2norm_bwd", 6)):
+    for name, passes in (("qk_l2norm_bwd", 6),):
         n, tot = kt[name]
         us = 1e3 * tot / n
         gbs = passes * row_bytes / (us * 1e-6) / 1e9

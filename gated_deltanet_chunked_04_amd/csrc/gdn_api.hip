@@ -47,7 +47,7 @@ struct Plan {
     int32_t forced = 0;
     int32_t esize = 2;
     // forward workspace
-    size_t o_qn = 0, o_kn = 0, o_gam = 0, o_w = 0, o_u = 0, o_cstat = 0, o_bos = 0, o_len = 0, o_choff = 0, o_segoff = 0,
+    size_t o_kn = 0, o_gam = 0, o_w = 0, o_u = 0, o_cstat = 0, o_bos = 0, o_len = 0, o_choff = 0, o_segoff = 0,
            o_ctab = 0, o_stab = 0, o_modes = 0, o_seginit = 0, o_prep = 0, fwd_bytes = 0;
     // backward workspace: the forward's layout, then these
     size_t o_modes_r = 0, o_seginit_r = 0, o_prep_r = 0, o_h = 0, o_gst = 0, o_tm = 0, o_dl = 0, o_ddl = 0,
@@ -177,10 +177,8 @@ gdn_status make_plan(const gdn_desc* d, Plan& p) {
         off = align_up(off + bytes);
         return o;
     };
-    if (d->flags & GDN_FLAG_QK_L2NORM) {  // normalised q and k, first: the same offsets in both layouts
-        p.o_qn = take(T * H * K * p.esize);
+    if (d->flags & GDN_FLAG_QK_L2NORM)  // normalised k rows, first: the same offset in both layouts
         p.o_kn = take(T * H * K * p.esize);
-    }
     p.o_gam = take(T * H * 4);
     p.o_w = take(T * H * K * p.esize);
     p.o_u = take(T * H * V * p.esize);
@@ -253,11 +251,10 @@ Geo make_geo(const gdn_desc* d, const Plan& p, unsigned char* ws) {
 // ---------------------------------------------------------------------------
 // Kernel timing (gdn_profile_enable / gdn_profile_read).
 enum KernelId { kKTables = 0, kKIntra, kKDecide, kKPrepass, kKScan, kKRecurOut, kKRecurStates,
-                kKBwdPrepass, kKBwdScan, kKBwdReverse, kKBwdChunk, kKDecode, kKL2Norm, kKL2NormBwd, kKCount };
+                kKBwdPrepass, kKBwdScan, kKBwdReverse, kKBwdChunk, kKDecode, kKL2NormBwd, kKCount };
 const char* const kKernelNames[kKCount] = {"tables", "intra", "cp_decide", "cp_prepass", "cp_scan",
                                            "recur_out", "recur_states", "bwd_cp_prepass", "bwd_cp_scan",
-                                           "bwd_reverse", "bwd_chunk", "recurrent", "qk_l2norm",
-                                           "qk_l2norm_bwd"};
+                                           "bwd_reverse", "bwd_chunk", "recurrent", "qk_l2norm_bwd"};
 struct Pending {
     int kid;
     hipEvent_t start, stop;
@@ -354,22 +351,9 @@ gdn_status check_ws(const Plan& p, size_t need, void* ws, size_t bytes) {
     return GDN_OK;
 }
 
-// With GDN_FLAG_QK_L2NORM: normalise the q rows into the workspace and point q at the copy
-// (the intra-chunk kernel normalises the k rows as it stages them and writes theirs); a no-op
-// otherwise.
-gdn_status run_l2norm_q(const gdn_desc* d, const Plan& p, unsigned char* ws, const void*& q, hipStream_t st) {
-    if (!(d->flags & GDN_FLAG_QK_L2NORM)) return GDN_OK;
-    const int64_t rows = p.Ttot * (int64_t)d->H;
-    NormArgs na{};
-    na.x0 = q;
-    na.y0 = ws + p.o_qn;
-    na.rows0 = rows;
-    if (rows > 0) GDN_LAUNCH(kKL2Norm, st, launch_l2norm(na, d->dtype, (int)d->K, false, st));
-    q = ws + p.o_qn;
-    return GDN_OK;
-}
-
-// Where the intra-chunk kernel writes the normalised k rows (GDN_FLAG_QK_L2NORM), else null.
+// GDN_FLAG_QK_L2NORM: the intra-chunk kernel normalises the k rows as it stages them and
+// writes them here for the later kernels (null without the flag); the kernels that read q
+// normalise its rows as they stage them (q_l2 in their arguments).
 void* kn_of(const gdn_desc* d, const Plan& p, unsigned char* ws) {
     return (d->flags & GDN_FLAG_QK_L2NORM) ? ws + p.o_kn : nullptr;
 }
@@ -495,7 +479,6 @@ gdn_status gdn_chunk_fwd(const gdn_desc* desc, const void* q, const void* k, con
     float* gam = reinterpret_cast<float*>(ws + p.o_gam);
     void* w = ws + p.o_w;
     void* u = ws + p.o_u;
-    if ((s = run_l2norm_q(desc, p, ws, q, st)) != GDN_OK) return s;
     // with GDN_FLAG_KEEP_FORWARD the intra pass also leaves T for the backward; with
     // GDN_FLAG_QK_L2NORM it normalises k and the later kernels read its copy
     void* kn = kn_of(desc, p, ws);
@@ -517,6 +500,7 @@ gdn_status gdn_chunk_fwd(const gdn_desc* desc, const void* q, const void* k, con
     ra.sT = final_state;
     ra.scale = desc->scale;
     ra.use_cp = p.cp_on;
+    ra.q_l2 = kn != nullptr;
     int32_t* modes = reinterpret_cast<int32_t*>(ws + p.o_modes);
     ra.modes = modes;
     ra.wins = windows_of(p, modes);
@@ -578,13 +562,8 @@ gdn_status gdn_chunk_bwd(const gdn_desc* desc, const void* q, const void* k, con
     // 1. the forward's intra-chunk pass (kept by a GDN_FLAG_KEEP_FORWARD forward, or recomputed),
     // on the normalised q and k with GDN_FLAG_QK_L2NORM (kept too, at the same offsets)
     const bool reuse = (desc->flags & GDN_FLAG_REUSE_FORWARD) != 0;
-    const void* q_raw = q;
     const void* k_raw = k;
     void* kn = kn_of(desc, p, ws);
-    if (kn) {
-        if (reuse) q = ws + p.o_qn;
-        else if ((s = run_l2norm_q(desc, p, ws, q, st)) != GDN_OK) return s;
-    }
     if (!reuse && (s = run_intra(desc, p, ws, k, v, g, beta, gam, w, u, st, ws + p.o_tm, kn)) != GDN_OK) return s;
     if (kn) k = kn;
     const int rt = recur_rows((int)desc->V, (int)desc->K);
@@ -657,6 +636,7 @@ gdn_status gdn_chunk_bwd(const gdn_desc* desc, const void* q, const void* k, con
     va.ddelta = ws + p.o_ddl;
     va.scale = desc->scale;
     va.use_cp = p.cp_on;
+    va.q_l2 = kn != nullptr;
     if (p.cp_on) {
         float* seginit_r = reinterpret_cast<float*>(ws + p.o_seginit_r);
         float* prep_r = reinterpret_cast<float*>(ws + p.o_prep_r);
@@ -705,17 +685,18 @@ gdn_status gdn_chunk_bwd(const gdn_desc* desc, const void* q, const void* k, con
     ba.dg = dg;
     ba.dbeta = dbeta;
     ba.scale = desc->scale;
+    ba.q_l2 = kn != nullptr;
     const int64_t tasks = p.total_chunks * (int64_t)desc->H;
     GDN_LAUNCH(kKBwdChunk, st, launch_bwd_chunk(ba, desc->dtype, (int)std::min<int64_t>(tasks, p.cus), st));
     // 5. dq and dk back through the normalisation to the raw rows, in place
     if ((desc->flags & GDN_FLAG_QK_L2NORM) && p.Ttot > 0) {
         NormArgs na{};
-        na.x0 = q_raw;
+        na.x0 = q;
         na.y0 = dq;
         na.x1 = k_raw;
         na.y1 = dk;
         na.rows0 = na.rows1 = p.Ttot * (int64_t)desc->H;
-        GDN_LAUNCH(kKL2NormBwd, st, launch_l2norm(na, desc->dtype, (int)desc->K, true, st));
+        GDN_LAUNCH(kKL2NormBwd, st, launch_l2norm_bwd(na, desc->dtype, (int)desc->K, st));
     }
     return GDN_OK;
 }

@@ -16,6 +16,7 @@
 //     dg as the in-chunk reverse cumulative sum of d(gam).
 #include "gdn_common.h"
 #include "gdn_kernels.h"
+#include "gdn_norm.h"
 
 namespace gdn {
 
@@ -124,7 +125,8 @@ __device__ __forceinline__ void rev_stage(const RevRegs<T, K, RT>& R, const RevL
     if (threadIdx.x < 64) L.sGam[threadIdx.x] = R.gam;
 }
 
-template <typename T, int K, int RT, int MODE>
+// kL2: q arrives raw and its rows are L2-normalised in registers before staging.
+template <typename T, int K, int RT, int MODE, bool kL2 = false>
 __global__ __launch_bounds__(RT * 4) void k_reverse(RevArgs a) {
     using C = VCfg<T, K, RT>;
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -247,6 +249,7 @@ __global__ __launch_bounds__(RT * 4) void k_reverse(RevArgs a) {
                 if (u / NV < cp) *reinterpret_cast<u32x4*>(dst + (size_t)(u / NV) * H * V + (u % NV) * C::VEC) = fkeep[it];
             }
         }
+        if constexpr (kL2) l2norm_rows<T, K>(R.q);
         rev_stage<T, K, RT>(R, L, a.scale);
         lds_sync();
         const int cn = max(ci - kDepth, cbeg);
@@ -486,7 +489,7 @@ template <typename T, int K, int RT, int MODE>
 hipError_t launch_reverse_t(const RevArgs& a, int64_t nsegs_grid, int vtiles, hipStream_t st) {
     using C = VCfg<T, K, RT>;
     static_assert(C::total <= 160 * 1024, "LDS budget");
-    auto kern = k_reverse<T, K, RT, MODE>;
+    auto kern = a.q_l2 ? k_reverse<T, K, RT, MODE, true> : k_reverse<T, K, RT, MODE, false>;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, C::total);
     if (e != hipSuccess) return e;
@@ -678,7 +681,9 @@ __device__ __forceinline__ Frag<float> neg(const Frag<float>& f) {
 // Sum over the four lanes that share ln (lane groups gq = 0..3).
 __device__ __forceinline__ float sum_gq(float x) { return sum_rows(x); }
 
-template <typename T, int K, int V>
+// kL2: q arrives raw and its rows are L2-normalised in registers before staging (dq is then
+// the gradient with respect to the normalised rows).
+template <typename T, int K, int V, bool kL2 = false>
 __global__ __launch_bounds__(512) void k_bwd_chunk(BwdChunkArgs a) {
     using C = BCfg<T, K, V>;
     constexpr int NT = C::NT;
@@ -741,6 +746,7 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(BwdChunkArgs a) {
         float* sDb = reinterpret_cast<float*>(sm + C::off_db);
         // ---- stage this task (the previous task's LDS reads are done) ---------------------
         lds_sync();
+        if constexpr (kL2) l2norm_rows<T, K>(R.q);
         put_tile_fo<T, K, C::NK, NT>(sQ, C::LDK, R.q);
         put_tile_fo<T, K, C::NK, NT>(sK, C::LDK, R.k);
         // dO enters every product together with the query scale (o = scale S q)
@@ -1202,7 +1208,7 @@ template <typename T, int K, int V>
 hipError_t launch_bwd_chunk_t(const BwdChunkArgs& a, int grid, hipStream_t st) {
     using C = BCfg<T, K, V>;
     static_assert(C::total <= 160 * 1024, "LDS budget");
-    auto kern = k_bwd_chunk<T, K, V>;
+    auto kern = a.q_l2 ? k_bwd_chunk<T, K, V, true> : k_bwd_chunk<T, K, V, false>;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, C::total);
     if (e != hipSuccess) return e;

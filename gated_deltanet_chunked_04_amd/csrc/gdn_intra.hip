@@ -77,23 +77,6 @@ __device__ __forceinline__ void intra_fetch(IntraRegs<T, K, V>& R, const IntraAr
     }
 }
 
-// Sum of squares of one 16-byte vector's elements.
-__device__ __forceinline__ float sumsq_vec(const u32x4& x, bf16_t) {
-    float s = 0.f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const float lo = __uint_as_float(x[i] << 16), hi = __uint_as_float(x[i] & 0xFFFF0000u);
-        s = fmaf(hi, hi, fmaf(lo, lo, s));
-    }
-    return s;
-}
-__device__ __forceinline__ float sumsq_vec(const u32x4& x, float) {
-    float s = 0.f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) s = fmaf(__uint_as_float(x[i]), __uint_as_float(x[i]), s);
-    return s;
-}
-
 // The q/k L2 normalisation of the fetched k rows, in registers: fetch_tile puts each row's
 // K / VEC vectors in that many consecutive lanes of one wave, so a row's sum of squares
 // takes log2 of that many cross-lane adds; x / sqrt(sum x^2 + eps), rounded to the input
@@ -106,12 +89,9 @@ __device__ __forceinline__ void normalise_k(u32x4 (&x)[N], T* kn, size_t ld_g, i
     constexpr int RPI = kThreads / NVR;
     static_assert(kThreads == 256 && 64 % NVR == 0, "the fetch_tile mapping of this kernel");
     const int r0 = (int)threadIdx.x / NVR, cv = (int)threadIdx.x % NVR;
+    l2norm_rows<T, K>(x);
 #pragma unroll
     for (int it = 0; it < N; ++it) {
-        float ss = sumsq_vec(x[it], T{});
-#pragma unroll
-        for (int o = NVR / 2; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
-        x[it] = scale_vec<T>(x[it], 1.f / sqrtf(ss + kL2Eps));
         const int r = r0 + it * RPI;
         if (r < rows) *reinterpret_cast<u32x4*>(kn + (size_t)r * ld_g + cv * VEC) = x[it];
     }

@@ -171,6 +171,7 @@ struct RecurArgs {
     void* delta;              // same modes: [Ttot,H,V] Delta = U - W S^T of every chunk, or null
     float scale;
     int32_t use_cp;           // segments >= 1 read seginit
+    int32_t q_l2;             // output modes: q is raw, its rows are L2-normalised as staged
 };
 
 struct DecideArgs {
@@ -214,6 +215,7 @@ struct RevArgs {
     void* ddelta;             // kRecurOut: [Ttot,H,V] dL/dDelta of every chunk, or null
     float scale;
     int32_t use_cp;
+    int32_t q_l2;             // q is raw, its rows are L2-normalised as staged
 };
 
 struct BwdChunkArgs {
@@ -236,6 +238,8 @@ struct BwdChunkArgs {
     float* dg;
     float* dbeta;
     float scale;
+    int32_t q_l2;             // q is raw, its rows are L2-normalised as staged (dq is then with
+                              // respect to the normalised rows)
 };
 
 struct TableArgs {

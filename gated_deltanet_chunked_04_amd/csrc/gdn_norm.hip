@@ -1,9 +1,10 @@
-// gdn_norm.hip -- L2 normalisation of the q and k rows over the key dimension, the
-// preprocessing that may precede the path (the FlashQLA pages put preprocessing ahead of the
-// fused kernels: edge.aivizor.me community post, its account of the chunked-prefill
-// pipeline; their workloads feed unit-norm q and k), and its reverse mode for the backward.
-// Each row is x / sqrt(sum x^2 + eps), eps = 1e-6; the backward maps dL/dxhat to dL/dx =
-// r (dxhat - xhat (xhat . dxhat)) with r = (sum x^2 + eps)^(-1/2).
+// gdn_norm.hip -- reverse mode of the L2 normalisation of the q and k rows over the key
+// dimension, the preprocessing that may precede the path (the FlashQLA pages put
+// preprocessing ahead of the fused kernels: edge.aivizor.me community post, its account of
+// the chunked-prefill pipeline; their workloads feed unit-norm q and k). The forward,
+// x / sqrt(sum x^2 + eps) with eps = 1e-6, happens inside the kernels that stage q and k
+// (l2norm_rows); the backward maps dL/dxhat to dL/dx = r (dxhat - xhat (xhat . dxhat)) with
+// r = (sum x^2 + eps)^(-1/2), here, after the per-chunk gradients.
 //
 // Pure streaming: a row is K contiguous values (256 bytes for bf16 at K = 128), held by
 // K*esize/16 consecutive lanes with one 16-byte vector each, so a wave reads and writes
@@ -58,8 +59,8 @@ __device__ __forceinline__ float row_sum(float s) {
     return s;
 }
 
-template <typename T, int K, bool kBwd>
-__global__ __launch_bounds__(kNormThreads) void k_l2norm(NormArgs a) {
+template <typename T, int K>
+__global__ __launch_bounds__(kNormThreads) void k_l2norm_bwd(NormArgs a) {
     constexpr int E = Vec16<T>::n;     // values per 16-byte vector
     constexpr int LPR = K / E;         // lanes per row: 8, 16 or 32
     constexpr int RPB = kNormThreads / LPR;
@@ -84,7 +85,7 @@ __global__ __launch_bounds__(kNormThreads) void k_l2norm(NormArgs a) {
             for (int e = 0; e < E; ++e) x[u][e] = y[u][e] = 0.f;
             if (live[u]) {
                 Vec16<T>::load(src[u], x[u]);
-                if (kBwd) Vec16<T>::load(dst[u], y[u]);
+                Vec16<T>::load(dst[u], y[u]);
             }
         }
 #pragma unroll
@@ -94,40 +95,34 @@ __global__ __launch_bounds__(kNormThreads) void k_l2norm(NormArgs a) {
             for (int e = 0; e < E; ++e) ss = fmaf(x[u][e], x[u][e], ss);
             const float r = 1.f / sqrtf(row_sum<LPR>(ss) + kL2Eps);
             float out[E];
-            if (kBwd) {
-                float dot = 0.f;
+            float dot = 0.f;
 #pragma unroll
-                for (int e = 0; e < E; ++e) dot = fmaf(x[u][e] * r, y[u][e], dot);
-                dot = row_sum<LPR>(dot);
+            for (int e = 0; e < E; ++e) dot = fmaf(x[u][e] * r, y[u][e], dot);
+            dot = row_sum<LPR>(dot);
 #pragma unroll
-                for (int e = 0; e < E; ++e) out[e] = r * (y[u][e] - x[u][e] * r * dot);
-            } else {
-#pragma unroll
-                for (int e = 0; e < E; ++e) out[e] = x[u][e] * r;
-            }
+            for (int e = 0; e < E; ++e) out[e] = r * (y[u][e] - x[u][e] * r * dot);
             if (live[u]) Vec16<T>::store(dst[u], out);
         }
     }
 }
 
 template <typename T, int K>
-hipError_t launch_t(const NormArgs& a, bool backward, hipStream_t st) {
+hipError_t launch_t(const NormArgs& a, hipStream_t st) {
     constexpr int RPB = kNormThreads / (K / Vec16<T>::n);
     const int64_t total = a.rows0 + a.rows1;
     if (total <= 0) return hipSuccess;
     const int64_t need = (total + (int64_t)RPB * kNormUnroll - 1) / ((int64_t)RPB * kNormUnroll);
     const int grid = (int)(need < 8192 ? need : 8192);  // grid-stride beyond that
-    if (backward) hipLaunchKernelGGL((k_l2norm<T, K, true>), dim3(grid), dim3(kNormThreads), 0, st, a);
-    else hipLaunchKernelGGL((k_l2norm<T, K, false>), dim3(grid), dim3(kNormThreads), 0, st, a);
+    hipLaunchKernelGGL((k_l2norm_bwd<T, K>), dim3(grid), dim3(kNormThreads), 0, st, a);
     return hipGetLastError();
 }
 
 }  // namespace
 
 // dtype 0 = bf16, 1 = fp32 (gdn_dtype); K in {64, 128}
-hipError_t launch_l2norm(const NormArgs& a, int dtype, int K, bool backward, hipStream_t st) {
-    if (dtype == 0) return K == 64 ? launch_t<bf16_t, 64>(a, backward, st) : launch_t<bf16_t, 128>(a, backward, st);
-    return K == 64 ? launch_t<float, 64>(a, backward, st) : launch_t<float, 128>(a, backward, st);
+hipError_t launch_l2norm_bwd(const NormArgs& a, int dtype, int K, hipStream_t st) {
+    if (dtype == 0) return K == 64 ? launch_t<bf16_t, 64>(a, st) : launch_t<bf16_t, 128>(a, st);
+    return K == 64 ? launch_t<float, 64>(a, st) : launch_t<float, 128>(a, st);
 }
 
 }  // namespace gdn

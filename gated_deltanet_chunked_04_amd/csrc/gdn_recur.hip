@@ -26,6 +26,7 @@
 // directly as B operands (see gdn_common.h); it is never written to LDS.
 #include "gdn_common.h"
 #include "gdn_kernels.h"
+#include "gdn_norm.h"
 
 namespace gdn {
 
@@ -354,7 +355,8 @@ __device__ __forceinline__ void chunk_part2(const RecurArgs& a, const ChunkLds<T
     }
 }
 
-template <typename T, int K, int RT, int MODE>
+// kL2 (output modes): q arrives raw and its rows are L2-normalised in registers before staging.
+template <typename T, int K, int RT, int MODE, bool kL2 = false>
 __global__ __launch_bounds__(RT * 4) void k_recur(RecurArgs a) {
     using C = RCfg<T, K, RT>;
     constexpr bool kOut = MODE == kRecurOut || MODE == kRecurOutRec;
@@ -480,6 +482,7 @@ __global__ __launch_bounds__(RT * 4) void k_recur(RecurArgs a) {
         }
         // (the output pass stages q over the tile just read: every wave's reads first)
         if (MODE == kRecurOutRec && a.delta) lds_sync();
+        if constexpr (kL2 && kOut) l2norm_rows<T, K>(R.q);
         chunk_stage<T, K, RT, kOut>(R, L);
         lds_sync();
         // operands kDepth chunks ahead (the last chunk again past the end), in three pieces
@@ -568,11 +571,11 @@ __global__ __launch_bounds__(RT * 4) void k_recur(RecurArgs a) {
     }
 }
 
-template <typename T, int K, int RT, int MODE>
+template <typename T, int K, int RT, int MODE, bool kL2 = false>
 hipError_t launch_recur_t(const RecurArgs& a, int64_t nsegs_grid, int vtiles, hipStream_t st) {
     using C = RCfg<T, K, RT>;
     static_assert(C::total <= 160 * 1024, "LDS budget");
-    auto kern = k_recur<T, K, RT, MODE>;
+    auto kern = k_recur<T, K, RT, MODE, kL2>;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, C::total);
     if (e != hipSuccess) return e;
@@ -916,8 +919,12 @@ hipError_t launch_recur(const RecurArgs& a, int dtype, int mode, int64_t nsegs_g
     const int RT = recur_rows(a.geo.V, K);
 #define GDN_RECUR_CASE(TT, KK, RR)                                                                         \
     if (K == KK && RT == RR) {                                                                             \
-        if (mode == kRecurOut) return launch_recur_t<TT, KK, RR, kRecurOut>(a, nsegs_grid, vtiles, st);     \
-        if (mode == kRecurOutRec) return launch_recur_t<TT, KK, RR, kRecurOutRec>(a, nsegs_grid, vtiles, st); \
+        if (mode == kRecurOut)                                                                             \
+            return a.q_l2 ? launch_recur_t<TT, KK, RR, kRecurOut, true>(a, nsegs_grid, vtiles, st)          \
+                          : launch_recur_t<TT, KK, RR, kRecurOut>(a, nsegs_grid, vtiles, st);               \
+        if (mode == kRecurOutRec)                                                                          \
+            return a.q_l2 ? launch_recur_t<TT, KK, RR, kRecurOutRec, true>(a, nsegs_grid, vtiles, st)       \
+                          : launch_recur_t<TT, KK, RR, kRecurOutRec>(a, nsegs_grid, vtiles, st);            \
         if (mode == kRecurPrepass) return launch_recur_t<TT, KK, RR, kRecurPrepass>(a, nsegs_grid, vtiles, st); \
         if (mode == kRecurStates) return launch_recur_t<TT, KK, RR, kRecurStates>(a, nsegs_grid, vtiles, st); \
     }

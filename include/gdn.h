@@ -102,14 +102,15 @@ typedef enum gdn_cp_mode {
 #define GDN_FLAG_KEEP_FORWARD 1
 #define GDN_FLAG_REUSE_FORWARD 2
 
-/* GDN_FLAG_QK_L2NORM: q and k are raw; the path first scales every row of K values (one token,
+/* GDN_FLAG_QK_L2NORM: q and k are raw; the path scales every row of K values (one token,
  * one head) to x / sqrt(sum x^2 + 1e-6) and runs on those rows, the preprocessing the pages place
  * ahead of the fused kernels (edge.aivizor.me community post, its account of the chunked-prefill
- * pipeline) with the unit-norm q and k their workloads use. The normalised copies live at the
- * start of the workspace (2 x T x H x K values in the input dtype more, in both layouts).
+ * pipeline) with the unit-norm q and k their workloads use. The kernels normalise the rows as
+ * they stage them; the intra-chunk kernel writes the normalised k rows once for the later ones,
+ * at the start of the workspace (T x H x K values in the input dtype more, in both layouts).
  * gdn_chunk_bwd then returns dq and dk with respect to the raw q and k:
  * dx = r (dxhat - xhat (xhat . dxhat)), r = (sum x^2 + 1e-6)^(-1/2). With
- * GDN_FLAG_REUSE_FORWARD the normalised copies come from the kept forward, which must have had
+ * GDN_FLAG_REUSE_FORWARD the normalised k rows come from the kept forward, which must have had
  * this flag too. gdn_intra_chunk and gdn_cp_modes normalise k; gdn_recurrent_fwd normalises q
  * and k inside its kernel (fp32 rows, not rounded to the input dtype). */
 #define GDN_FLAG_QK_L2NORM 4

@@ -240,13 +240,14 @@ def test_keep_forward_workspace(kw):
 
 @pytest.mark.parametrize("kw", [dict(), dict(B=2, H=4, T=1000, K=64, V=128), dict(T=300, H=3, K=64, V=64, dtype=torch.float32)])
 def test_qk_l2norm_workspace(kw):
-    """The q/k normalisation keeps two normalised copies (T x H x K values each, input dtype) at
-    the start of both workspace layouts and changes nothing else in the plan."""
+    """The q/k normalisation keeps one normalised copy of k (T x H x K values, input dtype) at
+    the start of both workspace layouts (q is normalised where it is staged) and changes
+    nothing else in the plan."""
     base = plan(**kw)
     l2 = plan(flags=_abi.GDN_FLAG_QK_L2NORM, **kw)
     esize = 4 if kw.get("dtype") == torch.float32 else 2
     rows = kw.get("B", 1) * kw.get("T", 32768) * kw.get("H", 16)
-    extra = 2 * (-(-(rows * kw.get("K", 128) * esize) // 256) * 256)
+    extra = -(-(rows * kw.get("K", 128) * esize) // 256) * 256
     assert l2["fwd_workspace_bytes"] == base["fwd_workspace_bytes"] + extra
     assert l2["bwd_workspace_bytes"] == base["bwd_workspace_bytes"] + extra
     for f in ("cp_on", "seg_chunks", "total_segments", "warmup_chunks", "warmup_max_chunks"):
