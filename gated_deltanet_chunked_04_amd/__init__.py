@@ -152,7 +152,7 @@ def gdn_chunk_fwd(q, k, v, g, beta, initial_state=None, *, scale=1.0, cu_seqlens
     """Forward. Returns (o, final_state or None). Runs on the current stream.
 
     qk_l2norm=True takes raw q and k and runs the path on their rows scaled to
-    x / sqrt(sum x^2 + 1e-6) (normalised inside the library, into the workspace).
+    x / sqrt(sum x^2 + 1e-6) (normalised inside the kernels as they stage the rows).
 
     keep_for_backward=True leaves the intra-chunk results (gate cumsum, W, U, T), the CP
     decisions, the sub-sequence entry states, every chunk's entry state and Delta in `workspace`
