@@ -174,6 +174,22 @@ def decode_bench(gdn, H, K, V, dtype, reps=50):
         out[f"B{B}"] = {"H": H, "K": K, "V": V, "tokens_per_call": B, "us_per_call": round(us, 2),
                         "tokens_per_s": round(B / (us * 1e-6), 1), "GB/s": round(nbytes / (us * 1e-6) / 1e9, 1),
                         "hbm_frac": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+        if B == 1:
+            # the same steps captured in a HIP graph (no host work per token): the GPU-side
+            # latency of one decode step
+            torch.cuda.synchronize()
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                for _ in range(reps):
+                    gdn.gdn_recurrent_fwd(q, k, v, g, beta, state, state_out=state, o=o)
+            graph.replay()
+            torch.cuda.synchronize()
+            e0.record()
+            graph.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            out["B1"]["graph_us_per_call"] = round(e0.elapsed_time(e1) * 1e3 / reps, 2)
+            del graph
     return out
 
 

@@ -142,3 +142,36 @@ def test_decode_continues_l2norm_prefill(gpu_lib):
     check(o_pre, o_ref[:, :T0], 1e-2, "prefill o")
     check(o_dec, o_ref[:, T0:], 1e-2, "decode o")
     check(s_dec, s_ref, 1e-2, "decode state")
+
+
+def test_decode_in_hip_graph(gpu_lib):
+    """Eight in-place decode steps captured in a HIP graph (launches only, no memsets): every
+    replay, with eager work and synchronisations between replays, matches the same eight steps
+    run eagerly from the same state, bit for bit."""
+    inp = small_inputs(B=1, T=8, H=4, K=128, V=128, seed=28)
+    d = to_dev(inp)
+    steps = [slice_tokens(d, t, t + 1) for t in range(8)]
+    state = d["initial_state"].clone()
+    o = torch.empty((1, 1, 4, 128), dtype=torch.bfloat16, device="cuda")
+    outs = [torch.empty_like(o) for _ in range(8)]
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for t, x in enumerate(steps):
+            gpu_lib.gdn_recurrent_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], state, state_out=state, o=outs[t])
+    ref_state = d["initial_state"].clone()
+    for rep in range(3):
+        start = ref_state.clone()
+        state.copy_(start)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        # the same steps eagerly, from the same start
+        s_e = start.clone()
+        for t, x in enumerate(steps):
+            o_e, _ = gpu_lib.gdn_recurrent_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], s_e, state_out=s_e)
+            torch.cuda.synchronize()
+            assert torch.equal(outs[t], o_e), (rep, t)
+        assert torch.equal(state, s_e), rep
+        ref_state = s_e * 0.5  # a different start for the next replay
+    del graph
