@@ -32,10 +32,19 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-METRIC = "GDN chunked-prefill fwd/bwd tokens/s and TFLOP/s (% roofline), B=1 H=16 T=32K"
+METRIC_BASE = "GDN chunked-prefill fwd/bwd tokens/s and TFLOP/s (% roofline)"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # dense bf16 MFMA
 FP32_PEAK_TFLOPS = 157.3       # dense fp32 MFMA
+FLUSH_BYTES = 1 << 30          # written between flushed calls: 4x the 256 MB Infinity Cache
+
+
+def metric_name(w, B, T, H, lengths):
+    """The metric string with the workload's shape, e.g. "... , B=1 H=16 T=32K"."""
+    if lengths is not None:
+        return f"{METRIC_BASE}, varlen {len(lengths)} seqs ({sum(lengths)} tokens) H={H}"
+    t = f"{T // 1024}K" if T % 1024 == 0 else str(T)
+    return f"{METRIC_BASE}, B={B} H={H} T={t}"
 
 
 def algorithmic_counts(B, T, H, K, V, esize, N, nseg_total, lengths=None):
@@ -81,7 +90,21 @@ def algorithmic_counts(B, T, H, K, V, esize, N, nseg_total, lengths=None):
             f_intra += c * (c - 1) * K + c * (c - 1) * (c - 2) / 3 + c * (c - 1) * (K + V)
             f_recur += 3 * 2 * c * K * V + c * (c + 1) * (K + V)
             f_bwd += 7 * 2 * c * K * V + c * c * (2 * V + 2 * (K + V) + K + V + 4 * K) + 2 * c ** 3 / 3
-    return dict(bytes=nb, flops=dict(fwd=(f_intra + f_recur) * H, bwd=f_bwd * H), tokens=toks)
+    # the method's algorithmic bytes: the forward's two kernels as the pages split them (K1 reads
+    # k, v, g, beta and writes w, u, gate cumsum; K3 reads q, k, w, u, gate cumsum and writes o),
+    # and the backward's minimal I/O (reads q, k, v, dO, g, beta; writes dq, dk, dv, dg, dbeta),
+    # which the per-chunk gradient kernel is priced at since it writes every gradient
+    # (per token-head at K = V = 128, bf16: intra 1,036 B, recur_out 1,284 B, the forward 2,320 B,
+    # the backward 1,808 B; a fully fused forward's floor, q, k, v, g, beta in and o out, 1,032 B)
+    alg = dict(
+        intra=th * ((2 * K + 2 * V) * esize + 12),
+        recur_out=th * ((3 * K + 2 * V) * esize + 4),
+        bwd_chunk=th * ((4 * K + 3 * V) * esize + 16),
+        fwd=th * ((5 * K + 4 * V) * esize + 16),
+        bwd=th * ((4 * K + 3 * V) * esize + 16),
+        fused_min=th * ((2 * K + 2 * V) * esize + 8),
+    )
+    return dict(bytes=nb, alg_bytes=alg, flops=dict(fwd=(f_intra + f_recur) * H, bwd=f_bwd * H), tokens=toks)
 
 
 # Source files that define each kernel (plus the shared headers): a traffic figure measured
@@ -235,6 +258,25 @@ def l2norm_leg(gdn, dev, cu, cu_host, cp, timed, steps):
     return out
 
 
+def copy_ceiling(buf, reps=10):
+    """A plain device-to-device copy through torch (one read and one write of each byte) of half
+    of `buf` into its other half, HIP-event timed: the practical streaming rate on this part."""
+    import torch
+    n = buf.numel() // 2
+    src, dst = buf[:n], buf[n:2 * n]
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    dst.copy_(src)
+    for a, b in ev:
+        a.record()
+        dst.copy_(src)
+        b.record()
+    torch.cuda.synchronize()
+    ts = sorted(a.elapsed_time(b) for a, b in ev)
+    med = ts[reps // 2]
+    return {"bytes_copied": int(n), "median_ms": round(med, 4), "GB/s": round(2 * n / (med * 1e-3) / 1e9, 1),
+            "frac": round(2 * n / (med * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -244,6 +286,8 @@ def main():
     ap.add_argument("--pass", dest="passes", default="both", choices=["both", "fwd", "bwd"])
     ap.add_argument("--cp", default=None, help="override the workload's CP mode (auto/off/on/exact/warmup)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--flushed-calls", type=int, default=50,
+                    help="calls timed one by one after a 1 GiB cache flush (median and minimum)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="also run one device-to-device copy of this many MiB (a reference for HBM "
                          "byte counters taken with rocprofv3 --pmc)")
@@ -328,21 +372,43 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    # 1 GiB written between flushed calls evicts the 256 MB Infinity Cache and the L2s, so each
+    # flushed call reads its inputs from HBM
+    flush_buf = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
+
+    def flushed(fn, n):
+        """HIP-event durations of n calls on the current stream, each after a flush (the flush
+        is outside the events); median and minimum in ms."""
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        for i in range(n):
+            flush_buf.fill_(i & 255)
+            ev[i][0].record()
+            fn()
+            ev[i][1].record()
+        torch.cuda.synchronize()
+        ts = sorted(a.elapsed_time(b) for a, b in ev)
+        return {"median_ms": round(ts[n // 2] if n % 2 else 0.5 * (ts[n // 2 - 1] + ts[n // 2]), 4),
+                "min_ms": round(ts[0], 4), "calls": n}
+
     for _ in range(args.warmup):
         step()
     ms = timed(step, args.steps)
     ms_fwd = timed(fwd, args.steps) if do_fwd else None
     ms_bwd = timed(bwd, args.steps) if do_bwd else None
+    fl_step = flushed(step, args.flushed_calls)
+    fl_fwd = flushed(fwd, args.flushed_calls) if do_fwd else None
+    fl_bwd = flushed(bwd, args.flushed_calls) if do_bwd else None
     ms_keep = None
     if do_fwd and do_bwd:
         step_keep()
         ms_keep = timed(step_keep, args.steps)
     l2 = l2norm_leg(gdn, dev, cu, cu_host, cp, timed, args.steps) if (do_fwd and do_bwd) else None
 
-    # Per-kernel durations: one more round of steps with every launch bracketed by HIP
-    # events on the launch stream (separate from the timed loops above).
+    # Per-kernel durations: one more round of steps, each after a flush, with every launch
+    # bracketed by HIP events on its launch stream (separate from the timed loops above).
     gdn.gdn_profile_enable(True)
-    for _ in range(args.steps):
+    for i in range(args.steps):
+        flush_buf.fill_(i & 255)
         step()
     torch.cuda.synchronize()
     kt = gdn.gdn_profile_read()
@@ -350,23 +416,50 @@ def main():
     # average duration of one launch, and total per step
     kernels = {name: {"launches": n, "avg_us": 1e3 * tot / n, "per_step_us": 1e3 * tot / args.steps}
                for name, (n, tot) in kt.items()}
+    copy = copy_ceiling(flush_buf)
+    del flush_buf
 
     esize = 2 if q.dtype == torch.bfloat16 else 4
     counts = algorithmic_counts(B, T, H, K, V, esize, N, plan["total_segments"], lengths)
     tokens = counts["tokens"]
+    alg = counts["alg_bytes"]
     flops_step = (counts["flops"]["fwd"] if do_fwd else 0) + (counts["flops"]["bwd"] if do_bwd else 0)
-    dominant = max((n for n in kernels if n in counts["bytes"]), key=lambda n: kernels[n]["per_step_us"])
+    # the dominant kernel among those the method's byte accounting prices (each launch covers
+    # the whole workload once)
+    dominant = max((n for n in kernels if n in alg), key=lambda n: kernels[n]["per_step_us"])
     dur_s = kernels[dominant]["avg_us"] * 1e-6
-    bytes_per_launch = counts["bytes"][dominant]  # every launch of it covers the whole workload once
-    achieved = bytes_per_launch / dur_s / 1e9
+    achieved = alg[dominant] / dur_s / 1e9
+    design = counts["bytes"][dominant]
     roofline = {"bound": "hbm", "kernel": dominant, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": measured_traffic(dominant, w.name),
-                "algorithmic_bytes_per_launch": int(bytes_per_launch), "avg_launch_us": round(dur_s * 1e6, 2)}
+                "algorithmic_bytes_per_launch": int(alg[dominant]), "avg_launch_us": round(dur_s * 1e6, 2),
+                # what this design's kernel actually has to move (its intermediates too)
+                "design_bytes_per_launch": int(design),
+                "design_frac": round(design / dur_s / 1e9 / HBM_PEAK_GBS, 4)}
     peak_mfma = BF16_PEAK_TFLOPS if esize == 2 else FP32_PEAK_TFLOPS
     tflops = flops_step / (ms * 1e-3) / 1e12
+
+    def kroof(n):
+        us = kernels[n]["avg_us"]
+        r = {"avg_launch_us": round(us, 2)}
+        if n in alg:
+            r["algorithmic_bytes"] = int(alg[n])
+            r["GB/s"] = round(alg[n] / (us * 1e-6) / 1e9, 1)
+            r["frac"] = round(alg[n] / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
+        if n in counts["bytes"]:
+            r["design_bytes"] = int(counts["bytes"][n])
+            r["design_frac"] = round(counts["bytes"][n] / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
+        return r
+
+    def pass_roofline(nbytes, flops, t_ms):
+        gbs = nbytes / (t_ms * 1e-3) / 1e9
+        return {"bound": "hbm", "algorithmic_bytes": int(nbytes), "GB/s": round(gbs, 1),
+                "frac": round(gbs / HBM_PEAK_GBS, 4), "frac_of_copy": round(gbs / copy["GB/s"], 4),
+                "mfma_frac": round(flops / (t_ms * 1e-3) / 1e12 / peak_mfma, 4)}
+
     line = {
-        "metric": METRIC,
+        "metric": metric_name(w, B, T, H, lengths),
         "value": round(tokens / (ms * 1e-3), 1),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -384,23 +477,27 @@ def main():
         "tflops": round(tflops, 2),
         "mfma_frac": round(tflops / peak_mfma, 4),
         "roofline": roofline,
+        # every call after a 1 GiB cache flush, HIP events around the call (median, minimum)
+        "flushed": {"step": fl_step, "tokens_per_s_median": round(tokens / (fl_step["median_ms"] * 1e-3), 1)},
+        "copy_ceiling": copy,
         "kernels_us_per_step": {n: round(x["per_step_us"], 2) for n, x in kernels.items()},
-        # every kernel with a byte model against the HBM roofline (HIP-event launch durations;
-        # the backward's reverse chain runs beside its state chain on a second stream, so
-        # those durations include shared time, and k_intra's average mixes the forward launch
-        # with the backward's, which also writes T: priced here at the forward's bytes)
-        "kernels_roofline": {
-            n: {"avg_launch_us": round(kernels[n]["avg_us"], 2), "algorithmic_bytes": int(b),
-                "GB/s": round(b / (kernels[n]["avg_us"] * 1e-6) / 1e9, 1),
-                "frac": round(b / (kernels[n]["avg_us"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
-            for n, b in counts["bytes"].items() if n in kernels},
+        # every kernel against the HBM roofline on flushed steps: "frac" on the method's
+        # algorithmic bytes where it prices the kernel, "design_frac" on what this design's kernel
+        # moves (the backward's reverse chain runs beside its state chain on a second stream, so
+        # those durations include shared time; k_intra's average mixes the forward launch with
+        # the backward's, which also writes T)
+        "kernels_roofline": {n: kroof(n) for n in kernels if n in alg or n in counts["bytes"]},
     }
     if do_fwd:
         line["fwd"] = {"ms": round(ms_fwd, 4), "tokens_per_s": round(tokens / (ms_fwd * 1e-3), 1),
-                       "tflops": round(counts["flops"]["fwd"] / (ms_fwd * 1e-3) / 1e12, 2)}
+                       "tflops": round(counts["flops"]["fwd"] / (ms_fwd * 1e-3) / 1e12, 2), "flushed": fl_fwd,
+                       # the pages' two-kernel method's bytes over the flushed median
+                       "roofline": pass_roofline(alg["fwd"], counts["flops"]["fwd"], fl_fwd["median_ms"]),
+                       "fused_min_bytes": int(alg["fused_min"])}
     if do_bwd:
         line["bwd"] = {"ms": round(ms_bwd, 4), "tokens_per_s": round(tokens / (ms_bwd * 1e-3), 1),
-                       "tflops": round(counts["flops"]["bwd"] / (ms_bwd * 1e-3) / 1e12, 2)}
+                       "tflops": round(counts["flops"]["bwd"] / (ms_bwd * 1e-3) / 1e12, 2), "flushed": fl_bwd,
+                       "roofline": pass_roofline(alg["bwd"], counts["flops"]["bwd"], fl_bwd["median_ms"])}
     if ms_keep is not None:
         line["keep_forward"] = {"ms_per_step": round(ms_keep, 4),
                                 "tokens_per_s": round(tokens / (ms_keep * 1e-3), 1)}

@@ -114,11 +114,32 @@ def gdn_workspace(q, v, *, cu_seqlens=None, cu_seqlens_host=None, cp_mode="auto"
 
 
 def _workspace(nbytes: int, device, workspace=None):
+    """(workspace tensor, its size in bytes). A caller's workspace must be a contiguous tensor on
+    the inputs' device whose first byte is 256-byte aligned; any element type (its size in bytes
+    is what the library is told)."""
     if workspace is not None:
-        if workspace.numel() * workspace.element_size() < nbytes:
-            raise ValueError("workspace too small")
-        return workspace
-    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+        if not isinstance(workspace, torch.Tensor) or workspace.device != torch.device(device):
+            raise ValueError(f"workspace must be a tensor on {device}")
+        if not workspace.is_contiguous():
+            raise ValueError("workspace must be contiguous")
+        if workspace.data_ptr() % 256:
+            raise ValueError("workspace must start at a 256-byte aligned address")
+        size = workspace.numel() * workspace.element_size()
+        if size < nbytes:
+            raise ValueError(f"workspace too small: {size} bytes, {nbytes} needed")
+        return workspace, size
+    ws = torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+    return ws, ws.numel()
+
+
+def _check_buffer(name, t, shape, dtype, device):
+    """A caller-supplied output (or upstream gradient) must be a contiguous tensor of exactly
+    this shape and dtype on the inputs' device: the library writes through its pointer."""
+    if t is None:
+        return
+    if (not isinstance(t, torch.Tensor) or tuple(t.shape) != tuple(shape) or t.dtype != dtype
+            or t.device != device or not t.is_contiguous()):
+        raise ValueError(f"{name}: expected a contiguous {tuple(shape)} {dtype} tensor on {device}")
 
 
 def _check_inputs(q, k, v, g, beta, initial_state, N):
@@ -170,17 +191,19 @@ def gdn_chunk_fwd(q, k, v, g, beta, initial_state=None, *, scale=1.0, cu_seqlens
     lib = load_library()
     nbytes = ctypes.c_size_t()
     check(lib.gdn_chunk_fwd_workspace_size(desc.ref, ctypes.byref(nbytes)), "gdn_chunk_fwd_workspace_size")
-    ws = _workspace(nbytes.value, q.device, workspace)
+    ws, ws_bytes = _workspace(nbytes.value, q.device, workspace)
     B, T, H, K = q.shape
     V = v.shape[-1]
     if o is None:
         o = torch.empty((B, T, H, V), dtype=q.dtype, device=q.device)
+    _check_buffer("o", o, (B, T, H, V), q.dtype, q.device)
     if output_final_state and final_state is None:
         final_state = torch.empty((N, H, V, K), dtype=torch.float32, device=q.device)
     if not output_final_state:
         final_state = None
+    _check_buffer("final_state", final_state, (N, H, V, K), torch.float32, q.device)
     check(lib.gdn_chunk_fwd(desc.ref, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state),
-                            _ptr(o), _ptr(final_state), _ptr(ws), ctypes.c_size_t(ws.numel()), _stream()),
+                            _ptr(o), _ptr(final_state), _ptr(ws), ctypes.c_size_t(ws_bytes), _stream()),
           "gdn_chunk_fwd")
     return o, final_state
 
@@ -201,12 +224,10 @@ def gdn_chunk_bwd(q, k, v, g, beta, d_o, initial_state=None, d_final_state=None,
     _check_inputs(q, k, v, g, beta, initial_state, N)
     B, T, H, K = q.shape
     V = v.shape[-1]
-    if tuple(d_o.shape) != (B, T, H, V) or d_o.dtype != q.dtype or not d_o.is_contiguous():
-        raise ValueError("d_o must match o")
-    if d_final_state is not None and (tuple(d_final_state.shape) != (N, H, V, K)
-                                      or d_final_state.dtype != torch.float32
-                                      or not d_final_state.is_contiguous()):
-        raise ValueError("d_final_state must be contiguous fp32 [N,H,V,K]")
+    if d_o is None:
+        raise ValueError("d_o is required")
+    _check_buffer("d_o", d_o, (B, T, H, V), q.dtype, q.device)
+    _check_buffer("d_final_state", d_final_state, (N, H, V, K), torch.float32, q.device)
     if reuse_forward and workspace is None:
         raise ValueError("reuse_forward needs the forward's workspace")
     desc = make_desc(q, v, scale=scale, cu_seqlens=cu_seqlens, cu_seqlens_host=cu_seqlens_host,
@@ -216,16 +237,23 @@ def gdn_chunk_bwd(q, k, v, g, beta, d_o, initial_state=None, d_final_state=None,
     lib = load_library()
     nbytes = ctypes.c_size_t()
     check(lib.gdn_chunk_bwd_workspace_size(desc.ref, ctypes.byref(nbytes)), "gdn_chunk_bwd_workspace_size")
-    ws = _workspace(nbytes.value, q.device, workspace)
+    ws, ws_bytes = _workspace(nbytes.value, q.device, workspace)
     if out is None:
         out = dict(dq=torch.empty_like(q), dk=torch.empty_like(k), dv=torch.empty_like(v),
                    dg=torch.empty_like(g), dbeta=torch.empty_like(beta),
                    d_initial_state=(torch.empty((N, H, V, K), dtype=torch.float32, device=q.device)
                                     if need_d_initial_state else None))
+    shapes = dict(dq=((B, T, H, K), q.dtype), dk=((B, T, H, K), q.dtype), dv=((B, T, H, V), q.dtype),
+                  dg=((B, T, H), torch.float32), dbeta=((B, T, H), torch.float32),
+                  d_initial_state=((N, H, V, K), torch.float32))
+    for name, (shape, dt) in shapes.items():
+        if name not in out or (out[name] is None and name != "d_initial_state"):
+            raise ValueError(f"out[{name!r}] is required")
+        _check_buffer(f"out[{name!r}]", out[name], shape, dt, q.device)
     check(lib.gdn_chunk_bwd(desc.ref, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state),
                             _ptr(d_o), _ptr(d_final_state), _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]),
                             _ptr(out["dg"]), _ptr(out["dbeta"]), _ptr(out["d_initial_state"]),
-                            _ptr(ws), ctypes.c_size_t(ws.numel()), _stream()),
+                            _ptr(ws), ctypes.c_size_t(ws_bytes), _stream()),
           "gdn_chunk_bwd")
     return out
 
@@ -238,12 +266,12 @@ def gdn_intra_chunk(k, v, g, beta, *, cu_seqlens=None, cu_seqlens_host=None, qk_
     lib = load_library()
     nbytes = ctypes.c_size_t()
     check(lib.gdn_chunk_fwd_workspace_size(desc.ref, ctypes.byref(nbytes)), "gdn_chunk_fwd_workspace_size")
-    ws = _workspace(nbytes.value, k.device)
+    ws, ws_bytes = _workspace(nbytes.value, k.device)
     gam = torch.empty((B, T, H), dtype=torch.float32, device=k.device)
     w = torch.empty_like(k)
     u = torch.empty_like(v)
     check(lib.gdn_intra_chunk(desc.ref, _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(gam), _ptr(w), _ptr(u),
-                              _ptr(ws), ctypes.c_size_t(ws.numel()), _stream()), "gdn_intra_chunk")
+                              _ptr(ws), ctypes.c_size_t(ws_bytes), _stream()), "gdn_intra_chunk")
     return gam, w, u
 
 
@@ -257,10 +285,10 @@ def gdn_cp_modes(k, v, g, beta, *, cu_seqlens=None, cu_seqlens_host=None, cp_mod
     lib = load_library()
     nbytes = ctypes.c_size_t()
     check(lib.gdn_chunk_fwd_workspace_size(desc.ref, ctypes.byref(nbytes)), "gdn_chunk_fwd_workspace_size")
-    ws = _workspace(nbytes.value, k.device)
+    ws, ws_bytes = _workspace(nbytes.value, k.device)
     modes = torch.empty((N, k.shape[2]), dtype=torch.int32, device=k.device)
     check(lib.gdn_cp_modes(desc.ref, _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(modes), _ptr(ws),
-                           ctypes.c_size_t(ws.numel()), _stream()), "gdn_cp_modes")
+                           ctypes.c_size_t(ws_bytes), _stream()), "gdn_cp_modes")
     return modes
 
 
@@ -282,6 +310,7 @@ def gdn_recurrent_fwd(q, k, v, g, beta, state=None, *, scale=1.0, state_out=None
         raise ValueError(f"state_out: expected contiguous fp32 {(B, H, V, K)} on {q.device}")
     if o is None:
         o = torch.empty((B, T, H, V), dtype=q.dtype, device=q.device)
+    _check_buffer("o", o, (B, T, H, V), q.dtype, q.device)
     desc = make_desc(q, v, scale=scale, qk_l2norm=qk_l2norm)
     check(load_library().gdn_recurrent_fwd(desc.ref, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
                                            _ptr(state), _ptr(state_out), _ptr(o), _stream()),
@@ -305,11 +334,17 @@ def gdn_profile_read() -> dict:
 
 class _GDNFunction(torch.autograd.Function):
     @staticmethod
-    def forward(ctx, q, k, v, g, beta, initial_state, scale, cu_seqlens, cp_mode, keep, l2):
-        ws = gdn_workspace(q, v, cu_seqlens=cu_seqlens, cp_mode=cp_mode, qk_l2norm=l2) if keep else None
-        o, sT = gdn_chunk_fwd(q, k, v, g, beta, initial_state, scale=scale, cu_seqlens=cu_seqlens,
-                              cp_mode=cp_mode, workspace=ws, keep_for_backward=keep, qk_l2norm=l2)
+    def forward(ctx, q, k, v, g, beta, initial_state, scale, cu_seqlens, cu_host, cp_mode, keep, l2):
+        # one host copy of cu_seqlens for every call of the step (planning reads the host copy;
+        # taking it from the device would synchronise once per call)
+        if cu_seqlens is not None and cu_host is None:
+            cu_host = cu_seqlens.detach().cpu()
+        cu = dict(cu_seqlens=cu_seqlens, cu_seqlens_host=cu_host)
+        ws = gdn_workspace(q, v, cp_mode=cp_mode, qk_l2norm=l2, **cu) if keep else None
+        o, sT = gdn_chunk_fwd(q, k, v, g, beta, initial_state, scale=scale, cp_mode=cp_mode, workspace=ws,
+                              keep_for_backward=keep, qk_l2norm=l2, **cu)
         ctx.save_for_backward(q, k, v, g, beta, initial_state, cu_seqlens)
+        ctx.cu_host = cu_host
         ctx.scale = scale
         ctx.cp_mode = cp_mode
         ctx.l2 = l2
@@ -322,25 +357,28 @@ class _GDNFunction(torch.autograd.Function):
         ws, ctx.ws = ctx.ws, None
         gr = gdn_chunk_bwd(q, k, v, g, beta, d_o.contiguous(), s0,
                            None if d_sT is None else d_sT.contiguous(), scale=ctx.scale,
-                           cu_seqlens=cu, cp_mode=ctx.cp_mode, need_d_initial_state=s0 is not None,
-                           workspace=ws, reuse_forward=ws is not None, qk_l2norm=ctx.l2)
+                           cu_seqlens=cu, cu_seqlens_host=ctx.cu_host, cp_mode=ctx.cp_mode,
+                           need_d_initial_state=s0 is not None, workspace=ws, reuse_forward=ws is not None,
+                           qk_l2norm=ctx.l2)
         return (gr["dq"], gr["dk"], gr["dv"], gr["dg"], gr["dbeta"], gr["d_initial_state"],
-                None, None, None, None, None)
+                None, None, None, None, None, None)
 
 
 def chunk_gated_delta_rule(q, k, v, g, beta, scale: float = 1.0, initial_state=None,
                            output_final_state: bool = True, cu_seqlens=None, cp_mode: str = "auto",
-                           keep_intermediates: bool = False, qk_l2norm: bool = False):
+                           keep_intermediates: bool = False, qk_l2norm: bool = False, cu_seqlens_host=None):
     """High-level call: (o, final_state) with autograd through gdn_chunk_bwd.
 
     q, k: [B,T,H,K]; v: [B,T,H,V] (bf16 or fp32); g (natural-log decay) and beta: [B,T,H] fp32;
-    initial_state: [N,H,V,K] fp32 or None; cu_seqlens: int32 [N+1] device tensor (B must be 1).
+    initial_state: [N,H,V,K] fp32 or None; cu_seqlens: int32 [N+1] device tensor (B must be 1), with
+    cu_seqlens_host its host copy if the caller has one (else one device-to-host copy per forward,
+    kept for the backward).
     keep_intermediates=True holds the forward's workspace (W, U, T, gate cumsum, CP entry states,
     chunk states and Delta) until the backward, which then skips recomputing them: more memory,
     less backward time. qk_l2norm=True normalises q and k rows inside the library
     (x / sqrt(sum x^2 + 1e-6)); gradients flow to the raw q and k.
     """
-    o, sT = _GDNFunction.apply(q, k, v, g, beta, initial_state, scale, cu_seqlens, cp_mode,
+    o, sT = _GDNFunction.apply(q, k, v, g, beta, initial_state, scale, cu_seqlens, cu_seqlens_host, cp_mode,
                                bool(keep_intermediates and torch.is_grad_enabled()
                                     and any(x.requires_grad for x in (q, k, v, g, beta))),
                                bool(qk_l2norm))

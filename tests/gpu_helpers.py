@@ -78,3 +78,22 @@ def gpu_fwd(dinp, **kw):
                               dinp["initial_state"], cu_seqlens=dinp.get("cu_seqlens"), **kw)
     torch.cuda.synchronize()
     return o, sT
+
+
+def raw_key_inputs(B=2, T=1000, H=2, K=128, V=128, dtype=torch.bfloat16, seed=21, kk=3.5):
+    """The workloads' distributions except that k is not unit-norm: every key row has
+    |k|^2 = kk (3.5), so with beta = sigmoid(N(0,1)) about 40% of tokens have beta |k|^2 > 2.
+    Those token maps exp(g)(I - beta k k^T) have an eigenvalue below -exp(g), so the gate decay
+    alone no longer bounds the warmup error: the CP decision must take the exact correction
+    although the gates decay fast (about -5 per chunk)."""
+    inp = small_inputs(B=B, T=T, H=H, K=K, V=V, dtype=torch.float32, seed=seed)
+    inp["k"] = (inp["k"] * kk ** 0.5).to(dtype)
+    inp["q"] = inp["q"].to(dtype)
+    inp["v"] = inp["v"].to(dtype)
+    return inp
+
+
+def seq_slices(cu):
+    """(n, start, end) of every non-empty sequence of a cu_seqlens tensor."""
+    c = [int(x) for x in cu]
+    return [(n, c[n], c[n + 1]) for n in range(len(c) - 1) if c[n + 1] > c[n]]

@@ -9,7 +9,7 @@ import pytest
 import torch
 
 from gdn_inputs import make_inputs
-from gpu_helpers import check, mid_decay_inputs, small_inputs, to_dev, tol_for
+from gpu_helpers import check, mid_decay_inputs, raw_key_inputs, seq_slices, small_inputs, to_dev, tol_for
 from oracle import ref_bwd
 
 pytestmark = pytest.mark.gpu
@@ -94,7 +94,13 @@ def test_backward_varlen(gpu_lib, cp, kw, dtype):
     inp = with_grads(small_inputs(H=3, K=K, V=V, dtype=dtype, lengths=lengths, seed=12))
     out = gpu_bwd(to_dev(inp), cp_mode=cp, **kw)
     ref = oracle_bwd(inp)
-    compare(out, ref, tol_for(dtype))
+    tol = tol_for(dtype)
+    compare(out, ref, tol)
+    # every sequence on its own: the token gradients of each sequence and its d(initial state)
+    for n, a, b in seq_slices(inp["cu_seqlens"]):
+        for name in NAMES[:5]:
+            check(out[name][:, a:b], ref[name][:, a:b], tol, f"{name} of sequence {n} ({b - a} tokens)")
+        check(out["d_initial_state"][n], ref["d_initial_state"][n], tol, f"d_initial_state of sequence {n}")
     # the empty sequence passes d(final state) straight through
     assert torch.equal(out["d_initial_state"][4].cpu(), inp["d_final_state"][4])
 
@@ -295,3 +301,16 @@ def test_backward_autocp_fills_idle_units(gpu_lib):
     out = gpu_bwd(d)
     heads = [0, 5, 23]
     compare({n: out[n].cpu() for n in NAMES}, oracle_bwd(inp, heads=heads), 1e-2, heads=heads)
+
+
+@pytest.mark.parametrize("dtype,K,V", [(torch.float32, 64, 64), (torch.bfloat16, 128, 128)])
+def test_backward_raw_keys_exact_correction(gpu_lib, dtype, K, V):
+    """Keys with |k|^2 = 3.5 (beta |k|^2 > 2 on part of every window, fast gate decay): both CP
+    directions must take the exact correction; all six gradients match the oracle."""
+    kw = dict(cp_mode="on", seg_chunks=4, warmup_chunks=2)
+    inp = with_grads(raw_key_inputs(K=K, V=V, dtype=dtype))
+    d = to_dev(inp)
+    modes = gpu_lib.gdn_cp_modes(d["k"], d["v"], d["g"], d["beta"], **kw).cpu()
+    assert (modes == 2).all(), modes
+    errs = compare(gpu_bwd(d, **kw), oracle_bwd(inp), tol_for(dtype))
+    print(f"raw keys {dtype} " + " ".join(f"{n}={e:.2e}" for n, e in errs.items()), flush=True)

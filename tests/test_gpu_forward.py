@@ -8,7 +8,8 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_helpers import BF16_TOL, check, gpu_fwd, mid_decay_inputs, oracle, rel_l2, small_inputs, to_dev, tol_for  # noqa: F401
+from gpu_helpers import (BF16_TOL, check, gpu_fwd, mid_decay_inputs, oracle, raw_key_inputs, rel_l2,  # noqa: F401
+                         seq_slices, small_inputs, to_dev, tol_for)
 from oracle.chunked import chunked_fwd
 
 pytestmark = pytest.mark.gpu
@@ -71,6 +72,10 @@ def test_forward_varlen(gpu_lib, cp, kw, dtype):
     o, sT = gpu_fwd(to_dev(inp), cp_mode=cp, **kw)
     tol = tol_for(dtype)
     check(o, o_ref, tol)
+    # every sequence on its own: a wrong 1- or 63-token sequence weighs little in the packed O
+    oc = o.cpu()
+    for n, a, b in seq_slices(inp["cu_seqlens"]):
+        check(oc[:, a:b], o_ref[:, a:b], tol, f"o of sequence {n} ({b - a} tokens)")
     for n in range(len(lengths)):
         check(sT[n], s_ref[n], tol, f"sequence {n}")
     # the empty sequence returns its initial state
@@ -165,3 +170,71 @@ def test_autocp_fills_idle_units(gpu_lib):
     o2, s2 = gpu_fwd(d, cp_mode="pages")
     check(o, o2.double().cpu(), BF16_TOL, "o vs serial")
     check(sT, s2.double().cpu(), BF16_TOL, "final_state vs serial")
+
+
+@pytest.mark.parametrize("dtype,K,V", [(torch.float32, 64, 64), (torch.bfloat16, 128, 128)])
+def test_raw_keys_take_the_exact_correction(gpu_lib, dtype, K, V):
+    """Keys with |k|^2 = 3.5 (not normalised, no qk_l2norm): beta |k|^2 > 2 on part of every
+    window, so the warmup's error bound does not hold and every sequence-head takes the exact
+    correction although the gates decay fast; the same gates with unit-norm keys take the
+    warmup. O and the final state match the oracle."""
+    kw = dict(cp_mode="on", seg_chunks=4, warmup_chunks=2)
+    inp = raw_key_inputs(K=K, V=V, dtype=dtype)
+    bk = inp["beta"] * inp["k"].float().pow(2).sum(-1)
+    assert float((bk > 2).float().mean()) > 0.2
+    d = to_dev(inp)
+    modes = gpu_lib.gdn_cp_modes(d["k"], d["v"], d["g"], d["beta"], **kw).cpu()
+    assert (modes == 2).all(), modes
+    unit = to_dev(small_inputs(K=K, V=V, dtype=dtype, seed=21))  # same seed: same gates and beta
+    assert torch.equal(unit["g"], d["g"]) and torch.equal(unit["beta"], d["beta"])
+    m1 = gpu_lib.gdn_cp_modes(unit["k"], unit["v"], unit["g"], unit["beta"], **kw).cpu()
+    assert (m1 == 1).all(), m1
+    o_ref, s_ref = oracle(inp)
+    o, sT = gpu_fwd(d, **kw)
+    tol = tol_for(dtype)
+    e_o = check(o, o_ref, tol, "o")
+    e_s = check(sT, s_ref, tol, "final_state")
+    print(f"raw keys {dtype} rel_l2 o={e_o:.2e} final={e_s:.2e}", flush=True)
+
+
+def test_binding_rejects_bad_buffers(gpu_lib):
+    """Caller-supplied outputs, upstream gradients and workspaces are checked in the binding
+    (device, shape, dtype, contiguity, alignment) before any pointer reaches the library."""
+    gdn = gpu_lib
+    d = to_dev(small_inputs(B=1, T=200, H=2, K=64, V=64, dtype=torch.float32))
+    args = (d["q"], d["k"], d["v"], d["g"], d["beta"], d["initial_state"])
+    B, T, H, K = d["q"].shape
+    with pytest.raises(ValueError, match="^o"):
+        gdn.gdn_chunk_fwd(*args, o=torch.empty((B, T, H, K)))  # host tensor
+    with pytest.raises(ValueError, match="^o"):
+        gdn.gdn_chunk_fwd(*args, o=torch.empty((B, T, H, K + 1), device="cuda"))
+    with pytest.raises(ValueError, match="^o"):
+        gdn.gdn_chunk_fwd(*args, o=torch.empty((B, T, K, H), device="cuda").transpose(2, 3))
+    with pytest.raises(ValueError, match="^final_state"):
+        gdn.gdn_chunk_fwd(*args, final_state=torch.empty((1, H, K, K), device="cuda", dtype=torch.bfloat16))
+    ws = torch.empty(1 << 22, dtype=torch.uint8, device="cuda")
+    with pytest.raises(ValueError, match="aligned"):
+        gdn.gdn_chunk_fwd(*args, workspace=ws[1:])
+    with pytest.raises(ValueError, match="too small"):
+        gdn.gdn_chunk_fwd(*args, workspace=ws[:256])
+    # a workspace of another element type is sized in bytes
+    o_ref, _ = gdn.gdn_chunk_fwd(*args)
+    o_ws, _ = gdn.gdn_chunk_fwd(*args, workspace=torch.empty(1 << 20, dtype=torch.float32, device="cuda"))
+    assert torch.equal(o_ref, o_ws)
+    d_o = torch.randn((B, T, H, K), device="cuda")
+    with pytest.raises(ValueError, match="^d_o"):
+        gdn.gdn_chunk_bwd(*args[:5], d_o.cpu(), d["initial_state"])
+    with pytest.raises(ValueError, match="d_final_state"):
+        gdn.gdn_chunk_bwd(*args[:5], d_o, d["initial_state"], torch.zeros((1, H, K, K)))
+    out = dict(dq=torch.empty_like(d["q"]), dk=torch.empty_like(d["k"]), dv=torch.empty_like(d["v"]),
+               dg=torch.empty_like(d["g"]), dbeta=torch.empty_like(d["beta"]),
+               d_initial_state=torch.empty((1, H, K, K), device="cuda"))
+    bad = dict(out, dg=torch.empty((B, T, H + 1), device="cuda"))
+    with pytest.raises(ValueError, match="dg"):
+        gdn.gdn_chunk_bwd(*args[:5], d_o, d["initial_state"], out=bad)
+    bad = dict(out, dk=out["dk"].cpu())
+    with pytest.raises(ValueError, match="dk"):
+        gdn.gdn_chunk_bwd(*args[:5], d_o, d["initial_state"], out=bad)
+    with pytest.raises(ValueError, match="^o"):
+        gdn.gdn_recurrent_fwd(d["q"][:, :3], d["k"][:, :3], d["v"][:, :3], d["g"][:, :3].contiguous(),
+                              d["beta"][:, :3].contiguous(), d["initial_state"], o=torch.empty((B, 3, H, K)))
