@@ -7,6 +7,7 @@ missing they raise instead of computing anything elsewhere.
 
   gdn_plan(...)               host-side plan (AutoCP decision, sub-sequence length, workspace)
   gdn_chunk_fwd(...)          O and the final state
+  gdn_chunk_fwd_noalloc(...)  the same on the library's fixed scratch array (no allocation)
   gdn_chunk_bwd(...)          gradients of <dO, O> + <dS_T, S_T>
   gdn_workspace(...)          one buffer that serves a forward that keeps its intermediates
                               and the backward that reuses them
@@ -24,10 +25,10 @@ import numpy as np
 import torch
 
 from ._abi import (CP_MODES, EXPORTS, GDN_DTYPE_BF16, GDN_DTYPE_FP32, GDN_FLAG_KEEP_FORWARD,  # noqa: F401
-                   GDN_FLAG_QK_L2NORM, GDN_FLAG_REUSE_FORWARD, GdnDesc, GdnError, GdnKernelTime, GdnPlanInfo, check,
+                   GDN_FLAG_QK_L2NORM, GDN_NOALLOC_SCRATCH_BYTES, GDN_FLAG_REUSE_FORWARD, GdnDesc, GdnError, GdnKernelTime, GdnPlanInfo, check,
                    load_library, status_string)
 
-__all__ = ["gdn_plan", "gdn_chunk_fwd", "gdn_chunk_bwd", "gdn_workspace", "gdn_intra_chunk", "gdn_cp_modes",
+__all__ = ["gdn_plan", "gdn_chunk_fwd", "gdn_chunk_fwd_noalloc", "gdn_chunk_bwd", "gdn_workspace", "gdn_intra_chunk", "gdn_cp_modes",
            "gdn_recurrent_fwd", "gdn_profile_enable", "gdn_profile_read", "chunk_gated_delta_rule", "load_library",
            "make_desc", "GdnError"]
 
@@ -205,6 +206,35 @@ def gdn_chunk_fwd(q, k, v, g, beta, initial_state=None, *, scale=1.0, cu_seqlens
     check(lib.gdn_chunk_fwd(desc.ref, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state),
                             _ptr(o), _ptr(final_state), _ptr(ws), ctypes.c_size_t(ws_bytes), _stream()),
           "gdn_chunk_fwd")
+    return o, final_state
+
+
+def gdn_chunk_fwd_noalloc(q, k, v, g, beta, initial_state=None, *, scale=1.0, cu_seqlens=None,
+                          cu_seqlens_host=None, output_final_state=True, cp_mode="auto", warmup_chunks=0,
+                          seg_chunks=0, warmup_eps=0.0, warmup_max_chunks=0, o=None, final_state=None,
+                          qk_l2norm=False):
+    """Forward on the library's fixed per-GPU scratch array instead of a workspace (for callers
+    that cannot allocate: pass `o` and `final_state` preallocated). Returns (o, final_state or None).
+    Problems whose forward workspace exceeds GDN_NOALLOC_SCRATCH_BYTES raise GdnError (workspace).
+    Calls that overlap on one GPU race on the shared array."""
+    N = _num_seqs(q, cu_seqlens)
+    _check_inputs(q, k, v, g, beta, initial_state, N)
+    desc = make_desc(q, v, scale=scale, cu_seqlens=cu_seqlens, cu_seqlens_host=cu_seqlens_host,
+                     cp_mode=cp_mode, warmup_chunks=warmup_chunks, seg_chunks=seg_chunks,
+                     warmup_eps=warmup_eps, warmup_max_chunks=warmup_max_chunks, qk_l2norm=qk_l2norm)
+    B, T, H, K = q.shape
+    V = v.shape[-1]
+    if o is None:
+        o = torch.empty((B, T, H, V), dtype=q.dtype, device=q.device)
+    _check_buffer("o", o, (B, T, H, V), q.dtype, q.device)
+    if output_final_state and final_state is None:
+        final_state = torch.empty((N, H, V, K), dtype=torch.float32, device=q.device)
+    if not output_final_state:
+        final_state = None
+    _check_buffer("final_state", final_state, (N, H, V, K), torch.float32, q.device)
+    check(load_library().gdn_chunk_fwd_noalloc(desc.ref, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                               _ptr(initial_state), _ptr(o), _ptr(final_state), _stream()),
+          "gdn_chunk_fwd_noalloc")
     return o, final_state
 
 

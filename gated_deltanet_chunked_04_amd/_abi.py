@@ -16,11 +16,12 @@ GDN_OK, GDN_ERR_INVALID_ARG, GDN_ERR_UNSUPPORTED, GDN_ERR_WORKSPACE, GDN_ERR_HIP
 GDN_DTYPE_BF16, GDN_DTYPE_FP32 = 0, 1
 CP_MODES = {"auto": 0, "off": 1, "on": 2, "exact": 3, "warmup": 4, "pages": 5}
 GDN_FLAG_KEEP_FORWARD, GDN_FLAG_REUSE_FORWARD, GDN_FLAG_QK_L2NORM = 1, 2, 4
-GDN_ABI_VERSION = 6
+GDN_ABI_VERSION = 7
+GDN_NOALLOC_SCRATCH_BYTES = 128 << 20
 
 # Declared entry points of include/gdn.h (checked by the ABI test).
 EXPORTS = ("gdn_abi_version", "gdn_status_string", "gdn_plan", "gdn_chunk_fwd_workspace_size",
-           "gdn_chunk_fwd", "gdn_chunk_bwd_workspace_size", "gdn_chunk_bwd", "gdn_intra_chunk",
+           "gdn_chunk_fwd", "gdn_chunk_fwd_noalloc", "gdn_chunk_bwd_workspace_size", "gdn_chunk_bwd", "gdn_intra_chunk",
            "gdn_cp_modes", "gdn_recurrent_fwd", "gdn_profile_enable", "gdn_profile_read")
 
 
@@ -84,6 +85,8 @@ def load_library(path: str = LIB_PATH):
         getattr(lib, f).argtypes = [dp, ctypes.POINTER(sz)]
     lib.gdn_chunk_fwd.restype = i32
     lib.gdn_chunk_fwd.argtypes = [dp] + [vp] * 8 + [vp, sz, vp]
+    lib.gdn_chunk_fwd_noalloc.restype = i32
+    lib.gdn_chunk_fwd_noalloc.argtypes = [dp] + [vp] * 8 + [vp]
     lib.gdn_chunk_bwd.restype = i32
     lib.gdn_chunk_bwd.argtypes = [dp] + [vp] * 14 + [vp, sz, vp]
     lib.gdn_intra_chunk.restype = i32

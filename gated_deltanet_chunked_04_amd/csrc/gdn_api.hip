@@ -416,6 +416,43 @@ gdn_status run_decide(const gdn_desc* d, const Plan& p, unsigned char* ws, int32
     return GDN_OK;
 }
 
+gdn_status run_fwd(const gdn_desc* desc, const Plan& p, const void* q, const void* k, const void* v,
+                   const float* g, const float* beta, const float* initial_state, void* o, float* final_state,
+                   unsigned char* ws, hipStream_t st);
+
+// ---------------------------------------------------------------------------
+// The forward's workspace for callers that cannot allocate (gdn_chunk_fwd_noalloc): a fixed
+// device array, one copy per GPU, resolved once per device with that device current. In host
+// code the array's name stands for a host-side shadow, not a device address: only the address
+// hipGetSymbolAddress returns for the device is ever handed to a kernel.
+constexpr size_t kNoAllocScratchBytes = GDN_NOALLOC_SCRATCH_BYTES;
+
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+namespace {
+
+gdn_status noalloc_scratch(hipStream_t st, unsigned char** out) {
+    static std::mutex mu;
+    static unsigned char* per_dev[kMaxDevices] = {};
+    int dev = -1;
+    if (hipStreamGetDevice(st, &dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return GDN_ERR_HIP;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!per_dev[dev]) {
+        int cur = -1;
+        if (hipGetDevice(&cur) != hipSuccess) return GDN_ERR_HIP;
+        if (cur != dev && hipSetDevice(dev) != hipSuccess) return GDN_ERR_HIP;
+        void* ptr = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (cur != dev && hipSetDevice(cur) != hipSuccess) return GDN_ERR_HIP;
+        if (e != hipSuccess || !ptr || reinterpret_cast<uintptr_t>(ptr) % kAlign) return GDN_ERR_HIP;
+        per_dev[dev] = static_cast<unsigned char*>(ptr);
+    }
+    *out = per_dev[dev];
+    return GDN_OK;
+}
+
 }  // namespace
 }  // namespace gdn
 
@@ -474,8 +511,35 @@ gdn_status gdn_chunk_fwd(const gdn_desc* desc, const void* q, const void* k, con
     if (s != GDN_OK) return s;
     if (p.Ttot > 0 && (!q || !k || !v || !g || !beta || !o)) return GDN_ERR_INVALID_ARG;
     if ((s = check_ws(p, p.fwd_bytes, workspace, workspace_bytes)) != GDN_OK) return s;
+    return run_fwd(desc, p, q, k, v, g, beta, initial_state, o, final_state,
+                   static_cast<unsigned char*>(workspace), reinterpret_cast<hipStream_t>(stream));
+}
+
+gdn_status gdn_chunk_fwd_noalloc(const gdn_desc* desc, const void* q, const void* k, const void* v, const float* g,
+                                 const float* beta, const float* initial_state, void* o, float* final_state,
+                                 void* stream) {
+    Plan p;
+    gdn_status s = make_plan(desc, p);
+    if (s != GDN_OK) return s;
+    // kept intermediates would be overwritten by the next call on the same GPU
+    if (desc->flags & (GDN_FLAG_KEEP_FORWARD | GDN_FLAG_REUSE_FORWARD)) return GDN_ERR_INVALID_ARG;
+    if (p.Ttot > 0 && (!q || !k || !v || !g || !beta || !o)) return GDN_ERR_INVALID_ARG;
+    if (p.fwd_bytes > kNoAllocScratchBytes) return GDN_ERR_WORKSPACE;
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-    unsigned char* ws = static_cast<unsigned char*>(workspace);
+    unsigned char* ws = nullptr;
+    if ((s = noalloc_scratch(st, &ws)) != GDN_OK) return s;
+    return run_fwd(desc, p, q, k, v, g, beta, initial_state, o, final_state, ws, st);
+}
+
+}  // extern "C"
+
+namespace gdn {
+namespace {
+
+gdn_status run_fwd(const gdn_desc* desc, const Plan& p, const void* q, const void* k, const void* v,
+                   const float* g, const float* beta, const float* initial_state, void* o, float* final_state,
+                   unsigned char* ws, hipStream_t st) {
+    gdn_status s = GDN_OK;
     float* gam = reinterpret_cast<float*>(ws + p.o_gam);
     void* w = ws + p.o_w;
     void* u = ws + p.o_u;
@@ -532,6 +596,11 @@ gdn_status gdn_chunk_fwd(const gdn_desc* desc, const void* q, const void* k, con
                                             (int)(desc->V / recur_rows((int)desc->V, (int)desc->K)), st));
     return GDN_OK;
 }
+
+}  // namespace
+}  // namespace gdn
+
+extern "C" {
 
 gdn_status gdn_chunk_bwd_workspace_size(const gdn_desc* desc, size_t* bytes) {
     if (!bytes) return GDN_ERR_INVALID_ARG;

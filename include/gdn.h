@@ -42,7 +42,8 @@
  *
  * Ownership and errors: the caller allocates every buffer, including the
  * workspace, whose size the *_workspace_size calls return. The library
- * allocates no memory, keeps no pointer after a call returns, never
+ * allocates no memory (gdn_chunk_fwd_noalloc's fixed scratch array is part of
+ * the library's image, see there), keeps no pointer after a call returns, never
  * synchronises the host with the device and never aborts. All work is
  * enqueued on `stream` (a hipStream_t; NULL = the default stream). Outputs
  * are overwritten, never accumulated, and must not alias inputs. Argument
@@ -59,7 +60,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 6
+#define GDN_ABI_VERSION 7
 
 typedef enum gdn_status {
     GDN_OK = 0,
@@ -184,6 +185,26 @@ gdn_status gdn_chunk_fwd(const gdn_desc* desc, const void* q, const void* k, con
                          const float* g, const float* beta, const float* initial_state,
                          void* o, float* final_state,
                          void* workspace, size_t workspace_bytes, void* stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph capture, serving loops
+ * or harnesses that forbid hipMalloc): gdn_chunk_fwd with its workspace taken from a fixed
+ * array inside the library, GDN_NOALLOC_SCRATCH_BYTES per GPU, which each GPU the call runs
+ * on holds from the first call there until the process ends (that first call resolves the
+ * array's address: make it once before capturing a graph). Same arguments, layouts and
+ * results as gdn_chunk_fwd without the workspace; the caller still owns every input and
+ * output. It allocates nothing.
+ * Errors: a descriptor whose forward workspace (gdn_chunk_fwd_workspace_size) exceeds
+ * GDN_NOALLOC_SCRATCH_BYTES returns GDN_ERR_WORKSPACE, and GDN_FLAG_KEEP_FORWARD or
+ * GDN_FLAG_REUSE_FORWARD returns GDN_ERR_INVALID_ARG (kept intermediates would not outlive
+ * the next call), both before any launch; otherwise as gdn_chunk_fwd.
+ * Every call on one GPU shares that GPU's array, and the array keeps the last call's contents
+ * (nothing in it needs to start at zero: every kernel writes what it reads in the same call).
+ * Calls that overlap on one GPU (on different streams, or from several host threads) race on
+ * the array: the caller serialises them. */
+#define GDN_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+gdn_status gdn_chunk_fwd_noalloc(const gdn_desc* desc, const void* q, const void* k, const void* v,
+                                 const float* g, const float* beta, const float* initial_state,
+                                 void* o, float* final_state, void* stream);
 
 /* Workspace bytes that gdn_chunk_bwd needs for `desc`. */
 gdn_status gdn_chunk_bwd_workspace_size(const gdn_desc* desc, size_t* bytes);

@@ -183,6 +183,23 @@ int main() {
                                  (float*)fake(7), fake(6), nullptr) == GDN_OK);
         EXPECT(g_launches == l0 + 1);
         for (int s = 0; s < 8; ++s) EXPECT(gdn_status_string((gdn_status)s) != nullptr);
+        // the no-allocation forward refuses, before any launch or HIP call, a problem beyond its
+        // fixed array, kept intermediates and missing tensors
+        const int l1 = g_launches;
+        gdn_desc big = base(1, 262144, 16, 128, 128, 0);
+        EXPECT(gdn_chunk_fwd_noalloc(&big, fake(2), fake(3), fake(4), (const float*)fake(5), (const float*)fake(6),
+                                     nullptr, fake(7), nullptr, nullptr) == GDN_ERR_WORKSPACE);
+        gdn_desc keep = base(1, 1000, 2, 128, 128, 0);
+        keep.flags = GDN_FLAG_KEEP_FORWARD;
+        EXPECT(gdn_chunk_fwd_noalloc(&keep, fake(2), fake(3), fake(4), (const float*)fake(5), (const float*)fake(6),
+                                     nullptr, fake(7), nullptr, nullptr) == GDN_ERR_INVALID_ARG);
+        keep.flags = GDN_FLAG_REUSE_FORWARD;
+        EXPECT(gdn_chunk_fwd_noalloc(&keep, fake(2), fake(3), fake(4), (const float*)fake(5), (const float*)fake(6),
+                                     nullptr, fake(7), nullptr, nullptr) == GDN_ERR_INVALID_ARG);
+        keep.flags = 0;
+        EXPECT(gdn_chunk_fwd_noalloc(&keep, fake(2), nullptr, fake(4), (const float*)fake(5), (const float*)fake(6),
+                                     nullptr, fake(7), nullptr, nullptr) == GDN_ERR_INVALID_ARG);
+        EXPECT(g_launches == l1);
     }
     if (failures) {
         fprintf(stderr, "%d expectation(s) failed\n", failures);
