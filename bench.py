@@ -458,6 +458,20 @@ def main():
                 "frac": round(gbs / HBM_PEAK_GBS, 4), "frac_of_copy": round(gbs / copy["GB/s"], 4),
                 "mfma_frac": round(flops / (t_ms * 1e-3) / 1e12 / peak_mfma, 4)}
 
+    cp_stats = None
+    if plan["cp_on"]:
+        # the per-boundary CP decision of this workload: the share of sub-sequence boundaries that
+        # take the warmup (forward; reverse for the backward's adjoint pass) and the head summary
+        fw, rv = gdn.gdn_cp_windows(k, v, g, beta, cu_seqlens=cu, cu_seqlens_host=cu_host, cp_mode=cp)
+        modes = gdn.gdn_cp_modes(k, v, g, beta, cu_seqlens=cu, cu_seqlens_host=cu_host, cp_mode=cp).cpu()
+        fw, rv = fw.cpu(), rv.cpu()
+        nb = int((fw >= 0).sum())
+        cp_stats = {"boundaries": nb,
+                    "warmup_frac_fwd": round(float((fw > 0).sum()) / max(nb, 1), 4),
+                    "warmup_frac_rev": round(float((rv > 0).sum()) / max(nb, 1), 4),
+                    "mean_window_chunks": round(float(fw[fw > 0].float().mean()) if (fw > 0).any() else 0.0, 2),
+                    "sequence_heads": {"all_warmup": int((modes == 1).sum()), "mixed": int((modes == 3).sum()),
+                                       "all_exact": int((modes == 2).sum())}}
     line = {
         "metric": metric_name(w, B, T, H, lengths),
         "value": round(tokens / (ms * 1e-3), 1),
@@ -477,6 +491,7 @@ def main():
         "tflops": round(tflops, 2),
         "mfma_frac": round(tflops / peak_mfma, 4),
         "roofline": roofline,
+        "cp": cp_stats,
         # every call after a 1 GiB cache flush, HIP events around the call (median, minimum)
         "flushed": {"step": fl_step, "tokens_per_s_median": round(tokens / (fl_step["median_ms"] * 1e-3), 1)},
         "copy_ceiling": copy,

@@ -12,7 +12,8 @@ missing they raise instead of computing anything elsewhere.
   gdn_workspace(...)          one buffer that serves a forward that keeps its intermediates
                               and the backward that reuses them
   gdn_intra_chunk(...)        the intra-chunk kernel alone (gate cumsum, w, u)
-  gdn_cp_modes(...)           per sequence-head CP decision (0 none, 1 warmup, 2 exact)
+  gdn_cp_modes(...)           per sequence-head CP decision (0 none, 1 warmup, 2 exact, 3 mixed)
+  gdn_cp_windows(...)         per-boundary CP decision (warmup window, or 0 for exact)
   gdn_recurrent_fwd(...)      token-by-token form from a given state (decoding after a prefill)
   chunk_gated_delta_rule(...) autograd wrapper over gdn_chunk_fwd / gdn_chunk_bwd
 """
@@ -29,7 +30,7 @@ from ._abi import (CP_MODES, EXPORTS, GDN_DTYPE_BF16, GDN_DTYPE_FP32, GDN_FLAG_K
                    load_library, status_string)
 
 __all__ = ["gdn_plan", "gdn_chunk_fwd", "gdn_chunk_fwd_noalloc", "gdn_chunk_bwd", "gdn_workspace", "gdn_intra_chunk", "gdn_cp_modes",
-           "gdn_recurrent_fwd", "gdn_profile_enable", "gdn_profile_read", "chunk_gated_delta_rule", "load_library",
+           "gdn_cp_windows", "gdn_recurrent_fwd", "gdn_profile_enable", "gdn_profile_read", "chunk_gated_delta_rule", "load_library",
            "make_desc", "GdnError"]
 
 
@@ -307,7 +308,8 @@ def gdn_intra_chunk(k, v, g, beta, *, cu_seqlens=None, cu_seqlens_host=None, qk_
 
 def gdn_cp_modes(k, v, g, beta, *, cu_seqlens=None, cu_seqlens_host=None, cp_mode="auto",
                  warmup_chunks=0, seg_chunks=0, warmup_eps=0.0, warmup_max_chunks=0, qk_l2norm=False):
-    """Per sequence-head CP decision [N, H] int32: 0 no split, 1 warmup, 2 exact."""
+    """Per sequence-head CP decision [N, H] int32: 0 no split, 1 every boundary warmup, 2 every
+    boundary exact, 3 mixed."""
     N = _num_seqs(k, cu_seqlens)
     desc = make_desc(k, v, cu_seqlens=cu_seqlens, cu_seqlens_host=cu_seqlens_host, cp_mode=cp_mode,
                      warmup_chunks=warmup_chunks, seg_chunks=seg_chunks, warmup_eps=warmup_eps,
@@ -320,6 +322,26 @@ def gdn_cp_modes(k, v, g, beta, *, cu_seqlens=None, cu_seqlens_host=None, cp_mod
     check(lib.gdn_cp_modes(desc.ref, _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(modes), _ptr(ws),
                            ctypes.c_size_t(ws_bytes), _stream()), "gdn_cp_modes")
     return modes
+
+
+def gdn_cp_windows(k, v, g, beta, *, cu_seqlens=None, cu_seqlens_host=None, cp_mode="auto", warmup_chunks=0,
+                   seg_chunks=0, warmup_eps=0.0, warmup_max_chunks=0, qk_l2norm=False, reverse=True):
+    """Per-boundary CP decision: (fwd, rev) int32 [total_segments, H] device tensors, row gs for the
+    boundary at the start of sub-sequence gs: the warmup window in chunks, 0 = exact, -1 = no
+    boundary (a sequence's first sub-sequence). rev (the backward's adjoint pass) is None unless
+    reverse=True."""
+    desc = make_desc(k, v, cu_seqlens=cu_seqlens, cu_seqlens_host=cu_seqlens_host, cp_mode=cp_mode,
+                     warmup_chunks=warmup_chunks, seg_chunks=seg_chunks, warmup_eps=warmup_eps,
+                     warmup_max_chunks=warmup_max_chunks, qk_l2norm=qk_l2norm)
+    lib = load_library()
+    plan = gdn_plan(desc)
+    ws, ws_bytes = _workspace(plan["fwd_workspace_bytes"], k.device)
+    shape = (plan["total_segments"], k.shape[2])
+    fwd = torch.empty(shape, dtype=torch.int32, device=k.device)
+    rev = torch.empty(shape, dtype=torch.int32, device=k.device) if reverse else None
+    check(lib.gdn_cp_windows(desc.ref, _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(fwd), _ptr(rev), _ptr(ws),
+                             ctypes.c_size_t(ws_bytes), _stream()), "gdn_cp_windows")
+    return fwd, rev
 
 
 def gdn_recurrent_fwd(q, k, v, g, beta, state=None, *, scale=1.0, state_out=None, o=None, qk_l2norm=False):

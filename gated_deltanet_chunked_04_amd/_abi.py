@@ -16,13 +16,13 @@ GDN_OK, GDN_ERR_INVALID_ARG, GDN_ERR_UNSUPPORTED, GDN_ERR_WORKSPACE, GDN_ERR_HIP
 GDN_DTYPE_BF16, GDN_DTYPE_FP32 = 0, 1
 CP_MODES = {"auto": 0, "off": 1, "on": 2, "exact": 3, "warmup": 4, "pages": 5}
 GDN_FLAG_KEEP_FORWARD, GDN_FLAG_REUSE_FORWARD, GDN_FLAG_QK_L2NORM = 1, 2, 4
-GDN_ABI_VERSION = 7
+GDN_ABI_VERSION = 8
 GDN_NOALLOC_SCRATCH_BYTES = 128 << 20
 
 # Declared entry points of include/gdn.h (checked by the ABI test).
 EXPORTS = ("gdn_abi_version", "gdn_status_string", "gdn_plan", "gdn_chunk_fwd_workspace_size",
            "gdn_chunk_fwd", "gdn_chunk_fwd_noalloc", "gdn_chunk_bwd_workspace_size", "gdn_chunk_bwd", "gdn_intra_chunk",
-           "gdn_cp_modes", "gdn_recurrent_fwd", "gdn_profile_enable", "gdn_profile_read")
+           "gdn_cp_modes", "gdn_cp_windows", "gdn_recurrent_fwd", "gdn_profile_enable", "gdn_profile_read")
 
 
 class GdnDesc(ctypes.Structure):
@@ -93,6 +93,8 @@ def load_library(path: str = LIB_PATH):
     lib.gdn_intra_chunk.argtypes = [dp] + [vp] * 7 + [vp, sz, vp]
     lib.gdn_cp_modes.restype = i32
     lib.gdn_cp_modes.argtypes = [dp] + [vp] * 5 + [vp, sz, vp]
+    lib.gdn_cp_windows.restype = i32
+    lib.gdn_cp_windows.argtypes = [dp] + [vp] * 6 + [vp, sz, vp]
     lib.gdn_recurrent_fwd.restype = i32
     lib.gdn_recurrent_fwd.argtypes = [dp] + [vp] * 8 + [vp]
     lib.gdn_profile_enable.restype = i32

@@ -48,9 +48,9 @@ struct Plan {
     int32_t esize = 2;
     // forward workspace
     size_t o_kn = 0, o_gam = 0, o_w = 0, o_u = 0, o_cstat = 0, o_bos = 0, o_len = 0, o_choff = 0, o_segoff = 0,
-           o_ctab = 0, o_stab = 0, o_modes = 0, o_seginit = 0, o_prep = 0, fwd_bytes = 0;
+           o_ctab = 0, o_stab = 0, o_modes = 0, o_bwin = 0, o_seginit = 0, o_prep = 0, fwd_bytes = 0;
     // backward workspace: the forward's layout, then these
-    size_t o_modes_r = 0, o_seginit_r = 0, o_prep_r = 0, o_h = 0, o_gst = 0, o_tm = 0, o_dl = 0, o_ddl = 0,
+    size_t o_modes_r = 0, o_bwin_r = 0, o_seginit_r = 0, o_prep_r = 0, o_h = 0, o_gst = 0, o_tm = 0, o_dl = 0, o_ddl = 0,
            bwd_bytes = 0;
     int32_t cus = 256;   // compute units (desc->num_cus, else the device's)
     int32_t bwd_ok = 1;  // fp32 backward supports K = V = 64 only (LDS)
@@ -183,7 +183,8 @@ gdn_status make_plan(const gdn_desc* d, Plan& p) {
     p.o_w = take(T * H * K * p.esize);
     p.o_u = take(T * H * V * p.esize);
     p.o_cstat = take((size_t)p.total_chunks * H * 8);
-    p.o_modes = take((size_t)p.N * H * 8);  // CP modes [N,H], then warmup windows [N,H]
+    p.o_modes = take((size_t)p.N * H * 4);  // CP mode per sequence-head [N,H]
+    p.o_bwin = take((size_t)p.total_segs * H * 4);  // warmup window per boundary [total_segs,H]
     if (p.varlen) {
         p.o_bos = take((size_t)p.N * 8);
         p.o_len = take((size_t)p.N * 4);
@@ -205,7 +206,8 @@ gdn_status make_plan(const gdn_desc* d, Plan& p) {
     p.fwd_bytes = std::max<size_t>((d->flags & GDN_FLAG_KEEP_FORWARD) ? off : p.o_tm, kAlign);
     // backward workspace continues after the forward's
     if (p.cp_on) {
-        p.o_modes_r = take((size_t)p.N * H * 8);
+        p.o_modes_r = take((size_t)p.N * H * 4);
+        p.o_bwin_r = take((size_t)p.total_segs * H * 4);
         p.o_seginit_r = take((size_t)p.total_segs * H * V * K * 4);
         p.o_prep_r = take((size_t)p.total_segs * H * (V + K) * K * 4);
     }
@@ -394,20 +396,18 @@ gdn_status run_intra(const gdn_desc* d, const Plan& p, unsigned char* ws, const 
     return GDN_OK;
 }
 
-// Each modes array [N,H] of the workspace is followed by the warmup windows [N,H] of the
-// same decision.
-int32_t* windows_of(const Plan& p, int32_t* modes) { return modes ? modes + (size_t)p.N * p.H : nullptr; }
-
-gdn_status run_decide(const gdn_desc* d, const Plan& p, unsigned char* ws, int32_t* modes, int32_t* wins,
-                      hipStream_t st, int reverse = 0, int32_t* modes_r = nullptr) {
+// The CP decision: per sequence-head modes [N,H] and per boundary windows [total_segs,H] in one
+// direction, and optionally the other direction's (the backward's adjoint pass) in the same launch.
+gdn_status run_decide(const gdn_desc* d, const Plan& p, unsigned char* ws, int32_t* modes, int32_t* bwin,
+                      hipStream_t st, int reverse = 0, int32_t* modes_r = nullptr, int32_t* bwin_r = nullptr) {
     DecideArgs da{};
     da.reverse = reverse;
     da.modes_r = modes_r;
-    da.wins_r = windows_of(p, modes_r);
+    da.bwin_r = bwin_r;
     da.geo = make_geo(d, p, ws);
     da.cstat = reinterpret_cast<const float2*>(ws + p.o_cstat);
     da.modes = modes;
-    da.wins = wins;
+    da.bwin = bwin;
     da.warmup = p.W;
     da.warmup_max = p.Wmax;
     da.log_eps = logf(p.eps);
@@ -566,12 +566,13 @@ gdn_status run_fwd(const gdn_desc* desc, const Plan& p, const void* q, const voi
     ra.use_cp = p.cp_on;
     ra.q_l2 = kn != nullptr;
     int32_t* modes = reinterpret_cast<int32_t*>(ws + p.o_modes);
+    int32_t* bwin = reinterpret_cast<int32_t*>(ws + p.o_bwin);
     ra.modes = modes;
-    ra.wins = windows_of(p, modes);
+    ra.bwin = bwin;
     if (p.cp_on) {
         float* seginit = reinterpret_cast<float*>(ws + p.o_seginit);
         float* prep = reinterpret_cast<float*>(ws + p.o_prep);
-        if ((s = run_decide(desc, p, ws, modes, windows_of(p, modes), st)) != GDN_OK) return s;
+        if ((s = run_decide(desc, p, ws, modes, bwin, st)) != GDN_OK) return s;
         ra.seginit_out = seginit;
         ra.prep = prep;
         const int rt = recur_rows((int)desc->V, (int)desc->K);
@@ -644,10 +645,12 @@ gdn_status gdn_chunk_bwd(const gdn_desc* desc, const void* q, const void* k, con
     // both CP decisions (forward windows for the state pass, windows after each segment for
     // the adjoint pass) in one launch ahead of the fork
     int32_t* modes = reinterpret_cast<int32_t*>(ws + p.o_modes);
+    int32_t* bwin = reinterpret_cast<int32_t*>(ws + p.o_bwin);
     int32_t* modes_r = p.cp_on ? reinterpret_cast<int32_t*>(ws + p.o_modes_r) : nullptr;
+    int32_t* bwin_r = p.cp_on ? reinterpret_cast<int32_t*>(ws + p.o_bwin_r) : nullptr;
     if (p.cp_on) {
-        if (reuse) s = run_decide(desc, p, ws, modes_r, windows_of(p, modes_r), st, 1);
-        else s = run_decide(desc, p, ws, modes, windows_of(p, modes), st, 0, modes_r);
+        if (reuse) s = run_decide(desc, p, ws, modes_r, bwin_r, st, 1);
+        else s = run_decide(desc, p, ws, modes, bwin, st, 0, modes_r, bwin_r);
         if (s != GDN_OK) return s;
     }
     std::lock_guard<std::mutex> side_lock(side_mutex());
@@ -668,7 +671,7 @@ gdn_status gdn_chunk_bwd(const gdn_desc* desc, const void* q, const void* k, con
     ra.scale = desc->scale;
     ra.use_cp = p.cp_on;
     ra.modes = modes;
-    ra.wins = windows_of(p, modes);
+    ra.bwin = bwin;
     ra.hstates = ws + p.o_h;
     ra.delta = ws + p.o_dl;
     if (!reuse && p.cp_on) {
@@ -710,7 +713,7 @@ gdn_status gdn_chunk_bwd(const gdn_desc* desc, const void* q, const void* k, con
         float* seginit_r = reinterpret_cast<float*>(ws + p.o_seginit_r);
         float* prep_r = reinterpret_cast<float*>(ws + p.o_prep_r);
         va.modes = modes_r;
-        va.wins = windows_of(p, modes_r);
+        va.bwin = bwin_r;
         va.seginit_out = seginit_r;
         va.prep = prep_r;
         GDN_LAUNCH(kKBwdPrepass, st, launch_reverse(va, desc->dtype, kRecurPrepass, p.total_segs, vktiles, st));
@@ -828,7 +831,26 @@ gdn_status gdn_cp_modes(const gdn_desc* desc, const void* k, const void* v, cons
     if ((s = run_intra(desc, p, ws, k, v, g, beta, reinterpret_cast<float*>(ws + p.o_gam), ws + p.o_w,
                        ws + p.o_u, st, nullptr, kn_of(desc, p, ws))) != GDN_OK)
         return s;
-    return run_decide(desc, p, ws, modes_out, windows_of(p, reinterpret_cast<int32_t*>(ws + p.o_modes)), st);
+    return run_decide(desc, p, ws, modes_out, reinterpret_cast<int32_t*>(ws + p.o_bwin), st);
+}
+
+gdn_status gdn_cp_windows(const gdn_desc* desc, const void* k, const void* v, const float* g, const float* beta,
+                          int32_t* fwd_windows, int32_t* rev_windows, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+    Plan p;
+    gdn_status s = make_plan(desc, p);
+    if (s != GDN_OK) return s;
+    if (!fwd_windows || (p.Ttot > 0 && (!k || !v || !g || !beta))) return GDN_ERR_INVALID_ARG;
+    if ((s = check_ws(p, p.fwd_bytes, workspace, workspace_bytes)) != GDN_OK) return s;
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    unsigned char* ws = static_cast<unsigned char*>(workspace);
+    if ((s = run_intra(desc, p, ws, k, v, g, beta, reinterpret_cast<float*>(ws + p.o_gam), ws + p.o_w,
+                       ws + p.o_u, st, nullptr, kn_of(desc, p, ws))) != GDN_OK)
+        return s;
+    // the per sequence-head summaries of both directions land in the forward workspace's modes
+    // array (the reverse one last, from the same thread)
+    int32_t* modes = reinterpret_cast<int32_t*>(ws + p.o_modes);
+    return run_decide(desc, p, ws, modes, fwd_windows, st, 0, rev_windows ? modes : nullptr, rev_windows);
 }
 
 gdn_status gdn_profile_enable(int enable) {

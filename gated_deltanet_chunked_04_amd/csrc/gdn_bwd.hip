@@ -158,20 +158,35 @@ __global__ __launch_bounds__(RT * 4) void k_reverse(RevArgs a) {
     int mode = 0;
     const bool last = sg.s == sg.nseg - 1;
     if (MODE == kRecurPrepass) {
+        // As the forward's prepass, mirrored: heads whose boundaries all take the warmup (mode 1)
+        // warm the adjoint leaving this segment over the window after it, into seginit; heads with
+        // exact boundaries (mode 2, or 3 mixed) prepare the link from this segment to the one before
+        // as a map G -> G M + R~ into prep: the exact map of this segment, or, where the boundary
+        // at its start takes the warmup, M = 0 and R~ = the warm adjoint over the window after it.
         mode = a.modes[sg.n * H + h];
+        int win = 0;
         if (mode == 1) {
-            // warmup: the chunks of the window after this segment, from a zero adjoint (or from d(final
-            // state) when the window reaches the sequence end)
             if (last || vt * RT >= V) return;
-            cbeg = sg.c1;
-            cend = min(sg.c1 + a.wins[sg.n * H + h], sg.nchunks);
-            if (cend == sg.nchunks && a.dsT)
+            win = a.bwin[(gs + 1) * H + h];  // the boundary at the start of the next segment
+        } else if (mode == 2 || mode == 3) {
+            if (sg.s == 0 || vt * RT >= V + K) return;
+            win = mode == 3 ? a.bwin[gs * H + h] : 0;
+        } else {
+            return;
+        }
+        if (win > 0) {
+            // the window starts where the boundary's segment starts; from a zero adjoint, or from
+            // d(final state) when it reaches the sequence end
+            const int cb = mode == 1 ? sg.c1 : sg.c0;
+            cbeg = cb;
+            cend = min(cb + win, sg.nchunks);
+            if (vt * RT >= V) cend = cbeg;  // the M rows of a warm link (whole tiles): M = 0
+            if (vt * RT < V && cend == sg.nchunks && a.dsT)
                 load_state<K>(accG, a.dsT + ((size_t)sg.n * H + h) * VK, row);
             else
 #pragma unroll
                 for (int kt = 0; kt < K / 16; ++kt) accG[kt] = zero4();
-        } else if (mode == 2) {
-            if (sg.s == 0 || vt * RT >= V + K) return;
+        } else {
 #pragma unroll
             for (int kt = 0; kt < K / 16; ++kt) {
                 f32x4 z = zero4();
@@ -181,8 +196,6 @@ __global__ __launch_bounds__(RT * 4) void k_reverse(RevArgs a) {
                 }
                 accG[kt] = z;
             }
-        } else {
-            return;
         }
     } else {
         if (!last && a.use_cp) {

@@ -165,8 +165,9 @@ struct RecurArgs {
     float* seginit_out;       // prepass: warmup states written here
     float* prep;              // prepass: exact maps per [total_segs,H]: R rows [V][K] fp32, then M^T
                               // [K][K] in the input precision, in a (V+K) x K fp32 slot
-    const int32_t* modes;     // [N,H] 0 none, 1 warmup, 2 exact
-    const int32_t* wins;      // [N,H] warmup window in chunks of the sequence-heads in mode 1
+    const int32_t* modes;     // [N,H] 0 no split, 1 every boundary warmup, 2 every one exact, 3 mixed
+    const int32_t* bwin;      // [total_segs,H] per boundary (the start of segment gs, s >= 1): the
+                              // warmup window in chunks, 0 = exact, -1 = no boundary (s = 0)
     void* hstates;            // kRecurStates, kRecurOutRec: [total_chunks,H,V,K] entry state of every chunk
     void* delta;              // same modes: [Ttot,H,V] Delta = U - W S^T of every chunk, or null
     float scale;
@@ -177,15 +178,15 @@ struct RecurArgs {
 struct DecideArgs {
     Geo geo;
     const float2* cstat;
-    int32_t* modes;
-    int32_t* wins;     // [N,H] warmup window taken (chunks), beside modes
+    int32_t* modes;    // [N,H] per sequence-head summary (see RecurArgs)
+    int32_t* bwin;     // [total_segs,H] per boundary window (see RecurArgs)
     int32_t warmup;    // shortest window W
     int32_t warmup_max;  // longest window (W .. W + 63)
     float log_eps;
     int32_t forced;  // 0 gate test, 1 warmup, 2 exact
     int32_t reverse; // 1: windows after each segment end (backward adjoint pass)
     int32_t* modes_r;  // optional second output: the reverse decision, from the same launch
-    int32_t* wins_r;
+    int32_t* bwin_r;
 };
 
 struct ScanArgs {
@@ -210,7 +211,8 @@ struct RevArgs {
     float* seginit_out;       // prepass: warmup adjoints written here
     float* prep;              // prepass: reverse maps, laid out as the forward's
     const int32_t* modes;
-    const int32_t* wins;      // [N,H] warmup window in chunks of the sequence-heads in mode 1
+    const int32_t* bwin;      // [total_segs,H] per boundary (the start of segment gs): the window after
+                              // it in chunks, 0 = exact, -1 = no boundary
     void* gstates;            // [total_chunks,H,V,K] adjoint of the state leaving every chunk
     void* ddelta;             // kRecurOut: [Ttot,H,V] dL/dDelta of every chunk, or null
     float scale;

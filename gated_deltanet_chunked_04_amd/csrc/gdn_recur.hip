@@ -388,18 +388,35 @@ __global__ __launch_bounds__(RT * 4) void k_recur(RecurArgs a) {
     int cbeg = sg.c0, cend = sg.c1;
     int mode = 0;
     if (MODE == kRecurPrepass) {
+        // Heads whose boundaries all take the warmup (mode 1): this workgroup warms the state
+        // entering its segment over the window before it, into seginit. Heads with exact
+        // boundaries (mode 2, or 3 when mixed with warmup ones): this workgroup prepares the link
+        // to the next segment as a map S -> S M + R~ into prep, the exact map of its segment, or,
+        // where that boundary takes the warmup, M = 0 and R~ = the warm state, so that the
+        // scan's S M + R~ restarts from it.
         mode = a.modes[sg.n * H + h];
+        int win = 0;  // warmup window of the boundary this workgroup prepares (0: exact map)
         if (mode == 1) {
             if (sg.s == 0 || vt * RT >= V) return;
-            cend = sg.c0;
-            cbeg = max(0, sg.c0 - a.wins[sg.n * H + h]);
-            if (cbeg == 0 && a.s0)
+            win = a.bwin[gs * H + h];
+        } else if (mode == 2 || mode == 3) {
+            if (sg.s == sg.nseg - 1 || vt * RT >= V + K) return;
+            win = mode == 3 ? a.bwin[(gs + 1) * H + h] : 0;
+        } else {
+            return;
+        }
+        if (win > 0) {
+            // the window ends where the boundary's segment starts
+            const int cb = mode == 1 ? sg.c0 : sg.c1;
+            cend = cb;
+            cbeg = max(0, cb - win);
+            if (vt * RT >= V) cbeg = cend;  // the M rows of a warm link (whole tiles): M = 0
+            if (vt * RT < V && cbeg == 0 && a.s0)
                 load_state<K>(accS, a.s0 + ((size_t)sg.n * H + h) * VK, row);
             else
 #pragma unroll
                 for (int kt = 0; kt < K / 16; ++kt) accS[kt] = zero4();
-        } else if (mode == 2) {
-            if (sg.s == sg.nseg - 1 || vt * RT >= V + K) return;
+        } else {
 #pragma unroll
             for (int kt = 0; kt < K / 16; ++kt) {
                 f32x4 z = zero4();
@@ -409,8 +426,6 @@ __global__ __launch_bounds__(RT * 4) void k_recur(RecurArgs a) {
                 }
                 accS[kt] = z;
             }
-        } else {
-            return;
         }
     } else {
         if (sg.s > 0 && a.use_cp) {
@@ -585,14 +600,15 @@ hipError_t launch_recur_t(const RecurArgs& a, int64_t nsegs_grid, int vtiles, hi
 }
 
 // ---------------------------------------------------------------------------
-// CP decision: one wave per sequence-head. Warmup over a window of w chunks is accepted
-// when, for every segment boundary whose window does not reach the sequence start, the
-// gate sum over the w chunks before it is <= log(eps) and beta |k|^2 <= 2 on those chunks
-// (then every token map exp(g)(I - beta k k^T) has spectral norm <= exp(g), so a wrong
-// state at the window start is damped by at least exp(window gate sum)). The window is the
-// shortest w in [W, Wmax] accepted at every boundary; with none, the exact correction.
-// Each lane walks the chunks before its boundaries once and sets bit w - W of a mask for
-// every accepted w; the wave ANDs the masks.
+// CP decision: one wave per sequence-head, one decision per boundary (the start of every
+// segment but the first). Warmup over a window of w chunks is accepted at a boundary when the
+// window reaches the sequence start (then it runs from the known state: exact), or when the
+// gate sum over its w chunks is <= log(eps) and beta |k|^2 <= 2 on them (then every token map
+// exp(g)(I - beta k k^T) has spectral norm <= exp(g), so a wrong state at the window start is
+// damped by at least exp(window gate sum)). Each boundary takes the shortest w in [W, Wmax]
+// that is accepted there, or the exact correction when none is. Each lane walks the chunks
+// before (reverse: after) its boundaries once and sets bit w - W of a mask for every accepted
+// w. The sequence-head's mode summarises its boundaries: 1 all warmup, 2 all exact, 3 mixed.
 __global__ __launch_bounds__(kThreads) void k_decide(DecideArgs a) {
     const int wave = wave_id(), lane = threadIdx.x & 63;
     const int64_t p = (int64_t)blockIdx.x * 4 + wave;
@@ -607,16 +623,19 @@ __global__ __launch_bounds__(kThreads) void k_decide(DecideArgs a) {
     // a.modes gets the decision for a.reverse's direction; a.modes_r, if given, the reverse one
     for (int dir = 0; dir < 2; ++dir) {
         int32_t* out = dir == 0 ? a.modes : a.modes_r;
-        int32_t* wout = dir == 0 ? a.wins : a.wins_r;
+        int32_t* wout = dir == 0 ? a.bwin : a.bwin_r;
         if (!out) continue;
         const bool rev = dir == 0 ? a.reverse != 0 : true;
-        int mode, win = W;
+        int32_t* bw = wout + segoff * H + h;  // this sequence-head's boundaries, stride H
+        if (lane == 0) bw[0] = -1;  // segment 0 has no boundary
+        int mode;
         if (nseg <= 1) {
             mode = 0;
         } else if (a.forced) {
             mode = a.forced;
+            for (int s = 1 + lane; s < nseg; s += 64) bw[(int64_t)s * H] = a.forced == 1 ? W : 0;
         } else {
-            uint64_t pass = all;
+            bool any_warm = false, any_exact = false;
             for (int s = 1 + lane; s < nseg; s += 64) {
                 const int cb = s * a.geo.seg_len;  // first chunk of segment s
                 // forward: the chunks before segment s; reverse: the chunks from segment s on
@@ -654,32 +673,22 @@ __global__ __launch_bounds__(kThreads) void k_decide(DecideArgs a) {
                     }
                     if (w0 + 32 >= avail) break;
                 }
-                pass &= m;
+                m &= all;
+                bw[(int64_t)s * H] = m ? W + __builtin_ctzll(m) : 0;
+                any_warm |= m != 0;
+                any_exact |= m == 0;
             }
-            // AND over the wave
-            uint32_t lo = (uint32_t)pass, hi = (uint32_t)(pass >> 32);
-#pragma unroll
-            for (int off = 32; off >= 1; off >>= 1) {
-                lo &= (uint32_t)__shfl_xor((int)lo, off);
-                hi &= (uint32_t)__shfl_xor((int)hi, off);
-            }
-            pass = ((uint64_t)hi << 32) | lo;
-            if (pass) {
-                mode = 1;
-                win = W + __builtin_ctzll(pass);
-            } else {
-                mode = 2;
-            }
+            // over the wave
+            const bool warm = __any(any_warm), exact = __any(any_exact);
+            mode = exact ? (warm ? 3 : 2) : 1;
         }
-        if (lane == 0) {
-            out[p] = mode;
-            if (wout) wout[p] = win;
-        }
+        if (lane == 0) out[p] = mode;
     }
 }
 
 // ---------------------------------------------------------------------------
-// Exact CP: S_{s+1} = S_s M_s + R~_s across segments, for sequence-heads in mode 2.
+// Exact CP: S_{s+1} = S_s M_s + R~_s across segments, for sequence-heads with an exact
+// boundary (modes 2 and 3; a warm link of a mixed head carries M = 0 and R~ = its warm state).
 // Grid (N, H, V/16): a workgroup carries 16 state rows through the segments of one
 // sequence-head. A link is bound by the vector-memory throughput of its CU (every
 // workgroup reads the whole M^T), so the rows are spread thin over many CUs: at 16 rows a
@@ -718,7 +727,8 @@ __global__ __launch_bounds__(256) void k_scan(ScanArgs a) {
     T* sS = reinterpret_cast<T*>(smem);
     const int n = blockIdx.x, h = blockIdx.y, vt = blockIdx.z;
     const int H = a.geo.H, V = a.geo.V;
-    if (a.modes[(int64_t)n * H + h] != 2) return;
+    const int mode = a.modes[(int64_t)n * H + h];
+    if (mode != 2 && mode != 3) return;  // heads with an exact boundary (warm links carry M = 0)
     int32_t nseg, nchunks;
     int64_t segoff, choff;
     seq_segs(a.geo, n, nseg, segoff, nchunks, choff);

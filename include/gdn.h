@@ -36,8 +36,8 @@
  * batch x heads ("AutoCP"; the pages' thresholds, B*H <= 40 or B*H <= 56 with
  * seq_len >= 8192, were tuned for a 132-SM part: here the default turns CP on when
  * the recurrence would otherwise leave compute units idle, GDN_CP_PAGES keeps the
- * pages' rule) and picks per sequence-head either the exact correction or a sliding-window
- * warmup of a few chunks where the gate decay makes the warmup exact within
+ * pages' rule) and picks per sub-sequence boundary either the exact correction or a
+ * sliding-window warmup of a few chunks where the gate decay makes the warmup exact within
  * tolerance ("gate-driven" warmup, "core advantages").
  *
  * Ownership and errors: the caller allocates every buffer, including the
@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 7
+#define GDN_ABI_VERSION 8
 
 typedef enum gdn_status {
     GDN_OK = 0,
@@ -259,14 +259,28 @@ gdn_status gdn_intra_chunk(const gdn_desc* desc, const void* k, const void* v,
                            float* gam_out, void* w_out, void* u_out,
                            void* workspace, size_t workspace_bytes, void* stream);
 
-/* CP decision per sequence-head, as the forward would take it:
- * modes_out [N, H] int32 (device): 0 = no split needed, 1 = warmup (over the shortest
- * window from warmup_chunks to warmup_max_chunks that meets the acceptance bound at every
- * sub-sequence start), 2 = exact.
+/* CP decision per sequence-head, as the forward would take it. The decision is made per
+ * boundary (the start of every sub-sequence but a sequence's first): the warmup over the
+ * shortest window from warmup_chunks to warmup_max_chunks chunks that meets the acceptance
+ * bound there, else the exact correction ("gate-driven" warmup, ollai.cn article, "core
+ * advantages"); the exact maps and the scan then run only across the exact boundaries.
+ * modes_out [N, H] int32 (device): 0 = no split needed, 1 = every boundary takes the warmup,
+ * 2 = every boundary takes the exact correction, 3 = both kinds (mixed).
  * Uses the forward workspace; runs the intra-chunk kernel to get the gates. */
 gdn_status gdn_cp_modes(const gdn_desc* desc, const void* k, const void* v,
                         const float* g, const float* beta, int32_t* modes_out,
                         void* workspace, size_t workspace_bytes, void* stream);
+
+/* The per-boundary CP decision itself (see gdn_cp_modes): fwd_windows [S, H] int32 (device),
+ * S = gdn_plan_info.total_segments, row gs for the boundary at the start of global sub-sequence
+ * gs (a sequence's sub-sequences are consecutive): the warmup window in chunks before it, 0 =
+ * exact correction, -1 = no boundary (a sequence's first sub-sequence). rev_windows, if not
+ * NULL, the same for the backward's adjoint pass (windows after each boundary). Uses the
+ * forward workspace; runs the intra-chunk kernel to get the gates. */
+gdn_status gdn_cp_windows(const gdn_desc* desc, const void* k, const void* v,
+                          const float* g, const float* beta, int32_t* fwd_windows,
+                          int32_t* rev_windows, void* workspace, size_t workspace_bytes,
+                          void* stream);
 
 /* Per-kernel timing, for measurement tools (off by default). While enabled, each kernel
  * launch of the calls above is bracketed by two HIP events recorded on the call's stream

@@ -97,3 +97,20 @@ def seq_slices(cu):
     """(n, start, end) of every non-empty sequence of a cu_seqlens tensor."""
     c = [int(x) for x in cu]
     return [(n, c[n], c[n + 1]) for n in range(len(c) - 1) if c[n + 1] > c[n]]
+
+
+def mixed_decay_inputs(T=8192, K=128, V=128, dtype=torch.bfloat16, seed=6):
+    """Two heads: head 0 with the workloads' gates (fast decay, about -5 per 64-token chunk)
+    everywhere; head 1 with a slow constant decay of -0.3 per chunk over the first half of the
+    sequence and the workloads' gates over the second half. With 16-chunk sub-sequences, the
+    boundaries of head 1 whose window lies in the slow half need the exact correction, the
+    others take the warmup: a mixed head."""
+    inp = small_inputs(B=1, T=T, H=2, K=K, V=V, dtype=dtype, seed=seed)
+    inp["g"][:, : T // 2, 1] = -0.3 / 64
+    return inp
+
+
+# per-boundary windows of mixed_decay_inputs at T = 8192, 16-chunk sub-sequences, W = 8, windows
+# up to 16 chunks: row s is the boundary at chunk 16 s (-1: none; 0: exact)
+MIXED_FWD_HEAD1 = [-1, 16, 0, 0, 0, 8, 8, 8]   # the window before chunk 16 reaches the start
+MIXED_REV_HEAD1 = [-1, 0, 0, 0, 8, 8, 8, 8]

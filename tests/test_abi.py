@@ -38,7 +38,7 @@ def test_exports_every_declared_symbol(lib):
     assert set(declared) == set(_abi.EXPORTS)
     for name in declared:
         assert hasattr(lib, name), name
-    assert lib.gdn_abi_version() == _abi.GDN_ABI_VERSION == 7
+    assert lib.gdn_abi_version() == _abi.GDN_ABI_VERSION == 8
 
 
 def test_status_strings(lib):

@@ -8,8 +8,9 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_helpers import (BF16_TOL, check, gpu_fwd, mid_decay_inputs, oracle, raw_key_inputs, rel_l2,  # noqa: F401
-                         seq_slices, small_inputs, to_dev, tol_for)
+from gpu_helpers import (BF16_TOL, MIXED_FWD_HEAD1, MIXED_REV_HEAD1, check, gpu_fwd, mid_decay_inputs,  # noqa: F401
+                         mixed_decay_inputs, oracle, raw_key_inputs, rel_l2, seq_slices, small_inputs, to_dev,
+                         tol_for)
 from oracle.chunked import chunked_fwd
 
 pytestmark = pytest.mark.gpu
@@ -117,7 +118,9 @@ def test_cp_modes_decision(gpu_lib):
     d = to_dev(inp)
     modes = gpu_lib.gdn_cp_modes(d["k"], d["v"], d["g"], d["beta"], cp_mode="on", seg_chunks=32)
     torch.cuda.synchronize()
-    assert modes.cpu().tolist() == [[1, 1, 2, 2]]
+    # heads 2, 3: exact at every boundary but the first, whose 32-chunk window reaches the
+    # sequence start (it runs from the known state there): mixed
+    assert modes.cpu().tolist() == [[1, 1, 3, 3]]
     o_ref, s_ref = oracle(inp)
     o, sT = gpu_fwd(d, cp_mode="on", seg_chunks=32)
     check(o, o_ref, 1e-2)
@@ -161,7 +164,9 @@ def test_autocp_fills_idle_units(gpu_lib):
     assert gdn.gdn_plan(gdn.make_desc(d["q"], d["v"]))["cp_on"] == 1
     assert gdn.gdn_plan(gdn.make_desc(d["q"], d["v"], cp_mode="pages"))["cp_on"] == 0
     modes = gdn.gdn_cp_modes(d["k"], d["v"], d["g"], d["beta"]).cpu()
-    assert set(modes.flatten().tolist()) == {1, 2}, modes
+    # head 5's first boundary (chunk 16) takes a window that reaches the sequence start, its
+    # second the exact correction: mixed; every other head takes the warmup everywhere
+    assert modes[:, 5].tolist() == [3, 3] and set(modes.flatten().tolist()) == {1, 3}, modes
     o, sT = gpu_fwd(d)
     heads = [0, 5, 23]
     o_ref, s_ref = oracle(inp, heads=heads)
@@ -183,8 +188,14 @@ def test_raw_keys_take_the_exact_correction(gpu_lib, dtype, K, V):
     bk = inp["beta"] * inp["k"].float().pow(2).sum(-1)
     assert float((bk > 2).float().mean()) > 0.2
     d = to_dev(inp)
-    modes = gpu_lib.gdn_cp_modes(d["k"], d["v"], d["g"], d["beta"], **kw).cpu()
-    assert (modes == 2).all(), modes
+    # 16 chunks in sub-sequences of 4: boundaries at chunks 4, 8, 12; windows of 2..4 chunks. Only
+    # the first boundary's 4-chunk window reaches the sequence start (runs from the known state),
+    # and only the last one's reaches its end in the reverse direction: every other boundary
+    # must take the exact correction.
+    fwd, rev = gpu_lib.gdn_cp_windows(d["k"], d["v"], d["g"], d["beta"], **kw)
+    for b in range(2):
+        assert fwd.cpu()[4 * b:4 * b + 4].T.tolist() == [[-1, 4, 0, 0]] * 2, fwd
+        assert rev.cpu()[4 * b:4 * b + 4].T.tolist() == [[-1, 0, 0, 4]] * 2, rev
     unit = to_dev(small_inputs(K=K, V=V, dtype=dtype, seed=21))  # same seed: same gates and beta
     assert torch.equal(unit["g"], d["g"]) and torch.equal(unit["beta"], d["beta"])
     m1 = gpu_lib.gdn_cp_modes(unit["k"], unit["v"], unit["g"], unit["beta"], **kw).cpu()
@@ -238,3 +249,33 @@ def test_binding_rejects_bad_buffers(gpu_lib):
     with pytest.raises(ValueError, match="^o"):
         gdn.gdn_recurrent_fwd(d["q"][:, :3], d["k"][:, :3], d["v"][:, :3], d["g"][:, :3].contiguous(),
                               d["beta"][:, :3].contiguous(), d["initial_state"], o=torch.empty((B, 3, H, K)))
+
+
+@pytest.mark.parametrize("dtype,K,V", [(torch.float32, 64, 64), (torch.bfloat16, 128, 128)])
+def test_cp_mixed_boundaries(gpu_lib, dtype, K, V):
+    """Per-boundary warmup/exact mixing: a head whose gates decay slowly over the first half of
+    the sequence and fast over the second takes the exact correction at the boundaries whose
+    window lies in the slow half and the warmup elsewhere (both directions); the forward
+    matches the oracle with the exact maps and the scan running across the exact boundaries
+    only."""
+    gdn = gpu_lib
+    inp = mixed_decay_inputs(K=K, V=V, dtype=dtype)
+    d = to_dev(inp)
+    kw = dict(cp_mode="on", seg_chunks=16)
+    fwd, rev = gdn.gdn_cp_windows(d["k"], d["v"], d["g"], d["beta"], **kw)
+    fwd, rev = fwd.cpu(), rev.cpu()
+    assert fwd[:, 1].tolist() == MIXED_FWD_HEAD1, fwd[:, 1]
+    assert rev[:, 1].tolist() == MIXED_REV_HEAD1, rev[:, 1]
+    assert fwd[0, 0] == -1 and (fwd[1:, 0] == 8).all() and rev[0, 0] == -1 and (rev[1:, 0] == 8).all()
+    modes = gdn.gdn_cp_modes(d["k"], d["v"], d["g"], d["beta"], **kw).cpu()
+    assert modes.tolist() == [[1, 3]], modes
+    o_ref, s_ref = oracle(inp)
+    o, sT = gpu_fwd(d, **kw)
+    tol = tol_for(dtype)
+    e_o = check(o, o_ref, tol, "o")
+    e_s = check(sT, s_ref, tol, "final_state")
+    # the mixed head alone, and against every boundary exact
+    check(o[:, :, 1], o_ref[:, :, 1], tol, "o of the mixed head")
+    o2, s2 = gpu_fwd(d, cp_mode="exact", seg_chunks=16)
+    check(o, o2.double().cpu(), tol, "o vs all exact")
+    print(f"mixed {dtype} rel_l2 o={e_o:.2e} final={e_s:.2e}", flush=True)

@@ -238,9 +238,9 @@ def test_l2norm_backward_edge_prefill_32k(gpu_lib):
         inp[n] = (x * (0.25 + 3.75 * torch.rand(x.shape[:-1] + (1,), generator=gen))).to(torch.bfloat16)
     d = to_dev(inp)
     modes = gdn.gdn_cp_modes(d["k"], d["v"], d["g"], d["beta"], qk_l2norm=True).cpu()
-    assert set(modes.flatten().tolist()) == {1, 2}, modes
+    assert (modes == 1).any() and (modes >= 2).any(), modes
     out = bwd(gdn, d)
-    heads = [int((modes[0] == 1).nonzero()[0]), int((modes[0] == 2).nonzero()[0])]
+    heads = [int((modes[0] == 1).nonzero()[0]), int((modes[0] >= 2).nonzero()[0])]
     x = {n: inp[n][:, :, heads] for n in ("q", "k", "v", "g", "beta", "d_o")}
     ref = ref_bwd_l2(x["q"], x["k"], x["v"], x["g"], x["beta"], x["d_o"], 1.0, inp["initial_state"][:, heads],
                      inp["d_final_state"][:, heads])
