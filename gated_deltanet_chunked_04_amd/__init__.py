@@ -25,8 +25,8 @@ from typing import Optional
 import numpy as np
 import torch
 
-from ._abi import (CP_MODES, EXPORTS, GDN_DTYPE_BF16, GDN_DTYPE_FP32, GDN_FLAG_KEEP_FORWARD,  # noqa: F401
-                   GDN_FLAG_QK_L2NORM, GDN_NOALLOC_SCRATCH_BYTES, GDN_FLAG_REUSE_FORWARD, GdnDesc, GdnError, GdnKernelTime, GdnPlanInfo, check,
+from ._abi import (CP_MODES, EXPORTS, GDN_DTYPE_BF16, GDN_DTYPE_FP32, GDN_FLAG_BWD_ADJOINT_PASS,  # noqa: F401
+                   GDN_FLAG_KEEP_FORWARD, GDN_FLAG_QK_L2NORM, GDN_NOALLOC_SCRATCH_BYTES, GDN_FLAG_REUSE_FORWARD, GdnDesc, GdnError, GdnKernelTime, GdnPlanInfo, check,
                    load_library, status_string)
 
 __all__ = ["gdn_plan", "gdn_chunk_fwd", "gdn_chunk_fwd_noalloc", "gdn_chunk_bwd", "gdn_workspace", "gdn_intra_chunk", "gdn_cp_modes",
@@ -242,7 +242,7 @@ def gdn_chunk_fwd_noalloc(q, k, v, g, beta, initial_state=None, *, scale=1.0, cu
 def gdn_chunk_bwd(q, k, v, g, beta, d_o, initial_state=None, d_final_state=None, *, scale=1.0,
                   cu_seqlens=None, cu_seqlens_host=None, cp_mode="auto", warmup_chunks=0, seg_chunks=0,
                   warmup_eps=0.0, warmup_max_chunks=0, workspace=None, need_d_initial_state=True, out=None,
-                  reuse_forward=False, qk_l2norm=False):
+                  reuse_forward=False, qk_l2norm=False, adjoint_pass=False):
     """Backward. Returns dict(dq, dk, dv, dg, dbeta, d_initial_state); `out` may hold them preallocated.
 
     qk_l2norm=True: the forward normalised q and k (see gdn_chunk_fwd); dq and dk are with respect
@@ -250,6 +250,9 @@ def gdn_chunk_bwd(q, k, v, g, beta, d_o, initial_state=None, d_final_state=None,
 
     reuse_forward=True takes the forward's intermediates from `workspace`, which must be the buffer a
     gdn_chunk_fwd(keep_for_backward=True) call on the same inputs and options wrote, untouched since.
+
+    adjoint_pass=True runs the reverse adjoint recurrence as a separate pass (GDN_FLAG_BWD_ADJOINT_PASS)
+    where the per-chunk kernel would otherwise carry the adjoint itself (for comparison).
     """
     N = _num_seqs(q, cu_seqlens)
     _check_inputs(q, k, v, g, beta, initial_state, N)
@@ -264,7 +267,8 @@ def gdn_chunk_bwd(q, k, v, g, beta, d_o, initial_state=None, d_final_state=None,
     desc = make_desc(q, v, scale=scale, cu_seqlens=cu_seqlens, cu_seqlens_host=cu_seqlens_host,
                      cp_mode=cp_mode, warmup_chunks=warmup_chunks, seg_chunks=seg_chunks,
                      warmup_eps=warmup_eps, warmup_max_chunks=warmup_max_chunks, qk_l2norm=qk_l2norm,
-                     flags=GDN_FLAG_REUSE_FORWARD if reuse_forward else 0)
+                     flags=(GDN_FLAG_REUSE_FORWARD if reuse_forward else 0)
+                     | (GDN_FLAG_BWD_ADJOINT_PASS if adjoint_pass else 0))
     lib = load_library()
     nbytes = ctypes.c_size_t()
     check(lib.gdn_chunk_bwd_workspace_size(desc.ref, ctypes.byref(nbytes)), "gdn_chunk_bwd_workspace_size")

@@ -15,7 +15,7 @@ LIB_PATH = os.path.join(HERE, "libgdn.so")
 GDN_OK, GDN_ERR_INVALID_ARG, GDN_ERR_UNSUPPORTED, GDN_ERR_WORKSPACE, GDN_ERR_HIP = range(5)
 GDN_DTYPE_BF16, GDN_DTYPE_FP32 = 0, 1
 CP_MODES = {"auto": 0, "off": 1, "on": 2, "exact": 3, "warmup": 4, "pages": 5}
-GDN_FLAG_KEEP_FORWARD, GDN_FLAG_REUSE_FORWARD, GDN_FLAG_QK_L2NORM = 1, 2, 4
+GDN_FLAG_KEEP_FORWARD, GDN_FLAG_REUSE_FORWARD, GDN_FLAG_QK_L2NORM, GDN_FLAG_BWD_ADJOINT_PASS = 1, 2, 4, 8
 GDN_ABI_VERSION = 8
 GDN_NOALLOC_SCRATCH_BYTES = 128 << 20
 

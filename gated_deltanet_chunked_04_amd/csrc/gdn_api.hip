@@ -68,7 +68,7 @@ gdn_status make_plan(const gdn_desc* d, Plan& p) {
     if (!d) return GDN_ERR_INVALID_ARG;
     for (int i = 0; i < 5; ++i)
         if (d->reserved[i] != 0) return GDN_ERR_INVALID_ARG;
-    if (d->flags & ~(GDN_FLAG_KEEP_FORWARD | GDN_FLAG_REUSE_FORWARD | GDN_FLAG_QK_L2NORM))
+    if (d->flags & ~(GDN_FLAG_KEEP_FORWARD | GDN_FLAG_REUSE_FORWARD | GDN_FLAG_QK_L2NORM | GDN_FLAG_BWD_ADJOINT_PASS))
         return GDN_ERR_INVALID_ARG;
     if (d->B < 1 || d->T < 0 || d->H < 1 || d->K < 1 || d->V < 1) return GDN_ERR_INVALID_ARG;
     if (!(d->chunk == 0 || d->chunk == 64)) return GDN_ERR_UNSUPPORTED;
@@ -653,12 +653,22 @@ gdn_status gdn_chunk_bwd(const gdn_desc* desc, const void* q, const void* k, con
         else s = run_decide(desc, p, ws, modes, bwin, st, 0, modes_r, bwin_r);
         if (s != GDN_OK) return s;
     }
-    std::lock_guard<std::mutex> side_lock(side_mutex());
+    // The per-chunk kernel carries the adjoint itself (one workgroup per sub-sequence and head,
+    // walking its chunks in reverse) where the sub-sequences are balanced: with CP, or uniform
+    // batches; then no adjoint pass runs and only the reverse CP (if any) goes to the side stream.
+    const bool carry = desc->V == 128 && desc->dtype == GDN_DTYPE_BF16 && (p.cp_on || !p.varlen) &&
+                       !(desc->flags & GDN_FLAG_BWD_ADJOINT_PASS) && p.total_segs * desc->H <= INT32_MAX;
+    const bool fork = p.cp_on || !carry;
+    std::unique_lock<std::mutex> side_lock(side_mutex(), std::defer_lock);
     SideStream side;
-    if ((s = side_stream(st, side)) != GDN_OK) return s;
-    hipStream_t st2 = side.s;
-    if (hipEventRecord(side.fork, st) != hipSuccess || hipStreamWaitEvent(st2, side.fork, 0) != hipSuccess)
-        return GDN_ERR_HIP;
+    hipStream_t st2 = st;
+    if (fork) {
+        side_lock.lock();
+        if ((s = side_stream(st, side)) != GDN_OK) return s;
+        st2 = side.s;
+        if (hipEventRecord(side.fork, st) != hipSuccess || hipStreamWaitEvent(st2, side.fork, 0) != hipSuccess)
+            return GDN_ERR_HIP;
+    }
     // 2. chunk-entry states and Delta, with the forward's CP (kept by the forward when reused)
     RecurArgs ra{};
     memset(&ra, 0, sizeof(ra));
@@ -728,11 +738,11 @@ gdn_status gdn_chunk_bwd(const gdn_desc* desc, const void* q, const void* k, con
         GDN_LAUNCH(kKBwdScan, st, launch_scan(sa, desc->dtype, st));
         va.seginit = seginit_r;
     }
-    GDN_LAUNCH(kKBwdReverse, st, launch_reverse(va, desc->dtype, kRecurOut, p.total_segs, vtiles, st));
+    if (!carry) GDN_LAUNCH(kKBwdReverse, st, launch_reverse(va, desc->dtype, kRecurOut, p.total_segs, vtiles, st));
     return GDN_OK;
     }();
     // join, also after a failed launch on the side stream
-    if (hipEventRecord(side.join, st2) != hipSuccess || hipStreamWaitEvent(st, side.join, 0) != hipSuccess)
+    if (fork && (hipEventRecord(side.join, st2) != hipSuccess || hipStreamWaitEvent(st, side.join, 0) != hipSuccess))
         return GDN_ERR_HIP;
     if (sr != GDN_OK) return sr;
     // 4. per-chunk gradients
@@ -758,6 +768,11 @@ gdn_status gdn_chunk_bwd(const gdn_desc* desc, const void* q, const void* k, con
     ba.dbeta = dbeta;
     ba.scale = desc->scale;
     ba.q_l2 = kn != nullptr;
+    ba.carry = carry;
+    ba.use_cp = p.cp_on;
+    ba.seginit_r = p.cp_on ? reinterpret_cast<const float*>(ws + p.o_seginit_r) : nullptr;
+    ba.dsT = d_final_state;
+    ba.ds0 = d_initial_state;
     const int64_t tasks = p.total_chunks * (int64_t)desc->H;
     GDN_LAUNCH(kKBwdChunk, st, launch_bwd_chunk(ba, desc->dtype, (int)std::min<int64_t>(tasks, p.cus), st));
     // 5. dq and dk back through the normalisation to the raw rows, in place

@@ -612,19 +612,20 @@ struct BCfg {
 // One task's operands in registers, in the two groups that are fetched at different
 // points of the previous task: the chunk rows (q, k, dO, Delta, dDelta, T, gate cumsum,
 // beta), then S, G and v.
-template <typename T, int K, int V>
+template <typename T, int K, int V, bool kCarry>
 struct BRegs {
     using C = BCfg<T, K, V>;
-    u32x4 q[C::NK], k[C::NK], d[C::NV], dl[C::NV], dd[C::NV];
-    u32x4 s[C::NS], g[C::NS];
+    // with the adjoint carried in the kernel, G and dDelta are formed here instead of loaded
+    u32x4 q[C::NK], k[C::NK], d[C::NV], dl[C::NV], dd[kCarry ? 1 : C::NV];
+    u32x4 s[C::NS], g[kCarry ? 1 : C::NS];
     float gam, beta;
 };
 
 // The next task's operands travel in small groups issued at different points of the
 // current task's WY side: a burst of all of them would stall the issuing waves on the
 // CU's load queue instead of draining behind the matrix work.
-template <int kGroup, typename T, int K, int V>
-__device__ __forceinline__ void bwd_fetch(BRegs<T, K, V>& R, const BwdChunkArgs& a, const ChunkTask& x) {
+template <int kGroup, typename T, int K, int V, bool kCarry>
+__device__ __forceinline__ void bwd_fetch(BRegs<T, K, V, kCarry>& R, const BwdChunkArgs& a, const ChunkTask& x) {
     using C = BCfg<T, K, V>;
     const int64_t H = a.geo.H;
     const size_t ok = ((size_t)x.t0 * H + x.h) * K, ov = ((size_t)x.t0 * H + x.h) * V;
@@ -642,11 +643,13 @@ __device__ __forceinline__ void bwd_fetch(BRegs<T, K, V>& R, const BwdChunkArgs&
         fetch_tile<T, V, C::NV, C::NT>(R.d, reinterpret_cast<const T*>(a.d_o) + ov, (size_t)H * V, x.c);
     } else if constexpr (kGroup == 2) {
         fetch_tile<T, V, C::NV, C::NT>(R.dl, reinterpret_cast<const T*>(a.delta) + ov, (size_t)H * V, x.c);
-        fetch_tile<T, V, C::NV, C::NT>(R.dd, reinterpret_cast<const T*>(a.ddelta) + ov, (size_t)H * V, x.c);
+        if constexpr (!kCarry)
+            fetch_tile<T, V, C::NV, C::NT>(R.dd, reinterpret_cast<const T*>(a.ddelta) + ov, (size_t)H * V, x.c);
     } else if constexpr (kGroup == 3) {
         fetch_tile<T, K, C::NS, C::NT>(R.s, reinterpret_cast<const T*>(a.hstates) + st, K, V);
     } else {
-        fetch_tile<T, K, C::NS, C::NT>(R.g, reinterpret_cast<const T*>(a.gstates) + st, K, V);
+        if constexpr (!kCarry)
+            fetch_tile<T, K, C::NS, C::NT>(R.g, reinterpret_cast<const T*>(a.gstates) + st, K, V);
     }
 }
 
@@ -694,12 +697,41 @@ __device__ __forceinline__ Frag<float> neg(const Frag<float>& f) {
 // Sum over the four lanes that share ln (lane groups gq = 0..3).
 __device__ __forceinline__ float sum_gq(float x) { return sum_rows(x); }
 
+// Per-slot scaling of a bf16 fragment by e^{gam}: slot e of lane group gq is row
+// k0 + kappa(gq, e) of the contraction, and gets the factor exp(gam[k0 + kappa(gq, e)]) (gam in LDS).
+__device__ __forceinline__ Frag<bf16_t> scale_slots_exp(const Frag<bf16_t>& f, const float* gam, int k0) {
+    const int gq = threadIdx.x >> 4 & 3;
+    const f32x4 a = *reinterpret_cast<const f32x4*>(gam + k0 + gq * 4);
+    const f32x4 b = *reinterpret_cast<const f32x4*>(gam + k0 + 16 + gq * 4);
+    Frag<bf16_t> o;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const f32x4& x = i < 2 ? a : b;  // u32 i holds slots 2i, 2i+1
+        const int e = (i & 1) * 2;
+        o.v[i] = pack_bf2(__uint_as_float(f.v[i] << 16) * fast_exp(x[e]),
+                          __uint_as_float(f.v[i] & 0xFFFF0000u) * fast_exp(x[e + 1]));
+    }
+    return o;
+}
+
 // kL2: q arrives raw and its rows are L2-normalised in registers before staging (dq is then
 // the gradient with respect to the normalised rows).
-template <typename T, int K, int V, bool kL2 = false>
+//
+// kCarry: the reverse adjoint recurrence runs inside this kernel. One workgroup per
+// (sub-sequence, head) walks its chunks from the last to the first and keeps G, the adjoint of
+// the state leaving the chunk, as fp32 accumulator tiles of G^T (wave w: value rows 16w ..
+// 16w+15, every k; V = 128), from the sub-sequence's entering adjoint (d(final state), or the
+// reverse CP's). Each task then forms what the adjoint pass would have stored:
+//   dDelta = P^T (scale dO) + diag(e^{Gam-gam}) K G^T          (P = L .* Q K^T)
+// and afterwards the adjoint entering the chunk, which the next task (the chunk before) uses:
+//   G <- e^Gam G + (e^gam Q)^T (scale dO) - W^T dDelta,   W^T dDelta = K^T diag(beta e^gam) dBv
+// with dBv = T^T dDelta from the WY side (W = T diag(beta e^gam) K), so W itself is never needed.
+// No adjoint pass, no per-chunk adjoint or dDelta round trip through memory.
+template <typename T, int K, int V, bool kL2 = false, bool kCarry = false>
 __global__ __launch_bounds__(512) void k_bwd_chunk(BwdChunkArgs a) {
     using C = BCfg<T, K, V>;
     constexpr int NT = C::NT;
+    static_assert(!kCarry || (V == 128 && sizeof(T) == 2), "the carried adjoint: one 16-row value tile per wave");
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
 
     const Geo& geo = a.geo;
@@ -718,9 +750,45 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(BwdChunkArgs a) {
     constexpr int VH = V / 32;     // v tiles per half
 
     ChunkTask cur;
-    int64_t t = next_chunk_task(geo, blockIdx.x, ntasks, cur);
-    if (t >= ntasks) return;
-    BRegs<T, K, V> R;  // the next task's operands
+    int64_t t = 0;
+    // kCarry: this workgroup's sub-sequence and head, walked from chunk sg.c1 - 1 down to sg.c0
+    SegLoc sg;
+    int64_t gseg = 0;
+    int hc = 0;
+    f32x4 accG[kCarry ? K / 16 : 1];  // G^T: rows k (tile kt), columns v = wave * 16 + ln
+    const int vrow = wave * 16 + ln;
+    const size_t VK = (size_t)V * K;
+    auto seg_task = [&](int ci, ChunkTask& x) {
+        x.gc = sg.choff + ci;
+        x.t0 = sg.bos + (int64_t)ci * 64;
+        x.h = hc;
+        x.c = min(64, sg.len - ci * 64);
+    };
+    if constexpr (kCarry) {
+        gseg = blockIdx.x / H;
+        hc = (int)(blockIdx.x - gseg * H);
+        if (!locate_seg(geo, gseg, sg)) return;
+        if (sg.s < sg.nseg - 1 && a.use_cp)
+            load_state<K>(accG, a.seginit_r + ((size_t)gseg * H + hc) * VK, vrow);
+        else if (a.dsT)
+            load_state<K>(accG, a.dsT + ((size_t)sg.n * H + hc) * VK, vrow);
+        else
+#pragma unroll
+            for (int kt = 0; kt < K / 16; ++kt) accG[kt] = zero4();
+        // the entering adjoint may come from a load: wait for it before any prefetch
+#pragma unroll
+        for (int kt = 0; kt < K / 16; ++kt) hold(accG[kt]);
+        if (sg.c1 <= sg.c0) {  // no chunks: the adjoint passes through
+            if (sg.s == 0 && a.ds0) store_state<K>(accG, a.ds0 + ((size_t)sg.n * H + hc) * VK, vrow);
+            return;
+        }
+        t = sg.c1 - 1;
+        seg_task((int)t, cur);
+    } else {
+        t = next_chunk_task(geo, blockIdx.x, ntasks, cur);
+        if (t >= ntasks) return;
+    }
+    BRegs<T, K, V, kCarry> R;  // the next task's operands
     VTRegs<T, K, V> RV;  // v and T of this task
     bwd_fetch<0>(R, a, cur);
     bwd_fetch<1>(R, a, cur);
@@ -766,7 +834,7 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(BwdChunkArgs a) {
         // scale * dO and Delta are read as row fragments only: rows in fragment order
         put_tile_fo<T, V, C::NV, NT>(sD, C::LDV, R.d, a.scale);
         put_tile_fo<T, V, C::NV, NT>(sDl, C::LDV, R.dl);
-        put_tile_fo<T, V, C::NV, NT>(sdU, C::LDV, R.dd);
+        if constexpr (!kCarry) put_tile_fo<T, V, C::NV, NT>(sdU, C::LDV, R.dd);
         if (tid < 64) {
             sGam[tid] = R.gam;
             sBeta[tid] = R.beta;
@@ -775,9 +843,17 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(BwdChunkArgs a) {
         // The last task fetches itself again: unconditional fetches end the previous
         // operands' live range at the staging above.
         ChunkTask nxt = cur;
-        const int64_t tn = next_chunk_task(geo, t + gridDim.x, ntasks, nxt);
-        const bool more = tn < ntasks;
-        if (!more) nxt = cur;
+        int64_t tn;
+        bool more;
+        if constexpr (kCarry) {
+            tn = t - 1;  // the chunk before
+            more = tn >= sg.c0;
+            if (more) seg_task((int)tn, nxt);
+        } else {
+            tn = next_chunk_task(geo, t + gridDim.x, ntasks, nxt);
+            more = tn < ntasks;
+            if (!more) nxt = cur;
+        }
 
         const int c = cur.c;
         const int64_t t0 = cur.t0;
@@ -819,11 +895,78 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(BwdChunkArgs a) {
                 for (int m = 0; m < 2; ++m) mma(PmQ[m], fk[m], qr[kb]);
             }
         }
+        // kCarry: P[r][j] = e^{gam_r - gam_j} (Q K^T)[r][j] (j <= r) for dDelta, staged over the
+        // dDelta tile (rows r, fragment order) until dDelta replaces it
+        T* sPr = sdU;
+        if constexpr (kCarry) {
+#pragma unroll
+            for (int m = 0; m < 2; ++m) {
+                const int jt = 2 * hf + m;
+                const f32x4 gj = ld4(sGam + jt * 16 + gq * 4);
+                f32x4 pv;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) pv[i] = (jt * 16 + gq * 4 + i <= r) ? PmQ[m][i] * fast_exp(gr - gj[i]) : 0.f;
+                store4(sPr + r * C::LDX + frag_pos(jt * 16 + gq * 4), pv);
+            }
+        }
         // S and G are fetched last in the previous task and staged only here, so that their
         // registers are free over that task's WY side and their loads land behind the products above
+        // (kCarry: G from its accumulators, rows v = this wave's 16 value rows)
         put_tile<T, K, C::NS, NT>(sS, C::LDK, R.s);
-        put_tile<T, K, C::NS, NT>(sG, C::LDK, R.g);
+        if constexpr (kCarry) {
+#pragma unroll
+            for (int kt = 0; kt < K / 16; ++kt) store4(sG + vrow * C::LDK + kt * 16 + gq * 4, accG[kt]);
+        } else {
+            put_tile<T, K, C::NS, NT>(sG, C::LDK, R.g);
+        }
         lds_sync();
+        // kCarry: dDelta^T tiles [v = this wave's rows][j] (stored after the next barrier, once
+        // every wave has read P), then the first part of the adjoint update
+        f32x4 ddT[kCarry ? 4 : 1];
+        if constexpr (kCarry) {
+            Frag<T> gfr[K / 32];
+#pragma unroll
+            for (int kb = 0; kb < K / 32; ++kb) frag_acc(gfr[kb], accG[2 * kb], accG[2 * kb + 1]);  // G rows v, slots k
+            // diag(e^{Gam-gam_j}) K G^T, column j of each tile
+#pragma unroll
+            for (int jt = 0; jt < 4; ++jt) {
+                ddT[jt] = zero4();
+                Frag<T> fk[K / 32];
+#pragma unroll
+                for (int kb = 0; kb < K / 32; ++kb) frag_row_fo(fk[kb], sK, C::LDK, jt * 16 + ln, kb * 32);  // K row j
+#pragma unroll
+                for (int kb = 0; kb < K / 32; ++kb) mma(ddT[jt], gfr[kb], fk[kb]);
+                ddT[jt] *= fast_exp(Gm - sGam[jt * 16 + ln]);
+            }
+            // + (scale dO)^T P: contraction over the chunk rows r >= j
+            Frag<T> dof[2];
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb) frag_col_fo(dof[rb], sD, C::LDV, vrow, rb * 32);  // scale dO column v, slots r
+#pragma unroll
+            for (int jt = 0; jt < 4; ++jt) {
+#pragma unroll
+                for (int rb = jt >> 1; rb < 2; ++rb) {
+                    Frag<T> fp;
+                    frag_col_fo(fp, sPr, C::LDX, jt * 16 + ln, rb * 32);  // P column j, slots r
+                    mma(ddT[jt], dof[rb], fp);
+                }
+            }
+            // G^T <- e^Gam G^T + Q^T diag(e^gam) (scale dO)  (the rest after the WY side)
+            const float eG = fast_exp(Gm);
+            Frag<T> dos[2];
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb) dos[rb] = scale_slots_exp(dof[rb], sGam, rb * 32);
+#pragma unroll
+            for (int kt = 0; kt < K / 16; ++kt) {
+                accG[kt] *= eG;
+#pragma unroll
+                for (int rb = 0; rb < 2; ++rb) {
+                    Frag<T> fq;
+                    frag_col_fo(fq, sQ, C::LDK, kt * 16 + ln, rb * 32);  // Q column k, slots r
+                    mma(accG[kt], fq, dos[rb]);
+                }
+            }
+        }
         // e^Gam <G, S> over the whole state (each thread a slice)
         float gs = 0.f;
         {
@@ -895,6 +1038,11 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(BwdChunkArgs a) {
         drow = sum_gq(drow);
         if (gq == 0) sRow[hf * 64 + r] = drow;
         lds_sync();  // every read of Delta is done: the exchange overwrites it
+        if constexpr (kCarry) {
+            // dDelta over P (every wave's reads of P are done): rows j, this wave's value columns
+#pragma unroll
+            for (int jt = 0; jt < 4; ++jt) store4(sdU + (jt * 16 + ln) * C::LDV + frag_pos(vrow - ln + gq * 4), ddT[jt]);
+        }
         // exchange L .* dP: sX[query r][key j]
 #pragma unroll
         for (int m = 0; m < 2; ++m) store4(sX + r * C::LDX + frag_pos((2 * hf + m) * 16 + gq * 4), LdP[m]);
@@ -1174,6 +1322,7 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(BwdChunkArgs a) {
                 if (ra < c) store4(dkp + kt * 16 + gq * 4, dkpart[i] + mk + bk * (ba * ega));
             }
         }
+        f32x4 bvk[kCarry ? VH : 1];  // kCarry: dBv[a = ra][this half's v tiles], for the adjoint update
         {
             T* dvp = reinterpret_cast<T*>(a.dv) + ((t0 + ra) * H + h) * V;
 #pragma unroll
@@ -1188,6 +1337,7 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(BwdChunkArgs a) {
                 }
                 dbeta_row += dot4(bv, ld4(sV + ra * C::LDV + frag_pos(vt * 16 + gq * 4)));
                 if (ra < c) store4(dvp + vt * 16 + gq * 4, bv * ba);
+                if constexpr (kCarry) bvk[i] = bv;
             }
         }
         bwd_fetch<3>(R, a, nxt);
@@ -1211,9 +1361,39 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(BwdChunkArgs a) {
         } else if (wave == 1) {
             if (lane < c) a.dbeta[(t0 + lane) * H + h] = sDb[lane] + sDb[64 + lane];
         }
+        if constexpr (kCarry) {
+            // G^T -= K^T X, X = diag(beta e^gam) dBv (= W^T dDelta): this lane's row a = ra of X over
+            // the state's space (every read of dW, V and the rest of the WY side is done), then
+            // every wave its value columns
+            T* sXb = reinterpret_cast<T*>(sm + C::off_s);
+            const float bea = ba * ega;
+#pragma unroll
+            for (int i = 0; i < VH; ++i) store4(sXb + ra * C::LDV + frag_pos((hf * VH + i) * 16 + gq * 4), bvk[i] * bea);
+            lds_sync();
+            Frag<T> nx[2];
+#pragma unroll
+            for (int ab = 0; ab < 2; ++ab) {
+                Frag<T> f;
+                frag_col_fo(f, sXb, C::LDV, vrow, ab * 32);  // X column v, slots a
+                nx[ab] = neg(f);
+            }
+#pragma unroll
+            for (int kt = 0; kt < K / 16; ++kt) {
+#pragma unroll
+                for (int ab = 0; ab < 2; ++ab) {
+                    Frag<T> fk;
+                    frag_col_fo(fk, sK, C::LDK, kt * 16 + ln, ab * 32);  // K column k, slots a
+                    mma(accG[kt], fk, nx[ab]);
+                }
+            }
+        }
         if (!more) break;
         cur = nxt;
         t = tn;
+    }
+    // the adjoint entering the sub-sequence's first chunk: d(initial state) at a sequence start
+    if constexpr (kCarry) {
+        if (sg.s == 0 && a.ds0) store_state<K>(accG, a.ds0 + ((size_t)sg.n * H + hc) * VK, vrow);
     }
 }
 
@@ -1222,6 +1402,13 @@ hipError_t launch_bwd_chunk_t(const BwdChunkArgs& a, int grid, hipStream_t st) {
     using C = BCfg<T, K, V>;
     static_assert(C::total <= 160 * 1024, "LDS budget");
     auto kern = a.q_l2 ? k_bwd_chunk<T, K, V, true> : k_bwd_chunk<T, K, V, false>;
+    if constexpr (V == 128 && sizeof(T) == 2) {
+        // one workgroup per (sub-sequence, head), each carrying its adjoint
+        if (a.carry) {
+            kern = a.q_l2 ? k_bwd_chunk<T, K, V, true, true> : k_bwd_chunk<T, K, V, false, true>;
+            grid = (int)(a.geo.total_segs * a.geo.H);
+        }
+    }
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, C::total);
     if (e != hipSuccess) return e;
@@ -1263,7 +1450,9 @@ hipError_t launch_reverse(const RevArgs& a, int dtype, int mode, int64_t nsegs_g
     }
 
 hipError_t launch_bwd_chunk(const BwdChunkArgs& a, int dtype, int grid, hipStream_t st) {
-    if (a.geo.total_chunks == 0 || grid < 1) return hipSuccess;
+    // (carrying the adjoint, sub-sequences without chunks still pass d(final state) through)
+    if ((a.carry ? a.geo.total_segs : a.geo.total_chunks) == 0 || grid < 1) return hipSuccess;
+    if (a.carry && (a.geo.V != 128 || dtype != 0)) return hipErrorInvalidValue;
     const int K = a.geo.K, V = a.geo.V;
     GDN_BWD_CASES(launch_bwd_chunk_t)
     return hipErrorInvalidValue;

@@ -242,6 +242,13 @@ struct BwdChunkArgs {
     float scale;
     int32_t q_l2;             // q is raw, its rows are L2-normalised as staged (dq is then with
                               // respect to the normalised rows)
+    // carry: one workgroup per (sub-sequence, head) carries the adjoint through its chunks in
+    // reverse (no adjoint pass: gstates and ddelta unused); V = 128, bf16 only
+    int32_t carry;
+    int32_t use_cp;           // carry: sub-sequences but a sequence's last start from seginit_r
+    const float* seginit_r;   // carry: [total_segs,H,V,K] adjoint leaving each sub-sequence (reverse CP)
+    const float* dsT;         // carry: [N,H,V,K] d(final state), or null
+    float* ds0;               // carry: [N,H,V,K] d(initial state) out, or null
 };
 
 struct TableArgs {

@@ -116,6 +116,14 @@ typedef enum gdn_cp_mode {
  * and k inside its kernel (fp32 rows, not rounded to the input dtype). */
 #define GDN_FLAG_QK_L2NORM 4
 
+/* GDN_FLAG_BWD_ADJOINT_PASS: gdn_chunk_bwd runs the reverse adjoint recurrence as a pass of its
+ * own that stores every chunk's adjoint and dDelta for the per-chunk gradient kernel. By default,
+ * at V = 128 in bf16 with CP on or a uniform batch, the per-chunk gradient kernel carries the
+ * adjoint itself (one workgroup per sub-sequence and head walking its chunks in reverse), which
+ * moves fewer bytes; the flag keeps the other path selectable, for comparison. Same results within
+ * rounding. */
+#define GDN_FLAG_BWD_ADJOINT_PASS 8
+
 /* Problem descriptor. Zero-initialise, then fill. */
 typedef struct gdn_desc {
     int64_t B, T, H, K, V;          /* batch, tokens per row (packed total if varlen), heads, key dim, value dim */

@@ -327,3 +327,25 @@ def test_backward_cp_mixed_boundaries(gpu_lib, dtype, K, V):
     d = to_dev(inp)
     errs = compare(gpu_bwd(d, cp_mode="on", seg_chunks=16), oracle_bwd(inp), tol_for(dtype))
     print(f"mixed {dtype} " + " ".join(f"{n}={e:.2e}" for n, e in errs.items()), flush=True)
+
+
+@pytest.mark.parametrize("K,cp,kw,lengths", [
+    (128, "off", {}, None), (128, "exact", dict(seg_chunks=3), None), (128, "warmup", dict(seg_chunks=4, warmup_chunks=3), None),
+    (64, "on", dict(seg_chunks=4), None), (128, "exact", dict(seg_chunks=2), [1, 63, 64, 65, 0, 700, 1500, 129]),
+])
+def test_backward_carried_adjoint_and_adjoint_pass(gpu_lib, K, cp, kw, lengths):
+    """At V = 128 in bf16 the per-chunk kernel carries the adjoint through each sub-sequence
+    (default); GDN_FLAG_BWD_ADJOINT_PASS runs the separate adjoint pass instead. Both match the
+    oracle on the same inputs, with CP off, exact, warmup, gated and packed sequences."""
+    if lengths is None:
+        inp = with_grads(small_inputs(B=2, T=1000, H=2, K=K, V=128, seed=23))
+    else:
+        inp = with_grads(small_inputs(H=3, K=K, V=128, lengths=lengths, seed=23))
+    d = to_dev(inp)
+    ref = oracle_bwd(inp, scale=0.9)
+    carried = gpu_bwd(d, scale=0.9, cp_mode=cp, **kw)
+    separate = gpu_bwd(d, scale=0.9, cp_mode=cp, adjoint_pass=True, **kw)
+    e1 = compare(carried, ref, 1e-2)
+    e2 = compare(separate, ref, 1e-2)
+    print("carried " + " ".join(f"{n}={e:.2e}" for n, e in e1.items()), flush=True)
+    print("separate " + " ".join(f"{n}={e:.2e}" for n, e in e2.items()), flush=True)
