@@ -277,6 +277,61 @@ def copy_ceiling(buf, reps=10):
             "frac": round(2 * n / (med * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
 
 
+def fused_leg(gdn, flush, reps=10):
+    """The fully fused forward against the two-kernel split (both CP off, bf16, K = V = 128) where
+    the plan picks it, a uniform batch of 8 x 4096 tokens and 64 heads (512 sequence-heads: two rounds
+    of recurrence workgroups), and on the packed-varlen workload's shape (8 sequences, H = 32, the
+    recurrence in one round). Inputs drawn on the device; flushed calls, median ms."""
+    import torch
+    from gdn_inputs import WORKLOADS, varlen_lengths
+    w = WORKLOADS["varlen_packed"]
+    lens, _ = varlen_lengths(w.varlen_count, *w.varlen_range, w.varlen_total, 0)
+    shapes = {"B8_H64_T4K": dict(B=8, T=4096, H=64, lengths=None),
+              "varlen_packed": dict(B=1, T=sum(lens), H=32, lengths=lens)}
+    out = {}
+    gen = torch.Generator(device="cuda").manual_seed(7)
+    for name, sh in shapes.items():
+        B, T, H = sh["B"], sh["T"], sh["H"]
+        K = V = 128
+        q = torch.nn.functional.normalize(torch.randn((B, T, H, K), device="cuda", generator=gen), dim=-1).bfloat16()
+        k = torch.nn.functional.normalize(torch.randn((B, T, H, K), device="cuda", generator=gen), dim=-1).bfloat16()
+        v = torch.randn((B, T, H, V), device="cuda", generator=gen).bfloat16()
+        g = -torch.nn.functional.softplus(torch.randn((B, T, H), device="cuda", generator=gen)) * 0.1
+        beta = torch.sigmoid(torch.randn((B, T, H), device="cuda", generator=gen))
+        cu = cu_host = None
+        if sh["lengths"] is not None:
+            import numpy as np
+            cu_host = torch.tensor(np.concatenate([[0], np.cumsum(sh["lengths"])]), dtype=torch.int32)
+            cu = cu_host.cuda()
+        N = B if cu is None else len(sh["lengths"])
+        o = torch.empty_like(v)
+        sT = torch.empty((N, H, V, K), dtype=torch.float32, device="cuda")
+        kw = dict(cu_seqlens=cu, cu_seqlens_host=cu_host, cp_mode="off", o=o, final_state=sT)
+        planned = gdn.gdn_plan(gdn.make_desc(q, v, cu_seqlens=cu, cu_seqlens_host=cu_host, cp_mode="off"))
+        ws = torch.empty(planned["fwd_workspace_bytes"], dtype=torch.uint8, device="cuda")
+        res = {"tokens": int(B * T), "heads": H, "planned_fused": planned["fused_fwd"]}
+        th = B * T * H
+        for label, fused in (("split", False), ("fused", True)):
+            def call():
+                gdn.gdn_chunk_fwd(q, k, v, g, beta, None, workspace=ws, fused=fused, **kw)
+            call()
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+            for i in range(reps):
+                flush(i)
+                ev[i][0].record()
+                call()
+                ev[i][1].record()
+            torch.cuda.synchronize()
+            ms = sorted(a.elapsed_time(b) for a, b in ev)[reps // 2]
+            res[label] = {"ms": round(ms, 4), "tokens_per_s": round(B * T / (ms * 1e-3), 1),
+                          # the bytes of that design: 2,320 B per token-head split, 1,032 B fused
+                          "GB/s": round(th * (2320 if label == "split" else 1032) / (ms * 1e-3) / 1e9, 1)}
+        res["fused_speedup"] = round(res["split"]["ms"] / res["fused"]["ms"], 3)
+        out[name] = res
+        del q, k, v, g, beta, o, sT, ws
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -286,6 +341,7 @@ def main():
     ap.add_argument("--pass", dest="passes", default="both", choices=["both", "fwd", "bwd"])
     ap.add_argument("--cp", default=None, help="override the workload's CP mode (auto/off/on/exact/warmup)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-fused-leg", action="store_true", help="skip the fused-forward comparison")
     ap.add_argument("--flushed-calls", type=int, default=50,
                     help="calls timed one by one after a 1 GiB cache flush (median and minimum)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -402,6 +458,7 @@ def main():
     if do_fwd and do_bwd:
         step_keep()
         ms_keep = timed(step_keep, args.steps)
+    fused = fused_leg(gdn, lambda i: flush_buf.fill_(i & 255)) if (do_fwd and not args.no_fused_leg) else None
     l2 = l2norm_leg(gdn, dev, cu, cu_host, cp, timed, args.steps) if (do_fwd and do_bwd) else None
 
     # Per-kernel durations: one more round of steps, each after a flush, with every launch
@@ -519,6 +576,8 @@ def main():
     if l2 is not None:
         l2["overhead_ms"] = round(l2["ms_per_step"] - ms, 4)
         line["qk_l2norm"] = l2
+    if fused is not None:
+        line["fused_forward"] = fused
     line["decode"] = decode_bench(gdn, H, K, V, q.dtype)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(inp, tokens, args.passes)

@@ -26,7 +26,7 @@ import numpy as np
 import torch
 
 from ._abi import (CP_MODES, EXPORTS, GDN_DTYPE_BF16, GDN_DTYPE_FP32, GDN_FLAG_BWD_ADJOINT_PASS,  # noqa: F401
-                   GDN_FLAG_KEEP_FORWARD, GDN_FLAG_QK_L2NORM, GDN_NOALLOC_SCRATCH_BYTES, GDN_FLAG_REUSE_FORWARD, GdnDesc, GdnError, GdnKernelTime, GdnPlanInfo, check,
+                   GDN_FLAG_FWD_FUSED, GDN_FLAG_FWD_SPLIT, GDN_FLAG_KEEP_FORWARD, GDN_FLAG_QK_L2NORM, GDN_NOALLOC_SCRATCH_BYTES, GDN_FLAG_REUSE_FORWARD, GdnDesc, GdnError, GdnKernelTime, GdnPlanInfo, check,
                    load_library, status_string)
 
 __all__ = ["gdn_plan", "gdn_chunk_fwd", "gdn_chunk_fwd_noalloc", "gdn_chunk_bwd", "gdn_workspace", "gdn_intra_chunk", "gdn_cp_modes",
@@ -95,7 +95,7 @@ def make_desc(q, v, **kw) -> Desc:
 def gdn_plan(desc: Desc) -> dict:
     info = GdnPlanInfo()
     check(load_library().gdn_plan(desc.ref, ctypes.byref(info)), "gdn_plan")
-    return {f: getattr(info, f) for f, _ in GdnPlanInfo._fields_}
+    return {f: getattr(info, f) for f, _ in GdnPlanInfo._fields_ if f != "reserved_out"}
 
 
 def gdn_workspace(q, v, *, cu_seqlens=None, cu_seqlens_host=None, cp_mode="auto", warmup_chunks=0,
@@ -164,6 +164,10 @@ def _check_inputs(q, k, v, g, beta, initial_state, N):
             raise ValueError(f"initial_state: expected contiguous fp32 {(N, H, V, K)} on {dev}")
 
 
+def _fused_flag(fused):
+    return 0 if fused is None else (GDN_FLAG_FWD_FUSED if fused else GDN_FLAG_FWD_SPLIT)
+
+
 def _num_seqs(q, cu_seqlens):
     return q.shape[0] if cu_seqlens is None else int(cu_seqlens.numel()) - 1
 
@@ -171,8 +175,12 @@ def _num_seqs(q, cu_seqlens):
 def gdn_chunk_fwd(q, k, v, g, beta, initial_state=None, *, scale=1.0, cu_seqlens=None,
                   cu_seqlens_host=None, output_final_state=True, cp_mode="auto", warmup_chunks=0,
                   seg_chunks=0, warmup_eps=0.0, warmup_max_chunks=0, workspace=None, o=None, final_state=None,
-                  keep_for_backward=False, qk_l2norm=False):
+                  keep_for_backward=False, qk_l2norm=False, fused=None):
     """Forward. Returns (o, final_state or None). Runs on the current stream.
+
+    fused=None lets the plan choose between the two-kernel split and the fully fused forward;
+    True asks for the fused one where it is supported (CP off, bf16, no kept intermediates), False
+    for the split.
 
     qk_l2norm=True takes raw q and k and runs the path on their rows scaled to
     x / sqrt(sum x^2 + 1e-6) (normalised inside the kernels as they stage the rows).
@@ -189,7 +197,7 @@ def gdn_chunk_fwd(q, k, v, g, beta, initial_state=None, *, scale=1.0, cu_seqlens
     desc = make_desc(q, v, scale=scale, cu_seqlens=cu_seqlens, cu_seqlens_host=cu_seqlens_host,
                      cp_mode=cp_mode, warmup_chunks=warmup_chunks, seg_chunks=seg_chunks,
                      warmup_eps=warmup_eps, warmup_max_chunks=warmup_max_chunks, qk_l2norm=qk_l2norm,
-                     flags=GDN_FLAG_KEEP_FORWARD if keep_for_backward else 0)
+                     flags=(GDN_FLAG_KEEP_FORWARD if keep_for_backward else 0) | _fused_flag(fused))
     lib = load_library()
     nbytes = ctypes.c_size_t()
     check(lib.gdn_chunk_fwd_workspace_size(desc.ref, ctypes.byref(nbytes)), "gdn_chunk_fwd_workspace_size")

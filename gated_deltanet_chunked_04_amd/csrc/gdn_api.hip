@@ -54,6 +54,7 @@ struct Plan {
            bwd_bytes = 0;
     int32_t cus = 256;   // compute units (desc->num_cus, else the device's)
     int32_t bwd_ok = 1;  // fp32 backward supports K = V = 64 only (LDS)
+    int32_t fused = 0;   // the forward runs fully fused (no CP, bf16, no kept intermediates)
 };
 
 int query_cus() {
@@ -68,8 +69,10 @@ gdn_status make_plan(const gdn_desc* d, Plan& p) {
     if (!d) return GDN_ERR_INVALID_ARG;
     for (int i = 0; i < 5; ++i)
         if (d->reserved[i] != 0) return GDN_ERR_INVALID_ARG;
-    if (d->flags & ~(GDN_FLAG_KEEP_FORWARD | GDN_FLAG_REUSE_FORWARD | GDN_FLAG_QK_L2NORM | GDN_FLAG_BWD_ADJOINT_PASS))
+    if (d->flags & ~(GDN_FLAG_KEEP_FORWARD | GDN_FLAG_REUSE_FORWARD | GDN_FLAG_QK_L2NORM | GDN_FLAG_BWD_ADJOINT_PASS |
+                     GDN_FLAG_FWD_FUSED | GDN_FLAG_FWD_SPLIT))
         return GDN_ERR_INVALID_ARG;
+    if ((d->flags & GDN_FLAG_FWD_FUSED) && (d->flags & GDN_FLAG_FWD_SPLIT)) return GDN_ERR_INVALID_ARG;
     if (d->B < 1 || d->T < 0 || d->H < 1 || d->K < 1 || d->V < 1) return GDN_ERR_INVALID_ARG;
     if (!(d->chunk == 0 || d->chunk == 64)) return GDN_ERR_UNSUPPORTED;
     if (!(d->K == 64 || d->K == 128) || !(d->V == 64 || d->V == 128)) return GDN_ERR_UNSUPPORTED;
@@ -215,6 +218,13 @@ gdn_status make_plan(const gdn_desc* d, Plan& p) {
     p.o_ddl = take(T * H * V * p.esize);
     p.bwd_bytes = std::max<size_t>(off, kAlign);
     p.bwd_ok = (d->dtype == GDN_DTYPE_BF16) || (d->K == 64 && d->V == 64);
+    // The fully fused forward: possible without CP, in bf16, when nothing is kept for the backward;
+    // chosen when the recurrence already needs at least two rounds of workgroups on the chip (then
+    // the split's intra kernel no longer runs beside an idle recurrence, and the bytes decide).
+    const bool fusable = !p.cp_on && d->dtype == GDN_DTYPE_BF16 && !(d->flags & GDN_FLAG_KEEP_FORWARD);
+    if (d->flags & GDN_FLAG_FWD_FUSED) p.fused = fusable;
+    else if (d->flags & GDN_FLAG_FWD_SPLIT) p.fused = 0;
+    else p.fused = fusable && units >= 2 * target;
     return GDN_OK;
 }
 
@@ -253,10 +263,10 @@ Geo make_geo(const gdn_desc* d, const Plan& p, unsigned char* ws) {
 // ---------------------------------------------------------------------------
 // Kernel timing (gdn_profile_enable / gdn_profile_read).
 enum KernelId { kKTables = 0, kKIntra, kKDecide, kKPrepass, kKScan, kKRecurOut, kKRecurStates,
-                kKBwdPrepass, kKBwdScan, kKBwdReverse, kKBwdChunk, kKDecode, kKL2NormBwd, kKCount };
+                kKBwdPrepass, kKBwdScan, kKBwdReverse, kKBwdChunk, kKDecode, kKL2NormBwd, kKFused, kKCount };
 const char* const kKernelNames[kKCount] = {"tables", "intra", "cp_decide", "cp_prepass", "cp_scan",
                                            "recur_out", "recur_states", "bwd_cp_prepass", "bwd_cp_scan",
-                                           "bwd_reverse", "bwd_chunk", "recurrent", "qk_l2norm_bwd"};
+                                           "bwd_reverse", "bwd_chunk", "recurrent", "qk_l2norm_bwd", "fused_fwd"};
 struct Pending {
     int kid;
     hipEvent_t start, stop;
@@ -361,25 +371,28 @@ void* kn_of(const gdn_desc* d, const Plan& p, unsigned char* ws) {
 }
 
 // Tables (varlen) + intra-chunk kernel into the given output buffers.
+// The varlen tables' arguments (built on the device from cu_seqlens into the workspace).
+TableArgs table_args(const gdn_desc* d, const Plan& p, unsigned char* ws) {
+    TableArgs t{};
+    t.cu = d->cu_seqlens;
+    t.N = p.N;
+    t.Ttot = p.Ttot;
+    t.seg_len = p.seg_len;
+    t.total_chunks = p.total_chunks;
+    t.total_segs = p.total_segs;
+    t.seq_bos = reinterpret_cast<int64_t*>(ws + p.o_bos);
+    t.seq_len = reinterpret_cast<int32_t*>(ws + p.o_len);
+    t.seq_choff = reinterpret_cast<int32_t*>(ws + p.o_choff);
+    t.seq_segoff = reinterpret_cast<int32_t*>(ws + p.o_segoff);
+    t.chunk_tab = reinterpret_cast<int2*>(ws + p.o_ctab);
+    t.seg_tab = reinterpret_cast<int4*>(ws + p.o_stab);
+    return t;
+}
+
 gdn_status run_intra(const gdn_desc* d, const Plan& p, unsigned char* ws, const void* k, const void* v,
                      const float* g, const float* beta, float* gam, void* w, void* u, hipStream_t st,
                      void* tmat = nullptr, void* kn = nullptr) {
-    if (p.varlen) {
-        TableArgs t{};
-        t.cu = d->cu_seqlens;
-        t.N = p.N;
-        t.Ttot = p.Ttot;
-        t.seg_len = p.seg_len;
-        t.total_chunks = p.total_chunks;
-        t.total_segs = p.total_segs;
-        t.seq_bos = reinterpret_cast<int64_t*>(ws + p.o_bos);
-        t.seq_len = reinterpret_cast<int32_t*>(ws + p.o_len);
-        t.seq_choff = reinterpret_cast<int32_t*>(ws + p.o_choff);
-        t.seq_segoff = reinterpret_cast<int32_t*>(ws + p.o_segoff);
-        t.chunk_tab = reinterpret_cast<int2*>(ws + p.o_ctab);
-        t.seg_tab = reinterpret_cast<int4*>(ws + p.o_stab);
-        GDN_LAUNCH(kKTables, st, launch_tables(t, st));
-    }
+    if (p.varlen) GDN_LAUNCH(kKTables, st, launch_tables(table_args(d, p, ws), st));
     IntraArgs ia{};
     ia.geo = make_geo(d, p, ws);
     ia.k = k;
@@ -491,6 +504,7 @@ gdn_status gdn_plan(const gdn_desc* desc, gdn_plan_info* out) {
     out->total_segments = p.total_segs;
     out->fwd_workspace_bytes = p.fwd_bytes;
     out->bwd_workspace_bytes = p.bwd_bytes;
+    out->fused_fwd = p.fused;
     return GDN_OK;
 }
 
@@ -540,6 +554,25 @@ gdn_status run_fwd(const gdn_desc* desc, const Plan& p, const void* q, const voi
                    const float* g, const float* beta, const float* initial_state, void* o, float* final_state,
                    unsigned char* ws, hipStream_t st) {
     gdn_status s = GDN_OK;
+    if (p.fused) {
+        if (p.varlen) GDN_LAUNCH(kKTables, st, launch_tables(table_args(desc, p, ws), st));
+        RecurArgs fa{};
+        memset(&fa, 0, sizeof(fa));
+        fa.geo = make_geo(desc, p, ws);
+        fa.q = q;
+        fa.k = k;
+        fa.fv = v;
+        fa.fg = g;
+        fa.fbeta = beta;
+        fa.s0 = initial_state;
+        fa.o = o;
+        fa.sT = final_state;
+        fa.scale = desc->scale;
+        fa.q_l2 = (desc->flags & GDN_FLAG_QK_L2NORM) != 0;
+        GDN_LAUNCH(kKFused, st, launch_fused(fa, desc->dtype, p.total_segs,
+                                             (int)(desc->V / recur_rows((int)desc->V, (int)desc->K)), st));
+        return GDN_OK;
+    }
     float* gam = reinterpret_cast<float*>(ws + p.o_gam);
     void* w = ws + p.o_w;
     void* u = ws + p.o_u;

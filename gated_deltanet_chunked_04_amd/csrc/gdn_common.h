@@ -325,7 +325,8 @@ struct SeqInfo {
 
 // ---------------------------------------------------------------------------
 // T = (I + A)^{-1} for a 64x64 strictly lower triangular fp32 A in LDS (leading dimension
-// kLdA), written to T in LDS; 256-thread workgroups. Diagonal 16x16 blocks by forward
+// kLdA), written to T in LDS; the first four waves of the workgroup do the work (all of its
+// waves must call it: it contains barriers). Diagonal 16x16 blocks by forward
 // substitution (wave b, lanes 0..15 = the columns of block b), then the off-diagonal
 // blocks level by level (T_ij = -T_ii sum_m A_im T_mj) with
 // fp32 matrix-core products. Starts and ends with the LDS in a consistent state for the
@@ -374,7 +375,7 @@ __device__ __forceinline__ void tri_inverse64(float* sA, float* sT) {
     // 3a: diagonal blocks by forward substitution (wave b, lanes 0..15 = columns of block b),
     // column-oriented: once x_j is final it updates every later row, so the dependent chain
     // is 15 fused multiply-adds long instead of one per product
-    if (gq == 0) {
+    if (gq == 0 && wave < 4) {  // (workgroups of more than four waves: the others wait)
         const int b = wave;
         const int col = ln;
         const float* ablk = sA + (16 * b) * kLdA + 16 * b;

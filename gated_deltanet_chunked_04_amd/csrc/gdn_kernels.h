@@ -173,6 +173,10 @@ struct RecurArgs {
     float scale;
     int32_t use_cp;           // segments >= 1 read seginit
     int32_t q_l2;             // output modes: q is raw, its rows are L2-normalised as staged
+    // the fully fused forward (launch_fused) reads the raw inputs instead of w, u and the gate cumsum
+    const void* fv;           // [Ttot,H,V]
+    const float* fg;          // [Ttot,H]
+    const float* fbeta;       // [Ttot,H]
 };
 
 struct DecideArgs {
@@ -277,6 +281,8 @@ hipError_t launch_decide(const DecideArgs& a, hipStream_t st);
 hipError_t launch_recur(const RecurArgs& a, int dtype, int mode, int64_t nsegs_grid, int vtiles,
                         hipStream_t st);
 hipError_t launch_scan(const ScanArgs& a, int dtype, hipStream_t st);
+// the fully fused forward without CP: grid (sequences, H, value-row tiles); bf16 only
+hipError_t launch_fused(const RecurArgs& a, int dtype, int64_t nseqs, int vtiles, hipStream_t st);
 hipError_t launch_reverse(const RevArgs& a, int dtype, int mode, int64_t nsegs_grid, int vtiles, hipStream_t st);
 // grid: persistent workgroups (one per CU; each walks tasks gc * H + h with a grid stride)
 hipError_t launch_bwd_chunk(const BwdChunkArgs& a, int dtype, int grid, hipStream_t st);

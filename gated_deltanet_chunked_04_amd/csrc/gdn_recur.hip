@@ -128,7 +128,8 @@ __device__ __forceinline__ void chunk_stage(const ChunkRegs<T, K, RT, kQ>& R, co
 //   kOut    : also produce O for value columns vcol0 + wave*16 ..
 // Part 1 writes this wave's share of the P tiles; the caller's barrier separates it
 // from part 2.
-template <typename T, int K, int RT, bool kOut>
+// kKfo: the K tile is stored in fragment order (the fused forward's layout) instead of row-major.
+template <typename T, int K, int RT, bool kOut, bool kKfo = false>
 __device__ __forceinline__ void chunk_part1(const ChunkLds<T, K, RT>& L, const f32x4 (&accS)[K / 16],
                                             Frag<T> (&sf)[K / 32], f32x4 (&accD)[4], f32x4 (&accO)[4]) {
     using C = RCfg<T, K, RT>;
@@ -179,7 +180,10 @@ __device__ __forceinline__ void chunk_part1(const ChunkLds<T, K, RT>& L, const f
             }
 #pragma unroll
             for (int m = 0; m < NPT; ++m)
-                if (pmm[m]) frag_row(fa[m], L.sK, C::LD, pjt[m] * 16 + ln, kb * 32);
+                if (pmm[m]) {
+                    if constexpr (kKfo) frag_row_fo(fa[m], L.sK, C::LD, pjt[m] * 16 + ln, kb * 32);
+                    else frag_row(fa[m], L.sK, C::LD, pjt[m] * 16 + ln, kb * 32);
+                }
 #pragma unroll
             for (int rt = 0; rt < 4; ++rt) {
                 mma(accD[rt], fw[rt], nsf[kb]);
@@ -238,7 +242,8 @@ __device__ __forceinline__ void chunk_part1(const ChunkLds<T, K, RT>& L, const f
 #pragma unroll
                 for (int m = 0; m < NPT; ++m) {
                     if (pmm[m]) {
-                        frag_row(fa[m], L.sK, C::LD, pjt[m] * 16 + ln, kb * 32);
+                        if constexpr (kKfo) frag_row_fo(fa[m], L.sK, C::LD, pjt[m] * 16 + ln, kb * 32);
+                        else frag_row(fa[m], L.sK, C::LD, pjt[m] * 16 + ln, kb * 32);
                         frag_row_fo(fb[m], L.sQ, C::LD, prt[m] * 16 + ln, kb * 32);
                     }
                 }
@@ -294,7 +299,7 @@ __device__ __forceinline__ void chunk_part1(const ChunkLds<T, K, RT>& L, const f
     }
 }
 
-template <typename T, int K, int RT, bool kOut>
+template <typename T, int K, int RT, bool kOut, bool kKfo = false>
 __device__ __forceinline__ void chunk_part2(const RecurArgs& a, const ChunkLds<T, K, RT>& L, f32x4 (&accS)[K / 16],
                                             f32x4 (&accD)[4], f32x4 (&accO)[4], int64_t t0, int c, int h,
                                             int vcol0, typename Pack4<T>::type (&okeep)[4]) {
@@ -349,7 +354,10 @@ __device__ __forceinline__ void chunk_part2(const RecurArgs& a, const ChunkLds<T
     for (int kb = 0; kb < 2; ++kb) {
         Frag<T> fa[K / 16];
 #pragma unroll
-        for (int kt = 0; kt < K / 16; ++kt) frag_col(fa[kt], L.sK, C::LD, kt * 16 + ln, kb * 32);  // K^T row k, slots j
+        for (int kt = 0; kt < K / 16; ++kt) {
+            if constexpr (kKfo) frag_col_fo(fa[kt], L.sK, C::LD, kt * 16 + ln, kb * 32);  // K^T row k, slots j
+            else frag_col(fa[kt], L.sK, C::LD, kt * 16 + ln, kb * 32);
+        }
 #pragma unroll
         for (int kt = 0; kt < K / 16; ++kt) mma(accS[kt], fa[kt], dtf[kb]);
     }
@@ -848,6 +856,273 @@ hipError_t launch_scan_t(const ScanArgs& a, hipStream_t st) {
 }
 
 // ---------------------------------------------------------------------------
+// Fully fused forward (no CP): the first kernel's intra-chunk step and the recurrence in one
+// workgroup per (sequence, head, row tile), chunk after chunk. The gate cumsum, A, T = (I+A)^-1
+// and the WY factors W = T diag(beta e^gam) K, U = T diag(beta) V[:, this tile] live in LDS only,
+// so the forward moves q, k, v, g, beta in and o out (1,032 B per token-head at K = V = 128 in
+// bf16) instead of the split's 2,320 B, at the price of the intra work on the recurrence's serial
+// chain. This is the pages' fully fused alternative, which they name as the better design at
+// large batch (announcement post, on the two-kernel split's extra memory I/O); the planner picks
+// it where the recurrence already runs in several rounds of workgroups.
+//
+// Layout: the recurrence's tiles (q and w in fragment order, u [64][RT], the P tiles, the gate
+// cumsum), k in fragment order (the Gram rows, and the recurrence through its fragment-order
+// reads), this tile's value columns of v [64][RT] row-major, A and T in fp32, beta. With eight
+// waves (RT = 128) waves 0-3 form W and waves 4-7 U; with four, every wave both.
+template <typename T, int K, int RT>
+struct FCfg {
+    using C = RCfg<T, K, RT>;
+    static constexpr int LDV = RT + RPad<T>::row;
+    static constexpr int off_v = C::total;
+    static constexpr int off_a = off_v + 64 * LDV * (int)sizeof(T);
+    static constexpr int off_t = off_a + 64 * kLdA * 4;
+    static constexpr int off_beta = off_t + 64 * kLdA * 4;
+    static constexpr int total = off_beta + 256;
+    static constexpr int IV = 64 * (RT / C::VEC) / C::NT;  // v vectors per thread
+    static_assert(IV * C::NT == 64 * (RT / C::VEC), "v tile split");
+};
+
+template <typename T, int K, int RT>
+struct FusedRegs {
+    using C = RCfg<T, K, RT>;
+    using F = FCfg<T, K, RT>;
+    u32x4 q[C::IQ], k[C::IQ], v[F::IV];
+    float g, beta;  // lanes of wave 0
+};
+
+template <typename T, int K, int RT>
+__device__ __forceinline__ void fused_fetch(FusedRegs<T, K, RT>& R, const RecurArgs& a, int64_t t0, int c, int h,
+                                            int vcol0) {
+    using C = RCfg<T, K, RT>;
+    using F = FCfg<T, K, RT>;
+    const int64_t H = a.geo.H;
+    const size_t ok = ((size_t)t0 * H + h) * K;
+    fetch_tile<T, K, C::IQ, C::NT>(R.q, reinterpret_cast<const T*>(a.q) + ok, (size_t)H * K, c);
+    fetch_tile<T, K, C::IQ, C::NT>(R.k, reinterpret_cast<const T*>(a.k) + ok, (size_t)H * K, c);
+    fetch_tile<T, RT, F::IV, C::NT>(R.v, reinterpret_cast<const T*>(a.fv) + ((size_t)t0 * H + h) * a.geo.V + vcol0,
+                                    (size_t)H * a.geo.V, c);
+    const int tid = threadIdx.x;
+    if (tid < 64) {
+        const bool in = tid < c;
+        const int64_t i = (t0 + (in ? tid : 0)) * H + h;
+        R.g = in ? a.fg[i] : 0.f;
+        R.beta = in ? a.fbeta[i] : 0.f;
+    }
+}
+
+// kL2: q and k arrive raw and their rows are L2-normalised in registers before staging.
+template <typename T, int K, int RT, bool kL2>
+__global__ __launch_bounds__(RT * 4) void k_fused(RecurArgs a) {
+    using C = RCfg<T, K, RT>;
+    using F = FCfg<T, K, RT>;
+    constexpr int NW = C::NW;
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    ChunkLds<T, K, RT> L;
+    L.sQ = reinterpret_cast<T*>(smem + C::off_q);
+    L.sK = reinterpret_cast<T*>(smem + C::off_k);
+    L.sW = reinterpret_cast<T*>(smem + C::off_w);
+    L.sU = reinterpret_cast<T*>(smem + C::off_u);
+    L.sPm = reinterpret_cast<T*>(smem + C::off_pm);
+    L.sGam = reinterpret_cast<float*>(smem + C::off_gam);
+    T* sV = reinterpret_cast<T*>(smem + F::off_v);
+    float* sA = reinterpret_cast<float*>(smem + F::off_a);
+    float* sT = reinterpret_cast<float*>(smem + F::off_t);
+    float* sBeta = reinterpret_cast<float*>(smem + F::off_beta);
+
+    const Geo& geo = a.geo;
+    const int64_t gs = blockIdx.x;
+    const int h = blockIdx.y;
+    const int vt = blockIdx.z;
+    const int V = geo.V;
+    SegLoc sg;
+    if (!locate_seg(geo, gs, sg)) return;
+    const int tid = threadIdx.x;
+    const int wave = wave_id(), lane = tid & 63, ln = lane & 15, gq = lane >> 4;
+    const int row = vt * RT + wave * 16 + ln;
+    const size_t VK = (size_t)V * K;
+    const int vcol0 = vt * RT;
+
+    f32x4 accS[K / 16];
+    if (a.s0) {
+        load_state<K>(accS, a.s0 + ((size_t)sg.n * geo.H + h) * VK, row);
+    } else {
+#pragma unroll
+        for (int kt = 0; kt < K / 16; ++kt) accS[kt] = zero4();
+    }
+#pragma unroll
+    for (int kt = 0; kt < K / 16; ++kt) hold(accS[kt]);
+    const int cbeg = sg.c0, cend = sg.c1;
+    if (cbeg < cend) {
+        typedef typename Pack4<T>::type PV;
+        PV okeep[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) okeep[i] = PV{};
+        FusedRegs<T, K, RT> R;
+        fused_fetch(R, a, sg.bos + (int64_t)cbeg * 64, min(64, sg.len - cbeg * 64), h, vcol0);
+        // the strictly upper blocks of T stay zero for every chunk
+        tri_zero_upper64(sT);
+        for (int ci = cbeg; ci < cend; ++ci) {
+            const int64_t t0 = sg.bos + (int64_t)ci * 64;
+            const int c = min(64, sg.len - ci * 64);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) hold(okeep[i]);
+            lds_sync();  // the previous chunk's LDS reads are done
+            // ---- stage: q, k (fragment order), this tile's v columns, gate cumsum, beta ----
+            if constexpr (kL2) {
+                l2norm_rows<T, K>(R.q);
+                l2norm_rows<T, K>(R.k);
+            }
+            put_tile_fo<T, K, C::IQ, C::NT>(L.sQ, C::LD, R.q);
+            put_tile_fo<T, K, C::IQ, C::NT>(L.sK, C::LD, R.k);
+            put_tile<T, RT, F::IV, C::NT>(sV, F::LDV, R.v);
+            if (wave == 0) {
+                const float x = wave_prefix_sum(R.g);  // rows past the chunk end carry the total
+                L.sGam[lane] = x;
+                sBeta[lane] = R.beta;
+            }
+            // the next chunk's operands (the last chunk again past the end)
+            {
+                const int cn = min(ci + 1, cend - 1);
+                fused_fetch(R, a, sg.bos + (int64_t)cn * 64, min(64, sg.len - cn * 64), h, vcol0);
+            }
+            lds_sync();
+            // ---- A = strict_lower(diag(beta) (e^{gam_r - gam_j} K K^T)): lower 16x16 tiles ----
+            {
+                constexpr int NTT = (10 + NW - 1) / NW;
+                f32x4 acc[NTT];
+                int ti[NTT], tj[NTT];
+                bool on[NTT];
+#pragma unroll
+                for (int m = 0; m < NTT; ++m) {
+                    const int idx = wave + NW * m;
+                    on[m] = idx < 10;
+                    ti[m] = tri_row(min(idx, 9));
+                    tj[m] = tri_col(min(idx, 9));
+                    acc[m] = zero4();
+                }
+#pragma unroll
+                for (int kb = 0; kb < K / 32; ++kb) {
+                    Frag<T> fa[NTT], fb[NTT];
+#pragma unroll
+                    for (int m = 0; m < NTT; ++m) {
+                        frag_row_fo(fa[m], L.sK, C::LD, tj[m] * 16 + ln, kb * 32);
+                        frag_row_fo(fb[m], L.sK, C::LD, ti[m] * 16 + ln, kb * 32);
+                    }
+#pragma unroll
+                    for (int m = 0; m < NTT; ++m) mma(acc[m], fa[m], fb[m]);
+                }
+                // acc[m][i] = k_j . k_r, j = tj*16 + gq*4 + i, r = ti*16 + ln
+#pragma unroll
+                for (int m = 0; m < NTT; ++m) {
+                    if (on[m]) {
+                        const int r = ti[m] * 16 + ln;
+                        const float gr = L.sGam[r], br = sBeta[r];
+                        const f32x4 gj = *reinterpret_cast<const f32x4*>(L.sGam + tj[m] * 16 + gq * 4);
+                        f32x4 val;
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const int j = tj[m] * 16 + gq * 4 + i;
+                            val[i] = (j < r) ? br * fast_exp(gr - gj[i]) * acc[m][i] : 0.f;
+                        }
+                        *reinterpret_cast<f32x4*>(sA + r * kLdA + tj[m] * 16 + gq * 4) = val;
+                    }
+                }
+            }
+            lds_sync();
+            // ---- T = (I + A)^-1 (waves 0-3) ----
+            tri_inverse64(sA, sT);
+            // ---- W = T diag(beta e^gam) K (row tile rw), U = T diag(beta) V (row tile ru) --------
+            {
+                const bool doW = NW == 4 || wave < 4;
+                const bool doU = NW == 4 || wave >= 4;
+                const int rt = wave & 3;
+                Frag<T> aw[2], au[2];
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb) {
+                    Frag<float> tf;
+                    frag_row(tf, sT, kLdA, rt * 16 + ln, kb * 32);
+                    const f32x4 b0 = *reinterpret_cast<const f32x4*>(sBeta + kb * 32 + gq * 4);
+                    const f32x4 b1 = *reinterpret_cast<const f32x4*>(sBeta + kb * 32 + 16 + gq * 4);
+                    const f32x4 g0 = *reinterpret_cast<const f32x4*>(L.sGam + kb * 32 + gq * 4);
+                    const f32x4 g1 = *reinterpret_cast<const f32x4*>(L.sGam + kb * 32 + 16 + gq * 4);
+                    float fw[8], fu[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const float tv = e < 4 ? tf.lo[e] : tf.hi[e - 4];
+                        const float bj = e < 4 ? b0[e] : b1[e - 4];
+                        const float gjv = e < 4 ? g0[e] : g1[e - 4];
+                        fu[e] = tv * bj;
+                        fw[e] = fu[e] * fast_exp(gjv);
+                    }
+                    aw[kb].v = u32x4{pack_bf2(fw[0], fw[1]), pack_bf2(fw[2], fw[3]), pack_bf2(fw[4], fw[5]),
+                                     pack_bf2(fw[6], fw[7])};
+                    au[kb].v = u32x4{pack_bf2(fu[0], fu[1]), pack_bf2(fu[2], fu[3]), pack_bf2(fu[4], fu[5]),
+                                     pack_bf2(fu[6], fu[7])};
+                }
+                const int nkb = (rt >> 1) + 1;  // T[r][j] = 0 for j > r
+                const int orow = rt * 16 + ln;
+                if (doW) {
+                    // transposed tiles: accw[ct][i] = W[orow][ct*16 + gq*4 + i]
+                    f32x4 accw[K / 16];
+#pragma unroll
+                    for (int ct = 0; ct < K / 16; ++ct) {
+                        accw[ct] = zero4();
+#pragma unroll
+                        for (int kb = 0; kb < 2; ++kb) {
+                            if (kb < nkb) {
+                                Frag<T> b;
+                                frag_col_fo(b, L.sK, C::LD, ct * 16 + ln, kb * 32);  // K^T row ct*16+ln, slots j
+                                mma(accw[ct], b, aw[kb]);
+                            }
+                        }
+                    }
+#pragma unroll
+                    for (int ct = 0; ct < K / 16; ++ct) store4(L.sW + orow * C::LD + frag_pos(ct * 16 + gq * 4), accw[ct]);
+                }
+                if (doU) {
+                    f32x4 accu[RT / 16];
+#pragma unroll
+                    for (int ct = 0; ct < RT / 16; ++ct) {
+                        accu[ct] = zero4();
+#pragma unroll
+                        for (int kb = 0; kb < 2; ++kb) {
+                            if (kb < nkb) {
+                                Frag<T> b;
+                                frag_col(b, sV, F::LDV, ct * 16 + ln, kb * 32);  // V^T row ct*16+ln, slots j
+                                mma(accu[ct], b, au[kb]);
+                            }
+                        }
+                    }
+#pragma unroll
+                    for (int ct = 0; ct < RT / 16; ++ct) store4(L.sU + orow * C::LDU + ct * 16 + gq * 4, accu[ct]);
+                }
+            }
+            lds_sync();
+            // ---- the recurrence step on the staged tiles ----
+            Frag<T> sf[K / 32];
+            f32x4 accD[4], accO[4];
+            chunk_part1<T, K, RT, true, true>(L, accS, sf, accD, accO);
+            lds_sync();  // P tiles complete
+            chunk_part2<T, K, RT, true, true>(a, L, accS, accD, accO, t0, c, h, vcol0, okeep);
+        }
+    }
+    if (a.sT) store_state<K>(accS, a.sT + ((size_t)sg.n * geo.H + h) * VK, row);
+}
+
+template <typename T, int K, int RT>
+hipError_t launch_fused_t(const RecurArgs& a, int64_t nseqs, int vtiles, hipStream_t st) {
+    using F = FCfg<T, K, RT>;
+    static_assert(F::total <= 160 * 1024, "LDS budget");
+    auto kern = a.q_l2 ? k_fused<T, K, RT, true> : k_fused<T, K, RT, false>;
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, F::total);
+    if (e != hipSuccess) return e;
+    dim3 grid((unsigned)nseqs, (unsigned)a.geo.H, (unsigned)vtiles);
+    hipLaunchKernelGGL(kern, grid, dim3(RT * 4), F::total, st, a);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // Varlen tables from the device cu_seqlens (one workgroup). Lengths and offsets are
 // clamped into [0, Ttot], so a bad cu_seqlens can never send a later kernel out of
 // bounds; entries the host sized but the device data does not fill stay marked unused.
@@ -948,6 +1223,17 @@ hipError_t launch_recur(const RecurArgs& a, int dtype, int mode, int64_t nsegs_g
         GDN_RECUR_CASE(float, 128, 128)
     }
 #undef GDN_RECUR_CASE
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_fused(const RecurArgs& a, int dtype, int64_t nseqs, int vtiles, hipStream_t st) {
+    if (nseqs == 0) return hipSuccess;
+    if (dtype != 0) return hipErrorInvalidValue;  // bf16 only (fp32 tiles exceed the LDS)
+    const int K = a.geo.K;
+    const int RT = recur_rows(a.geo.V, K);
+    if (K == 64 && RT == 64) return launch_fused_t<bf16_t, 64, 64>(a, nseqs, vtiles, st);
+    if (K == 128 && RT == 64) return launch_fused_t<bf16_t, 128, 64>(a, nseqs, vtiles, st);
+    if (K == 128 && RT == 128) return launch_fused_t<bf16_t, 128, 128>(a, nseqs, vtiles, st);
     return hipErrorInvalidValue;
 }
 

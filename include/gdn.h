@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 8
+#define GDN_ABI_VERSION 9
 
 typedef enum gdn_status {
     GDN_OK = 0,
@@ -124,6 +124,16 @@ typedef enum gdn_cp_mode {
  * rounding. */
 #define GDN_FLAG_BWD_ADJOINT_PASS 8
 
+/* The fully fused forward: with CP off, bf16 inputs and no kept intermediates, gdn_chunk_fwd can run
+ * the intra-chunk step and the recurrence in one kernel (one workgroup per sequence, head and row
+ * tile, walking the chunks in order), so w, u and the gate cumsum never go to memory: 1,032 instead
+ * of 2,320 bytes per token-head at K = V = 128. The pages name the fully fused design as the one
+ * with less memory I/O at large batch (announcement post, on the two-kernel split). The plan picks it
+ * where it measures faster (gdn_plan_info.fused_fwd); GDN_FLAG_FWD_FUSED asks for it wherever it is
+ * supported, GDN_FLAG_FWD_SPLIT never. Same results within rounding. */
+#define GDN_FLAG_FWD_FUSED 16
+#define GDN_FLAG_FWD_SPLIT 32
+
 /* Problem descriptor. Zero-initialise, then fill. */
 typedef struct gdn_desc {
     int64_t B, T, H, K, V;          /* batch, tokens per row (packed total if varlen), heads, key dim, value dim */
@@ -161,6 +171,8 @@ typedef struct gdn_plan_info {
     int64_t total_segments;         /* sum over sequences of sub-sequence counts */
     size_t fwd_workspace_bytes;
     size_t bwd_workspace_bytes;
+    int32_t fused_fwd;              /* 1 if gdn_chunk_fwd runs the fully fused forward */
+    int32_t reserved_out[3];
 } gdn_plan_info;
 
 /* ABI version (GDN_ABI_VERSION of the built library). */

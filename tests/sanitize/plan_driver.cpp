@@ -83,7 +83,7 @@ int main() {
         d.cu_seqlens_host = cu.data();
         d.cp_mode = trial % 6;
         d.seg_chunks = trial % 3 == 0 ? 16 + trial % 40 : 0;
-        d.flags = trial % 8 == 0 ? GDN_FLAG_QK_L2NORM : 0;
+        d.flags = (trial % 8 == 0 ? GDN_FLAG_QK_L2NORM : 0) | (trial % 5 == 0 ? GDN_FLAG_FWD_FUSED : 0);
         gdn_plan_info p;
         EXPECT(gdn_plan(&d, &p) == GDN_OK);
         ++plans;

@@ -12,6 +12,7 @@ hipError_t launch_intra(const IntraArgs&, int, int, hipStream_t) { ++g_launches;
 hipError_t launch_decide(const DecideArgs&, hipStream_t) { ++g_launches; return hipSuccess; }
 hipError_t launch_recur(const RecurArgs&, int, int, int64_t, int, hipStream_t) { ++g_launches; return hipSuccess; }
 hipError_t launch_scan(const ScanArgs&, int, hipStream_t) { ++g_launches; return hipSuccess; }
+hipError_t launch_fused(const RecurArgs&, int, int64_t, int, hipStream_t) { ++g_launches; return hipSuccess; }
 hipError_t launch_reverse(const RevArgs&, int, int, int64_t, int, hipStream_t) { ++g_launches; return hipSuccess; }
 hipError_t launch_bwd_chunk(const BwdChunkArgs&, int, int, hipStream_t) { ++g_launches; return hipSuccess; }
 hipError_t launch_decode(const DecodeArgs&, int, int, int, hipStream_t) { ++g_launches; return hipSuccess; }

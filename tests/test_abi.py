@@ -38,7 +38,7 @@ def test_exports_every_declared_symbol(lib):
     assert set(declared) == set(_abi.EXPORTS)
     for name in declared:
         assert hasattr(lib, name), name
-    assert lib.gdn_abi_version() == _abi.GDN_ABI_VERSION == 8
+    assert lib.gdn_abi_version() == _abi.GDN_ABI_VERSION == 9
 
 
 def test_status_strings(lib):
@@ -157,7 +157,7 @@ def test_argument_errors(lib):
     d2.c.reserved[3] = 1
     assert lib.gdn_plan(d2.ref, ctypes.byref(out)) == 1
     # unknown flag bits
-    for bad_flag in (16, 32, 1 << 30, -1):
+    for bad_flag in (64, 128, 1 << 30, -1):
         d2 = desc()
         d2.c.flags = bad_flag
         assert lib.gdn_plan(d2.ref, ctypes.byref(out)) == 1, bad_flag
@@ -257,3 +257,23 @@ def test_qk_l2norm_workspace(kw):
     # the Python keyword sets the same bit
     assert gdn.gdn_plan(desc(qk_l2norm=True, **kw)) == l2
 
+
+
+def test_fused_forward_plan():
+    """The fully fused forward: chosen without CP in bf16 when the recurrence needs at least two
+    rounds of workgroups (N*H*v_tiles >= 2 * slots), never with CP, fp32 or kept intermediates;
+    the flags force either path where it is possible."""
+    # 256 CUs, K = V = 128: one recurrence workgroup per CU and sequence-head
+    assert plan(B=8, H=64, T=4096)["fused_fwd"] == 1          # 512 sequence-heads: two rounds
+    assert plan(B=8, H=32, T=4096)["fused_fwd"] == 0          # 256: one round
+    assert plan(B=1, H=16, T=32768)["fused_fwd"] == 0         # CP on
+    assert plan(B=8, H=64, T=4096, dtype=torch.float32)["fused_fwd"] == 0
+    assert plan(B=8, H=64, T=4096, flags=gdn.GDN_FLAG_KEEP_FORWARD)["fused_fwd"] == 0
+    assert plan(B=8, H=32, T=4096, flags=gdn.GDN_FLAG_FWD_FUSED)["fused_fwd"] == 1
+    assert plan(B=8, H=64, T=4096, flags=gdn.GDN_FLAG_FWD_SPLIT)["fused_fwd"] == 0
+    assert plan(B=1, H=16, T=32768, flags=gdn.GDN_FLAG_FWD_FUSED)["fused_fwd"] == 0  # CP on: split
+    # K = V = 64: two recurrence workgroups per CU
+    assert plan(B=16, H=64, T=2048, K=64, V=64)["fused_fwd"] == 1   # 1024 >= 2 * 512
+    assert plan(B=16, H=32, T=2048, K=64, V=64)["fused_fwd"] == 0
+    with pytest.raises(gdn.GdnError):
+        plan(flags=gdn.GDN_FLAG_FWD_FUSED | gdn.GDN_FLAG_FWD_SPLIT)
