@@ -342,6 +342,8 @@ def main():
     ap.add_argument("--cp", default=None, help="override the workload's CP mode (auto/off/on/exact/warmup)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-fused-leg", action="store_true", help="skip the fused-forward comparison")
+    ap.add_argument("--only-step", action="store_true",
+                    help="time the step only (no flushed calls, no extra legs, no CPU baseline): for profilers")
     ap.add_argument("--flushed-calls", type=int, default=50,
                     help="calls timed one by one after a 1 GiB cache flush (median and minimum)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -449,6 +451,18 @@ def main():
     for _ in range(args.warmup):
         step()
     ms = timed(step, args.steps)
+    if args.only_step:
+        gdn.gdn_profile_enable(True)
+        for _ in range(args.steps):
+            step()
+        torch.cuda.synchronize()
+        kt = gdn.gdn_profile_read()
+        gdn.gdn_profile_enable(False)
+        print(json.dumps({"metric": metric_name(w, B, T, H, lengths), "ms_per_step": round(ms, 4),
+                          "steps": args.steps, "warmup": args.warmup, "config": {"workload": w.name},
+                          "kernels_us_per_step": {n: round(1e3 * t / args.steps, 2) for n, (c, t) in kt.items()}}),
+              flush=True)
+        return
     ms_fwd = timed(fwd, args.steps) if do_fwd else None
     ms_bwd = timed(bwd, args.steps) if do_bwd else None
     fl_step = flushed(step, args.flushed_calls)

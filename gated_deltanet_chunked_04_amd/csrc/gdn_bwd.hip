@@ -25,6 +25,14 @@ namespace {
 template <typename T> struct BPad;
 template <> struct BPad<bf16_t> { static constexpr int row = 8; };
 template <> struct BPad<float> { static constexpr int row = 4; };
+// The [64][K] tiles that k_bwd_chunk reads transposed most (K, Q, dW) and its 64x64 matrices:
+// in bf16 at K = V = 128 a row stride of K + 16 elements (144; 80 for 64 columns) halves the cost
+// of the transpose reads of fragment-order tiles against K + 8, whose rows collide in the LDS banks
+// on every such read (measured with the LDS bank-conflict counters: k_bwd_chunk 531 -> 485 us at
+// the 32K workload). The LDS budget leaves the other tiles at K + 8.
+template <typename T> struct BPadK;
+template <> struct BPadK<bf16_t> { static constexpr int row = 16; };
+template <> struct BPadK<float> { static constexpr int row = 4; };
 
 // ---------------------------------------------------------------------------
 // Reverse adjoint recurrence. RT adjoint rows (value rows, or V + M-hat rows in the
@@ -561,13 +569,16 @@ constexpr WyPlace place_wy(int h0, int h1, int tail, int vmat, int xmat) {
 template <typename T, int K, int V>
 struct BCfg {
     static constexpr int VEC = Elem<T>::kVec;
-    static constexpr int LDK = K + BPad<T>::row;
+    static constexpr int LDK = (K == 128 && V == 128) ? K + BPadK<T>::row : K + BPad<T>::row;
+    static constexpr int LDS = K + BPad<T>::row;
     static constexpr int LDV = V + BPad<T>::row;
-    static constexpr int LDX = 64 + BPad<T>::row;
+    static constexpr int LDX = (K == 128 && V == 128) ? 64 + BPadK<T>::row : 64 + BPad<T>::row;
     static constexpr int kMK = 64 * LDK * (int)sizeof(T);  // one [64][K] matrix
+    static constexpr int LDU = LDV;  // dDelta
     static constexpr int kMV = 64 * LDV * (int)sizeof(T);  // one [64][V] matrix
+    static constexpr int kMU = 64 * LDU * (int)sizeof(T);  // the dDelta tile
     static constexpr int kMX = 64 * LDX * (int)sizeof(T);  // one [64][64] matrix
-    static constexpr int kSt = V * LDK * (int)sizeof(T);   // one [V][K] state
+    static constexpr int kSt = V * LDS * (int)sizeof(T);   // one [V][K] state
     static constexpr int off_k = 0;
     // state side
     static constexpr int off_s = kMK;
@@ -577,7 +588,7 @@ struct BCfg {
     static constexpr int off_dl = off_d + kMV;   // Delta, then the L .* dP exchange
     static constexpr int off_x = off_dl;
     static constexpr int off_dd = off_dl + kMV;  // dDelta (the WY side's dU)
-    static constexpr int end_state = off_dd + kMV;
+    static constexpr int end_state = off_dd + kMU;
     // WY side
     static constexpr int off_dw = off_s;
     static constexpr WyPlace wy = place_wy(off_dw + kMK, off_dd, end_state, kMV, kMX);
@@ -834,7 +845,7 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(BwdChunkArgs a) {
         // scale * dO and Delta are read as row fragments only: rows in fragment order
         put_tile_fo<T, V, C::NV, NT>(sD, C::LDV, R.d, a.scale);
         put_tile_fo<T, V, C::NV, NT>(sDl, C::LDV, R.dl);
-        if constexpr (!kCarry) put_tile_fo<T, V, C::NV, NT>(sdU, C::LDV, R.dd);
+        if constexpr (!kCarry) put_tile_fo<T, V, C::NV, NT>(sdU, C::LDU, R.dd);
         if (tid < 64) {
             sGam[tid] = R.gam;
             sBeta[tid] = R.beta;
@@ -912,12 +923,12 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(BwdChunkArgs a) {
         // S and G are fetched last in the previous task and staged only here, so that their
         // registers are free over that task's WY side and their loads land behind the products above
         // (kCarry: G from its accumulators, rows v = this wave's 16 value rows)
-        put_tile<T, K, C::NS, NT>(sS, C::LDK, R.s);
+        put_tile<T, K, C::NS, NT>(sS, C::LDS, R.s);
         if constexpr (kCarry) {
 #pragma unroll
-            for (int kt = 0; kt < K / 16; ++kt) store4(sG + vrow * C::LDK + kt * 16 + gq * 4, accG[kt]);
+            for (int kt = 0; kt < K / 16; ++kt) store4(sG + vrow * C::LDS + kt * 16 + gq * 4, accG[kt]);
         } else {
-            put_tile<T, K, C::NS, NT>(sG, C::LDK, R.g);
+            put_tile<T, K, C::NS, NT>(sG, C::LDS, R.g);
         }
         lds_sync();
         // kCarry: dDelta^T tiles [v = this wave's rows][j] (stored after the next barrier, once
@@ -976,7 +987,7 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(BwdChunkArgs a) {
                 const int vv = e / (K / VEC), kk = (e % (K / VEC)) * VEC;
 #pragma unroll
                 for (int i = 0; i < VEC; i += 4)
-                    gs += dot4(ld4(sG + vv * C::LDK + kk + i), ld4(sS + vv * C::LDK + kk + i));
+                    gs += dot4(ld4(sG + vv * C::LDS + kk + i), ld4(sS + vv * C::LDS + kk + i));
             }
         }
         // ---- dKt^T[k][r] = sum_v G[v][k] Delta[r][v]  (rows k of this half, cols r) ------------
@@ -992,7 +1003,7 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(BwdChunkArgs a) {
                 Frag<T> fg[KH];
 #pragma unroll
                 for (int i = 0; i < KH; ++i)
-                    frag_col(fg[i], sG, C::LDK, (hf * KH + i) * 16 + ln, vb * 32);  // G^T row k, slots v
+                    frag_col(fg[i], sG, C::LDS, (hf * KH + i) * 16 + ln, vb * 32);  // G^T row k, slots v
 #pragma unroll
                 for (int i = 0; i < KH; ++i) mma(dKT[i], fg[i], dtr[vb]);
             }
@@ -1041,7 +1052,7 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(BwdChunkArgs a) {
         if constexpr (kCarry) {
             // dDelta over P (every wave's reads of P are done): rows j, this wave's value columns
 #pragma unroll
-            for (int jt = 0; jt < 4; ++jt) store4(sdU + (jt * 16 + ln) * C::LDV + frag_pos(vrow - ln + gq * 4), ddT[jt]);
+            for (int jt = 0; jt < 4; ++jt) store4(sdU + (jt * 16 + ln) * C::LDU + frag_pos(vrow - ln + gq * 4), ddT[jt]);
         }
         // exchange L .* dP: sX[query r][key j]
 #pragma unroll
@@ -1075,7 +1086,7 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(BwdChunkArgs a) {
             for (int j = 0; j < KW; ++j)
 #pragma unroll
                 for (int vb = 0; vb < V / 32; ++vb)
-                    frag_col(sfc[j][vb], sS, C::LDK, k0 + j * 16 + ln, vb * 32);  // S^T row k, slots v
+                    frag_col(sfc[j][vb], sS, C::LDS, k0 + j * 16 + ln, vb * 32);  // S^T row k, slots v
 #pragma unroll
             for (int m = 0; m < 2; ++m) {
                 const int rr = 2 * hf + m;
@@ -1084,7 +1095,7 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(BwdChunkArgs a) {
                 for (int vb = 0; vb < V / 32; ++vb) {
                     frag_row_fo(fdo[vb], sD, C::LDV, rr * 16 + ln, vb * 32);
                     Frag<T> f;
-                    frag_row_fo(f, sdU, C::LDV, rr * 16 + ln, vb * 32);
+                    frag_row_fo(f, sdU, C::LDU, rr * 16 + ln, vb * 32);
                     fdd[vb] = neg(f);
                 }
 #pragma unroll
@@ -1169,7 +1180,7 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(BwdChunkArgs a) {
 #pragma unroll
             for (int kb = 0; kb < K / 32; ++kb) frag_row_fo(wf[kb], sdW, C::LDK, ra, kb * 32);
 #pragma unroll
-            for (int vb = 0; vb < V / 32; ++vb) frag_row_fo(uf[vb], sdU, C::LDV, ra, vb * 32);
+            for (int vb = 0; vb < V / 32; ++vb) frag_row_fo(uf[vb], sdU, C::LDU, ra, vb * 32);
             // both b tiles (the mask below zeroes b >= a)
             f32x4 x[2], y[2];
 #pragma unroll
@@ -1332,7 +1343,7 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(BwdChunkArgs a) {
 #pragma unroll
                 for (int xb = 0; xb < 2; ++xb) {
                     Frag<T> fu;
-                    frag_col_fo(fu, sdU, C::LDV, vt * 16 + ln, xb * 32);  // dU^T row v, slots x
+                    frag_col_fo(fu, sdU, C::LDU, vt * 16 + ln, xb * 32);  // dU^T row v, slots x
                     mma(bv, fu, ta[xb]);
                 }
                 dbeta_row += dot4(bv, ld4(sV + ra * C::LDV + frag_pos(vt * 16 + gq * 4)));
