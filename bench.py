@@ -47,7 +47,7 @@ def metric_name(w, B, T, H, lengths):
     return f"{METRIC_BASE}, B={B} H={H} T={t}"
 
 
-def algorithmic_counts(B, T, H, K, V, esize, N, nseg_total, lengths=None):
+def algorithmic_counts(B, T, H, K, V, esize, N, nseg_total, lengths=None, carried=False):
     """Algorithmic bytes and flops per kernel for the whole workload.
 
     Bytes count each operand a kernel must read once and each result it writes once
@@ -63,6 +63,8 @@ def algorithmic_counts(B, T, H, K, V, esize, N, nseg_total, lengths=None):
       bwd_chunk    reads q, k, v, dO, Delta, dDelta, T, gate cumsum, beta and the chunk's
                    state and adjoint; writes dq, dk, dv, dg, dbeta
                                                   (2K+4V+64) e + 8 + (2K+V) e + 8 + 2 V K e / 64
+                   carrying the adjoint it reads neither dDelta nor the adjoints
+                                                  (2K+3V+64) e + 8 + (2K+V) e + 8 + V K e / 64
     Flops per chunk of c tokens (C=64; triangular products at half):
       forward   intra: c(c-1)K + c(c-1)(c-2)/3 + c(c-1)(K+V);  recur: 3*2cKV + c(c+1)(K+V)
       backward  the reverse-mode products of the chunk map: dQt, dDelta (both terms), dKt,
@@ -81,7 +83,9 @@ def algorithmic_counts(B, T, H, K, V, esize, N, nseg_total, lengths=None):
         recur_out=th * ((3 * K + 2 * V) * esize + 4) + N * H * V * K * 4 * 2 + max(nseg_total - N, 0) * H * V * K * 4,
         recur_states=th * ((2 * K + 2 * V) * esize + 4) + chunks * H * st,
         bwd_reverse=th * ((3 * K + 2 * V) * esize + 4) + chunks * H * st,
-        bwd_chunk=th * ((2 * K + 4 * V + 64) * esize + 8 + (2 * K + V) * esize + 8) + 2 * chunks * H * st,
+        bwd_chunk=(th * ((2 * K + 3 * V + 64) * esize + 8 + (2 * K + V) * esize + 8) + chunks * H * st
+                   if carried else
+                   th * ((2 * K + 4 * V + 64) * esize + 8 + (2 * K + V) * esize + 8) + 2 * chunks * H * st),
     )
     f_intra = f_recur = f_bwd = 0.0
     for n in lens:
@@ -491,7 +495,8 @@ def main():
     del flush_buf
 
     esize = 2 if q.dtype == torch.bfloat16 else 4
-    counts = algorithmic_counts(B, T, H, K, V, esize, N, plan["total_segments"], lengths)
+    counts = algorithmic_counts(B, T, H, K, V, esize, N, plan["total_segments"], lengths,
+                                carried=bool(plan["bwd_carried"]))
     tokens = counts["tokens"]
     alg = counts["alg_bytes"]
     flops_step = (counts["flops"]["fwd"] if do_fwd else 0) + (counts["flops"]["bwd"] if do_bwd else 0)

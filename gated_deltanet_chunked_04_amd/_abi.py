@@ -48,7 +48,8 @@ class GdnPlanInfo(ctypes.Structure):
         ("max_len", ctypes.c_int64), ("total_chunks", ctypes.c_int64),
         ("total_segments", ctypes.c_int64),
         ("fwd_workspace_bytes", ctypes.c_size_t), ("bwd_workspace_bytes", ctypes.c_size_t),
-        ("fused_fwd", ctypes.c_int32), ("reserved_out", ctypes.c_int32 * 3),
+        ("fused_fwd", ctypes.c_int32), ("bwd_carried", ctypes.c_int32),
+        ("reserved_out", ctypes.c_int32 * 2),
     ]
 
 

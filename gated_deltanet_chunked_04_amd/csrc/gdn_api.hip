@@ -228,6 +228,14 @@ gdn_status make_plan(const gdn_desc* d, Plan& p) {
     return GDN_OK;
 }
 
+// The per-chunk backward kernel carries the adjoint itself (one workgroup per sub-sequence and
+// head, walking its chunks in reverse) where the sub-sequences are balanced: with CP, or uniform
+// batches. Then no adjoint pass runs.
+static bool bwd_carries(const gdn_desc* d, const Plan& p) {
+    return d->V == 128 && d->dtype == GDN_DTYPE_BF16 && (p.cp_on || !p.varlen) &&
+           !(d->flags & GDN_FLAG_BWD_ADJOINT_PASS) && p.total_segs * d->H <= INT32_MAX;
+}
+
 Geo make_geo(const gdn_desc* d, const Plan& p, unsigned char* ws) {
     Geo g;
     memset(&g, 0, sizeof(g));
@@ -505,6 +513,7 @@ gdn_status gdn_plan(const gdn_desc* desc, gdn_plan_info* out) {
     out->fwd_workspace_bytes = p.fwd_bytes;
     out->bwd_workspace_bytes = p.bwd_bytes;
     out->fused_fwd = p.fused;
+    out->bwd_carried = bwd_carries(desc, p) ? 1 : 0;
     return GDN_OK;
 }
 
@@ -686,11 +695,8 @@ gdn_status gdn_chunk_bwd(const gdn_desc* desc, const void* q, const void* k, con
         else s = run_decide(desc, p, ws, modes, bwin, st, 0, modes_r, bwin_r);
         if (s != GDN_OK) return s;
     }
-    // The per-chunk kernel carries the adjoint itself (one workgroup per sub-sequence and head,
-    // walking its chunks in reverse) where the sub-sequences are balanced: with CP, or uniform
-    // batches; then no adjoint pass runs and only the reverse CP (if any) goes to the side stream.
-    const bool carry = desc->V == 128 && desc->dtype == GDN_DTYPE_BF16 && (p.cp_on || !p.varlen) &&
-                       !(desc->flags & GDN_FLAG_BWD_ADJOINT_PASS) && p.total_segs * desc->H <= INT32_MAX;
+    // With the carried adjoint only the reverse CP (if any) goes to the side stream.
+    const bool carry = bwd_carries(desc, p);
     const bool fork = p.cp_on || !carry;
     std::unique_lock<std::mutex> side_lock(side_mutex(), std::defer_lock);
     SideStream side;

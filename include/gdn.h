@@ -172,7 +172,9 @@ typedef struct gdn_plan_info {
     size_t fwd_workspace_bytes;
     size_t bwd_workspace_bytes;
     int32_t fused_fwd;              /* 1 if gdn_chunk_fwd runs the fully fused forward */
-    int32_t reserved_out[3];
+    int32_t bwd_carried;            /* 1 if gdn_chunk_bwd's per-chunk kernel carries the adjoint
+                                       (no separate adjoint pass) */
+    int32_t reserved_out[2];
 } gdn_plan_info;
 
 /* ABI version (GDN_ABI_VERSION of the built library). */

@@ -277,3 +277,13 @@ def test_fused_forward_plan():
     assert plan(B=16, H=32, T=2048, K=64, V=64)["fused_fwd"] == 0
     with pytest.raises(gdn.GdnError):
         plan(flags=gdn.GDN_FLAG_FWD_FUSED | gdn.GDN_FLAG_FWD_SPLIT)
+
+
+def test_carried_backward_plan():
+    """The backward's per-chunk kernel carries the adjoint (no separate adjoint pass) in bf16 at
+    V = 128 for uniform batches and CP plans, unless the caller asks for the adjoint pass."""
+    assert plan(B=1, H=16, T=32768)["bwd_carried"] == 1                   # CP on
+    assert plan(B=8, H=32, T=4096)["bwd_carried"] == 1                    # uniform batch
+    assert plan(B=1, H=16, T=32768, dtype=torch.float32)["bwd_carried"] == 0
+    assert plan(B=1, H=16, T=32768, K=64, V=64)["bwd_carried"] == 0
+    assert plan(B=1, H=16, T=32768, flags=gdn.GDN_FLAG_BWD_ADJOINT_PASS)["bwd_carried"] == 0
