@@ -55,6 +55,7 @@ struct Plan {
     int32_t cus = 256;   // compute units (desc->num_cus, else the device's)
     int32_t bwd_ok = 1;  // fp32 backward supports K = V = 64 only (LDS)
     int32_t fused = 0;   // the forward runs fully fused (no CP, bf16, no kept intermediates)
+    int32_t carry = 0;   // the backward's per-chunk kernel carries the adjoint (no adjoint pass)
 };
 
 int query_cus() {
@@ -214,8 +215,15 @@ gdn_status make_plan(const gdn_desc* d, Plan& p) {
         p.o_seginit_r = take((size_t)p.total_segs * H * V * K * 4);
         p.o_prep_r = take((size_t)p.total_segs * H * (V + K) * K * 4);
     }
-    p.o_gst = take((size_t)p.total_chunks * H * V * K * p.esize);
-    p.o_ddl = take(T * H * V * p.esize);
+    // The per-chunk backward kernel carries the adjoint itself (one workgroup per sub-sequence and
+    // head, walking its chunks in reverse) where the sub-sequences are balanced: with CP, or uniform
+    // batches. Then no adjoint pass runs, and the chunk-exit adjoints and dDelta take no space.
+    p.carry = d->V == 128 && d->dtype == GDN_DTYPE_BF16 && (p.cp_on || !p.varlen) &&
+              !(d->flags & GDN_FLAG_BWD_ADJOINT_PASS) && p.total_segs * d->H <= INT32_MAX;
+    if (!p.carry) {
+        p.o_gst = take((size_t)p.total_chunks * H * V * K * p.esize);
+        p.o_ddl = take(T * H * V * p.esize);
+    }
     p.bwd_bytes = std::max<size_t>(off, kAlign);
     p.bwd_ok = (d->dtype == GDN_DTYPE_BF16) || (d->K == 64 && d->V == 64);
     // The fully fused forward: possible without CP, in bf16, when nothing is kept for the backward;
@@ -226,14 +234,6 @@ gdn_status make_plan(const gdn_desc* d, Plan& p) {
     else if (d->flags & GDN_FLAG_FWD_SPLIT) p.fused = 0;
     else p.fused = fusable && units >= 2 * target;
     return GDN_OK;
-}
-
-// The per-chunk backward kernel carries the adjoint itself (one workgroup per sub-sequence and
-// head, walking its chunks in reverse) where the sub-sequences are balanced: with CP, or uniform
-// batches. Then no adjoint pass runs.
-static bool bwd_carries(const gdn_desc* d, const Plan& p) {
-    return d->V == 128 && d->dtype == GDN_DTYPE_BF16 && (p.cp_on || !p.varlen) &&
-           !(d->flags & GDN_FLAG_BWD_ADJOINT_PASS) && p.total_segs * d->H <= INT32_MAX;
 }
 
 Geo make_geo(const gdn_desc* d, const Plan& p, unsigned char* ws) {
@@ -513,7 +513,7 @@ gdn_status gdn_plan(const gdn_desc* desc, gdn_plan_info* out) {
     out->fwd_workspace_bytes = p.fwd_bytes;
     out->bwd_workspace_bytes = p.bwd_bytes;
     out->fused_fwd = p.fused;
-    out->bwd_carried = bwd_carries(desc, p) ? 1 : 0;
+    out->bwd_carried = p.carry;
     return GDN_OK;
 }
 
@@ -696,7 +696,7 @@ gdn_status gdn_chunk_bwd(const gdn_desc* desc, const void* q, const void* k, con
         if (s != GDN_OK) return s;
     }
     // With the carried adjoint only the reverse CP (if any) goes to the side stream.
-    const bool carry = bwd_carries(desc, p);
+    const bool carry = p.carry != 0;
     const bool fork = p.cp_on || !carry;
     std::unique_lock<std::mutex> side_lock(side_mutex(), std::defer_lock);
     SideStream side;
@@ -753,8 +753,8 @@ gdn_status gdn_chunk_bwd(const gdn_desc* desc, const void* q, const void* k, con
     va.d_o = d_o;
     va.dsT = d_final_state;
     va.ds0 = d_initial_state;
-    va.gstates = ws + p.o_gst;
-    va.ddelta = ws + p.o_ddl;
+    va.gstates = carry ? nullptr : ws + p.o_gst;
+    va.ddelta = carry ? nullptr : ws + p.o_ddl;
     va.scale = desc->scale;
     va.use_cp = p.cp_on;
     va.q_l2 = kn != nullptr;
@@ -796,9 +796,9 @@ gdn_status gdn_chunk_bwd(const gdn_desc* desc, const void* q, const void* k, con
     ba.gam = gam;
     ba.d_o = d_o;
     ba.delta = ws + p.o_dl;
-    ba.ddelta = ws + p.o_ddl;
+    ba.ddelta = carry ? nullptr : ws + p.o_ddl;
     ba.hstates = ws + p.o_h;
-    ba.gstates = ws + p.o_gst;
+    ba.gstates = carry ? nullptr : ws + p.o_gst;
     ba.tmat = ws + p.o_tm;
     ba.dq = dq;
     ba.dk = dk;

@@ -79,9 +79,10 @@ typedef enum gdn_cp_mode {
     GDN_CP_AUTO = 0,   /* CP when the recurrence would leave compute units idle without it: the
                           sequence-heads' row tiles fill at most half of its workgroup slots
                           and the longest sequence spans two sub-sequences of 16 chunks or
-                          more; per sequence-head gate test picks warmup or exact */
+                          more; a gate test at every sub-sequence boundary picks warmup
+                          or exact there */
     GDN_CP_OFF = 1,    /* one serial pass per sequence-head */
-    GDN_CP_ON = 2,     /* CP regardless of the shape rule; per sequence-head gate test */
+    GDN_CP_ON = 2,     /* CP regardless of the shape rule; per-boundary gate test */
     GDN_CP_EXACT = 3,  /* CP, exact correction for every sequence-head */
     GDN_CP_WARMUP = 4, /* CP, warmup for every sequence-head (caller asserts fast decay) */
     GDN_CP_PAGES = 5   /* the pages' AutoCP thresholds, tuned for a 132-SM part: CP iff

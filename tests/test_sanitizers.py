@@ -1,8 +1,8 @@
 """Host code under AddressSanitizer and UndefinedBehaviorSanitizer (no GPU).
 
 Two small programs are built for the CPU with the sanitizers and run:
-  * tests/sanitize/plan_driver.cpp links the host part of libgdn (gdn_api.hip, compiled for the
-    host only) with stub kernel launchers: a sweep of the AutoCP planner and the workspace
+  * tests/sanitize/plan_driver.cpp links the host part of libgdn (gdn_api.hip; the sanitizers
+    instrument its host code only) with stub kernel launchers: a sweep of the AutoCP planner and the workspace
     layout over uniform and packed shapes, every documented argument error, and the forward's
     launch sequence;
   * tests/sanitize/oracle_driver.c runs the CPU oracle's forward and reverse mode on packed
