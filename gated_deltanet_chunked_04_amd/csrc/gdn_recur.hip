@@ -619,9 +619,12 @@ hipError_t launch_recur_t(const RecurArgs& a, int64_t nsegs_grid, int vtiles, hi
 // w. The sequence-head's mode summarises its boundaries: 1 all warmup, 2 all exact, 3 mixed.
 __global__ __launch_bounds__(kThreads) void k_decide(DecideArgs a) {
     const int wave = wave_id(), lane = threadIdx.x & 63;
-    const int64_t p = (int64_t)blockIdx.x * 4 + wave;
+    // one wave per sequence-head and direction (the two directions of one launch side by side)
+    const int ndir = a.modes_r ? 2 : 1;
+    const int64_t pd = (int64_t)blockIdx.x * 4 + wave;
     const int H = a.geo.H;
-    if (p >= (int64_t)a.geo.N * H) return;
+    if (pd >= (int64_t)a.geo.N * H * ndir) return;
+    const int64_t p = pd / ndir;
     const int n = (int)(p / H), h = (int)(p % H);
     int32_t nseg, nchunks;
     int64_t segoff, choff;
@@ -629,10 +632,10 @@ __global__ __launch_bounds__(kThreads) void k_decide(DecideArgs a) {
     const int W = a.warmup, span = a.warmup_max - a.warmup + 1;  // 1 .. 64 candidate windows
     const uint64_t all = span >= 64 ? ~0ull : ((1ull << span) - 1);
     // a.modes gets the decision for a.reverse's direction; a.modes_r, if given, the reverse one
-    for (int dir = 0; dir < 2; ++dir) {
+    {
+        const int dir = (int)(pd % ndir);
         int32_t* out = dir == 0 ? a.modes : a.modes_r;
         int32_t* wout = dir == 0 ? a.bwin : a.bwin_r;
-        if (!out) continue;
         const bool rev = dir == 0 ? a.reverse != 0 : true;
         int32_t* bw = wout + segoff * H + h;  // this sequence-head's boundaries, stride H
         if (lane == 0) bw[0] = -1;  // segment 0 has no boundary
@@ -1238,7 +1241,7 @@ hipError_t launch_fused(const RecurArgs& a, int dtype, int64_t nseqs, int vtiles
 }
 
 hipError_t launch_decide(const DecideArgs& a, hipStream_t st) {
-    const int64_t p = (int64_t)a.geo.N * a.geo.H;
+    const int64_t p = (int64_t)a.geo.N * a.geo.H * (a.modes_r ? 2 : 1);
     if (p == 0) return hipSuccess;
     hipLaunchKernelGGL(k_decide, dim3((unsigned)((p + 3) / 4)), dim3(kThreads), 0, st, a);
     return hipGetLastError();
