@@ -372,23 +372,35 @@ __device__ __forceinline__ void tri_inverse64(float* sA, float* sT) {
     const int wave = wave_id();
     const int lane = tid & 63;
     const int ln = lane & 15, gq = lane >> 4;
-    // 3a: diagonal blocks by forward substitution (wave b, lanes 0..15 = columns of block b),
-    // column-oriented: once x_j is final it updates every later row, so the dependent chain
-    // is 15 fused multiply-adds long instead of one per product
-    if (gq == 0 && wave < 4) {  // (workgroups of more than four waves: the others wait)
+    // 3a: diagonal blocks by forward substitution, wave b for block b (the first four waves; in
+    // larger workgroups the others wait). Lane (ln, gq) holds column ln of rows gq, gq+4, gq+8,
+    // gq+12 and those rows of A (contiguous: four 16-byte reads each). Column-oriented: once
+    // x_j is final its row group hands it to the other three (two row swaps and two adds, exact
+    // since they add zeros) and every row below subtracts A[r][j] x_j; A is zero on and above
+    // the diagonal, so the rows at or above j take no predicate.
+    if (wave < 4) {
         const int b = wave;
-        const int col = ln;
         const float* ablk = sA + (16 * b) * kLdA + 16 * b;
-        float x[16];
+        float av[4][16];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) x[r] = (r == col) ? 1.f : 0.f;
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int c4 = 0; c4 < 4; ++c4) {
+                const f32x4 t = *reinterpret_cast<const f32x4*>(ablk + (gq + 4 * i) * kLdA + 4 * c4);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) av[i][4 * c4 + e] = t[e];
+            }
+        float x[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x[i] = (gq + 4 * i == ln) ? 1.f : 0.f;
 #pragma unroll
         for (int j = 0; j < 15; ++j) {
+            const float xj = sum_rows(gq == (j & 3) ? x[j >> 2] : 0.f);
 #pragma unroll
-            for (int r = j + 1; r < 16; ++r) x[r] -= ablk[r * kLdA + j] * x[j];
+            for (int i = 0; i < 4; ++i) x[i] -= av[i][j] * xj;
         }
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sT[(16 * b + r) * kLdA + 16 * b + col] = x[r];
+        for (int i = 0; i < 4; ++i) sT[(16 * b + gq + 4 * i) * kLdA + 16 * b + ln] = x[i];
     }
     lds_sync();
     if (wave < 3) tri_offdiag_block(sA, sT, wave + 1, wave);
