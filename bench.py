@@ -339,8 +339,8 @@ def fused_leg(gdn, flush, reps=10):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="edge_prefill")
     ap.add_argument("--pass", dest="passes", default="both", choices=["both", "fwd", "bwd"])
     ap.add_argument("--cp", default=None, help="override the workload's CP mode (auto/off/on/exact/warmup)")
