@@ -1129,13 +1129,20 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(BwdChunkArgs a) {
                 frag_row_fo(xr[1], sX, C::LDX, row, 32);
                 T* dq = reinterpret_cast<T*>(a.dq) + ((t0 + row) * H + h) * K + k0;
                 float qd = 0.f;
+                f32x4 accq[KW];
 #pragma unroll
                 for (int j = 0; j < KW; ++j) {
                     qd += dot4(dQT[j][m], ld4(sQ + row * C::LDK + frag_pos(k0 + j * 16 + gq * 4)));
-                    f32x4 acc = dQT[j][m] * eg;
-                    mma(acc, kc[j][0], xr[0]);
-                    mma(acc, kc[j][1], xr[1]);
-                    if (row < c) store4(dq + j * 16 + gq * 4, acc);
+                    accq[j] = dQT[j][m] * eg;
+                    mma(accq[j], kc[j][0], xr[0]);
+                    mma(accq[j], kc[j][1], xr[1]);
+                }
+                if constexpr (KW == 2) {
+                    store_pair<T>(dq, accq[0], accq[1], row < c);  // k0 = 32w: whole 32-column runs
+                } else {
+#pragma unroll
+                    for (int j = 0; j < KW; ++j)
+                        if (row < c) store4(dq + j * 16 + gq * 4, accq[j]);
                 }
                 qd = sum_gq(qd) * eg;
                 if (gq == 0) sQd[w * 64 + row] = qd;
@@ -1313,6 +1320,7 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(BwdChunkArgs a) {
         const float ba = sBeta[ra], ega = fast_exp(sGam[ra]);
         {
             T* dkp = reinterpret_cast<T*>(a.dk) + ((t0 + ra) * H + h) * K;
+            f32x4 dkv[KH];
 #pragma unroll
             for (int i = 0; i < KH; ++i) {
                 const int kt = hf * KH + i;
@@ -1330,12 +1338,16 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(BwdChunkArgs a) {
                 const float s = dot4(bk, ld4(sK + ra * C::LDK + frag_pos(kt * 16 + gq * 4)));
                 dbeta_row += ega * s;
                 dgam_row += ba * ega * s;
-                if (ra < c) store4(dkp + kt * 16 + gq * 4, dkpart[i] + mk + bk * (ba * ega));
+                dkv[i] = dkpart[i] + mk + bk * (ba * ega);
             }
+            // this half's k tiles in pairs: whole 32-column runs of the row
+#pragma unroll
+            for (int i = 0; i < KH; i += 2) store_pair<T>(dkp + (hf * KH + i) * 16, dkv[i], dkv[i + 1], ra < c);
         }
         f32x4 bvk[kCarry ? VH : 1];  // kCarry: dBv[a = ra][this half's v tiles], for the adjoint update
         {
             T* dvp = reinterpret_cast<T*>(a.dv) + ((t0 + ra) * H + h) * V;
+            f32x4 dvv[VH];
 #pragma unroll
             for (int i = 0; i < VH; ++i) {
                 const int vt = hf * VH + i;
@@ -1347,9 +1359,11 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(BwdChunkArgs a) {
                     mma(bv, fu, ta[xb]);
                 }
                 dbeta_row += dot4(bv, ld4(sV + ra * C::LDV + frag_pos(vt * 16 + gq * 4)));
-                if (ra < c) store4(dvp + vt * 16 + gq * 4, bv * ba);
+                dvv[i] = bv * ba;
                 if constexpr (kCarry) bvk[i] = bv;
             }
+#pragma unroll
+            for (int i = 0; i < VH; i += 2) store_pair<T>(dvp + (hf * VH + i) * 16, dvv[i], dvv[i + 1], ra < c);
         }
         bwd_fetch<3>(R, a, nxt);
         bwd_fetch<4>(R, a, nxt);

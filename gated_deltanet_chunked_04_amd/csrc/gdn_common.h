@@ -275,6 +275,36 @@ __device__ __forceinline__ void store4(bf16_t* p, const f32x4& x) {
 }
 __device__ __forceinline__ void store4(float* p, const f32x4& x) { *reinterpret_cast<f32x4*>(p) = x; }
 
+// Two accumulator tiles of one row stored as the row's 32 columns from c0 (a multiple of 32;
+// p points at column c0): lane (ln, gq) holds columns c0 + 4gq .. +3 of `lo` and c0 + 16 + 4gq ..
+// +3 of `hi`. In bf16 two row swaps among the row's four lanes (ln + 16 gq) give lane gq the 16
+// contiguous bytes at columns c0 + 8gq, one store each. Every lane of the wave must call it;
+// `ok` gates the store.
+template <typename T>
+__device__ __forceinline__ void store_pair(T* p, const f32x4& lo, const f32x4& hi, bool ok);
+template <>
+__device__ __forceinline__ void store_pair<bf16_t>(bf16_t* p, const f32x4& lo, const f32x4& hi, bool ok) {
+    const int gq = (threadIdx.x & 63) >> 4;
+    u32x2 x = u32x2{pack_bf2(lo.x, lo.y), pack_bf2(lo.z, lo.w)};
+    u32x2 y = u32x2{pack_bf2(hi.x, hi.y), pack_bf2(hi.z, hi.w)};
+#pragma unroll
+    for (int d = 0; d < 2; ++d) {
+        const auto s32 = __builtin_amdgcn_permlane32_swap(x[d], y[d], false, false);
+        const auto s16 = __builtin_amdgcn_permlane16_swap(s32[0], s32[1], false, false);
+        x[d] = s16[0];
+        y[d] = s16[1];
+    }
+    if (ok) *reinterpret_cast<u32x4*>(p + 8 * gq) = u32x4{x[0], x[1], y[0], y[1]};
+}
+template <>
+__device__ __forceinline__ void store_pair<float>(float* p, const f32x4& lo, const f32x4& hi, bool ok) {
+    const int gq = (threadIdx.x & 63) >> 4;
+    if (ok) {
+        store4(p + 4 * gq, lo);
+        store4(p + 16 + 4 * gq, hi);
+    }
+}
+
 // Four fp32 values in the storage type, as the register image one vector store writes.
 template <typename T> struct Pack4;
 template <> struct Pack4<bf16_t> {

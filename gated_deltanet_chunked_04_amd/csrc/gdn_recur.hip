@@ -452,11 +452,14 @@ __global__ __launch_bounds__(RT * 4) void k_recur(RecurArgs a) {
     typedef typename Pack4<T>::type PV;
     constexpr int NFL = 64 * (RT / C::VEC) / C::NT;  // Delta flush vectors per thread
     PV okeep[4], hkeep[K / 16];
+    u32x4 hst[K / 32];  // bf16: the chunk-entry state as stored (16 contiguous bytes per lane)
     u32x4 fkeep[NFL];
 #pragma unroll
     for (int i = 0; i < 4; ++i) okeep[i] = PV{};
 #pragma unroll
     for (int i = 0; i < K / 16; ++i) hkeep[i] = PV{};
+#pragma unroll
+    for (int i = 0; i < K / 32; ++i) hst[i] = u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
     for (int i = 0; i < NFL; ++i) fkeep[i] = u32x4{0u, 0u, 0u, 0u};
     // The states and output passes prefetch one chunk ahead; the prepass, which has little
@@ -478,14 +481,35 @@ __global__ __launch_bounds__(RT * 4) void k_recur(RecurArgs a) {
 #pragma unroll
         for (int i = 0; i < K / 16; ++i) hold(hkeep[i]);
 #pragma unroll
+        for (int i = 0; i < K / 32; ++i) hold(hst[i]);
+#pragma unroll
         for (int i = 0; i < NFL; ++i) hold(fkeep[i]);
         if (kRec) {
             // entry state of this chunk, in the input precision
             T* hs = reinterpret_cast<T*>(a.hstates) + ((size_t)(sg.choff + ci) * H + h) * VK + (size_t)row * K;
 #pragma unroll
             for (int kt = 0; kt < K / 16; ++kt) hkeep[kt] = Pack4<T>::make(accS[kt]);
+            if constexpr (sizeof(T) == 2) {
+                // the four lanes of a row (ln + 16 gq) hold 8-byte pieces of columns kt*16 + gq*4:
+                // two row swaps per pair of tiles give lane gq the 16 contiguous bytes at columns
+                // 32m + 8gq, so a row's 64-byte runs go out in one store each
 #pragma unroll
-            for (int kt = 0; kt < K / 16; ++kt) *reinterpret_cast<PV*>(hs + kt * 16 + gq * 4) = hkeep[kt];
+                for (int m = 0; m < K / 32; ++m) {
+                    PV x = hkeep[2 * m], y = hkeep[2 * m + 1];
+#pragma unroll
+                    for (int d = 0; d < 2; ++d) {
+                        const auto s32 = __builtin_amdgcn_permlane32_swap(x[d], y[d], false, false);
+                        const auto s16 = __builtin_amdgcn_permlane16_swap(s32[0], s32[1], false, false);
+                        x[d] = s16[0];
+                        y[d] = s16[1];
+                    }
+                    hst[m] = u32x4{x[0], x[1], y[0], y[1]};
+                    *reinterpret_cast<u32x4*>(hs + 32 * m + 8 * gq) = hst[m];
+                }
+            } else {
+#pragma unroll
+                for (int kt = 0; kt < K / 16; ++kt) *reinterpret_cast<PV*>(hs + kt * 16 + gq * 4) = hkeep[kt];
+            }
         }
         lds_sync();  // previous chunk's LDS reads are done
         if (kRec && a.delta && ci > cbeg) {
