@@ -55,6 +55,11 @@ struct RCfg {
     static constexpr int off_pm = off_u + 64 * LDU * (int)sizeof(T);
     static constexpr int off_gam = off_pm + 64 * LDP * (int)sizeof(T);
     static constexpr int total = off_gam + 256;
+    // the output passes stage each chunk's O rows here and store them as whole rows (after the
+    // next chunk's first barrier, or after the loop for the last chunk)
+    static constexpr int off_o = total;
+    static constexpr int total_out = off_o + 64 * LDU * (int)sizeof(T);
+    static constexpr bool stage_o = total_out <= 160 * 1024;  // (fp32 at K = 128: no room)
     static_assert(64 * LDU <= 64 * LD, "the q tile holds a [64][RT] Delta tile");
     // register prefetch: 16-byte vectors per thread
     static constexpr int NVK = K / VEC;                        // vectors per row of q/k/w
@@ -108,6 +113,7 @@ struct ChunkLds {
     T* sU;
     T* sPm;
     float* sGam;
+    T* sO = nullptr;  // output staging [64][RT] (row-major), or null: O goes straight to memory
 };
 
 template <typename T, int K, int RT, bool kQ>
@@ -323,13 +329,21 @@ __device__ __forceinline__ void chunk_part2(const RecurArgs& a, const ChunkLds<T
         const int V = a.geo.V;
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) okeep[rt] = Pack4<T>::make(accO[rt] * a.scale);
-        // a full chunk (the wave-uniform common case) stores with no branch per row
+        if (L.sO) {
+            // staged; stored as whole rows by the caller
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt) {
-            const int r = rt * 16 + ln;
-            if (c == 64 || r < c)
-                *reinterpret_cast<typename Pack4<T>::type*>(o + ((t0 + r) * H + h) * V + vcol0 + wave * 16 + gq * 4) =
+            for (int rt = 0; rt < 4; ++rt)
+                *reinterpret_cast<typename Pack4<T>::type*>(L.sO + (rt * 16 + ln) * C::LDU + wave * 16 + gq * 4) =
                     okeep[rt];
+        } else {
+            // a full chunk (the wave-uniform common case) stores with no branch per row
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) {
+                const int r = rt * 16 + ln;
+                if (c == 64 || r < c)
+                    *reinterpret_cast<typename Pack4<T>::type*>(o + ((t0 + r) * H + h) * V + vcol0 + wave * 16 +
+                                                                gq * 4) = okeep[rt];
+            }
         }
     }
     // S^T <- e^Gam S^T + K^T diag(e^{Gam-gam}) Delta
@@ -378,6 +392,8 @@ __global__ __launch_bounds__(RT * 4) void k_recur(RecurArgs a) {
     L.sU = reinterpret_cast<T*>(smem + C::off_u);
     L.sPm = reinterpret_cast<T*>(smem + C::off_pm);
     L.sGam = reinterpret_cast<float*>(smem + C::off_gam);
+    constexpr bool kStageO = kOut && C::stage_o;
+    if constexpr (kStageO) L.sO = reinterpret_cast<T*>(smem + C::off_o);
 
     const Geo& geo = a.geo;
     const int64_t gs = blockIdx.x;
@@ -452,6 +468,7 @@ __global__ __launch_bounds__(RT * 4) void k_recur(RecurArgs a) {
     typedef typename Pack4<T>::type PV;
     constexpr int NFL = 64 * (RT / C::VEC) / C::NT;  // Delta flush vectors per thread
     PV okeep[4], hkeep[K / 16];
+    u32x4 okeep_rows[NFL];  // output passes: the previous chunk's O rows as stored
     u32x4 hst[K / 32];  // bf16: the chunk-entry state as stored (16 contiguous bytes per lane)
     u32x4 fkeep[NFL];
 #pragma unroll
@@ -462,6 +479,8 @@ __global__ __launch_bounds__(RT * 4) void k_recur(RecurArgs a) {
     for (int i = 0; i < K / 32; ++i) hst[i] = u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
     for (int i = 0; i < NFL; ++i) fkeep[i] = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < NFL; ++i) okeep_rows[i] = u32x4{0u, 0u, 0u, 0u};
     // The states and output passes prefetch one chunk ahead; the prepass, which has little
     // work per chunk to cover the loads, two chunks ahead in two alternating buffers.
     constexpr int kDepth = MODE == kRecurPrepass ? 2 : 1;
@@ -484,6 +503,8 @@ __global__ __launch_bounds__(RT * 4) void k_recur(RecurArgs a) {
         for (int i = 0; i < K / 32; ++i) hold(hst[i]);
 #pragma unroll
         for (int i = 0; i < NFL; ++i) hold(fkeep[i]);
+#pragma unroll
+        for (int i = 0; i < NFL; ++i) hold(okeep_rows[i]);
         if (kRec) {
             // entry state of this chunk, in the input precision
             T* hs = reinterpret_cast<T*>(a.hstates) + ((size_t)(sg.choff + ci) * H + h) * VK + (size_t)row * K;
@@ -512,6 +533,21 @@ __global__ __launch_bounds__(RT * 4) void k_recur(RecurArgs a) {
             }
         }
         lds_sync();  // previous chunk's LDS reads are done
+        if (kStageO && ci > cbeg) {
+            // the previous chunk's O rows (a full chunk), staged by every wave: whole rows out
+            T* dst = reinterpret_cast<T*>(a.o) + ((t0 - 64) * H + h) * V + vt * RT;
+            constexpr int NV = RT / C::VEC;
+#pragma unroll
+            for (int it = 0; it < NFL; ++it) {
+                const int u = (int)threadIdx.x + it * C::NT;
+                okeep_rows[it] = *reinterpret_cast<const u32x4*>(L.sO + (u / NV) * C::LDU + (u % NV) * C::VEC);
+            }
+#pragma unroll
+            for (int it = 0; it < NFL; ++it) {
+                const int u = (int)threadIdx.x + it * C::NT;
+                *reinterpret_cast<u32x4*>(dst + (size_t)(u / NV) * H * V + (u % NV) * C::VEC) = okeep_rows[it];
+            }
+        }
         if (kRec && a.delta && ci > cbeg) {
             // the previous chunk's Delta, staged over the q tile
             T* dst = reinterpret_cast<T*>(a.delta) + ((t0 - 64) * H + h) * V + vt * RT;
@@ -588,11 +624,16 @@ __global__ __launch_bounds__(RT * 4) void k_recur(RecurArgs a) {
         for (int ci = cbeg; ci < cend; ++ci) step(R0, ci);
     }
 
-    if (kRec && a.delta && cbeg < cend) {
+    if ((kStageO || (kRec && a.delta)) && cbeg < cend) {
         lds_sync();
         const int cl = cend - 1;
-        flush_tile<T, RT, C::NT>(reinterpret_cast<T*>(a.delta) + ((sg.bos + (int64_t)cl * 64) * H + h) * V + vt * RT,
-                                 (size_t)H * V, min(64, sg.len - cl * 64), L.sQ, C::LDU);
+        const size_t toff = ((sg.bos + (int64_t)cl * 64) * H + h) * V + vt * RT;
+        if (kStageO)
+            flush_tile<T, RT, C::NT>(reinterpret_cast<T*>(a.o) + toff, (size_t)H * V, min(64, sg.len - cl * 64), L.sO,
+                                     C::LDU);
+        if (kRec && a.delta)
+            flush_tile<T, RT, C::NT>(reinterpret_cast<T*>(a.delta) + toff, (size_t)H * V, min(64, sg.len - cl * 64),
+                                     L.sQ, C::LDU);
     }
     if (MODE == kRecurPrepass) {
         if (mode == 1) {
@@ -621,13 +662,14 @@ __global__ __launch_bounds__(RT * 4) void k_recur(RecurArgs a) {
 template <typename T, int K, int RT, int MODE, bool kL2 = false>
 hipError_t launch_recur_t(const RecurArgs& a, int64_t nsegs_grid, int vtiles, hipStream_t st) {
     using C = RCfg<T, K, RT>;
-    static_assert(C::total <= 160 * 1024, "LDS budget");
+    constexpr int lds = (MODE == kRecurOut || MODE == kRecurOutRec) && C::stage_o ? C::total_out : C::total;
+    static_assert(lds <= 160 * 1024, "LDS budget");
     auto kern = k_recur<T, K, RT, MODE, kL2>;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, C::total);
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (e != hipSuccess) return e;
     dim3 grid((unsigned)nsegs_grid, (unsigned)a.geo.H, (unsigned)vtiles);
-    hipLaunchKernelGGL(kern, grid, dim3(C::NT), C::total, st, a);
+    hipLaunchKernelGGL(kern, grid, dim3(C::NT), lds, st, a);
     return hipGetLastError();
 }
 
