@@ -60,6 +60,14 @@ struct RCfg {
     static constexpr int off_o = total;
     static constexpr int total_out = off_o + 64 * LDU * (int)sizeof(T);
     static constexpr bool stage_o = total_out <= 160 * 1024;  // (fp32 at K = 128: no room)
+    // the passes that record chunk-entry states stage each one here ([RT][K], row-major) and store
+    // the workgroup's RT contiguous state rows as one linear block
+    static constexpr int LDH = K + RPad<T>::row;
+    static constexpr int h_bytes = RT * LDH * (int)sizeof(T);
+    static constexpr int lds_of(bool out, bool rec) {
+        return (out && stage_o ? total_out : total) +
+               (rec && (out && stage_o ? total_out : total) + h_bytes <= 160 * 1024 ? h_bytes : 0);
+    }
     static_assert(64 * LDU <= 64 * LD, "the q tile holds a [64][RT] Delta tile");
     // register prefetch: 16-byte vectors per thread
     static constexpr int NVK = K / VEC;                        // vectors per row of q/k/w
@@ -114,6 +122,7 @@ struct ChunkLds {
     T* sPm;
     float* sGam;
     T* sO = nullptr;  // output staging [64][RT] (row-major), or null: O goes straight to memory
+    T* sH = nullptr;  // chunk-entry state staging [RT][K] (row-major), or null
 };
 
 template <typename T, int K, int RT, bool kQ>
@@ -394,6 +403,9 @@ __global__ __launch_bounds__(RT * 4) void k_recur(RecurArgs a) {
     L.sGam = reinterpret_cast<float*>(smem + C::off_gam);
     constexpr bool kStageO = kOut && C::stage_o;
     if constexpr (kStageO) L.sO = reinterpret_cast<T*>(smem + C::off_o);
+    constexpr int kOffH = kStageO ? C::total_out : C::total;
+    constexpr bool kStageH = kRec && C::lds_of(kOut, kRec) > kOffH;
+    if constexpr (kStageH) L.sH = reinterpret_cast<T*>(smem + kOffH);
 
     const Geo& geo = a.geo;
     const int64_t gs = blockIdx.x;
@@ -469,14 +481,16 @@ __global__ __launch_bounds__(RT * 4) void k_recur(RecurArgs a) {
     constexpr int NFL = 64 * (RT / C::VEC) / C::NT;  // Delta flush vectors per thread
     PV okeep[4], hkeep[K / 16];
     u32x4 okeep_rows[NFL];  // output passes: the previous chunk's O rows as stored
-    u32x4 hst[K / 32];  // bf16: the chunk-entry state as stored (16 contiguous bytes per lane)
+    // the chunk-entry state as stored: 16-byte vectors per lane
+    constexpr int NHS = (K / 32 > RT * K / C::VEC / C::NT) ? K / 32 : RT * K / C::VEC / C::NT;
+    u32x4 hst[NHS];
     u32x4 fkeep[NFL];
 #pragma unroll
     for (int i = 0; i < 4; ++i) okeep[i] = PV{};
 #pragma unroll
     for (int i = 0; i < K / 16; ++i) hkeep[i] = PV{};
 #pragma unroll
-    for (int i = 0; i < K / 32; ++i) hst[i] = u32x4{0u, 0u, 0u, 0u};
+    for (int i = 0; i < NHS; ++i) hst[i] = u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
     for (int i = 0; i < NFL; ++i) fkeep[i] = u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
@@ -500,39 +514,40 @@ __global__ __launch_bounds__(RT * 4) void k_recur(RecurArgs a) {
 #pragma unroll
         for (int i = 0; i < K / 16; ++i) hold(hkeep[i]);
 #pragma unroll
-        for (int i = 0; i < K / 32; ++i) hold(hst[i]);
+        for (int i = 0; i < NHS; ++i) hold(hst[i]);
 #pragma unroll
         for (int i = 0; i < NFL; ++i) hold(fkeep[i]);
 #pragma unroll
         for (int i = 0; i < NFL; ++i) hold(okeep_rows[i]);
-        if (kRec) {
-            // entry state of this chunk, in the input precision
+        if (kStageH) {
+            // entry state of this chunk, in the input precision, staged (stored after the barrier)
+#pragma unroll
+            for (int kt = 0; kt < K / 16; ++kt)
+                *reinterpret_cast<PV*>(L.sH + (wave * 16 + ln) * C::LDH + kt * 16 + gq * 4) = Pack4<T>::make(accS[kt]);
+        } else if (kRec) {
+            // entry state of this chunk, in the input precision (no LDS room to stage it: fp32
+            // at K = 128)
             T* hs = reinterpret_cast<T*>(a.hstates) + ((size_t)(sg.choff + ci) * H + h) * VK + (size_t)row * K;
 #pragma unroll
             for (int kt = 0; kt < K / 16; ++kt) hkeep[kt] = Pack4<T>::make(accS[kt]);
-            if constexpr (sizeof(T) == 2) {
-                // the four lanes of a row (ln + 16 gq) hold 8-byte pieces of columns kt*16 + gq*4:
-                // two row swaps per pair of tiles give lane gq the 16 contiguous bytes at columns
-                // 32m + 8gq, so a row's 64-byte runs go out in one store each
 #pragma unroll
-                for (int m = 0; m < K / 32; ++m) {
-                    PV x = hkeep[2 * m], y = hkeep[2 * m + 1];
-#pragma unroll
-                    for (int d = 0; d < 2; ++d) {
-                        const auto s32 = __builtin_amdgcn_permlane32_swap(x[d], y[d], false, false);
-                        const auto s16 = __builtin_amdgcn_permlane16_swap(s32[0], s32[1], false, false);
-                        x[d] = s16[0];
-                        y[d] = s16[1];
-                    }
-                    hst[m] = u32x4{x[0], x[1], y[0], y[1]};
-                    *reinterpret_cast<u32x4*>(hs + 32 * m + 8 * gq) = hst[m];
-                }
-            } else {
-#pragma unroll
-                for (int kt = 0; kt < K / 16; ++kt) *reinterpret_cast<PV*>(hs + kt * 16 + gq * 4) = hkeep[kt];
-            }
+            for (int kt = 0; kt < K / 16; ++kt) *reinterpret_cast<PV*>(hs + kt * 16 + gq * 4) = hkeep[kt];
         }
         lds_sync();  // previous chunk's LDS reads are done
+        if constexpr (kStageH) {
+            // the workgroup's RT rows of this chunk's entry state are one contiguous block
+            T* hs = reinterpret_cast<T*>(a.hstates) + ((size_t)(sg.choff + ci) * H + h) * VK + (size_t)vt * RT * K;
+            constexpr int NHV = RT * K / C::VEC / C::NT;  // 16-byte vectors per thread
+            static_assert(NHV * C::NT * C::VEC == RT * K && NHV <= NHS, "state block split");
+#pragma unroll
+            for (int it = 0; it < NHV; ++it) {
+                const int e = ((int)threadIdx.x + it * C::NT) * C::VEC;
+                hst[it] = *reinterpret_cast<const u32x4*>(L.sH + (e / K) * C::LDH + e % K);
+            }
+#pragma unroll
+            for (int it = 0; it < NHV; ++it)
+                *reinterpret_cast<u32x4*>(hs + ((int)threadIdx.x + it * C::NT) * C::VEC) = hst[it];
+        }
         if (kStageO && ci > cbeg) {
             // the previous chunk's O rows (a full chunk), staged by every wave: whole rows out
             T* dst = reinterpret_cast<T*>(a.o) + ((t0 - 64) * H + h) * V + vt * RT;
@@ -662,7 +677,7 @@ __global__ __launch_bounds__(RT * 4) void k_recur(RecurArgs a) {
 template <typename T, int K, int RT, int MODE, bool kL2 = false>
 hipError_t launch_recur_t(const RecurArgs& a, int64_t nsegs_grid, int vtiles, hipStream_t st) {
     using C = RCfg<T, K, RT>;
-    constexpr int lds = (MODE == kRecurOut || MODE == kRecurOutRec) && C::stage_o ? C::total_out : C::total;
+    constexpr int lds = C::lds_of(MODE == kRecurOut || MODE == kRecurOutRec, MODE == kRecurStates || MODE == kRecurOutRec);
     static_assert(lds <= 160 * 1024, "LDS budget");
     auto kern = k_recur<T, K, RT, MODE, kL2>;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
