@@ -209,11 +209,23 @@ __global__ __launch_bounds__(kThreads) void k_intra(IntraArgs args) {
         // ---- stage 3: T = (I + A)^{-1} --------------------------------------------------
         tri_inverse64(sA, sT);
         if (args.tmat) {
-            // T for the backward, in the input precision: thread -> row tid/4, 16 columns
-            const int tr = tid >> 2, tc = (tid & 3) * 16;
-            T* dst = reinterpret_cast<T*>(args.tmat) + ((size_t)gc * H + h) * 4096 + tr * 64 + tc;
+            // T for the backward, in the input precision: the 64 x 64 block is contiguous, so
+            // consecutive threads store consecutive 16-byte vectors (whole lines)
+            constexpr int VEC = Elem<T>::kVec;
+            T* dst = reinterpret_cast<T*>(args.tmat) + ((size_t)gc * H + h) * 4096;
 #pragma unroll
-            for (int i = 0; i < 16; i += 4) store4(dst + i, *reinterpret_cast<const f32x4*>(sT + tr * kLdA + tc + i));
+            for (int it = 0; it < 4096 / VEC / kThreads; ++it) {
+                const int e = (tid + it * kThreads) * VEC;
+                const float* src = sT + (e >> 6) * kLdA + (e & 63);
+                if constexpr (sizeof(T) == 2) {
+                    const f32x4 x0 = *reinterpret_cast<const f32x4*>(src);
+                    const f32x4 x1 = *reinterpret_cast<const f32x4*>(src + 4);
+                    *reinterpret_cast<u32x4*>(dst + e) = u32x4{pack_bf2(x0.x, x0.y), pack_bf2(x0.z, x0.w),
+                                                               pack_bf2(x1.x, x1.y), pack_bf2(x1.z, x1.w)};
+                } else {
+                    *reinterpret_cast<f32x4*>(dst + e) = *reinterpret_cast<const f32x4*>(src);
+                }
+            }
         }
         if (wave == 1) {
             // chunk statistics for the CP decision
