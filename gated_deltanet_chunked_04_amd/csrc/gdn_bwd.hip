@@ -607,6 +607,14 @@ struct BCfg {
     static constexpr int off_sc = off_dgs + 256;    // [16] fp32 scalars (two per wave)
     static constexpr int off_db = off_sc + 64;      // [2][64] fp32 dbeta parts (one per wave half)
     static constexpr int total = off_db + 512;
+    // Where the WY side leaves a hole between its last matrix (dT) and dDelta large enough (bf16 at
+    // K = V = 128: the state side's Q, dO and Delta tiles, dead once the state side ends), dq
+    // and then dk and dv are staged there ([64][K + 8], row-major) and stored as whole rows.
+    static constexpr int LDG = K + BPad<T>::row;
+    static constexpr int kMG = 64 * LDG * (int)sizeof(T);
+    static constexpr int off_gst = wy.off[4] + kMX;  // past dT
+    static constexpr bool stage_grads = sizeof(T) == 2 && K == V && wy.end == end_state &&
+                                        off_gst >= off_q && off_gst + 2 * kMG <= off_dd;
     static_assert(LDX <= LDV, "the exchange fits over Delta");
     static_assert(kMK <= kSt, "dW fits over S");
     // eight waves; 16-byte vectors per thread of one task's operands
@@ -1120,6 +1128,7 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(BwdChunkArgs a) {
                 frag_col_fo(kc[j][0], sK, C::LDK, k0 + j * 16 + ln, 0);  // K^T row k, slots j'
                 frag_col_fo(kc[j][1], sK, C::LDK, k0 + j * 16 + ln, 32);
             }
+            f32x4 dqs[C::stage_grads ? KW : 1][2];  // staging: dq tiles of rows (2hf+m)*16+ln
 #pragma unroll
             for (int m = 0; m < 2; ++m) {
                 const int row = (2 * hf + m) * 16 + ln;
@@ -1137,7 +1146,10 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(BwdChunkArgs a) {
                     mma(accq[j], kc[j][0], xr[0]);
                     mma(accq[j], kc[j][1], xr[1]);
                 }
-                if constexpr (KW == 2) {
+                if constexpr (C::stage_grads) {
+#pragma unroll
+                    for (int j = 0; j < KW; ++j) dqs[j][m] = accq[j];  // staged after the barrier below
+                } else if constexpr (KW == 2) {
                     store_pair<T>(dq, accq[0], accq[1], row < c);  // k0 = 32w: whole 32-column runs
                 } else {
 #pragma unroll
@@ -1148,6 +1160,14 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(BwdChunkArgs a) {
                 if (gq == 0) sQd[w * 64 + row] = qd;
             }
             lds_sync();  // the state side's LDS reads are done: the WY side reuses the space
+            if constexpr (C::stage_grads) {
+                T* sGq = reinterpret_cast<T*>(sm + C::off_gst);
+#pragma unroll
+                for (int j = 0; j < KW; ++j)
+#pragma unroll
+                    for (int m = 0; m < 2; ++m)
+                        store4(sGq + ((2 * hf + m) * 16 + ln) * C::LDG + k0 + j * 16 + gq * 4, dqs[j][m]);
+            }
             // dW (rows r) in the operand type, over S
 #pragma unroll
             for (int j = 0; j < KW; ++j)
@@ -1176,6 +1196,11 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(BwdChunkArgs a) {
         put_tile_fo<T, V, C::NV, NT>(sV, C::LDV, RV.v);  // fragment order
         put_tile_fo<T, 64, C::NX, NT>(sTm, C::LDX, RV.t);
         lds_sync();
+        if constexpr (C::stage_grads) {
+            // dq as whole rows (no loads are in flight here: the next task's start after this)
+            flush_tile<T, K, NT>(reinterpret_cast<T*>(a.dq) + (t0 * H + h) * K, (size_t)H * K, c,
+                                 reinterpret_cast<const T*>(sm + C::off_gst), C::LDG);
+        }
         // The next task's operands load over the rest of this one, issued late (where few
         // registers are live, so that nothing spills or waits on them) and in groups.
         bwd_fetch<0>(R, a, nxt);
@@ -1340,9 +1365,15 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(BwdChunkArgs a) {
                 dgam_row += ba * ega * s;
                 dkv[i] = dkpart[i] + mk + bk * (ba * ega);
             }
-            // this half's k tiles in pairs: whole 32-column runs of the row
+            if constexpr (C::stage_grads) {
+                T* sGk = reinterpret_cast<T*>(sm + C::off_gst);
 #pragma unroll
-            for (int i = 0; i < KH; i += 2) store_pair<T>(dkp + (hf * KH + i) * 16, dkv[i], dkv[i + 1], ra < c);
+                for (int i = 0; i < KH; ++i) store4(sGk + ra * C::LDG + (hf * KH + i) * 16 + gq * 4, dkv[i]);
+            } else {
+                // this half's k tiles in pairs: whole 32-column runs of the row
+#pragma unroll
+                for (int i = 0; i < KH; i += 2) store_pair<T>(dkp + (hf * KH + i) * 16, dkv[i], dkv[i + 1], ra < c);
+            }
         }
         f32x4 bvk[kCarry ? VH : 1];  // kCarry: dBv[a = ra][this half's v tiles], for the adjoint update
         {
@@ -1362,11 +1393,19 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(BwdChunkArgs a) {
                 dvv[i] = bv * ba;
                 if constexpr (kCarry) bvk[i] = bv;
             }
+            if constexpr (C::stage_grads) {
+                T* sGv = reinterpret_cast<T*>(sm + C::off_gst + C::kMG);
 #pragma unroll
-            for (int i = 0; i < VH; i += 2) store_pair<T>(dvp + (hf * VH + i) * 16, dvv[i], dvv[i + 1], ra < c);
+                for (int i = 0; i < VH; ++i) store4(sGv + ra * C::LDG + (hf * VH + i) * 16 + gq * 4, dvv[i]);
+            } else {
+#pragma unroll
+                for (int i = 0; i < VH; i += 2) store_pair<T>(dvp + (hf * VH + i) * 16, dvv[i], dvv[i + 1], ra < c);
+            }
         }
-        bwd_fetch<3>(R, a, nxt);
-        bwd_fetch<4>(R, a, nxt);
+        if constexpr (!C::stage_grads) {
+            bwd_fetch<3>(R, a, nxt);
+            bwd_fetch<4>(R, a, nxt);
+        }
         dbeta_row = sum_gq(dbeta_row);
         dgam_row = sum_gq(dgam_row);
         if (gq == 0) {
@@ -1374,6 +1413,17 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(BwdChunkArgs a) {
             sDb[hf * 64 + ra] = dbeta_row;
         }
         lds_sync();
+        if constexpr (C::stage_grads) {
+            // dk and dv as whole rows
+            flush_tile<T, K, NT>(reinterpret_cast<T*>(a.dk) + (t0 * H + h) * K, (size_t)H * K, c,
+                                 reinterpret_cast<const T*>(sm + C::off_gst), C::LDG);
+            flush_tile<T, V, NT>(reinterpret_cast<T*>(a.dv) + (t0 * H + h) * V, (size_t)H * V, c,
+                                 reinterpret_cast<const T*>(sm + C::off_gst + C::kMG), C::LDG);
+            // the next task's S (and G) after these stores, so that no wait for their data
+            // registers lands on those loads
+            bwd_fetch<3>(R, a, nxt);
+            bwd_fetch<4>(R, a, nxt);
+        }
         // ---- dbeta, and d(gam) total with dg = reverse cumulative sum within the chunk ---------
         if (wave == 0) {
             // suffix sum over the chunk's rows: a prefix scan over the lanes in reversed order
