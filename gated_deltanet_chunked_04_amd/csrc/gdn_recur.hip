@@ -44,29 +44,38 @@ struct RCfg {
     static constexpr int NW = RT / 16;
     static constexpr int NT = NW * 64;
     static constexpr int VEC = Elem<T>::kVec;
-    static constexpr int LD = K + RPad<T>::row;
-    static constexpr int LDU = RT + RPad<T>::row;
+    // row strides of K + 16 (bf16) elements: the transposed and the row-fragment reads of the
+    // staged tiles then meet no bank conflicts (measured: the states pass 180 -> 155 us)
+    static constexpr int LD = K + 2 * RPad<T>::row;
+    static constexpr int LDU = RT + 2 * RPad<T>::row;
     static constexpr int LDP = 64 + RPad<T>::row;
     static constexpr int kMat = 64 * LD * (int)sizeof(T);
-    static constexpr int off_q = 0;
-    static constexpr int off_k = off_q + kMat;
+    // the prepass uses k, w, u and the gate cumsum only; the states pass also the q tile (Delta
+    // is staged over it); the output passes also q and the P tiles. Each mode allocates only its
+    // part, so that prepass workgroups share CUs.
+    static constexpr int off_k = 0;
     static constexpr int off_w = off_k + kMat;
     static constexpr int off_u = off_w + kMat;
-    static constexpr int off_pm = off_u + 64 * LDU * (int)sizeof(T);
-    static constexpr int off_gam = off_pm + 64 * LDP * (int)sizeof(T);
-    static constexpr int total = off_gam + 256;
+    static constexpr int off_gam = off_u + 64 * LDU * (int)sizeof(T);
+    static constexpr int end_prep = off_gam + 256;
+    static constexpr int off_q = end_prep;
+    static constexpr int end_states = off_q + kMat;
+    static constexpr int off_pm = end_states;
+    static constexpr int total = off_pm + 64 * LDP * (int)sizeof(T);
     // the output passes stage each chunk's O rows here and store them as whole rows (after the
     // next chunk's first barrier, or after the loop for the last chunk)
     static constexpr int off_o = total;
     static constexpr int total_out = off_o + 64 * LDU * (int)sizeof(T);
     static constexpr bool stage_o = total_out <= 160 * 1024;  // (fp32 at K = 128: no room)
-    // the passes that record chunk-entry states stage each one here ([RT][K], row-major) and store
-    // the workgroup's RT contiguous state rows as one linear block
+    // the passes that record chunk-entry states stage each one past their part ([RT][K],
+    // row-major) and store the workgroup's RT contiguous state rows as one linear block
     static constexpr int LDH = K + RPad<T>::row;
     static constexpr int h_bytes = RT * LDH * (int)sizeof(T);
+    static constexpr int base_of(bool out, bool rec) {
+        return out ? (stage_o ? total_out : total) : (rec ? end_states : end_prep);
+    }
     static constexpr int lds_of(bool out, bool rec) {
-        return (out && stage_o ? total_out : total) +
-               (rec && (out && stage_o ? total_out : total) + h_bytes <= 160 * 1024 ? h_bytes : 0);
+        return base_of(out, rec) + (rec && base_of(out, rec) + h_bytes <= 160 * 1024 ? h_bytes : 0);
     }
     static_assert(64 * LDU <= 64 * LD, "the q tile holds a [64][RT] Delta tile");
     // register prefetch: 16-byte vectors per thread
@@ -403,7 +412,7 @@ __global__ __launch_bounds__(RT * 4) void k_recur(RecurArgs a) {
     L.sGam = reinterpret_cast<float*>(smem + C::off_gam);
     constexpr bool kStageO = kOut && C::stage_o;
     if constexpr (kStageO) L.sO = reinterpret_cast<T*>(smem + C::off_o);
-    constexpr int kOffH = kStageO ? C::total_out : C::total;
+    constexpr int kOffH = C::base_of(kOut, kRec);
     constexpr bool kStageH = kRec && C::lds_of(kOut, kRec) > kOffH;
     if constexpr (kStageH) L.sH = reinterpret_cast<T*>(smem + kOffH);
 
