@@ -43,8 +43,8 @@ struct VCfg {
     static constexpr int NW = RT / 16;
     static constexpr int NT = NW * 64;
     static constexpr int VEC = Elem<T>::kVec;
-    static constexpr int LD = K + BPad<T>::row;     // row-major q, scaled q, k, w  [64][K]
-    static constexpr int LDD = RT + BPad<T>::row;   // row-major dO tile            [64][RT]
+    static constexpr int LD = K + 2 * BPad<T>::row;    // row-major q, scaled q, k, w  [64][K]
+    static constexpr int LDD = RT + 2 * BPad<T>::row;  // row-major dO tile            [64][RT]
     static constexpr int LDP = 64 + BPad<T>::row;   // P^T                          [64][64]
     static constexpr int kMat = 64 * LD * (int)sizeof(T);
     static constexpr int off_q = 0;                 // Q
