@@ -13,10 +13,14 @@ Prints one JSON line: tokens/s of the step (and of the forward and backward
 timed alone), TFLOP/s on algorithmic flops, the roofline fraction of the
 step's dominant kernel (algorithmic bytes over its HIP-event-timed launch
 duration) and the CPU oracle timed on this host's cores. The headline step
-recomputes the forward's intra-chunk results in the backward; "keep_forward"
-reports the opt-in variant whose backward starts from the forward's kept
-workspace instead (more memory held between the passes, less backward work);
-"qk_l2norm" the same step on raw q and k, normalised inside the library.
+is what the autograd wrapper runs by default: the backward recomputes the
+forward's intra-chunk results and CP preprocessing. "reuse_cp" reports the
+variant whose forward hands its CP decisions and sub-sequence entry states
+(fp32 [segments, H, V, K], 16 MB at the default workload) to the backward,
+which skips the forward-direction CP preprocessing; "keep_forward" the
+opt-in variant whose backward starts from the forward's kept workspace (more
+memory held between the passes, less backward work); "qk_l2norm" the same
+step on raw q and k, normalised inside the library.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--pass both|fwd|bwd]
                   [--no-cpu-baseline]
@@ -230,6 +234,7 @@ def l2norm_leg(gdn, dev, cu, cu_host, cp, timed, steps):
     q, k, v, g, beta, s0 = (dev[x] for x in ("q", "k", "v", "g", "beta", "initial_state"))
     kw = dict(cu_seqlens=cu, cu_seqlens_host=cu_host, cp_mode=cp, qk_l2norm=True)
     ws = gdn.gdn_workspace(q, v, **kw)
+    cps = gdn.gdn_cp_states(q, v, **kw)
     o = torch.empty_like(v)
     B, T, H, K = q.shape
     N = B if cu is None else int(cu.numel()) - 1
@@ -239,9 +244,9 @@ def l2norm_leg(gdn, dev, cu, cu_host, cp, timed, steps):
                  d_initial_state=torch.empty_like(sT))
 
     def step():
-        gdn.gdn_chunk_fwd(q, k, v, g, beta, s0, workspace=ws, o=o, final_state=sT, **kw)
+        gdn.gdn_chunk_fwd(q, k, v, g, beta, s0, workspace=ws, o=o, final_state=sT, cp_states=cps, **kw)
         gdn.gdn_chunk_bwd(q, k, v, g, beta, dev["d_o"], s0, dev["d_final_state"], workspace=ws,
-                          out=grads, **kw)
+                          out=grads, cp_states=cps, **kw)
 
     step()
     ms = timed(step, steps)
@@ -394,19 +399,30 @@ def main():
                  dbeta=torch.empty_like(beta), d_initial_state=torch.empty((N, H, V, K), dtype=torch.float32,
                                                                           device="cuda"))
 
-    def fwd():
-        gdn.gdn_chunk_fwd(q, k, v, g, beta, s0, cu_seqlens=cu, cu_seqlens_host=cu_host, cp_mode=cp,
-                          workspace=ws, o=o, final_state=sT)
+    # the forward's CP decisions and sub-sequence entry states, handed to the backward (None
+    # without CP, or when the backward runs without a forward)
+    cps = (gdn.gdn_cp_states(q, v, cu_seqlens=cu, cu_seqlens_host=cu_host, cp_mode=cp)
+           if do_fwd and do_bwd else None)
 
-    def bwd():
+    def fwd(carry=False):
+        gdn.gdn_chunk_fwd(q, k, v, g, beta, s0, cu_seqlens=cu, cu_seqlens_host=cu_host, cp_mode=cp,
+                          workspace=ws, o=o, final_state=sT, cp_states=cps if carry else None)
+
+    def bwd(carry=False):
         gdn.gdn_chunk_bwd(q, k, v, g, beta, dev["d_o"], s0, dev["d_final_state"], cu_seqlens=cu,
-                          cu_seqlens_host=cu_host, cp_mode=cp, workspace=ws, out=grads)
+                          cu_seqlens_host=cu_host, cp_mode=cp, workspace=ws, out=grads,
+                          cp_states=cps if carry else None)
 
     def step():
         if do_fwd:
             fwd()
         if do_bwd:
             bwd()
+
+    def step_reuse_cp():
+        # the backward takes the forward-direction CP results from the forward
+        fwd(True)
+        bwd(True)
 
     def step_keep():
         # the opt-in variant: the forward keeps W, U, T, the gate cumsum and the CP entry
@@ -472,10 +488,13 @@ def main():
     fl_step = flushed(step, args.flushed_calls)
     fl_fwd = flushed(fwd, args.flushed_calls) if do_fwd else None
     fl_bwd = flushed(bwd, args.flushed_calls) if do_bwd else None
-    ms_keep = None
+    ms_keep = ms_rcp = None
     if do_fwd and do_bwd:
         step_keep()
         ms_keep = timed(step_keep, args.steps)
+        if cps is not None:
+            step_reuse_cp()
+            ms_rcp = timed(step_reuse_cp, args.steps)
     fused = fused_leg(gdn, lambda i: flush_buf.fill_(i & 255)) if (do_fwd and not args.no_fused_leg) else None
     l2 = l2norm_leg(gdn, dev, cu, cu_host, cp, timed, args.steps) if (do_fwd and do_bwd) else None
 
@@ -589,6 +608,10 @@ def main():
         line["bwd"] = {"ms": round(ms_bwd, 4), "tokens_per_s": round(tokens / (ms_bwd * 1e-3), 1),
                        "tflops": round(counts["flops"]["bwd"] / (ms_bwd * 1e-3) / 1e12, 2), "flushed": fl_bwd,
                        "roofline": pass_roofline(alg["bwd"], counts["flops"]["bwd"], fl_bwd["median_ms"])}
+    if ms_rcp is not None:
+        line["reuse_cp"] = {"ms_per_step": round(ms_rcp, 4),
+                                "tokens_per_s": round(tokens / (ms_rcp * 1e-3), 1),
+                                "cp_states_bytes": int(cps.numel())}
     if ms_keep is not None:
         line["keep_forward"] = {"ms_per_step": round(ms_keep, 4),
                                 "tokens_per_s": round(tokens / (ms_keep * 1e-3), 1)}

@@ -11,6 +11,8 @@ missing they raise instead of computing anything elsewhere.
   gdn_chunk_bwd(...)          gradients of <dO, O> + <dS_T, S_T>
   gdn_workspace(...)          one buffer that serves a forward that keeps its intermediates
                               and the backward that reuses them
+  gdn_cp_states(...)          the small buffer that carries the forward's CP decisions and
+                              sub-sequence entry states to the backward
   gdn_intra_chunk(...)        the intra-chunk kernel alone (gate cumsum, w, u)
   gdn_cp_modes(...)           per sequence-head CP decision (0 none, 1 warmup, 2 exact, 3 mixed)
   gdn_cp_windows(...)         per-boundary CP decision (warmup window, or 0 for exact)
@@ -26,10 +28,10 @@ import numpy as np
 import torch
 
 from ._abi import (CP_MODES, EXPORTS, GDN_DTYPE_BF16, GDN_DTYPE_FP32, GDN_FLAG_BWD_ADJOINT_PASS,  # noqa: F401
-                   GDN_FLAG_FWD_FUSED, GDN_FLAG_FWD_SPLIT, GDN_FLAG_KEEP_FORWARD, GDN_FLAG_QK_L2NORM, GDN_NOALLOC_SCRATCH_BYTES, GDN_FLAG_REUSE_FORWARD, GdnDesc, GdnError, GdnKernelTime, GdnPlanInfo, check,
+                   GDN_FLAG_FWD_FUSED, GDN_FLAG_FWD_SPLIT, GDN_FLAG_KEEP_FORWARD, GDN_FLAG_QK_L2NORM, GDN_NOALLOC_SCRATCH_BYTES, GDN_FLAG_REUSE_FORWARD, GDN_FLAG_REUSE_CP, GdnDesc, GdnError, GdnKernelTime, GdnPlanInfo, check,
                    load_library, status_string)
 
-__all__ = ["gdn_plan", "gdn_chunk_fwd", "gdn_chunk_fwd_noalloc", "gdn_chunk_bwd", "gdn_workspace", "gdn_intra_chunk", "gdn_cp_modes",
+__all__ = ["gdn_plan", "gdn_chunk_fwd", "gdn_chunk_fwd_noalloc", "gdn_chunk_bwd", "gdn_workspace", "gdn_cp_states", "gdn_intra_chunk", "gdn_cp_modes",
            "gdn_cp_windows", "gdn_recurrent_fwd", "gdn_profile_enable", "gdn_profile_read", "chunk_gated_delta_rule", "load_library",
            "make_desc", "GdnError"]
 
@@ -47,7 +49,7 @@ class Desc:
 
     def __init__(self, B, T, H, K, V, dtype, *, scale=1.0, cu_seqlens=None, cu_seqlens_host=None,
                  cp_mode="auto", warmup_chunks=0, seg_chunks=0, warmup_eps=0.0, num_cus=0, flags=0,
-                 warmup_max_chunks=0, qk_l2norm=False):
+                 warmup_max_chunks=0, qk_l2norm=False, cp_states=None):
         d = GdnDesc()
         d.B, d.T, d.H, d.K, d.V = int(B), int(T), int(H), int(K), int(V)
         d.chunk = 64
@@ -80,6 +82,9 @@ class Desc:
         d.warmup_eps = float(warmup_eps)
         d.num_cus = int(num_cus)
         d.flags = int(flags) | (GDN_FLAG_QK_L2NORM if qk_l2norm else 0)
+        self._cp = cp_states
+        if cp_states is not None:
+            d.cp_states = cp_states.data_ptr()
         self.c = d
 
     @property
@@ -113,6 +118,32 @@ def gdn_workspace(q, v, *, cu_seqlens=None, cu_seqlens_host=None, cp_mode="auto"
     check(lib.gdn_chunk_fwd_workspace_size(dk.ref, ctypes.byref(f)), "gdn_chunk_fwd_workspace_size")
     check(lib.gdn_chunk_bwd_workspace_size(dr.ref, ctypes.byref(b)), "gdn_chunk_bwd_workspace_size")
     return torch.empty(max(f.value, b.value, 256), dtype=torch.uint8, device=q.device)
+
+
+def gdn_cp_states(q, v, *, cu_seqlens=None, cu_seqlens_host=None, cp_mode="auto", warmup_chunks=0,
+                  seg_chunks=0, warmup_eps=0.0, warmup_max_chunks=0, qk_l2norm=False):
+    """The buffer (uint8 device tensor) in which gdn_chunk_fwd(cp_states=...) leaves its CP
+    decisions and sub-sequence entry states for gdn_chunk_bwd(cp_states=...) on the same inputs and
+    options; None when the plan has CP off (nothing to carry)."""
+    desc = make_desc(q, v, cu_seqlens=cu_seqlens, cu_seqlens_host=cu_seqlens_host, cp_mode=cp_mode,
+                     warmup_chunks=warmup_chunks, seg_chunks=seg_chunks, warmup_eps=warmup_eps,
+                     warmup_max_chunks=warmup_max_chunks, qk_l2norm=qk_l2norm)
+    nbytes = gdn_plan(desc)["cp_states_bytes"]
+    return torch.empty(nbytes, dtype=torch.uint8, device=q.device) if nbytes else None
+
+
+def _check_cp_states(cp_states, desc, device):
+    """A caller's CP-state buffer: contiguous, on the inputs' device, 256-byte aligned and at least
+    the plan's cp_states_bytes."""
+    if cp_states is None:
+        return
+    if not isinstance(cp_states, torch.Tensor) or cp_states.device != torch.device(device):
+        raise ValueError(f"cp_states must be a tensor on {device}")
+    if not cp_states.is_contiguous() or cp_states.data_ptr() % 256:
+        raise ValueError("cp_states must be contiguous and start at a 256-byte aligned address")
+    need = gdn_plan(desc)["cp_states_bytes"]
+    if cp_states.numel() * cp_states.element_size() < need:
+        raise ValueError(f"cp_states too small: {need} bytes needed (gdn_cp_states)")
 
 
 def _workspace(nbytes: int, device, workspace=None):
@@ -175,7 +206,7 @@ def _num_seqs(q, cu_seqlens):
 def gdn_chunk_fwd(q, k, v, g, beta, initial_state=None, *, scale=1.0, cu_seqlens=None,
                   cu_seqlens_host=None, output_final_state=True, cp_mode="auto", warmup_chunks=0,
                   seg_chunks=0, warmup_eps=0.0, warmup_max_chunks=0, workspace=None, o=None, final_state=None,
-                  keep_for_backward=False, qk_l2norm=False, fused=None):
+                  keep_for_backward=False, qk_l2norm=False, fused=None, cp_states=None):
     """Forward. Returns (o, final_state or None). Runs on the current stream.
 
     fused=None lets the plan choose between the two-kernel split and the fully fused forward;
@@ -189,6 +220,9 @@ def gdn_chunk_fwd(q, k, v, g, beta, initial_state=None, *, scale=1.0, cu_seqlens
     decisions, the sub-sequence entry states, every chunk's entry state and Delta in `workspace`
     (required; see gdn_workspace), so that gdn_chunk_bwd(reuse_forward=True) on the same inputs
     and options skips recomputing them.
+
+    cp_states (see gdn_cp_states): the forward writes its CP decisions and sub-sequence entry
+    states there, for gdn_chunk_bwd(cp_states=...) to skip the forward CP preprocessing.
     """
     N = _num_seqs(q, cu_seqlens)
     _check_inputs(q, k, v, g, beta, initial_state, N)
@@ -197,7 +231,9 @@ def gdn_chunk_fwd(q, k, v, g, beta, initial_state=None, *, scale=1.0, cu_seqlens
     desc = make_desc(q, v, scale=scale, cu_seqlens=cu_seqlens, cu_seqlens_host=cu_seqlens_host,
                      cp_mode=cp_mode, warmup_chunks=warmup_chunks, seg_chunks=seg_chunks,
                      warmup_eps=warmup_eps, warmup_max_chunks=warmup_max_chunks, qk_l2norm=qk_l2norm,
-                     flags=(GDN_FLAG_KEEP_FORWARD if keep_for_backward else 0) | _fused_flag(fused))
+                     flags=(GDN_FLAG_KEEP_FORWARD if keep_for_backward else 0) | _fused_flag(fused),
+                     cp_states=cp_states)
+    _check_cp_states(cp_states, desc, q.device)
     lib = load_library()
     nbytes = ctypes.c_size_t()
     check(lib.gdn_chunk_fwd_workspace_size(desc.ref, ctypes.byref(nbytes)), "gdn_chunk_fwd_workspace_size")
@@ -250,7 +286,7 @@ def gdn_chunk_fwd_noalloc(q, k, v, g, beta, initial_state=None, *, scale=1.0, cu
 def gdn_chunk_bwd(q, k, v, g, beta, d_o, initial_state=None, d_final_state=None, *, scale=1.0,
                   cu_seqlens=None, cu_seqlens_host=None, cp_mode="auto", warmup_chunks=0, seg_chunks=0,
                   warmup_eps=0.0, warmup_max_chunks=0, workspace=None, need_d_initial_state=True, out=None,
-                  reuse_forward=False, qk_l2norm=False, adjoint_pass=False):
+                  reuse_forward=False, qk_l2norm=False, adjoint_pass=False, cp_states=None):
     """Backward. Returns dict(dq, dk, dv, dg, dbeta, d_initial_state); `out` may hold them preallocated.
 
     qk_l2norm=True: the forward normalised q and k (see gdn_chunk_fwd); dq and dk are with respect
@@ -261,6 +297,10 @@ def gdn_chunk_bwd(q, k, v, g, beta, d_o, initial_state=None, d_final_state=None,
 
     adjoint_pass=True runs the reverse adjoint recurrence as a separate pass (GDN_FLAG_BWD_ADJOINT_PASS)
     where the per-chunk kernel would otherwise carry the adjoint itself (for comparison).
+
+    cp_states: the buffer a gdn_chunk_fwd(cp_states=...) on the same inputs and options filled; the
+    backward takes the forward CP decisions and sub-sequence entry states from it (GDN_FLAG_REUSE_CP)
+    instead of recomputing them.
     """
     N = _num_seqs(q, cu_seqlens)
     _check_inputs(q, k, v, g, beta, initial_state, N)
@@ -276,7 +316,10 @@ def gdn_chunk_bwd(q, k, v, g, beta, d_o, initial_state=None, d_final_state=None,
                      cp_mode=cp_mode, warmup_chunks=warmup_chunks, seg_chunks=seg_chunks,
                      warmup_eps=warmup_eps, warmup_max_chunks=warmup_max_chunks, qk_l2norm=qk_l2norm,
                      flags=(GDN_FLAG_REUSE_FORWARD if reuse_forward else 0)
-                     | (GDN_FLAG_BWD_ADJOINT_PASS if adjoint_pass else 0))
+                     | (GDN_FLAG_BWD_ADJOINT_PASS if adjoint_pass else 0)
+                     | (GDN_FLAG_REUSE_CP if cp_states is not None else 0),
+                     cp_states=cp_states)
+    _check_cp_states(cp_states, desc, q.device)
     lib = load_library()
     nbytes = ctypes.c_size_t()
     check(lib.gdn_chunk_bwd_workspace_size(desc.ref, ctypes.byref(nbytes)), "gdn_chunk_bwd_workspace_size")
@@ -398,39 +441,46 @@ def gdn_profile_read() -> dict:
 
 class _GDNFunction(torch.autograd.Function):
     @staticmethod
-    def forward(ctx, q, k, v, g, beta, initial_state, scale, cu_seqlens, cu_host, cp_mode, keep, l2):
+    def forward(ctx, q, k, v, g, beta, initial_state, scale, cu_seqlens, cu_host, cp_mode, keep, l2, carry_cp):
         # one host copy of cu_seqlens for every call of the step (planning reads the host copy;
         # taking it from the device would synchronise once per call)
         if cu_seqlens is not None and cu_host is None:
             cu_host = cu_seqlens.detach().cpu()
         cu = dict(cu_seqlens=cu_seqlens, cu_seqlens_host=cu_host)
         ws = gdn_workspace(q, v, cp_mode=cp_mode, qk_l2norm=l2, **cu) if keep else None
+        # with carry_cp the CP decisions and sub-sequence entry states (a few MB) go to the
+        # backward, which then skips the forward CP preprocessing; with keep, the workspace
+        # carries them already
+        cps = gdn_cp_states(q, v, cp_mode=cp_mode, qk_l2norm=l2, **cu) if carry_cp and not keep else None
         o, sT = gdn_chunk_fwd(q, k, v, g, beta, initial_state, scale=scale, cp_mode=cp_mode, workspace=ws,
-                              keep_for_backward=keep, qk_l2norm=l2, **cu)
+                              keep_for_backward=keep, qk_l2norm=l2, cp_states=cps, **cu)
         ctx.save_for_backward(q, k, v, g, beta, initial_state, cu_seqlens)
         ctx.cu_host = cu_host
         ctx.scale = scale
         ctx.cp_mode = cp_mode
         ctx.l2 = l2
         ctx.ws = ws
+        ctx.cps = cps
         return o, sT
 
     @staticmethod
     def backward(ctx, d_o, d_sT):
         q, k, v, g, beta, s0, cu = ctx.saved_tensors
         ws, ctx.ws = ctx.ws, None
+        cps, ctx.cps = ctx.cps, None
         gr = gdn_chunk_bwd(q, k, v, g, beta, d_o.contiguous(), s0,
                            None if d_sT is None else d_sT.contiguous(), scale=ctx.scale,
                            cu_seqlens=cu, cu_seqlens_host=ctx.cu_host, cp_mode=ctx.cp_mode,
                            need_d_initial_state=s0 is not None, workspace=ws, reuse_forward=ws is not None,
-                           qk_l2norm=ctx.l2)
+                           qk_l2norm=ctx.l2, cp_states=cps)
         return (gr["dq"], gr["dk"], gr["dv"], gr["dg"], gr["dbeta"], gr["d_initial_state"],
-                None, None, None, None, None, None)
+                None, None, None, None, None, None, None)
 
 
 def chunk_gated_delta_rule(q, k, v, g, beta, scale: float = 1.0, initial_state=None,
                            output_final_state: bool = True, cu_seqlens=None, cp_mode: str = "auto",
-                           keep_intermediates: bool = False, qk_l2norm: bool = False, cu_seqlens_host=None):
+                           keep_intermediates: bool = False, qk_l2norm: bool = False, cu_seqlens_host=None,
+                           carry_cp_states: bool = False):
     """High-level call: (o, final_state) with autograd through gdn_chunk_bwd.
 
     q, k: [B,T,H,K]; v: [B,T,H,V] (bf16 or fp32); g (natural-log decay) and beta: [B,T,H] fp32;
@@ -439,11 +489,13 @@ def chunk_gated_delta_rule(q, k, v, g, beta, scale: float = 1.0, initial_state=N
     kept for the backward).
     keep_intermediates=True holds the forward's workspace (W, U, T, gate cumsum, CP entry states,
     chunk states and Delta) until the backward, which then skips recomputing them: more memory,
-    less backward time. qk_l2norm=True normalises q and k rows inside the library
+    less backward time. carry_cp_states=True keeps only the forward's CP decisions and sub-sequence
+    entry states (gdn_cp_states: fp32 [segments, H, V, K], 16 MB at B=1 H=16 T=32K) for the
+    backward, which then skips the forward CP preprocessing and recomputes the rest. qk_l2norm=True normalises q and k rows inside the library
     (x / sqrt(sum x^2 + 1e-6)); gradients flow to the raw q and k.
     """
+    grad = torch.is_grad_enabled() and any(x is not None and x.requires_grad
+                                           for x in (q, k, v, g, beta, initial_state))
     o, sT = _GDNFunction.apply(q, k, v, g, beta, initial_state, scale, cu_seqlens, cu_seqlens_host, cp_mode,
-                               bool(keep_intermediates and torch.is_grad_enabled()
-                                    and any(x.requires_grad for x in (q, k, v, g, beta))),
-                               bool(qk_l2norm))
+                               bool(keep_intermediates and grad), bool(qk_l2norm), bool(carry_cp_states and grad))
     return (o, sT) if output_final_state else (o, None)

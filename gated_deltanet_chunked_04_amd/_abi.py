@@ -16,8 +16,8 @@ GDN_OK, GDN_ERR_INVALID_ARG, GDN_ERR_UNSUPPORTED, GDN_ERR_WORKSPACE, GDN_ERR_HIP
 GDN_DTYPE_BF16, GDN_DTYPE_FP32 = 0, 1
 CP_MODES = {"auto": 0, "off": 1, "on": 2, "exact": 3, "warmup": 4, "pages": 5}
 GDN_FLAG_KEEP_FORWARD, GDN_FLAG_REUSE_FORWARD, GDN_FLAG_QK_L2NORM, GDN_FLAG_BWD_ADJOINT_PASS = 1, 2, 4, 8
-GDN_FLAG_FWD_FUSED, GDN_FLAG_FWD_SPLIT = 16, 32
-GDN_ABI_VERSION = 9
+GDN_FLAG_FWD_FUSED, GDN_FLAG_FWD_SPLIT, GDN_FLAG_REUSE_CP = 16, 32, 64
+GDN_ABI_VERSION = 10
 GDN_NOALLOC_SCRATCH_BYTES = 128 << 20
 
 # Declared entry points of include/gdn.h (checked by the ABI test).
@@ -37,6 +37,7 @@ class GdnDesc(ctypes.Structure):
         ("seg_chunks", ctypes.c_int32), ("warmup_eps", ctypes.c_float),
         ("num_cus", ctypes.c_int32), ("flags", ctypes.c_int32), ("warmup_max_chunks", ctypes.c_int32),
         ("reserved", ctypes.c_int32 * 5),
+        ("cp_states", ctypes.c_void_p),
     ]
 
 
@@ -48,6 +49,7 @@ class GdnPlanInfo(ctypes.Structure):
         ("max_len", ctypes.c_int64), ("total_chunks", ctypes.c_int64),
         ("total_segments", ctypes.c_int64),
         ("fwd_workspace_bytes", ctypes.c_size_t), ("bwd_workspace_bytes", ctypes.c_size_t),
+        ("cp_states_bytes", ctypes.c_size_t),
         ("fused_fwd", ctypes.c_int32), ("bwd_carried", ctypes.c_int32),
         ("reserved_out", ctypes.c_int32 * 2),
     ]

@@ -52,6 +52,8 @@ struct Plan {
     // backward workspace: the forward's layout, then these
     size_t o_modes_r = 0, o_bwin_r = 0, o_seginit_r = 0, o_prep_r = 0, o_h = 0, o_gst = 0, o_tm = 0, o_dl = 0, o_ddl = 0,
            bwd_bytes = 0;
+    // desc->cp_states: the forward-direction CP decisions, windows and sub-sequence entry states
+    size_t c_bwin = 0, c_seginit = 0, cp_bytes = 0;
     int32_t cus = 256;   // compute units (desc->num_cus, else the device's)
     int32_t bwd_ok = 1;  // fp32 backward supports K = V = 64 only (LDS)
     int32_t fused = 0;   // the forward runs fully fused (no CP, bf16, no kept intermediates)
@@ -71,8 +73,9 @@ gdn_status make_plan(const gdn_desc* d, Plan& p) {
     for (int i = 0; i < 5; ++i)
         if (d->reserved[i] != 0) return GDN_ERR_INVALID_ARG;
     if (d->flags & ~(GDN_FLAG_KEEP_FORWARD | GDN_FLAG_REUSE_FORWARD | GDN_FLAG_QK_L2NORM | GDN_FLAG_BWD_ADJOINT_PASS |
-                     GDN_FLAG_FWD_FUSED | GDN_FLAG_FWD_SPLIT))
+                     GDN_FLAG_FWD_FUSED | GDN_FLAG_FWD_SPLIT | GDN_FLAG_REUSE_CP))
         return GDN_ERR_INVALID_ARG;
+    if (reinterpret_cast<uintptr_t>(d->cp_states) % kAlign) return GDN_ERR_INVALID_ARG;
     if ((d->flags & GDN_FLAG_FWD_FUSED) && (d->flags & GDN_FLAG_FWD_SPLIT)) return GDN_ERR_INVALID_ARG;
     if (d->B < 1 || d->T < 0 || d->H < 1 || d->K < 1 || d->V < 1) return GDN_ERR_INVALID_ARG;
     if (!(d->chunk == 0 || d->chunk == 64)) return GDN_ERR_UNSUPPORTED;
@@ -200,7 +203,12 @@ gdn_status make_plan(const gdn_desc* d, Plan& p) {
     if (p.cp_on) {
         p.o_seginit = take((size_t)p.total_segs * H * V * K * 4);
         p.o_prep = take((size_t)p.total_segs * H * (V + K) * K * 4);
+        // the same three regions in the caller's desc->cp_states
+        p.c_bwin = align_up((size_t)p.N * H * 4);
+        p.c_seginit = p.c_bwin + align_up((size_t)p.total_segs * H * 4);
+        p.cp_bytes = p.c_seginit + align_up((size_t)p.total_segs * H * V * K * 4);
     }
+    if ((d->flags & GDN_FLAG_REUSE_CP) && p.cp_on && !d->cp_states) return GDN_ERR_INVALID_ARG;
     // T = (I + A)^{-1} per chunk, the chunk-entry states h and Delta = U - W S^T: written by
     // the forward when it keeps its intermediates, always by the backward (which reads them);
     // the same offsets in both layouts
@@ -378,6 +386,25 @@ void* kn_of(const gdn_desc* d, const Plan& p, unsigned char* ws) {
     return (d->flags & GDN_FLAG_QK_L2NORM) ? ws + p.o_kn : nullptr;
 }
 
+// Where the forward-direction CP decisions (per sequence-head mode, per boundary window) and
+// sub-sequence entry states live: the caller's desc->cp_states when set and `caller` (the
+// forward always writes them there; a backward reads them there when it reuses the forward's
+// results), else the workspace.
+struct CpRegion {
+    int32_t* modes;
+    int32_t* bwin;
+    float* seginit;  // null without CP
+};
+CpRegion cp_region(const gdn_desc* d, const Plan& p, unsigned char* ws, bool caller) {
+    if (caller && d->cp_states && p.cp_on) {
+        unsigned char* c = static_cast<unsigned char*>(d->cp_states);
+        return {reinterpret_cast<int32_t*>(c), reinterpret_cast<int32_t*>(c + p.c_bwin),
+                reinterpret_cast<float*>(c + p.c_seginit)};
+    }
+    return {reinterpret_cast<int32_t*>(ws + p.o_modes), reinterpret_cast<int32_t*>(ws + p.o_bwin),
+            p.cp_on ? reinterpret_cast<float*>(ws + p.o_seginit) : nullptr};
+}
+
 // Tables (varlen) + intra-chunk kernel into the given output buffers.
 // The varlen tables' arguments (built on the device from cu_seqlens into the workspace).
 TableArgs table_args(const gdn_desc* d, const Plan& p, unsigned char* ws) {
@@ -512,6 +539,7 @@ gdn_status gdn_plan(const gdn_desc* desc, gdn_plan_info* out) {
     out->total_segments = p.total_segs;
     out->fwd_workspace_bytes = p.fwd_bytes;
     out->bwd_workspace_bytes = p.bwd_bytes;
+    out->cp_states_bytes = p.cp_bytes;
     out->fused_fwd = p.fused;
     out->bwd_carried = p.carry;
     return GDN_OK;
@@ -607,12 +635,13 @@ gdn_status run_fwd(const gdn_desc* desc, const Plan& p, const void* q, const voi
     ra.scale = desc->scale;
     ra.use_cp = p.cp_on;
     ra.q_l2 = kn != nullptr;
-    int32_t* modes = reinterpret_cast<int32_t*>(ws + p.o_modes);
-    int32_t* bwin = reinterpret_cast<int32_t*>(ws + p.o_bwin);
+    const CpRegion cpr = cp_region(desc, p, ws, true);
+    int32_t* modes = cpr.modes;
+    int32_t* bwin = cpr.bwin;
     ra.modes = modes;
     ra.bwin = bwin;
     if (p.cp_on) {
-        float* seginit = reinterpret_cast<float*>(ws + p.o_seginit);
+        float* seginit = cpr.seginit;
         float* prep = reinterpret_cast<float*>(ws + p.o_prep);
         if ((s = run_decide(desc, p, ws, modes, bwin, st)) != GDN_OK) return s;
         ra.seginit_out = seginit;
@@ -686,12 +715,16 @@ gdn_status gdn_chunk_bwd(const gdn_desc* desc, const void* q, const void* k, con
     // from the caller's after (1) and joined to it before (4).
     // both CP decisions (forward windows for the state pass, windows after each segment for
     // the adjoint pass) in one launch ahead of the fork
-    int32_t* modes = reinterpret_cast<int32_t*>(ws + p.o_modes);
-    int32_t* bwin = reinterpret_cast<int32_t*>(ws + p.o_bwin);
+    // the forward-direction CP results come from the forward (kept workspace or desc->cp_states)
+    // or are recomputed into the workspace
+    const bool reuse_cp = reuse || (desc->flags & GDN_FLAG_REUSE_CP);
+    const CpRegion cpr = cp_region(desc, p, ws, reuse_cp);
+    int32_t* modes = cpr.modes;
+    int32_t* bwin = cpr.bwin;
     int32_t* modes_r = p.cp_on ? reinterpret_cast<int32_t*>(ws + p.o_modes_r) : nullptr;
     int32_t* bwin_r = p.cp_on ? reinterpret_cast<int32_t*>(ws + p.o_bwin_r) : nullptr;
     if (p.cp_on) {
-        if (reuse) s = run_decide(desc, p, ws, modes_r, bwin_r, st, 1);
+        if (reuse_cp) s = run_decide(desc, p, ws, modes_r, bwin_r, st, 1);
         else s = run_decide(desc, p, ws, modes, bwin, st, 0, modes_r, bwin_r);
         if (s != GDN_OK) return s;
     }
@@ -723,8 +756,8 @@ gdn_status gdn_chunk_bwd(const gdn_desc* desc, const void* q, const void* k, con
     ra.bwin = bwin;
     ra.hstates = ws + p.o_h;
     ra.delta = ws + p.o_dl;
-    if (!reuse && p.cp_on) {
-        float* seginit = reinterpret_cast<float*>(ws + p.o_seginit);
+    if (!reuse_cp && p.cp_on) {
+        float* seginit = cpr.seginit;
         float* prep = reinterpret_cast<float*>(ws + p.o_prep);
         ra.seginit_out = seginit;
         ra.prep = prep;
@@ -738,6 +771,8 @@ gdn_status gdn_chunk_bwd(const gdn_desc* desc, const void* q, const void* k, con
         sa.modes = modes;
         GDN_LAUNCH(kKScan, st, launch_scan(sa, desc->dtype, st));
         ra.seginit = seginit;
+    } else if (p.cp_on) {
+        ra.seginit = cpr.seginit;
     }
     if (!reuse) GDN_LAUNCH(kKRecurStates, st, launch_recur(ra, desc->dtype, kRecurStates, p.total_segs, vtiles, st));
     // 3. reverse adjoint pass, with CP mirrored (windows and scan from the sequence end)
@@ -832,7 +867,8 @@ gdn_status gdn_recurrent_fwd(const gdn_desc* desc, const void* q, const void* k,
     if (!desc) return GDN_ERR_INVALID_ARG;
     for (int i = 0; i < 5; ++i)
         if (desc->reserved[i] != 0) return GDN_ERR_INVALID_ARG;
-    if (desc->cu_seqlens || desc->cu_seqlens_host || (desc->flags & ~GDN_FLAG_QK_L2NORM)) return GDN_ERR_INVALID_ARG;
+    if (desc->cu_seqlens || desc->cu_seqlens_host || desc->cp_states || (desc->flags & ~GDN_FLAG_QK_L2NORM))
+        return GDN_ERR_INVALID_ARG;
     if (desc->B < 1 || desc->T < 0 || desc->H < 1 || desc->K < 1 || desc->V < 1) return GDN_ERR_INVALID_ARG;
     if (!(desc->K == 64 || desc->K == 128) || !(desc->V == 64 || desc->V == 128)) return GDN_ERR_UNSUPPORTED;
     if (desc->dtype != GDN_DTYPE_BF16 && desc->dtype != GDN_DTYPE_FP32) return GDN_ERR_INVALID_ARG;

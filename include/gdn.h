@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 9
+#define GDN_ABI_VERSION 10
 
 typedef enum gdn_status {
     GDN_OK = 0,
@@ -135,6 +135,20 @@ typedef enum gdn_cp_mode {
 #define GDN_FLAG_FWD_FUSED 16
 #define GDN_FLAG_FWD_SPLIT 32
 
+/* Carrying the forward's CP results to the backward (a checkpoint of a few MB instead of the
+ * intra-chunk intermediates): with CP on, the backward's chunk-state pass needs the same
+ * sub-sequence entry states that the forward's CP preprocessing (decision, prepass, segment scan;
+ * ollai.cn article, "technical principles") already produced. gdn_chunk_fwd writes its CP
+ * decisions and those states to desc->cp_states when that pointer is set; gdn_chunk_bwd with
+ * GDN_FLAG_REUSE_CP reads them from there instead of running the forward-direction
+ * preprocessing again (it still recomputes the intra-chunk pass and decides the reverse
+ * direction itself). The caller guarantees that a gdn_chunk_fwd of the same inputs and
+ * descriptor (flags aside) last wrote the buffer. A GDN_FLAG_REUSE_FORWARD backward reads them
+ * there too when the pointer is set (its forward wrote them there); any other backward leaves
+ * the buffer alone. Without CP the flag does nothing and the buffer is not touched.
+ * GDN_FLAG_REUSE_CP with CP on and desc->cp_states NULL returns GDN_ERR_INVALID_ARG. */
+#define GDN_FLAG_REUSE_CP 64
+
 /* Problem descriptor. Zero-initialise, then fill. */
 typedef struct gdn_desc {
     int64_t B, T, H, K, V;          /* batch, tokens per row (packed total if varlen), heads, key dim, value dim */
@@ -156,6 +170,9 @@ typedef struct gdn_desc {
                                        length (at least warmup_chunks, at most warmup_chunks+63);
                                        equal to warmup_chunks keeps one fixed window */
     int32_t reserved[5];            /* must be zero */
+    void* cp_states;                /* device buffer of gdn_plan_info.cp_states_bytes bytes, 256-byte
+                                       aligned, or NULL: see GDN_FLAG_REUSE_CP (owned by the caller;
+                                       gdn_recurrent_fwd requires NULL) */
 } gdn_desc;
 
 /* Host-side plan of a call (filled by gdn_plan; no device work). */
@@ -172,6 +189,8 @@ typedef struct gdn_plan_info {
     int64_t total_segments;         /* sum over sequences of sub-sequence counts */
     size_t fwd_workspace_bytes;
     size_t bwd_workspace_bytes;
+    size_t cp_states_bytes;         /* size of desc->cp_states (CP decisions and sub-sequence entry
+                                       states, fp32 [total_segments, H, V, K]); 0 when CP is off */
     int32_t fused_fwd;              /* 1 if gdn_chunk_fwd runs the fully fused forward */
     int32_t bwd_carried;            /* 1 if gdn_chunk_bwd's per-chunk kernel carries the adjoint
                                        (no separate adjoint pass) */
@@ -241,7 +260,8 @@ gdn_status gdn_chunk_bwd_workspace_size(const gdn_desc* desc, size_t* bytes);
  *   dg, dbeta       : outputs [B,T,H] fp32 (dg is with respect to the raw per-token g)
  *   d_initial_state : output [N,H,V,K] fp32, or NULL (not written)
  * The forward is recomputed inside, unless desc->flags has GDN_FLAG_REUSE_FORWARD (then the
- * intra-chunk pass and the forward CP preprocessing come from the workspace; see above).
+ * intra-chunk pass and the forward CP preprocessing come from the workspace; see above) or
+ * GDN_FLAG_REUSE_CP (then the forward CP preprocessing comes from desc->cp_states).
  * The reverse adjoint pass runs on a second stream of the library's (one per device, made on
  * the first call with the default priority), forked from `stream` and joined back to it
  * before the per-chunk gradients: work enqueued on `stream` afterwards sees every output.

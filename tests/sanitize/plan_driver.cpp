@@ -96,6 +96,21 @@ int main() {
         EXPECT(gdn_chunk_fwd(&d, fake(2), fake(3), fake(4), (const float*)fake(5), (const float*)fake(6), nullptr,
                              fake(7), (float*)fake(8), fake(9), p.fwd_workspace_bytes, nullptr) == GDN_OK);
         EXPECT(g_launches > before || cu[N] == 0);
+        EXPECT((p.cp_states_bytes > 0) == (p.cp_on != 0));
+        if (p.cp_on) {
+            // the same forward leaving its CP results in a caller buffer: the same launches
+            const int nf = g_launches - before;
+            gdn_desc c = d;
+            c.cp_states = fake(14);
+            const int l1 = g_launches;
+            EXPECT(gdn_chunk_fwd(&c, fake(2), fake(3), fake(4), (const float*)fake(5), (const float*)fake(6), nullptr,
+                                 fake(7), (float*)fake(8), fake(9), p.fwd_workspace_bytes, nullptr) == GDN_OK);
+            EXPECT(g_launches - l1 == nf);
+            c.cp_states = nullptr;
+            c.flags |= GDN_FLAG_REUSE_CP;  // a backward told to reuse it needs it
+            EXPECT(gdn_plan(&c, &p) == GDN_ERR_INVALID_ARG);
+            EXPECT(gdn_plan(&d, &p) == GDN_OK);
+        }
         EXPECT(gdn_intra_chunk(&d, fake(3), fake(4), (const float*)fake(5), (const float*)fake(6), (float*)fake(10),
                                fake(11), fake(12), fake(9), p.fwd_workspace_bytes, nullptr) == GDN_OK);
         EXPECT(gdn_cp_modes(&d, fake(3), fake(4), (const float*)fake(5), (const float*)fake(6), (int32_t*)fake(13),
@@ -120,7 +135,9 @@ int main() {
         gdn_desc e = d;
         e.reserved[4] = 1;
         EXPECT(gdn_plan(&e, &p) == GDN_ERR_INVALID_ARG);
-        e = d; e.flags = 64;
+        e = d; e.flags = 128;
+        EXPECT(gdn_plan(&e, &p) == GDN_ERR_INVALID_ARG);
+        e = d; e.cp_states = reinterpret_cast<void*>(0x10010);  // misaligned
         EXPECT(gdn_plan(&e, &p) == GDN_ERR_INVALID_ARG);
         e = d; e.chunk = 32;
         EXPECT(gdn_plan(&e, &p) == GDN_ERR_UNSUPPORTED);

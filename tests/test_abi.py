@@ -38,7 +38,7 @@ def test_exports_every_declared_symbol(lib):
     assert set(declared) == set(_abi.EXPORTS)
     for name in declared:
         assert hasattr(lib, name), name
-    assert lib.gdn_abi_version() == _abi.GDN_ABI_VERSION == 9
+    assert lib.gdn_abi_version() == _abi.GDN_ABI_VERSION == 10
 
 
 def test_status_strings(lib):
@@ -157,7 +157,7 @@ def test_argument_errors(lib):
     d2.c.reserved[3] = 1
     assert lib.gdn_plan(d2.ref, ctypes.byref(out)) == 1
     # unknown flag bits
-    for bad_flag in (64, 128, 1 << 30, -1):
+    for bad_flag in (128, 256, 1 << 30, -1):
         d2 = desc()
         d2.c.flags = bad_flag
         assert lib.gdn_plan(d2.ref, ctypes.byref(out)) == 1, bad_flag
@@ -211,6 +211,9 @@ def test_recurrent_errors_before_launch(lib):
         assert lib.gdn_recurrent_fwd(d2.ref, p, p, p, p, p, None, p, p, None) == code, field
     d2 = desc(T=1, H=2)
     d2.c.cu_seqlens = 0x1000  # no packed sequences in the recurrent form
+    assert lib.gdn_recurrent_fwd(d2.ref, p, p, p, p, p, None, p, p, None) == 1
+    d2 = desc(T=1, H=2)
+    d2.c.cp_states = 0x1000  # no CP in the recurrent form
     assert lib.gdn_recurrent_fwd(d2.ref, p, p, p, p, p, None, p, p, None) == 1
 
 
@@ -287,3 +290,32 @@ def test_carried_backward_plan():
     assert plan(B=1, H=16, T=32768, dtype=torch.float32)["bwd_carried"] == 0
     assert plan(B=1, H=16, T=32768, K=64, V=64)["bwd_carried"] == 0
     assert plan(B=1, H=16, T=32768, flags=gdn.GDN_FLAG_BWD_ADJOINT_PASS)["bwd_carried"] == 0
+
+
+def test_cp_states_plan(lib):
+    """The buffer that carries the forward's CP results to the backward: the per sequence-head
+    modes, the per-boundary windows and the fp32 sub-sequence entry states [segments, H, V, K],
+    each region 256-byte aligned; none without CP. A backward told to reuse it needs it (with CP
+    on), and it must be 256-byte aligned."""
+    p = plan()  # B=1 H=16 T=32K: CP on, 16 sub-sequences of 32 chunks
+    assert p["cp_on"] == 1 and p["total_segments"] == 16
+    assert p["cp_states_bytes"] == 256 + 1024 + 16 * 16 * 128 * 128 * 4
+    v = plan(B=1, H=4, T=4000, K=64, V=128, dtype=torch.float32, cp_mode="on")
+    a = lambda n: -(-n // 256) * 256  # noqa: E731
+    assert v["cp_states_bytes"] == a(4 * 4) + a(v["total_segments"] * 4 * 4) + v["total_segments"] * 4 * 128 * 64 * 4
+    assert plan(B=8, H=32, T=4096)["cp_on"] == 0 and plan(B=8, H=32, T=4096)["cp_states_bytes"] == 0
+    out = _abi.GdnPlanInfo()
+    d = desc(flags=_abi.GDN_FLAG_REUSE_CP)  # CP on, no buffer
+    assert lib.gdn_plan(d.ref, ctypes.byref(out)) == 1
+    d.c.cp_states = 0x10000
+    assert lib.gdn_plan(d.ref, ctypes.byref(out)) == 0
+    d.c.cp_states = 0x10010  # misaligned
+    assert lib.gdn_plan(d.ref, ctypes.byref(out)) == 1
+    # without CP the flag does nothing
+    d = desc(B=8, H=32, T=4096, flags=_abi.GDN_FLAG_REUSE_CP)
+    assert lib.gdn_plan(d.ref, ctypes.byref(out)) == 0 and out.cp_on == 0
+    # the workspaces do not depend on it
+    d = desc(flags=_abi.GDN_FLAG_REUSE_CP)
+    d.c.cp_states = 0x10000
+    r = gdn.gdn_plan(d)
+    assert (r["fwd_workspace_bytes"], r["bwd_workspace_bytes"]) == (p["fwd_workspace_bytes"], p["bwd_workspace_bytes"])

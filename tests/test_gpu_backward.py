@@ -75,6 +75,12 @@ CASES = [
     (torch.bfloat16, 64, 128, "exact", dict(seg_chunks=4)),
     (torch.bfloat16, 128, 64, "off", {}),
     (torch.bfloat16, 64, 64, "auto", {}),
+    # longer sub-sequences (8 chunks or more), ragged ones included
+    (torch.float32, 64, 64, "exact", dict(seg_chunks=8)),
+    (torch.float32, 64, 64, "exact", dict(seg_chunks=9)),
+    (torch.bfloat16, 128, 128, "exact", dict(seg_chunks=8)),
+    (torch.bfloat16, 64, 128, "exact", dict(seg_chunks=11)),
+    (torch.bfloat16, 128, 128, "on", dict(seg_chunks=8, warmup_chunks=3)),
 ]
 
 
@@ -87,7 +93,8 @@ def test_backward_small(gpu_lib, dtype, K, V, cp, kw):
 
 
 @pytest.mark.parametrize("cp,kw", [("off", {}), ("exact", dict(seg_chunks=2)),
-                                   ("warmup", dict(seg_chunks=3, warmup_chunks=2))])
+                                   ("warmup", dict(seg_chunks=3, warmup_chunks=2)),
+                                   ("exact", dict(seg_chunks=8)), ("on", dict(seg_chunks=9, warmup_chunks=2))])
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
 def test_backward_varlen(gpu_lib, cp, kw, dtype):
     K = V = 64 if dtype == torch.float32 else 128
@@ -169,6 +176,14 @@ def test_backward_edge_prefill_32k(gpu_lib):
     torch.cuda.synchronize()
     for n in NAMES:
         assert torch.equal(got[n], ref[n]), n
+    # the variant whose forward hands its CP results to the backward
+    cps = gdn.gdn_cp_states(d["q"], d["v"])
+    assert cps is not None
+    gdn.gdn_chunk_fwd(*args, d["initial_state"], workspace=ws, cp_states=cps)
+    got = gdn.gdn_chunk_bwd(*args, d["d_o"], d["initial_state"], d["d_final_state"], workspace=ws, cp_states=cps)
+    torch.cuda.synchronize()
+    for n in NAMES:
+        assert torch.equal(got[n], ref[n]), n
     # one warmup head and one exact head
     heads = [int((modes[0] == 1).nonzero()[0]), int((modes[0] >= 2).nonzero()[0])]
     errs = compare({n: ref[n].cpu() for n in NAMES}, oracle_bwd(inp, heads=heads), 1e-2, heads=heads)
@@ -211,6 +226,43 @@ def test_backward_reuses_forward(gpu_lib, dtype, K, V, cp, kw, lengths):
         assert torch.equal(got[n], ref[n]), n
     # and against the oracle
     compare(got, oracle_bwd(inp, scale=0.8), tol_for(dtype))
+    # only the CP decisions and sub-sequence entry states handed over (none without CP)
+    plain = {n: x for n, x in opts.items() if n != "scale"}
+    cps = gdn.gdn_cp_states(d["q"], d["v"], **plain)
+    assert (cps is None) == (gdn.gdn_plan(gdn.make_desc(d["q"], d["v"], **plain))["cp_on"] == 0)
+    if cps is not None:
+        cps.fill_(0xA5)
+        ws.fill_(0x5A)
+        o2, s2 = gdn.gdn_chunk_fwd(*args, d["initial_state"], workspace=ws, cp_states=cps, **opts)
+        ws.fill_(0x5A)  # the backward reads nothing of the forward's workspace
+        got = gdn.gdn_chunk_bwd(*args, d["d_o"], d["initial_state"], d["d_final_state"], workspace=ws,
+                                cp_states=cps, **opts)
+        torch.cuda.synchronize()
+        assert torch.equal(o0, o2) and torch.equal(s0, s2)
+        for n in NAMES:
+            assert torch.equal(got[n], ref[n]), n
+
+
+def test_autograd_wrapper_carries_cp_states(gpu_lib):
+    """The autograd wrapper can hand the forward's CP results to the backward: its gradients equal the
+    recomputing backward's bit for bit, with packed sequences and CP on."""
+    gdn = gpu_lib
+    inp = with_grads(small_inputs(H=3, K=128, V=128, dtype=torch.bfloat16, lengths=[700, 3000, 65, 2500], seed=18))
+    d = to_dev(inp)
+    opts = dict(cu_seqlens=d["cu_seqlens"], cp_mode="on")
+    assert gdn.gdn_cp_states(d["q"], d["v"], seg_chunks=0, **opts) is not None
+    leaves = {n: d[n].clone().requires_grad_(True) for n in ("q", "k", "v", "g", "beta", "initial_state")}
+    o, sT = gdn.chunk_gated_delta_rule(leaves["q"], leaves["k"], leaves["v"], leaves["g"], leaves["beta"],
+                                       initial_state=leaves["initial_state"], carry_cp_states=True, **opts)
+    loss = (o.float() * d["d_o"].float()).sum() + (sT * d["d_final_state"]).sum()
+    loss.backward()
+    ref = gdn.gdn_chunk_bwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["d_o"], d["initial_state"],
+                            d["d_final_state"], **opts)
+    torch.cuda.synchronize()
+    pairs = dict(q="dq", k="dk", v="dv", g="dg", beta="dbeta", initial_state="d_initial_state")
+    for n, r in pairs.items():
+        assert torch.equal(leaves[n].grad, ref[r]), n
+    compare(ref, oracle_bwd(inp), 1e-2)
 
 
 def test_autograd_wrapper_keep_intermediates(gpu_lib):

@@ -50,6 +50,12 @@ CASES = [
     (torch.bfloat16, 64, 128, "exact", dict(seg_chunks=4)),
     (torch.bfloat16, 128, 64, "warmup", dict(seg_chunks=4)),
     (torch.bfloat16, 64, 64, "auto", {}),
+    # longer sub-sequences (8 chunks or more), ragged ones included
+    (torch.float32, 64, 64, "exact", dict(seg_chunks=8)),
+    (torch.float32, 128, 128, "exact", dict(seg_chunks=9)),
+    (torch.bfloat16, 128, 128, "exact", dict(seg_chunks=8)),
+    (torch.bfloat16, 64, 128, "exact", dict(seg_chunks=11)),
+    (torch.bfloat16, 128, 128, "on", dict(seg_chunks=8, warmup_chunks=3)),
 ]
 
 
@@ -64,7 +70,8 @@ def test_forward_small(gpu_lib, dtype, K, V, cp, kw):
 
 
 @pytest.mark.parametrize("cp,kw", [("off", {}), ("exact", dict(seg_chunks=2)),
-                                   ("warmup", dict(seg_chunks=3, warmup_chunks=2))])
+                                   ("warmup", dict(seg_chunks=3, warmup_chunks=2)),
+                                   ("exact", dict(seg_chunks=8)), ("on", dict(seg_chunks=9, warmup_chunks=2))])
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
 def test_forward_varlen(gpu_lib, cp, kw, dtype):
     lengths = [1, 63, 64, 65, 0, 700, 1500, 129]
