@@ -357,9 +357,12 @@ struct SeqInfo {
 // T = (I + A)^{-1} for a 64x64 strictly lower triangular fp32 A in LDS (leading dimension
 // kLdA), written to T in LDS; the first four waves of the workgroup do the work (all of its
 // waves must call it: it contains barriers). Diagonal 16x16 blocks by forward
-// substitution (wave b, lanes 0..15 = the columns of block b), then the off-diagonal
-// blocks level by level (T_ij = -T_ii sum_m A_im T_mj) with
-// fp32 matrix-core products. Starts and ends with the LDS in a consistent state for the
+// substitution (wave b for block b), then the off-diagonal blocks with fp32 matrix-core
+// products in two levels, as a 2 x 2 blocking of 32 x 32 blocks: the off-diagonal blocks
+// T_10 and T_32 of the two diagonal 32-blocks (T_ij = -T_ii A_ij T_jj), then the four blocks
+// of the off-diagonal 32-block, T_ij = -sum_m T_im Y_mj with Y_mj = sum_n A_mn T_nj, one per
+// wave (three barriers after the substitution instead of four for a level per block
+// diagonal). Starts and ends with the LDS in a consistent state for the
 // whole workgroup (the caller's barrier before, this routine's last barrier after). Writes
 // only the diagonal and strictly lower blocks of T: the caller zeroes the strictly upper
 // blocks once (tri_zero_upper64), since nothing writes them afterwards.
@@ -433,11 +436,42 @@ __device__ __forceinline__ void tri_inverse64(float* sA, float* sT) {
         for (int i = 0; i < 4; ++i) sT[(16 * b + gq + 4 * i) * kLdA + 16 * b + ln] = x[i];
     }
     lds_sync();
-    if (wave < 3) tri_offdiag_block(sA, sT, wave + 1, wave);
+    // the off-diagonal blocks of the two 32 x 32 diagonal blocks: T_10 and T_32
+    if (wave < 2) tri_offdiag_block(sA, sT, 2 * wave + 1, 2 * wave);
     lds_sync();
-    if (wave < 2) tri_offdiag_block(sA, sT, wave + 2, wave);
-    lds_sync();
-    if (wave == 0) tri_offdiag_block(sA, sT, 3, 0);
+    // the 32 x 32 off-diagonal block, one 16 x 16 block (i, j) per wave, i in {2, 3}, j in {0, 1}:
+    // T_ij = -sum_{m=2}^{i} T_im Y_mj with Y_mj = sum_{n=j}^{1} A_mn T_nj (each wave forms the Y
+    // blocks it needs itself, so the level needs no further barrier)
+    if (wave < 4) {
+        const int i = 2 + (wave >> 1), j = wave & 1;
+        f32x4 y[2];
+#pragma unroll
+        for (int m = 2; m < 4; ++m) {
+            f32x4 acc = zero4();
+            if (m <= i) {
+                for (int n = j; n < 2; ++n) {
+                    const f32x4 a = *reinterpret_cast<const f32x4*>(sA + (16 * m + ln) * kLdA + 16 * n + 4 * gq);
+                    f32x4 b;
+                    b.x = sT[(16 * n + 4 * gq + 0) * kLdA + 16 * j + ln];
+                    b.y = sT[(16 * n + 4 * gq + 1) * kLdA + 16 * j + ln];
+                    b.z = sT[(16 * n + 4 * gq + 2) * kLdA + 16 * j + ln];
+                    b.w = sT[(16 * n + 4 * gq + 3) * kLdA + 16 * j + ln];
+                    mma_f32_k16(acc, a, b);
+                }
+            }
+            y[m - 2] = acc;  // y[s] = Y_mj[4 gq + s][ln]: a B operand as is
+        }
+        f32x4 r = zero4();
+#pragma unroll
+        for (int m = 2; m < 4; ++m) {
+            if (m <= i) {
+                const f32x4 a = *reinterpret_cast<const f32x4*>(sT + (16 * i + ln) * kLdA + 16 * m + 4 * gq);
+                mma_f32_k16(r, a, y[m - 2]);
+            }
+        }
+#pragma unroll
+        for (int s = 0; s < 4; ++s) sT[(16 * i + 4 * gq + s) * kLdA + 16 * j + ln] = -r[s];
+    }
     lds_sync();
 }
 

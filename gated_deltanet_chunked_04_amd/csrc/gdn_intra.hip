@@ -17,8 +17,8 @@
 // Persistent workgroups of 4 waves, two per CU, each taking one (chunk, head) at a time.
 // K is staged in LDS with its rows in fragment order (one 16-byte read per row fragment
 // of the Gram tiles), V row-major; T*K and T*V read their columns with LDS transpose loads. The inverse is blocked:
-// 16x16 diagonal blocks by forward substitution, then off-diagonal blocks level by
-// level with fp32 matrix-core products. T stays fp32; the products T*K and T*V run on
+// 16x16 diagonal blocks by forward substitution, then off-diagonal blocks in two levels
+// with fp32 matrix-core products. T stays fp32; the products T*K and T*V run on
 // the matrix cores in the input precision with fp32 accumulation. For the backward the
 // kernel also writes T in the input precision.
 #include "gdn_common.h"
@@ -34,7 +34,9 @@ namespace {
 constexpr int kThreads = 256;
 
 template <typename T> struct IntraPad;
-template <> struct IntraPad<bf16_t> { static constexpr int row = 8; };
+// bf16 rows of K + 16 elements (288 bytes): the 16-byte row-fragment reads of K and the
+// transposed reads of V meet no bank conflicts (at K + 8, two-way)
+template <> struct IntraPad<bf16_t> { static constexpr int row = 16; };
 template <> struct IntraPad<float> { static constexpr int row = 4; };
 
 
