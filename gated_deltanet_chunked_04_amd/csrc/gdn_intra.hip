@@ -160,32 +160,48 @@ __global__ __launch_bounds__(kThreads) void k_intra(IntraArgs args) {
         lds_sync();
 
         // ---- stage 2: A = strict_lower(diag(beta) (D .* K K^T)) -----------------------
-        // this wave's lower tiles (wave, wave + 4, wave + 8), their k32 products side by side
+        // A K fragment serves as either operand (both use the same slot map), so each wave reads
+        // the row blocks it needs once: waves 0 and 1 hold blocks 2w and 2w + 1 and form the three
+        // tiles among them, waves 2 and 3 hold blocks 0, 1 and w and form tiles (w, 0) and (w, 1)
+        // (40 fragment reads per task instead of two per tile product, 96)
         {
             constexpr int NTT = 3;
             f32x4 acc[NTT];
             int ti[NTT], tj[NTT];
             bool on[NTT];
-            // (waves with two tiles recompute the last one instead of branching; only the
-            // stores are skipped, so the products form one straight block)
 #pragma unroll
-            for (int m = 0; m < NTT; ++m) {
-                const int idx = wave + 4 * m;
-                on[m] = idx < 10;
-                ti[m] = tri_row(min(idx, 9));
-                tj[m] = tri_col(min(idx, 9));
-                acc[m] = zero4();
-            }
+            for (int m = 0; m < NTT; ++m) acc[m] = zero4();
+            if (wave < 2) {
+                const int b0 = 2 * wave, b1 = 2 * wave + 1;
+                ti[0] = b0; tj[0] = b0;
+                ti[1] = b1; tj[1] = b0;
+                ti[2] = b1; tj[2] = b1;
+                on[0] = on[1] = on[2] = true;
 #pragma unroll
-            for (int kb = 0; kb < K / 32; ++kb) {
-                Frag<T> fa[NTT], fb[NTT];
-#pragma unroll
-                for (int m = 0; m < NTT; ++m) {
-                    frag_row_fo(fa[m], sK, S::LDK, tj[m] * 16 + ln, kb * 32);
-                    frag_row_fo(fb[m], sK, S::LDK, ti[m] * 16 + ln, kb * 32);
+                for (int kb = 0; kb < K / 32; ++kb) {
+                    Frag<T> f0, f1;
+                    frag_row_fo(f0, sK, S::LDK, b0 * 16 + ln, kb * 32);
+                    frag_row_fo(f1, sK, S::LDK, b1 * 16 + ln, kb * 32);
+                    mma(acc[0], f0, f0);
+                    mma(acc[1], f0, f1);
+                    mma(acc[2], f1, f1);
                 }
+            } else {
+                const int b2 = wave;
+                ti[0] = b2; tj[0] = 0;
+                ti[1] = b2; tj[1] = 1;
+                ti[2] = b2; tj[2] = 1;
+                on[0] = on[1] = true;
+                on[2] = false;
 #pragma unroll
-                for (int m = 0; m < NTT; ++m) mma(acc[m], fa[m], fb[m]);
+                for (int kb = 0; kb < K / 32; ++kb) {
+                    Frag<T> f0, f1, f2;
+                    frag_row_fo(f0, sK, S::LDK, ln, kb * 32);
+                    frag_row_fo(f1, sK, S::LDK, 16 + ln, kb * 32);
+                    frag_row_fo(f2, sK, S::LDK, b2 * 16 + ln, kb * 32);
+                    mma(acc[0], f0, f2);
+                    mma(acc[1], f1, f2);
+                }
             }
             // acc[m][i] = k_j . k_r with j = tj*16 + gq*4 + i, r = ti*16 + ln: four consecutive
             // columns of row r, one vector store
