@@ -696,6 +696,13 @@ __device__ __forceinline__ f32x4 ld4(const bf16_t* p) {
 }
 __device__ __forceinline__ f32x4 ld4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
 
+// x.lo * y.lo + x.hi * y.hi + acc for two packed bf16 pairs (one v_dot2 instruction)
+__device__ __forceinline__ float dot2_bf16(uint32_t x, uint32_t y, float acc) {
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, x), __builtin_bit_cast(bf16x2_t, y), acc,
+                                           false);
+}
+
 __device__ __forceinline__ float dot4(const f32x4& a, const f32x4& b) {
     return a[0] * b[0] + a[1] * b[1] + a[2] * b[2] + a[3] * b[3];
 }
@@ -986,16 +993,24 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(BwdChunkArgs a) {
                 }
             }
         }
-        // e^Gam <G, S> over the whole state (each thread a slice)
+        // e^Gam <G, S> over the whole state (each thread a slice; in bf16 two products per
+        // instruction, exact in fp32, with fp32 accumulation)
         float gs = 0.f;
         {
             constexpr int VEC = Elem<T>::kVec;
 #pragma unroll 4
             for (int e = tid; e < V * K / VEC; e += NT) {
                 const int vv = e / (K / VEC), kk = (e % (K / VEC)) * VEC;
+                if constexpr (sizeof(T) == 2) {
+                    const u32x4 gv = *reinterpret_cast<const u32x4*>(sG + vv * C::LDS + kk);
+                    const u32x4 sv = *reinterpret_cast<const u32x4*>(sS + vv * C::LDS + kk);
 #pragma unroll
-                for (int i = 0; i < VEC; i += 4)
-                    gs += dot4(ld4(sG + vv * C::LDS + kk + i), ld4(sS + vv * C::LDS + kk + i));
+                    for (int i = 0; i < 4; ++i) gs = dot2_bf16(gv[i], sv[i], gs);
+                } else {
+#pragma unroll
+                    for (int i = 0; i < VEC; i += 4)
+                        gs += dot4(ld4(sG + vv * C::LDS + kk + i), ld4(sS + vv * C::LDS + kk + i));
+                }
             }
         }
         // ---- dKt^T[k][r] = sum_v G[v][k] Delta[r][v]  (rows k of this half, cols r) ------------
