@@ -606,7 +606,9 @@ struct BCfg {
     static constexpr int off_dgs = off_qd + 1024;   // [64] state-side d(gam)
     static constexpr int off_sc = off_dgs + 256;    // [16] fp32 scalars (two per wave)
     static constexpr int off_db = off_sc + 64;      // [2][64] fp32 dbeta parts (one per wave half)
-    static constexpr int total = off_db + 512;
+    static constexpr int off_eg = off_db + 512;     // [64] e^{gam_r}
+    static constexpr int off_er = off_eg + 256;     // [64] e^{Gam - gam_r}
+    static constexpr int total = off_er + 256;
     // Where the WY side leaves a hole between its last matrix (dT) and dDelta large enough (bf16 at
     // K = V = 128: the state side's Q, dO and Delta tiles, dead once the state side ends), dq
     // and then dk and dv are staged there ([64][K + 8], row-major) and stored as whole rows.
@@ -723,22 +725,22 @@ __device__ __forceinline__ Frag<float> neg(const Frag<float>& f) {
 // Sum over the four lanes that share ln (lane groups gq = 0..3).
 __device__ __forceinline__ float sum_gq(float x) { return sum_rows(x); }
 
-// Per-slot scaling of a bf16 fragment by e^{gam}: slot e of lane group gq is row
-// k0 + kappa(gq, e) of the contraction, and gets the factor exp(gam[k0 + kappa(gq, e)]) (gam in LDS).
-__device__ __forceinline__ Frag<bf16_t> scale_slots_exp(const Frag<bf16_t>& f, const float* gam, int k0) {
+// Per-slot scaling of a bf16 fragment by a per-row factor f (in LDS): slot e of lane group gq is
+// row k0 + kappa(gq, e) of the contraction and gets f[k0 + kappa(gq, e)].
+__device__ __forceinline__ Frag<bf16_t> scale_slots(const Frag<bf16_t>& x, const float* f, int k0) {
     const int gq = threadIdx.x >> 4 & 3;
-    const f32x4 a = *reinterpret_cast<const f32x4*>(gam + k0 + gq * 4);
-    const f32x4 b = *reinterpret_cast<const f32x4*>(gam + k0 + 16 + gq * 4);
+    const f32x4 a = *reinterpret_cast<const f32x4*>(f + k0 + gq * 4);
+    const f32x4 b = *reinterpret_cast<const f32x4*>(f + k0 + 16 + gq * 4);
     Frag<bf16_t> o;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const f32x4& x = i < 2 ? a : b;  // u32 i holds slots 2i, 2i+1
+        const f32x4& y = i < 2 ? a : b;  // u32 i holds slots 2i, 2i+1
         const int e = (i & 1) * 2;
-        o.v[i] = pack_bf2(__uint_as_float(f.v[i] << 16) * fast_exp(x[e]),
-                          __uint_as_float(f.v[i] & 0xFFFF0000u) * fast_exp(x[e + 1]));
+        o.v[i] = pack_bf2(__uint_as_float(x.v[i] << 16) * y[e], __uint_as_float(x.v[i] & 0xFFFF0000u) * y[e + 1]);
     }
     return o;
 }
+
 
 // kL2: q arrives raw and its rows are L2-normalised in registers before staging (dq is then
 // the gradient with respect to the normalised rows).
@@ -851,6 +853,8 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(BwdChunkArgs a) {
         float* sDgs = reinterpret_cast<float*>(sm + C::off_dgs);
         float* sSc = reinterpret_cast<float*>(sm + C::off_sc);
         float* sDb = reinterpret_cast<float*>(sm + C::off_db);
+        float* sEg = reinterpret_cast<float*>(sm + C::off_eg);
+        float* sEr = reinterpret_cast<float*>(sm + C::off_er);
         // ---- stage this task (the previous task's LDS reads are done) ---------------------
         lds_sync();
         if constexpr (kL2) l2norm_rows<T, K>(R.q);
@@ -862,8 +866,13 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(BwdChunkArgs a) {
         put_tile_fo<T, V, C::NV, NT>(sDl, C::LDV, R.dl);
         if constexpr (!kCarry) put_tile_fo<T, V, C::NV, NT>(sdU, C::LDU, R.dd);
         if (tid < 64) {
+            // the decay factors that depend on one row only, once per chunk (the chunk total
+            // Gam is the last row's cumsum)
+            const float gtot = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(R.gam), 63));
             sGam[tid] = R.gam;
             sBeta[tid] = R.beta;
+            sEg[tid] = fast_exp(R.gam);
+            sEr[tid] = fast_exp(gtot - R.gam);
         }
         lds_sync();
         // The last task fetches itself again: unconditional fetches end the previous
@@ -886,7 +895,7 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(BwdChunkArgs a) {
         const int h = cur.h;
         const float Gm = sGam[63];
         const float gr = sGam[r];
-        const float ekt = fast_exp(Gm - gr);
+        const float ekt = sEr[r];
 
         // ======================= state side, rows r of this wave =======================
         // ---- P (rows j, cols r) and dP^T[j][r] = sum_v Delta[j][v] dO[r][v], this half's j tiles
@@ -924,15 +933,21 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(BwdChunkArgs a) {
         // kCarry: P[r][j] = e^{gam_r - gam_j} (Q K^T)[r][j] (j <= r) for dDelta, staged over the
         // dDelta tile (rows r, fragment order) until dDelta replaces it
         T* sPr = sdU;
+        // the causal decay e^{gam_r - gam_j} (0 for j > r) of this lane's P entries, used here and
+        // for L .* dP below
+        f32x4 dec[2];
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+            const int jt = 2 * hf + m;
+            const f32x4 gj = ld4(sGam + jt * 16 + gq * 4);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) dec[m][i] = (jt * 16 + gq * 4 + i <= r) ? fast_exp(gr - gj[i]) : 0.f;
+        }
         if constexpr (kCarry) {
 #pragma unroll
             for (int m = 0; m < 2; ++m) {
                 const int jt = 2 * hf + m;
-                const f32x4 gj = ld4(sGam + jt * 16 + gq * 4);
-                f32x4 pv;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) pv[i] = (jt * 16 + gq * 4 + i <= r) ? PmQ[m][i] * fast_exp(gr - gj[i]) : 0.f;
-                store4(sPr + r * C::LDX + frag_pos(jt * 16 + gq * 4), pv);
+                store4(sPr + r * C::LDX + frag_pos(jt * 16 + gq * 4), PmQ[m] * dec[m]);
             }
         }
         // S and G are fetched last in the previous task and staged only here, so that their
@@ -962,7 +977,7 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(BwdChunkArgs a) {
                 for (int kb = 0; kb < K / 32; ++kb) frag_row_fo(fk[kb], sK, C::LDK, jt * 16 + ln, kb * 32);  // K row j
 #pragma unroll
                 for (int kb = 0; kb < K / 32; ++kb) mma(ddT[jt], gfr[kb], fk[kb]);
-                ddT[jt] *= fast_exp(Gm - sGam[jt * 16 + ln]);
+                ddT[jt] *= sEr[jt * 16 + ln];
             }
             // + (scale dO)^T P: contraction over the chunk rows r >= j
             Frag<T> dof[2];
@@ -981,7 +996,7 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(BwdChunkArgs a) {
             const float eG = fast_exp(Gm);
             Frag<T> dos[2];
 #pragma unroll
-            for (int rb = 0; rb < 2; ++rb) dos[rb] = scale_slots_exp(dof[rb], sGam, rb * 32);
+            for (int rb = 0; rb < 2; ++rb) dos[rb] = scale_slots(dof[rb], sEg, rb * 32);
 #pragma unroll
             for (int kt = 0; kt < K / 16; ++kt) {
                 accG[kt] *= eG;
@@ -1038,11 +1053,9 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(BwdChunkArgs a) {
         for (int m = 0; m < 2; ++m) {
             const int jt = 2 * hf + m;
             f32x4 colpart;
-            const f32x4 gj = ld4(sGam + jt * 16 + gq * 4);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int j = jt * 16 + gq * 4 + i;
-                const float e = (j <= r) ? fast_exp(gr - gj[i]) : 0.f;
+                const float e = dec[m][i];
                 const float x = dPT[m][i] * PmQ[m][i] * e;  // dP .* P at (query r, key j)
                 drow += x;
                 colpart[i] = x;
@@ -1147,7 +1160,7 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(BwdChunkArgs a) {
 #pragma unroll
             for (int m = 0; m < 2; ++m) {
                 const int row = (2 * hf + m) * 16 + ln;
-                const float eg = fast_exp(sGam[row]);
+                const float eg = sEg[row];
                 Frag<T> xr[2];
                 frag_row_fo(xr[0], sX, C::LDX, row, 0);  // (L .* dP) row r, slots j'
                 frag_row_fo(xr[1], sX, C::LDX, row, 32);
@@ -1254,13 +1267,13 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(BwdChunkArgs a) {
 #pragma unroll
             for (int m = 0; m < 2; ++m) {
                 const int bt = 2 * hf + m;
-                const f32x4 gb = ld4(sGam + bt * 16 + gq * 4);
+                const f32x4 gb = ld4(sEg + bt * 16 + gq * 4);  // e^{gam_b}
                 const f32x4 bb = ld4(sBeta + bt * 16 + gq * 4);
                 f32x4 dT;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int b = bt * 16 + gq * 4 + e;
-                    dT[e] = (b < ra) ? bb[e] * (fast_exp(gb[e]) * x[m][e] + y[m][e]) : 0.f;
+                    dT[e] = (b < ra) ? bb[e] * (gb[e] * x[m][e] + y[m][e]) : 0.f;
                 }
                 store4(sDT + ra * C::LDX + frag_pos(bt * 16 + gq * 4), dT);  // dT[a][b], fragment order
             }
@@ -1357,7 +1370,7 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(BwdChunkArgs a) {
         frag_row_fo(mrow[1], sMx, C::LDX, ra, 32);
         frag_col_fo(mcol[0], sMx, C::LDX, ra, 0);  // Mx column a, slots c
         frag_col_fo(mcol[1], sMx, C::LDX, ra, 32);
-        const float ba = sBeta[ra], ega = fast_exp(sGam[ra]);
+        const float ba = sBeta[ra], ega = sEg[ra];
         {
             T* dkp = reinterpret_cast<T*>(a.dk) + ((t0 + ra) * H + h) * K;
             f32x4 dkv[KH];
