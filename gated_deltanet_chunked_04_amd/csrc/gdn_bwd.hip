@@ -1313,7 +1313,7 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(BwdChunkArgs a) {
             Frag<T> kra[K / 32];
 #pragma unroll
             for (int kb = 0; kb < K / 32; ++kb) frag_row_fo(kra[kb], sK, C::LDK, ra, kb * 32);
-            const float ba = sBeta[ra], ga = sGam[ra];
+            const float ba = sBeta[ra];
             f32x4 dd[2], kkk[2];
 #pragma unroll
             for (int m = 0; m < 2; ++m) {
@@ -1341,19 +1341,18 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(BwdChunkArgs a) {
             for (int m = 0; m < 2; ++m) {
                 const int ct = 2 * hf + m;
                 const f32x4 d = dd[m], kk = kkk[m];
-                const f32x4 gc = ld4(sGam + ct * 16 + gq * 4);
                 f32x4 colpart, mx;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int cc = ct * 16 + gq * 4 + e;
                     const bool lower = cc < ra;
-                    const float dec = lower ? fast_exp(ga - gc[e]) : 0.f;
-                    const float ar = dec * kk[e];  // raw A[a][c]
+                    const float dcy = lower ? dec[m][e] : 0.f;  // the causal decay of P, without its diagonal
+                    const float ar = dcy * kk[e];  // raw A[a][c]
                     const float dA = lower ? -d[e] : 0.f;
                     dbeta_row += dA * ar;
                     dgam_row += dA * ar * ba;
                     colpart[e] = dA * ar * ba;
-                    mx[e] = dA * ba * dec;
+                    mx[e] = dA * ba * dcy;
                 }
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
