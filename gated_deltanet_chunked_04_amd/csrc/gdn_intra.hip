@@ -51,7 +51,8 @@ struct IntraSmem {
     static constexpr int off_gam = off_a + 64 * kLdA * 4;
     static constexpr int off_beta = off_gam + 256;
     static constexpr int off_kk = off_beta + 256;
-    static constexpr int total = off_kk + 256;
+    static constexpr int off_eg = off_kk + 256;  // e^{gam_j}
+    static constexpr int total = off_eg + 256;
 };
 
 
@@ -114,6 +115,7 @@ __global__ __launch_bounds__(kThreads) void k_intra(IntraArgs args) {
     float* sGam = reinterpret_cast<float*>(smem + S::off_gam);
     float* sBeta = reinterpret_cast<float*>(smem + S::off_beta);
     float* sKK = reinterpret_cast<float*>(smem + S::off_kk);
+    float* sEg = reinterpret_cast<float*>(smem + S::off_eg);
 
     const Geo& geo = args.geo;
     const int64_t H = geo.H;
@@ -155,6 +157,7 @@ __global__ __launch_bounds__(kThreads) void k_intra(IntraArgs args) {
             const float x = wave_prefix_sum(g_in);
             sGam[lane] = x;   // rows past the chunk end carry the chunk total
             sBeta[lane] = b_in;
+            sEg[lane] = fast_exp(x);
             if (in) args.gam[(t0 + lane) * H + h] = x;
         }
         lds_sync();
@@ -263,15 +266,15 @@ __global__ __launch_bounds__(kThreads) void k_intra(IntraArgs args) {
             // slots 0..3: columns kb*32 + gq*4 + e; slots 4..7: 16 further
             const f32x4 b0 = *reinterpret_cast<const f32x4*>(sBeta + kb * 32 + gq * 4);
             const f32x4 b1 = *reinterpret_cast<const f32x4*>(sBeta + kb * 32 + 16 + gq * 4);
-            const f32x4 g0 = *reinterpret_cast<const f32x4*>(sGam + kb * 32 + gq * 4);
-            const f32x4 g1 = *reinterpret_cast<const f32x4*>(sGam + kb * 32 + 16 + gq * 4);
+            const f32x4 g0 = *reinterpret_cast<const f32x4*>(sEg + kb * 32 + gq * 4);  // e^{gam_j}
+            const f32x4 g1 = *reinterpret_cast<const f32x4*>(sEg + kb * 32 + 16 + gq * 4);
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const float tv = e < 4 ? tf.lo[e] : tf.hi[e - 4];
                 const float bj = e < 4 ? b0[e] : b1[e - 4];
                 const float gjv = e < 4 ? g0[e] : g1[e - 4];
                 fu[e] = tv * bj;
-                fw[e] = fu[e] * fast_exp(gjv);
+                fw[e] = fu[e] * gjv;
             }
             if constexpr (sizeof(T) == 2) {
                 aw[kb].v = u32x4{pack_bf2(fw[0], fw[1]), pack_bf2(fw[2], fw[3]), pack_bf2(fw[4], fw[5]),
