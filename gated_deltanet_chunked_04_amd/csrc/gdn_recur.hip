@@ -57,7 +57,9 @@ struct RCfg {
     static constexpr int off_w = off_k + kMat;
     static constexpr int off_u = off_w + kMat;
     static constexpr int off_gam = off_u + 64 * LDU * (int)sizeof(T);
-    static constexpr int end_prep = off_gam + 256;
+    static constexpr int off_eg = off_gam + 256;  // e^{gam_r}, once per chunk
+    static constexpr int off_er = off_eg + 256;   // e^{Gam - gam_r}
+    static constexpr int end_prep = off_er + 256;
     static constexpr int off_q = end_prep;
     static constexpr int end_states = off_q + kMat;
     static constexpr int off_pm = end_states;
@@ -130,6 +132,8 @@ struct ChunkLds {
     T* sU;
     T* sPm;
     float* sGam;
+    float* sEg = nullptr;  // e^{gam_r} and e^{Gam - gam_r} per chunk row, or null: computed where used
+    float* sEr = nullptr;
     T* sO = nullptr;  // output staging [64][RT] (row-major), or null: O goes straight to memory
     T* sH = nullptr;  // chunk-entry state staging [RT][K] (row-major), or null
 };
@@ -144,7 +148,15 @@ __device__ __forceinline__ void chunk_stage(const ChunkRegs<T, K, RT, kQ>& R, co
     put_tile_fo<T, K, C::IQ, C::NT>(L.sW, C::LD, R.w);
     put_tile<T, K, C::IQ, C::NT>(L.sK, C::LD, R.k);
     put_tile<T, RT, C::IU, C::NT>(L.sU, C::LDU, R.u);
-    if (threadIdx.x < 64) L.sGam[threadIdx.x] = R.gam;
+    if (threadIdx.x < 64) {
+        L.sGam[threadIdx.x] = R.gam;
+        if (L.sEg) {
+            // the chunk total is the last row's cumsum (rows past the chunk end repeat it)
+            const float gtot = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(R.gam), 63));
+            L.sEg[threadIdx.x] = fast_exp(R.gam);
+            L.sEr[threadIdx.x] = fast_exp(gtot - R.gam);
+        }
+    }
 }
 
 // One chunk of the recurrence for this wave's 16 state rows (columns of S^T).
@@ -319,7 +331,7 @@ __device__ __forceinline__ void chunk_part1(const ChunkLds<T, K, RT>& L, const f
     }
     if (kOut) {
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt) accO[rt] *= fast_exp(L.sGam[rt * 16 + ln]);
+        for (int rt = 0; rt < 4; ++rt) accO[rt] *= L.sEg ? L.sEg[rt * 16 + ln] : fast_exp(L.sGam[rt * 16 + ln]);
     }
 }
 
@@ -370,13 +382,18 @@ __device__ __forceinline__ void chunk_part2(const RecurArgs& a, const ChunkLds<T
     Frag<T> dtf[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-        const f32x4 g0 = *reinterpret_cast<const f32x4*>(L.sGam + kb * 32 + gq * 4);
-        const f32x4 g1 = *reinterpret_cast<const f32x4*>(L.sGam + kb * 32 + 16 + gq * 4);
         f32x4 r0, r1;
+        if (L.sEr) {
+            r0 = *reinterpret_cast<const f32x4*>(L.sEr + kb * 32 + gq * 4);
+            r1 = *reinterpret_cast<const f32x4*>(L.sEr + kb * 32 + 16 + gq * 4);
+        } else {
+            const f32x4 g0 = *reinterpret_cast<const f32x4*>(L.sGam + kb * 32 + gq * 4);
+            const f32x4 g1 = *reinterpret_cast<const f32x4*>(L.sGam + kb * 32 + 16 + gq * 4);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            r0[i] = fast_exp(G - g0[i]);
-            r1[i] = fast_exp(G - g1[i]);
+            for (int i = 0; i < 4; ++i) {
+                r0[i] = fast_exp(G - g0[i]);
+                r1[i] = fast_exp(G - g1[i]);
+            }
         }
         frag_acc_rows(dtf[kb], accD[2 * kb], accD[2 * kb + 1], r0, r1);
     }
@@ -410,6 +427,12 @@ __global__ __launch_bounds__(RT * 4) void k_recur(RecurArgs a) {
     L.sU = reinterpret_cast<T*>(smem + C::off_u);
     L.sPm = reinterpret_cast<T*>(smem + C::off_pm);
     L.sGam = reinterpret_cast<float*>(smem + C::off_gam);
+    if constexpr (MODE == kRecurPrepass) {
+        // the prepass, with the least work per chunk step, takes the per-row exponentials from
+        // tables made once per chunk (measured: the output pass does better computing its own)
+        L.sEg = reinterpret_cast<float*>(smem + C::off_eg);
+        L.sEr = reinterpret_cast<float*>(smem + C::off_er);
+    }
     constexpr bool kStageO = kOut && C::stage_o;
     if constexpr (kStageO) L.sO = reinterpret_cast<T*>(smem + C::off_o);
     constexpr int kOffH = C::base_of(kOut, kRec);
