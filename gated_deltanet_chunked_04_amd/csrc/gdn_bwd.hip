@@ -55,7 +55,8 @@ struct VCfg {
     static constexpr int off_pm = off_do + 64 * LDD * (int)sizeof(T);
     static constexpr int off_dd = off_pm + 64 * LDP * (int)sizeof(T);   // dDelta tile [64][RT]
     static constexpr int off_gam = off_dd + 64 * LDD * (int)sizeof(T);
-    static constexpr int total = off_gam + 256;
+    static constexpr int off_er = off_gam + 256;  // e^{Gam - gam_j}, once per chunk
+    static constexpr int total = off_er + 256;
     static constexpr int NVK = K / VEC;
     static constexpr int NVD = RT / VEC;
     static constexpr int IK = 64 * NVK / NT;   // q, k, w rows
@@ -114,6 +115,7 @@ struct RevLds {
     T* sD;   // dO
     T* sPm;  // P^T [j][r]
     float* sGam;
+    float* sEr;  // e^{Gam - gam_j}
 };
 
 template <typename T, int K, int RT>
@@ -130,7 +132,12 @@ __device__ __forceinline__ void rev_stage(const RevRegs<T, K, RT>& R, const RevL
         *reinterpret_cast<u32x4*>(L.sQs + r * C::LD + cv * C::VEC) = scale_vec<T>(R.q[it], scale * fast_exp(R.gq[it]));
     }
     put_tile<T, RT, C::ID, C::NT>(L.sD, C::LDD, R.d);
-    if (threadIdx.x < 64) L.sGam[threadIdx.x] = R.gam;
+    if (threadIdx.x < 64) {
+        // the chunk total is the last row's cumsum (rows past the chunk end repeat it)
+        const float gtot = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(R.gam), 63));
+        L.sGam[threadIdx.x] = R.gam;
+        L.sEr[threadIdx.x] = fast_exp(gtot - R.gam);
+    }
 }
 
 // kL2: q arrives raw and its rows are L2-normalised in registers before staging.
@@ -146,6 +153,7 @@ __global__ __launch_bounds__(RT * 4) void k_reverse(RevArgs a) {
     L.sD = reinterpret_cast<T*>(smem + C::off_do);
     L.sPm = reinterpret_cast<T*>(smem + C::off_pm);
     L.sGam = reinterpret_cast<float*>(smem + C::off_gam);
+    L.sEr = reinterpret_cast<float*>(smem + C::off_er);
     T* sDd = reinterpret_cast<T*>(smem + C::off_dd);
 
     const Geo& geo = a.geo;
@@ -399,11 +407,7 @@ __global__ __launch_bounds__(RT * 4) void k_reverse(RevArgs a) {
             }
         }
 #pragma unroll
-        for (int jt = 0; jt < 4; ++jt) {
-            const f32x4 gj = *reinterpret_cast<const f32x4*>(L.sGam + jt * 16 + gq * 4);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) accD[jt][i] *= fast_exp(Gm - gj[i]);
-        }
+        for (int jt = 0; jt < 4; ++jt) accD[jt] *= *reinterpret_cast<const f32x4*>(L.sEr + jt * 16 + gq * 4);
         rev_fetch<1>(R, a, tn, cnn, h, dcol0);
         // bf16: dO and the gate cumsum too (every chunk's loads land together in one burst
         // across the chip, so the last piece needs most of a step to arrive); fp32, whose
