@@ -1237,12 +1237,15 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(BwdChunkArgs a) {
         // registers are live, so that nothing spills or waits on them) and in groups.
         bwd_fetch<0>(R, a, nxt);
         const int ra = r;
+        f32x4 kkk[2];  // K K^T, rows c of this half's tiles, cols a = ra (from the dT step)
         // ---- dT[a][b] = beta_b e^{gam_b} (dW K^T)[a][b] + beta_b (dU V^T)[a][b], b < a, this
         // half's b tiles (rows b, cols a), exchanged through LDS as dT[a][b]
         {
-            Frag<T> wf[K / 32], uf[V / 32];
+            Frag<T> wf[K / 32], uf[V / 32], kra[K / 32];
 #pragma unroll
             for (int kb = 0; kb < K / 32; ++kb) frag_row_fo(wf[kb], sdW, C::LDK, ra, kb * 32);
+#pragma unroll
+            for (int kb = 0; kb < K / 32; ++kb) frag_row_fo(kra[kb], sK, C::LDK, ra, kb * 32);
 #pragma unroll
             for (int vb = 0; vb < V / 32; ++vb) frag_row_fo(uf[vb], sdU, C::LDU, ra, vb * 32);
             // both b tiles (the mask below zeroes b >= a)
@@ -1251,14 +1254,19 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(BwdChunkArgs a) {
             for (int m = 0; m < 2; ++m) {
                 x[m] = zero4();
                 y[m] = zero4();
+                kkk[m] = zero4();
             }
+            // the same K row fragments give K K^T (rows c = b, cols a) for the dA step below
 #pragma unroll
             for (int kb = 0; kb < K / 32; ++kb) {
                 Frag<T> fk[2];
 #pragma unroll
                 for (int m = 0; m < 2; ++m) frag_row_fo(fk[m], sK, C::LDK, (2 * hf + m) * 16 + ln, kb * 32);
 #pragma unroll
-                for (int m = 0; m < 2; ++m) mma(x[m], fk[m], wf[kb]);  // rows b, cols a: (K dW^T)[b][a]
+                for (int m = 0; m < 2; ++m) {
+                    mma(x[m], fk[m], wf[kb]);      // rows b, cols a: (K dW^T)[b][a]
+                    mma(kkk[m], fk[m], kra[kb]);   // rows c, cols a: k_c . k_a
+                }
             }
 #pragma unroll
             for (int vb = 0; vb < V / 32; ++vb) {
@@ -1314,16 +1322,10 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(BwdChunkArgs a) {
         frag_col_fo(ta[0], sTm, C::LDX, ra, 0);  // T column a, slots x
         frag_col_fo(ta[1], sTm, C::LDX, ra, 32);
         {
-            Frag<T> kra[K / 32];
-#pragma unroll
-            for (int kb = 0; kb < K / 32; ++kb) frag_row_fo(kra[kb], sK, C::LDK, ra, kb * 32);
             const float ba = sBeta[ra];
-            f32x4 dd[2], kkk[2];
+            f32x4 dd[2];
 #pragma unroll
-            for (int m = 0; m < 2; ++m) {
-                dd[m] = zero4();
-                kkk[m] = zero4();
-            }
+            for (int m = 0; m < 2; ++m) dd[m] = zero4();
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
                 Frag<T> fy[2];
@@ -1332,14 +1334,6 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(BwdChunkArgs a) {
                     frag_col(fy[m], sY, C::LDX, (2 * hf + m) * 16 + ln, kb * 32);  // Y^T row c, slots x
 #pragma unroll
                 for (int m = 0; m < 2; ++m) mma(dd[m], fy[m], ta[kb]);  // rows c, cols a: (T^T Y)^T
-            }
-#pragma unroll
-            for (int kb = 0; kb < K / 32; ++kb) {
-                Frag<T> fk[2];
-#pragma unroll
-                for (int m = 0; m < 2; ++m) frag_row_fo(fk[m], sK, C::LDK, (2 * hf + m) * 16 + ln, kb * 32);
-#pragma unroll
-                for (int m = 0; m < 2; ++m) mma(kkk[m], fk[m], kra[kb]);  // rows c, cols a: k_c . k_a
             }
 #pragma unroll
             for (int m = 0; m < 2; ++m) {
