@@ -1117,7 +1117,8 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(BwdChunkArgs a) {
             }
         }
         // ======= state side, k slice w (KW tiles), row tiles 2hf, 2hf+1 of the chunk =======
-        // dQt^T[k][r] = sum_v S[v][k] dO[r][v],  dW^T[k][r] = -sum_v S[v][k] dDelta[r][v]
+        // dQt^T[k][r] = sum_v S[v][k] dO[r][v],  dW^T[k][r] = -sum_v S[v][k] dDelta[r][v] (the
+        // products accumulate the sum; its sign is applied where dW is staged)
         {
             const int k0 = w * (K / 4);
             f32x4 dQT[KW][2], dWT[KW][2];
@@ -1134,9 +1135,7 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(BwdChunkArgs a) {
 #pragma unroll
                 for (int vb = 0; vb < V / 32; ++vb) {
                     frag_row_fo(fdo[vb], sD, C::LDV, rr * 16 + ln, vb * 32);
-                    Frag<T> f;
-                    frag_row_fo(f, sdU, C::LDU, rr * 16 + ln, vb * 32);
-                    fdd[vb] = neg(f);
+                    frag_row_fo(fdd[vb], sdU, C::LDU, rr * 16 + ln, vb * 32);
                 }
 #pragma unroll
                 for (int j = 0; j < KW; ++j) {
@@ -1206,7 +1205,7 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(BwdChunkArgs a) {
 #pragma unroll
                 for (int m = 0; m < 2; ++m) {
                     const int row = (2 * hf + m) * 16 + ln;
-                    store4(sdW + row * C::LDK + frag_pos(k0 + j * 16 + gq * 4), row < c ? dWT[j][m] : zero4());
+                    store4(sdW + row * C::LDK + frag_pos(k0 + j * 16 + gq * 4), row < c ? -dWT[j][m] : zero4());
                 }
         }
 
@@ -1466,17 +1465,13 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(BwdChunkArgs a) {
             // the state's space (every read of dW, V and the rest of the WY side is done), then
             // every wave its value columns
             T* sXb = reinterpret_cast<T*>(sm + C::off_s);
-            const float bea = ba * ega;
+            const float bea = -ba * ega;  // negated: G^T -= K^T X
 #pragma unroll
             for (int i = 0; i < VH; ++i) store4(sXb + ra * C::LDV + frag_pos((hf * VH + i) * 16 + gq * 4), bvk[i] * bea);
             lds_sync();
-            Frag<T> nx[2];
+            Frag<T> nx[2];  // -X
 #pragma unroll
-            for (int ab = 0; ab < 2; ++ab) {
-                Frag<T> f;
-                frag_col_fo(f, sXb, C::LDV, vrow, ab * 32);  // X column v, slots a
-                nx[ab] = neg(f);
-            }
+            for (int ab = 0; ab < 2; ++ab) frag_col_fo(nx[ab], sXb, C::LDV, vrow, ab * 32);  // -X column v, slots a
 #pragma unroll
             for (int kt = 0; kt < K / 16; ++kt) {
 #pragma unroll
