@@ -713,19 +713,6 @@ __device__ __forceinline__ float dot4(const f32x4& a, const f32x4& b) {
     return a[0] * b[0] + a[1] * b[1] + a[2] * b[2] + a[3] * b[3];
 }
 
-// Negated copy of a fragment.
-__device__ __forceinline__ Frag<bf16_t> neg(const Frag<bf16_t>& f) {
-    Frag<bf16_t> n;
-    n.v = f.v ^ u32x4{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
-    return n;
-}
-__device__ __forceinline__ Frag<float> neg(const Frag<float>& f) {
-    Frag<float> n;
-    n.lo = -f.lo;
-    n.hi = -f.hi;
-    return n;
-}
-
 // Sum over the four lanes that share ln (lane groups gq = 0..3).
 __device__ __forceinline__ float sum_gq(float x) { return sum_rows(x); }
 
