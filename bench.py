@@ -234,7 +234,6 @@ def l2norm_leg(gdn, dev, cu, cu_host, cp, timed, steps):
     q, k, v, g, beta, s0 = (dev[x] for x in ("q", "k", "v", "g", "beta", "initial_state"))
     kw = dict(cu_seqlens=cu, cu_seqlens_host=cu_host, cp_mode=cp, qk_l2norm=True)
     ws = gdn.gdn_workspace(q, v, **kw)
-    cps = gdn.gdn_cp_states(q, v, **kw)
     o = torch.empty_like(v)
     B, T, H, K = q.shape
     N = B if cu is None else int(cu.numel()) - 1
@@ -244,9 +243,8 @@ def l2norm_leg(gdn, dev, cu, cu_host, cp, timed, steps):
                  d_initial_state=torch.empty_like(sT))
 
     def step():
-        gdn.gdn_chunk_fwd(q, k, v, g, beta, s0, workspace=ws, o=o, final_state=sT, cp_states=cps, **kw)
-        gdn.gdn_chunk_bwd(q, k, v, g, beta, dev["d_o"], s0, dev["d_final_state"], workspace=ws,
-                          out=grads, cp_states=cps, **kw)
+        gdn.gdn_chunk_fwd(q, k, v, g, beta, s0, workspace=ws, o=o, final_state=sT, **kw)
+        gdn.gdn_chunk_bwd(q, k, v, g, beta, dev["d_o"], s0, dev["d_final_state"], workspace=ws, out=grads, **kw)
 
     step()
     ms = timed(step, steps)
