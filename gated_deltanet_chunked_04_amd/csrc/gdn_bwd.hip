@@ -534,7 +534,7 @@ hipError_t launch_reverse_t(const RevArgs& a, int64_t nsegs_grid, int vtiles, hi
 // the value dimension:
 //   dQt = dO S, dW = -dDelta S     (S read as column slices: waves w, w+4 own k in
 //                                   [K/4 w, K/4 (w+1)) and split the chunk-row tiles)
-//   dKt = Delta G, dP = dO Delta^T (waves w, w+4 own chunk rows r = 16w .. 16w+15 and split
+//   dKt = Delta G, dP = dO Delta^T (waves w, w+4 own chunk rows of one 16-row tile each and split
 //                                   the tiles along the other dimension)
 // so no partial sums over k cross waves. Most tiles are
 // held transposed (rows over k or chunk rows, columns over r), which makes them A
@@ -758,12 +758,18 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(BwdChunkArgs a) {
     const int64_t ntasks = geo.total_chunks * H;
     const int tid = threadIdx.x;
     const int wave = wave_id(), lane = tid & 63, ln = lane & 15, gq = lane >> 4;
-    // Waves w and w + 4 share the chunk rows 16w .. 16w+15 in the row-split products and
-    // split the tiles along the other dimension: half hf takes the j, c, b tiles 2hf, 2hf+1,
-    // the k tiles hf*K/32 .., the v tiles hf*V/32 .. and, in the column-split products,
-    // the row tiles 2hf, 2hf+1 of its k slice.
+    // Wave w + 4 hf (half hf) takes, in the row-split products, the chunk rows of row tile rt
+    // (w for the first half, 3 - w for the second) and splits the tiles along the other
+    // dimension with the other half: half hf takes the j, c, b tiles 2hf, 2hf+1, the k tiles
+    // hf*K/32 .., the v tiles hf*V/32 .. and, in the column-split products, the row tiles 2hf,
+    // 2hf+1 of its k slice. The mirrored row tiles of the second half make the two waves on one
+    // SIMD share the causal triangle's tiles evenly: nlive of a wave's two j (b) tiles lie on
+    // or below the diagonal, and the P / dP and dT products compute only those (a branch on the
+    // count, wave-uniform).
     const int w = wave & 3, hf = wave >> 2;
-    const int r = w * 16 + ln;     // this lane's chunk row in "column" roles
+    const int rt = hf ? 3 - w : w;
+    const int nlive = (2 * hf <= rt) + (2 * hf + 1 <= rt);
+    const int r = rt * 16 + ln;    // this lane's chunk row in "column" roles
     constexpr int KW = K / 64;     // k tiles (of 16) per k slice in the column-split products
     constexpr int KH = K / 32;     // k tiles per half
     constexpr int VH = V / 32;     // v tiles per half
@@ -897,29 +903,36 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(BwdChunkArgs a) {
             for (int kb = 0; kb < K / 32; ++kb) frag_row_fo(qr[kb], sQ, C::LDK, r, kb * 32);
 #pragma unroll
             for (int vb = 0; vb < V / 32; ++vb) frag_row_fo(dor[vb], sD, C::LDV, r, vb * 32);
-            // both j tiles (the mask below zeroes j > r): one straight block of independent
-            // products instead of a branch per tile
+            // the live j tiles (the mask below zeroes j > r within them): one straight block of
+            // independent products per tile count
 #pragma unroll
             for (int m = 0; m < 2; ++m) {
                 dPT[m] = zero4();
                 PmQ[m] = zero4();
             }
+            auto products = [&](auto nm_) {
+                constexpr int NM = decltype(nm_)::value;
 #pragma unroll
-            for (int vb = 0; vb < V / 32; ++vb) {
-                Frag<T> fd[2];
+                for (int vb = 0; vb < V / 32; ++vb) {
+                    Frag<T> fd[NM];
 #pragma unroll
-                for (int m = 0; m < 2; ++m) frag_row_fo(fd[m], sDl, C::LDV, (2 * hf + m) * 16 + ln, vb * 32);
+                    for (int m = 0; m < NM; ++m) frag_row_fo(fd[m], sDl, C::LDV, (2 * hf + m) * 16 + ln, vb * 32);
 #pragma unroll
-                for (int m = 0; m < 2; ++m) mma(dPT[m], fd[m], dor[vb]);
-            }
+                    for (int m = 0; m < NM; ++m) mma(dPT[m], fd[m], dor[vb]);
+                }
 #pragma unroll
-            for (int kb = 0; kb < K / 32; ++kb) {
-                Frag<T> fk[2];
+                for (int kb = 0; kb < K / 32; ++kb) {
+                    Frag<T> fk[NM];
 #pragma unroll
-                for (int m = 0; m < 2; ++m) frag_row_fo(fk[m], sK, C::LDK, (2 * hf + m) * 16 + ln, kb * 32);
+                    for (int m = 0; m < NM; ++m) frag_row_fo(fk[m], sK, C::LDK, (2 * hf + m) * 16 + ln, kb * 32);
 #pragma unroll
-                for (int m = 0; m < 2; ++m) mma(PmQ[m], fk[m], qr[kb]);
-            }
+                    for (int m = 0; m < NM; ++m) mma(PmQ[m], fk[m], qr[kb]);
+                }
+            };
+            if (nlive == 2)
+                products(std::integral_constant<int, 2>{});
+            else if (nlive == 1)
+                products(std::integral_constant<int, 1>{});
         }
         // kCarry: P[r][j] = e^{gam_r - gam_j} (Q K^T)[r][j] (j <= r) for dDelta, staged over the
         // dDelta tile (rows r, fragment order) until dDelta replaces it
@@ -932,7 +945,7 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(BwdChunkArgs a) {
             const int jt = 2 * hf + m;
             const f32x4 gj = ld4(sGam + jt * 16 + gq * 4);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) dec[m][i] = (jt * 16 + gq * 4 + i <= r) ? fast_exp(gr - gj[i]) : 0.f;
+            for (int i = 0; i < 4; ++i) dec[m][i] = (jt <= rt && jt * 16 + gq * 4 + i <= r) ? fast_exp(gr - gj[i]) : 0.f;
         }
         if constexpr (kCarry) {
 #pragma unroll
@@ -1227,40 +1240,86 @@ __global__ __launch_bounds__(512) void k_bwd_chunk(BwdChunkArgs a) {
         // ---- dT[a][b] = beta_b e^{gam_b} (dW K^T)[a][b] + beta_b (dU V^T)[a][b], b < a, this
         // half's b tiles (rows b, cols a), exchanged through LDS as dT[a][b]
         {
-            Frag<T> wf[K / 32], uf[V / 32], kra[K / 32];
-#pragma unroll
-            for (int kb = 0; kb < K / 32; ++kb) frag_row_fo(wf[kb], sdW, C::LDK, ra, kb * 32);
-#pragma unroll
-            for (int kb = 0; kb < K / 32; ++kb) frag_row_fo(kra[kb], sK, C::LDK, ra, kb * 32);
-#pragma unroll
-            for (int vb = 0; vb < V / 32; ++vb) frag_row_fo(uf[vb], sdU, C::LDU, ra, vb * 32);
-            // both b tiles (the mask below zeroes b >= a)
             f32x4 x[2], y[2];
+            if constexpr (kL2) {
+                // both b tiles, masked: with the raw-q normalisation the count branch below
+                // needs one register more than the kernel has
+                Frag<T> wf[K / 32], uf[V / 32], kra[K / 32];
 #pragma unroll
-            for (int m = 0; m < 2; ++m) {
-                x[m] = zero4();
-                y[m] = zero4();
-                kkk[m] = zero4();
-            }
-            // the same K row fragments give K K^T (rows c = b, cols a) for the dA step below
+                for (int kb = 0; kb < K / 32; ++kb) frag_row_fo(wf[kb], sdW, C::LDK, ra, kb * 32);
 #pragma unroll
-            for (int kb = 0; kb < K / 32; ++kb) {
-                Frag<T> fk[2];
+                for (int kb = 0; kb < K / 32; ++kb) frag_row_fo(kra[kb], sK, C::LDK, ra, kb * 32);
 #pragma unroll
-                for (int m = 0; m < 2; ++m) frag_row_fo(fk[m], sK, C::LDK, (2 * hf + m) * 16 + ln, kb * 32);
+                for (int vb = 0; vb < V / 32; ++vb) frag_row_fo(uf[vb], sdU, C::LDU, ra, vb * 32);
+                // both b tiles (the mask below zeroes b >= a)
 #pragma unroll
                 for (int m = 0; m < 2; ++m) {
-                    mma(x[m], fk[m], wf[kb]);      // rows b, cols a: (K dW^T)[b][a]
-                    mma(kkk[m], fk[m], kra[kb]);   // rows c, cols a: k_c . k_a
+                    x[m] = zero4();
+                    y[m] = zero4();
+                    kkk[m] = zero4();
                 }
-            }
+                // the same K row fragments give K K^T (rows c = b, cols a) for the dA step below
 #pragma unroll
-            for (int vb = 0; vb < V / 32; ++vb) {
-                Frag<T> fv[2];
+                for (int kb = 0; kb < K / 32; ++kb) {
+                    Frag<T> fk[2];
 #pragma unroll
-                for (int m = 0; m < 2; ++m) frag_row_fo(fv[m], sV, C::LDV, (2 * hf + m) * 16 + ln, vb * 32);
+                    for (int m = 0; m < 2; ++m) frag_row_fo(fk[m], sK, C::LDK, (2 * hf + m) * 16 + ln, kb * 32);
 #pragma unroll
-                for (int m = 0; m < 2; ++m) mma(y[m], fv[m], uf[vb]);
+                    for (int m = 0; m < 2; ++m) {
+                        mma(x[m], fk[m], wf[kb]);      // rows b, cols a: (K dW^T)[b][a]
+                        mma(kkk[m], fk[m], kra[kb]);   // rows c, cols a: k_c . k_a
+                    }
+                }
+#pragma unroll
+                for (int vb = 0; vb < V / 32; ++vb) {
+                    Frag<T> fv[2];
+#pragma unroll
+                    for (int m = 0; m < 2; ++m) frag_row_fo(fv[m], sV, C::LDV, (2 * hf + m) * 16 + ln, vb * 32);
+#pragma unroll
+                    for (int m = 0; m < 2; ++m) mma(y[m], fv[m], uf[vb]);
+                }
+            } else {
+                // the live b tiles (the mask below zeroes b >= a within them)
+#pragma unroll
+                for (int m = 0; m < 2; ++m) {
+                    x[m] = zero4();
+                    y[m] = zero4();
+                    kkk[m] = zero4();
+                }
+                auto products = [&](auto nm_) {
+                    constexpr int NM = decltype(nm_)::value;
+                    Frag<T> wf[K / 32], uf[V / 32], kra[K / 32];
+#pragma unroll
+                    for (int kb = 0; kb < K / 32; ++kb) frag_row_fo(wf[kb], sdW, C::LDK, ra, kb * 32);
+#pragma unroll
+                    for (int kb = 0; kb < K / 32; ++kb) frag_row_fo(kra[kb], sK, C::LDK, ra, kb * 32);
+#pragma unroll
+                    for (int vb = 0; vb < V / 32; ++vb) frag_row_fo(uf[vb], sdU, C::LDU, ra, vb * 32);
+                    // the same K row fragments give K K^T (rows c = b, cols a) for the dA step below
+#pragma unroll
+                    for (int kb = 0; kb < K / 32; ++kb) {
+                        Frag<T> fk[NM];
+#pragma unroll
+                        for (int m = 0; m < NM; ++m) frag_row_fo(fk[m], sK, C::LDK, (2 * hf + m) * 16 + ln, kb * 32);
+#pragma unroll
+                        for (int m = 0; m < NM; ++m) {
+                            mma(x[m], fk[m], wf[kb]);      // rows b, cols a: (K dW^T)[b][a]
+                            mma(kkk[m], fk[m], kra[kb]);   // rows c, cols a: k_c . k_a
+                        }
+                    }
+#pragma unroll
+                    for (int vb = 0; vb < V / 32; ++vb) {
+                        Frag<T> fv[NM];
+#pragma unroll
+                        for (int m = 0; m < NM; ++m) frag_row_fo(fv[m], sV, C::LDV, (2 * hf + m) * 16 + ln, vb * 32);
+#pragma unroll
+                        for (int m = 0; m < NM; ++m) mma(y[m], fv[m], uf[vb]);
+                    }
+                };
+                if (nlive == 2)
+                    products(std::integral_constant<int, 2>{});
+                else if (nlive == 1)
+                    products(std::integral_constant<int, 1>{});
             }
 #pragma unroll
             for (int m = 0; m < 2; ++m) {
