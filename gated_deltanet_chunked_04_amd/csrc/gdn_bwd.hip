@@ -14,6 +14,8 @@
 //   WY side: with T = (I + A)^{-1} (written by the intra-chunk kernel); dT = dW Bk^T + dU Bv^T,
 //     dA = strict_lower(-T^T dT T^T), dBk = T^T dW, dBv = T^T dU  ->  dk, dv, dbeta, and
 //     dg as the in-chunk reverse cumulative sum of d(gam).
+#include <type_traits>
+
 #include "gdn_common.h"
 #include "gdn_kernels.h"
 #include "gdn_norm.h"
