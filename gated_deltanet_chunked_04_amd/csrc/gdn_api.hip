@@ -446,6 +446,10 @@ gdn_status run_intra(const gdn_desc* d, const Plan& p, unsigned char* ws, const 
 
 // The CP decision: per sequence-head modes [N,H] and per boundary windows [total_segs,H] in one
 // direction, and optionally the other direction's (the backward's adjoint pass) in the same launch.
+// The CP prepasses run on the ranked grid (sequence-heads with exact maps dispatched first)
+// for uniform-length batches whose sequence-head count fits one grid dimension.
+int32_t prepass_ranked(const Plan& p) { return !p.varlen && (int64_t)p.N * p.H <= 65535 ? 1 : 0; }
+
 gdn_status run_decide(const gdn_desc* d, const Plan& p, unsigned char* ws, int32_t* modes, int32_t* bwin,
                       hipStream_t st, int reverse = 0, int32_t* modes_r = nullptr, int32_t* bwin_r = nullptr) {
     DecideArgs da{};
@@ -646,6 +650,7 @@ gdn_status run_fwd(const gdn_desc* desc, const Plan& p, const void* q, const voi
         if ((s = run_decide(desc, p, ws, modes, bwin, st)) != GDN_OK) return s;
         ra.seginit_out = seginit;
         ra.prep = prep;
+        ra.ranked = prepass_ranked(p);
         const int rt = recur_rows((int)desc->V, (int)desc->K);
         GDN_LAUNCH(kKPrepass, st, launch_recur(ra, desc->dtype, kRecurPrepass, p.total_segs,
                                                (int)((desc->V + desc->K + rt - 1) / rt), st));
@@ -761,6 +766,7 @@ gdn_status gdn_chunk_bwd(const gdn_desc* desc, const void* q, const void* k, con
         float* prep = reinterpret_cast<float*>(ws + p.o_prep);
         ra.seginit_out = seginit;
         ra.prep = prep;
+        ra.ranked = prepass_ranked(p);
         GDN_LAUNCH(kKPrepass, st, launch_recur(ra, desc->dtype, kRecurPrepass, p.total_segs, vktiles, st));
         ScanArgs sa{};
         memset(&sa, 0, sizeof(sa));
@@ -800,6 +806,7 @@ gdn_status gdn_chunk_bwd(const gdn_desc* desc, const void* q, const void* k, con
         va.bwin = bwin_r;
         va.seginit_out = seginit_r;
         va.prep = prep_r;
+        va.ranked = prepass_ranked(p);
         GDN_LAUNCH(kKBwdPrepass, st, launch_reverse(va, desc->dtype, kRecurPrepass, p.total_segs, vktiles, st));
         ScanArgs sa{};
         memset(&sa, 0, sizeof(sa));

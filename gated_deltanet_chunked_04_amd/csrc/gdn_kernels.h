@@ -128,6 +128,56 @@ __device__ __forceinline__ void seq_segs(const Geo& g, int32_t n, int32_t& nseg,
     }
 }
 
+// The CP prepasses of uniform-length batches run on a grid (vtiles x segments, sequence-heads)
+// whose second index is a priority rank: the sequence-heads with exact maps (modes 2 and 3),
+// whose workgroups walk whole sub-sequences, come first in dispatch order, the others (warm
+// windows only) after them. With the grid in plain order the long workgroups of a late head
+// wait for free CUs behind the short ones. This is the sequence-head at rank q (those with
+// exact maps in index order, then the rest), computed by every wave of the workgroup alike.
+__device__ __forceinline__ int32_t head_by_rank(const int32_t* modes, int32_t nh, int32_t q) {
+    const int lane = threadIdx.x & 63;
+    int32_t nlong = 0;
+    for (int32_t b = 0; b < nh; b += 64) {
+        const int32_t p = b + lane;
+        nlong += __popcll(__ballot(p < nh && modes[p] >= 2));
+    }
+    const bool want_long = q < nlong;
+    int32_t k = want_long ? q : q - nlong;
+    for (int32_t b = 0; b < nh; b += 64) {
+        const int32_t p = b + lane;
+        const bool ok = p < nh && (modes[p] >= 2) == want_long;
+        const uint64_t m = __ballot(ok);
+        const int32_t c = __popcll(m);
+        if (k < c) {
+            // the k-th lane of m
+            const uint32_t below = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+            return b + (int32_t)__builtin_ctzll(__ballot(ok && (int32_t)below == k));
+        }
+        k -= c;
+    }
+    return -1;
+}
+
+// The (global segment, head, row tile) of a CP prepass workgroup: the ranked grid above when
+// `ranked`, else (segment, head, row tile) = (blockIdx.x, blockIdx.y, blockIdx.z).
+__device__ __forceinline__ bool prepass_item(const Geo& geo, const int32_t* modes, bool ranked, int vtiles,
+                                             int64_t& gs, int& h, int& vt) {
+    if (!ranked) {
+        gs = blockIdx.x;
+        h = blockIdx.y;
+        vt = blockIdx.z;
+        return true;
+    }
+    const int32_t p = head_by_rank(modes, geo.N * geo.H, (int32_t)blockIdx.y);
+    if (p < 0) return false;
+    vt = (int)(blockIdx.x % vtiles);
+    const int32_t s = (int32_t)(blockIdx.x / vtiles);
+    const int32_t n = p / geo.H;
+    h = p - n * geo.H;
+    gs = (int64_t)n * geo.nseg + s;
+    return true;
+}
+
 // ---------------------------------------------------------------------------
 struct IntraArgs {
     Geo geo;
@@ -173,6 +223,7 @@ struct RecurArgs {
     float scale;
     int32_t use_cp;           // segments >= 1 read seginit
     int32_t q_l2;             // output modes: q is raw, its rows are L2-normalised as staged
+    int32_t ranked;           // prepass: the ranked grid (see head_by_rank)
     // the fully fused forward (launch_fused) reads the raw inputs instead of w, u and the gate cumsum
     const void* fv;           // [Ttot,H,V]
     const float* fg;          // [Ttot,H]
@@ -222,6 +273,7 @@ struct RevArgs {
     float scale;
     int32_t use_cp;
     int32_t q_l2;             // q is raw, its rows are L2-normalised as staged
+    int32_t ranked;           // prepass: the ranked grid (see head_by_rank)
 };
 
 struct BwdChunkArgs {

@@ -440,9 +440,15 @@ __global__ __launch_bounds__(RT * 4) void k_recur(RecurArgs a) {
     if constexpr (kStageH) L.sH = reinterpret_cast<T*>(smem + kOffH);
 
     const Geo& geo = a.geo;
-    const int64_t gs = blockIdx.x;
-    const int h = blockIdx.y;
-    const int vt = blockIdx.z;
+    int64_t gs_ = blockIdx.x;
+    int h_ = blockIdx.y, vt_ = blockIdx.z;
+    if constexpr (MODE == kRecurPrepass) {
+        // the prepass grid may be ranked (sequence-heads with exact maps dispatched first)
+        if (!prepass_item(geo, a.modes, a.ranked != 0, (geo.V + K + RT - 1) / RT, gs_, h_, vt_)) return;
+    }
+    const int64_t gs = gs_;
+    const int h = h_;
+    const int vt = vt_;
     const int V = geo.V;
     const int64_t H = geo.H;
     SegLoc sg;
@@ -715,7 +721,11 @@ hipError_t launch_recur_t(const RecurArgs& a, int64_t nsegs_grid, int vtiles, hi
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (e != hipSuccess) return e;
-    dim3 grid((unsigned)nsegs_grid, (unsigned)a.geo.H, (unsigned)vtiles);
+    // the prepass's ranked grid (row tiles x segments, sequence-heads by rank), else (segments,
+    // heads, row tiles)
+    const dim3 grid = MODE == kRecurPrepass && a.ranked
+                          ? dim3((unsigned)(vtiles * a.geo.nseg), (unsigned)(a.geo.N * a.geo.H), 1u)
+                          : dim3((unsigned)nsegs_grid, (unsigned)a.geo.H, (unsigned)vtiles);
     hipLaunchKernelGGL(kern, grid, dim3(C::NT), lds, st, a);
     return hipGetLastError();
 }
