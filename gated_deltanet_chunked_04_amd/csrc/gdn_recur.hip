@@ -852,7 +852,7 @@ struct ScanMap {
     f32x4 r[SC::NRT][SC::KW];    // R~[rt*16 + ln][(w KW + j) * 16 + gq*4 ..]
 };
 
-template <typename T, int K>
+template <typename T, int K, int kDepth>
 __global__ __launch_bounds__(256) void k_scan(ScanArgs a) {
     using SC = ScanCfg<T, K>;
     constexpr int KW = SC::KW;
@@ -910,7 +910,9 @@ __global__ __launch_bounds__(256) void k_scan(ScanArgs a) {
     // reverse: G_{s-1} = G_s M_s + R_s, s = nseg-1 .. 1 (adjoint leaving segment s-1)
     auto src_of = [&](int step) { return a.reverse ? nseg - 1 - step : step; };
     const int nsteps = nseg - 1;
-    constexpr int kDepth = 4;
+    // maps in flight: four, or two (half the registers: the backward's reverse scan then fits
+    // beside a workgroup of the chunk-state pass, which it runs next to)
+    static_assert(kDepth == 2 || kDepth == 4, "two or four maps in flight");
     ScanMap<T, K> mb[kDepth];
     f32x4 accA[NRT][KW], accB[NRT][KW];
 #pragma unroll
@@ -961,18 +963,23 @@ __global__ __launch_bounds__(256) void k_scan(ScanArgs a) {
     for (; step + kDepth <= nsteps; step += kDepth) {
         one(mb[0], accA, accB, step);
         one(mb[1], accB, accA, step + 1);
-        one(mb[2], accA, accB, step + 2);
-        one(mb[3], accB, accA, step + 3);
+        if constexpr (kDepth == 4) {
+            one(mb[2], accA, accB, step + 2);
+            one(mb[3], accB, accA, step + 3);
+        }
     }
     if (step < nsteps) one(mb[0], accA, accB, step);
-    if (step + 1 < nsteps) one(mb[1], accB, accA, step + 1);
-    if (step + 2 < nsteps) one(mb[2], accA, accB, step + 2);
+    if constexpr (kDepth == 4) {
+        if (step + 1 < nsteps) one(mb[1], accB, accA, step + 1);
+        if (step + 2 < nsteps) one(mb[2], accA, accB, step + 2);
+    }
 }
 
 template <typename T, int K>
 hipError_t launch_scan_t(const ScanArgs& a, hipStream_t st) {
     using SC = ScanCfg<T, K>;
-    auto kern = k_scan<T, K>;
+    // the reverse scan runs beside the backward's chunk-state pass: two maps in flight
+    auto kern = a.reverse ? k_scan<T, K, 2> : k_scan<T, K, 4>;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, SC::total);
     if (e != hipSuccess) return e;
