@@ -447,8 +447,10 @@ gdn_status run_intra(const gdn_desc* d, const Plan& p, unsigned char* ws, const 
 // The CP decision: per sequence-head modes [N,H] and per boundary windows [total_segs,H] in one
 // direction, and optionally the other direction's (the backward's adjoint pass) in the same launch.
 // The CP prepasses run on the ranked grid (sequence-heads with exact maps dispatched first)
-// for uniform-length batches whose sequence-head count fits one grid dimension.
-int32_t prepass_ranked(const Plan& p) { return !p.varlen && (int64_t)p.N * p.H <= 65535 ? 1 : 0; }
+// for uniform-length batches (its one dimension holds every workgroup).
+int32_t prepass_ranked(const Plan& p) {
+    return !p.varlen && (int64_t)p.N * p.H * p.nseg * 4 < ((int64_t)1 << 31) ? 1 : 0;
+}
 
 gdn_status run_decide(const gdn_desc* d, const Plan& p, unsigned char* ws, int32_t* modes, int32_t* bwin,
                       hipStream_t st, int reverse = 0, int32_t* modes_r = nullptr, int32_t* bwin_r = nullptr) {

@@ -128,38 +128,36 @@ __device__ __forceinline__ void seq_segs(const Geo& g, int32_t n, int32_t& nseg,
     }
 }
 
-// The CP prepasses of uniform-length batches run on a grid (vtiles x segments, sequence-heads)
-// whose second index is a priority rank: the sequence-heads with exact maps (modes 2 and 3),
-// whose workgroups walk whole sub-sequences, come first in dispatch order, the others (warm
-// windows only) after them. With the grid in plain order the long workgroups of a late head
-// wait for free CUs behind the short ones. This is the sequence-head at rank q (those with
-// exact maps in index order, then the rest), computed by every wave of the workgroup alike.
-__device__ __forceinline__ int32_t head_by_rank(const int32_t* modes, int32_t nh, int32_t q) {
+// The CP prepasses of uniform-length batches run on a one-dimensional grid in which the
+// workgroups of the sequence-heads with exact maps (modes 2 and 3), which walk whole
+// sub-sequences, come first in dispatch order, the row tiles of each segment (the map rows
+// too) side by side; the other sequence-heads (warm windows only) follow in the order of the
+// plain grid (row tile slowest, then head, then sequence, then segment). With the plain grid
+// the long workgroups of a late head wait for free CUs behind the short ones. Sequence-heads
+// are counted in the key order h * N + n (head major), the plain grid's.
+// The sequence-head (n * H + h) of rank q among those with (long) or without exact maps.
+__device__ __forceinline__ int32_t head_of_rank(const int32_t* modes, int32_t N, int32_t H, bool long_, int32_t q) {
     const int lane = threadIdx.x & 63;
-    int32_t nlong = 0;
+    const int32_t nh = N * H;
     for (int32_t b = 0; b < nh; b += 64) {
-        const int32_t p = b + lane;
-        nlong += __popcll(__ballot(p < nh && modes[p] >= 2));
-    }
-    const bool want_long = q < nlong;
-    int32_t k = want_long ? q : q - nlong;
-    for (int32_t b = 0; b < nh; b += 64) {
-        const int32_t p = b + lane;
-        const bool ok = p < nh && (modes[p] >= 2) == want_long;
+        const int32_t k = b + lane;
+        const int32_t p = k < nh ? (k % N) * H + k / N : 0;
+        const bool ok = k < nh && (modes[p] >= 2) == long_;
         const uint64_t m = __ballot(ok);
         const int32_t c = __popcll(m);
-        if (k < c) {
-            // the k-th lane of m
+        if (q < c) {
+            // the q-th lane of m
             const uint32_t below = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-            return b + (int32_t)__builtin_ctzll(__ballot(ok && (int32_t)below == k));
+            const int32_t kk = b + (int32_t)__builtin_ctzll(__ballot(ok && (int32_t)below == q));
+            return (kk % N) * H + kk / N;
         }
-        k -= c;
+        q -= c;
     }
     return -1;
 }
 
-// The (global segment, head, row tile) of a CP prepass workgroup: the ranked grid above when
-// `ranked`, else (segment, head, row tile) = (blockIdx.x, blockIdx.y, blockIdx.z).
+// The (global segment, head, row tile) of a CP prepass workgroup: the ranked one-dimensional
+// grid above when `ranked`, else (segment, head, row tile) = (blockIdx.x, blockIdx.y, blockIdx.z).
 __device__ __forceinline__ bool prepass_item(const Geo& geo, const int32_t* modes, bool ranked, int vtiles,
                                              int64_t& gs, int& h, int& vt) {
     if (!ranked) {
@@ -168,13 +166,28 @@ __device__ __forceinline__ bool prepass_item(const Geo& geo, const int32_t* mode
         vt = blockIdx.z;
         return true;
     }
-    const int32_t p = head_by_rank(modes, geo.N * geo.H, (int32_t)blockIdx.y);
+    const int lane = threadIdx.x & 63;
+    const int32_t nh = geo.N * geo.H, nseg = geo.nseg;
+    int32_t nlong = 0;
+    for (int32_t b = 0; b < nh; b += 64) nlong += __popcll(__ballot(b + lane < nh && modes[b + lane] >= 2));
+    const int64_t L = blockIdx.x, per_head = (int64_t)nseg * vtiles, A = (int64_t)nlong * per_head;
+    int32_t p, s;
+    if (L < A) {  // heads with exact maps: row tiles fastest (both are whole walks), then segments
+        const int64_t w = L % per_head;
+        p = head_of_rank(modes, geo.N, geo.H, true, (int32_t)(L / per_head));
+        vt = (int)(w % vtiles);
+        s = (int32_t)(w / vtiles);
+    } else {  // the others: row tile, then head rank, then segment
+        const int64_t Lr = L - A, per_vt = (int64_t)(nh - nlong) * nseg;
+        vt = (int)(Lr / per_vt);
+        const int64_t r = Lr % per_vt;
+        p = head_of_rank(modes, geo.N, geo.H, false, (int32_t)(r / nseg));
+        s = (int32_t)(r % nseg);
+    }
     if (p < 0) return false;
-    vt = (int)(blockIdx.x % vtiles);
-    const int32_t s = (int32_t)(blockIdx.x / vtiles);
     const int32_t n = p / geo.H;
     h = p - n * geo.H;
-    gs = (int64_t)n * geo.nseg + s;
+    gs = (int64_t)n * nseg + s;
     return true;
 }
 

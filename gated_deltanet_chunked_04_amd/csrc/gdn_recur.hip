@@ -721,10 +721,10 @@ hipError_t launch_recur_t(const RecurArgs& a, int64_t nsegs_grid, int vtiles, hi
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (e != hipSuccess) return e;
-    // the prepass's ranked grid (row tiles x segments, sequence-heads by rank), else (segments,
-    // heads, row tiles)
+    // the prepass's ranked one-dimensional grid (see prepass_item), else (segments, heads, row
+    // tiles)
     const dim3 grid = MODE == kRecurPrepass && a.ranked
-                          ? dim3((unsigned)(vtiles * a.geo.nseg), (unsigned)(a.geo.N * a.geo.H), 1u)
+                          ? dim3((unsigned)((int64_t)vtiles * a.geo.nseg * a.geo.N * a.geo.H), 1u, 1u)
                           : dim3((unsigned)nsegs_grid, (unsigned)a.geo.H, (unsigned)vtiles);
     hipLaunchKernelGGL(kern, grid, dim3(C::NT), lds, st, a);
     return hipGetLastError();
