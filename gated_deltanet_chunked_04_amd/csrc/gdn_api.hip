@@ -748,6 +748,13 @@ gdn_status gdn_chunk_bwd(const gdn_desc* desc, const void* q, const void* k, con
         if (hipEventRecord(side.fork, st) != hipSuccess || hipStreamWaitEvent(st2, side.fork, 0) != hipSuccess)
             return GDN_ERR_HIP;
     }
+    // Without CP the reverse adjoint pass walks whole sequences and is the longer chain: it goes
+    // on the caller's stream, which the hardware reaches first after the fork, so that all its
+    // workgroups (the longest sequences' too) take the chip at once and the states pass fills
+    // in behind them; otherwise the forward-direction chain stays on the caller's stream.
+    const bool swap = fork && !carry && !p.cp_on;
+    const hipStream_t sm = swap ? st2 : st;  // the forward-direction chain (2)
+    const hipStream_t sr2 = swap ? st : st2;  // the reverse chain (3)
     // 2. chunk-entry states and Delta, with the forward's CP (kept by the forward when reused)
     RecurArgs ra{};
     memset(&ra, 0, sizeof(ra));
@@ -769,7 +776,7 @@ gdn_status gdn_chunk_bwd(const gdn_desc* desc, const void* q, const void* k, con
         ra.seginit_out = seginit;
         ra.prep = prep;
         ra.ranked = prepass_ranked(p);
-        GDN_LAUNCH(kKPrepass, st, launch_recur(ra, desc->dtype, kRecurPrepass, p.total_segs, vktiles, st));
+        GDN_LAUNCH(kKPrepass, sm, launch_recur(ra, desc->dtype, kRecurPrepass, p.total_segs, vktiles, sm));
         ScanArgs sa{};
         memset(&sa, 0, sizeof(sa));
         sa.geo = ra.geo;
@@ -777,15 +784,15 @@ gdn_status gdn_chunk_bwd(const gdn_desc* desc, const void* q, const void* k, con
         sa.prep = prep;
         sa.seginit = seginit;
         sa.modes = modes;
-        GDN_LAUNCH(kKScan, st, launch_scan(sa, desc->dtype, st));
+        GDN_LAUNCH(kKScan, sm, launch_scan(sa, desc->dtype, sm));
         ra.seginit = seginit;
     } else if (p.cp_on) {
         ra.seginit = cpr.seginit;
     }
-    if (!reuse) GDN_LAUNCH(kKRecurStates, st, launch_recur(ra, desc->dtype, kRecurStates, p.total_segs, vtiles, st));
+    if (!reuse) GDN_LAUNCH(kKRecurStates, sm, launch_recur(ra, desc->dtype, kRecurStates, p.total_segs, vtiles, sm));
     // 3. reverse adjoint pass, with CP mirrored (windows and scan from the sequence end)
     const gdn_status sr = [&]() -> gdn_status {
-    hipStream_t st = st2;
+    hipStream_t st = sr2;
     RevArgs va;
     memset(&va, 0, sizeof(va));
     va.geo = ra.geo;
