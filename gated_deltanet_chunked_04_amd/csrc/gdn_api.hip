@@ -48,7 +48,7 @@ struct Plan {
     int32_t esize = 2;
     // forward workspace
     size_t o_kn = 0, o_gam = 0, o_w = 0, o_u = 0, o_cstat = 0, o_bos = 0, o_len = 0, o_choff = 0, o_segoff = 0,
-           o_ctab = 0, o_stab = 0, o_modes = 0, o_bwin = 0, o_seginit = 0, o_prep = 0, fwd_bytes = 0;
+           o_ctab = 0, o_stab = 0, o_sord = 0, o_modes = 0, o_bwin = 0, o_seginit = 0, o_prep = 0, fwd_bytes = 0;
     // backward workspace: the forward's layout, then these
     size_t o_modes_r = 0, o_bwin_r = 0, o_seginit_r = 0, o_prep_r = 0, o_h = 0, o_gst = 0, o_tm = 0, o_dl = 0, o_ddl = 0,
            bwd_bytes = 0;
@@ -58,6 +58,7 @@ struct Plan {
     int32_t bwd_ok = 1;  // fp32 backward supports K = V = 64 only (LDS)
     int32_t fused = 0;   // the forward runs fully fused (no CP, bf16, no kept intermediates)
     int32_t carry = 0;   // the backward's per-chunk kernel carries the adjoint (no adjoint pass)
+    int32_t seg_order = 0;  // varlen: the recurrence grids take the segments most chunks first
 };
 
 int query_cus() {
@@ -199,6 +200,11 @@ gdn_status make_plan(const gdn_desc* d, Plan& p) {
         p.o_segoff = take((size_t)(p.N + 1) * 4);
         p.o_ctab = take((size_t)p.total_chunks * 8);
         p.o_stab = take((size_t)p.total_segs * 16);
+        // Longest sequences first in the recurrence grids (ranked by one workgroup, so for a
+        // bounded count; the one-dimensional grid's work-items, at most 4 * H * V per segment,
+        // must fit 32 bits).
+        p.seg_order = p.total_segs <= kOrderMaxSegs && (int64_t)p.total_segs * H * V * 4 < ((int64_t)1 << 32);
+        if (p.seg_order) p.o_sord = take((size_t)p.total_segs * 4);
     }
     if (p.cp_on) {
         p.o_seginit = take((size_t)p.total_segs * H * V * K * 4);
@@ -265,6 +271,7 @@ Geo make_geo(const gdn_desc* d, const Plan& p, unsigned char* ws) {
         g.seq_segoff = reinterpret_cast<const int32_t*>(ws + p.o_segoff);
         g.chunk_tab = reinterpret_cast<const int2*>(ws + p.o_ctab);
         g.seg_tab = reinterpret_cast<const int4*>(ws + p.o_stab);
+        if (p.seg_order) g.seg_order = reinterpret_cast<const int32_t*>(ws + p.o_sord);
     }
     return g;
 }
@@ -421,6 +428,7 @@ TableArgs table_args(const gdn_desc* d, const Plan& p, unsigned char* ws) {
     t.seq_segoff = reinterpret_cast<int32_t*>(ws + p.o_segoff);
     t.chunk_tab = reinterpret_cast<int2*>(ws + p.o_ctab);
     t.seg_tab = reinterpret_cast<int4*>(ws + p.o_stab);
+    t.seg_order = p.seg_order ? reinterpret_cast<int32_t*>(ws + p.o_sord) : nullptr;
     return t;
 }
 

@@ -164,6 +164,8 @@ __global__ __launch_bounds__(RT * 4) void k_reverse(RevArgs a) {
     if constexpr (MODE == kRecurPrepass) {
         // the prepass grid may be ranked (sequence-heads with exact maps dispatched first)
         if (!prepass_item(geo, a.modes, a.ranked != 0, (geo.V + K + RT - 1) / RT, gs_, h_, vt_)) return;
+    } else if (geo.seg_order) {
+        ordered_seg_item(geo, geo.V / RT, gs_, h_, vt_);
     }
     const int64_t gs = gs_;
     const int h = h_;
@@ -526,10 +528,12 @@ hipError_t launch_reverse_t(const RevArgs& a, int64_t nsegs_grid, int vtiles, hi
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, C::total);
     if (e != hipSuccess) return e;
-    // the prepass's ranked one-dimensional grid (see prepass_item), else (segments, heads, row
-    // tiles)
+    // the prepass's ranked one-dimensional grid (see prepass_item), the varlen segment order's
+    // (see ordered_seg_item), else (segments, heads, row tiles)
     const dim3 grid = MODE == kRecurPrepass && a.ranked
                           ? dim3((unsigned)((int64_t)vtiles * a.geo.nseg * a.geo.N * a.geo.H), 1u, 1u)
+                      : MODE != kRecurPrepass && a.geo.seg_order
+                          ? dim3((unsigned)(nsegs_grid * a.geo.H * vtiles), 1u, 1u)
                           : dim3((unsigned)nsegs_grid, (unsigned)a.geo.H, (unsigned)vtiles);
     hipLaunchKernelGGL(kern, grid, dim3(C::NT), C::total, st, a);
     return hipGetLastError();

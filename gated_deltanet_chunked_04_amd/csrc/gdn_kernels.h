@@ -25,6 +25,7 @@ struct Geo {
     const int32_t* seq_segoff;  // [N+1] first global segment of each sequence
     const int2* chunk_tab;      // [total_chunks] (n, chunk index in sequence); n < 0: unused
     const int4* seg_tab;        // [total_segs]   (n, s, c0, c1); n < 0: unused
+    const int32_t* seg_order;   // [total_segs]   (varlen) segments, most chunks first; null: none
 };
 
 struct ChunkLoc {
@@ -191,6 +192,19 @@ __device__ __forceinline__ bool prepass_item(const Geo& geo, const int32_t* mode
     return true;
 }
 
+// The (global segment, head, row tile) of a varlen recurrence workgroup when the varlen tables
+// hold a segment order: a one-dimensional grid, segment rank slowest, then head, then row tile,
+// so that the longest sequences' workgroups are dispatched first (when the workgroups outnumber
+// the CUs, or share the chip with another pass, the rest fill in behind them).
+__device__ __forceinline__ void ordered_seg_item(const Geo& geo, int vtiles, int64_t& gs, int& h, int& vt) {
+    const int64_t L = blockIdx.x, per_seg = (int64_t)geo.H * vtiles;
+    const int64_t r = L / per_seg;
+    const int w = (int)(L - r * per_seg);
+    gs = geo.seg_order[r];
+    h = w / vtiles;
+    vt = w - h * vtiles;
+}
+
 // ---------------------------------------------------------------------------
 struct IntraArgs {
     Geo geo;
@@ -333,7 +347,11 @@ struct TableArgs {
     int32_t* seq_segoff;
     int2* chunk_tab;
     int4* seg_tab;
+    int32_t* seg_order;  // null: no order built (at most kOrderMaxSegs segments otherwise)
 };
+
+// Segments a varlen segment order is built for (one workgroup ranks them all in LDS).
+constexpr int kOrderMaxSegs = 512;
 
 // State rows per workgroup of the recurrence kernels: all 128 value rows when
 // V = K = 128 (8 waves), else 64 (4 waves). V and K are multiples of it.

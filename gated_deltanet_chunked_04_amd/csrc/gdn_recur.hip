@@ -445,6 +445,8 @@ __global__ __launch_bounds__(RT * 4) void k_recur(RecurArgs a) {
     if constexpr (MODE == kRecurPrepass) {
         // the prepass grid may be ranked (sequence-heads with exact maps dispatched first)
         if (!prepass_item(geo, a.modes, a.ranked != 0, (geo.V + K + RT - 1) / RT, gs_, h_, vt_)) return;
+    } else if (geo.seg_order) {
+        ordered_seg_item(geo, geo.V / RT, gs_, h_, vt_);
     }
     const int64_t gs = gs_;
     const int h = h_;
@@ -721,10 +723,12 @@ hipError_t launch_recur_t(const RecurArgs& a, int64_t nsegs_grid, int vtiles, hi
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (e != hipSuccess) return e;
-    // the prepass's ranked one-dimensional grid (see prepass_item), else (segments, heads, row
-    // tiles)
+    // the prepass's ranked one-dimensional grid (see prepass_item), the varlen segment order's
+    // (see ordered_seg_item), else (segments, heads, row tiles)
     const dim3 grid = MODE == kRecurPrepass && a.ranked
                           ? dim3((unsigned)((int64_t)vtiles * a.geo.nseg * a.geo.N * a.geo.H), 1u, 1u)
+                      : MODE != kRecurPrepass && a.geo.seg_order
+                          ? dim3((unsigned)(nsegs_grid * a.geo.H * vtiles), 1u, 1u)
                           : dim3((unsigned)nsegs_grid, (unsigned)a.geo.H, (unsigned)vtiles);
     hipLaunchKernelGGL(kern, grid, dim3(C::NT), lds, st, a);
     return hipGetLastError();
@@ -1262,9 +1266,14 @@ hipError_t launch_fused_t(const RecurArgs& a, int64_t nseqs, int vtiles, hipStre
 __global__ __launch_bounds__(kThreads) void k_tables(TableArgs a) {
     __shared__ int32_t s_ch[kThreads], s_sg[kThreads];
     __shared__ int32_t s_base[2];
+    __shared__ int32_t s_key[kOrderMaxSegs];  // chunks per segment, for the segment order
     const int tid = threadIdx.x;
+    const bool order = a.seg_order != nullptr && a.total_segs <= kOrderMaxSegs;
     for (int64_t i = tid; i < a.total_chunks; i += kThreads) a.chunk_tab[i] = make_int2(-1, 0);
-    for (int64_t i = tid; i < a.total_segs; i += kThreads) a.seg_tab[i] = make_int4(-1, 0, 0, 0);
+    for (int64_t i = tid; i < a.total_segs; i += kThreads) {
+        a.seg_tab[i] = make_int4(-1, 0, 0, 0);
+        if (order) s_key[i] = 0;
+    }
     if (tid == 0) {
         s_base[0] = 0;
         s_base[1] = 0;
@@ -1323,8 +1332,27 @@ __global__ __launch_bounds__(kThreads) void k_tables(TableArgs a) {
         for (int s = 0; s < nsg; ++s) {
             const int c0 = s * a.seg_len;
             const int c1 = min(c0 + a.seg_len, nch);
-            if (so + s < a.total_segs) a.seg_tab[so + s] = make_int4(n, s, nsg == 1 ? 0 : c0, nsg == 1 ? nch : c1);
+            if (so + s < a.total_segs) {
+                a.seg_tab[so + s] = make_int4(n, s, nsg == 1 ? 0 : c0, nsg == 1 ? nch : c1);
+                if (order) s_key[so + s] = nsg == 1 ? nch : c1 - c0;
+            }
         }
+    }
+    if (a.seg_order == nullptr) return;
+    __syncthreads();
+    // The segment order, most chunks first, ties in index order: segment i's rank counts the
+    // segments that go before it, so the ranks are a permutation of 0..total_segs-1.
+    for (int64_t i = tid; i < a.total_segs; i += kThreads) {
+        int64_t r = i;
+        if (order) {
+            const int32_t ki = s_key[i];
+            r = 0;
+            for (int j = 0; j < (int)a.total_segs; ++j) {
+                const int32_t kj = s_key[j];
+                r += (kj > ki) || (kj == ki && j < i);
+            }
+        }
+        a.seg_order[r] = (int32_t)i;
     }
 }
 
