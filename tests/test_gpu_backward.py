@@ -9,8 +9,8 @@ import pytest
 import torch
 
 from gdn_inputs import make_inputs
-from gpu_helpers import (check, mid_decay_inputs, mixed_decay_inputs, raw_key_inputs, seq_slices, small_inputs,
-                         to_dev, tol_for)
+from gpu_helpers import (check, gpu_fwd, mid_decay_inputs, mixed_decay_inputs, oracle, raw_key_inputs, seq_slices,
+                         small_inputs, to_dev, tol_for)
 from oracle import ref_bwd
 
 pytestmark = pytest.mark.gpu
@@ -111,6 +111,46 @@ def test_backward_varlen(gpu_lib, cp, kw, dtype):
         check(out["d_initial_state"][n], ref["d_initial_state"][n], tol, f"d_initial_state of sequence {n}")
     # the empty sequence passes d(final state) straight through
     assert torch.equal(out["d_initial_state"][4].cpu(), inp["d_final_state"][4])
+
+
+def many_lengths(nseq, seed):
+    """Packed lengths with many equal chunk counts (ties of the longest-first order, which ranks
+    them by index), an increasing run, a repeated longest length and empty sequences."""
+    rng = np.random.default_rng(seed)
+    top = 400 if nseq <= 64 else 140
+    body = sorted(int(x) for x in rng.integers(1, top, nseq - 8))
+    return [top - 100] * 4 + [0, 1, 64, 65] + body
+
+
+@pytest.mark.parametrize("nseq,cp,kw", [(40, "off", {}), (40, "exact", dict(seg_chunks=2)),
+                                        (600, "off", {}), (600, "exact", dict(seg_chunks=1))])
+def test_varlen_many_sequences(gpu_lib, nseq, cp, kw):
+    """Packed varlen, forward and backward, with the recurrence grids taking the segments in the
+    varlen tables' longest-first order (at most 512 segments) and in plain grid order past that
+    bound; every sequence checked on its own."""
+    lengths = many_lengths(nseq, seed=nseq)
+    nch = [-(-n // 64) for n in lengths]
+    per = kw.get("seg_chunks")
+    segs = len(lengths) if per is None else sum(max(1, -(-c // per)) for c in nch)
+    assert (segs <= 512) == (nseq == 40), segs  # the case is on the intended side of the bound
+    inp = with_grads(small_inputs(H=2, K=128, V=128, dtype=torch.bfloat16, lengths=lengths, seed=33))
+    tol = tol_for(torch.bfloat16)
+    d = to_dev(inp)
+    o, sT = gpu_fwd(d, cp_mode=cp, **kw)
+    o_ref, s_ref = oracle(inp)
+    check(o, o_ref, tol, "o")
+    check(sT, s_ref, tol, "final_state")
+    out = gpu_bwd(d, cp_mode=cp, **kw)
+    ref = oracle_bwd(inp)
+    compare(out, ref, tol)
+    oc = o.cpu()
+    for n, a, b in seq_slices(inp["cu_seqlens"]):
+        if b - a < 64:
+            continue  # the short ones weigh little but are covered by the packed checks above
+        check(oc[:, a:b], o_ref[:, a:b], tol, f"o of sequence {n}")
+        check(out["dk"][:, a:b], ref["dk"][:, a:b], tol, f"dk of sequence {n}")
+        check(out["d_initial_state"][n], ref["d_initial_state"][n], tol, f"d_initial_state of sequence {n}")
+    assert torch.equal(sT[4].cpu(), inp["initial_state"][4])
 
 
 def test_backward_no_initial_state_no_final_grad(gpu_lib):
