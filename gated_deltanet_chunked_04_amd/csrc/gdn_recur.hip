@@ -1067,9 +1067,9 @@ __global__ __launch_bounds__(RT * 4) void k_fused(RecurArgs a) {
     float* sBeta = reinterpret_cast<float*>(smem + F::off_beta);
 
     const Geo& geo = a.geo;
-    const int64_t gs = blockIdx.x;
-    const int h = blockIdx.y;
-    const int vt = blockIdx.z;
+    int64_t gs = blockIdx.x;
+    int h = blockIdx.y, vt = blockIdx.z;
+    if (geo.seg_order) ordered_seg_item(geo, geo.V / RT, gs, h, vt);  // varlen: longest first
     const int V = geo.V;
     SegLoc sg;
     if (!locate_seg(geo, gs, sg)) return;
@@ -1254,7 +1254,8 @@ hipError_t launch_fused_t(const RecurArgs& a, int64_t nseqs, int vtiles, hipStre
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, F::total);
     if (e != hipSuccess) return e;
-    dim3 grid((unsigned)nseqs, (unsigned)a.geo.H, (unsigned)vtiles);
+    const dim3 grid = a.geo.seg_order ? dim3((unsigned)(nseqs * a.geo.H * vtiles), 1u, 1u)
+                                      : dim3((unsigned)nseqs, (unsigned)a.geo.H, (unsigned)vtiles);
     hipLaunchKernelGGL(kern, grid, dim3(RT * 4), F::total, st, a);
     return hipGetLastError();
 }
