@@ -200,10 +200,9 @@ gdn_status make_plan(const gdn_desc* d, Plan& p) {
         p.o_segoff = take((size_t)(p.N + 1) * 4);
         p.o_ctab = take((size_t)p.total_chunks * 8);
         p.o_stab = take((size_t)p.total_segs * 16);
-        // Longest sequences first in the recurrence grids (ranked by one workgroup, so for a
-        // bounded count; the one-dimensional grid's work-items, at most 4 * H * V per segment,
-        // must fit 32 bits).
-        p.seg_order = p.total_segs <= kOrderMaxSegs && (int64_t)p.total_segs * H * V * 4 < ((int64_t)1 << 32);
+        // Longest sequences first in the recurrence grids (the one-dimensional grid's work-items,
+        // at most 4 * H * V per segment, must fit 32 bits).
+        p.seg_order = (int64_t)p.total_segs * H * V * 4 < ((int64_t)1 << 32);
         if (p.seg_order) p.o_sord = take((size_t)p.total_segs * 4);
     }
     if (p.cp_on) {

@@ -347,11 +347,11 @@ struct TableArgs {
     int32_t* seq_segoff;
     int2* chunk_tab;
     int4* seg_tab;
-    int32_t* seg_order;  // null: no order built (at most kOrderMaxSegs segments otherwise)
+    int32_t* seg_order;  // null: no order built
 };
 
-// Segments a varlen segment order is built for (one workgroup ranks them all in LDS).
-constexpr int kOrderMaxSegs = 512;
+// Bins of the varlen segment order's counting sort (chunk counts; longer segments share the last).
+constexpr int kOrderBins = 4096;
 
 // State rows per workgroup of the recurrence kernels: all 128 value rows when
 // V = K = 128 (8 waves), else 64 (4 waves). V and K are multiples of it.

@@ -1267,14 +1267,10 @@ hipError_t launch_fused_t(const RecurArgs& a, int64_t nseqs, int vtiles, hipStre
 __global__ __launch_bounds__(kThreads) void k_tables(TableArgs a) {
     __shared__ int32_t s_ch[kThreads], s_sg[kThreads];
     __shared__ int32_t s_base[2];
-    __shared__ int32_t s_key[kOrderMaxSegs];  // chunks per segment, for the segment order
+    __shared__ int32_t s_bin[kOrderBins];  // the segment order's counting sort
     const int tid = threadIdx.x;
-    const bool order = a.seg_order != nullptr && a.total_segs <= kOrderMaxSegs;
     for (int64_t i = tid; i < a.total_chunks; i += kThreads) a.chunk_tab[i] = make_int2(-1, 0);
-    for (int64_t i = tid; i < a.total_segs; i += kThreads) {
-        a.seg_tab[i] = make_int4(-1, 0, 0, 0);
-        if (order) s_key[i] = 0;
-    }
+    for (int64_t i = tid; i < a.total_segs; i += kThreads) a.seg_tab[i] = make_int4(-1, 0, 0, 0);
     if (tid == 0) {
         s_base[0] = 0;
         s_base[1] = 0;
@@ -1321,40 +1317,66 @@ __global__ __launch_bounds__(kThreads) void k_tables(TableArgs a) {
         a.seq_segoff[a.N] = s_base[1];
     }
     __syncthreads();
-    // fill: thread per sequence
-    for (int n = tid; n < a.N; n += kThreads) {
-        const int32_t len = a.seq_len[n];
-        const int32_t nch = (len + 63) / 64;
-        const int64_t co = a.seq_choff[n];
-        for (int j = 0; j < nch; ++j)
-            if (co + j < a.total_chunks) a.chunk_tab[co + j] = make_int2(n, j);
-        const int64_t so = a.seq_segoff[n];
-        const int32_t nsg = a.seq_segoff[n + 1] - a.seq_segoff[n];
-        for (int s = 0; s < nsg; ++s) {
-            const int c0 = s * a.seg_len;
-            const int c1 = min(c0 + a.seg_len, nch);
-            if (so + s < a.total_segs) {
-                a.seg_tab[so + s] = make_int4(n, s, nsg == 1 ? 0 : c0, nsg == 1 ? nch : c1);
-                if (order) s_key[so + s] = nsg == 1 ? nch : c1 - c0;
+    // fill: a wave per 64 sequences; each sequence's chunk entries are written by all 64 lanes
+    // (its count and first chunk shuffled from the lane that holds it), its segment entries by
+    // its own lane
+    const int lane = tid & 63;
+    for (int nb = tid - lane; nb < a.N; nb += kThreads) {
+        const int n = nb + lane;
+        const int32_t nch = n < a.N ? (a.seq_len[n] + 63) / 64 : 0;
+        const int32_t co = n < a.N ? a.seq_choff[n] : 0;
+        for (int src = 0; src < 64; ++src) {
+            const int32_t m = __shfl(nch, src), cs = __shfl(co, src);
+            for (int j = lane; j < m; j += 64)
+                if (cs + j < a.total_chunks) a.chunk_tab[cs + j] = make_int2(nb + src, j);
+        }
+        if (n < a.N) {
+            const int64_t so = a.seq_segoff[n];
+            const int32_t nsg = a.seq_segoff[n + 1] - a.seq_segoff[n];
+            for (int s = 0; s < nsg; ++s) {
+                const int c0 = s * a.seg_len;
+                const int c1 = min(c0 + a.seg_len, nch);
+                if (so + s < a.total_segs) a.seg_tab[so + s] = make_int4(n, s, nsg == 1 ? 0 : c0, nsg == 1 ? nch : c1);
             }
         }
     }
     if (a.seg_order == nullptr) return;
+    // The segment order, most chunks first: a counting sort on the chunk count (clamped to the
+    // last bin). Segments with equal counts land in any order, which changes no result (every
+    // workgroup's work is the same wherever the grid puts it); unused entries count as empty.
+    auto bin_of = [&](int64_t i) {
+        const int4 e = a.seg_tab[i];
+        return e.x < 0 ? 0 : min(e.w - e.z, kOrderBins - 1);
+    };
+    for (int i = tid; i < kOrderBins; i += kThreads) s_bin[i] = 0;
+    __syncthreads();  // also makes this workgroup's segment entries visible to all its threads
+    for (int64_t i = tid; i < a.total_segs; i += kThreads) atomicAdd(&s_bin[bin_of(i)], 1);
     __syncthreads();
-    // The segment order, most chunks first, ties in index order: segment i's rank counts the
-    // segments that go before it, so the ranks are a permutation of 0..total_segs-1.
-    for (int64_t i = tid; i < a.total_segs; i += kThreads) {
-        int64_t r = i;
-        if (order) {
-            const int32_t ki = s_key[i];
-            r = 0;
-            for (int j = 0; j < (int)a.total_segs; ++j) {
-                const int32_t kj = s_key[j];
-                r += (kj > ki) || (kj == ki && j < i);
-            }
-        }
-        a.seg_order[r] = (int32_t)i;
+    // first slot of each bin: the segments in the bins above it (thread t sums the bins of
+    // ranks [t P, t P + P) counted from the top, then a scan over the threads)
+    constexpr int P = kOrderBins / kThreads;
+    int32_t cnt[P], sum = 0;
+#pragma unroll
+    for (int j = 0; j < P; ++j) {
+        cnt[j] = s_bin[kOrderBins - 1 - (tid * P + j)];
+        sum += cnt[j];
     }
+    s_ch[tid] = sum;
+    __syncthreads();
+    for (int off = 1; off < kThreads; off <<= 1) {
+        const int32_t x = tid >= off ? s_ch[tid - off] : 0;
+        __syncthreads();
+        s_ch[tid] += x;
+        __syncthreads();
+    }
+    int32_t at = s_ch[tid] - sum;
+#pragma unroll
+    for (int j = 0; j < P; ++j) {
+        s_bin[kOrderBins - 1 - (tid * P + j)] = at;
+        at += cnt[j];
+    }
+    __syncthreads();
+    for (int64_t i = tid; i < a.total_segs; i += kThreads) a.seg_order[atomicAdd(&s_bin[bin_of(i)], 1)] = (int32_t)i;
 }
 
 }  // namespace
