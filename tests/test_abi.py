@@ -142,6 +142,34 @@ def test_varlen_plan():
     assert p["total_segments"] == segs
 
 
+def varlen_plan(lens, H, **kw):
+    cu = torch.tensor([0] + list(torch.tensor(lens).cumsum(0)), dtype=torch.int32)
+    d = gdn.Desc(1, int(cu[-1]), H, 128, 128, torch.bfloat16, num_cus=256, **kw)
+    hc = cu.numpy().astype("int32")
+    d.c.num_seqs = len(lens)
+    d.c.cu_seqlens = 0x1000  # never dereferenced by the planner
+    d.c.cu_seqlens_host = hc.ctypes.data
+    return gdn.gdn_plan(d)
+
+
+def test_varlen_plan_imbalance():
+    """AutoCP on packed sequences that fill every recurrence slot: split only when the longest
+    sequence takes 1.5x the chunk steps per slot the batch needs, into sub-sequences of half that."""
+    lens = [14000, 1500, 9000, 3000, 16000, 4000, 12000, 6252]  # 65,752 tokens, longest 250 chunks
+    p = varlen_plan(lens, 32)
+    nch = [-(-n // 64) for n in lens]
+    balance = -(-sum(nch) * 32 // 256)
+    assert max(nch) * 2 >= 3 * balance
+    assert p["cp_on"] == 1 and p["seg_chunks"] == max(32, (balance + 1) // 2)
+    assert p["total_segments"] == sum(max(1, -(-c // p["seg_chunks"])) for c in nch)
+    # equal lengths: no split (the longest takes exactly the balance)
+    assert varlen_plan([8192] * 8, 32)["cp_on"] == 0
+    # mild imbalance below 1.5x: no split
+    assert varlen_plan([9000, 7000] * 4, 32)["cp_on"] == 0
+    # the workload's definition wins when it says off
+    assert varlen_plan(lens, 32, cp_mode="off")["cp_on"] == 0
+
+
 def test_argument_errors(lib):
     d = desc()
     out = _abi.GdnPlanInfo()
