@@ -79,8 +79,10 @@ typedef enum gdn_cp_mode {
     GDN_CP_AUTO = 0,   /* CP when the recurrence would leave compute units idle without it: the
                           sequence-heads' row tiles fill at most half of its workgroup slots
                           and the longest sequence spans two sub-sequences of 16 chunks or
-                          more; a gate test at every sub-sequence boundary picks warmup
-                          or exact there */
+                          more; or, for packed sequences, when the longest one takes 1.5x
+                          (and at least 64) the chunk steps per slot the batch needs, in
+                          sub-sequences of half that (at least 32); a gate test at every
+                          sub-sequence boundary picks warmup or exact there */
     GDN_CP_OFF = 1,    /* one serial pass per sequence-head */
     GDN_CP_ON = 2,     /* CP regardless of the shape rule; per-boundary gate test */
     GDN_CP_EXACT = 3,  /* CP, exact correction for every sequence-head */
