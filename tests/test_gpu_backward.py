@@ -149,6 +149,27 @@ def test_varlen_many_sequences(gpu_lib, nseq, cp, kw):
     assert torch.equal(sT[4].cpu(), inp["initial_state"][4])
 
 
+def test_varlen_auto_cp_imbalance(gpu_lib):
+    """AutoCP's packed-sequence case: 4 sequences x 32 heads fill the recurrence slots, but the
+    longest (64 chunks) takes far more than the 12 chunk steps per slot the batch needs, so AUTO
+    splits it into 32-chunk sub-sequences; forward and backward against the oracle."""
+    import gated_deltanet_chunked_04_amd as gdn
+    lengths = [512, 4096, 500, 520]
+    inp = with_grads(small_inputs(H=32, K=128, V=128, dtype=torch.bfloat16, lengths=lengths, seed=41))
+    d = to_dev(inp)
+    p = gdn.gdn_plan(gdn.make_desc(d["q"], d["v"], cu_seqlens=d["cu_seqlens"], cu_seqlens_host=inp["cu_seqlens"],
+                                   cp_mode="auto"))
+    if p["cp_on"] != 1:
+        pytest.skip(f"AutoCP's slot count on this device leaves CP off ({p['seg_chunks']} chunks)")
+    assert p["seg_chunks"] == 32 and p["total_segments"] == 5
+    tol = tol_for(torch.bfloat16)
+    o, sT = gpu_fwd(d, cp_mode="auto")
+    o_ref, s_ref = oracle(inp)
+    check(o, o_ref, tol, "o")
+    check(sT, s_ref, tol, "final_state")
+    compare(gpu_bwd(d, cp_mode="auto"), oracle_bwd(inp), tol)
+
+
 def test_backward_no_initial_state_no_final_grad(gpu_lib):
     inp = with_grads(small_inputs(B=1, T=300, H=2, K=64, V=64, dtype=torch.float32, init_std=None))
     inp["d_final_state"] = None
