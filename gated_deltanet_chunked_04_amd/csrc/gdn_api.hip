@@ -160,6 +160,10 @@ gdn_status make_plan(const gdn_desc* d, Plan& p) {
         } else {
             const int64_t want = std::max<int64_t>(1, target / std::max<int64_t>(units, 1));
             seg_len = std::max<int64_t>(16, (max_nt + want - 1) / want);
+            // CP asked for on a batch that already fills the slots: sub-sequences of half the
+            // chunk steps per slot it needs, as AUTO takes for unequal packed sequences
+            if (seg_len >= max_nt && d->cp_mode != GDN_CP_AUTO && d->cp_mode != GDN_CP_PAGES)
+                seg_len = std::max<int64_t>(16, (balance + 1) / 2);
         }
         if (seg_len >= max_nt) {
             cp = false;

@@ -84,7 +84,9 @@ typedef enum gdn_cp_mode {
                           sub-sequences of half that (at least 32); a gate test at every
                           sub-sequence boundary picks warmup or exact there */
     GDN_CP_OFF = 1,    /* one serial pass per sequence-head */
-    GDN_CP_ON = 2,     /* CP regardless of the shape rule; per-boundary gate test */
+    GDN_CP_ON = 2,     /* CP regardless of the shape rule; per-boundary gate test. Without
+                          seg_chunks, a batch that already fills the slots takes sub-sequences
+                          of half the chunk steps per slot it needs (at least 16) */
     GDN_CP_EXACT = 3,  /* CP, exact correction for every sequence-head */
     GDN_CP_WARMUP = 4, /* CP, warmup for every sequence-head (caller asserts fast decay) */
     GDN_CP_PAGES = 5   /* the pages' AutoCP thresholds, tuned for a 132-SM part: CP iff

@@ -168,6 +168,11 @@ def test_varlen_plan_imbalance():
     assert varlen_plan([9000, 7000] * 4, 32)["cp_on"] == 0
     # the workload's definition wins when it says off
     assert varlen_plan(lens, 32, cp_mode="off")["cp_on"] == 0
+    # CP asked for on a slot-filling batch: the same balanced length, for equal lengths too
+    p = varlen_plan(lens, 32, cp_mode="on")
+    assert p["cp_on"] == 1 and p["seg_chunks"] == (balance + 1) // 2
+    p = varlen_plan([8192] * 8, 32, cp_mode="exact")
+    assert p["cp_on"] == 1 and p["seg_chunks"] == 64 and p["total_segments"] == 16
 
 
 def test_argument_errors(lib):
